@@ -1,0 +1,260 @@
+"""Seeded synthetic inputs for the TokenMixer-Large block stack.
+
+This module is shared by the CPU oracle and by the GPU tests/bench. It holds
+the workload descriptions and the random draws only: none of the method's
+arithmetic lives here.
+
+Draws follow one recipe everywhere:
+
+* ``numpy.random.Generator(PCG64(SeedSequence(seed, spawn_key=key)))`` and
+  ``standard_normal(dtype=float32)``;
+* key ``(0,)`` for the token tensor X, key ``(1, layer, sub, kind, position)``
+  for one position's slice of a weight bank, so every slice can be regenerated
+  on its own, in any order, in parallel;
+* token values are N(0, 1); up / gate / router weights N(0, 1/fan_in) with
+  fan_in the input width W; every down matrix 0.01 * N(0, 1/fan_in) with
+  fan_in its hidden size (the pages' down-matrix small init, TokenMixer-Large
+  summary section 2.4.4, realised with the normal init the workloads state);
+* for bf16 workloads every draw is rounded to the nearest bf16 value
+  (ties to even) by torch's fp32 -> bf16 conversion, so both sides consume
+  the very same bf16-representable numbers.
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+from concurrent.futures import ProcessPoolExecutor
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+SUB_MIX = 0
+SUB_REVERT = 1
+
+# weight kinds (values match the C header's TMX_W_* enumerators)
+K_NORM_GAIN = 0
+K_UP = 1
+K_GATE = 2
+K_DOWN = 3
+K_ROUTER = 4
+K_EXP_UP = 5
+K_EXP_GATE = 6
+K_EXP_DOWN = 7
+K_SH_UP = 8
+K_SH_GATE = 9
+K_SH_DOWN = 10
+
+KIND_NAMES = {
+    K_NORM_GAIN: "norm_gain", K_UP: "up", K_GATE: "gate", K_DOWN: "down",
+    K_ROUTER: "router", K_EXP_UP: "exp_up", K_EXP_GATE: "exp_gate",
+    K_EXP_DOWN: "exp_down", K_SH_UP: "sh_up", K_SH_GATE: "sh_gate",
+    K_SH_DOWN: "sh_down",
+}
+
+DENSE_KINDS = (K_UP, K_GATE, K_DOWN)
+MOE_KINDS = (K_ROUTER, K_EXP_UP, K_EXP_GATE, K_EXP_DOWN, K_SH_UP, K_SH_GATE, K_SH_DOWN)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Shape and init of one block-stack workload."""
+    name: str
+    B: int
+    T: int
+    H: int
+    D: int
+    L: int
+    hidden_mix: int = 0      # dense per-token hidden of the mix sub-layer
+    hidden_rev: int = 0      # dense per-token hidden of the revert sub-layer
+    E: int = 0               # routed experts per position (0 = dense)
+    top_k: int = 0
+    expert_hidden: int = 0
+    shared_hidden: int = 0
+    alpha: float = 0.0       # 0 means E / top_k
+    eps: float = 1e-6
+    gap: int = 2             # inter-residual gap (0 = none)
+    dtype: str = "bf16"      # "bf16" or "f32"
+    seed: int = 0
+    down_scale: float = 0.01
+
+    # -- derived -----------------------------------------------------------
+    @property
+    def moe(self) -> bool:
+        return self.E > 0
+
+    @property
+    def dh(self) -> int:
+        return self.D // self.H
+
+    @property
+    def gate_scale(self) -> float:
+        return self.alpha if self.alpha != 0.0 else self.E / self.top_k
+
+    def positions(self, sub: int) -> int:
+        return self.H if sub == SUB_MIX else self.T
+
+    def width(self, sub: int) -> int:
+        return self.T * self.D // self.H if sub == SUB_MIX else self.D
+
+    def hidden(self, sub: int) -> int:
+        return self.hidden_mix if sub == SUB_MIX else self.hidden_rev
+
+    def kinds(self):
+        return MOE_KINDS if self.moe else DENSE_KINDS
+
+    def kind_shape(self, sub: int, kind: int) -> Tuple[int, ...]:
+        """Logical row-major shape of one (sub-layer, kind) bank, all positions."""
+        P, W = self.positions(sub), self.width(sub)
+        if kind == K_NORM_GAIN:
+            return (W,)
+        if kind in (K_UP, K_GATE):
+            return (P, W, self.hidden(sub))
+        if kind == K_DOWN:
+            return (P, self.hidden(sub), W)
+        if kind == K_ROUTER:
+            return (P, W, self.E)
+        if kind in (K_EXP_UP, K_EXP_GATE):
+            return (P, self.E, W, self.expert_hidden)
+        if kind == K_EXP_DOWN:
+            return (P, self.E, self.expert_hidden, W)
+        if kind in (K_SH_UP, K_SH_GATE):
+            return (P, W, self.shared_hidden)
+        if kind == K_SH_DOWN:
+            return (P, self.shared_hidden, W)
+        raise ValueError(f"unknown kind {kind}")
+
+    def fan_in(self, sub: int, kind: int) -> int:
+        if kind == K_DOWN:
+            return self.hidden(sub)
+        if kind == K_EXP_DOWN:
+            return self.expert_hidden
+        if kind == K_SH_DOWN:
+            return self.shared_hidden
+        return self.width(sub)
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads of the block-stack forward (TokenMixer-Large summary,
+# sections 2.3-2.4; batch sizes as in the reproduction README's commands).
+WORKLOADS: Dict[int, Workload] = {
+    1: Workload("tiny_dense_fp32", B=128, T=4, H=4, D=32, L=1, hidden_mix=64,
+                hidden_rev=64, gap=2, dtype="f32", seed=0),
+    2: Workload("dense_pertoken_swiglu", B=4096, T=16, H=16, D=256, L=4,
+                hidden_mix=1024, hidden_rev=1024, gap=2, seed=1),
+    3: Workload("uneven_mixing_h8", B=4096, T=16, H=8, D=256, L=4,
+                hidden_mix=1024, hidden_rev=1024, gap=2, seed=2),
+    4: Workload("sparse_pertoken_moe", B=4096, T=16, H=16, D=512, L=8, E=16,
+                top_k=4, expert_hidden=256, shared_hidden=512, alpha=4.0,
+                gap=2, seed=3),
+    5: Workload("large_moe_15b", B=8192, T=32, H=32, D=768, L=8, E=32,
+                top_k=4, expert_hidden=384, shared_hidden=768, alpha=8.0,
+                gap=2, seed=4),
+}
+
+
+# ---------------------------------------------------------------------------
+# draws
+# ---------------------------------------------------------------------------
+
+def _rng(seed: int, key: Tuple[int, ...]) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=key)))
+
+
+def to_bf16_values(a: np.ndarray) -> np.ndarray:
+    """Nearest bf16 values (ties to even) of an fp32 array, returned as fp32."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def _finish(cfg: Workload, a: np.ndarray) -> np.ndarray:
+    return to_bf16_values(a) if cfg.dtype == "bf16" else a
+
+
+def make_x(cfg: Workload, seed: Optional[int] = None, B: Optional[int] = None) -> np.ndarray:
+    """Token tensor X [B, T, D], N(0, 1) (fp32 array of dtype-representable values)."""
+    s = cfg.seed if seed is None else seed
+    n = cfg.B if B is None else B
+    a = _rng(s, (0,)).standard_normal((n, cfg.T, cfg.D), dtype=np.float32)
+    return _finish(cfg, a)
+
+
+def weight_slice(cfg: Workload, layer: int, sub: int, kind: int, p: int,
+                 seed: Optional[int] = None) -> np.ndarray:
+    """One position's slice of a weight bank (fp32 array, dtype-representable)."""
+    shape = cfg.kind_shape(sub, kind)
+    if kind == K_NORM_GAIN:
+        return np.ones(shape, np.float32)
+    s = cfg.seed if seed is None else seed
+    a = _rng(s, (1, layer, sub, kind, p)).standard_normal(shape[1:], dtype=np.float32)
+    std = np.float32(1.0 / np.sqrt(cfg.fan_in(sub, kind)))
+    if kind in (K_DOWN, K_EXP_DOWN, K_SH_DOWN):
+        std = np.float32(std * cfg.down_scale)
+    return _finish(cfg, a * std)
+
+
+def weight_bank(cfg: Workload, layer: int, sub: int, kind: int,
+                seed: Optional[int] = None) -> np.ndarray:
+    """A whole (layer, sub-layer, kind) bank, all positions stacked."""
+    if kind == K_NORM_GAIN:
+        return weight_slice(cfg, layer, sub, kind, 0, seed)
+    P = cfg.positions(sub)
+    return np.stack([weight_slice(cfg, layer, sub, kind, p, seed) for p in range(P)])
+
+
+def _bank_job(args):
+    cfg, layer, sub, kind, seed = args
+    return (layer, sub, kind), weight_bank(cfg, layer, sub, kind, seed)
+
+
+def all_weights(cfg: Workload, seed: Optional[int] = None, workers: int = 0):
+    """{(layer, sub, kind): bank} for every bank of the stack (layers 1..L).
+
+    ``workers`` > 1 generates banks in a process pool (same values: every
+    slice has its own seed key).
+    """
+    jobs = [(cfg, l, s, k, seed) for l in range(1, cfg.L + 1) for s in (SUB_MIX, SUB_REVERT)
+            for k in cfg.kinds()]
+    if workers and workers > 1:
+        with ProcessPoolExecutor(max_workers=workers) as ex:
+            return dict(ex.map(_bank_job, jobs))
+    return dict(_bank_job(j) for j in jobs)
+
+
+def default_workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def param_count(cfg: Workload) -> int:
+    """Number of weight values of the stack (norm gains excluded)."""
+    total = 0
+    for sub in (SUB_MIX, SUB_REVERT):
+        for kind in cfg.kinds():
+            total += int(np.prod(cfg.kind_shape(sub, kind)))
+    return total * cfg.L
+
+
+class WeightSource:
+    """Lazy (layer, sub, kind, position) -> fp32 slice, with an optional cache
+    of whole banks (e.g. banks already generated for a GPU upload)."""
+
+    def __init__(self, cfg: Workload, banks=None, seed: Optional[int] = None):
+        self.cfg = cfg
+        self.banks = banks
+        self.seed = seed
+
+    def __call__(self, layer: int, sub: int, kind: int, p: int) -> np.ndarray:
+        if self.banks is not None and (layer, sub, kind) in self.banks:
+            b = self.banks[(layer, sub, kind)]
+            return b if kind == K_NORM_GAIN else b[p]
+        return weight_slice(self.cfg, layer, sub, kind, p, self.seed)

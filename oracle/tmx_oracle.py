@@ -1,0 +1,312 @@
+"""Plain, slow fp64 CPU oracle of the TokenMixer-Large block-stack forward.
+
+TEST INFRASTRUCTURE ONLY. It exists to check the HIP path; it is imported by
+``tests/``, by ``__graft_entry__.smoke()`` and by ``bench.py``'s cpu_baseline
+leg, and by nothing else. It shares no code with the HIP library: every index
+map and formula below is written out again from the pages.
+
+Citations name the page and the equation / section / table they follow:
+
+* [TML] "TokenMixer-Large: Scaling Up Large Ranking Models in Industrial
+  Recommenders", the paper-archivist summary (sections 2.3-2.4, Eq. 9-21).
+* [TML-README] the fay85/tokenmixerlarge README (block diagram in Pre-Norm
+  form, flag table, documented deviations).
+* [RMX-GUIDE] the samxiexs/RankMixer reproduction guide (section 5 token
+  mixing constraints, section 6.1 per-token weight layout).
+* [RMX-BOOK] the fun-rec mdbook chapter 7.4 on RankMixer (7.4.1, 7.4.2).
+
+Precision contract (the pages fix none, see the readings in the design doc): all
+arithmetic is fp64. In bf16 mode the value is rounded to bf16 (round to
+nearest, ties to even) exactly at the storage points the GPU path has:
+the normalised rows x_hat, the SwiGLU hidden U, and each sub-layer output
+(residual + F [+ inter-residual]) rounded once. Everything else (norm
+statistics, router logits, softmax, gates, down outputs, the combine and the
+residual sums) stays unrounded.
+
+Pins: every function here is checked in ``tests/test_oracle_*.py`` against
+something other than itself (closed forms, textbook routines, brute force,
+hand-worked fixtures under ``tests/golden/``). No function is unpinned.
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Dict, Optional, Tuple
+
+import numpy as np
+
+__all__ = [
+    "round_bf16", "mix", "revert", "rmsnorm", "silu", "softmax", "swiglu",
+    "route", "moe", "sublayer_positions", "block_forward", "stack_forward",
+    "flops_per_sample", "param_count_closed_form",
+]
+
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+# ---------------------------------------------------------------------------
+# rounding point
+# ---------------------------------------------------------------------------
+
+def round_bf16(x) -> np.ndarray:
+    """rho(x): nearest bfloat16 value of fp64 x, ties to even, as fp64.
+
+    bfloat16 keeps 8 significant bits (1 implicit + 7 stored) and the fp32
+    exponent range, so a normal value m * 2**e (0.5 <= |m| < 1) is quantised
+    to a multiple of 2**(e - 8); subnormals to multiples of 2**-133.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    finite = np.isfinite(x)
+    xf = np.where(finite, x, 0.0)
+    _, e = np.frexp(xf)
+    q = np.maximum(e - 8, -133)
+    y = np.ldexp(np.rint(np.ldexp(xf, -q)), q)       # exact scaling; rint = half-even
+    y = np.where(np.abs(y) > BF16_MAX, np.copysign(np.inf, y), y)
+    return np.where(finite, y, x)
+
+
+def _rho(x, on: bool):
+    return round_bf16(x) if on else x
+
+
+# ---------------------------------------------------------------------------
+# Mix / Revert   [TML] Eq. 9-11 and Eq. 13-15
+# ---------------------------------------------------------------------------
+
+def mix(X: np.ndarray, H: int) -> np.ndarray:
+    """Mixing: split every token into H heads of width dh = D/H (Eq. 9); mixed
+    token h concatenates head h of tokens 1..T (Eq. 10); stacking gives
+    H in R^{H x T*D/H} (Eq. 11). Per sample:
+    Hm[h, t*dh + j] = X[t, h*dh + j].
+    D must be a multiple of H ([RMX-GUIDE] section 5)."""
+    B, T, D = X.shape
+    if D % H:
+        raise ValueError("D must be divisible by H")
+    dh = D // H
+    out = np.empty((B, H, T * dh), dtype=X.dtype)
+    for h in range(H):
+        for t in range(T):
+            out[:, h, t * dh:(t + 1) * dh] = X[:, t, h * dh:(h + 1) * dh]
+    return out
+
+
+def revert(Hm: np.ndarray, T: int) -> np.ndarray:
+    """Reverting: split every mixed token into T pieces of width dh (Eq. 13);
+    token t concatenates piece t of mixed tokens 1..H (Eq. 14-15). Per sample:
+    X_rev[t, h*dh + j] = Hm[h, t*dh + j] -- the inverse of ``mix``."""
+    B, H, Wm = Hm.shape
+    if Wm % T:
+        raise ValueError("mixed width must be divisible by T")
+    dh = Wm // T
+    out = np.empty((B, T, H * dh), dtype=Hm.dtype)
+    for t in range(T):
+        for h in range(H):
+            out[:, t, h * dh:(h + 1) * dh] = Hm[:, h, t * dh:(t + 1) * dh]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm, Swish, SwiGLU   [TML] section 2.3.2-2.3.3, Eq. 17-18
+# ---------------------------------------------------------------------------
+
+def rmsnorm(v: np.ndarray, gamma: Optional[np.ndarray], eps: float) -> np.ndarray:
+    """Llama-style RMSNorm over the last axis (no mean centring, [TML] 2.3.3;
+    [TML-README] 'RMSNorm + no bias'): v / sqrt(mean(v^2) + eps) * gamma."""
+    v = np.asarray(v, dtype=np.float64)
+    ms = np.mean(v * v, axis=-1, keepdims=True)
+    r = 1.0 / np.sqrt(ms + eps)
+    out = v * r
+    if gamma is not None:
+        out = out * np.asarray(gamma, dtype=np.float64)
+    return out
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """Swish with beta = 1: z * sigmoid(z) ([TML] Eq. 17)."""
+    z = np.asarray(z, dtype=np.float64)
+    # sigmoid written in the branch that never overflows exp
+    e = np.exp(-np.abs(z))
+    sig = np.where(z >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+    return z * sig
+
+
+def softmax(l: np.ndarray) -> np.ndarray:
+    l = np.asarray(l, dtype=np.float64)
+    m = np.max(l, axis=-1, keepdims=True)
+    e = np.exp(l - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def swiglu(v: np.ndarray, w_up: np.ndarray, w_gate: np.ndarray, w_down: np.ndarray,
+           rho: bool = False) -> np.ndarray:
+    """pSwiGLU of one position: FC_down(Swish(FC_gate(v)) * FC_up(v)) ([TML]
+    Eq. 17-18), no bias, row-vector convention v @ W with W_up, W_gate [W, h]
+    and W_down [h, W] ([RMX-GUIDE] 6.1: W1 [T, D, kD], W2 [T, kD, D]).
+    In bf16 mode the hidden U is rounded to bf16 before the down projection."""
+    v = np.asarray(v, dtype=np.float64)
+    g = v @ np.asarray(w_gate, dtype=np.float64)
+    u = v @ np.asarray(w_up, dtype=np.float64)
+    U = _rho(silu(g) * u, rho)
+    return U @ np.asarray(w_down, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Sparse-Pertoken MoE   [TML] section 2.4, Eq. 19-21
+# ---------------------------------------------------------------------------
+
+def route(xhat: np.ndarray, w_router: np.ndarray, top_k: int, alpha: float):
+    """Router of one position: logits l = xhat @ Wr, pi = softmax(l) over all
+    E experts, chosen set = the top_k experts under the key (-l_e, e) (largest
+    logit first, ties to the lowest index), gate = alpha * pi of the chosen
+    experts, not renormalised ([TML] Eq. 19 and 21).
+
+    Returns (idx [n, k] int, gate [n, k], logits [n, E], pi [n, E]).
+    Output slots follow the same key order."""
+    xhat = np.asarray(xhat, dtype=np.float64)
+    logits = xhat @ np.asarray(w_router, dtype=np.float64)
+    n, E = logits.shape
+    if not 1 <= top_k <= E:
+        raise ValueError("need 1 <= top_k <= E")
+    pi = softmax(logits)
+    experts = np.broadcast_to(np.arange(E), logits.shape)
+    order = np.lexsort((experts, -logits), axis=-1)   # primary -l, then e
+    idx = order[:, :top_k]
+    gate = alpha * np.take_along_axis(pi, idx, axis=-1)
+    return idx, gate, logits, pi
+
+
+def moe(xhat: np.ndarray, w_router, exp_up, exp_gate, exp_down,
+        sh_up, sh_gate, sh_down, top_k: int, alpha: float, rho: bool = False):
+    """Sparse-Pertoken MoE of one position ([TML] Eq. 19-21): the routed
+    experts' SwiGLU outputs weighted by alpha * pi, plus the always-on shared
+    SwiGLU expert of this position, ungated ([TML] 2.4.2). Only the chosen
+    experts are evaluated, each on its own rows.
+
+    Returns (y [n, W], idx, gate)."""
+    idx, gate, _, _ = route(xhat, w_router, top_k, alpha)
+    n = xhat.shape[0]
+    E = np.asarray(w_router).shape[1]
+    routed = np.zeros((n, np.asarray(exp_down).shape[-1]))
+    for e in range(E):
+        rows, slots = np.nonzero(idx == e)
+        if rows.size == 0:
+            continue
+        ye = swiglu(xhat[rows], exp_up[e], exp_gate[e], exp_down[e], rho)
+        routed[rows] += gate[rows, slots][:, None] * ye
+    shared = swiglu(xhat, sh_up, sh_gate, sh_down, rho)
+    return routed + shared, idx, gate
+
+
+# ---------------------------------------------------------------------------
+# sub-layer, block, stack   [TML] Eq. 12 and 16 in Pre-Norm form,
+# [TML-README] block diagram, [TML] 2.3.4 inter-residual
+# ---------------------------------------------------------------------------
+
+WeightGetter = Callable[[int, int, int, int], np.ndarray]
+
+# weight kind ids (same numbering as the seeded generator and the C header)
+_K_GAIN, _K_UP, _K_GATE, _K_DOWN = 0, 1, 2, 3
+_K_ROUTER, _K_EUP, _K_EGATE, _K_EDOWN, _K_SUP, _K_SGATE, _K_SDOWN = 4, 5, 6, 7, 8, 9, 10
+
+
+def sublayer_positions(x: np.ndarray, resid: np.ndarray, cfg, layer: int, sub: int,
+                       weights: WeightGetter, extra: Optional[np.ndarray] = None,
+                       rho: bool = False, record: Optional[dict] = None) -> np.ndarray:
+    """One Pre-Norm sub-layer over position-major rows:
+    out[:, p] = resid[:, p] + F_p(RMSNorm(x[:, p])) [+ extra[:, p]], rounded
+    once in bf16 mode. x, resid, extra are [n, P, W]; F_p is the position's
+    own SwiGLU (dense) or Sparse-Pertoken MoE. ``record`` (optional dict)
+    receives per-position routing {(p): (idx, gate)} for MoE sub-layers."""
+    n, P, W = x.shape
+    gain = weights(layer, sub, _K_GAIN, 0)
+    F = np.zeros((n, P, W))
+    for p in range(P):
+        xh = _rho(rmsnorm(x[:, p, :], gain, cfg.eps), rho)
+        if cfg.E == 0:
+            F[:, p] = swiglu(xh, weights(layer, sub, _K_UP, p), weights(layer, sub, _K_GATE, p),
+                             weights(layer, sub, _K_DOWN, p), rho)
+        else:
+            y, idx, gate = moe(xh, weights(layer, sub, _K_ROUTER, p),
+                               weights(layer, sub, _K_EUP, p), weights(layer, sub, _K_EGATE, p),
+                               weights(layer, sub, _K_EDOWN, p), weights(layer, sub, _K_SUP, p),
+                               weights(layer, sub, _K_SGATE, p), weights(layer, sub, _K_SDOWN, p),
+                               cfg.top_k, cfg.gate_scale, rho)
+            F[:, p] = y
+            if record is not None:
+                record[p] = (idx, gate)
+    out = np.asarray(resid, dtype=np.float64) + F
+    if extra is not None:
+        out = out + np.asarray(extra, dtype=np.float64)
+    return _rho(out, rho)
+
+
+def block_forward(X: np.ndarray, cfg, layer: int, weights: WeightGetter,
+                  extra: Optional[np.ndarray] = None, rho: bool = False,
+                  trace: Optional[dict] = None) -> np.ndarray:
+    """One TokenMixer-Large block in Pre-Norm form ([TML-README] diagram;
+    [TML] Eq. 12, 16 with Pre-Norm per section 2.3.3):
+        Hm      = Mix(X)
+        H_next  = Hm + F_mix(Norm(Hm))              (intra-mixing residual)
+        X_rev   = Revert(H_next)
+        X_next  = X + F_rev(Norm(X_rev)) [+ extra]  (residual to the block input)
+    ``extra`` is the inter-residual term added before the single rounding."""
+    Hm = mix(X, cfg.H)
+    Hn = sublayer_positions(Hm, Hm, cfg, layer, 0, weights, None, rho,
+                            None if trace is None else trace.setdefault((layer, 0), {}))
+    Xr = revert(Hn, cfg.T)
+    if trace is not None:
+        trace[("in", layer, 0)] = X
+        trace[("in", layer, 1)] = Xr
+    return sublayer_positions(Xr, X, cfg, layer, 1, weights, extra, rho,
+                              None if trace is None else trace.setdefault((layer, 1), {}))
+
+
+def stack_forward(X: np.ndarray, cfg, weights: WeightGetter, rho: Optional[bool] = None,
+                  trace: Optional[dict] = None) -> np.ndarray:
+    """The L-block stack with inter-residuals ([TML] 2.3.4; [TML-README]):
+    Y_0 = X; Z_l = Block_l(Y_{l-1}); Y_l = Z_l + Y_{l-g} when g > 0,
+    l mod g == 0 and l < L (never after the last block); else Y_l = Z_l.
+    Returns Y_L. ``rho`` defaults to the workload dtype being bf16."""
+    if rho is None:
+        rho = cfg.dtype == "bf16"
+    Y = [np.asarray(X, dtype=np.float64)]
+    g = cfg.gap
+    for l in range(1, cfg.L + 1):
+        extra = Y[l - g] if (g > 0 and l % g == 0 and l < cfg.L) else None
+        Y.append(block_forward(Y[l - 1], cfg, l, weights, extra, rho, trace))
+    return Y[cfg.L]
+
+
+# ---------------------------------------------------------------------------
+# closed forms of the work   [RMX-BOOK] 7.4.2 (Param = FLOPs = 2TkD^2 MACs)
+# ---------------------------------------------------------------------------
+
+def param_count_closed_form(cfg) -> int:
+    """Weights of the stack: dense L * sum_sub 3 P W h; MoE
+    L * sum_sub P (3 E W h_e + 3 W h_s + W E). Norm gains excluded."""
+    total = 0
+    for sub in (0, 1):
+        P = cfg.H if sub == 0 else cfg.T
+        W = cfg.T * cfg.D // cfg.H if sub == 0 else cfg.D
+        if cfg.E == 0:
+            h = cfg.hidden_mix if sub == 0 else cfg.hidden_rev
+            total += 3 * P * W * h
+        else:
+            total += P * (3 * cfg.E * W * cfg.expert_hidden + 3 * W * cfg.shared_hidden + W * cfg.E)
+    return cfg.L * total
+
+
+def flops_per_sample(cfg) -> int:
+    """Algorithmic GEMM FLOPs (2 per multiply-add) of one sample's forward:
+    up, gate and down of every position; for MoE only the k chosen experts,
+    the shared expert and the router count."""
+    total = 0
+    for sub in (0, 1):
+        P = cfg.H if sub == 0 else cfg.T
+        W = cfg.T * cfg.D // cfg.H if sub == 0 else cfg.D
+        if cfg.E == 0:
+            h = cfg.hidden_mix if sub == 0 else cfg.hidden_rev
+            total += 2 * P * 3 * W * h
+        else:
+            total += 2 * P * (3 * cfg.top_k * W * cfg.expert_hidden
+                              + 3 * W * cfg.shared_hidden + W * cfg.E)
+    return cfg.L * total

@@ -1,0 +1,465 @@
+"""Pins of the CPU oracle against the pages and plain mathematics.
+
+Every oracle function is checked here against something other than itself:
+hand-worked fixtures (tests/golden), closed forms, textbook routines (numpy
+reshape/swapaxes, torch's bf16 conversion), brute-force enumeration, and
+invariants the pages state. Each test names the mistake it would catch.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import datagen as dg
+import oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _num(s):
+    """Parse the small expression language of the golden files."""
+    return float(eval(s.replace("^", "**"), {"__builtins__": {}},
+                      {"ln3": math.log(3.0), "inf": math.inf}))
+
+
+# ---------------------------------------------------------------------------
+# rho (bf16 rounding)
+# ---------------------------------------------------------------------------
+
+def test_round_bf16_hand_cases():
+    g = _load("bf16_rounding.json")
+    for src, want in g["cases"]:
+        got = float(orc.round_bf16(_num(src)))
+        assert got == _num(want), (src, got, want)
+
+
+def test_round_bf16_matches_torch_on_fp32_inputs():
+    # Reduces to a library routine: for fp32 inputs, rounding to bf16 is
+    # torch's fp32 -> bf16 conversion (round to nearest even).
+    import torch
+    rng = np.random.default_rng(7)
+    a = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * np.float32(10.0) ** rng.integers(-30, 30, 200000).astype(np.float32),
+        # exact ties: bf16 value + half a spacing
+        (np.float32(1.0) + np.arange(1, 2000, dtype=np.float32) * np.float32(2.0 ** -8)),
+    ]).astype(np.float32)
+    a = a[np.isfinite(a)]
+    want = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+    got = orc.round_bf16(a.astype(np.float64))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_round_bf16_is_idempotent_and_monotone():
+    rng = np.random.default_rng(3)
+    x = np.sort(rng.standard_normal(10000) * 100)
+    y = orc.round_bf16(x)
+    np.testing.assert_array_equal(orc.round_bf16(y), y)
+    assert np.all(np.diff(y) >= 0)
+    assert np.max(np.abs(y - x) / np.abs(x)) <= 2.0 ** -8 * (1 + 1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Mix / Revert  (Eq. 9-15)
+# ---------------------------------------------------------------------------
+
+def test_mix_revert_hand_cases():
+    g = _load("mix_revert_maps.json")
+    for c in g["cases"]:
+        X = np.array(c["X"], dtype=np.float64)[None]
+        want = np.array(c["mixed"], dtype=np.float64)[None]
+        got = orc.mix(X, c["H"])
+        np.testing.assert_array_equal(got, want)
+        np.testing.assert_array_equal(orc.revert(want, c["T"]), X)
+
+
+@pytest.mark.parametrize("T,H,D", [(4, 4, 32), (16, 16, 256), (16, 8, 256), (16, 16, 512),
+                                   (32, 32, 768), (3, 6, 12), (5, 1, 10), (1, 1, 8)])
+def test_mix_is_textbook_reshape_swap(T, H, D):
+    # Reduces to a textbook routine: reshape (T, H, dh) -> swap axes -> reshape.
+    rng = np.random.default_rng(T * 100 + H)
+    X = rng.standard_normal((3, T, D))
+    dh = D // H
+    ref = X.reshape(3, T, H, dh).swapaxes(1, 2).reshape(3, H, T * dh)
+    Hm = orc.mix(X, H)
+    np.testing.assert_array_equal(Hm, ref)
+    # bijection: Revert(Mix(X)) == X and Mix(Revert(Hm)) == Hm bit-exactly
+    np.testing.assert_array_equal(orc.revert(Hm, T), X)
+    np.testing.assert_array_equal(orc.mix(orc.revert(Hm, T), H), Hm)
+
+
+def test_mix_rejects_indivisible_width():
+    with pytest.raises(ValueError):
+        orc.mix(np.zeros((1, 4, 10)), 4)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm, Swish, SwiGLU, MoE hand examples
+# ---------------------------------------------------------------------------
+
+def test_rmsnorm_closed_forms():
+    v = np.array([[3.0, 4.0]])
+    eps = 1e-6
+    r = 1.0 / math.sqrt(12.5 + eps)
+    np.testing.assert_allclose(orc.rmsnorm(v, None, eps), [[3 * r, 4 * r]], rtol=1e-15)
+    # output rms is 1 * (1 - O(eps)): exactly sqrt(ms / (ms + eps))
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((50, 37))
+    y = orc.rmsnorm(x, None, eps)
+    ms = np.mean(x * x, axis=1)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=1)), np.sqrt(ms / (ms + eps)), rtol=1e-13)
+    # scale invariance up to the eps term: with eps = 0 exact for c = 2^k
+    np.testing.assert_allclose(orc.rmsnorm(8.0 * x, None, 0.0), orc.rmsnorm(x, None, 0.0), rtol=1e-15)
+    # gain multiplies per column
+    gamma = np.arange(1, 38, dtype=np.float64)
+    np.testing.assert_allclose(orc.rmsnorm(x, gamma, eps), y * gamma, rtol=1e-15)
+
+
+def test_silu_closed_forms():
+    z = np.array([0.0, math.log(3.0), -math.log(3.0), 50.0, -50.0, 1.0])
+    s = orc.silu(z)
+    assert s[0] == 0.0
+    assert s[1] == pytest.approx(0.75 * math.log(3.0), rel=1e-15)
+    assert s[2] == pytest.approx(-0.25 * math.log(3.0), rel=1e-15)
+    assert s[3] == pytest.approx(50.0, rel=1e-15)
+    assert abs(s[4]) < 1e-19
+    assert s[5] == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+    # odd part: silu(z) - silu(-z) = z
+    zz = np.linspace(-20, 20, 401)
+    np.testing.assert_allclose(orc.silu(zz) - orc.silu(-zz), zz, atol=1e-13)
+
+
+def test_softmax_closed_form():
+    p = orc.softmax(np.array([[math.log(3.0), 0.0], [1000.0, 1000.0]]))
+    np.testing.assert_allclose(p, [[0.75, 0.25], [0.5, 0.5]], rtol=1e-15)
+
+
+def test_dense_sublayer_hand_example():
+    g = _load("sublayer_hand.json")
+    d = g["dense"]
+    cfg = dg.Workload("hand", B=1, T=1, H=1, D=2, L=1, hidden_mix=1, hidden_rev=1, eps=0.0,
+                      dtype="f32", gap=0)
+    W = {dg.K_NORM_GAIN: np.ones(2), dg.K_UP: np.array(d["w_up"])[None],
+         dg.K_GATE: np.array(d["w_gate"])[None], dg.K_DOWN: np.array(d["w_down"])[None]}
+
+    def weights(layer, sub, kind, p):
+        return W[kind] if kind == dg.K_NORM_GAIN else W[kind][p]
+
+    x = np.array(d["x"])[None, None]
+    out = orc.sublayer_positions(x, x, cfg, 1, 0, weights)
+    np.testing.assert_allclose(out[0, 0], [_num(e) for e in d["expected"]], rtol=1e-15)
+
+
+def test_moe_hand_example():
+    g = _load("sublayer_hand.json")
+    d, m = g["dense"], g["moe"]
+    z = np.zeros((2, 1))
+    exp_up = np.stack([np.array(d["w_up"]), z])
+    exp_gate = np.stack([np.array(d["w_gate"]), z])
+    exp_down = np.stack([np.array(d["w_down"]), np.zeros((1, 2))])
+    sh_down = np.array([[0.0, 1.0]])
+    x = np.array([m["x"]])
+    y, idx, gate = orc.moe(x, np.array(m["w_router"]), exp_up, exp_gate, exp_down,
+                           np.array(d["w_up"]), np.array(d["w_gate"]), sh_down,
+                           m["top_k"], m["alpha"])
+    assert idx.tolist() == [m["expected_idx"]]
+    np.testing.assert_allclose(gate[0], [_num(v) for v in m["expected_gate"]], rtol=1e-15)
+    np.testing.assert_allclose(x[0] + y[0], [_num(e) for e in m["expected"]], rtol=1e-15)
+
+
+def test_swiglu_orientation_nonsquare():
+    # Row-vector convention with W_up/W_gate [W, h], W_down [h, W]; written
+    # element by element on a non-square case so a transposed operand fails.
+    rng = np.random.default_rng(11)
+    W, h = 3, 5
+    v = rng.standard_normal((2, W))
+    Wu, Wg, Wd = rng.standard_normal((W, h)), rng.standard_normal((W, h)), rng.standard_normal((h, W))
+    want = np.zeros((2, W))
+    for n in range(2):
+        for k in range(W):
+            acc = 0.0
+            for j in range(h):
+                gj = sum(v[n, i] * Wg[i, j] for i in range(W))
+                uj = sum(v[n, i] * Wu[i, j] for i in range(W))
+                acc += gj / (1.0 + math.exp(-gj)) * uj * Wd[j, k]
+            want[n, k] = acc
+    np.testing.assert_allclose(orc.swiglu(v, Wu, Wg, Wd), want, rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# router (Eq. 19-21): brute force, ties, exact arithmetic
+# ---------------------------------------------------------------------------
+
+def _brute_force_topk(l, k):
+    """Enumerate all k-subsets; the unique one whose members all beat every
+    non-member under the key (-l_e, e)."""
+    E = len(l)
+    key = lambda e: (-l[e], e)
+    winners = [S for S in itertools.combinations(range(E), k)
+               if all(key(a) < key(b) for a in S for b in range(E) if b not in S)]
+    assert len(winners) == 1
+    return sorted(winners[0], key=key)
+
+
+@pytest.mark.parametrize("E,k", [(2, 1), (4, 2), (6, 3), (8, 4), (8, 1), (8, 8), (5, 4)])
+def test_route_brute_force(E, k):
+    rng = np.random.default_rng(E * 10 + k)
+    n, W = 40, 6
+    x = rng.standard_normal((n, W))
+    Wr = rng.standard_normal((W, E))
+    # plant exact ties in half the rows: integer-valued logits
+    xi = rng.integers(-2, 3, (n, W)).astype(np.float64)
+    Wi = rng.integers(-1, 2, (W, E)).astype(np.float64)
+    for xx, ww in ((x, Wr), (xi, Wi)):
+        idx, gate, logits, pi = orc.route(xx, ww, k, 1.5)
+        for r in range(n):
+            assert idx[r].tolist() == _brute_force_topk(logits[r].tolist(), k)
+        np.testing.assert_allclose(pi.sum(1), 1.0, rtol=1e-14)
+        np.testing.assert_allclose(gate, 1.5 * np.take_along_axis(pi, idx, 1), rtol=0)
+
+
+def test_route_duplicate_columns_tie_to_lowest_index():
+    # duplicated router columns give bit-identical logits: lowest index wins
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((30, 16))
+    base = rng.standard_normal((16, 4))
+    Wr = np.concatenate([base, base], axis=1)      # experts e and e+4 tie
+    idx, _, _, _ = orc.route(x, Wr, 4, 2.0)
+    for r in range(30):
+        top = np.argsort(-(x[r] @ base), kind="stable")[:2]
+        # the two best columns each appear twice; the lower copies come first
+        assert idx[r].tolist() == [top[0], top[0] + 4, top[1], top[1] + 4]
+
+
+def test_route_rejects_bad_k():
+    with pytest.raises(ValueError):
+        orc.route(np.zeros((1, 2)), np.zeros((2, 3)), 4, 1.0)
+
+
+# ---------------------------------------------------------------------------
+# MoE invariants
+# ---------------------------------------------------------------------------
+
+def _rand_moe(rng, W=6, E=5, he=3, hs=4):
+    return dict(w_router=rng.standard_normal((W, E)), exp_up=rng.standard_normal((E, W, he)),
+                exp_gate=rng.standard_normal((E, W, he)), exp_down=rng.standard_normal((E, he, W)),
+                sh_up=rng.standard_normal((W, hs)), sh_gate=rng.standard_normal((W, hs)),
+                sh_down=rng.standard_normal((hs, W)))
+
+
+def test_moe_full_topk_is_soft_mixture():
+    # top_k = E, alpha = 1: sum_e pi_e SwiGLU_e + shared (dense gated sum)
+    rng = np.random.default_rng(1)
+    w = _rand_moe(rng)
+    x = rng.standard_normal((20, 6))
+    y, _, _ = orc.moe(x, **w, top_k=5, alpha=1.0)
+    logits = x @ w["w_router"]
+    pi = np.exp(logits) / np.exp(logits).sum(1, keepdims=True)
+    want = orc.swiglu(x, w["sh_up"], w["sh_gate"], w["sh_down"])
+    for e in range(5):
+        want = want + pi[:, e:e + 1] * orc.swiglu(x, w["exp_up"][e], w["exp_gate"][e], w["exp_down"][e])
+    np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-12)
+
+
+def test_moe_sparse_equals_dense_compute_then_mask():
+    # TML-README deviation: evaluating every expert then masking the unchosen
+    # ones gives the same output as sparse evaluation.
+    rng = np.random.default_rng(2)
+    w = _rand_moe(rng)
+    x = rng.standard_normal((25, 6))
+    y, idx, gate = orc.moe(x, **w, top_k=2, alpha=2.5)
+    logits = x @ w["w_router"]
+    pi = np.exp(logits - logits.max(1, keepdims=True))
+    pi /= pi.sum(1, keepdims=True)
+    ranks = np.argsort(np.argsort(-logits, axis=1, kind="stable"), axis=1, kind="stable")
+    mask = ranks < 2
+    all_out = np.stack([orc.swiglu(x, w["exp_up"][e], w["exp_gate"][e], w["exp_down"][e])
+                        for e in range(5)], axis=1)           # [n, E, W]
+    want = 2.5 * np.einsum("ne,new->nw", pi * mask, all_out) + orc.swiglu(
+        x, w["sh_up"], w["sh_gate"], w["sh_down"])
+    np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-12)
+
+
+def test_moe_expert_relabelling_invariance():
+    rng = np.random.default_rng(3)
+    w = _rand_moe(rng)
+    x = rng.standard_normal((25, 6))
+    y, _, _ = orc.moe(x, **w, top_k=3, alpha=5 / 3)
+    perm = rng.permutation(5)
+    w2 = dict(w)
+    w2["w_router"] = w["w_router"][:, perm]
+    for kk in ("exp_up", "exp_gate", "exp_down"):
+        w2[kk] = w[kk][perm]
+    y2, _, _ = orc.moe(x, **w2, top_k=3, alpha=5 / 3)
+    np.testing.assert_allclose(y2, y, rtol=1e-12, atol=1e-14)
+
+
+def test_moe_linear_in_alpha_without_shared():
+    rng = np.random.default_rng(4)
+    w = _rand_moe(rng)
+    for kk in ("sh_up", "sh_gate", "sh_down"):
+        w[kk] = np.zeros_like(w[kk])
+    x = rng.standard_normal((25, 6))
+    y1, _, _ = orc.moe(x, **w, top_k=2, alpha=1.0)
+    y3, _, _ = orc.moe(x, **w, top_k=2, alpha=3.0)
+    np.testing.assert_allclose(y3, 3.0 * y1, rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# stack wiring (Pre-Norm block, residual to block input, inter-residual)
+# ---------------------------------------------------------------------------
+
+def _zero_down(getter, subs=(0, 1)):
+    downs = (dg.K_DOWN, dg.K_EXP_DOWN, dg.K_SH_DOWN)
+
+    def g(layer, sub, kind, p):
+        w = getter(layer, sub, kind, p)
+        return np.zeros_like(w) if (kind in downs and sub in subs) else w
+    return g
+
+
+SMALL = {
+    "dense": dg.Workload("small_dense", B=6, T=4, H=2, D=8, L=4, hidden_mix=12, hidden_rev=10,
+                         dtype="bf16", seed=9),
+    "moe": dg.Workload("small_moe", B=6, T=4, H=4, D=8, L=8, E=4, top_k=2, expert_hidden=6,
+                       shared_hidden=5, alpha=2.0, dtype="bf16", seed=10),
+    "tiny": dg.Workload("tiny1", B=5, T=4, H=4, D=32, L=1, hidden_mix=64, hidden_rev=64,
+                        dtype="f32", seed=0),
+}
+
+
+@pytest.mark.parametrize("name,mult", [("dense", 2.0), ("moe", 8.0), ("tiny", 1.0)])
+def test_zero_down_makes_every_block_identity(name, mult):
+    # Every F = 0 => Z_l = Y_{l-1}; inter-residuals double the stream at
+    # l = 2, 4, 6 (< L): Y_L = 2^{#inter} X bit-exactly (L=1: X, 4: 2X, 8: 8X)
+    cfg = SMALL[name]
+    X = dg.make_x(cfg).astype(np.float64)
+    Y = orc.stack_forward(X, cfg, _zero_down(dg.WeightSource(cfg)))
+    np.testing.assert_array_equal(Y, mult * X)
+
+
+@pytest.mark.parametrize("name,mult", [("dense", 2.0), ("moe", 8.0)])
+def test_revert_residual_goes_to_block_input(name, mult):
+    # Mix sub-layer active, revert sub-layer F = 0: with the residual to the
+    # block input X (TML Eq. 16) every block is exactly the identity. The
+    # other reading (residual to X_rev) would leak the mix sub-layer's F.
+    cfg = SMALL[name]
+    X = dg.make_x(cfg).astype(np.float64)
+    Y = orc.stack_forward(X, cfg, _zero_down(dg.WeightSource(cfg), subs=(1,)))
+    np.testing.assert_array_equal(Y, mult * X)
+
+
+def test_single_token_single_head_reduces_to_nested_prenorm_mlp():
+    # T = H = 1: Mix and Revert are the identity, so one block is
+    # X + F_rev(N(X + F_mix(N(X)))) -- written here with a plain einsum
+    # formulation of SwiGLU.
+    cfg = dg.Workload("t1", B=7, T=1, H=1, D=6, L=1, hidden_mix=5, hidden_rev=4, dtype="f32", seed=12)
+    ws = dg.WeightSource(cfg)
+    X = dg.make_x(cfg).astype(np.float64)
+
+    def f(v, sub):
+        Wu, Wg, Wd = (ws(1, sub, k, 0).astype(np.float64) for k in (dg.K_UP, dg.K_GATE, dg.K_DOWN))
+        n = v / np.sqrt(np.mean(v ** 2, -1, keepdims=True) + cfg.eps)
+        g = np.einsum("bi,ij->bj", n, Wg)
+        u = np.einsum("bi,ij->bj", n, Wu)
+        return np.einsum("bj,jk->bk", g / (1 + np.exp(-g)) * u, Wd)
+
+    x = X[:, 0]
+    h1 = x + f(x, 0)
+    want = x + f(h1, 1)
+    Y = orc.stack_forward(X, cfg, ws)
+    np.testing.assert_allclose(Y[:, 0], want, rtol=1e-13, atol=1e-15)
+
+
+def test_which_elements_change_follows_revert_map():
+    # Only mixed position h* has a non-zero down bank: after the mix
+    # sub-layer and Revert, only columns h*·dh..(h*+1)·dh of every token may
+    # differ from the block input (TML Eq. 13-15).
+    cfg = dg.Workload("wc", B=4, T=4, H=2, D=8, L=1, hidden_mix=6, hidden_rev=6, dtype="f32", seed=13)
+    ws = dg.WeightSource(cfg)
+    hstar, dh = 1, cfg.D // cfg.H
+
+    def g(layer, sub, kind, p):
+        w = ws(layer, sub, kind, p)
+        return np.zeros_like(w) if (kind == dg.K_DOWN and p != hstar) else w
+
+    X = dg.make_x(cfg).astype(np.float64)
+    Hm = orc.mix(X, cfg.H)
+    Hn = orc.sublayer_positions(Hm, Hm, cfg, 1, 0, g)
+    Xr = orc.revert(Hn, cfg.T)
+    changed = np.any(Xr != X, axis=(0, 1))
+    assert changed[hstar * dh:(hstar + 1) * dh].all()
+    assert not changed[:hstar * dh].any() and not changed[(hstar + 1) * dh:].any()
+
+
+def test_inter_residual_positions():
+    # With the revert F = 0 but a marker added through "extra", the
+    # inter-residual must enter at l = 2, 4, 6 only (gap 2, never at l = L).
+    cfg = SMALL["moe"].with_(L=6, gap=2)
+    X = dg.make_x(cfg).astype(np.float64)
+    Y = orc.stack_forward(X, cfg, _zero_down(dg.WeightSource(cfg)))
+    np.testing.assert_array_equal(Y, 4.0 * X)            # l=2: 2X, l=4: 4X, l=6 = L: none
+    cfg3 = SMALL["dense"].with_(L=6, gap=3)
+    Y3 = orc.stack_forward(dg.make_x(cfg3).astype(np.float64), cfg3,
+                           _zero_down(dg.WeightSource(cfg3)))
+    np.testing.assert_array_equal(Y3, 2.0 * dg.make_x(cfg3))   # l=3 only
+    cfg0 = SMALL["dense"].with_(gap=0)
+    Y0 = orc.stack_forward(dg.make_x(cfg0).astype(np.float64), cfg0, _zero_down(dg.WeightSource(cfg0)))
+    np.testing.assert_array_equal(Y0, dg.make_x(cfg0))
+
+
+@pytest.mark.parametrize("name", ["dense", "moe"])
+def test_samples_are_independent(name):
+    cfg = SMALL[name]
+    ws = dg.WeightSource(cfg)
+    X = dg.make_x(cfg).astype(np.float64)
+    Y = orc.stack_forward(X, cfg, ws)
+    sub = [4, 1]
+    np.testing.assert_array_equal(orc.stack_forward(X[sub], cfg, ws), Y[sub])
+
+
+def test_bf16_mode_outputs_are_bf16_values():
+    cfg = SMALL["moe"]
+    Y = orc.stack_forward(dg.make_x(cfg).astype(np.float64), cfg, dg.WeightSource(cfg))
+    np.testing.assert_array_equal(orc.round_bf16(Y), Y)
+
+
+def test_bf16_and_fp64_modes_agree_to_bf16_precision():
+    cfg = SMALL["dense"]
+    ws = dg.WeightSource(cfg)
+    X = dg.make_x(cfg).astype(np.float64)
+    a = orc.stack_forward(X, cfg, ws, rho=True)
+    b = orc.stack_forward(X, cfg, ws, rho=False)
+    err = np.max(np.abs(a - b), axis=-1) / np.max(np.abs(b), axis=-1)
+    assert err.max() < 2e-2 and err.max() > 0
+
+
+# ---------------------------------------------------------------------------
+# closed forms of the work (RMX-BOOK 7.4.2; TML 3.4 scale)
+# ---------------------------------------------------------------------------
+
+def test_param_counts():
+    for i, cfg in dg.WORKLOADS.items():
+        assert orc.param_count_closed_form(cfg) == dg.param_count(cfg)
+    assert orc.param_count_closed_form(dg.WORKLOADS[5]) == 15_414_067_200   # the ~15B model
+    assert 15e9 <= orc.param_count_closed_form(dg.WORKLOADS[5]) < 16e9
+    assert orc.param_count_closed_form(dg.WORKLOADS[4]) == 1_814_036_480
+    assert orc.param_count_closed_form(dg.WORKLOADS[2]) == 100_663_296
+    assert orc.param_count_closed_form(dg.WORKLOADS[3]) == 100_663_296
+
+
+def test_flops_equal_params_for_dense_pertoken():
+    # Per-token FFN: Param = FLOPs (in multiply-adds) per sample (RMX-BOOK 7.4.2)
+    for i in (1, 2, 3):
+        cfg = dg.WORKLOADS[i]
+        assert orc.flops_per_sample(cfg) == 2 * orc.param_count_closed_form(cfg)
+    assert orc.flops_per_sample(dg.WORKLOADS[2]) == 201_326_592
+    assert orc.flops_per_sample(dg.WORKLOADS[4]) == 1_212_153_856
+    assert orc.flops_per_sample(dg.WORKLOADS[5]) == 5_460_983_808
