@@ -1,0 +1,175 @@
+#!/usr/bin/env python3
+"""Throughput of the TokenMixer-Large block-stack forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload N] [--no-cpu-baseline]
+
+A step is one tmx_block_stack_forward over one batch of the workload (all
+blocks, both sub-layers, inter-residuals) with inputs and weights already
+resident in HBM. Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-stack forward samples/s + TFLOP/s (% bf16 MFMA peak), 1×MI355X"
+BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def time_launches(fn, reps, stream):
+    """Average duration (ms) of `fn()` launches with HIP events on `stream`."""
+    import torch
+    fn()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def cpu_baseline(wl, banks, x, budget_s):
+    """The oracle as it stands, on a bounded sample of the same workload."""
+    import datagen as dg
+    import oracle as orc
+    ws = dg.WeightSource(wl, banks)
+    probe = 4
+    t0 = time.perf_counter()
+    orc.stack_forward(x[:probe].astype(np.float64), wl, ws)
+    tp = time.perf_counter() - t0
+    n = int(max(probe, min(wl.B, probe * budget_s / max(tp, 1e-3))))
+    t0 = time.perf_counter()
+    orc.stack_forward(x[:n].astype(np.float64), wl, ws)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    return {"value": n / dt, "unit": "samples/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {wl.B} samples of the same workload, full {wl.L}-block stack "
+                      f"in fp64 numpy ({dt:.1f} s)"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, help="workload id 1..5 (default 2)")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build runs the block stack on a single "
+              "MI355X (samples shard over GPUs with replicated weights; see DESIGN.md).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import datagen as dg
+    from token_moe_amd import runner, tmx
+    import oracle as orc
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    tmx.load_library()
+    wl = dg.WORKLOADS[args.workload]
+    log("workload", wl)
+    t0 = time.perf_counter()
+    banks = dg.weight_banks(wl)
+    x = dg.make_x(wl)
+    log(f"generated inputs in {time.perf_counter() - t0:.1f} s")
+    ctx = runner.make_context(wl, banks)
+    xd = runner.host_tensor(wl, x).cuda()
+    yd = torch.empty_like(xd)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    log("weights resident; warming up")
+
+    for _ in range(args.warmup):
+        ctx.block_stack_forward(xd, yd, wl.B, sp)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        ctx.block_stack_forward(xd, yd, wl.B, sp)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    flops = orc.flops_per_sample(wl) * wl.B
+    samples_s = wl.B / (ms / 1e3)
+    tflops = flops / (ms / 1e3) / 1e12
+    log(f"{ms:.3f} ms/step, {samples_s:.0f} samples/s, {tflops:.1f} TFLOP/s")
+    if not np.all(np.isfinite(yd[:64].float().cpu().numpy())):
+        raise RuntimeError("non-finite output")
+
+    # dominant kernel: the fused per-position SwiGLU MLP. For a dense workload
+    # one sub-layer call is exactly one launch of it.
+    roofline = None
+    kernel = {}
+    if not wl.moe:
+        xr = torch.empty_like(xd)
+        per = []
+        for sub in (0, 1):
+            P, W, h = wl.positions(sub), wl.width(sub), wl.hidden(sub)
+            if sub == 0:
+                fn = lambda: ctx.sublayer_forward(0, 0, xd, None, None, xr, wl.B, sp)
+            else:
+                fn = lambda: ctx.sublayer_forward(0, 1, xr, xd, None, yd, wl.B, sp)
+            kms = time_launches(fn, args.kernel_reps, stream)
+            kfl = 2.0 * wl.B * P * 3 * W * h
+            per.append((kms, kfl))
+            kernel[f"mlp_{'mix' if sub == 0 else 'revert'}_ms"] = round(kms, 5)
+        kms = sum(p[0] for p in per) / len(per)
+        kfl = sum(p[1] for p in per) / len(per)
+        achieved = kfl / (kms / 1e3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                    "traffic": None, "kernel": f"mlp_kernel<{wl.width(1)}, DENSE>",
+                    "flop_per_launch": kfl, "launch_ms": round(kms, 5)}
+        log(f"fused MLP kernel: {kms:.4f} ms/launch, {achieved:.1f} TFLOP/s")
+
+    out = {
+        "metric": METRIC, "value": round(samples_s, 1), "unit": "samples/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32", "data": "synthetic",
+        "tflops": round(tflops, 2), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "D": wl.D, "L": wl.L,
+                   "hidden": [wl.hidden_mix, wl.hidden_rev], "E": wl.E, "top_k": wl.top_k,
+                   "expert_hidden": wl.expert_hidden, "shared_hidden": wl.shared_hidden,
+                   "flop_per_step": flops},
+        "roofline": roofline,
+    }
+    out.update(kernel)
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(wl, banks, x, args.cpu_seconds)
+    ctx.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -23,7 +23,6 @@ from __future__ import annotations
 
 import dataclasses
 import os
-from concurrent.futures import ProcessPoolExecutor
 from typing import Dict, Optional, Tuple
 
 import numpy as np
@@ -173,6 +172,18 @@ def to_bf16_values(a: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).to(torch.float32).numpy()
 
 
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Bit patterns of the nearest bf16 values (ties to even) of finite fp32
+    data: input quantisation for bulk generation (a CPU test checks it equals
+    torch's fp32 -> bf16 conversion)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    return ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
+    return (np.asarray(u, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
 def _finish(cfg: Workload, a: np.ndarray) -> np.ndarray:
     return to_bf16_values(a) if cfg.dtype == "bf16" else a
 
@@ -185,46 +196,32 @@ def make_x(cfg: Workload, seed: Optional[int] = None, B: Optional[int] = None) -
     return _finish(cfg, a)
 
 
-def weight_slice(cfg: Workload, layer: int, sub: int, kind: int, p: int,
-                 seed: Optional[int] = None) -> np.ndarray:
-    """One position's slice of a weight bank (fp32 array, dtype-representable)."""
+def _draw(cfg: Workload, layer: int, sub: int, kind: int, p: int, seed: Optional[int]) -> np.ndarray:
+    """Unrounded fp32 draw of one position's slice: N(0, 1/fan_in), downs x0.01."""
     shape = cfg.kind_shape(sub, kind)
-    if kind == K_NORM_GAIN:
-        return np.ones(shape, np.float32)
     s = cfg.seed if seed is None else seed
     a = _rng(s, (1, layer, sub, kind, p)).standard_normal(shape[1:], dtype=np.float32)
     std = np.float32(1.0 / np.sqrt(cfg.fan_in(sub, kind)))
     if kind in (K_DOWN, K_EXP_DOWN, K_SH_DOWN):
         std = np.float32(std * cfg.down_scale)
-    return _finish(cfg, a * std)
+    a *= std
+    return a
+
+
+def weight_slice(cfg: Workload, layer: int, sub: int, kind: int, p: int,
+                 seed: Optional[int] = None) -> np.ndarray:
+    """One position's slice of a weight bank (fp32 array, dtype-representable)."""
+    if kind == K_NORM_GAIN:
+        return np.ones(cfg.kind_shape(sub, kind), np.float32)
+    return _finish(cfg, _draw(cfg, layer, sub, kind, p, seed))
 
 
 def weight_bank(cfg: Workload, layer: int, sub: int, kind: int,
                 seed: Optional[int] = None) -> np.ndarray:
-    """A whole (layer, sub-layer, kind) bank, all positions stacked."""
+    """A whole (layer, sub-layer, kind) bank, all positions stacked (fp32 values)."""
     if kind == K_NORM_GAIN:
         return weight_slice(cfg, layer, sub, kind, 0, seed)
-    P = cfg.positions(sub)
-    return np.stack([weight_slice(cfg, layer, sub, kind, p, seed) for p in range(P)])
-
-
-def _bank_job(args):
-    cfg, layer, sub, kind, seed = args
-    return (layer, sub, kind), weight_bank(cfg, layer, sub, kind, seed)
-
-
-def all_weights(cfg: Workload, seed: Optional[int] = None, workers: int = 0):
-    """{(layer, sub, kind): bank} for every bank of the stack (layers 1..L).
-
-    ``workers`` > 1 generates banks in a process pool (same values: every
-    slice has its own seed key).
-    """
-    jobs = [(cfg, l, s, k, seed) for l in range(1, cfg.L + 1) for s in (SUB_MIX, SUB_REVERT)
-            for k in cfg.kinds()]
-    if workers and workers > 1:
-        with ProcessPoolExecutor(max_workers=workers) as ex:
-            return dict(ex.map(_bank_job, jobs))
-    return dict(_bank_job(j) for j in jobs)
+    return np.stack([weight_slice(cfg, layer, sub, kind, p, seed) for p in range(cfg.positions(sub))])
 
 
 def default_workers() -> int:
@@ -233,6 +230,40 @@ def default_workers() -> int:
     except AttributeError:  # pragma: no cover
         n = os.cpu_count() or 1
     return max(1, min(16, n))
+
+
+def weight_banks(cfg: Workload, seed: Optional[int] = None, workers: int = 0):
+    """{(layer 1..L, sub, kind): bank} for every matrix bank of the stack.
+
+    bf16 workloads give uint16 arrays of bf16 bit patterns, fp32 workloads
+    float32 arrays. Slices are drawn in a thread pool (the generator releases
+    the GIL); every slice has its own seed key, so the values do not depend
+    on ``workers``."""
+    from concurrent.futures import ThreadPoolExecutor
+    bf16 = cfg.dtype == "bf16"
+    banks = {}
+    jobs = []
+    for l in range(1, cfg.L + 1):
+        for s in (SUB_MIX, SUB_REVERT):
+            for k in cfg.kinds():
+                shape = cfg.kind_shape(s, k)
+                arr = np.empty(shape, np.uint16 if bf16 else np.float32)
+                banks[(l, s, k)] = arr
+                jobs.extend((arr, l, s, k, p) for p in range(shape[0]))
+
+    def run(job):
+        arr, l, s, k, p = job
+        a = _draw(cfg, l, s, k, p, seed)
+        arr[p] = f32_to_bf16_bits(a) if bf16 else a
+
+    n = workers or default_workers()
+    if n > 1:
+        with ThreadPoolExecutor(max_workers=n) as ex:
+            list(ex.map(run, jobs))
+    else:
+        for j in jobs:
+            run(j)
+    return banks
 
 
 def param_count(cfg: Workload) -> int:
@@ -245,8 +276,8 @@ def param_count(cfg: Workload) -> int:
 
 
 class WeightSource:
-    """Lazy (layer, sub, kind, position) -> fp32 slice, with an optional cache
-    of whole banks (e.g. banks already generated for a GPU upload)."""
+    """Lazy (layer 1..L, sub, kind, position) -> fp32 slice. With ``banks``
+    (from :func:`weight_banks`) slices are decoded from them, else drawn."""
 
     def __init__(self, cfg: Workload, banks=None, seed: Optional[int] = None):
         self.cfg = cfg
@@ -254,7 +285,9 @@ class WeightSource:
         self.seed = seed
 
     def __call__(self, layer: int, sub: int, kind: int, p: int) -> np.ndarray:
+        if kind == K_NORM_GAIN:
+            return weight_slice(self.cfg, layer, sub, kind, p, self.seed)
         if self.banks is not None and (layer, sub, kind) in self.banks:
-            b = self.banks[(layer, sub, kind)]
-            return b if kind == K_NORM_GAIN else b[p]
+            b = self.banks[(layer, sub, kind)][p]
+            return bf16_bits_to_f32(b) if b.dtype == np.uint16 else b
         return weight_slice(self.cfg, layer, sub, kind, p, self.seed)

@@ -1,0 +1,167 @@
+/*
+ * tmx.h -- C ABI of the MI355X (gfx950) TokenMixer-Large block-stack forward.
+ *
+ * The library computes the forward pass of the block stack described in
+ * "TokenMixer-Large: Scaling Up Large Ranking Models in Industrial
+ * Recommenders" (paper summary, sections 2.3-2.4, Eq. 9-21) and in the
+ * tokenmixerlarge README's block diagram (Pre-Norm form):
+ *
+ *   for l = 1..L:   Hm     = Mix(Y_{l-1})                          (Eq. 9-11)
+ *                   H_next = Hm + F_mix(RMSNorm(Hm))               (Eq. 12, Pre-Norm)
+ *                   X_rev  = Revert(H_next)                        (Eq. 13-15)
+ *                   Z_l    = Y_{l-1} + F_rev(RMSNorm(X_rev))       (Eq. 16, Pre-Norm)
+ *                   Y_l    = Z_l + Y_{l-g} if g > 0, l % g == 0, l < L   (section 2.3.4)
+ *
+ * where every position p of a sub-layer owns its weights: F_p is a
+ * per-token SwiGLU (Eq. 17-18) or a Sparse-Pertoken MoE (Eq. 19-21: top-k
+ * softmax routing, gates alpha * pi, plus an always-on per-token shared
+ * expert).  Mix sub-layer: P = H positions of width W = T*D/H.  Revert
+ * sub-layer: P = T positions of width W = D.
+ *
+ * Conventions for every entry point:
+ *  - Plain pointers and sizes only.  Tensors are dense row-major.
+ *  - "device" pointers are HIP device allocations on the context's device;
+ *    the caller owns them and the library never frees them.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Compute entry
+ *    points only enqueue work (no host synchronisation, no host copies) and
+ *    return before it has run; launch errors are reported as TMX_ERR_DEVICE.
+ *  - All argument validation happens before anything is enqueued.  On any
+ *    non-TMX_OK status nothing was enqueued and tmx_last_error() describes
+ *    the failure.
+ *  - A context is used by one host thread at a time.
+ *  - Layers are numbered 0..L-1 (layer l here is the pages' block l+1).
+ */
+#ifndef TMX_H
+#define TMX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tmx_status {
+  TMX_OK = 0,
+  TMX_ERR_INVALID_ARG = 1, /* bad shape, index, pointer or size */
+  TMX_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+  TMX_ERR_OOM = 3,         /* device allocation failed */
+  TMX_ERR_DEVICE = 4,      /* a HIP runtime call or kernel launch failed */
+  TMX_ERR_STATE = 5        /* e.g. forward before every weight was loaded */
+} tmx_status;
+
+typedef enum tmx_dtype { TMX_F32 = 0, TMX_BF16 = 1 } tmx_dtype;
+
+typedef enum tmx_sublayer { TMX_MIX = 0, TMX_REVERT = 1 } tmx_sublayer;
+
+/* Weight kinds and their logical row-major layouts, with P and W of the
+ * sub-layer (MIX: P = H, W = T*D/H; REVERT: P = T, W = D), h the dense
+ * hidden of that sub-layer, E routed experts, h_e expert hidden, h_s
+ * shared-expert hidden.  Row-vector convention y = x @ W (the RankMixer
+ * reproduction guide's per-token banks W1 [T, D, kD], W2 [T, kD, D]). */
+typedef enum tmx_weight_kind {
+  TMX_W_NORM_GAIN = 0, /* [W]          RMSNorm gain, optional (default 1)  */
+  TMX_W_UP = 1,        /* [P, W, h]    dense SwiGLU up       (Eq. 17-18)   */
+  TMX_W_GATE = 2,      /* [P, W, h]    dense SwiGLU gate                   */
+  TMX_W_DOWN = 3,      /* [P, h, W]    dense SwiGLU down                   */
+  TMX_W_ROUTER = 4,    /* [P, W, E]    router, logits = x_hat @ Wr (Eq. 19) */
+  TMX_W_EXP_UP = 5,    /* [P, E, W, h_e] routed experts (Eq. 19)           */
+  TMX_W_EXP_GATE = 6,  /* [P, E, W, h_e]                                   */
+  TMX_W_EXP_DOWN = 7,  /* [P, E, h_e, W]                                   */
+  TMX_W_SH_UP = 8,     /* [P, W, h_s]  per-token shared expert (Eq. 20)    */
+  TMX_W_SH_GATE = 9,   /* [P, W, h_s]                                      */
+  TMX_W_SH_DOWN = 10   /* [P, h_s, W]                                      */
+} tmx_weight_kind;
+
+/* Model configuration; the pages' problem statement (B, T, H, D, hidden, E,
+ * top_k, L) plus the numerical knobs.  E = 0 selects the dense per-token
+ * SwiGLU block; E > 0 the Sparse-Pertoken MoE in both sub-layers. */
+typedef struct tmx_config {
+  int32_t B_max;          /* largest batch a forward call may pass (>= 1)     */
+  int32_t T;              /* tokens per sample (>= 1)                          */
+  int32_t H;              /* heads / mixed tokens; D % H == 0 (RankMixer guide
+                             section 5)                                        */
+  int32_t D;              /* token width                                       */
+  int32_t L;              /* number of blocks (>= 1)                           */
+  int32_t hidden_mix;     /* dense: per-position hidden of the MIX sub-layer   */
+  int32_t hidden_rev;     /* dense: per-position hidden of the REVERT sub-layer*/
+  int32_t E;              /* routed experts per position (0 = dense)           */
+  int32_t top_k;          /* experts chosen per row, 1 <= top_k <= E           */
+  int32_t expert_hidden;  /* h_e                                               */
+  int32_t shared_hidden;  /* h_s                                               */
+  float alpha;            /* gate-value scaling (Eq. 21); 0 means E / top_k    */
+  float eps;              /* RMSNorm epsilon (> 0)                             */
+  int32_t inter_residual_gap; /* g (section 2.3.4); 0 disables               */
+  int32_t dtype;          /* tmx_dtype of activations and weights              */
+} tmx_config;
+
+typedef struct tmx_ctx tmx_ctx;
+
+/* Validate `cfg`, select `device` (hipSetDevice) and allocate the context:
+ * weight storage for all L blocks and a workspace sized for B_max.
+ * bf16 contexts additionally need D/H % 8 == 0, every sub-layer width W a
+ * multiple of 64 and every hidden size a multiple of 64; MoE contexts in
+ * bf16 need E % 16 == 0 and top_k <= 8 (TMX_ERR_UNSUPPORTED otherwise).
+ * On error *out is set to NULL and nothing stays allocated. */
+tmx_status tmx_create(const tmx_config* cfg, int device, tmx_ctx** out);
+
+/* Free everything the context owns (device memory, streams are the
+ * caller's).  NULL is a no-op. */
+tmx_status tmx_destroy(tmx_ctx* ctx);
+
+/* Human-readable description of the last failure: of `ctx`, or of the
+ * calling thread's last failed tmx_create when ctx is NULL.  The string is
+ * owned by the library and valid until the next call on the same ctx. */
+const char* tmx_last_error(const tmx_ctx* ctx);
+
+/* Copy one weight bank (kind, layout as above, element type = ctx dtype)
+ * of block `layer` (0..L-1), sub-layer `sublayer` (TMX_MIX / TMX_REVERT)
+ * into the context and repack it into the kernels' fragment layout.
+ * `src` is a host or device pointer (detected with hipPointerGetAttributes);
+ * the call copies and the caller keeps ownership.  `nbytes` must equal the
+ * bank's exact size.  Dense contexts accept NORM_GAIN, UP, GATE, DOWN; MoE
+ * contexts NORM_GAIN, ROUTER and the EXP_* / SH_* kinds.  The call is
+ * synchronous (it waits for `stream`); it is not meant for timed loops. */
+tmx_status tmx_load_weights(tmx_ctx* ctx, int layer, int sublayer, int kind,
+                            const void* src, size_t nbytes, void* stream);
+
+/* Y_L = block stack applied to x_in.  x_in, x_out: device, [B, T, D]
+ * row-major, ctx dtype, 16-byte aligned, not overlapping; 1 <= B <= B_max.
+ * TMX_ERR_STATE if any required weight bank was never loaded. */
+tmx_status tmx_block_stack_forward(tmx_ctx* ctx, const void* x_in, void* x_out,
+                                   int B, void* stream);
+
+/* The router of one MoE sub-layer (Eq. 19-21): x is that sub-layer's input
+ * in block layout [B, T, D] (for TMX_MIX the Mix map is applied inside),
+ * rows are normalised with the sub-layer's RMSNorm and rounded to the ctx
+ * dtype, logits = x_hat @ Wr_p, pi = softmax over all E, and the top_k
+ * experts under the key (-logit, expert index) are written in that order:
+ * idx [B, P, top_k] int32 and gate [B, P, top_k] float32 = alpha * pi
+ * (device pointers).  TMX_ERR_UNSUPPORTED on a dense context. */
+tmx_status tmx_moe_route(tmx_ctx* ctx, int layer, int sublayer, const void* x,
+                         int B, int32_t* idx, float* gate, void* stream);
+
+/* One sub-layer, for teacher-forced checks; runs the same kernels as the
+ * forward.  All tensors are [B, T, D] in block layout (device).
+ *   TMX_MIX:    x_out = Revert(Mix(x_in) + F_mix(RMSNorm(Mix(x_in))));
+ *               `resid` and `extra` must be NULL.
+ *   TMX_REVERT: x_out = resid + F_rev(RMSNorm(x_in)) [+ extra];
+ *               `resid` is the block input, `extra` (nullable) the
+ *               inter-residual term.
+ * The result is rounded once to the ctx dtype.  A chain of these calls
+ * reproduces tmx_block_stack_forward bit for bit. */
+tmx_status tmx_sublayer_forward(tmx_ctx* ctx, int layer, int sublayer,
+                                const void* x_in, const void* resid,
+                                const void* extra, void* x_out, int B,
+                                void* stream);
+
+/* Apply Mix (inverse = 0: out [B, H, T*D/H]) or Revert (inverse = 1:
+ * in [B, H, T*D/H] -> out [B, T, D]) with the same device index code the
+ * sub-layer kernels use; bit-exact data movement (Eq. 9-11, 13-15). */
+tmx_status tmx_debug_permute(tmx_ctx* ctx, const void* in, void* out, int B,
+                             int inverse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TMX_H */

@@ -1,0 +1,230 @@
+"""Sparse-Pertoken MoE path on the GPU (router, bucket, grouped experts,
+shared expert + combine) vs the fp64 oracle."""
+import numpy as np
+import pytest
+
+import datagen as dg
+import oracle as orc
+from gpu_common import (TOL, context, drop, oracle_sublayer, require_gpu, row_err, sample_rows,
+                        say, stream, to_dev, to_np)
+
+pytestmark = pytest.mark.gpu
+
+# small MoE stack: ragged batch, W = 128 in both sub-layers
+SMALL_MOE = dg.Workload("small_moe_bf16", B=300, T=4, H=4, D=128, L=3, E=16, top_k=4,
+                        expert_hidden=64, shared_hidden=128, alpha=4.0, gap=2, seed=31)
+SMALL_MOE_F32 = SMALL_MOE.with_(name="small_moe_f32", dtype="f32", B=64, D=32, E=6, top_k=2,
+                                expert_hidden=16, shared_hidden=24, alpha=3.0, seed=32)
+
+DELTA = {"bf16": 1e-3, "f32": 1e-5}
+
+
+def _route_gpu(ctx, wl, layer, sub, xd, B):
+    import torch
+    P = wl.positions(sub)
+    idx = torch.empty((B, P, wl.top_k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((B, P, wl.top_k), dtype=torch.float32, device="cuda")
+    ctx.moe_route(layer, sub, xd, B, idx, gate, stream())
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), gate.cpu().numpy().astype(np.float64)
+
+
+def _route_oracle(wl, ws, layer1, sub, x_rows):
+    """Oracle routing of rows x_rows [n, T, D] (block layout)."""
+    rho = wl.dtype == "bf16"
+    v = orc.mix(x_rows, wl.H) if sub == 0 else x_rows
+    n, P, W = v.shape
+    out = []
+    for p in range(P):
+        xh = orc.rmsnorm(v[:, p], ws(layer1, sub, dg.K_NORM_GAIN, 0), wl.eps)
+        if rho:
+            xh = orc.round_bf16(xh)
+        out.append(orc.route(xh, ws(layer1, sub, dg.K_ROUTER, p), wl.top_k, wl.gate_scale))
+    idx = np.stack([o[0] for o in out], 1)
+    gate = np.stack([o[1] for o in out], 1)
+    logits = np.stack([o[2] for o in out], 1)
+    return idx, gate, logits
+
+
+def _check_routing(wl, idx_g, gate_g, idx_o, gate_o, logits):
+    """Exact on rows whose k-th/(k+1)-th logit margin exceeds delta; the rest
+    must be delta-valid. Returns the number of banded rows."""
+    d = DELTA[wl.dtype]
+    k, E = wl.top_k, logits.shape[-1]
+    srt = -np.sort(-logits, axis=-1)
+    kth = srt[..., k - 1]
+    margin = kth - (srt[..., k] if k < E else -np.inf)
+    clear = margin > d
+    assert np.array_equal(idx_g[clear], idx_o[clear])
+    np.testing.assert_allclose(gate_g[clear], gate_o[clear], rtol=1e-5, atol=0)
+    band = np.argwhere(~clear)
+    for pos in band:
+        r = tuple(pos)
+        chosen = set(idx_g[r].tolist())
+        assert len(chosen) == k
+        l = logits[r]
+        for e in range(E):
+            if e in chosen:
+                assert l[e] >= kth[r] - d
+            else:
+                assert l[e] <= kth[r] + d
+    return len(band)
+
+
+@pytest.mark.parametrize("which", ["small_bf16", "small_f32"])
+def test_small_moe_stack_all_rows(which):
+    require_gpu()
+    wl = SMALL_MOE if which == "small_bf16" else SMALL_MOE_F32
+    say("small moe stack", wl)
+    ctx, banks, ws = context(which, wl)
+    import torch
+    x = dg.make_x(wl)
+    xd = to_dev(wl, x)
+    y = torch.empty_like(xd)
+    ctx.block_stack_forward(xd, y, wl.B, stream())
+    torch.cuda.synchronize()
+    ref = orc.stack_forward(x.astype(np.float64), wl, ws)
+    err = row_err(to_np(y), ref)
+    say("small moe err", which, err)
+    assert err <= TOL[wl.dtype]
+    y2 = torch.empty_like(xd)
+    ctx.block_stack_forward(xd, y2, wl.B, stream())
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("which", ["small_bf16", "small_f32", "w4"])
+@pytest.mark.parametrize("sub", [0, 1])
+def test_route_matches_oracle(which, sub):
+    require_gpu()
+    wl = {"small_bf16": SMALL_MOE, "small_f32": SMALL_MOE_F32, "w4": dg.WORKLOADS[4]}[which]
+    say("route", which, sub)
+    ctx, banks, ws = context(which, wl)
+    x = dg.make_x(wl)
+    idx_g, gate_g = _route_gpu(ctx, wl, 0, sub, to_dev(wl, x), wl.B)
+    rows = sample_rows(wl.B, 512, seed=sub) if wl.B > 512 else np.arange(wl.B)
+    idx_o, gate_o, logits = _route_oracle(wl, ws, 1, sub, x[rows].astype(np.float64))
+    nb = _check_routing(wl, idx_g[rows], gate_g[rows], idx_o, gate_o, logits)
+    say("route banded rows", which, sub, nb, "of", idx_o.shape[0] * idx_o.shape[1])
+    # every row's selection is k distinct experts
+    s = np.sort(idx_g, axis=-1)
+    assert np.all(s[..., 1:] != s[..., :-1]) and s.min() >= 0 and s.max() < wl.E
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_route_exact_ties_lowest_index(dtype):
+    """Dyadic router weights, +-1 inputs and duplicated router columns: every
+    logit is exact, ties are exact, and the lowest index must win."""
+    require_gpu()
+    import torch
+    from token_moe_amd import runner
+    wl = SMALL_MOE.with_(name="ties", L=1, B=256) if dtype == "bf16" else SMALL_MOE_F32.with_(name="ties32", L=1)
+    banks = dg.weight_banks(wl)
+    rng = np.random.default_rng(5)
+    for sub in (0, 1):
+        P, W, E = wl.positions(sub), wl.width(sub), wl.E
+        half = rng.integers(-64, 65, (P, W, E // 2)).astype(np.float32) / np.float32(64.0)
+        wr = np.concatenate([half, half], axis=-1)           # expert e and e + E/2 tie exactly
+        banks[(1, sub, dg.K_ROUTER)] = dg.f32_to_bf16_bits(wr) if dtype == "bf16" else wr
+    ctx = runner.make_context(wl, banks)
+    ws = dg.WeightSource(wl, banks)
+    x = np.where(rng.random((wl.B, wl.T, wl.D)) < 0.5, -1.0, 1.0).astype(np.float32)
+    for sub in (0, 1):
+        idx_g, gate_g = _route_gpu(ctx, wl, 0, sub, to_dev(wl, x), wl.B)
+        idx_o, gate_o, logits = _route_oracle(wl, ws, 1, sub, x.astype(np.float64))
+        if dtype == "bf16":
+            # x_hat = +-1 exactly, logits are exact dyadic sums: routing must match bit for bit
+            np.testing.assert_array_equal(idx_g, idx_o)
+        else:
+            # fp32 x_hat = +-(1+eps)^-1/2 is inexact, but tied columns stay tied
+            half = wl.E // 2
+            lo = idx_g % half
+            for r in np.ndindex(idx_g.shape[:2]):
+                for s in range(wl.top_k):
+                    e = idx_g[r][s]
+                    if e >= half:   # an upper copy may only be taken after its lower twin
+                        assert e - half in idx_g[r][:s].tolist()
+        np.testing.assert_allclose(gate_g, gate_o, rtol=1e-5)
+    ctx.close()
+
+
+@pytest.mark.parametrize("sub", [0, 1])
+def test_skewed_routing_and_empty_buckets(sub):
+    """Positive inputs, positive router columns except expert 5 (all
+    negative): expert 5's bucket is always empty, and expert 3 (column x10)
+    is chosen by every row, so its bucket holds all B rows (several tiles)."""
+    require_gpu()
+    import torch
+    from token_moe_amd import runner
+    wl = SMALL_MOE.with_(name="skew", L=1)
+    banks = dg.weight_banks(wl)
+    for s in (0, 1):
+        wr = np.abs(dg.bf16_bits_to_f32(banks[(1, s, dg.K_ROUTER)]))
+        wr[..., 3] *= 10.0
+        wr[..., 5] = -wr[..., 5]
+        banks[(1, s, dg.K_ROUTER)] = dg.f32_to_bf16_bits(wr)
+    ctx = runner.make_context(wl, banks)
+    ws = dg.WeightSource(wl, banks)
+    x = np.abs(dg.make_x(wl))
+    resid = dg.make_x(wl, seed=77)
+    xd, rd = to_dev(wl, x), to_dev(wl, resid)
+    idx_g, _ = _route_gpu(ctx, wl, 0, sub, xd, wl.B)
+    assert not np.any(idx_g == 5)
+    assert np.all(idx_g[..., 0] == 3)
+    out = torch.empty_like(xd)
+    if sub == 0:
+        ctx.sublayer_forward(0, 0, xd, None, None, out, wl.B, stream())
+        torch.cuda.synchronize()
+        ref = oracle_sublayer(wl, ws, 1, 0, x.astype(np.float64))
+    else:
+        ctx.sublayer_forward(0, 1, xd, rd, None, out, wl.B, stream())
+        torch.cuda.synchronize()
+        ref = oracle_sublayer(wl, ws, 1, 1, x.astype(np.float64), resid.astype(np.float64))
+    err = row_err(to_np(out), ref)
+    say("skewed err", sub, err)
+    assert err <= TOL["bf16"]
+    ctx.close()
+
+
+@pytest.mark.parametrize("sub", [0, 1])
+def test_moe_sublayer_teacher_forced_full_batch(sub):
+    require_gpu()
+    import torch
+    wl = dg.WORKLOADS[4]
+    say("moe sublayer cfg4", sub)
+    ctx, banks, ws = context("w4", wl)
+    x = dg.make_x(wl)
+    xd = to_dev(wl, x)
+    out = torch.empty_like(xd)
+    rows = sample_rows(wl.B, 24, seed=40 + sub)
+    if sub == 0:
+        ctx.sublayer_forward(0, 0, xd, None, None, out, wl.B, stream())
+        torch.cuda.synchronize()
+        ref = oracle_sublayer(wl, ws, 1, 0, x[rows].astype(np.float64))
+    else:
+        xr = to_dev(wl, dg.make_x(wl, seed=wl.seed + 100))
+        ctx.sublayer_forward(0, 1, xr, xd, None, out, wl.B, stream())
+        torch.cuda.synchronize()
+        ref = oracle_sublayer(wl, ws, 1, 1, to_np(xr)[rows], x[rows].astype(np.float64))
+    err = row_err(to_np(out)[rows], ref)
+    say("moe sublayer err", sub, err)
+    assert err <= TOL["bf16"]
+
+
+def test_moe_stack_full_batch_sampled():
+    require_gpu()
+    import torch
+    wl = dg.WORKLOADS[4]
+    say("moe stack cfg4")
+    ctx, banks, ws = context("w4", wl)
+    x = dg.make_x(wl)
+    xd = to_dev(wl, x)
+    y = torch.empty_like(xd)
+    ctx.block_stack_forward(xd, y, wl.B, stream())
+    torch.cuda.synchronize()
+    rows = sample_rows(wl.B, 8, seed=44)
+    ref = orc.stack_forward(x[rows].astype(np.float64), wl, ws)
+    err = row_err(to_np(y)[rows], ref)
+    say("moe stack err", err)
+    assert err <= TOL["bf16"]
+    drop("w4")

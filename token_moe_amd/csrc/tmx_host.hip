@@ -1,0 +1,586 @@
+// tmx_host.hip -- the C ABI (include/tmx.h): validation, weight storage and
+// repacking, workspace, and the launch sequence of the block-stack forward.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "tmx.h"
+#include "tmx_internal.h"
+
+using namespace tmx;
+
+namespace {
+
+constexpr int NKINDS = 11;
+thread_local std::string g_create_error;
+
+struct Bank {
+  void* ptr = nullptr;    // device storage (packed for bf16 matrices, fp32 for gains)
+  size_t elems = 0;       // logical element count
+  bool loaded = false;
+};
+
+}  // namespace
+
+struct tmx_ctx {
+  tmx_config cfg{};
+  int device = 0;
+  float alpha = 0.f;
+  std::vector<Bank> banks;      // [L][2][NKINDS]
+  // workspace
+  void* act[3] = {nullptr, nullptr, nullptr};  // [B_max, T, D] each
+  void* xrev = nullptr;                        // [B_max, T, D]
+  uint16_t* xhat = nullptr;                    // [P][B_max][W] (max over sub-layers)
+  int32_t* idx = nullptr;                      // [B_max][P][k]
+  float* gate = nullptr;                       // [B_max][P][k]
+  int* rows = nullptr;                         // [P][B_max*k]
+  int4* tiles = nullptr;                       // [P][max_tiles]
+  int* ntiles = nullptr;                       // [P]
+  int* counts = nullptr;                       // [P][E]
+  float* part = nullptr;                       // [B_max][P][k][W]
+  std::vector<void*> allocs;
+  std::string err;
+};
+
+namespace {
+
+tmx_status fail(tmx_ctx* c, tmx_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (c)
+    c->err = buf;
+  else
+    g_create_error = buf;
+  return s;
+}
+
+size_t esize(const tmx_config& c) { return c.dtype == TMX_BF16 ? 2 : 4; }
+int positions(const tmx_config& c, int sub) { return sub == TMX_MIX ? c.H : c.T; }
+int width(const tmx_config& c, int sub) { return sub == TMX_MIX ? c.T * (c.D / c.H) : c.D; }
+int dense_hidden(const tmx_config& c, int sub) { return sub == TMX_MIX ? c.hidden_mix : c.hidden_rev; }
+bool is_moe(const tmx_config& c) { return c.E > 0; }
+
+// logical [G, K, N] view of a matrix bank; returns false for non-matrix kinds
+bool bank_dims(const tmx_config& c, int sub, int kind, int64_t* G, int* K, int* N) {
+  const int P = positions(c, sub), W = width(c, sub);
+  switch (kind) {
+    case TMX_W_UP: case TMX_W_GATE: *G = P; *K = W; *N = dense_hidden(c, sub); return true;
+    case TMX_W_DOWN: *G = P; *K = dense_hidden(c, sub); *N = W; return true;
+    case TMX_W_ROUTER: *G = P; *K = W; *N = c.E; return true;
+    case TMX_W_EXP_UP: case TMX_W_EXP_GATE: *G = (int64_t)P * c.E; *K = W; *N = c.expert_hidden; return true;
+    case TMX_W_EXP_DOWN: *G = (int64_t)P * c.E; *K = c.expert_hidden; *N = W; return true;
+    case TMX_W_SH_UP: case TMX_W_SH_GATE: *G = P; *K = W; *N = c.shared_hidden; return true;
+    case TMX_W_SH_DOWN: *G = P; *K = c.shared_hidden; *N = W; return true;
+    default: return false;
+  }
+}
+
+bool kind_applies(const tmx_config& c, int kind) {
+  if (kind == TMX_W_NORM_GAIN) return true;
+  if (is_moe(c)) return kind >= TMX_W_ROUTER && kind <= TMX_W_SH_DOWN;
+  return kind >= TMX_W_UP && kind <= TMX_W_DOWN;
+}
+
+size_t kind_elems(const tmx_config& c, int sub, int kind) {
+  if (kind == TMX_W_NORM_GAIN) return (size_t)width(c, sub);
+  int64_t G;
+  int K, N;
+  if (!bank_dims(c, sub, kind, &G, &K, &N)) return 0;
+  return (size_t)G * K * N;
+}
+
+Bank& bank(tmx_ctx* c, int layer, int sub, int kind) {
+  return c->banks[((size_t)layer * 2 + sub) * NKINDS + kind];
+}
+
+// storage of a bank: gate and up share one interleaved fragment buffer in bf16
+Bank& storage(tmx_ctx* c, int layer, int sub, int kind) {
+  if (c->cfg.dtype == TMX_BF16) {
+    if (kind == TMX_W_UP) kind = TMX_W_GATE;
+    if (kind == TMX_W_EXP_UP) kind = TMX_W_EXP_GATE;
+    if (kind == TMX_W_SH_UP) kind = TMX_W_SH_GATE;
+  }
+  return bank(c, layer, sub, kind);
+}
+
+void release(tmx_ctx* c) {
+  for (void* p : c->allocs) (void)hipFree(p);
+  c->allocs.clear();
+}
+
+tmx_status dev_alloc(tmx_ctx* c, void** p, size_t bytes, const char* what) {
+  *p = nullptr;
+  if (bytes == 0) return TMX_OK;
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    *p = nullptr;
+    return fail(c, e == hipErrorOutOfMemory ? TMX_ERR_OOM : TMX_ERR_DEVICE, "hipMalloc(%zu bytes) for %s: %s",
+                bytes, what, hipGetErrorString(e));
+  }
+  c->allocs.push_back(*p);
+  return TMX_OK;
+}
+
+tmx_status check_launch(tmx_ctx* c, hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(c, TMX_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return TMX_OK;
+}
+
+tmx_status validate_config(const tmx_config* cfg) {
+  if (!cfg) return fail(nullptr, TMX_ERR_INVALID_ARG, "cfg is NULL");
+  const tmx_config& c = *cfg;
+  if (c.dtype != TMX_F32 && c.dtype != TMX_BF16)
+    return fail(nullptr, TMX_ERR_INVALID_ARG, "dtype must be TMX_F32 (0) or TMX_BF16 (1), got %d", c.dtype);
+  if (c.B_max < 1 || c.T < 1 || c.H < 1 || c.D < 1 || c.L < 1)
+    return fail(nullptr, TMX_ERR_INVALID_ARG, "B_max, T, H, D, L must be >= 1 (got %d, %d, %d, %d, %d)", c.B_max,
+                c.T, c.H, c.D, c.L);
+  if (c.D % c.H != 0) return fail(nullptr, TMX_ERR_INVALID_ARG, "D (%d) must be divisible by H (%d)", c.D, c.H);
+  if (!(c.eps > 0.f)) return fail(nullptr, TMX_ERR_INVALID_ARG, "eps must be > 0");
+  if (c.inter_residual_gap < 0) return fail(nullptr, TMX_ERR_INVALID_ARG, "inter_residual_gap must be >= 0");
+  if (c.E < 0) return fail(nullptr, TMX_ERR_INVALID_ARG, "E must be >= 0");
+  if (c.E == 0) {
+    if (c.hidden_mix < 1 || c.hidden_rev < 1)
+      return fail(nullptr, TMX_ERR_INVALID_ARG, "dense config needs hidden_mix, hidden_rev >= 1");
+  } else {
+    if (c.top_k < 1 || c.top_k > c.E)
+      return fail(nullptr, TMX_ERR_INVALID_ARG, "need 1 <= top_k <= E (top_k %d, E %d)", c.top_k, c.E);
+    if (c.expert_hidden < 1 || c.shared_hidden < 1)
+      return fail(nullptr, TMX_ERR_INVALID_ARG, "MoE config needs expert_hidden, shared_hidden >= 1");
+    if (c.alpha < 0.f) return fail(nullptr, TMX_ERR_INVALID_ARG, "alpha must be >= 0");
+  }
+  const int64_t act = (int64_t)c.B_max * c.T * c.D;
+  if (act > (int64_t)1 << 40) return fail(nullptr, TMX_ERR_INVALID_ARG, "B_max*T*D too large");
+
+  const int dh = c.D / c.H;
+  if (c.dtype == TMX_BF16) {
+    if (dh % 8 != 0)
+      return fail(nullptr, TMX_ERR_UNSUPPORTED, "bf16 path needs D/H %% 8 == 0 (16-byte Mix segments), got %d", dh);
+    for (int sub = 0; sub < 2; ++sub) {
+      const int W = width(c, sub);
+      if (!mlp_width_supported(W))
+        return fail(nullptr, TMX_ERR_UNSUPPORTED, "bf16 path supports sub-layer widths 128, 256, 512, 768; got %d",
+                    W);
+      const int hs[3] = {c.E ? c.expert_hidden : dense_hidden(c, sub), c.E ? c.shared_hidden : 64, 64};
+      for (int h : hs)
+        if (h % 64 != 0) return fail(nullptr, TMX_ERR_UNSUPPORTED, "bf16 path needs hidden sizes %% 64 == 0, got %d", h);
+    }
+    if (c.E > 0 && (c.E % 16 != 0 || c.E > 64))
+      return fail(nullptr, TMX_ERR_UNSUPPORTED, "bf16 MoE needs E %% 16 == 0 and E <= 64, got %d", c.E);
+    if (c.E > 0 && c.top_k > 8) return fail(nullptr, TMX_ERR_UNSUPPORTED, "bf16 MoE needs top_k <= 8");
+  } else {
+    if (c.E > 256 || c.top_k > 64) return fail(nullptr, TMX_ERR_UNSUPPORTED, "fp32 MoE needs E <= 256, top_k <= 64");
+    const int hmax = std::max({c.hidden_mix, c.hidden_rev, c.expert_hidden, c.shared_hidden});
+    const int Wmax = std::max(width(c, 0), width(c, 1));
+    if ((2LL * Wmax + hmax + std::max(c.E, 1) + 2) * 4 > 65536)
+      return fail(nullptr, TMX_ERR_UNSUPPORTED, "fp32 path needs (2W + hidden + E) * 4 bytes <= 64 KiB of LDS");
+  }
+  return TMX_OK;
+}
+
+int moe_bm(const tmx_config& c, int sub) { return mlp_bm_for_width(width(c, sub)); }
+int moe_max_tiles(const tmx_config& c, int sub, int B) {
+  const int bm = moe_bm(c, sub);
+  return (int)(((int64_t)B * c.top_k + bm - 1) / bm) + c.E;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool sublayer_ready(tmx_ctx* c, int layer, int sub) {
+  for (int k = 1; k < NKINDS; ++k)
+    if (kind_applies(c->cfg, k) && !bank(c, layer, sub, k).loaded) return false;
+  return true;
+}
+
+tmx_status check_ready(tmx_ctx* c) {
+  for (int l = 0; l < c->cfg.L; ++l)
+    for (int s = 0; s < 2; ++s)
+      if (!sublayer_ready(c, l, s))
+        return fail(c, TMX_ERR_STATE, "weights of layer %d sub-layer %d are not all loaded", l, s);
+  return TMX_OK;
+}
+
+// ---- one sub-layer --------------------------------------------------------------
+tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const void* resid, const void* extra,
+                        void* x_out, int B, hipStream_t st) {
+  const tmx_config& cfg = c->cfg;
+  const int P = positions(cfg, sub), W = width(cfg, sub);
+  RowMap map{cfg.T, cfg.D, cfg.D / cfg.H, sub == TMX_MIX ? 1 : 0};
+  if (sub == TMX_MIX) resid = x_in;   // H itself, read through the Mix map
+  const float* gain = static_cast<const float*>(bank(c, layer, sub, TMX_W_NORM_GAIN).ptr);
+
+  if (cfg.dtype == TMX_F32) {
+    F32Args a{};
+    a.B = B; a.P = P; a.W = W; a.hidden = is_moe(cfg) ? 0 : dense_hidden(cfg, sub);
+    a.E = cfg.E; a.top_k = cfg.top_k; a.expert_hidden = cfg.expert_hidden; a.shared_hidden = cfg.shared_hidden;
+    a.alpha = c->alpha; a.eps = cfg.eps; a.map = map;
+    a.x = static_cast<const float*>(x_in); a.gain = gain;
+    a.resid = static_cast<const float*>(resid); a.extra = static_cast<const float*>(extra);
+    a.out = static_cast<float*>(x_out);
+    auto w = [&](int k) { return static_cast<const float*>(bank(c, layer, sub, k).ptr); };
+    a.w_up = w(TMX_W_UP); a.w_gate = w(TMX_W_GATE); a.w_down = w(TMX_W_DOWN);
+    a.w_router = w(TMX_W_ROUTER); a.e_up = w(TMX_W_EXP_UP); a.e_gate = w(TMX_W_EXP_GATE);
+    a.e_down = w(TMX_W_EXP_DOWN); a.s_up = w(TMX_W_SH_UP); a.s_gate = w(TMX_W_SH_GATE); a.s_down = w(TMX_W_SH_DOWN);
+    return check_launch(c, launch_f32_sublayer(a, st), "f32 sub-layer launch");
+  }
+
+  MlpArgs a{};
+  a.B = B; a.P = P; a.map = map; a.eps = cfg.eps;
+  a.x = static_cast<const uint16_t*>(x_in); a.gain = gain;
+  a.resid = static_cast<const uint16_t*>(resid); a.extra = static_cast<const uint16_t*>(extra);
+  a.out = static_cast<uint16_t*>(x_out);
+  const int bm = mlp_bm_for_width(W);
+  if (!is_moe(cfg)) {
+    a.hidden = dense_hidden(cfg, sub);
+    a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_GATE).ptr);
+    a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_DOWN).ptr);
+    a.rtiles = (B + bm - 1) / bm;
+    return check_launch(c, launch_mlp(MLP_DENSE, W, a, P * a.rtiles, st), "dense MLP launch");
+  }
+
+  // MoE: norm + route -> bucket -> routed experts -> shared expert + combine
+  RouteArgs r{};
+  r.B = B; r.P = P; r.E = cfg.E; r.top_k = cfg.top_k; r.alpha = c->alpha; r.eps = cfg.eps; r.map = map;
+  r.x = static_cast<const uint16_t*>(x_in); r.gain = gain;
+  r.wr = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_ROUTER).ptr);
+  r.xhat = c->xhat; r.idx = c->idx; r.gate = c->gate;
+  tmx_status s = check_launch(c, launch_norm_route(W, r, st), "router launch");
+  if (s != TMX_OK) return s;
+
+  BucketArgs k{};
+  k.B = B; k.P = P; k.E = cfg.E; k.top_k = cfg.top_k; k.bm = bm; k.max_tiles = moe_max_tiles(cfg, sub, B);
+  k.idx = c->idx; k.rows = c->rows; k.tiles = c->tiles; k.ntiles = c->ntiles; k.counts = c->counts;
+  s = check_launch(c, launch_bucket(k, st), "bucket launch");
+  if (s != TMX_OK) return s;
+
+  a.xhat = c->xhat; a.top_k = cfg.top_k; a.E = cfg.E; a.max_tiles = k.max_tiles;
+  a.rows = c->rows; a.tiles = c->tiles; a.ntiles = c->ntiles; a.gate = c->gate; a.part = c->part;
+  a.hidden = cfg.expert_hidden;
+  a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_EXP_GATE).ptr);
+  a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_EXP_DOWN).ptr);
+  s = check_launch(c, launch_mlp(MLP_ROUTED, W, a, P * a.max_tiles, st), "routed MLP launch");
+  if (s != TMX_OK) return s;
+
+  a.hidden = cfg.shared_hidden;
+  a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_SH_GATE).ptr);
+  a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_SH_DOWN).ptr);
+  a.rtiles = (B + bm - 1) / bm;
+  return check_launch(c, launch_mlp(MLP_SHARED, W, a, P * a.rtiles, st), "shared MLP launch");
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+tmx_status check_act(tmx_ctx* c, const void* p, const char* name) {
+  if (!p) return fail(c, TMX_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(c, TMX_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+  return TMX_OK;
+}
+
+tmx_status check_B(tmx_ctx* c, int B) {
+  if (B < 1 || B > c->cfg.B_max)
+    return fail(c, TMX_ERR_INVALID_ARG, "B = %d outside [1, B_max = %d]", B, c->cfg.B_max);
+  return TMX_OK;
+}
+
+bool overlaps(const void* a, const void* b, size_t n) {
+  const char* x = static_cast<const char*>(a);
+  const char* y = static_cast<const char*>(b);
+  return x < y + n && y < x + n;
+}
+
+}  // namespace
+
+// =============================================================================
+// C ABI
+// =============================================================================
+
+extern "C" {
+
+const char* tmx_last_error(const tmx_ctx* ctx) { return ctx ? ctx->err.c_str() : g_create_error.c_str(); }
+
+tmx_status tmx_create(const tmx_config* cfg, int device, tmx_ctx** out) {
+  if (!out) return fail(nullptr, TMX_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  tmx_status s = validate_config(cfg);
+  if (s != TMX_OK) return s;
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess || ndev == 0) {
+    (void)hipGetLastError();
+    return fail(nullptr, TMX_ERR_DEVICE, "no HIP device available (%s)", hipGetErrorString(e));
+  }
+  if (device < 0 || device >= ndev)
+    return fail(nullptr, TMX_ERR_INVALID_ARG, "device %d outside [0, %d)", device, ndev);
+  if ((e = hipSetDevice(device)) != hipSuccess)
+    return fail(nullptr, TMX_ERR_DEVICE, "hipSetDevice(%d): %s", device, hipGetErrorString(e));
+
+  tmx_ctx* c = new tmx_ctx();
+  c->cfg = *cfg;
+  c->device = device;
+  c->alpha = cfg->E > 0 ? (cfg->alpha != 0.f ? cfg->alpha : (float)cfg->E / (float)cfg->top_k) : 0.f;
+  c->banks.resize((size_t)cfg->L * 2 * NKINDS);
+  const tmx_config& C = c->cfg;
+  const size_t es = esize(C);
+
+  auto bail = [&](tmx_status st) {
+    g_create_error = c->err;
+    release(c);
+    delete c;
+    return st;
+  };
+
+  for (int l = 0; l < C.L; ++l)
+    for (int sub = 0; sub < 2; ++sub)
+      for (int k = 0; k < NKINDS; ++k) {
+        if (!kind_applies(C, k)) continue;
+        Bank& b = bank(c, l, sub, k);
+        b.elems = kind_elems(C, sub, k);
+        if (k == TMX_W_NORM_GAIN) {
+          s = dev_alloc(c, &b.ptr, b.elems * sizeof(float), "norm gain");
+          if (s != TMX_OK) return bail(s);
+          std::vector<float> ones(b.elems, 1.0f);
+          if ((e = hipMemcpy(b.ptr, ones.data(), b.elems * sizeof(float), hipMemcpyHostToDevice)) != hipSuccess)
+            return bail(fail(c, TMX_ERR_DEVICE, "gain init: %s", hipGetErrorString(e)));
+          b.loaded = true;
+          continue;
+        }
+        if (C.dtype == TMX_BF16 && (k == TMX_W_UP || k == TMX_W_EXP_UP || k == TMX_W_SH_UP)) continue;
+        size_t n = b.elems;
+        if (C.dtype == TMX_BF16 && (k == TMX_W_GATE || k == TMX_W_EXP_GATE || k == TMX_W_SH_GATE)) n *= 2;
+        s = dev_alloc(c, &b.ptr, n * es, "weights");
+        if (s != TMX_OK) return bail(s);
+      }
+
+  const int64_t act = (int64_t)C.B_max * C.T * C.D;
+  for (int i = 0; i < 3; ++i)
+    if ((s = dev_alloc(c, &c->act[i], act * es, "activations")) != TMX_OK) return bail(s);
+  if ((s = dev_alloc(c, &c->xrev, act * es, "activations")) != TMX_OK) return bail(s);
+
+  if (C.E > 0 && C.dtype == TMX_BF16) {
+    const int Pmax = std::max(C.H, C.T), Wmax = std::max(width(C, 0), width(C, 1));
+    int64_t tiles = 0, xh = 0, part = 0;
+    for (int sub = 0; sub < 2; ++sub) {
+      tiles = std::max<int64_t>(tiles, (int64_t)positions(C, sub) * moe_max_tiles(C, sub, C.B_max));
+      xh = std::max<int64_t>(xh, (int64_t)positions(C, sub) * C.B_max * width(C, sub));
+      part = std::max<int64_t>(part, (int64_t)positions(C, sub) * C.B_max * C.top_k * width(C, sub));
+    }
+    (void)Wmax;
+    const int64_t rk = (int64_t)C.B_max * Pmax * C.top_k;
+    if ((s = dev_alloc(c, (void**)&c->xhat, xh * 2, "x_hat")) != TMX_OK) return bail(s);
+    if ((s = dev_alloc(c, (void**)&c->idx, rk * 4, "routing")) != TMX_OK) return bail(s);
+    if ((s = dev_alloc(c, (void**)&c->gate, rk * 4, "routing")) != TMX_OK) return bail(s);
+    if ((s = dev_alloc(c, (void**)&c->rows, rk * 4, "bucket rows")) != TMX_OK) return bail(s);
+    if ((s = dev_alloc(c, (void**)&c->tiles, tiles * sizeof(int4), "bucket tiles")) != TMX_OK) return bail(s);
+    if ((s = dev_alloc(c, (void**)&c->ntiles, Pmax * 4, "bucket tiles")) != TMX_OK) return bail(s);
+    if ((s = dev_alloc(c, (void**)&c->counts, (int64_t)Pmax * C.E * 4, "bucket counts")) != TMX_OK) return bail(s);
+    if ((s = dev_alloc(c, (void**)&c->part, part * 4, "expert partials")) != TMX_OK) return bail(s);
+  }
+  *out = c;
+  return TMX_OK;
+}
+
+tmx_status tmx_destroy(tmx_ctx* ctx) {
+  if (!ctx) return TMX_OK;
+  (void)hipSetDevice(ctx->device);
+  release(ctx);
+  delete ctx;
+  return TMX_OK;
+}
+
+tmx_status tmx_load_weights(tmx_ctx* c, int layer, int sub, int kind, const void* src, size_t nbytes,
+                            void* stream) {
+  if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
+  const tmx_config& C = c->cfg;
+  if (layer < 0 || layer >= C.L) return fail(c, TMX_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, C.L);
+  if (sub != TMX_MIX && sub != TMX_REVERT) return fail(c, TMX_ERR_INVALID_ARG, "sublayer must be 0 or 1, got %d", sub);
+  if (kind < 0 || kind >= NKINDS) return fail(c, TMX_ERR_INVALID_ARG, "unknown weight kind %d", kind);
+  if (!kind_applies(C, kind))
+    return fail(c, TMX_ERR_INVALID_ARG, "weight kind %d does not apply to a %s context", kind,
+                is_moe(C) ? "MoE" : "dense");
+  if (!src) return fail(c, TMX_ERR_INVALID_ARG, "src is NULL");
+  const size_t es = esize(C);
+  const size_t elems = kind_elems(C, sub, kind);
+  if (nbytes != elems * es)
+    return fail(c, TMX_ERR_INVALID_ARG, "nbytes %zu != expected %zu for kind %d", nbytes, elems * es, kind);
+
+  hipError_t e = hipSetDevice(c->device);
+  if (e != hipSuccess) return fail(c, TMX_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(e));
+  hipStream_t st = as_stream(stream);
+
+  bool src_dev = false;
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, src) == hipSuccess)
+    src_dev = attr.type == hipMemoryTypeDevice;
+  (void)hipGetLastError();
+
+  Bank& b = bank(c, layer, sub, kind);
+  if (kind == TMX_W_NORM_GAIN) {
+    std::vector<float> g(elems);
+    std::vector<unsigned char> raw(nbytes);
+    e = hipMemcpy(raw.data(), src, nbytes, src_dev ? hipMemcpyDeviceToHost : hipMemcpyHostToHost);
+    if (e != hipSuccess) return fail(c, TMX_ERR_DEVICE, "gain copy: %s", hipGetErrorString(e));
+    for (size_t i = 0; i < elems; ++i) {
+      if (es == 4) {
+        memcpy(&g[i], &raw[i * 4], 4);
+      } else {
+        uint16_t h;
+        memcpy(&h, &raw[i * 2], 2);
+        uint32_t u = (uint32_t)h << 16;
+        memcpy(&g[i], &u, 4);
+      }
+    }
+    e = hipMemcpy(b.ptr, g.data(), elems * sizeof(float), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail(c, TMX_ERR_DEVICE, "gain upload: %s", hipGetErrorString(e));
+    b.loaded = true;
+    return TMX_OK;
+  }
+
+  if (C.dtype == TMX_F32) {
+    e = hipMemcpyAsync(b.ptr, src, nbytes, src_dev ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(c, TMX_ERR_DEVICE, "weight copy: %s", hipGetErrorString(e));
+    b.loaded = true;
+    return TMX_OK;
+  }
+
+  // bf16: stage on the device, then repack into MFMA fragments
+  void* stage = nullptr;
+  e = hipMalloc(&stage, nbytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(c, e == hipErrorOutOfMemory ? TMX_ERR_OOM : TMX_ERR_DEVICE, "staging buffer: %s",
+                hipGetErrorString(e));
+  }
+  e = hipMemcpyAsync(stage, src, nbytes, src_dev ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, st);
+  int64_t G;
+  int K, N;
+  bank_dims(C, sub, kind, &G, &K, &N);
+  const bool gu = kind == TMX_W_UP || kind == TMX_W_GATE || kind == TMX_W_EXP_UP || kind == TMX_W_EXP_GATE ||
+                  kind == TMX_W_SH_UP || kind == TMX_W_SH_GATE;
+  const int which = (kind == TMX_W_UP || kind == TMX_W_EXP_UP || kind == TMX_W_SH_UP) ? 1 : 0;
+  if (e == hipSuccess)
+    e = launch_pack(static_cast<const uint16_t*>(stage), static_cast<uint16_t*>(storage(c, layer, sub, kind).ptr),
+                    (int)G, K, N, gu ? 0 : 1, which, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  (void)hipFree(stage);
+  if (e != hipSuccess) return fail(c, TMX_ERR_DEVICE, "weight upload/pack: %s", hipGetErrorString(e));
+  b.loaded = true;
+  return TMX_OK;
+}
+
+tmx_status tmx_sublayer_forward(tmx_ctx* c, int layer, int sub, const void* x_in, const void* resid,
+                                const void* extra, void* x_out, int B, void* stream) {
+  if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
+  tmx_status s;
+  if (layer < 0 || layer >= c->cfg.L) return fail(c, TMX_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, c->cfg.L);
+  if (sub != TMX_MIX && sub != TMX_REVERT) return fail(c, TMX_ERR_INVALID_ARG, "sublayer must be 0 or 1");
+  if ((s = check_B(c, B)) != TMX_OK) return s;
+  if ((s = check_act(c, x_in, "x_in")) != TMX_OK) return s;
+  if ((s = check_act(c, x_out, "x_out")) != TMX_OK) return s;
+  const size_t bytes = (size_t)B * c->cfg.T * c->cfg.D * esize(c->cfg);
+  if (sub == TMX_MIX) {
+    if (resid || extra) return fail(c, TMX_ERR_INVALID_ARG, "MIX sub-layer takes no resid/extra (pass NULL)");
+  } else {
+    if ((s = check_act(c, resid, "resid")) != TMX_OK) return s;
+    if (extra && !aligned16(extra)) return fail(c, TMX_ERR_INVALID_ARG, "extra must be 16-byte aligned");
+    if (overlaps(resid, x_out, bytes) || (extra && overlaps(extra, x_out, bytes)))
+      return fail(c, TMX_ERR_INVALID_ARG, "x_out overlaps an input");
+  }
+  if (overlaps(x_in, x_out, bytes)) return fail(c, TMX_ERR_INVALID_ARG, "x_in and x_out overlap");
+  if (!sublayer_ready(c, layer, sub))
+    return fail(c, TMX_ERR_STATE, "weights of layer %d sub-layer %d are not all loaded", layer, sub);
+  (void)hipSetDevice(c->device);
+  return run_sublayer(c, layer, sub, x_in, resid, extra, x_out, B, as_stream(stream));
+}
+
+tmx_status tmx_block_stack_forward(tmx_ctx* c, const void* x_in, void* x_out, int B, void* stream) {
+  if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
+  tmx_status s;
+  if ((s = check_B(c, B)) != TMX_OK) return s;
+  if ((s = check_act(c, x_in, "x_in")) != TMX_OK) return s;
+  if ((s = check_act(c, x_out, "x_out")) != TMX_OK) return s;
+  const size_t bytes = (size_t)B * c->cfg.T * c->cfg.D * esize(c->cfg);
+  if (overlaps(x_in, x_out, bytes)) return fail(c, TMX_ERR_INVALID_ARG, "x_in and x_out overlap");
+  if ((s = check_ready(c)) != TMX_OK) return s;
+  (void)hipSetDevice(c->device);
+  hipStream_t st = as_stream(stream);
+  const int L = c->cfg.L, g = c->cfg.inter_residual_gap;
+  const void* cur = x_in;    // Y_{l-1}
+  const void* save = x_in;   // Y_{l-g}: the output of the last multiple of g
+  for (int l = 1; l <= L; ++l) {
+    if ((s = run_sublayer(c, l - 1, TMX_MIX, cur, nullptr, nullptr, c->xrev, B, st)) != TMX_OK) return s;
+    const bool inter = g > 0 && l % g == 0 && l < L;
+    void* dst = x_out;
+    if (l < L)
+      for (void* cand : c->act)
+        if (cand != cur && cand != save) {
+          dst = cand;
+          break;
+        }
+    if ((s = run_sublayer(c, l - 1, TMX_REVERT, c->xrev, cur, inter ? save : nullptr, dst, B, st)) != TMX_OK)
+      return s;
+    if (g > 0 && l % g == 0) save = dst;
+    cur = dst;
+  }
+  return TMX_OK;
+}
+
+tmx_status tmx_moe_route(tmx_ctx* c, int layer, int sub, const void* x, int B, int32_t* idx, float* gate,
+                         void* stream) {
+  if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
+  const tmx_config& C = c->cfg;
+  if (!is_moe(C)) return fail(c, TMX_ERR_UNSUPPORTED, "tmx_moe_route needs an MoE context (E > 0)");
+  tmx_status s;
+  if (layer < 0 || layer >= C.L) return fail(c, TMX_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, C.L);
+  if (sub != TMX_MIX && sub != TMX_REVERT) return fail(c, TMX_ERR_INVALID_ARG, "sublayer must be 0 or 1");
+  if ((s = check_B(c, B)) != TMX_OK) return s;
+  if ((s = check_act(c, x, "x")) != TMX_OK) return s;
+  if (!idx || !gate) return fail(c, TMX_ERR_INVALID_ARG, "idx and gate must be non-NULL");
+  if (!bank(c, layer, sub, TMX_W_ROUTER).loaded)
+    return fail(c, TMX_ERR_STATE, "router of layer %d sub-layer %d is not loaded", layer, sub);
+  (void)hipSetDevice(c->device);
+  hipStream_t st = as_stream(stream);
+  const int P = positions(C, sub), W = width(C, sub);
+  RowMap map{C.T, C.D, C.D / C.H, sub == TMX_MIX ? 1 : 0};
+  const float* gain = static_cast<const float*>(bank(c, layer, sub, TMX_W_NORM_GAIN).ptr);
+  if (C.dtype == TMX_F32) {
+    F32Args a{};
+    a.B = B; a.P = P; a.W = W; a.E = C.E; a.top_k = C.top_k; a.expert_hidden = C.expert_hidden;
+    a.shared_hidden = C.shared_hidden; a.alpha = c->alpha; a.eps = C.eps; a.map = map;
+    a.x = static_cast<const float*>(x); a.gain = gain;
+    a.w_router = static_cast<const float*>(bank(c, layer, sub, TMX_W_ROUTER).ptr);
+    a.idx = idx; a.gate_out = gate; a.route_only = 1;
+    return check_launch(c, launch_f32_sublayer(a, st), "f32 router launch");
+  }
+  RouteArgs r{};
+  r.B = B; r.P = P; r.E = C.E; r.top_k = C.top_k; r.alpha = c->alpha; r.eps = C.eps; r.map = map;
+  r.x = static_cast<const uint16_t*>(x); r.gain = gain;
+  r.wr = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_ROUTER).ptr);
+  r.xhat = nullptr; r.idx = idx; r.gate = gate;
+  return check_launch(c, launch_norm_route(W, r, st), "router launch");
+}
+
+tmx_status tmx_debug_permute(tmx_ctx* c, const void* in, void* out, int B, int inverse, void* stream) {
+  if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
+  tmx_status s;
+  if ((s = check_B(c, B)) != TMX_OK) return s;
+  if (!in || !out) return fail(c, TMX_ERR_INVALID_ARG, "in/out must be non-NULL");
+  if (inverse != 0 && inverse != 1) return fail(c, TMX_ERR_INVALID_ARG, "inverse must be 0 or 1");
+  const size_t bytes = (size_t)B * c->cfg.T * c->cfg.D * esize(c->cfg);
+  if (overlaps(in, out, bytes)) return fail(c, TMX_ERR_INVALID_ARG, "in and out overlap");
+  (void)hipSetDevice(c->device);
+  return check_launch(c,
+                      launch_permute(in, out, B, c->cfg.T, c->cfg.D, c->cfg.H, (int)esize(c->cfg), inverse,
+                                     as_stream(stream)),
+                      "permute launch");
+}
+
+}  // extern "C"

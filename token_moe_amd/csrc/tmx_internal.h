@@ -1,0 +1,103 @@
+// tmx_internal.h -- argument blocks and launchers shared between the host
+// library (tmx_host.hip) and the kernel files.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tmx_device.h"
+
+namespace tmx {
+
+enum MlpMode { MLP_DENSE = 0, MLP_ROUTED = 1, MLP_SHARED = 2 };
+
+// One launch of the fused per-position SwiGLU MLP over row tiles:
+//   DENSE : out = rho(resid + SwiGLU_p(rho(RMSNorm(x_p))) [+ extra])
+//   ROUTED: part[b,p,s] = gate[b,p,s] * SwiGLU_{p,e}(xhat[p, b])   (bucket rows)
+//   SHARED: out = rho(resid + SwiGLU_p,sh(xhat[p,b]) + sum_s part[b,p,s] [+ extra])
+struct MlpArgs {
+  int B;               // batch rows
+  int P;               // positions of the sub-layer
+  int hidden;          // hidden size of the MLP (dense h, h_e or h_s)
+  RowMap map;          // block-layout map of x / resid / extra / out
+  float eps;
+  const uint16_t* x;       // DENSE source, [B, T, D]
+  const float* gain;       // DENSE: RMSNorm gain [W]
+  const uint16_t* xhat;    // ROUTED / SHARED source, [P][B][W]
+  const uint16_t* wgu;     // packed gate|up fragments
+  const uint16_t* wd;      // packed down fragments
+  const uint16_t* resid;   // DENSE / SHARED
+  const uint16_t* extra;   // nullable
+  uint16_t* out;           // DENSE / SHARED
+  int top_k, E, max_tiles;
+  const int* rows;         // ROUTED: [P][B*top_k] bucket entries (b*top_k + slot)
+  const int4* tiles;       // ROUTED: [P][max_tiles] (expert, start, count, 0)
+  const int* ntiles;       // ROUTED: [P]
+  const float* gate;       // ROUTED: [B][P][top_k]
+  float* part;             // ROUTED writes / SHARED reads, [B][P][top_k][W]
+  int rtiles;              // DENSE / SHARED: row tiles per position
+};
+
+struct RouteArgs {
+  int B, P, E, top_k;
+  float alpha, eps;
+  RowMap map;
+  const uint16_t* x;       // block layout [B, T, D]
+  const float* gain;       // [W]
+  const uint16_t* wr;      // packed router fragments
+  uint16_t* xhat;          // [P][B][W] (nullable)
+  int32_t* idx;            // [B][P][top_k]
+  float* gate;             // [B][P][top_k]
+};
+
+struct BucketArgs {
+  int B, P, E, top_k, bm, max_tiles;
+  const int32_t* idx;      // [B][P][top_k]
+  int* rows;               // [P][B*top_k]
+  int4* tiles;             // [P][max_tiles]
+  int* ntiles;             // [P]
+  int* counts;             // [P][E]
+};
+
+// bf16 launchers (return hipError_t of the launch)
+int mlp_bm_for_width(int W);
+bool mlp_width_supported(int W);
+hipError_t launch_mlp(int mode, int W, const MlpArgs& a, int grid, hipStream_t s);
+hipError_t launch_norm_route(int W, const RouteArgs& a, hipStream_t s);
+hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
+// Repack G row-major [K, N] bf16 matrices into MFMA B-operand fragments.
+// layout 0 (gate|up interleave, `which` = 0 gate / 1 up), layout 1 (k-major).
+hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int G, int K, int N, int layout,
+                       int which, hipStream_t s);
+hipError_t launch_permute(const void* in, void* out, int B, int T, int D, int H, int elem_bytes,
+                          int inverse, hipStream_t s);
+
+// fp32 path
+struct F32Args {
+  int B, P, W, hidden, E, top_k, expert_hidden, shared_hidden;
+  float alpha, eps;
+  RowMap map;
+  const float* x;
+  const float* gain;
+  const float* resid;      // nullable when route_only
+  const float* extra;      // nullable
+  float* out;              // nullable when route_only
+  // dense
+  const float* w_up;
+  const float* w_gate;
+  const float* w_down;
+  // moe
+  const float* w_router;
+  const float* e_up;
+  const float* e_gate;
+  const float* e_down;
+  const float* s_up;
+  const float* s_gate;
+  const float* s_down;
+  int32_t* idx;            // nullable
+  float* gate_out;         // nullable
+  int route_only;
+};
+hipError_t launch_f32_sublayer(const F32Args& a, hipStream_t s);
+
+}  // namespace tmx

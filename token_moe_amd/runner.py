@@ -1,0 +1,48 @@
+"""Glue between a workload description and a libtmx context: build the
+tmx_config, upload the seeded weight banks. Marshalling only -- every step
+of the forward runs in libtmx.so."""
+from __future__ import annotations
+
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+from . import tmx
+
+# weight kinds use the same numbering in the seeded generator and tmx.h
+
+
+def config_from_workload(wl, B_max: Optional[int] = None) -> tmx.tmx_config:
+    return tmx.make_config(
+        B_max=B_max or wl.B, T=wl.T, H=wl.H, D=wl.D, L=wl.L,
+        hidden_mix=wl.hidden_mix, hidden_rev=wl.hidden_rev, E=wl.E, top_k=wl.top_k,
+        expert_hidden=wl.expert_hidden, shared_hidden=wl.shared_hidden, alpha=wl.alpha,
+        eps=wl.eps, inter_residual_gap=wl.gap,
+        dtype=tmx.TMX_BF16 if wl.dtype == "bf16" else tmx.TMX_F32)
+
+
+def torch_dtype(wl):
+    import torch
+    return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+
+def host_tensor(wl, a: np.ndarray):
+    """fp32 numpy array of dtype-representable values -> contiguous CPU torch tensor."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch_dtype(wl)).contiguous()
+
+
+def upload_weights(ctx: tmx.Context, wl, banks: Dict[Tuple[int, int, int], np.ndarray]):
+    """banks: {(layer 1..L, sub, kind): fp32 array or CPU torch tensor}.
+    Layer l of the pages is layer l-1 of the C ABI."""
+    import torch
+    for (layer, sub, kind), arr in banks.items():
+        t = arr if isinstance(arr, torch.Tensor) else host_tensor(wl, arr)
+        t = t.contiguous()
+        ctx.load_weights(layer - 1, sub, kind, t.data_ptr(), t.numel() * t.element_size())
+
+
+def make_context(wl, banks, B_max: Optional[int] = None, device: int = 0) -> tmx.Context:
+    ctx = tmx.Context(config_from_workload(wl, B_max), device)
+    upload_weights(ctx, wl, banks)
+    return ctx
