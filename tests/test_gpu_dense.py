@@ -11,7 +11,7 @@ pytestmark = pytest.mark.gpu
 
 # small bf16 dense stack: ragged batch (300 = 2*128 + 44), H != T, W_mix 256, W_rev 128
 SMALL_BF16 = dg.Workload("small_dense_bf16", B=300, T=4, H=2, D=128, L=4, hidden_mix=128,
-                         hidden_rev=192, gap=2, seed=21)
+                         hidden_rev=256, gap=2, seed=21)
 
 
 def _stack(wl, ctx, x_dev, B):

@@ -17,7 +17,7 @@ def test_permute_bit_exact(T, H, D, dtype):
     from token_moe_amd import tmx
     say("permute", T, H, D, dtype)
     B = 37
-    cfg = tmx.make_config(B_max=B, T=T, H=H, D=D, L=1, hidden_mix=64, hidden_rev=64,
+    cfg = tmx.make_config(B_max=B, T=T, H=H, D=D, L=1, hidden_mix=128, hidden_rev=128,
                           dtype=tmx.TMX_BF16 if dtype == "bf16" else tmx.TMX_F32)
     if dtype == "bf16" and (D // H) % 8:
         pytest.skip("bf16 contexts need D/H % 8 == 0")

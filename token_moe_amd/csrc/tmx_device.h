@@ -9,6 +9,7 @@ namespace tmx {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32 (bf16 is carried as its 16-bit pattern)
@@ -66,10 +67,15 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Fragment layout of v_mfma_f32_16x16x32_bf16 (wave64):
+// Fragment layouts (wave64, 8 bf16 = 16 bytes per lane for A and B):
+// v_mfma_f32_16x16x32_bf16
 //   A (16 x 32, M x K): lane l holds A[l % 16][8*(l/16) + i], i = 0..7
 //   B (32 x 16, K x N): lane l holds B[8*(l/16) + i][l % 16]
 //   C (16 x 16):        lane l holds C[4*(l/16) + v][l % 16], v = 0..3
+// v_mfma_f32_32x32x16_bf16
+//   A (32 x 16, M x K): lane l holds A[l % 32][8*(l/32) + i], i = 0..7
+//   B (16 x 32, K x N): lane l holds B[8*(l/32) + i][l % 32]
+//   C (32 x 32):        lane l holds C[8*(v/4) + 4*(l/32) + v%4][l % 32], v = 0..15
 // A packed weight fragment is the 64 x 8 bf16 block a wave loads as B, so
 // each lane reads 16 contiguous bytes.
 constexpr int FRAG_ELEMS = 512;

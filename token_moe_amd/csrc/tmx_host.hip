@@ -169,9 +169,10 @@ tmx_status validate_config(const tmx_config* cfg) {
       if (!mlp_width_supported(W))
         return fail(nullptr, TMX_ERR_UNSUPPORTED, "bf16 path supports sub-layer widths 128, 256, 512, 768; got %d",
                     W);
-      const int hs[3] = {c.E ? c.expert_hidden : dense_hidden(c, sub), c.E ? c.shared_hidden : 64, 64};
+      const int hs[2] = {c.E ? c.expert_hidden : dense_hidden(c, sub), c.E ? c.shared_hidden : MLP_HC};
       for (int h : hs)
-        if (h % 64 != 0) return fail(nullptr, TMX_ERR_UNSUPPORTED, "bf16 path needs hidden sizes %% 64 == 0, got %d", h);
+        if (h % MLP_HC != 0)
+          return fail(nullptr, TMX_ERR_UNSUPPORTED, "bf16 path needs hidden sizes %% %d == 0, got %d", MLP_HC, h);
     }
     if (c.E > 0 && (c.E % 16 != 0 || c.E > 64))
       return fail(nullptr, TMX_ERR_UNSUPPORTED, "bf16 MoE needs E %% 16 == 0 and E <= 64, got %d", c.E);
@@ -468,7 +469,7 @@ tmx_status tmx_load_weights(tmx_ctx* c, int layer, int sub, int kind, const void
   const int which = (kind == TMX_W_UP || kind == TMX_W_EXP_UP || kind == TMX_W_SH_UP) ? 1 : 0;
   if (e == hipSuccess)
     e = launch_pack(static_cast<const uint16_t*>(stage), static_cast<uint16_t*>(storage(c, layer, sub, kind).ptr),
-                    (int)G, K, N, gu ? 0 : 1, which, st);
+                    (int)G, K, N, gu ? 0 : 1, which, kind == TMX_W_ROUTER ? FRAG_16x16x32 : FRAG_32x32x16, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   (void)hipFree(stage);
   if (e != hipSuccess) return fail(c, TMX_ERR_DEVICE, "weight upload/pack: %s", hipGetErrorString(e));

@@ -11,6 +11,12 @@ namespace tmx {
 
 enum MlpMode { MLP_DENSE = 0, MLP_ROUTED = 1, MLP_SHARED = 2 };
 
+// hidden units per chunk of the fused MLP (hidden sizes must be multiples)
+constexpr int MLP_HC = 128;
+
+// B-operand fragment shapes of the packer
+enum FragShape { FRAG_16x16x32 = 0, FRAG_32x32x16 = 1 };
+
 // One launch of the fused per-position SwiGLU MLP over row tiles:
 //   DENSE : out = rho(resid + SwiGLU_p(rho(RMSNorm(x_p))) [+ extra])
 //   ROUTED: part[b,p,s] = gate[b,p,s] * SwiGLU_{p,e}(xhat[p, b])   (bucket rows)
@@ -65,10 +71,12 @@ bool mlp_width_supported(int W);
 hipError_t launch_mlp(int mode, int W, const MlpArgs& a, int grid, hipStream_t s);
 hipError_t launch_norm_route(int W, const RouteArgs& a, hipStream_t s);
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
-// Repack G row-major [K, N] bf16 matrices into MFMA B-operand fragments.
-// layout 0 (gate|up interleave, `which` = 0 gate / 1 up), layout 1 (k-major).
+// Repack G row-major [K, N] bf16 matrices into MFMA B-operand fragments of
+// shape `frag` (FragShape). layout 0: gate|up interleave (`which` = 0 gate,
+// 1 up), frag = ((g*NB + nb)*KB + kb)*2 + which; layout 1: k-major,
+// frag = (g*KB + kb)*NB + nb.
 hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int G, int K, int N, int layout,
-                       int which, hipStream_t s);
+                       int which, int frag, hipStream_t s);
 hipError_t launch_permute(const void* in, void* out, int B, int T, int D, int H, int elem_bytes,
                           int inverse, hipStream_t s);
 

@@ -8,7 +8,7 @@
 //             DENSE: rows are gathered through the Mix map (Eq. 9-11) and
 //             RMS-normalised in LDS (section 2.3.3); ROUTED / SHARED read
 //             the already normalised rows of the MoE path.
-//   loop over hidden chunks of HC = 64:
+//   loop over hidden chunks of HC = 128:
 //     GEMM1   S_gate, S_up [BM, HC] = x_hat @ W_gate/up[:, chunk]   (MFMA)
 //     U       rho(silu(S_gate) * S_up) -> LDS (double buffered)
 //     GEMM2   O [BM, W] += U @ W_down[chunk, :]                    (MFMA)
@@ -17,31 +17,40 @@
 //             ROUTED: part[b, p, slot] = gate * O           (fp32)
 //             SHARED: out = rho(resid + O + sum_slot part [+ extra])
 //
-// Wave roles: GEMM1 splits the tile 2 (rows) x 2 (hidden) between the
-// waves; GEMM2 splits the W output columns 4 ways.  x_hat and U fragments
-// come from LDS; weight fragments are pre-packed so every lane issues one
-// 16-byte global load per fragment and each fragment is read by at most two
-// waves.  The O accumulator stays in registers for the whole K loop.
+// MFMA shape: v_mfma_f32_32x32x16_bf16 (measured on MI355X near the dense
+// bf16 rate even at one wave per SIMD; the 16x16x32 form reaches about half).
+// Wave roles: 8 waves (two per SIMD) as 2 (row halves) x 4 (columns). In
+// GEMM1 wave (wr, wc) owns hidden units [32wc, 32wc+32) of the chunk for its
+// BM/2 rows (a gate block and an up block, so silu(g)*u is lane-local); in
+// GEMM2 it owns output columns [W/4 * wc, W/4 * (wc+1)) of its rows.
+// x_hat and U fragments are read from LDS; weight fragments are pre-packed so
+// a wave reads each one with a single 16-byte load per lane (each fragment is
+// read by the two waves of a column).  The per-step weight fragments stream
+// through a register ring that runs ahead across the GEMM1 / GEMM2 phases
+// and across chunks.
 #include "tmx_internal.h"
 
 namespace tmx {
 
 namespace {
 
-constexpr int NT = 256;
-constexpr int HC = 64;          // hidden chunk
-constexpr int US = HC + 8;      // U row stride (elements); +16 B keeps rows on distinct banks
+constexpr int NT = 512;   // 8 waves
 
 template <int W>
 struct MlpShape {
-  static constexpr int BM = (W <= 256) ? 128 : 64;
-  static constexpr int XS = W + 8;            // x_hat row stride (elements)
-  static constexpr int KB1 = W / 32;          // GEMM1 k-steps
-  static constexpr int RB1 = BM / 32;         // GEMM1 16-row blocks per wave
-  static constexpr int RB2 = BM / 16;         // GEMM2 16-row blocks (all rows)
-  static constexpr int NBW = W / 64;          // GEMM2 16-col blocks per wave
-  static_assert(W % 64 == 0, "W must be a multiple of 64");
-  static_assert(KB1 % 2 == 0, "double buffer assumes an even number of k-steps");
+  static constexpr int BM = (W <= 256) ? 128 : 64;  // rows per workgroup
+  static constexpr int HC = MLP_HC;                 // hidden chunk
+  static constexpr int XS = W + 8;                  // x_hat row stride (+16 B: rows on distinct banks)
+  static constexpr int US = HC + 8;                 // U row stride
+  static constexpr int RBW = BM / 64;               // 32-row blocks per wave (half the rows)
+  static constexpr int NBO = W / 128;               // GEMM2 32-column blocks per wave
+  static constexpr int S1 = W / 16;                 // GEMM1 k-steps per chunk
+  static constexpr int S2 = HC / 16;                // GEMM2 k-steps per chunk
+  static constexpr int S = S1 + S2;
+  static constexpr int DEPTH = (W <= 512) ? 4 : 2;  // weight-fragment prefetch distance (steps)
+  static constexpr int NBR = NBO > 2 ? NBO : 2;     // fragments per step
+  static_assert(W % 128 == 0, "W must be a multiple of 128");
+  static_assert(S1 % DEPTH == 0 && S2 % DEPTH == 0, "ring slots must line up across phases and chunks");
 };
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
@@ -54,10 +63,15 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+__device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
 template <int W, int MODE>
 __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
   using S = MlpShape<W>;
-  constexpr int BM = S::BM, XS = S::XS, KB1 = S::KB1, RB1 = S::RB1, RB2 = S::RB2, NBW = S::NBW;
+  constexpr int BM = S::BM, XS = S::XS, US = S::US, RBW = S::RBW, NBO = S::NBO;
+  constexpr int S1 = S::S1, S2 = S::S2, NS = S::S, DEPTH = S::DEPTH, NBR = S::NBR, HC = S::HC;
 
   __shared__ __attribute__((aligned(16))) uint16_t xs[BM * XS];
   __shared__ __attribute__((aligned(16))) uint16_t us[2 * BM * US];
@@ -66,9 +80,12 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l16 = lane & 15;
-  const int q = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps addresses scalar
+  const int l32 = lane & 31;
+  const int h32 = lane >> 5;
+  const int wr = wave >> 2;                 // row half
+  const int wc = wave & 3;                  // column quarter
+  const int row0 = wr * (BM / 2);
 
   // ---- which tile: blocks of one position are kept on one XCD ------------
   // Workgroup i is dispatched to XCD i % 8; with P % 8 == 0 every XCD walks
@@ -112,6 +129,32 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
     rowb[r] = b;
     rowent[r] = ent;
   }
+
+  // ---- weight fragment stream -------------------------------------------------
+  const int NC = a.hidden / HC;
+  const int NBh = a.hidden / 32;            // hidden 32-blocks of the whole MLP
+  const int KBd = a.hidden / 16;            // GEMM2 k-steps over the whole hidden
+  const uint16_t* wgu = a.wgu + (size_t)group * NBh * (W / 16) * 2 * FRAG_ELEMS;
+  const uint16_t* wd = a.wd + (size_t)group * KBd * (W / 32) * FRAG_ELEMS;
+
+  uint4 ring[DEPTH][NBR];
+  // step s of chunk c: GEMM1 k-step s (< S1): gate and up fragments of hidden
+  // block 4c + wc; GEMM2 k-step s - S1: down fragments of this wave's columns
+  auto issue = [&](uint4* dst, int c, int s) {
+    if (s < S1) {
+      const uint16_t* f = wgu + ((size_t)((c * 4 + wc) * (W / 16) + s) * 2) * FRAG_ELEMS + lane * 8;
+      dst[0] = ldg16(f);
+      dst[1] = ldg16(f + FRAG_ELEMS);
+    } else {
+      const int kb = c * (HC / 16) + (s - S1);
+#pragma unroll
+      for (int j = 0; j < NBO; ++j)
+        dst[j] = ldg16(wd + ((size_t)kb * (W / 32) + wc * NBO + j) * FRAG_ELEMS + lane * 8);
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < DEPTH; ++s) issue(ring[s], 0, s);
+
   __syncthreads();
 
   // ---- prologue: rows -> LDS ------------------------------------------------
@@ -157,125 +200,102 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
   }
 
   // ---- main loop ---------------------------------------------------------------
-  const int NC = a.hidden / HC;
-  const int NBh = a.hidden / 16;            // hidden 16-blocks of the whole MLP
-  const int KB2 = a.hidden / 32;            // GEMM2 k-steps over the whole hidden
-  const uint16_t* wgu = a.wgu + (size_t)group * NBh * KB1 * 2 * FRAG_ELEMS;
-  const uint16_t* wd = a.wd + (size_t)group * KB2 * (W / 16) * FRAG_ELEMS;
-  const int wr = wave >> 1, wc = wave & 1;  // GEMM1 role
+  f32x16 oacc[RBW][NBO];
+#pragma unroll
+  for (int i = 0; i < RBW; ++i)
+#pragma unroll
+    for (int j = 0; j < NBO; ++j) oacc[i][j] = f32x16{};
 
-  f32x4 oacc[RB2][NBW];
-#pragma unroll
-  for (int i = 0; i < RB2; ++i)
-#pragma unroll
-    for (int j = 0; j < NBW; ++j) oacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // GEMM1 B fragments: [buf][nb2*2 + which]
-  uint4 b1[2][4];
-  uint4 b2[2][NBW];
-
-  auto load_b1 = [&](uint4* dst, int c, int kb) {
-#pragma unroll
-    for (int nb2 = 0; nb2 < 2; ++nb2) {
-      const int hb = c * 4 + wc * 2 + nb2;
-      const uint16_t* f = wgu + ((size_t)(hb * KB1 + kb) * 2) * FRAG_ELEMS + lane * 8;
-      dst[nb2 * 2 + 0] = ldg16(f);
-      dst[nb2 * 2 + 1] = ldg16(f + FRAG_ELEMS);
-    }
-  };
-  auto load_b2 = [&](int c) {
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int j = 0; j < NBW; ++j) {
-        const int kb = c * 2 + kb2;
-        const int nb = wave * NBW + j;
-        b2[kb2][j] = ldg16(wd + ((size_t)kb * (W / 16) + nb) * FRAG_ELEMS + lane * 8);
-      }
+  // refill a ring slot with the fragments of step s of chunk c (the step
+  // index may run past the chunk into the next one)
+  auto refill = [&](uint4* dst, int c, int s) {
+    if (s < NS)
+      issue(dst, c, s);
+    else if (c + 1 < NC)
+      issue(dst, c + 1, s - NS);
   };
 
-  load_b1(b1[0], 0, 0);
   for (int c = 0; c < NC; ++c) {
     uint16_t* ub = us + (c & 1) * BM * US;
-    f32x4 sg[RB1][2], su[RB1][2];
+    f32x16 sg[RBW], su[RBW];
 #pragma unroll
-    for (int i = 0; i < RB1; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        sg[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        su[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+    for (int i = 0; i < RBW; ++i) {
+      sg[i] = f32x16{};
+      su[i] = f32x16{};
+    }
 
+    // GEMM1: k-steps in groups of DEPTH so ring slots are compile-time
+    for (int g = 0; g < S1 / DEPTH; ++g) {
 #pragma unroll
-    for (int kb = 0; kb < KB1; ++kb) {
-      if (kb + 1 < KB1)
-        load_b1(b1[(kb + 1) & 1], c, kb + 1);
-      else
-        load_b2(c);
-      const uint4* bb = b1[kb & 1];
+      for (int d = 0; d < DEPTH; ++d) {
+        const int s = g * DEPTH + d;
 #pragma unroll
-      for (int rb = 0; rb < RB1; ++rb) {
-        const int row = wr * (BM / 2) + rb * 16 + l16;
-        const bf16x8 af = as_bf16x8(*reinterpret_cast<const uint4*>(&xs[row * XS + kb * 32 + q * 8]));
-#pragma unroll
-        for (int nb2 = 0; nb2 < 2; ++nb2) {
-          sg[rb][nb2] = mfma16x16x32(af, as_bf16x8(bb[nb2 * 2 + 0]), sg[rb][nb2]);
-          su[rb][nb2] = mfma16x16x32(af, as_bf16x8(bb[nb2 * 2 + 1]), su[rb][nb2]);
+        for (int rb = 0; rb < RBW; ++rb) {
+          const uint4 af = *reinterpret_cast<const uint4*>(&xs[(row0 + rb * 32 + l32) * XS + s * 16 + h32 * 8]);
+          sg[rb] = mfma32(af, ring[d][0], sg[rb]);
+          su[rb] = mfma32(af, ring[d][1], su[rb]);
         }
+        refill(ring[d], c, s + DEPTH);
       }
     }
 
-    // U = rho(silu(gate) * up) into LDS; C layout: lane holds rows 4q+v, col l16
+    // U = rho(silu(gate) * up); C layout of 32x32: lane holds column l32,
+    // rows 8*(v/4) + 4*h32 + v%4 of each 32-row block
 #pragma unroll
-    for (int rb = 0; rb < RB1; ++rb)
+    for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-      for (int nb2 = 0; nb2 < 2; ++nb2)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = wr * (BM / 2) + rb * 16 + q * 4 + v;
-          const int col = (wc * 2 + nb2) * 16 + l16;
-          ub[row * US + col] = f2bf(silu(sg[rb][nb2][v]) * su[rb][nb2][v]);
-        }
+      for (int v = 0; v < 16; ++v) {
+        const int row = row0 + rb * 32 + 8 * (v >> 2) + 4 * h32 + (v & 3);
+        ub[row * US + wc * 32 + l32] = f2bf(silu(sg[rb][v]) * su[rb][v]);
+      }
     __syncthreads();
 
-    if (c + 1 < NC) load_b1(b1[0], c + 1, 0);
-
+    // GEMM2: O += U @ W_down[chunk]
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+    for (int g = 0; g < S2 / DEPTH; ++g) {
 #pragma unroll
-      for (int rb = 0; rb < RB2; ++rb) {
-        const int row = rb * 16 + l16;
-        const bf16x8 af = as_bf16x8(*reinterpret_cast<const uint4*>(&ub[row * US + kb2 * 32 + q * 8]));
+      for (int d = 0; d < DEPTH; ++d) {
+        const int k2 = g * DEPTH + d;
 #pragma unroll
-        for (int j = 0; j < NBW; ++j) oacc[rb][j] = mfma16x16x32(af, as_bf16x8(b2[kb2][j]), oacc[rb][j]);
+        for (int rb = 0; rb < RBW; ++rb) {
+          const uint4 af = *reinterpret_cast<const uint4*>(&ub[(row0 + rb * 32 + l32) * US + k2 * 16 + h32 * 8]);
+#pragma unroll
+          for (int j = 0; j < NBO; ++j) oacc[rb][j] = mfma32(af, ring[d][j], oacc[rb][j]);
+        }
+        refill(ring[d], c, S1 + k2 + DEPTH);
       }
     }
   }
 
   // ---- epilogue ----------------------------------------------------------------
+  // column part of the block-layout offset, once per output column block
+  int64_t coloff[NBO];
 #pragma unroll
-  for (int rb = 0; rb < RB2; ++rb)
+  for (int j = 0; j < NBO; ++j) coloff[j] = a.map.offset(0, p, (wc * NBO + j) * 32 + l32);
+  const int64_t rowstride = (int64_t)a.map.T * a.map.D;
+
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = rb * 16 + q * 4 + v;
+  for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = row0 + rb * 32 + 8 * (v >> 2) + 4 * h32 + (v & 3);
       const int b = rowb[r];
       if (b < 0) continue;
       if (MODE == MLP_ROUTED) {
-        const int ent = rowent[r];
-        const int s = ent - b * a.top_k;
+        const int s = rowent[r] - b * a.top_k;
         const size_t gi = ((size_t)b * a.P + p) * a.top_k + s;
         const float g = a.gate[gi];
-        float* dst = a.part + gi * W;
+        float* dst = a.part + gi * W + wc * NBO * 32 + l32;
 #pragma unroll
-        for (int j = 0; j < NBW; ++j) dst[(wave * NBW + j) * 16 + l16] = g * oacc[rb][j][v];
+        for (int j = 0; j < NBO; ++j) dst[j * 32] = g * oacc[rb][j][v];
       } else {
+        const int64_t rbase = (int64_t)b * rowstride;
 #pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-          const int col = (wave * NBW + j) * 16 + l16;
-          const int64_t off = a.map.offset(b, p, col);
+        for (int j = 0; j < NBO; ++j) {
+          const int64_t off = rbase + coloff[j];
           float val = oacc[rb][j][v];
           if (MODE == MLP_SHARED) {
-            const float* src = a.part + ((size_t)b * a.P + p) * a.top_k * W + col;
+            const float* src = a.part + ((size_t)b * a.P + p) * a.top_k * W + (wc * NBO + j) * 32 + l32;
             for (int s = 0; s < a.top_k; ++s) val += src[(size_t)s * W];
           }
           val += bf2f(a.resid[off]);

@@ -189,30 +189,32 @@ __global__ __launch_bounds__(BK_NT) void bucket_kernel(const BucketArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// pack: row-major [G][K][N] bf16 -> MFMA B-operand fragments (16x16x32):
-// fragment (k-block kb of 32, n-block nb of 16), lane = 16*(kk/8) + nn,
-// element i = kk % 8.
+// pack: row-major [G][K][N] bf16 -> MFMA B-operand fragments.
+//   FRAG_16x16x32: k-block 32, n-block 16, lane = 16*(kk/8) + nn
+//   FRAG_32x32x16: k-block 16, n-block 32, lane = 32*(kk/8) + nn
+// element i = kk % 8 within the lane's 16 bytes.
 //   layout 0: frag = ((g*NB + nb)*KB + kb)*2 + which   (gate|up interleaved)
 //   layout 1: frag = (g*KB + kb)*NB + nb               (down, router)
 // ---------------------------------------------------------------------------
 __global__ void pack_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int G, int K,
-                            int N, int layout, int which) {
+                            int N, int layout, int which, int frag32) {
   const int64_t total = (int64_t)G * K * N;
-  const int KB = K / 32, NB = N / 16;
+  const int KF = frag32 ? 16 : 32, NF = frag32 ? 32 : 16;
+  const int KB = K / KF, NB = N / NF;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int n = (int)(i % N);
     const int64_t gk = i / N;
     const int k = (int)(gk % K);
     const int g = (int)(gk / K);
-    const int kb = k >> 5, kk = k & 31, nb = n >> 4, nn = n & 15;
-    const int lane = (kk >> 3) * 16 + nn, e = kk & 7;
-    int64_t frag;
+    const int kb = k / KF, kk = k % KF, nb = n / NF, nn = n % NF;
+    const int lane = (kk >> 3) * NF + nn, e = kk & 7;
+    int64_t f;
     if (layout == 0)
-      frag = (((int64_t)g * NB + nb) * KB + kb) * 2 + which;
+      f = (((int64_t)g * NB + nb) * KB + kb) * 2 + which;
     else
-      frag = ((int64_t)g * KB + kb) * NB + nb;
-    dst[frag * FRAG_ELEMS + lane * 8 + e] = src[i];
+      f = ((int64_t)g * KB + kb) * NB + nb;
+    dst[f * FRAG_ELEMS + lane * 8 + e] = src[i];
   }
 }
 
@@ -265,10 +267,11 @@ hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int G, int K, int N, int layout, int which,
-                       hipStream_t s) {
+                       int frag, hipStream_t s) {
   const int64_t total = (int64_t)G * K * N;
   const int64_t blocks = std::min<int64_t>((total + 255) / 256, 65536);
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, G, K, N, layout, which);
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, G, K, N, layout, which,
+                     frag == FRAG_32x32x16 ? 1 : 0);
   return hipGetLastError();
 }
 

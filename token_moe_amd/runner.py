@@ -27,8 +27,14 @@ def torch_dtype(wl):
 
 
 def host_tensor(wl, a: np.ndarray):
-    """fp32 numpy array of dtype-representable values -> contiguous CPU torch tensor."""
+    """Numpy array -> contiguous CPU torch tensor of the workload dtype.
+    uint16 arrays are taken as bf16 bit patterns; float arrays as values
+    (already representable in the workload dtype)."""
     import torch
+    if a.dtype == np.uint16:
+        if wl.dtype != "bf16":
+            raise ValueError("bf16 bit patterns given for a non-bf16 workload")
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch_dtype(wl)).contiguous()
 
 
