@@ -47,10 +47,12 @@ struct MlpShape {
   static constexpr int S1 = W / 16;                 // GEMM1 k-steps per chunk
   static constexpr int S2 = HC / 16;                // GEMM2 k-steps per chunk
   static constexpr int S = S1 + S2;
-  static constexpr int DEPTH = (W <= 512) ? 4 : 2;  // weight-fragment prefetch distance (steps)
+  static constexpr int DEPTH = (W <= 256) ? 8 : (W <= 512) ? 4 : 2;  // weight prefetch distance (steps)
   static constexpr int NBR = NBO > 2 ? NBO : 2;     // fragments per step
+  static constexpr int YS = (S1 - S2) / 2;          // ping-pong barrier step inside GEMM1
   static_assert(W % 128 == 0, "W must be a multiple of 128");
-  static_assert(S1 % DEPTH == 0 && S2 % DEPTH == 0, "ring slots must line up across phases and chunks");
+  static_assert(S1 % DEPTH == 0 && S2 % DEPTH == 0 && DEPTH % 2 == 0,
+                "ring slots must line up across phases and chunks");
 };
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
@@ -67,11 +69,25 @@ __device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+
+// silu(z) = z * sigmoid(z) with the hardware exp and reciprocal (~1 ulp
+// each); the result is rounded to bf16 right after, so this is exact enough.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
 template <int W, int MODE>
 __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
   using S = MlpShape<W>;
   constexpr int BM = S::BM, XS = S::XS, US = S::US, RBW = S::RBW, NBO = S::NBO;
-  constexpr int S1 = S::S1, S2 = S::S2, NS = S::S, DEPTH = S::DEPTH, NBR = S::NBR, HC = S::HC;
+  constexpr int S1 = S::S1, S2 = S::S2, NS = S::S, DEPTH = S::DEPTH, NBR = S::NBR, HC = S::HC, YS = S::YS;
 
   __shared__ __attribute__((aligned(16))) uint16_t xs[BM * XS];
   __shared__ __attribute__((aligned(16))) uint16_t us[2 * BM * US];
@@ -157,46 +173,114 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
 
   __syncthreads();
 
-  // ---- prologue: rows -> LDS ------------------------------------------------
+  // ---- prologue: rows -> LDS (all of a lane's loads in flight at once) ------
+  // Unit u = (row, 8 columns); lane-consecutive units cover one row, so for
+  // DENSE the RMS statistics reduce across those lanes before x_hat is
+  // written (RMSNorm in fp32, rho to bf16: TokenMixer-Large section 2.3.3).
   constexpr int U8 = W / 8;
-  for (int u = tid; u < BM * U8; u += NT) {
-    const int r = u / U8, c8 = u - r * U8;
-    const int b = rowb[r];
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (b >= 0) {
-      if (MODE == MLP_DENSE)
-        v = ldg16(a.x + a.map.offset(b, p, c8 * 8));
-      else
-        v = ldg16(a.xhat + ((size_t)p * a.B + b) * W + c8 * 8);
-    }
-    *reinterpret_cast<uint4*>(&xs[r * XS + c8 * 8]) = v;
-  }
-  __syncthreads();
-
-  if (MODE == MLP_DENSE) {
-    // RMSNorm per row (fp32 statistics), rho to bf16, in place.
-    for (int r = wave; r < BM; r += NT / 64) {
-      float ss = 0.f;
-      for (int c8 = lane; c8 < U8; c8 += 64) {
-        const uint4 v = *reinterpret_cast<const uint4*>(&xs[r * XS + c8 * 8]);
-        const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
+  constexpr int NPRO = BM * U8 / NT;
+  static_assert((BM * U8) % NT == 0, "prologue units must divide evenly");
+  {
+    uint4 v[NPRO];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float f = bf2f(h[i]);
-          ss += f * f;
+    for (int i = 0; i < NPRO; ++i) {
+      const int u = tid + i * NT;
+      const int r = u / U8, c8 = u - r * U8;
+      const int b = rowb[r];
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (b >= 0) {
+        if (MODE == MLP_DENSE)
+          v[i] = ldg16(a.x + a.map.offset(b, p, c8 * 8));
+        else
+          v[i] = ldg16(a.xhat + ((size_t)p * a.B + b) * W + c8 * 8);
+      }
+    }
+    constexpr bool kFusedNorm = (U8 <= 64 || U8 % 64 == 0);
+    if constexpr (MODE == MLP_DENSE && kFusedNorm) {
+      // lanes per row within a wave (U8 <= 64) or waves per row (U8 > 64)
+      constexpr int LPR = U8 < 64 ? U8 : 64;
+      constexpr int WPR = U8 > 64 ? U8 / 64 : 1;
+      float ss[NPRO];
+#pragma unroll
+      for (int i = 0; i < NPRO; ++i) {
+        const uint16_t* h = reinterpret_cast<const uint16_t*>(&v[i]);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = bf2f(h[e]);
+          acc += f * f;
+        }
+#pragma unroll
+        for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+        ss[i] = acc;
+      }
+      if (WPR > 1) {
+        // rows wider than a wave: combine the per-wave partial sums in LDS
+        float* red = reinterpret_cast<float*>(us);      // U region is free until GEMM1
+#pragma unroll
+        for (int i = 0; i < NPRO; ++i)
+          if (lane == 0) red[i * (NT / 64) + wave] = ss[i];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NPRO; ++i) {
+          const int w0 = (wave / WPR) * WPR;
+          float t = 0.f;
+          for (int w = 0; w < WPR; ++w) t += red[i * (NT / 64) + w0 + w];
+          ss[i] = t;
         }
       }
-      ss = wave_sum(ss);
-      const float rinv = 1.0f / sqrtf(ss / (float)W + a.eps);
-      for (int c8 = lane; c8 < U8; c8 += 64) {
-        uint4 v = *reinterpret_cast<const uint4*>(&xs[r * XS + c8 * 8]);
-        uint16_t* h = reinterpret_cast<uint16_t*>(&v);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = f2bf(bf2f(h[i]) * rinv * a.gain[c8 * 8 + i]);
-        *reinterpret_cast<uint4*>(&xs[r * XS + c8 * 8]) = v;
+      for (int i = 0; i < NPRO; ++i) {
+        const int u = tid + i * NT;
+        const int c8 = u % U8;
+        const float rinv = 1.0f / sqrtf(ss[i] / (float)W + a.eps);
+        uint16_t* h = reinterpret_cast<uint16_t*>(&v[i]);
+        float n[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) n[e] = bf2f(h[e]) * rinv * a.gain[c8 * 8 + e];
+        v[i].x = pack_bf16x2(n[0], n[1]);
+        v[i].y = pack_bf16x2(n[2], n[3]);
+        v[i].z = pack_bf16x2(n[4], n[5]);
+        v[i].w = pack_bf16x2(n[6], n[7]);
       }
     }
+#pragma unroll
+    for (int i = 0; i < NPRO; ++i) {
+      const int u = tid + i * NT;
+      const int r = u / U8, c8 = u - r * U8;
+      *reinterpret_cast<uint4*>(&xs[r * XS + c8 * 8]) = v[i];
+    }
     __syncthreads();
+    if constexpr (MODE == MLP_DENSE && !kFusedNorm) {
+      // rows that do not tile waves: one wave per row, in place in LDS
+      for (int r = wave; r < BM; r += NT / 64) {
+        float acc = 0.f;
+        for (int c8 = lane; c8 < U8; c8 += 64) {
+          const uint4 q = *reinterpret_cast<const uint4*>(&xs[r * XS + c8 * 8]);
+          const uint16_t* h = reinterpret_cast<const uint16_t*>(&q);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float f = bf2f(h[e]);
+            acc += f * f;
+          }
+        }
+        acc = wave_sum(acc);
+        const float rinv = 1.0f / sqrtf(acc / (float)W + a.eps);
+        for (int c8 = lane; c8 < U8; c8 += 64) {
+          uint4 q = *reinterpret_cast<const uint4*>(&xs[r * XS + c8 * 8]);
+          const uint16_t* h = reinterpret_cast<const uint16_t*>(&q);
+          float n[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) n[e] = bf2f(h[e]) * rinv * a.gain[c8 * 8 + e];
+          q.x = pack_bf16x2(n[0], n[1]);
+          q.y = pack_bf16x2(n[2], n[3]);
+          q.z = pack_bf16x2(n[4], n[5]);
+          q.w = pack_bf16x2(n[6], n[7]);
+          *reinterpret_cast<uint4*>(&xs[r * XS + c8 * 8]) = q;
+        }
+      }
+      __syncthreads();
+    }
   }
 
   // ---- main loop ---------------------------------------------------------------
@@ -215,6 +299,16 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
       issue(dst, c + 1, s - NS);
   };
 
+  // Ping-pong of the two row groups (wr = 0: A, wr = 1: B). Each chunk is
+  //   GEMM1 steps [0, YS) | barrier Y | GEMM1 steps [YS, S1) + U | barrier X | GEMM2
+  // and group B runs one extra barrier before the loop, group A one after it,
+  // so A's X pairs with B's Y and A's Y with B's X: while one group computes
+  // silu(gate)*up on the VALU, the other group's waves on the same SIMDs keep
+  // the MFMA pipe busy. Each group reads only its own U rows, after its own X
+  // barrier; a U buffer is rewritten only after the next Y barrier, which every
+  // wave reaches after finishing its GEMM2 reads.
+  if (wr == 1) __syncthreads();
+
   for (int c = 0; c < NC; ++c) {
     uint16_t* ub = us + (c & 1) * BM * US;
     f32x16 sg[RBW], su[RBW];
@@ -224,86 +318,154 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
       su[i] = f32x16{};
     }
 
-    // GEMM1: k-steps in groups of DEPTH so ring slots are compile-time
-    for (int g = 0; g < S1 / DEPTH; ++g) {
-#pragma unroll
-      for (int d = 0; d < DEPTH; ++d) {
-        const int s = g * DEPTH + d;
-#pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) {
-          const uint4 af = *reinterpret_cast<const uint4*>(&xs[(row0 + rb * 32 + l32) * XS + s * 16 + h32 * 8]);
-          sg[rb] = mfma32(af, ring[d][0], sg[rb]);
-          su[rb] = mfma32(af, ring[d][1], su[rb]);
-        }
-        refill(ring[d], c, s + DEPTH);
-      }
-    }
-
-    // U = rho(silu(gate) * up); C layout of 32x32: lane holds column l32,
-    // rows 8*(v/4) + 4*h32 + v%4 of each 32-row block
+    // GEMM1 (fully unrolled: ring slots and the barrier point are
+    // compile-time). The x_hat fragments of step s+1 are read from LDS while
+    // step s runs; sched_barrier pins each step's loads where they are issued.
+    uint4 xa[2][RBW];
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb)
+      xa[0][rb] = *reinterpret_cast<const uint4*>(&xs[(row0 + rb * 32 + l32) * XS + h32 * 8]);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = row0 + rb * 32 + 8 * (v >> 2) + 4 * h32 + (v & 3);
-        ub[row * US + wc * 32 + l32] = f2bf(silu(sg[rb][v]) * su[rb][v]);
+    for (int s = 0; s < S1; ++s) {
+      if (s == YS) __syncthreads();                              // barrier Y
+      const int d = s % DEPTH;
+      if (s + 1 < S1) {
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb)
+          xa[(s + 1) & 1][rb] =
+              *reinterpret_cast<const uint4*>(&xs[(row0 + rb * 32 + l32) * XS + (s + 1) * 16 + h32 * 8]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) {
+        // S^T = W^T x_hat^T: the packed weight fragment is the A operand
+        // (W^T rows = hidden units) and the x_hat rows are the B operand
+        sg[rb] = mfma32(ring[d][0], xa[s & 1][rb], sg[rb]);
+        su[rb] = mfma32(ring[d][1], xa[s & 1][rb], su[rb]);
+      }
+      refill(ring[d], c, s + DEPTH);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // U = rho(silu(gate) * up). C layout of S^T (32 hidden x 32 rows): lane
+    // holds row l32 and hidden 8*(v/4) + 4*h32 + v%4, i.e. 4 consecutive
+    // hidden units per v-group -> one 8-byte LDS store each
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      const int row = row0 + rb * 32 + l32;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        float uv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) uv[i] = silu_fast(sg[rb][4 * g4 + i]) * su[rb][4 * g4 + i];
+        uint2 w2;
+        w2.x = pack_bf16x2(uv[0], uv[1]);
+        w2.y = pack_bf16x2(uv[2], uv[3]);
+        *reinterpret_cast<uint2*>(&ub[row * US + wc * 32 + 8 * g4 + 4 * h32]) = w2;
+      }
+    }
     __syncthreads();
 
-    // GEMM2: O += U @ W_down[chunk]
+    // GEMM2: O^T += W_down[chunk]^T U^T, U fragments read one step ahead
+    uint4 ua[2][RBW];
 #pragma unroll
-    for (int g = 0; g < S2 / DEPTH; ++g) {
+    for (int rb = 0; rb < RBW; ++rb)
+      ua[0][rb] = *reinterpret_cast<const uint4*>(&ub[(row0 + rb * 32 + l32) * US + h32 * 8]);
 #pragma unroll
-      for (int d = 0; d < DEPTH; ++d) {
-        const int k2 = g * DEPTH + d;
+    for (int k2 = 0; k2 < S2; ++k2) {
+      const int d = (S1 + k2) % DEPTH;
+      if (k2 + 1 < S2) {
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) {
-          const uint4 af = *reinterpret_cast<const uint4*>(&ub[(row0 + rb * 32 + l32) * US + k2 * 16 + h32 * 8]);
+        for (int rb = 0; rb < RBW; ++rb)
+          ua[(k2 + 1) & 1][rb] =
+              *reinterpret_cast<const uint4*>(&ub[(row0 + rb * 32 + l32) * US + (k2 + 1) * 16 + h32 * 8]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int j = 0; j < NBO; ++j) oacc[rb][j] = mfma32(af, ring[d][j], oacc[rb][j]);
+      for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+        for (int j = 0; j < NBO; ++j) oacc[rb][j] = mfma32(ring[d][j], ua[k2 & 1][rb], oacc[rb][j]);   // O^T block
+      refill(ring[d], c, S1 + k2 + DEPTH);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (wr == 0) __syncthreads();
+
+  // ---- epilogue ----------------------------------------------------------------
+  // O goes through LDS (the x_hat region, free now) one row half at a time,
+  // so every global access is a 16-byte vector: residual / extra / output
+  // through the row map (8 consecutive columns never straddle a Mix
+  // segment since D/H % 8 == 0), partials as fp32 rows.
+  // stage row stride SS = W + 4 floats: 16 consecutive rows land on distinct
+  // 16-byte bank groups for the 16-byte writes below
+  constexpr int SS = W + 4;
+  static_assert((BM / 2) * SS * 4 <= BM * XS * 2, "stage must fit in the x_hat region");
+  float* stage = reinterpret_cast<float*>(xs);
+#pragma unroll 1
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();
+    if (wr == half) {
+      // C layout of an O^T block (32 columns x 32 rows): lane holds row l32 and
+      // columns 8*(v/4) + 4*h32 + v%4 -> 4 consecutive columns per v-group
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+        for (int j = 0; j < NBO; ++j)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int r = rb * 32 + l32;
+            const int col = (wc * NBO + j) * 32 + 8 * g4 + 4 * h32;
+            *reinterpret_cast<float4*>(&stage[r * SS + col]) =
+                make_float4(oacc[rb][j][4 * g4], oacc[rb][j][4 * g4 + 1], oacc[rb][j][4 * g4 + 2],
+                            oacc[rb][j][4 * g4 + 3]);
+          }
+    }
+    __syncthreads();
+    for (int u = tid; u < (BM / 2) * U8; u += NT) {
+      const int r = u / U8, c8 = u - r * U8;
+      const int R = half * (BM / 2) + r;
+      const int b = rowb[R];
+      if (b < 0) continue;
+      const float4 o0 = *reinterpret_cast<const float4*>(&stage[r * SS + c8 * 8]);
+      const float4 o1 = *reinterpret_cast<const float4*>(&stage[r * SS + c8 * 8 + 4]);
+      float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+      if (MODE == MLP_ROUTED) {
+        const int slot = rowent[R] - b * a.top_k;
+        const size_t gi = ((size_t)b * a.P + p) * a.top_k + slot;
+        const float g = a.gate[gi];
+        float4* dst = reinterpret_cast<float4*>(a.part + gi * W + c8 * 8);
+        dst[0] = make_float4(g * o[0], g * o[1], g * o[2], g * o[3]);
+        dst[1] = make_float4(g * o[4], g * o[5], g * o[6], g * o[7]);
+      } else {
+        if (MODE == MLP_SHARED) {
+          const float* src = a.part + ((size_t)b * a.P + p) * a.top_k * W + c8 * 8;
+          for (int sl = 0; sl < a.top_k; ++sl) {
+            const float4 q0 = *reinterpret_cast<const float4*>(src + (size_t)sl * W);
+            const float4 q1 = *reinterpret_cast<const float4*>(src + (size_t)sl * W + 4);
+            o[0] += q0.x; o[1] += q0.y; o[2] += q0.z; o[3] += q0.w;
+            o[4] += q1.x; o[5] += q1.y; o[6] += q1.z; o[7] += q1.w;
+          }
         }
-        refill(ring[d], c, S1 + k2 + DEPTH);
+        const int64_t off = a.map.offset(b, p, c8 * 8);
+        const uint4 rv = ldg16(a.resid + off);
+        const uint16_t* rh = reinterpret_cast<const uint16_t*>(&rv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] += bf2f(rh[i]);
+        if (a.extra) {
+          const uint4 ev = ldg16(a.extra + off);
+          const uint16_t* eh = reinterpret_cast<const uint16_t*>(&ev);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[i] += bf2f(eh[i]);
+        }
+        uint4 w;
+        w.x = pack_bf16x2(o[0], o[1]);
+        w.y = pack_bf16x2(o[2], o[3]);
+        w.z = pack_bf16x2(o[4], o[5]);
+        w.w = pack_bf16x2(o[6], o[7]);
+        *reinterpret_cast<uint4*>(a.out + off) = w;
       }
     }
   }
-
-  // ---- epilogue ----------------------------------------------------------------
-  // column part of the block-layout offset, once per output column block
-  int64_t coloff[NBO];
-#pragma unroll
-  for (int j = 0; j < NBO; ++j) coloff[j] = a.map.offset(0, p, (wc * NBO + j) * 32 + l32);
-  const int64_t rowstride = (int64_t)a.map.T * a.map.D;
-
-#pragma unroll
-  for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = row0 + rb * 32 + 8 * (v >> 2) + 4 * h32 + (v & 3);
-      const int b = rowb[r];
-      if (b < 0) continue;
-      if (MODE == MLP_ROUTED) {
-        const int s = rowent[r] - b * a.top_k;
-        const size_t gi = ((size_t)b * a.P + p) * a.top_k + s;
-        const float g = a.gate[gi];
-        float* dst = a.part + gi * W + wc * NBO * 32 + l32;
-#pragma unroll
-        for (int j = 0; j < NBO; ++j) dst[j * 32] = g * oacc[rb][j][v];
-      } else {
-        const int64_t rbase = (int64_t)b * rowstride;
-#pragma unroll
-        for (int j = 0; j < NBO; ++j) {
-          const int64_t off = rbase + coloff[j];
-          float val = oacc[rb][j][v];
-          if (MODE == MLP_SHARED) {
-            const float* src = a.part + ((size_t)b * a.P + p) * a.top_k * W + (wc * NBO + j) * 32 + l32;
-            for (int s = 0; s < a.top_k; ++s) val += src[(size_t)s * W];
-          }
-          val += bf2f(a.resid[off]);
-          if (a.extra) val += bf2f(a.extra[off]);
-          a.out[off] = f2bf(val);
-        }
-      }
-    }
 }
 
 template <int W>
