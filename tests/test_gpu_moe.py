@@ -251,3 +251,59 @@ def test_moe_stack_full_batch_sampled():
     say("moe stack err", err)
     assert err <= TOL["bf16"]
     drop("w4")
+
+
+# ---------------------------------------------------------------------------
+# the large MoE stack (B=8192, T=H=32, D=768, E=32, ~15.4e9 weights) at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("sub", [0, 1])
+def test_large_moe_sublayer_and_route_full_batch(sub):
+    require_gpu()
+    import torch
+    wl = dg.WORKLOADS[5]
+    say("large moe: generating / uploading weights (first use)", sub)
+    ctx, banks, ws = context("w5", wl)
+    x = dg.make_x(wl)
+    xd = to_dev(wl, x)
+    # routing of sampled rows, teacher-forced on the same input
+    idx_g, gate_g = _route_gpu(ctx, wl, 0, sub, xd, wl.B)
+    rows = sample_rows(wl.B, 192, seed=50 + sub)
+    idx_o, gate_o, logits, bound = _route_oracle(wl, ws, 1, sub, x[rows].astype(np.float64))
+    nb = _check_routing(wl, idx_g[rows], gate_g[rows], idx_o, gate_o, logits, bound)
+    say("large route banded rows", sub, nb)
+    # one sub-layer at the full batch, oracle on sampled rows
+    out = torch.empty_like(xd)
+    rows = sample_rows(wl.B, 10, seed=60 + sub)
+    if sub == 0:
+        ctx.sublayer_forward(0, 0, xd, None, None, out, wl.B, stream())
+        torch.cuda.synchronize()
+        ref = oracle_sublayer(wl, ws, 1, 0, x[rows].astype(np.float64))
+    else:
+        xr = to_dev(wl, dg.make_x(wl, seed=wl.seed + 100))
+        ctx.sublayer_forward(0, 1, xr, xd, None, out, wl.B, stream())
+        torch.cuda.synchronize()
+        ref = oracle_sublayer(wl, ws, 1, 1, to_np(xr)[rows], x[rows].astype(np.float64))
+    err = row_err(to_np(out)[rows], ref)
+    say("large moe sublayer err", sub, err)
+    assert err <= TOL["bf16"]
+
+
+def test_large_moe_stack_full_batch_sampled():
+    require_gpu()
+    import torch
+    wl = dg.WORKLOADS[5]
+    ctx, banks, ws = context("w5", wl)
+    x = dg.make_x(wl)
+    xd = to_dev(wl, x)
+    y = torch.empty_like(xd)
+    ctx.block_stack_forward(xd, y, wl.B, stream())
+    torch.cuda.synchronize()
+    yn = to_np(y)
+    assert np.all(np.isfinite(yn[::97]))
+    rows = sample_rows(wl.B, 3, seed=70)
+    ref = orc.stack_forward(x[rows].astype(np.float64), wl, ws)
+    err = row_err(yn[rows], ref)
+    say("large moe stack err", err)
+    assert err <= TOL["bf16"]
+    drop("w5")
