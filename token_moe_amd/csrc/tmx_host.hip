@@ -30,6 +30,7 @@ struct Bank {
 struct tmx_ctx {
   tmx_config cfg{};
   int device = 0;
+  int workers = 0;              // persistent-kernel grid: compute units on the device
   float alpha = 0.f;
   std::vector<Bank> banks;      // [L][2][NKINDS]
   // workspace
@@ -244,7 +245,7 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
     a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_GATE).ptr);
     a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_DOWN).ptr);
     a.rtiles = (B + bm - 1) / bm;
-    return check_launch(c, launch_mlp(MLP_DENSE, W, a, P * a.rtiles, st), "dense MLP launch");
+    return check_launch(c, launch_mlp(MLP_DENSE, W, a, P * a.rtiles, c->workers, st), "dense MLP launch");
   }
 
   // MoE: norm + route -> bucket -> routed experts -> shared expert + combine
@@ -267,14 +268,14 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   a.hidden = cfg.expert_hidden;
   a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_EXP_GATE).ptr);
   a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_EXP_DOWN).ptr);
-  s = check_launch(c, launch_mlp(MLP_ROUTED, W, a, P * a.max_tiles, st), "routed MLP launch");
+  s = check_launch(c, launch_mlp(MLP_ROUTED, W, a, P * a.max_tiles, 0, st), "routed MLP launch");
   if (s != TMX_OK) return s;
 
   a.hidden = cfg.shared_hidden;
   a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_SH_GATE).ptr);
   a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_SH_DOWN).ptr);
   a.rtiles = (B + bm - 1) / bm;
-  return check_launch(c, launch_mlp(MLP_SHARED, W, a, P * a.rtiles, st), "shared MLP launch");
+  return check_launch(c, launch_mlp(MLP_SHARED, W, a, P * a.rtiles, c->workers, st), "shared MLP launch");
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -326,6 +327,10 @@ tmx_status tmx_create(const tmx_config* cfg, int device, tmx_ctx** out) {
   tmx_ctx* c = new tmx_ctx();
   c->cfg = *cfg;
   c->device = device;
+  if ((e = hipDeviceGetAttribute(&c->workers, hipDeviceAttributeMultiprocessorCount, device)) != hipSuccess) {
+    delete c;
+    return fail(nullptr, TMX_ERR_DEVICE, "compute-unit count: %s", hipGetErrorString(e));
+  }
   c->alpha = cfg->E > 0 ? (cfg->alpha != 0.f ? cfg->alpha : (float)cfg->E / (float)cfg->top_k) : 0.f;
   c->banks.resize((size_t)cfg->L * 2 * NKINDS);
   const tmx_config& C = c->cfg;

@@ -68,7 +68,9 @@ struct BucketArgs {
 // bf16 launchers (return hipError_t of the launch)
 int mlp_bm_for_width(int W);
 bool mlp_width_supported(int W);
-hipError_t launch_mlp(int mode, int W, const MlpArgs& a, int grid, hipStream_t s);
+// tiles = P * (rtiles or max_tiles); the grid is min(tiles, workers & ~7):
+// each workgroup walks tiles blockIdx.x, blockIdx.x + grid, ...
+hipError_t launch_mlp(int mode, int W, const MlpArgs& a, int tiles, int workers, hipStream_t s);
 hipError_t launch_norm_route(int W, const RouteArgs& a, hipStream_t s);
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
 // Repack G row-major [K, N] bf16 matrices into MFMA B-operand fragments of

@@ -88,11 +88,28 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
   using S = MlpShape<W>;
   constexpr int BM = S::BM, XS = S::XS, US = S::US, RBW = S::RBW, NBO = S::NBO;
   constexpr int S1 = S::S1, S2 = S::S2, NS = S::S, DEPTH = S::DEPTH, NBR = S::NBR, HC = S::HC, YS = S::YS;
+  constexpr int U8 = W / 8;                    // 16-byte units per row
+  constexpr int NPRO = BM * U8 / NT;           // row units per lane per tile
+  constexpr int NE = (BM / 2) * U8 / NT;       // per row half
+  static_assert((BM * U8) % NT == 0 && ((BM / 2) * U8) % NT == 0, "row units must divide evenly");
 
-  __shared__ __attribute__((aligned(16))) uint16_t xs[BM * XS];
-  __shared__ __attribute__((aligned(16))) uint16_t us[2 * BM * US];
-  __shared__ int rowb[BM];
-  __shared__ int rowent[BM];
+  // LDS: x_hat tile + two U buffers during the main loop; between tiles the
+  // same bytes hold the fp32 output tile (all rows at once when it fits in
+  // 160 KB, else one row half at a time). Stage row stride W + 4 floats: 16
+  // consecutive rows land on distinct 16-byte bank groups.
+  constexpr int XBYTES = BM * XS * 2, UBYTES = 2 * BM * US * 2;
+  constexpr int SS = W + 4;
+  constexpr int ROWTAB = 4 * BM * 4;
+  constexpr int NPART = (BM * SS * 4 + ROWTAB <= 160 * 1024) ? 1 : 2;
+  constexpr int SBYTES = (BM / NPART) * SS * 4;
+  constexpr int SMEM = (XBYTES + UBYTES > SBYTES) ? XBYTES + UBYTES : SBYTES;
+  static_assert(SMEM + ROWTAB <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  __shared__ int rowb[2][BM];
+  __shared__ int rowent[2][BM];
+  uint16_t* const xs = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* const us = reinterpret_cast<uint16_t*>(smem + XBYTES);
+  float* const stage = reinterpret_cast<float*>(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,102 +120,143 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
   const int wc = wave & 3;                  // column quarter
   const int row0 = wr * (BM / 2);
 
-  // ---- which tile: blocks of one position are kept on one XCD ------------
-  // Workgroup i is dispatched to XCD i % 8; with P % 8 == 0 every XCD walks
-  // the tiles of positions xcd, xcd + 8, ... so a position's weights stay in
-  // that XCD's L2.
+  // ---- tiles ------------------------------------------------------------------
+  // The kernel is persistent: workgroup i walks tiles i, i + G, i + 2G, ...
+  // (G = grid size, a multiple of 8 when there are more tiles than
+  // workgroups). Tile index j sits on XCD j % 8 -- the XCD that dispatches
+  // workgroup j % G -- and with P % 8 == 0 XCD x owns the contiguous
+  // positions [x*P/8, (x+1)*P/8): a position's weights stay in that XCD's L2,
+  // and neighbouring mixed positions, whose Mix segments share cache lines of
+  // the block-layout rows, are read and written by the same XCD.
   const int per_pos = (MODE == MLP_ROUTED) ? a.max_tiles : a.rtiles;
-  int p, t;
-  {
-    const int i = blockIdx.x;
+  const int total = a.P * per_pos;
+  struct Tile {
+    int p, t, group, start, nrows;
+  };
+  auto decode = [&](int j, Tile& T) -> bool {
     if ((a.P & 7) == 0) {
-      const int xcd = i & 7, j = i >> 3;
-      p = xcd + 8 * (j / per_pos);
-      t = j % per_pos;
+      const int xcd = j & 7, q = j >> 3;
+      T.p = xcd * (a.P >> 3) + q / per_pos;
+      T.t = q % per_pos;
     } else {
-      p = i / per_pos;
-      t = i % per_pos;
+      T.p = j / per_pos;
+      T.t = j % per_pos;
     }
-  }
-  int group = p, nrows, start;
-  if (MODE == MLP_ROUTED) {
-    if (t >= a.ntiles[p]) return;                       // uniform per workgroup
-    const int4 tl = a.tiles[(size_t)p * a.max_tiles + t];
-    group = p * a.E + tl.x;
-    start = tl.y;
-    nrows = tl.z;
-  } else {
-    start = t * BM;
-    nrows = min(BM, a.B - start);
-  }
-
-  for (int r = tid; r < BM; r += NT) {
-    int b = -1, ent = 0;
-    if (r < nrows) {
-      if (MODE == MLP_ROUTED) {
-        ent = a.rows[(size_t)p * a.B * a.top_k + start + r];
-        b = ent / a.top_k;
-      } else {
-        b = start + r;
+    if (MODE == MLP_ROUTED) {
+      if (T.t >= a.ntiles[T.p]) return false;
+      const int4 tl = a.tiles[(size_t)T.p * a.max_tiles + T.t];
+      T.group = T.p * a.E + tl.x;
+      T.start = tl.y;
+      T.nrows = tl.z;
+    } else {
+      T.group = T.p;
+      T.start = T.t * BM;
+      T.nrows = min(BM, a.B - T.start);
+    }
+    return true;
+  };
+  auto next_valid = [&](int j, Tile& T) -> int {
+    while (j < total && !decode(j, T)) j += gridDim.x;
+    return j;
+  };
+  auto set_rows = [&](const Tile& T, int buf) {
+    for (int r = tid; r < BM; r += NT) {
+      int b = -1, ent = 0;
+      if (r < T.nrows) {
+        if (MODE == MLP_ROUTED) {
+          ent = a.rows[(size_t)T.p * a.B * a.top_k + T.start + r];
+          b = ent / a.top_k;
+        } else {
+          b = T.start + r;
+        }
       }
+      rowb[buf][r] = b;
+      rowent[buf][r] = ent;
     }
-    rowb[r] = b;
-    rowent[r] = ent;
-  }
+  };
 
   // ---- weight fragment stream -------------------------------------------------
   const int NC = a.hidden / HC;
   const int NBh = a.hidden / 32;            // hidden 32-blocks of the whole MLP
   const int KBd = a.hidden / 16;            // GEMM2 k-steps over the whole hidden
-  const uint16_t* wgu = a.wgu + (size_t)group * NBh * (W / 16) * 2 * FRAG_ELEMS;
-  const uint16_t* wd = a.wd + (size_t)group * KBd * (W / 32) * FRAG_ELEMS;
-
+  struct Stream {
+    const uint16_t* gu;
+    const uint16_t* d;
+    int rot;
+  };
+  // Hidden chunks are visited in a rotated order (chunk (c + t) mod NC at
+  // iteration c, t = row tile): the sum over chunks is the same, and the
+  // workgroups of one position, which run side by side on one XCD, stream
+  // different parts of the weights.
+  auto bind = [&](const Tile& T) -> Stream {
+    return Stream{a.wgu + (size_t)T.group * NBh * (W / 16) * 2 * FRAG_ELEMS,
+                  a.wd + (size_t)T.group * KBd * (W / 32) * FRAG_ELEMS, T.t % NC};
+  };
   uint4 ring[DEPTH][NBR];
   // step s of chunk c: GEMM1 k-step s (< S1): gate and up fragments of hidden
   // block 4c + wc; GEMM2 k-step s - S1: down fragments of this wave's columns
-  auto issue = [&](uint4* dst, int c, int s) {
+  auto issue = [&](uint4* dst, const Stream& w, int c, int s) {
+    c += w.rot;
+    if (c >= NC) c -= NC;
     if (s < S1) {
-      const uint16_t* f = wgu + ((size_t)((c * 4 + wc) * (W / 16) + s) * 2) * FRAG_ELEMS + lane * 8;
+      const uint16_t* f = w.gu + ((size_t)((c * 4 + wc) * (W / 16) + s) * 2) * FRAG_ELEMS + lane * 8;
       dst[0] = ldg16(f);
       dst[1] = ldg16(f + FRAG_ELEMS);
     } else {
       const int kb = c * (HC / 16) + (s - S1);
 #pragma unroll
       for (int j = 0; j < NBO; ++j)
-        dst[j] = ldg16(wd + ((size_t)kb * (W / 32) + wc * NBO + j) * FRAG_ELEMS + lane * 8);
+        dst[j] = ldg16(w.d + ((size_t)kb * (W / 32) + wc * NBO + j) * FRAG_ELEMS + lane * 8);
     }
   };
-#pragma unroll
-  for (int s = 0; s < DEPTH; ++s) issue(ring[s], 0, s);
+  // refill a ring slot with the fragments of step s of chunk c; a step past
+  // the chunk end belongs to chunk c+1, and past the last chunk to chunk 0
+  // of the workgroup's next tile (or, after its last tile, to a chunk that
+  // is re-read and never used). The stream never stops and the loads are
+  // issued unconditionally, so the wait counters stay uniform: a conditional
+  // load here makes the compiler drain the whole ring (vmcnt(0)) at every
+  // chunk boundary.
+  Stream cw, nw;
+  auto refill = [&](uint4* dst, int c, int s) {
+    if (s >= NS) {
+      s -= NS;
+      const bool last = c + 1 >= NC;
+      Stream w;
+      w.gu = last ? nw.gu : cw.gu;
+      w.d = last ? nw.d : cw.d;
+      w.rot = last ? nw.rot : cw.rot;
+      issue(dst, w, last ? 0 : c + 1, s);
+    } else {
+      issue(dst, cw, c, s);
+    }
+  };
 
-  __syncthreads();
-
-  // ---- prologue: rows -> LDS (all of a lane's loads in flight at once) ------
-  // Unit u = (row, 8 columns); lane-consecutive units cover one row, so for
-  // DENSE the RMS statistics reduce across those lanes before x_hat is
-  // written (RMSNorm in fp32, rho to bf16: TokenMixer-Large section 2.3.3).
-  constexpr int U8 = W / 8;
-  constexpr int NPRO = BM * U8 / NT;
-  static_assert((BM * U8) % NT == 0, "prologue units must divide evenly");
-  {
-    uint4 v[NPRO];
+  // ---- row I/O ----------------------------------------------------------------
+  // Unit u = (row, 8 columns) of the tile; lane-consecutive units cover one
+  // row. Every global access of the rows is one 16-byte vector (8 columns
+  // never straddle a Mix segment since D/H % 8 == 0).
+  auto load_x = [&](int tix, int buf, const Tile& T, uint4* v) {
 #pragma unroll
     for (int i = 0; i < NPRO; ++i) {
-      const int u = tid + i * NT;
+      const int u = tix + i * NT;
       const int r = u / U8, c8 = u - r * U8;
-      const int b = rowb[r];
+      const int b = rowb[buf][r];
       v[i] = make_uint4(0, 0, 0, 0);
       if (b >= 0) {
         if (MODE == MLP_DENSE)
-          v[i] = ldg16(a.x + a.map.offset(b, p, c8 * 8));
+          v[i] = ldg16(a.x + a.map.offset(b, T.p, c8 * 8));
         else
-          v[i] = ldg16(a.xhat + ((size_t)p * a.B + b) * W + c8 * 8);
+          v[i] = ldg16(a.xhat + ((size_t)T.p * a.B + b) * W + c8 * 8);
       }
     }
+  };
+  // x rows -> LDS x_hat; for DENSE the RMS statistics reduce across the lanes
+  // of a row before x_hat is written (RMSNorm in fp32, rho to bf16:
+  // TokenMixer-Large section 2.3.3)
+  auto store_x = [&](int tix, uint4* v) {
     constexpr bool kFusedNorm = (U8 <= 64 || U8 % 64 == 0);
     if constexpr (MODE == MLP_DENSE && kFusedNorm) {
-      // lanes per row within a wave (U8 <= 64) or waves per row (U8 > 64)
-      constexpr int LPR = U8 < 64 ? U8 : 64;
+      constexpr int LPR = U8 < 64 ? U8 : 64;  // lanes per row within a wave
       constexpr int WPR = U8 > 64 ? U8 / 64 : 1;
       float ss[NPRO];
 #pragma unroll
@@ -216,7 +274,7 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
       }
       if (WPR > 1) {
         // rows wider than a wave: combine the per-wave partial sums in LDS
-        float* red = reinterpret_cast<float*>(us);      // U region is free until GEMM1
+        float* red = reinterpret_cast<float*>(us);
 #pragma unroll
         for (int i = 0; i < NPRO; ++i)
           if (lane == 0) red[i * (NT / 64) + wave] = ss[i];
@@ -228,13 +286,14 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
           for (int w = 0; w < WPR; ++w) t += red[i * (NT / 64) + w0 + w];
           ss[i] = t;
         }
+        __syncthreads();
       }
 #pragma unroll
       for (int i = 0; i < NPRO; ++i) {
-        const int u = tid + i * NT;
+        const int u = tix + i * NT;
         const int c8 = u % U8;
         const float rinv = 1.0f / sqrtf(ss[i] / (float)W + a.eps);
-        uint16_t* h = reinterpret_cast<uint16_t*>(&v[i]);
+        const uint16_t* h = reinterpret_cast<const uint16_t*>(&v[i]);
         float n[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) n[e] = bf2f(h[e]) * rinv * a.gain[c8 * 8 + e];
@@ -246,7 +305,7 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < NPRO; ++i) {
-      const int u = tid + i * NT;
+      const int u = tix + i * NT;
       const int r = u / U8, c8 = u - r * U8;
       *reinterpret_cast<uint4*>(&xs[r * XS + c8 * 8]) = v[i];
     }
@@ -281,190 +340,239 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
       }
       __syncthreads();
     }
-  }
-
-  // ---- main loop ---------------------------------------------------------------
-  f32x16 oacc[RBW][NBO];
+  };
+  // residual rows of the tile, same unit order as load_x
+  auto load_resid = [&](int tix, int buf, const Tile& T, uint4* rv) {
 #pragma unroll
-  for (int i = 0; i < RBW; ++i)
-#pragma unroll
-    for (int j = 0; j < NBO; ++j) oacc[i][j] = f32x16{};
-
-  // refill a ring slot with the fragments of step s of chunk c (the step
-  // index may run past the chunk into the next one)
-  auto refill = [&](uint4* dst, int c, int s) {
-    if (s < NS)
-      issue(dst, c, s);
-    else if (c + 1 < NC)
-      issue(dst, c + 1, s - NS);
+    for (int i = 0; i < NPRO; ++i) {
+      const int u = tix + i * NT;
+      const int r = u / U8, c8 = u - r * U8;
+      const int b = rowb[buf][r];
+      rv[i] = b >= 0 ? ldg16(a.resid + a.map.offset(b, T.p, c8 * 8)) : make_uint4(0, 0, 0, 0);
+    }
   };
 
-  // Ping-pong of the two row groups (wr = 0: A, wr = 1: B). Each chunk is
-  //   GEMM1 steps [0, YS) | barrier Y | GEMM1 steps [YS, S1) + U | barrier X | GEMM2
-  // and group B runs one extra barrier before the loop, group A one after it,
-  // so A's X pairs with B's Y and A's Y with B's X: while one group computes
-  // silu(gate)*up on the VALU, the other group's waves on the same SIMDs keep
-  // the MFMA pipe busy. Each group reads only its own U rows, after its own X
-  // barrier; a U buffer is rewritten only after the next Y barrier, which every
-  // wave reaches after finishing its GEMM2 reads.
-  if (wr == 1) __syncthreads();
+  // ---- first tile ---------------------------------------------------------------
+  Tile cur, nx;
+  int ci = next_valid(blockIdx.x, cur);
+  if (ci >= total) return;                                     // uniform per workgroup
+  int ni = next_valid(ci + gridDim.x, nx);
+  int buf = 0;
+  set_rows(cur, 0);
+  cw = bind(cur);
+  nw = ni < total ? bind(nx) : cw;
+#pragma unroll
+  for (int s = 0; s < DEPTH; ++s) issue(ring[s], cw, 0, s);
+  __syncthreads();
+  {
+    uint4 v[NPRO];
+    load_x(tid, 0, cur, v);
+    store_x(tid, v);
+  }
 
-  for (int c = 0; c < NC; ++c) {
-    uint16_t* ub = us + (c & 1) * BM * US;
-    f32x16 sg[RBW], su[RBW];
+  while (true) {
+    // ---- main loop ---------------------------------------------------------------
+    f32x16 oacc[RBW][NBO];
 #pragma unroll
-    for (int i = 0; i < RBW; ++i) {
-      sg[i] = f32x16{};
-      su[i] = f32x16{};
-    }
+    for (int i = 0; i < RBW; ++i)
+#pragma unroll
+      for (int j = 0; j < NBO; ++j) oacc[i][j] = f32x16{};
 
-    // GEMM1 (fully unrolled: ring slots and the barrier point are
-    // compile-time). The x_hat fragments of step s+1 are read from LDS while
-    // step s runs; sched_barrier pins each step's loads where they are issued.
-    uint4 xa[2][RBW];
+    // Ping-pong of the two row groups (wr = 0: A, wr = 1: B). Each chunk is
+    //   GEMM1 steps [0, YS) | barrier Y | GEMM1 steps [YS, S1) + U | barrier X | GEMM2
+    // and group B runs one extra barrier before the loop, group A one after
+    // it, so A's X pairs with B's Y and A's Y with B's X: while one group
+    // computes silu(gate)*up on the VALU, the other group's waves on the same
+    // SIMDs keep the MFMA pipe busy. Each group reads only its own U rows,
+    // after its own X barrier; a U buffer is rewritten only after the next Y
+    // barrier, which every wave reaches after finishing its GEMM2 reads.
+    if (wr == 1) __syncthreads();
+
+    for (int c = 0; c < NC; ++c) {
+      uint16_t* ub = us + (c & 1) * BM * US;
+      f32x16 sg[RBW], su[RBW];
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
-      xa[0][rb] = *reinterpret_cast<const uint4*>(&xs[(row0 + rb * 32 + l32) * XS + h32 * 8]);
-#pragma unroll
-    for (int s = 0; s < S1; ++s) {
-      if (s == YS) __syncthreads();                              // barrier Y
-      const int d = s % DEPTH;
-      if (s + 1 < S1) {
-#pragma unroll
-        for (int rb = 0; rb < RBW; ++rb)
-          xa[(s + 1) & 1][rb] =
-              *reinterpret_cast<const uint4*>(&xs[(row0 + rb * 32 + l32) * XS + (s + 1) * 16 + h32 * 8]);
+      for (int i = 0; i < RBW; ++i) {
+        sg[i] = f32x16{};
+        su[i] = f32x16{};
       }
-      __builtin_amdgcn_sched_barrier(0);
+
+      // GEMM1 (fully unrolled: ring slots and the barrier point are
+      // compile-time). The x_hat fragments of step s+1 are read from LDS while
+      // step s runs; sched_barrier pins each step's loads where they are issued.
+      uint4 xa[2][RBW];
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb)
+        xa[0][rb] = *reinterpret_cast<const uint4*>(&xs[(row0 + rb * 32 + l32) * XS + h32 * 8]);
+#pragma unroll
+      for (int s = 0; s < S1; ++s) {
+        if (s == YS) __syncthreads();                              // barrier Y
+        const int d = s % DEPTH;
+        if (s + 1 < S1) {
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb)
+            xa[(s + 1) & 1][rb] =
+                *reinterpret_cast<const uint4*>(&xs[(row0 + rb * 32 + l32) * XS + (s + 1) * 16 + h32 * 8]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+          // S^T = W^T x_hat^T: the packed weight fragment is the A operand
+          // (W^T rows = hidden units) and the x_hat rows are the B operand
+          sg[rb] = mfma32(ring[d][0], xa[s & 1][rb], sg[rb]);
+          su[rb] = mfma32(ring[d][1], xa[s & 1][rb], su[rb]);
+        }
+        refill(ring[d], c, s + DEPTH);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // U = rho(silu(gate) * up). C layout of S^T (32 hidden x 32 rows): lane
+      // holds row l32 and hidden 8*(v/4) + 4*h32 + v%4, i.e. 4 consecutive
+      // hidden units per v-group -> one 8-byte LDS store each
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) {
-        // S^T = W^T x_hat^T: the packed weight fragment is the A operand
-        // (W^T rows = hidden units) and the x_hat rows are the B operand
-        sg[rb] = mfma32(ring[d][0], xa[s & 1][rb], sg[rb]);
-        su[rb] = mfma32(ring[d][1], xa[s & 1][rb], su[rb]);
+        const int row = row0 + rb * 32 + l32;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          float uv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) uv[i] = silu_fast(sg[rb][4 * g4 + i]) * su[rb][4 * g4 + i];
+          uint2 w2;
+          w2.x = pack_bf16x2(uv[0], uv[1]);
+          w2.y = pack_bf16x2(uv[2], uv[3]);
+          *reinterpret_cast<uint2*>(&ub[row * US + wc * 32 + 8 * g4 + 4 * h32]) = w2;
+        }
       }
-      refill(ring[d], c, s + DEPTH);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      __syncthreads();                                             // barrier X
 
-    // U = rho(silu(gate) * up). C layout of S^T (32 hidden x 32 rows): lane
-    // holds row l32 and hidden 8*(v/4) + 4*h32 + v%4, i.e. 4 consecutive
-    // hidden units per v-group -> one 8-byte LDS store each
+      // GEMM2: O^T += W_down[chunk]^T U^T, U fragments read one step ahead
+      uint4 ua[2][RBW];
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) {
-      const int row = row0 + rb * 32 + l32;
+      for (int rb = 0; rb < RBW; ++rb)
+        ua[0][rb] = *reinterpret_cast<const uint4*>(&ub[(row0 + rb * 32 + l32) * US + h32 * 8]);
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        float uv[4];
+      for (int k2 = 0; k2 < S2; ++k2) {
+        const int d = (S1 + k2) % DEPTH;
+        if (k2 + 1 < S2) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) uv[i] = silu_fast(sg[rb][4 * g4 + i]) * su[rb][4 * g4 + i];
-        uint2 w2;
-        w2.x = pack_bf16x2(uv[0], uv[1]);
-        w2.y = pack_bf16x2(uv[2], uv[3]);
-        *reinterpret_cast<uint2*>(&ub[row * US + wc * 32 + 8 * g4 + 4 * h32]) = w2;
-      }
-    }
-    __syncthreads();
-
-    // GEMM2: O^T += W_down[chunk]^T U^T, U fragments read one step ahead
-    uint4 ua[2][RBW];
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
-      ua[0][rb] = *reinterpret_cast<const uint4*>(&ub[(row0 + rb * 32 + l32) * US + h32 * 8]);
-#pragma unroll
-    for (int k2 = 0; k2 < S2; ++k2) {
-      const int d = (S1 + k2) % DEPTH;
-      if (k2 + 1 < S2) {
+          for (int rb = 0; rb < RBW; ++rb)
+            ua[(k2 + 1) & 1][rb] =
+                *reinterpret_cast<const uint4*>(&ub[(row0 + rb * 32 + l32) * US + (k2 + 1) * 16 + h32 * 8]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb)
-          ua[(k2 + 1) & 1][rb] =
-              *reinterpret_cast<const uint4*>(&ub[(row0 + rb * 32 + l32) * US + (k2 + 1) * 16 + h32 * 8]);
+#pragma unroll
+          for (int j = 0; j < NBO; ++j) oacc[rb][j] = mfma32(ring[d][j], ua[k2 & 1][rb], oacc[rb][j]);   // O^T block
+        refill(ring[d], c, S1 + k2 + DEPTH);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-        for (int j = 0; j < NBO; ++j) oacc[rb][j] = mfma32(ring[d][j], ua[k2 & 1][rb], oacc[rb][j]);   // O^T block
-      refill(ring[d], c, S1 + k2 + DEPTH);
-      __builtin_amdgcn_sched_barrier(0);
     }
-  }
-  if (wr == 0) __syncthreads();
+    if (wr == 0) __syncthreads();
 
-  // ---- epilogue ----------------------------------------------------------------
-  // O goes through LDS (the x_hat region, free now) one row half at a time,
-  // so every global access is a 16-byte vector: residual / extra / output
-  // through the row map (8 consecutive columns never straddle a Mix
-  // segment since D/H % 8 == 0), partials as fp32 rows.
-  // stage row stride SS = W + 4 floats: 16 consecutive rows land on distinct
-  // 16-byte bank groups for the 16-byte writes below
-  constexpr int SS = W + 4;
-  static_assert((BM / 2) * SS * 4 <= BM * XS * 2, "stage must fit in the x_hat region");
-  float* stage = reinterpret_cast<float*>(xs);
-#pragma unroll 1
-  for (int half = 0; half < 2; ++half) {
-    __syncthreads();
-    if (wr == half) {
-      // C layout of an O^T block (32 columns x 32 rows): lane holds row l32 and
-      // columns 8*(v/4) + 4*h32 + v%4 -> 4 consecutive columns per v-group
+    // ---- between tiles: stage O, start the next tile's loads, epilogue --------
+    // The ring already holds the next tile's first fragments (see refill).
+    const bool has_next = ni < total;
+    if (has_next) set_rows(nx, buf ^ 1);
+    // an opaque copy of the thread index: keeps the compiler from hoisting
+    // the epilogue's and the next prologue's address arithmetic out of the
+    // tile loop, where it would stay live through the main loop
+    int etid = tid;
+    asm volatile("" : "+v"(etid));
+    constexpr bool PREF_R = (NPART == 1) && (MODE != MLP_ROUTED);
+    constexpr int PR = BM / NPART;           // rows per staged part
+    constexpr int NE = PR * U8 / NT;         // units per lane per part
+    static_assert((PR * U8) % NT == 0, "part units must divide evenly");
+    uint4 pr[PREF_R ? NPRO : 1];
+    // defined on every path: a conditionally written px becomes a value
+    // carried around the tile loop and stays live through the main loop
+    uint4 px[NPRO];
 #pragma unroll
-      for (int rb = 0; rb < RBW; ++rb)
+    for (int i = 0; i < NPRO; ++i) px[i] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < NBO; ++j)
+    for (int part = 0; part < NPART; ++part) {
+      __syncthreads();
+      if (NPART == 1 || wr == part) {
+        // C layout of an O^T block (32 columns x 32 rows): lane holds row l32
+        // and columns 8*(v/4) + 4*h32 + v%4 -> 4 consecutive columns per v-group
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int r = rb * 32 + l32;
-            const int col = (wc * NBO + j) * 32 + 8 * g4 + 4 * h32;
-            *reinterpret_cast<float4*>(&stage[r * SS + col]) =
-                make_float4(oacc[rb][j][4 * g4], oacc[rb][j][4 * g4 + 1], oacc[rb][j][4 * g4 + 2],
-                            oacc[rb][j][4 * g4 + 3]);
+        for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+          for (int j = 0; j < NBO; ++j)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int r = (NPART == 1 ? row0 : 0) + rb * 32 + l32;
+              const int col = (wc * NBO + j) * 32 + 8 * g4 + 4 * h32;
+              *reinterpret_cast<float4*>(&stage[r * SS + col]) =
+                  make_float4(oacc[rb][j][4 * g4], oacc[rb][j][4 * g4 + 1], oacc[rb][j][4 * g4 + 2],
+                              oacc[rb][j][4 * g4 + 3]);
+            }
+      }
+      __syncthreads();
+      if (part == NPART - 1) {
+        if constexpr (PREF_R) load_resid(etid, buf, cur, pr);
+        if (has_next) load_x(etid, buf ^ 1, nx, px);
+      }
+      // O goes out of LDS in 16-byte units: residual / extra / output through
+      // the row map, partials as fp32 rows
+#pragma unroll
+      for (int i = 0; i < NE; ++i) {
+        const int u = etid + i * NT;
+        const int r = u / U8, c8 = u - r * U8;
+        const int R = part * PR + r;
+        const int b = rowb[buf][R];
+        if (b < 0) continue;
+        const float4 o0 = *reinterpret_cast<const float4*>(&stage[r * SS + c8 * 8]);
+        const float4 o1 = *reinterpret_cast<const float4*>(&stage[r * SS + c8 * 8 + 4]);
+        float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+        if (MODE == MLP_ROUTED) {
+          const int slot = rowent[buf][R] - b * a.top_k;
+          const size_t gi = ((size_t)b * a.P + cur.p) * a.top_k + slot;
+          const float g = a.gate[gi];
+          float4* dst = reinterpret_cast<float4*>(a.part + gi * W + c8 * 8);
+          dst[0] = make_float4(g * o[0], g * o[1], g * o[2], g * o[3]);
+          dst[1] = make_float4(g * o[4], g * o[5], g * o[6], g * o[7]);
+        } else {
+          if (MODE == MLP_SHARED) {
+            const float* src = a.part + ((size_t)b * a.P + cur.p) * a.top_k * W + c8 * 8;
+            for (int sl = 0; sl < a.top_k; ++sl) {
+              const float4 q0 = *reinterpret_cast<const float4*>(src + (size_t)sl * W);
+              const float4 q1 = *reinterpret_cast<const float4*>(src + (size_t)sl * W + 4);
+              o[0] += q0.x; o[1] += q0.y; o[2] += q0.z; o[3] += q0.w;
+              o[4] += q1.x; o[5] += q1.y; o[6] += q1.z; o[7] += q1.w;
+            }
           }
-    }
-    __syncthreads();
-    for (int u = tid; u < (BM / 2) * U8; u += NT) {
-      const int r = u / U8, c8 = u - r * U8;
-      const int R = half * (BM / 2) + r;
-      const int b = rowb[R];
-      if (b < 0) continue;
-      const float4 o0 = *reinterpret_cast<const float4*>(&stage[r * SS + c8 * 8]);
-      const float4 o1 = *reinterpret_cast<const float4*>(&stage[r * SS + c8 * 8 + 4]);
-      float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-      if (MODE == MLP_ROUTED) {
-        const int slot = rowent[R] - b * a.top_k;
-        const size_t gi = ((size_t)b * a.P + p) * a.top_k + slot;
-        const float g = a.gate[gi];
-        float4* dst = reinterpret_cast<float4*>(a.part + gi * W + c8 * 8);
-        dst[0] = make_float4(g * o[0], g * o[1], g * o[2], g * o[3]);
-        dst[1] = make_float4(g * o[4], g * o[5], g * o[6], g * o[7]);
-      } else {
-        if (MODE == MLP_SHARED) {
-          const float* src = a.part + ((size_t)b * a.P + p) * a.top_k * W + c8 * 8;
-          for (int sl = 0; sl < a.top_k; ++sl) {
-            const float4 q0 = *reinterpret_cast<const float4*>(src + (size_t)sl * W);
-            const float4 q1 = *reinterpret_cast<const float4*>(src + (size_t)sl * W + 4);
-            o[0] += q0.x; o[1] += q0.y; o[2] += q0.z; o[3] += q0.w;
-            o[4] += q1.x; o[5] += q1.y; o[6] += q1.z; o[7] += q1.w;
+          const int64_t off = a.map.offset(b, cur.p, c8 * 8);
+          uint4 rvv;
+          if constexpr (PREF_R) rvv = pr[i];
+          else rvv = ldg16(a.resid + off);
+          const uint16_t* rh = reinterpret_cast<const uint16_t*>(&rvv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] += bf2f(rh[e]);
+          if (a.extra) {
+            const uint4 ev = ldg16(a.extra + off);
+            const uint16_t* eh = reinterpret_cast<const uint16_t*>(&ev);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] += bf2f(eh[e]);
           }
+          uint4 w;
+          w.x = pack_bf16x2(o[0], o[1]);
+          w.y = pack_bf16x2(o[2], o[3]);
+          w.z = pack_bf16x2(o[4], o[5]);
+          w.w = pack_bf16x2(o[6], o[7]);
+          *reinterpret_cast<uint4*>(a.out + off) = w;
         }
-        const int64_t off = a.map.offset(b, p, c8 * 8);
-        const uint4 rv = ldg16(a.resid + off);
-        const uint16_t* rh = reinterpret_cast<const uint16_t*>(&rv);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] += bf2f(rh[i]);
-        if (a.extra) {
-          const uint4 ev = ldg16(a.extra + off);
-          const uint16_t* eh = reinterpret_cast<const uint16_t*>(&ev);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) o[i] += bf2f(eh[i]);
-        }
-        uint4 w;
-        w.x = pack_bf16x2(o[0], o[1]);
-        w.y = pack_bf16x2(o[2], o[3]);
-        w.z = pack_bf16x2(o[4], o[5]);
-        w.w = pack_bf16x2(o[6], o[7]);
-        *reinterpret_cast<uint4*>(a.out + off) = w;
       }
     }
+    if (!has_next) break;
+    __syncthreads();                       // staging reads done before x_hat is rewritten
+    store_x(etid, px);
+    cur = nx;
+    ci = ni;
+    buf ^= 1;
+    cw = nw;
+    ni = next_valid(ci + gridDim.x, nx);
+    nw = ni < total ? bind(nx) : cw;
   }
 }
 
@@ -484,8 +592,12 @@ bool mlp_width_supported(int W) { return W == 128 || W == 256 || W == 512 || W =
 
 int mlp_bm_for_width(int W) { return W <= 256 ? 128 : 64; }
 
-hipError_t launch_mlp(int mode, int W, const MlpArgs& a, int grid, hipStream_t s) {
-  if (grid <= 0) return hipSuccess;
+hipError_t launch_mlp(int mode, int W, const MlpArgs& a, int tiles, int workers, hipStream_t s) {
+  if (tiles <= 0) return hipSuccess;
+  // persistent grid: at most `workers` workgroups, a multiple of 8 so that a
+  // workgroup's tiles all sit on its own XCD
+  workers &= ~7;
+  const int grid = (workers <= 0 || tiles <= workers) ? tiles : workers;
   switch (W) {
     case 128: return launch_w<128>(mode, a, grid, s);
     case 256: return launch_w<256>(mode, a, grid, s);
