@@ -56,6 +56,24 @@ def test_small_bf16_stack_all_rows_ragged():
         assert torch.equal(yb, y_full[:B])
 
 
+# odd H: the Mix sub-layer cannot pair adjacent positions in one tile; W = 768
+ODD_H = dg.Workload("odd_h_dense_bf16", B=100, T=3, H=3, D=768, L=2, hidden_mix=128,
+                    hidden_rev=256, gap=2, seed=23)
+
+
+def test_odd_positions_stack_all_rows():
+    require_gpu()
+    wl = ODD_H
+    say("odd-H dense stack", wl)
+    ctx, banks, ws = context("odd_h", wl)
+    x = dg.make_x(wl)
+    y = to_np(_stack(wl, ctx, to_dev(wl, x), wl.B))
+    ref = orc.stack_forward(x.astype(np.float64), wl, ws)
+    err = row_err(y, ref)
+    say("odd-H err", err)
+    assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("wid", [2, 3])
 @pytest.mark.parametrize("sub", [0, 1])
 def test_dense_sublayer_teacher_forced_full_batch(wid, sub):

@@ -211,6 +211,15 @@ tmx_status check_ready(tmx_ctx* c) {
 }
 
 // ---- one sub-layer --------------------------------------------------------------
+// Row tiling of the per-position MLP. On the Mix map two adjacent positions
+// share a tile (BM/2 rows each): their segments of a token are adjacent in
+// the block layout, so the tile reads and writes whole 2*D/H-element runs.
+void set_row_tiles(MlpArgs& a, int sub, int P, int B, int bm) {
+  a.pair = (sub == TMX_MIX && P % 2 == 0) ? 1 : 0;
+  const int rows = a.pair ? bm / 2 : bm;
+  a.rtiles = (B + rows - 1) / rows;
+}
+
 tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const void* resid, const void* extra,
                         void* x_out, int B, hipStream_t st) {
   const tmx_config& cfg = c->cfg;
@@ -244,8 +253,9 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
     a.hidden = dense_hidden(cfg, sub);
     a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_GATE).ptr);
     a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_DOWN).ptr);
-    a.rtiles = (B + bm - 1) / bm;
-    return check_launch(c, launch_mlp(MLP_DENSE, W, a, P * a.rtiles, c->workers, st), "dense MLP launch");
+    set_row_tiles(a, sub, P, B, bm);
+    return check_launch(c, launch_mlp(MLP_DENSE, W, a, (a.pair ? P / 2 : P) * a.rtiles, c->workers, st),
+                        "dense MLP launch");
   }
 
   // MoE: norm + route -> bucket -> routed experts -> shared expert + combine
@@ -274,8 +284,9 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   a.hidden = cfg.shared_hidden;
   a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_SH_GATE).ptr);
   a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_SH_DOWN).ptr);
-  a.rtiles = (B + bm - 1) / bm;
-  return check_launch(c, launch_mlp(MLP_SHARED, W, a, P * a.rtiles, c->workers, st), "shared MLP launch");
+  set_row_tiles(a, sub, P, B, bm);
+  return check_launch(c, launch_mlp(MLP_SHARED, W, a, (a.pair ? P / 2 : P) * a.rtiles, c->workers, st),
+                      "shared MLP launch");
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -41,7 +41,9 @@ struct MlpArgs {
   const int* ntiles;       // ROUTED: [P]
   const float* gate;       // ROUTED: [B][P][top_k]
   float* part;             // ROUTED writes / SHARED reads, [B][P][top_k][W]
-  int rtiles;              // DENSE / SHARED: row tiles per position
+  int rtiles;              // DENSE / SHARED: row tiles per position unit
+  int pair;                // DENSE / SHARED: 1 = a tile holds BM/2 rows of each of two
+                           // adjacent positions (2q in rows [0, BM/2), 2q+1 above)
 };
 
 struct RouteArgs {

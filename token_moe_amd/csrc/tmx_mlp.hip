@@ -128,20 +128,29 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
   // positions [x*P/8, (x+1)*P/8): a position's weights stay in that XCD's L2,
   // and neighbouring mixed positions, whose Mix segments share cache lines of
   // the block-layout rows, are read and written by the same XCD.
+  // Position units: one position, or with `pair` two adjacent positions
+  // whose Mix segments are adjacent in memory (p and p+1 of one token share
+  // each 2*D/H-element run), so a tile's loads and stores cover whole runs
+  // instead of every other half of them.
+  const bool pair = (MODE != MLP_ROUTED) && a.pair;
+  constexpr int HB = BM / 2;                 // rows of one position in a paired tile
+  const int NPU = pair ? a.P / 2 : a.P;
   const int per_pos = (MODE == MLP_ROUTED) ? a.max_tiles : a.rtiles;
-  const int total = a.P * per_pos;
+  const int total = NPU * per_pos;
   struct Tile {
     int p, t, group, start, nrows;
   };
   auto decode = [&](int j, Tile& T) -> bool {
-    if ((a.P & 7) == 0) {
+    int pu;
+    if ((NPU & 7) == 0) {
       const int xcd = j & 7, q = j >> 3;
-      T.p = xcd * (a.P >> 3) + q / per_pos;
+      pu = xcd * (NPU >> 3) + q / per_pos;
       T.t = q % per_pos;
     } else {
-      T.p = j / per_pos;
+      pu = j / per_pos;
       T.t = j % per_pos;
     }
+    T.p = pair ? 2 * pu : pu;
     if (MODE == MLP_ROUTED) {
       if (T.t >= a.ntiles[T.p]) return false;
       const int4 tl = a.tiles[(size_t)T.p * a.max_tiles + T.t];
@@ -149,12 +158,15 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
       T.start = tl.y;
       T.nrows = tl.z;
     } else {
+      const int rb = pair ? HB : BM;
       T.group = T.p;
-      T.start = T.t * BM;
-      T.nrows = min(BM, a.B - T.start);
+      T.start = T.t * rb;
+      T.nrows = min(rb, a.B - T.start);
     }
     return true;
   };
+  // position of tile row r
+  auto rowpos = [&](const Tile& T, int r) -> int { return T.p + ((pair && r >= HB) ? 1 : 0); };
   auto next_valid = [&](int j, Tile& T) -> int {
     while (j < total && !decode(j, T)) j += gridDim.x;
     return j;
@@ -162,13 +174,14 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
   auto set_rows = [&](const Tile& T, int buf) {
     for (int r = tid; r < BM; r += NT) {
       int b = -1, ent = 0;
-      if (r < T.nrows) {
-        if (MODE == MLP_ROUTED) {
+      if (MODE == MLP_ROUTED) {
+        if (r < T.nrows) {
           ent = a.rows[(size_t)T.p * a.B * a.top_k + T.start + r];
           b = ent / a.top_k;
-        } else {
-          b = T.start + r;
         }
+      } else {
+        const int rr = (pair && r >= HB) ? r - HB : r;   // row within its position
+        if (rr < T.nrows) b = T.start + rr;
       }
       rowb[buf][r] = b;
       rowent[buf][r] = ent;
@@ -188,9 +201,11 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
   // iteration c, t = row tile): the sum over chunks is the same, and the
   // workgroups of one position, which run side by side on one XCD, stream
   // different parts of the weights.
+  // (with `pair` the row group wr computes position p + wr and streams its weights)
   auto bind = [&](const Tile& T) -> Stream {
-    return Stream{a.wgu + (size_t)T.group * NBh * (W / 16) * 2 * FRAG_ELEMS,
-                  a.wd + (size_t)T.group * KBd * (W / 32) * FRAG_ELEMS, T.t % NC};
+    const int g = T.group + (pair ? wr : 0);
+    return Stream{a.wgu + (size_t)g * NBh * (W / 16) * 2 * FRAG_ELEMS,
+                  a.wd + (size_t)g * KBd * (W / 32) * FRAG_ELEMS, T.t % NC};
   };
   uint4 ring[DEPTH][NBR];
   // step s of chunk c: GEMM1 k-step s (< S1): gate and up fragments of hidden
@@ -243,10 +258,11 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
       const int b = rowb[buf][r];
       v[i] = make_uint4(0, 0, 0, 0);
       if (b >= 0) {
+        const int p = rowpos(T, r);
         if (MODE == MLP_DENSE)
-          v[i] = ldg16(a.x + a.map.offset(b, T.p, c8 * 8));
+          v[i] = ldg16(a.x + a.map.offset(b, p, c8 * 8));
         else
-          v[i] = ldg16(a.xhat + ((size_t)T.p * a.B + b) * W + c8 * 8);
+          v[i] = ldg16(a.xhat + ((size_t)p * a.B + b) * W + c8 * 8);
       }
     }
   };
@@ -348,7 +364,7 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
       const int u = tix + i * NT;
       const int r = u / U8, c8 = u - r * U8;
       const int b = rowb[buf][r];
-      rv[i] = b >= 0 ? ldg16(a.resid + a.map.offset(b, T.p, c8 * 8)) : make_uint4(0, 0, 0, 0);
+      rv[i] = b >= 0 ? ldg16(a.resid + a.map.offset(b, rowpos(T, r), c8 * 8)) : make_uint4(0, 0, 0, 0);
     }
   };
 
@@ -533,8 +549,9 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
           dst[0] = make_float4(g * o[0], g * o[1], g * o[2], g * o[3]);
           dst[1] = make_float4(g * o[4], g * o[5], g * o[6], g * o[7]);
         } else {
+          const int p = rowpos(cur, R);
           if (MODE == MLP_SHARED) {
-            const float* src = a.part + ((size_t)b * a.P + cur.p) * a.top_k * W + c8 * 8;
+            const float* src = a.part + ((size_t)b * a.P + p) * a.top_k * W + c8 * 8;
             for (int sl = 0; sl < a.top_k; ++sl) {
               const float4 q0 = *reinterpret_cast<const float4*>(src + (size_t)sl * W);
               const float4 q1 = *reinterpret_cast<const float4*>(src + (size_t)sl * W + 4);
@@ -542,7 +559,7 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
               o[4] += q1.x; o[5] += q1.y; o[6] += q1.z; o[7] += q1.w;
             }
           }
-          const int64_t off = a.map.offset(b, cur.p, c8 * 8);
+          const int64_t off = a.map.offset(b, p, c8 * 8);
           uint4 rvv;
           if constexpr (PREF_R) rvv = pr[i];
           else rvv = ldg16(a.resid + off);
