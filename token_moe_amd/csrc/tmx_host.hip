@@ -43,7 +43,8 @@ struct tmx_ctx {
   int4* tiles = nullptr;                       // [P][max_tiles]
   int* ntiles = nullptr;                       // [P]
   int* counts = nullptr;                       // [P][E]
-  float* part = nullptr;                       // [B_max][P][k][W]
+  int* qhead = nullptr;                        // [8] routed-MLP tile queues
+  uint16_t* part = nullptr;                    // [B_max][P][k][W] bf16
   std::vector<void*> allocs;
   std::string err;
 };
@@ -214,8 +215,8 @@ tmx_status check_ready(tmx_ctx* c) {
 // Row tiling of the per-position MLP. On the Mix map two adjacent positions
 // share a tile (BM/2 rows each): their segments of a token are adjacent in
 // the block layout, so the tile reads and writes whole 2*D/H-element runs.
-void set_row_tiles(MlpArgs& a, int sub, int P, int B, int bm) {
-  a.pair = (sub == TMX_MIX && P % 2 == 0) ? 1 : 0;
+void set_row_tiles(MlpArgs& a, int sub, int W, int P, int B, int bm) {
+  a.pair = (sub == TMX_MIX && P % 2 == 0 && mlp_pairs_positions(W)) ? 1 : 0;
   const int rows = a.pair ? bm / 2 : bm;
   a.rtiles = (B + rows - 1) / rows;
 }
@@ -253,7 +254,7 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
     a.hidden = dense_hidden(cfg, sub);
     a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_GATE).ptr);
     a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_DOWN).ptr);
-    set_row_tiles(a, sub, P, B, bm);
+    set_row_tiles(a, sub, W, P, B, bm);
     return check_launch(c, launch_mlp(MLP_DENSE, W, a, (a.pair ? P / 2 : P) * a.rtiles, c->workers, st),
                         "dense MLP launch");
   }
@@ -269,22 +270,23 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
 
   BucketArgs k{};
   k.B = B; k.P = P; k.E = cfg.E; k.top_k = cfg.top_k; k.bm = bm; k.max_tiles = moe_max_tiles(cfg, sub, B);
-  k.idx = c->idx; k.rows = c->rows; k.tiles = c->tiles; k.ntiles = c->ntiles; k.counts = c->counts;
+  k.idx = c->idx; k.rows = c->rows; k.tiles = c->tiles; k.ntiles = c->ntiles; k.counts = c->counts; k.qhead = c->qhead;
   s = check_launch(c, launch_bucket(k, st), "bucket launch");
   if (s != TMX_OK) return s;
 
   a.xhat = c->xhat; a.top_k = cfg.top_k; a.E = cfg.E; a.max_tiles = k.max_tiles;
   a.rows = c->rows; a.tiles = c->tiles; a.ntiles = c->ntiles; a.gate = c->gate; a.part = c->part;
+  a.qhead = c->qhead;
   a.hidden = cfg.expert_hidden;
   a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_EXP_GATE).ptr);
   a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_EXP_DOWN).ptr);
-  s = check_launch(c, launch_mlp(MLP_ROUTED, W, a, P * a.max_tiles, 0, st), "routed MLP launch");
+  s = check_launch(c, launch_mlp(MLP_ROUTED, W, a, P * a.max_tiles, c->workers, st), "routed MLP launch");
   if (s != TMX_OK) return s;
 
   a.hidden = cfg.shared_hidden;
   a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_SH_GATE).ptr);
   a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_SH_DOWN).ptr);
-  set_row_tiles(a, sub, P, B, bm);
+  set_row_tiles(a, sub, W, P, B, bm);
   return check_launch(c, launch_mlp(MLP_SHARED, W, a, (a.pair ? P / 2 : P) * a.rtiles, c->workers, st),
                       "shared MLP launch");
 }
@@ -398,7 +400,8 @@ tmx_status tmx_create(const tmx_config* cfg, int device, tmx_ctx** out) {
     if ((s = dev_alloc(c, (void**)&c->tiles, tiles * sizeof(int4), "bucket tiles")) != TMX_OK) return bail(s);
     if ((s = dev_alloc(c, (void**)&c->ntiles, Pmax * 4, "bucket tiles")) != TMX_OK) return bail(s);
     if ((s = dev_alloc(c, (void**)&c->counts, (int64_t)Pmax * C.E * 4, "bucket counts")) != TMX_OK) return bail(s);
-    if ((s = dev_alloc(c, (void**)&c->part, part * 4, "expert partials")) != TMX_OK) return bail(s);
+    if ((s = dev_alloc(c, (void**)&c->qhead, 8 * 4, "tile queues")) != TMX_OK) return bail(s);
+    if ((s = dev_alloc(c, (void**)&c->part, part * 2, "expert partials")) != TMX_OK) return bail(s);
   }
   *out = c;
   return TMX_OK;

@@ -19,7 +19,7 @@ enum FragShape { FRAG_16x16x32 = 0, FRAG_32x32x16 = 1 };
 
 // One launch of the fused per-position SwiGLU MLP over row tiles:
 //   DENSE : out = rho(resid + SwiGLU_p(rho(RMSNorm(x_p))) [+ extra])
-//   ROUTED: part[b,p,s] = gate[b,p,s] * SwiGLU_{p,e}(xhat[p, b])   (bucket rows)
+//   ROUTED: part[b,p,s] = rho(gate[b,p,s] * SwiGLU_{p,e}(xhat[p, b]))   (bucket rows)
 //   SHARED: out = rho(resid + SwiGLU_p,sh(xhat[p,b]) + sum_s part[b,p,s] [+ extra])
 struct MlpArgs {
   int B;               // batch rows
@@ -40,7 +40,9 @@ struct MlpArgs {
   const int4* tiles;       // ROUTED: [P][max_tiles] (expert, start, count, 0)
   const int* ntiles;       // ROUTED: [P]
   const float* gate;       // ROUTED: [B][P][top_k]
-  float* part;             // ROUTED writes / SHARED reads, [B][P][top_k][W]
+  uint16_t* part;          // ROUTED writes / SHARED reads, [B][P][top_k][W] bf16
+                           // (gated expert outputs, each rounded to bf16)
+  int* qhead;              // ROUTED: [8] per-XCD tile-queue heads, zero at launch
   int rtiles;              // DENSE / SHARED: row tiles per position unit
   int pair;                // DENSE / SHARED: 1 = a tile holds BM/2 rows of each of two
                            // adjacent positions (2q in rows [0, BM/2), 2q+1 above)
@@ -65,6 +67,7 @@ struct BucketArgs {
   int4* tiles;             // [P][max_tiles]
   int* ntiles;             // [P]
   int* counts;             // [P][E]
+  int* qhead;              // [8] tile-queue heads of the routed MLP, zeroed here
 };
 
 // bf16 launchers (return hipError_t of the launch)
@@ -73,6 +76,8 @@ bool mlp_width_supported(int W);
 // tiles = P * (rtiles or max_tiles); the grid is min(tiles, workers & ~7):
 // each workgroup walks tiles blockIdx.x, blockIdx.x + grid, ...
 hipError_t launch_mlp(int mode, int W, const MlpArgs& a, int tiles, int workers, hipStream_t s);
+// whether DENSE / SHARED tiles of this width may hold two adjacent positions
+bool mlp_pairs_positions(int W);
 hipError_t launch_norm_route(int W, const RouteArgs& a, hipStream_t s);
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
 // Repack G row-major [K, N] bf16 matrices into MFMA B-operand fragments of

@@ -28,29 +28,42 @@
 // read by the two waves of a column).  The per-step weight fragments stream
 // through a register ring that runs ahead across the GEMM1 / GEMM2 phases
 // and across chunks.
+#include <type_traits>
+
 #include "tmx_internal.h"
 
 namespace tmx {
 
 namespace {
 
-constexpr int NT = 512;   // 8 waves
+// Waves per workgroup for a row width. 8 waves (two per SIMD, two row
+// groups, 256 registers each) hide one group's SiLU and row I/O behind the
+// other group's MFMAs, and let a Mix tile hold two adjacent positions; they
+// are used where a wave's 64 rows keep each weight fragment busy for two
+// MFMAs (W = 256) or the accumulators of a 4-wave tile would not fit
+// (W = 768). 4 waves (one per SIMD, 512 registers each, every wave on all BM
+// rows) double the reuse of each weight fragment where BM is only 64
+// (W = 512) and serve W = 128.
+constexpr int mlp_waves(int W) { return (W == 256 || W > 512) ? 8 : 4; }
 
-template <int W>
+template <int W, int NW>
 struct MlpShape {
+  static constexpr int NT = 64 * NW;
   static constexpr int BM = (W <= 256) ? 128 : 64;  // rows per workgroup
   static constexpr int HC = MLP_HC;                 // hidden chunk
   static constexpr int XS = W + 8;                  // x_hat row stride (+16 B: rows on distinct banks)
   static constexpr int US = HC + 8;                 // U row stride
-  static constexpr int RBW = BM / 64;               // 32-row blocks per wave (half the rows)
+  static constexpr int NRG = NW / 4;                // row groups of waves
+  static constexpr int RBW = BM / (32 * NRG);       // 32-row blocks per wave
   static constexpr int NBO = W / 128;               // GEMM2 32-column blocks per wave
   static constexpr int S1 = W / 16;                 // GEMM1 k-steps per chunk
   static constexpr int S2 = HC / 16;                // GEMM2 k-steps per chunk
   static constexpr int S = S1 + S2;
-  static constexpr int DEPTH = (W <= 256) ? 8 : (W <= 512) ? 4 : 2;  // weight prefetch distance (steps)
+  static constexpr int DEPTH = (NW == 4) ? 4 : (W <= 256) ? 8 : (W <= 512) ? 4 : 2;  // weight prefetch distance (steps)
   static constexpr int NBR = NBO > 2 ? NBO : 2;     // fragments per step
   static constexpr int YS = (S1 - S2) / 2;          // ping-pong barrier step inside GEMM1
   static_assert(W % 128 == 0, "W must be a multiple of 128");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(S1 % DEPTH == 0 && S2 % DEPTH == 0 && DEPTH % 2 == 0,
                 "ring slots must line up across phases and chunks");
 };
@@ -83,15 +96,15 @@ __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
-template <int W, int MODE>
-__global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
-  using S = MlpShape<W>;
+template <int W, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
+  using S = MlpShape<W, NW>;
+  constexpr int NT = S::NT;
   constexpr int BM = S::BM, XS = S::XS, US = S::US, RBW = S::RBW, NBO = S::NBO;
   constexpr int S1 = S::S1, S2 = S::S2, NS = S::S, DEPTH = S::DEPTH, NBR = S::NBR, HC = S::HC, YS = S::YS;
   constexpr int U8 = W / 8;                    // 16-byte units per row
   constexpr int NPRO = BM * U8 / NT;           // row units per lane per tile
-  constexpr int NE = (BM / 2) * U8 / NT;       // per row half
-  static_assert((BM * U8) % NT == 0 && ((BM / 2) * U8) % NT == 0, "row units must divide evenly");
+  static_assert((BM * U8) % NT == 0, "row units must divide evenly");
 
   // LDS: x_hat tile + two U buffers during the main loop; between tiles the
   // same bytes hold the fp32 output tile (all rows at once when it fits in
@@ -99,14 +112,16 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
   // consecutive rows land on distinct 16-byte bank groups.
   constexpr int XBYTES = BM * XS * 2, UBYTES = 2 * BM * US * 2;
   constexpr int SS = W + 4;
-  constexpr int ROWTAB = 4 * BM * 4;
+  constexpr int ROWTAB = 6 * BM * 4;
   constexpr int NPART = (BM * SS * 4 + ROWTAB <= 160 * 1024) ? 1 : 2;
   constexpr int SBYTES = (BM / NPART) * SS * 4;
   constexpr int SMEM = (XBYTES + UBYTES > SBYTES) ? XBYTES + UBYTES : SBYTES;
   static_assert(SMEM + ROWTAB <= 160 * 1024, "LDS budget");
+  static_assert(NW == 8 || NPART == 1, "one wave per SIMD stages all rows at once");
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ int rowb[2][BM];
-  __shared__ int rowent[2][BM];
+  __shared__ int rowgi[2][BM];       // ROUTED: flat (b, p, slot) index of the row
+  __shared__ float rowg[2][BM];      // ROUTED: gate of the row
   uint16_t* const xs = reinterpret_cast<uint16_t*>(smem);
   uint16_t* const us = reinterpret_cast<uint16_t*>(smem + XBYTES);
   float* const stage = reinterpret_cast<float*>(smem);
@@ -116,9 +131,37 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps addresses scalar
   const int l32 = lane & 31;
   const int h32 = lane >> 5;
-  const int wr = wave >> 2;                 // row half
+  const int wr = NW == 8 ? wave >> 2 : 0;   // row group
   const int wc = wave & 3;                  // column quarter
   const int row0 = wr * (BM / 2);
+
+  // ---- per-lane columns -------------------------------------------------------
+  // Row I/O moves 16-byte units (8 columns); unit u of a tile is row u / U8,
+  // columns 8 * (u % U8). When NT is a multiple of U8 a lane's columns are
+  // the same for every unit and tile, so the column part of the block-layout
+  // offset (a division by D/H for the Mix map) and the RMSNorm gains are
+  // computed once here.
+  constexpr bool LANE_COL = (NT % U8) == 0;
+  const int lw0 = (tid % U8) * 8;
+  const int64_t rowstride = (int64_t)a.map.T * a.map.D;
+  const int pstride = a.map.mix ? a.map.dh : a.map.D;
+  const int lcol = a.map.mix ? (lw0 / a.map.dh) * a.map.D + lw0 % a.map.dh : lw0;
+  auto uoff = [&](int b, int p, int c8) -> int64_t {
+    if constexpr (LANE_COL)
+      return b * rowstride + lcol + (int64_t)p * pstride;
+    else
+      return a.map.offset(b, p, c8 * 8);
+  };
+  // the lane's 8 gains, loaded next to each tile's x rows (registers held
+  // through the main loop would cost spills)
+  auto load_gain = [&](float* g) {
+    if constexpr (MODE == MLP_DENSE && LANE_COL) {
+      const float4 g0 = *reinterpret_cast<const float4*>(a.gain + lw0);
+      const float4 g1 = *reinterpret_cast<const float4*>(a.gain + lw0 + 4);
+      g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
+      g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+    }
+  };
 
   // ---- tiles ------------------------------------------------------------------
   // The kernel is persistent: workgroup i walks tiles i, i + G, i + 2G, ...
@@ -132,7 +175,7 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
   // whose Mix segments are adjacent in memory (p and p+1 of one token share
   // each 2*D/H-element run), so a tile's loads and stores cover whole runs
   // instead of every other half of them.
-  const bool pair = (MODE != MLP_ROUTED) && a.pair;
+  const bool pair = (NW == 8) && (MODE != MLP_ROUTED) && a.pair;
   constexpr int HB = BM / 2;                 // rows of one position in a paired tile
   const int NPU = pair ? a.P / 2 : a.P;
   const int per_pos = (MODE == MLP_ROUTED) ? a.max_tiles : a.rtiles;
@@ -171,20 +214,52 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
     while (j < total && !decode(j, T)) j += gridDim.x;
     return j;
   };
+  // ROUTED tiles come from queues instead: bucket sizes are uneven, so a
+  // fixed assignment would leave some workgroups with twice the work. With
+  // P % 8 == 0 each XCD has a queue over its own positions (the position
+  // ranges of the static mapping), else one queue covers all positions.
+  // Entry k of a queue is the k-th non-empty tile of its positions in order;
+  // heads are zeroed by the bucket kernel, which runs just before.
+  __shared__ int qslot;
+  const bool split_q = (a.P & 7) == 0;
+  const int qx = split_q ? (int)(blockIdx.x & 7) : 0;
+  const int NPX = split_q ? (a.P >> 3) : a.P;
+  auto qdecode = [&](int k, Tile& T) -> bool {
+    int p = qx * NPX;
+    for (int q = 0; q < NPX; ++q, ++p) {
+      const int n = a.ntiles[p];
+      if (k < n) {
+        const int4 tl = a.tiles[(size_t)p * a.max_tiles + k];
+        T.p = p;
+        T.t = k;
+        T.group = p * a.E + tl.x;
+        T.start = tl.y;
+        T.nrows = tl.z;
+        return true;
+      }
+      k -= n;
+    }
+    return false;
+  };
   auto set_rows = [&](const Tile& T, int buf) {
     for (int r = tid; r < BM; r += NT) {
-      int b = -1, ent = 0;
+      int b = -1;
       if (MODE == MLP_ROUTED) {
+        int gi = 0;
+        float g = 0.f;
         if (r < T.nrows) {
-          ent = a.rows[(size_t)T.p * a.B * a.top_k + T.start + r];
+          const int ent = a.rows[(size_t)T.p * a.B * a.top_k + T.start + r];   // b * top_k + slot
           b = ent / a.top_k;
+          gi = (b * a.P + T.p) * a.top_k + (ent - b * a.top_k);
+          g = a.gate[gi];
         }
+        rowgi[buf][r] = gi;
+        rowg[buf][r] = g;
       } else {
         const int rr = (pair && r >= HB) ? r - HB : r;   // row within its position
         if (rr < T.nrows) b = T.start + rr;
       }
       rowb[buf][r] = b;
-      rowent[buf][r] = ent;
     }
   };
 
@@ -210,13 +285,17 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
   uint4 ring[DEPTH][NBR];
   // step s of chunk c: GEMM1 k-step s (< S1): gate and up fragments of hidden
   // block 4c + wc; GEMM2 k-step s - S1: down fragments of this wave's columns
-  auto issue = [&](uint4* dst, const Stream& w, int c, int s) {
+  auto issue = [&](uint4* dst, const Stream& w, int c, int s) __attribute__((always_inline)) {
     c += w.rot;
     if (c >= NC) c -= NC;
     if (s < S1) {
       const uint16_t* f = w.gu + ((size_t)((c * 4 + wc) * (W / 16) + s) * 2) * FRAG_ELEMS + lane * 8;
       dst[0] = ldg16(f);
       dst[1] = ldg16(f + FRAG_ELEMS);
+      // whole-slot writes on every path keep the ring in registers (a slot
+      // written in part on some paths is left in scratch memory)
+#pragma unroll
+      for (int j = 2; j < NBR; ++j) dst[j] = make_uint4(0, 0, 0, 0);
     } else {
       const int kb = c * (HC / 16) + (s - S1);
 #pragma unroll
@@ -260,7 +339,7 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
       if (b >= 0) {
         const int p = rowpos(T, r);
         if (MODE == MLP_DENSE)
-          v[i] = ldg16(a.x + a.map.offset(b, p, c8 * 8));
+          v[i] = ldg16(a.x + uoff(b, p, c8));
         else
           v[i] = ldg16(a.xhat + ((size_t)p * a.B + b) * W + c8 * 8);
       }
@@ -269,7 +348,7 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
   // x rows -> LDS x_hat; for DENSE the RMS statistics reduce across the lanes
   // of a row before x_hat is written (RMSNorm in fp32, rho to bf16:
   // TokenMixer-Large section 2.3.3)
-  auto store_x = [&](int tix, uint4* v) {
+  auto store_x = [&](int tix, uint4* v, const float* lgain) {
     constexpr bool kFusedNorm = (U8 <= 64 || U8 % 64 == 0);
     if constexpr (MODE == MLP_DENSE && kFusedNorm) {
       constexpr int LPR = U8 < 64 ? U8 : 64;  // lanes per row within a wave
@@ -312,7 +391,7 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
         const uint16_t* h = reinterpret_cast<const uint16_t*>(&v[i]);
         float n[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) n[e] = bf2f(h[e]) * rinv * a.gain[c8 * 8 + e];
+        for (int e = 0; e < 8; ++e) n[e] = bf2f(h[e]) * rinv * (LANE_COL ? lgain[e] : a.gain[c8 * 8 + e]);
         v[i].x = pack_bf16x2(n[0], n[1]);
         v[i].y = pack_bf16x2(n[2], n[3]);
         v[i].z = pack_bf16x2(n[4], n[5]);
@@ -364,26 +443,42 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
       const int u = tix + i * NT;
       const int r = u / U8, c8 = u - r * U8;
       const int b = rowb[buf][r];
-      rv[i] = b >= 0 ? ldg16(a.resid + a.map.offset(b, rowpos(T, r), c8 * 8)) : make_uint4(0, 0, 0, 0);
+      rv[i] = b >= 0 ? ldg16(a.resid + uoff(b, rowpos(T, r), c8)) : make_uint4(0, 0, 0, 0);
     }
   };
 
   // ---- first tile ---------------------------------------------------------------
   Tile cur, nx;
-  int ci = next_valid(blockIdx.x, cur);
-  if (ci >= total) return;                                     // uniform per workgroup
-  int ni = next_valid(ci + gridDim.x, nx);
+  int ci = 0, ni = 0;
+  bool has_nx;
+  if constexpr (MODE == MLP_ROUTED) {
+    __shared__ int qfirst[2];
+    if (tid == 0) {
+      qfirst[0] = atomicAdd(&a.qhead[qx], 1);
+      qfirst[1] = atomicAdd(&a.qhead[qx], 1);
+    }
+    __syncthreads();
+    if (!qdecode(qfirst[0], cur)) return;                      // uniform per workgroup
+    has_nx = qdecode(qfirst[1], nx);
+  } else {
+    ci = next_valid(blockIdx.x, cur);
+    if (ci >= total) return;                                   // uniform per workgroup
+    ni = next_valid(ci + gridDim.x, nx);
+    has_nx = ni < total;
+  }
   int buf = 0;
   set_rows(cur, 0);
   cw = bind(cur);
-  nw = ni < total ? bind(nx) : cw;
+  nw = has_nx ? bind(nx) : cw;
 #pragma unroll
   for (int s = 0; s < DEPTH; ++s) issue(ring[s], cw, 0, s);
   __syncthreads();
   {
     uint4 v[NPRO];
+    float g[8];
+    load_gain(g);
     load_x(tid, 0, cur, v);
-    store_x(tid, v);
+    store_x(tid, v, g);
   }
 
   while (true) {
@@ -394,102 +489,247 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
 #pragma unroll
       for (int j = 0; j < NBO; ++j) oacc[i][j] = f32x16{};
 
-    // Ping-pong of the two row groups (wr = 0: A, wr = 1: B). Each chunk is
-    //   GEMM1 steps [0, YS) | barrier Y | GEMM1 steps [YS, S1) + U | barrier X | GEMM2
-    // and group B runs one extra barrier before the loop, group A one after
-    // it, so A's X pairs with B's Y and A's Y with B's X: while one group
-    // computes silu(gate)*up on the VALU, the other group's waves on the same
-    // SIMDs keep the MFMA pipe busy. Each group reads only its own U rows,
-    // after its own X barrier; a U buffer is rewritten only after the next Y
-    // barrier, which every wave reaches after finishing its GEMM2 reads.
-    if (wr == 1) __syncthreads();
+    if constexpr (NW == 8) {
+      // Ping-pong of the two row groups (wr = 0: A, wr = 1: B). Each chunk is
+      //   GEMM1 steps [0, YS) | barrier Y | GEMM1 steps [YS, S1) + U | barrier X | GEMM2
+      // and group B runs one extra barrier before the loop, group A one after
+      // it, so A's X pairs with B's Y and A's Y with B's X: while one group
+      // computes silu(gate)*up on the VALU, the other group's waves on the same
+      // SIMDs keep the MFMA pipe busy. Each group reads only its own U rows,
+      // after its own X barrier; a U buffer is rewritten only after the next Y
+      // barrier, which every wave reaches after finishing its GEMM2 reads.
+      if (wr == 1) __syncthreads();
 
-    for (int c = 0; c < NC; ++c) {
-      uint16_t* ub = us + (c & 1) * BM * US;
-      f32x16 sg[RBW], su[RBW];
-#pragma unroll
-      for (int i = 0; i < RBW; ++i) {
-        sg[i] = f32x16{};
-        su[i] = f32x16{};
-      }
-
-      // GEMM1 (fully unrolled: ring slots and the barrier point are
-      // compile-time). The x_hat fragments of step s+1 are read from LDS while
-      // step s runs; sched_barrier pins each step's loads where they are issued.
-      uint4 xa[2][RBW];
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb)
-        xa[0][rb] = *reinterpret_cast<const uint4*>(&xs[(row0 + rb * 32 + l32) * XS + h32 * 8]);
-#pragma unroll
-      for (int s = 0; s < S1; ++s) {
-        if (s == YS) __syncthreads();                              // barrier Y
-        const int d = s % DEPTH;
-        if (s + 1 < S1) {
-#pragma unroll
-          for (int rb = 0; rb < RBW; ++rb)
-            xa[(s + 1) & 1][rb] =
-                *reinterpret_cast<const uint4*>(&xs[(row0 + rb * 32 + l32) * XS + (s + 1) * 16 + h32 * 8]);
+      for (int c = 0; c < NC; ++c) {
+        uint16_t* ub = us + (c & 1) * BM * US;
+        f32x16 sg[RBW], su[RBW];
+  #pragma unroll
+        for (int i = 0; i < RBW; ++i) {
+          sg[i] = f32x16{};
+          su[i] = f32x16{};
         }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
+
+        // GEMM1 (fully unrolled: ring slots and the barrier point are
+        // compile-time). The x_hat fragments of step s+1 are read from LDS while
+        // step s runs; sched_barrier pins each step's loads where they are issued.
+        uint4 xa[2][RBW];
+  #pragma unroll
+        for (int rb = 0; rb < RBW; ++rb)
+          xa[0][rb] = *reinterpret_cast<const uint4*>(&xs[(row0 + rb * 32 + l32) * XS + h32 * 8]);
+  #pragma unroll
+        for (int s = 0; s < S1; ++s) {
+          if (s == YS) __syncthreads();                              // barrier Y
+          const int d = s % DEPTH;
+          if (s + 1 < S1) {
+  #pragma unroll
+            for (int rb = 0; rb < RBW; ++rb)
+              xa[(s + 1) & 1][rb] =
+                  *reinterpret_cast<const uint4*>(&xs[(row0 + rb * 32 + l32) * XS + (s + 1) * 16 + h32 * 8]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+          for (int rb = 0; rb < RBW; ++rb) {
+            // S^T = W^T x_hat^T: the packed weight fragment is the A operand
+            // (W^T rows = hidden units) and the x_hat rows are the B operand
+            sg[rb] = mfma32(ring[d][0], xa[s & 1][rb], sg[rb]);
+            su[rb] = mfma32(ring[d][1], xa[s & 1][rb], su[rb]);
+          }
+          refill(ring[d], c, s + DEPTH);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // U = rho(silu(gate) * up). C layout of S^T (32 hidden x 32 rows): lane
+        // holds row l32 and hidden 8*(v/4) + 4*h32 + v%4, i.e. 4 consecutive
+        // hidden units per v-group -> one 8-byte LDS store each
+  #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
-          // S^T = W^T x_hat^T: the packed weight fragment is the A operand
-          // (W^T rows = hidden units) and the x_hat rows are the B operand
-          sg[rb] = mfma32(ring[d][0], xa[s & 1][rb], sg[rb]);
-          su[rb] = mfma32(ring[d][1], xa[s & 1][rb], su[rb]);
+          const int row = row0 + rb * 32 + l32;
+  #pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            float uv[4];
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) uv[i] = silu_fast(sg[rb][4 * g4 + i]) * su[rb][4 * g4 + i];
+            uint2 w2;
+            w2.x = pack_bf16x2(uv[0], uv[1]);
+            w2.y = pack_bf16x2(uv[2], uv[3]);
+            *reinterpret_cast<uint2*>(&ub[row * US + wc * 32 + 8 * g4 + 4 * h32]) = w2;
+          }
         }
-        refill(ring[d], c, s + DEPTH);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+        __syncthreads();                                             // barrier X
 
-      // U = rho(silu(gate) * up). C layout of S^T (32 hidden x 32 rows): lane
-      // holds row l32 and hidden 8*(v/4) + 4*h32 + v%4, i.e. 4 consecutive
-      // hidden units per v-group -> one 8-byte LDS store each
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) {
-        const int row = row0 + rb * 32 + l32;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          float uv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) uv[i] = silu_fast(sg[rb][4 * g4 + i]) * su[rb][4 * g4 + i];
-          uint2 w2;
-          w2.x = pack_bf16x2(uv[0], uv[1]);
-          w2.y = pack_bf16x2(uv[2], uv[3]);
-          *reinterpret_cast<uint2*>(&ub[row * US + wc * 32 + 8 * g4 + 4 * h32]) = w2;
-        }
-      }
-      __syncthreads();                                             // barrier X
-
-      // GEMM2: O^T += W_down[chunk]^T U^T, U fragments read one step ahead
-      uint4 ua[2][RBW];
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb)
-        ua[0][rb] = *reinterpret_cast<const uint4*>(&ub[(row0 + rb * 32 + l32) * US + h32 * 8]);
-#pragma unroll
-      for (int k2 = 0; k2 < S2; ++k2) {
-        const int d = (S1 + k2) % DEPTH;
-        if (k2 + 1 < S2) {
-#pragma unroll
+        // GEMM2: O^T += W_down[chunk]^T U^T, U fragments read one step ahead
+        uint4 ua[2][RBW];
+  #pragma unroll
+        for (int rb = 0; rb < RBW; ++rb)
+          ua[0][rb] = *reinterpret_cast<const uint4*>(&ub[(row0 + rb * 32 + l32) * US + h32 * 8]);
+  #pragma unroll
+        for (int k2 = 0; k2 < S2; ++k2) {
+          const int d = (S1 + k2) % DEPTH;
+          if (k2 + 1 < S2) {
+  #pragma unroll
+            for (int rb = 0; rb < RBW; ++rb)
+              ua[(k2 + 1) & 1][rb] =
+                  *reinterpret_cast<const uint4*>(&ub[(row0 + rb * 32 + l32) * US + (k2 + 1) * 16 + h32 * 8]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
           for (int rb = 0; rb < RBW; ++rb)
-            ua[(k2 + 1) & 1][rb] =
-                *reinterpret_cast<const uint4*>(&ub[(row0 + rb * 32 + l32) * US + (k2 + 1) * 16 + h32 * 8]);
+  #pragma unroll
+            for (int j = 0; j < NBO; ++j) oacc[rb][j] = mfma32(ring[d][j], ua[k2 & 1][rb], oacc[rb][j]);   // O^T block
+          refill(ring[d], c, S1 + k2 + DEPTH);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (wr == 0) __syncthreads();
+    } else {
+      // One wave per SIMD: every wave runs all BM rows, and the VALU work
+      // (silu(gate) * up) is software-pipelined against the MFMAs instead of
+      // against a second wave. Chunk schedule, i = hidden chunk:
+      //   preamble   GEMM1(0); U(0) -> U buffer 0; barrier
+      //   iteration  GEMM1(i); GEMM2(i-1) with U(i) -> buffer i&1 computed
+      //              between its MFMAs; barrier                 (0 < i < NC)
+      //   postamble  GEMM2(NC-1)
+      // GEMM2(i-1) reads buffer (i-1)&1, complete since the previous
+      // barrier; buffer i&1 was last read by GEMM2(i-2), before it. The
+      // weight stream follows the same order, into the next tile's preamble.
+      f32x16 sg[RBW], su[RBW];
+      uint4 xa[2][RBW];
+      uint4 ua[2][RBW];
+      constexpr int SPS = RBW * 4 / S2;        // U groups (4 hidden units) per GEMM2 step
+      static_assert((RBW * 4) % S2 == 0, "U groups must spread evenly over GEMM2 steps");
+      auto read_xa = [&](uint4* dst, int q) {
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb)
+          dst[rb] = *reinterpret_cast<const uint4*>(&xs[(rb * 32 + l32) * XS + q * 16 + h32 * 8]);
+      };
+      auto read_ua = [&](uint4* dst, const uint16_t* ub, int t) {
 #pragma unroll
-          for (int j = 0; j < NBO; ++j) oacc[rb][j] = mfma32(ring[d][j], ua[k2 & 1][rb], oacc[rb][j]);   // O^T block
-        refill(ring[d], c, S1 + k2 + DEPTH);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int rb = 0; rb < RBW; ++rb)
+          dst[rb] = *reinterpret_cast<const uint4*>(&ub[(rb * 32 + l32) * US + t * 16 + h32 * 8]);
+      };
+      // U group gi (row block gi/4, hidden units 8*(gi%4) + 4*h32 + 0..3 of
+      // this wave's 32): rho(silu(gate) * up), one 8-byte LDS store
+      auto u_group = [&](uint16_t* ub, int gi) __attribute__((always_inline)) {
+        const int rb = gi >> 2, g4 = gi & 3;
+        float uv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) uv[e] = silu_fast(sg[rb][4 * g4 + e]) * su[rb][4 * g4 + e];
+        uint2 w2;
+        w2.x = pack_bf16x2(uv[0], uv[1]);
+        w2.y = pack_bf16x2(uv[2], uv[3]);
+        *reinterpret_cast<uint2*>(&ub[(rb * 32 + l32) * US + wc * 32 + 8 * g4 + 4 * h32]) = w2;
+      };
+      // GEMM1 of chunk c over S1 k-steps; `after(q)` issues the refill for
+      // stream position q + DEPTH and `last` (the final step) may prefetch
+      // the first GEMM2 operands
+      auto gemm1 = [&](auto refill_at, auto at_last) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < RBW; ++i) {
+          sg[i] = f32x16{};
+          su[i] = f32x16{};
+        }
+        read_xa(xa[0], 0);
+#pragma unroll
+        for (int q = 0; q < S1; ++q) {
+          const int d = q % DEPTH;
+          if (q + 1 < S1) read_xa(xa[(q + 1) & 1], q + 1);
+          else at_last();
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb) {
+            sg[rb] = mfma32(ring[d][0], xa[q & 1][rb], sg[rb]);
+            su[rb] = mfma32(ring[d][1], xa[q & 1][rb], su[rb]);
+          }
+          refill_at(ring[d], q + DEPTH);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      // GEMM2 of one chunk from U buffer `ub` (its first operands already in
+      // ua[0]); with `with_u` the next chunk's U groups go to `ubw` between
+      // the MFMAs, SPS groups per k-step
+      auto gemm2 = [&](const uint16_t* ub, uint16_t* ubw, auto with_u_tag, auto refill_at, auto pos0_tag)
+          __attribute__((always_inline)) {
+        constexpr bool with_u = decltype(with_u_tag)::value;
+        constexpr int pos0 = decltype(pos0_tag)::value;
+#pragma unroll
+        for (int t = 0; t < S2; ++t) {
+          const int d = (pos0 + t) % DEPTH;
+          if (t + 1 < S2) read_ua(ua[(t + 1) & 1], ub, t + 1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+            for (int j = 0; j < NBO; ++j) oacc[rb][j] = mfma32(ring[d][j], ua[t & 1][rb], oacc[rb][j]);
+          if constexpr (with_u) {
+#pragma unroll
+            for (int k = 0; k < SPS; ++k) u_group(ubw, t * SPS + k);
+          }
+          refill_at(ring[d], pos0 + t + DEPTH);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+
+      // preamble: stream positions q < S1 are GEMM1(0); beyond, GEMM1(1) of
+      // iteration 1, or with a single chunk the postamble's GEMM2(0)
+      gemm1([&](uint4* dst, int q2) __attribute__((always_inline)) {
+              if (q2 < S1) {
+                issue(dst, cw, 0, q2);
+              } else if (NC > 1) {
+                issue(dst, cw, 1, q2 - S1);
+              } else {
+                issue(dst, cw, 0, q2);
+              }
+            },
+            [] {});
+#pragma unroll
+      for (int gi = 0; gi < RBW * 4; ++gi) u_group(us, gi);
+      __syncthreads();
+
+      // iterations: positions [0, S1) GEMM1(i), [S1, NS) GEMM2(i-1); past
+      // NS the next iteration's GEMM1(i+1), or for the last iteration the
+      // postamble's GEMM2(NC-1)
+      auto iteration = [&](int i, auto last_tag) __attribute__((always_inline)) {
+        constexpr bool LAST = decltype(last_tag)::value;
+        uint16_t* ubw = us + (i & 1) * BM * US;
+        const uint16_t* ubr = us + ((i - 1) & 1) * BM * US;
+        auto refill_at = [&](uint4* dst, int q2) __attribute__((always_inline)) {
+          if (q2 < S1) {
+            issue(dst, cw, i, q2);
+          } else if (q2 < NS) {
+            issue(dst, cw, i - 1, q2);
+          } else if (!LAST) {
+            issue(dst, cw, i + 1, q2 - NS);
+          } else {
+            issue(dst, cw, NC - 1, q2 - NS + S1);
+          }
+        };
+        gemm1(refill_at, [&] { read_ua(ua[0], ubr, 0); });
+        gemm2(ubr, ubw, std::true_type{}, refill_at, std::integral_constant<int, S1>{});
+        __syncthreads();
+      };
+      for (int i = 1; i + 1 < NC; ++i) iteration(i, std::integral_constant<bool, false>{});
+      if (NC > 1) iteration(NC - 1, std::integral_constant<bool, true>{});
+
+      // postamble: GEMM2(NC-1); past its end the stream enters the next
+      // tile's preamble
+      {
+        const uint16_t* ubr = us + ((NC - 1) & 1) * BM * US;
+        read_ua(ua[0], ubr, 0);
+        gemm2(ubr, nullptr, std::false_type{},
+              [&](uint4* dst, int q2) __attribute__((always_inline)) {
+                if (q2 < S2) issue(dst, cw, NC - 1, S1 + q2);
+                else issue(dst, nw, 0, q2 - S2);
+              },
+              std::integral_constant<int, 0>{});
       }
     }
-    if (wr == 0) __syncthreads();
 
     // ---- between tiles: stage O, start the next tile's loads, epilogue --------
     // The ring already holds the next tile's first fragments (see refill).
-    const bool has_next = ni < total;
+    const bool has_next = has_nx;
     if (has_next) set_rows(nx, buf ^ 1);
+    // the tile after next (read back after the staging barriers below)
+    if (MODE == MLP_ROUTED && has_next && tid == 0) qslot = atomicAdd(&a.qhead[qx], 1);
     // an opaque copy of the thread index: keeps the compiler from hoisting
     // the epilogue's and the next prologue's address arithmetic out of the
     // tile loop, where it would stay live through the main loop
@@ -503,8 +743,11 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
     // defined on every path: a conditionally written px becomes a value
     // carried around the tile loop and stays live through the main loop
     uint4 px[NPRO];
+    float pg[8];
 #pragma unroll
     for (int i = 0; i < NPRO; ++i) px[i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pg[e] = 0.f;
 #pragma unroll
     for (int part = 0; part < NPART; ++part) {
       __syncthreads();
@@ -527,78 +770,121 @@ __global__ __launch_bounds__(NT, 1) void mlp_kernel(const MlpArgs a) {
       __syncthreads();
       if (part == NPART - 1) {
         if constexpr (PREF_R) load_resid(etid, buf, cur, pr);
-        if (has_next) load_x(etid, buf ^ 1, nx, px);
+        if (has_next) {
+          load_gain(pg);
+          load_x(etid, buf ^ 1, nx, px);
+        }
       }
       // O goes out of LDS in 16-byte units: residual / extra / output through
-      // the row map, partials as fp32 rows
+      // the row map, gated expert outputs as bf16 rows. Units go in batches
+      // of UB whose global loads (partials, extra) are all issued before any
+      // is consumed, so a lane keeps several loads in flight.
+      constexpr int UB = (NW == 4 && NE % 4 == 0) ? 4 : (NE % 2 == 0) ? 2 : 1;
 #pragma unroll
-      for (int i = 0; i < NE; ++i) {
-        const int u = etid + i * NT;
-        const int r = u / U8, c8 = u - r * U8;
-        const int R = part * PR + r;
-        const int b = rowb[buf][R];
-        if (b < 0) continue;
-        const float4 o0 = *reinterpret_cast<const float4*>(&stage[r * SS + c8 * 8]);
-        const float4 o1 = *reinterpret_cast<const float4*>(&stage[r * SS + c8 * 8 + 4]);
-        float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-        if (MODE == MLP_ROUTED) {
-          const int slot = rowent[buf][R] - b * a.top_k;
-          const size_t gi = ((size_t)b * a.P + cur.p) * a.top_k + slot;
-          const float g = a.gate[gi];
-          float4* dst = reinterpret_cast<float4*>(a.part + gi * W + c8 * 8);
-          dst[0] = make_float4(g * o[0], g * o[1], g * o[2], g * o[3]);
-          dst[1] = make_float4(g * o[4], g * o[5], g * o[6], g * o[7]);
+      for (int i0 = 0; i0 < NE; i0 += UB) {
+        float o[UB][8];
+        int bu[UB], pu[UB], c8u[UB], Ru[UB];
+#pragma unroll
+        for (int k = 0; k < UB; ++k) {
+          const int u = etid + (i0 + k) * NT;
+          const int r = u / U8;
+          c8u[k] = u - r * U8;
+          Ru[k] = part * PR + r;
+          bu[k] = rowb[buf][Ru[k]];
+          pu[k] = rowpos(cur, Ru[k]);
+          const float4 o0 = *reinterpret_cast<const float4*>(&stage[r * SS + c8u[k] * 8]);
+          const float4 o1 = *reinterpret_cast<const float4*>(&stage[r * SS + c8u[k] * 8 + 4]);
+          o[k][0] = o0.x; o[k][1] = o0.y; o[k][2] = o0.z; o[k][3] = o0.w;
+          o[k][4] = o1.x; o[k][5] = o1.y; o[k][6] = o1.z; o[k][7] = o1.w;
+        }
+        if constexpr (MODE == MLP_ROUTED) {
+#pragma unroll
+          for (int k = 0; k < UB; ++k) {
+            if (bu[k] < 0) continue;
+            const float g = rowg[buf][Ru[k]];
+            uint4 w;
+            w.x = pack_bf16x2(g * o[k][0], g * o[k][1]);
+            w.y = pack_bf16x2(g * o[k][2], g * o[k][3]);
+            w.z = pack_bf16x2(g * o[k][4], g * o[k][5]);
+            w.w = pack_bf16x2(g * o[k][6], g * o[k][7]);
+            *reinterpret_cast<uint4*>(a.part + (size_t)rowgi[buf][Ru[k]] * W + c8u[k] * 8) = w;
+          }
         } else {
-          const int p = rowpos(cur, R);
-          if (MODE == MLP_SHARED) {
-            const float* src = a.part + ((size_t)b * a.P + p) * a.top_k * W + c8 * 8;
-            for (int sl = 0; sl < a.top_k; ++sl) {
-              const float4 q0 = *reinterpret_cast<const float4*>(src + (size_t)sl * W);
-              const float4 q1 = *reinterpret_cast<const float4*>(src + (size_t)sl * W + 4);
-              o[0] += q0.x; o[1] += q0.y; o[2] += q0.z; o[3] += q0.w;
-              o[4] += q1.x; o[5] += q1.y; o[6] += q1.z; o[7] += q1.w;
+          if constexpr (MODE == MLP_SHARED) {
+            // the routed experts' gated outputs, four slots at a time
+            for (int s0 = 0; s0 < a.top_k; s0 += 4) {
+              uint4 q[UB][4];
+#pragma unroll
+              for (int k = 0; k < UB; ++k)
+#pragma unroll
+                for (int sl = 0; sl < 4; ++sl) {
+                  q[k][sl] = make_uint4(0, 0, 0, 0);
+                  if (bu[k] >= 0 && s0 + sl < a.top_k)
+                    q[k][sl] = ldg16(a.part + (((size_t)bu[k] * a.P + pu[k]) * a.top_k + s0 + sl) * W + c8u[k] * 8);
+                }
+#pragma unroll
+              for (int k = 0; k < UB; ++k)
+#pragma unroll
+                for (int sl = 0; sl < 4; ++sl) {
+                  const uint16_t* qh = reinterpret_cast<const uint16_t*>(&q[k][sl]);
+#pragma unroll
+                  for (int e = 0; e < 8; ++e) o[k][e] += bf2f(qh[e]);
+                }
             }
           }
-          const int64_t off = a.map.offset(b, p, c8 * 8);
-          uint4 rvv;
-          if constexpr (PREF_R) rvv = pr[i];
-          else rvv = ldg16(a.resid + off);
-          const uint16_t* rh = reinterpret_cast<const uint16_t*>(&rvv);
+          int64_t off[UB];
+          uint4 ev[UB];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] += bf2f(rh[e]);
-          if (a.extra) {
-            const uint4 ev = ldg16(a.extra + off);
-            const uint16_t* eh = reinterpret_cast<const uint16_t*>(&ev);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] += bf2f(eh[e]);
+          for (int k = 0; k < UB; ++k) {
+            off[k] = uoff(bu[k] < 0 ? 0 : bu[k], pu[k], c8u[k]);
+            ev[k] = make_uint4(0, 0, 0, 0);
+            if (a.extra && bu[k] >= 0) ev[k] = ldg16(a.extra + off[k]);
           }
-          uint4 w;
-          w.x = pack_bf16x2(o[0], o[1]);
-          w.y = pack_bf16x2(o[2], o[3]);
-          w.z = pack_bf16x2(o[4], o[5]);
-          w.w = pack_bf16x2(o[6], o[7]);
-          *reinterpret_cast<uint4*>(a.out + off) = w;
+#pragma unroll
+          for (int k = 0; k < UB; ++k) {
+            if (bu[k] < 0) continue;
+            uint4 rvv;
+            if constexpr (PREF_R) rvv = pr[i0 + k];
+            else rvv = ldg16(a.resid + off[k]);
+            const uint16_t* rh = reinterpret_cast<const uint16_t*>(&rvv);
+            const uint16_t* eh = reinterpret_cast<const uint16_t*>(&ev[k]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[k][e] += bf2f(rh[e]) + bf2f(eh[e]);
+            uint4 w;
+            w.x = pack_bf16x2(o[k][0], o[k][1]);
+            w.y = pack_bf16x2(o[k][2], o[k][3]);
+            w.z = pack_bf16x2(o[k][4], o[k][5]);
+            w.w = pack_bf16x2(o[k][6], o[k][7]);
+            *reinterpret_cast<uint4*>(a.out + off[k]) = w;
+          }
         }
       }
     }
     if (!has_next) break;
+    const int knext = qslot;
     __syncthreads();                       // staging reads done before x_hat is rewritten
-    store_x(etid, px);
+    store_x(etid, px, pg);
     cur = nx;
-    ci = ni;
     buf ^= 1;
     cw = nw;
-    ni = next_valid(ci + gridDim.x, nx);
-    nw = ni < total ? bind(nx) : cw;
+    if constexpr (MODE == MLP_ROUTED) {
+      has_nx = qdecode(knext, nx);
+    } else {
+      ci = ni;
+      ni = next_valid(ci + gridDim.x, nx);
+      has_nx = ni < total;
+    }
+    nw = has_nx ? bind(nx) : cw;
   }
 }
 
 template <int W>
 hipError_t launch_w(int mode, const MlpArgs& a, int grid, hipStream_t s) {
+  constexpr int NW = mlp_waves(W);
   switch (mode) {
-    case MLP_DENSE: hipLaunchKernelGGL((mlp_kernel<W, MLP_DENSE>), dim3(grid), dim3(NT), 0, s, a); break;
-    case MLP_ROUTED: hipLaunchKernelGGL((mlp_kernel<W, MLP_ROUTED>), dim3(grid), dim3(NT), 0, s, a); break;
-    default: hipLaunchKernelGGL((mlp_kernel<W, MLP_SHARED>), dim3(grid), dim3(NT), 0, s, a); break;
+    case MLP_DENSE: hipLaunchKernelGGL((mlp_kernel<W, MLP_DENSE, NW>), dim3(grid), dim3(64 * NW), 0, s, a); break;
+    case MLP_ROUTED: hipLaunchKernelGGL((mlp_kernel<W, MLP_ROUTED, NW>), dim3(grid), dim3(64 * NW), 0, s, a); break;
+    default: hipLaunchKernelGGL((mlp_kernel<W, MLP_SHARED, NW>), dim3(grid), dim3(64 * NW), 0, s, a); break;
   }
   return hipGetLastError();
 }
@@ -608,6 +894,8 @@ hipError_t launch_w(int mode, const MlpArgs& a, int grid, hipStream_t s) {
 bool mlp_width_supported(int W) { return W == 128 || W == 256 || W == 512 || W == 768; }
 
 int mlp_bm_for_width(int W) { return W <= 256 ? 128 : 64; }
+
+bool mlp_pairs_positions(int W) { return mlp_waves(W) == 8; }
 
 hipError_t launch_mlp(int mode, int W, const MlpArgs& a, int tiles, int workers, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;

@@ -130,6 +130,8 @@ __global__ __launch_bounds__(BK_NT) void bucket_kernel(const BucketArgs a) {
   const int chunk = (a.B + BK_NT - 1) / BK_NT;
   const int b0 = min(a.B, t * chunk), b1 = min(a.B, b0 + chunk);
 
+  // the routed MLP launched next takes its tiles from these queues
+  if (p == 0 && t < 8) a.qhead[t] = 0;
   for (int e = 0; e < E; ++e) cnt[e * BK_NT + t] = 0;
   for (int b = b0; b < b1; ++b)
     for (int s = 0; s < k; ++s) cnt[a.idx[((size_t)b * a.P + p) * k + s] * BK_NT + t] += 1;
