@@ -44,6 +44,7 @@ struct tmx_ctx {
   int* ntiles = nullptr;                       // [P]
   int* counts = nullptr;                       // [P][E]
   int* qhead = nullptr;                        // [8] routed-MLP tile queues
+  int* hist = nullptr;                         // [P][ceil(B/64)][E] router choices per chunk
   uint16_t* part = nullptr;                    // [B_max][P][k][W] bf16
   std::vector<void*> allocs;
   std::string err;
@@ -264,13 +265,13 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   r.B = B; r.P = P; r.E = cfg.E; r.top_k = cfg.top_k; r.alpha = c->alpha; r.eps = cfg.eps; r.map = map;
   r.x = static_cast<const uint16_t*>(x_in); r.gain = gain;
   r.wr = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_ROUTER).ptr);
-  r.xhat = c->xhat; r.idx = c->idx; r.gate = c->gate;
+  r.xhat = c->xhat; r.idx = c->idx; r.gate = c->gate; r.hist = c->hist;
   tmx_status s = check_launch(c, launch_norm_route(W, r, st), "router launch");
   if (s != TMX_OK) return s;
 
   BucketArgs k{};
   k.B = B; k.P = P; k.E = cfg.E; k.top_k = cfg.top_k; k.bm = bm; k.max_tiles = moe_max_tiles(cfg, sub, B);
-  k.idx = c->idx; k.rows = c->rows; k.tiles = c->tiles; k.ntiles = c->ntiles; k.counts = c->counts; k.qhead = c->qhead;
+  k.idx = c->idx; k.rows = c->rows; k.tiles = c->tiles; k.ntiles = c->ntiles; k.counts = c->counts; k.qhead = c->qhead; k.hist = c->hist;
   s = check_launch(c, launch_bucket(k, st), "bucket launch");
   if (s != TMX_OK) return s;
 
@@ -401,6 +402,8 @@ tmx_status tmx_create(const tmx_config* cfg, int device, tmx_ctx** out) {
     if ((s = dev_alloc(c, (void**)&c->ntiles, Pmax * 4, "bucket tiles")) != TMX_OK) return bail(s);
     if ((s = dev_alloc(c, (void**)&c->counts, (int64_t)Pmax * C.E * 4, "bucket counts")) != TMX_OK) return bail(s);
     if ((s = dev_alloc(c, (void**)&c->qhead, 8 * 4, "tile queues")) != TMX_OK) return bail(s);
+    if ((s = dev_alloc(c, (void**)&c->hist, (int64_t)Pmax * ((C.B_max + 63) / 64) * C.E * 4, "router counts")) != TMX_OK)
+      return bail(s);
     if ((s = dev_alloc(c, (void**)&c->part, part * 2, "expert partials")) != TMX_OK) return bail(s);
   }
   *out = c;

@@ -58,6 +58,7 @@ struct RouteArgs {
   uint16_t* xhat;          // [P][B][W] (nullable)
   int32_t* idx;            // [B][P][top_k]
   float* gate;             // [B][P][top_k]
+  int* hist;               // nullable: [P][ceil(B/64)][E] choices per 64-row chunk
 };
 
 struct BucketArgs {
@@ -67,6 +68,7 @@ struct BucketArgs {
   int4* tiles;             // [P][max_tiles]
   int* ntiles;             // [P]
   int* counts;             // [P][E]
+  const int* hist;         // [P][ceil(B/64)][E] from norm_route
   int* qhead;              // [8] tile-queue heads of the routed MLP, zeroed here
 };
 

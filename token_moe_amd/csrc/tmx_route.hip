@@ -23,28 +23,105 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
 //   gate   = alpha * pi[chosen]     (not renormalised)
 // Each lane holds its rows' elements directly in the MFMA A-fragment layout
 // (row l%16, k = 32*kb + 8*(l/16) + i), so x_hat never goes through LDS; the
-// 16 x E logits are transposed through LDS for the per-row selection.
+// selection runs on the MFMA output layout with cross-lane reductions. The
+// workgroup (64 rows of one position) also counts its choices per expert
+// for the bucket kernel.
 // ---------------------------------------------------------------------------
 constexpr int RT_WAVES = 4;
 
-template <int W>
+// 16-lane butterflies on DPP (one DPP row = 16 lanes = the lanes holding one
+// row's logits): quad xor 1, quad xor 2, half-row mirror, row mirror leave
+// the reduction of all 16 lanes in every lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+constexpr int DPP_QXOR1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int DPP_QXOR2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int DPP_HMIRROR = 0x141; // row_half_mirror
+constexpr int DPP_MIRROR = 0x140;  // row_mirror
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<DPP_QXOR1>(v));
+  v = fmaxf(v, dpp_f<DPP_QXOR2>(v));
+  v = fmaxf(v, dpp_f<DPP_HMIRROR>(v));
+  return fmaxf(v, dpp_f<DPP_MIRROR>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<DPP_QXOR1>(v);
+  v += dpp_f<DPP_QXOR2>(v);
+  v += dpp_f<DPP_HMIRROR>(v);
+  return v + dpp_f<DPP_MIRROR>(v);
+}
+// (value, index) maximum: larger value, lower index on ties
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& bv, int& be) {
+  const float ov = dpp_f<CTRL>(bv);
+  const int oe = dpp_i<CTRL>(be);
+  if (ov > bv || (ov == bv && oe < be)) {
+    bv = ov;
+    be = oe;
+  }
+}
+__device__ __forceinline__ void row16_argmax(float& bv, int& be) {
+  argmax_step<DPP_QXOR1>(bv, be);
+  argmax_step<DPP_QXOR2>(bv, be);
+  argmax_step<DPP_HMIRROR>(bv, be);
+  argmax_step<DPP_MIRROR>(bv, be);
+}
+
+template <int W, int NBE>
 __global__ __launch_bounds__(64 * RT_WAVES) void norm_route_kernel(const RouteArgs a) {
   constexpr int KB = W / 32;
   constexpr int EMAX = 64;
-  __shared__ float lg_s[RT_WAVES][16][EMAX + 1];
+  constexpr int NFR = KB * NBE;              // router fragments of one position
+  __shared__ int hist_s[EMAX];
+  __shared__ __attribute__((aligned(16))) uint16_t wr_s[NFR * FRAG_ELEMS];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, q = lane >> 4;
   const int tiles = (a.B + 16 * RT_WAVES - 1) / (16 * RT_WAVES);
   const int p = blockIdx.x / tiles;
-  const int row = (blockIdx.x % tiles) * 16 * RT_WAVES + wave * 16 + l16;
+  const int chunk = blockIdx.x % tiles;
+  const int row = chunk * 16 * RT_WAVES + wave * 16 + l16;
   const bool valid = row < a.B;
+  if (a.hist)
+    for (int e = threadIdx.x; e < a.E; e += blockDim.x) hist_s[e] = 0;
+  // the position's router fragments, staged once for the four waves
+  {
+    const uint16_t* src = a.wr + (size_t)p * NFR * FRAG_ELEMS;
+    for (int i = threadIdx.x * 8; i < NFR * FRAG_ELEMS; i += 64 * RT_WAVES * 8)
+      *reinterpret_cast<uint4*>(&wr_s[i]) = ldg16(src + i);
+  }
 
+  // row offset + column offsets of this lane's 8-column runs (k-blocks of
+  // 32 columns, the lane's quarter q); the Mix map's division by D/H is
+  // stepped through instead of repeated
+  const int64_t rbase = (int64_t)(valid ? row : 0) * a.map.T * a.map.D;
   uint4 xr[KB];
   float ss = 0.f;
+  {
+    const int dh = a.map.mix ? a.map.dh : W;
+    int seg = (q * 8) / dh, j = q * 8 - seg * dh;
+    const int64_t pbase = a.map.mix ? (int64_t)p * a.map.dh : (int64_t)p * a.map.D;
+    const int64_t segstride = a.map.mix ? a.map.D : 0;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int64_t off = rbase + pbase + seg * segstride + j;
+      xr[kb] = valid ? ldg16(a.x + off) : make_uint4(0, 0, 0, 0);
+      j += 32;
+      while (j >= dh) {
+        j -= dh;
+        ++seg;
+      }
+    }
+  }
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    xr[kb] = valid ? ldg16(a.x + a.map.offset(row, p, kb * 32 + q * 8)) : make_uint4(0, 0, 0, 0);
     const uint16_t* h = reinterpret_cast<const uint16_t*>(&xr[kb]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -56,137 +133,164 @@ __global__ __launch_bounds__(64 * RT_WAVES) void norm_route_kernel(const RouteAr
   ss += __shfl_xor(ss, 16, 64);
   ss += __shfl_xor(ss, 32, 64);
   const float rinv = 1.0f / sqrtf(ss / (float)W + a.eps);
-
-  const int NBE = a.E / 16;
-  f32x4 lg[EMAX / 16];
+  __syncthreads();                           // router fragments staged
+  // the rows stay packed between the two passes: without this fence the
+  // compiler keeps the first pass's fp32 copies (2 registers per element)
 #pragma unroll
-  for (int j = 0; j < EMAX / 16; ++j) lg[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint16_t* wr = a.wr + (size_t)p * KB * NBE * FRAG_ELEMS;
+  for (int kb = 0; kb < KB; ++kb) asm volatile("" : "+v"(xr[kb].x), "+v"(xr[kb].y), "+v"(xr[kb].z), "+v"(xr[kb].w));
+
+  f32x4 lg[NBE];
+#pragma unroll
+  for (int j = 0; j < NBE; ++j) lg[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* wr = wr_s + lane * 8;
 
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     uint16_t* h = reinterpret_cast<uint16_t*>(&xr[kb]);
+    const float4 g0 = *reinterpret_cast<const float4*>(a.gain + kb * 32 + q * 8);
+    const float4 g1 = *reinterpret_cast<const float4*>(a.gain + kb * 32 + q * 8 + 4);
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = f2bf(bf2f(h[i]) * rinv * a.gain[kb * 32 + q * 8 + i]);
+    for (int i = 0; i < 8; ++i) h[i] = f2bf(bf2f(h[i]) * rinv * gv[i]);
     if (valid && a.xhat)
       *reinterpret_cast<uint4*>(a.xhat + ((size_t)p * a.B + row) * W + kb * 32 + q * 8) = xr[kb];
     const bf16x8 af = as_bf16x8(xr[kb]);
 #pragma unroll
-    for (int j = 0; j < EMAX / 16; ++j)
-      if (j < NBE) lg[j] = mfma16x16x32(af, as_bf16x8(ldg16(wr + ((size_t)kb * NBE + j) * FRAG_ELEMS + lane * 8)), lg[j]);
+    for (int j = 0; j < NBE; ++j)
+      lg[j] = mfma16x16x32(af, as_bf16x8(*reinterpret_cast<const uint4*>(wr + (kb * NBE + j) * FRAG_ELEMS)), lg[j]);
   }
 
-  // C layout: lane holds logits[row 4q+v][expert 16j + l16]
+  // Softmax and top-k per row. C layout: lane (l16, q) holds the logits of
+  // rows 4q+v (v = 0..3) for experts 16j + l16, so a row's E logits sit in
+  // the 16 lanes of one DPP row and every reduction is a 16-lane butterfly.
+  // Selection key: larger logit first, the lower expert index on ties.
+  const int rb0 = chunk * 16 * RT_WAVES + wave * 16 + 4 * q;
 #pragma unroll
-  for (int j = 0; j < EMAX / 16; ++j)
-    if (j < NBE)
+  for (int v = 0; v < 4; ++v) {
+    float m = lg[0][v];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) lg_s[wave][q * 4 + v][j * 16 + l16] = lg[j][v];
-  __syncthreads();
-
-  if (q == 0 && valid) {
-    const float* l = lg_s[wave][l16];
-    float m = l[0];
-    for (int e = 1; e < a.E; ++e) m = fmaxf(m, l[e]);
+    for (int j = 1; j < NBE; ++j) m = fmaxf(m, lg[j][v]);
+    m = row16_max(m);
     float den = 0.f;
-    for (int e = 0; e < a.E; ++e) den += expf(l[e] - m);
-    uint64_t taken = 0;
-    const size_t o = ((size_t)row * a.P + p) * a.top_k;
+#pragma unroll
+    for (int j = 0; j < NBE; ++j) den += expf(lg[j][v] - m);
+    den = row16_sum(den);
+    const int r = rb0 + v;
+    const size_t o_rk = ((size_t)r * a.P + p) * a.top_k;
+    uint32_t taken = 0;
     for (int s = 0; s < a.top_k; ++s) {
-      int be = -1;
-      float bl = 0.f;
-      for (int e = 0; e < a.E; ++e) {
-        if ((taken >> e) & 1ull) continue;
-        if (be < 0 || l[e] > bl) {  // strict: ties keep the lower index
-          be = e;
-          bl = l[e];
+      float bv = -INFINITY;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int j = 0; j < NBE; ++j)
+        if (!((taken >> j) & 1u) && lg[j][v] > bv) {   // j ascending: ties keep the lower index
+          bv = lg[j][v];
+          be = 16 * j + l16;
         }
+      row16_argmax(bv, be);
+      if ((be & 15) == l16) taken |= 1u << (be >> 4);
+      if (r < a.B && l16 == (s & 15)) {
+        a.idx[o_rk + s] = be;
+        a.gate[o_rk + s] = a.alpha * (expf(bv - m) / den);
+        if (a.hist) atomicAdd(&hist_s[be], 1);
       }
-      taken |= 1ull << be;
-      a.idx[o + s] = be;
-      a.gate[o + s] = a.alpha * (expf(bl - m) / den);
     }
+  }
+  if (a.hist) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < a.E; e += blockDim.x)
+      a.hist[((size_t)p * tiles + chunk) * a.E + e] = hist_s[e];
   }
 }
 
 // ---------------------------------------------------------------------------
 // bucket: MoEPermute of the TokenMixer-Large systems section (2.5.1) --
-// rows reordered from batch-first to expert-first.  One workgroup per
-// position.  Thread t owns a contiguous run of batch rows; per-(expert,
-// thread) counts are scanned in (expert, thread) order, so every expert's
-// list is in ascending batch order (stable, deterministic).  Also emits the
-// tile list (expert, start, count) the grouped MLP walks.
+// rows reordered from batch-first to expert-first. One workgroup per
+// (position, 64-row chunk): from the router's per-chunk expert counts it
+// takes the start of its chunk's entries in every expert list, then places
+// its entries in (row, slot) order with wave ballots, so every list is in
+// ascending (batch row, slot) order (stable, deterministic). Workgroup
+// (p, 0) also emits the tile list (expert, start, count) the grouped MLP
+// walks and the per-expert counts.
 // ---------------------------------------------------------------------------
 constexpr int BK_NT = 256;
 constexpr int BK_EMAX = 64;
+constexpr int BK_ROWS = 16 * RT_WAVES;   // rows per chunk, as counted by norm_route
 
 __global__ __launch_bounds__(BK_NT) void bucket_kernel(const BucketArgs a) {
-  __shared__ int cnt[BK_EMAX * BK_NT];
-  __shared__ int part_s[BK_NT];
-  __shared__ int tstart[BK_EMAX + 1];
-  const int t = threadIdx.x;
-  const int p = blockIdx.x;
+  __shared__ int base_s[BK_EMAX];          // start of this chunk's entries per expert
+  __shared__ int tot_s[BK_EMAX];
+  __shared__ int wcnt[BK_NT / 64][BK_EMAX];
+  __shared__ int run_s[BK_EMAX];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int E = a.E, k = a.top_k;
-  const int chunk = (a.B + BK_NT - 1) / BK_NT;
-  const int b0 = min(a.B, t * chunk), b1 = min(a.B, b0 + chunk);
-
+  const int C = (a.B + BK_ROWS - 1) / BK_ROWS;
+  const int p = blockIdx.x / C, c = blockIdx.x % C;
   // the routed MLP launched next takes its tiles from these queues
-  if (p == 0 && t < 8) a.qhead[t] = 0;
-  for (int e = 0; e < E; ++e) cnt[e * BK_NT + t] = 0;
-  for (int b = b0; b < b1; ++b)
-    for (int s = 0; s < k; ++s) cnt[a.idx[((size_t)b * a.P + p) * k + s] * BK_NT + t] += 1;
-  __syncthreads();
+  if (blockIdx.x == 0 && t < 8) a.qhead[t] = 0;
 
-  // exclusive scan over the flattened (expert, thread) array; thread t owns
-  // the E consecutive entries [t*E, (t+1)*E)
-  int local = 0;
-  for (int i = 0; i < E; ++i) local += cnt[t * E + i];
-  part_s[t] = local;
-  __syncthreads();
-  for (int off = 1; off < BK_NT; off <<= 1) {
-    const int v = (t >= off) ? part_s[t - off] : 0;
-    __syncthreads();
-    part_s[t] += v;
-    __syncthreads();
-  }
-  int run = part_s[t] - local;
-  for (int i = 0; i < E; ++i) {
-    const int c = cnt[t * E + i];
-    cnt[t * E + i] = run;
-    run += c;
-  }
-  __syncthreads();
-
-  int* rows = a.rows + (size_t)p * a.B * k;
-  for (int b = b0; b < b1; ++b)
-    for (int s = 0; s < k; ++s) {
-      const int e = a.idx[((size_t)b * a.P + p) * k + s];
-      const int pos = cnt[e * BK_NT + t]++;
-      rows[pos] = b * k + s;
+  if (t < E) {
+    int tot = 0, pre = 0;
+    const int* h = a.hist + (size_t)p * C * E + t;
+    for (int cc = 0; cc < C; ++cc) {
+      const int n = h[(size_t)cc * E];
+      tot += n;
+      if (cc < c) pre += n;
     }
+    tot_s[t] = tot;
+    base_s[t] = pre;
+    run_s[t] = 0;
+  }
   __syncthreads();
-
-  // counts and tiles (cnt[e*NT + NT-1] now holds the end of expert e)
   if (t == 0) {
-    int nt = 0;
+    int off = 0;
     for (int e = 0; e < E; ++e) {
-      tstart[e] = nt;
-      const int beg = (e == 0) ? 0 : cnt[(e - 1) * BK_NT + BK_NT - 1];
-      const int end = cnt[e * BK_NT + BK_NT - 1];
-      nt += (end - beg + a.bm - 1) / a.bm;
+      base_s[e] += off;
+      off += tot_s[e];
     }
-    tstart[E] = nt;
+  }
+  __syncthreads();
+
+  // tiles and counts of the position
+  if (c == 0 && t == 0) {
+    int nt = 0, off = 0;
+    int4* tl = a.tiles + (size_t)p * a.max_tiles;
+    for (int e = 0; e < E; ++e) {
+      const int n = tot_s[e];
+      a.counts[(size_t)p * E + e] = n;
+      for (int s0 = 0; s0 < n; s0 += a.bm) tl[nt++] = make_int4(e, off + s0, min(a.bm, n - s0), 0);
+      off += n;
+    }
     a.ntiles[p] = nt;
   }
-  __syncthreads();
-  if (t < E) {
-    const int e = t;
-    const int beg = (e == 0) ? 0 : cnt[(e - 1) * BK_NT + BK_NT - 1];
-    const int end = cnt[e * BK_NT + BK_NT - 1];
-    a.counts[(size_t)p * E + e] = end - beg;
-    int4* tl = a.tiles + (size_t)p * a.max_tiles;
-    int j = tstart[e];
-    for (int s0 = beg; s0 < end; s0 += a.bm) tl[j++] = make_int4(e, s0, min(a.bm, end - s0), 0);
+
+  const int r0 = c * BK_ROWS;
+  const int nent = min(BK_ROWS, a.B - r0) * k;
+  int* rows = a.rows + (size_t)p * a.B * k;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes below this one
+  for (int i0 = 0; i0 < nent; i0 += BK_NT) {
+    const int id = i0 + t;
+    const int b = r0 + id / k, sl = id % k;
+    const int e = id < nent ? a.idx[((size_t)b * a.P + p) * k + sl] : -1;
+    int rank = 0;
+    for (int ee = 0; ee < E; ++ee) {
+      const uint64_t m = __ballot(e == ee);
+      if (e == ee) rank = __popcll(m & lt);
+      if (lane == 0) wcnt[wave][ee] = __popcll(m);
+    }
+    __syncthreads();
+    if (e >= 0) {
+      int pos = base_s[e] + run_s[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+      rows[pos] = b * k + sl;
+    }
+    __syncthreads();
+    if (t < E) {
+      int n = 0;
+      for (int w = 0; w < BK_NT / 64; ++w) n += wcnt[w][t];
+      run_s[t] += n;
+    }
+    __syncthreads();
   }
 }
 
@@ -244,11 +348,22 @@ __global__ void permute_kernel(const TE* __restrict__ in, TE* __restrict__ out, 
   }
 }
 
+template <int W, int NBE>
+hipError_t launch_route_wn(const RouteArgs& a, hipStream_t s) {
+  const int tiles = (a.B + 16 * RT_WAVES - 1) / (16 * RT_WAVES);
+  hipLaunchKernelGGL((norm_route_kernel<W, NBE>), dim3(a.P * tiles), dim3(64 * RT_WAVES), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int W>
 hipError_t launch_route_w(const RouteArgs& a, hipStream_t s) {
-  const int tiles = (a.B + 16 * RT_WAVES - 1) / (16 * RT_WAVES);
-  hipLaunchKernelGGL((norm_route_kernel<W>), dim3(a.P * tiles), dim3(64 * RT_WAVES), 0, s, a);
-  return hipGetLastError();
+  switch (a.E / 16) {
+    case 1: return launch_route_wn<W, 1>(a, s);
+    case 2: return launch_route_wn<W, 2>(a, s);
+    case 3: return launch_route_wn<W, 3>(a, s);
+    case 4: return launch_route_wn<W, 4>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -264,7 +379,8 @@ hipError_t launch_norm_route(int W, const RouteArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(bucket_kernel, dim3(a.P), dim3(BK_NT), 0, s, a);
+  const int C = (a.B + BK_ROWS - 1) / BK_ROWS;
+  hipLaunchKernelGGL(bucket_kernel, dim3(a.P * C), dim3(BK_NT), 0, s, a);
   return hipGetLastError();
 }
 
