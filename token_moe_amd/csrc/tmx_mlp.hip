@@ -482,6 +482,12 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
   }
 
   while (true) {
+    // ROUTED: the next tile's bucket entry of row tid, loaded now so that its
+    // latency is spent under this tile's main loop
+    int nent = 0;
+    if constexpr (MODE == MLP_ROUTED)
+      if (has_nx && tid < nx.nrows) nent = a.rows[(size_t)nx.p * a.B * a.top_k + nx.start + tid];
+
     // ---- main loop ---------------------------------------------------------------
     f32x16 oacc[RBW][NBO];
 #pragma unroll
@@ -727,7 +733,26 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
     // ---- between tiles: stage O, start the next tile's loads, epilogue --------
     // The ring already holds the next tile's first fragments (see refill).
     const bool has_next = has_nx;
-    if (has_next) set_rows(nx, buf ^ 1);
+    float ngate = 0.f;                     // ROUTED: gate of the next tile's row tid
+    if (has_next) {
+      if constexpr (MODE == MLP_ROUTED) {
+        // row table of the next tile from the entry loaded before the main
+        // loop; its gate is stored after this epilogue (only the next
+        // epilogue reads it), so that load is not waited for here
+        if (tid < BM) {
+          int b = -1, gi = 0;
+          if (tid < nx.nrows) {
+            b = nent / a.top_k;
+            gi = (b * a.P + nx.p) * a.top_k + (nent - b * a.top_k);
+            ngate = a.gate[gi];
+          }
+          rowb[buf ^ 1][tid] = b;
+          rowgi[buf ^ 1][tid] = gi;
+        }
+      } else {
+        set_rows(nx, buf ^ 1);
+      }
+    }
     // the tile after next (read back after the staging barriers below)
     if (MODE == MLP_ROUTED && has_next && tid == 0) qslot = atomicAdd(&a.qhead[qx], 1);
     // an opaque copy of the thread index: keeps the compiler from hoisting
@@ -861,6 +886,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
       }
     }
     if (!has_next) break;
+    if (MODE == MLP_ROUTED && tid < BM) rowg[buf ^ 1][tid] = ngate;
     const int knext = qslot;
     __syncthreads();                       // staging reads done before x_hat is rewritten
     store_x(etid, px, pg);

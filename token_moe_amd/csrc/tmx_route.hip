@@ -222,6 +222,8 @@ __global__ __launch_bounds__(BK_NT) void bucket_kernel(const BucketArgs a) {
   __shared__ int tot_s[BK_EMAX];
   __shared__ int wcnt[BK_NT / 64][BK_EMAX];
   __shared__ int run_s[BK_EMAX];
+  __shared__ int gtot[BK_NT / 16][BK_EMAX];   // per chunk-group partial counts (E >= 16)
+  __shared__ int gpre[BK_NT / 16][BK_EMAX];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int E = a.E, k = a.top_k;
   const int C = (a.B + BK_ROWS - 1) / BK_ROWS;
@@ -229,13 +231,29 @@ __global__ __launch_bounds__(BK_NT) void bucket_kernel(const BucketArgs a) {
   // the routed MLP launched next takes its tiles from these queues
   if (blockIdx.x == 0 && t < 8) a.qhead[t] = 0;
 
+  // chunk counts of the position: thread (group g, expert e) sums chunks
+  // g, g + G, ...; the G partial sums per expert are then added in LDS
+  {
+    const int G = BK_NT / E;
+    const int e = t % E, g = t / E;
+    int tot = 0, pre = 0;
+    if (g < G) {
+      const int* h = a.hist + (size_t)p * C * E + e;
+      for (int cc = g; cc < C; cc += G) {
+        const int n = h[(size_t)cc * E];
+        tot += n;
+        if (cc < c) pre += n;
+      }
+      gtot[g][e] = tot;
+      gpre[g][e] = pre;
+    }
+  }
+  __syncthreads();
   if (t < E) {
     int tot = 0, pre = 0;
-    const int* h = a.hist + (size_t)p * C * E + t;
-    for (int cc = 0; cc < C; ++cc) {
-      const int n = h[(size_t)cc * E];
-      tot += n;
-      if (cc < c) pre += n;
+    for (int g = 0; g < BK_NT / E; ++g) {
+      tot += gtot[g][t];
+      pre += gpre[g][t];
     }
     tot_s[t] = tot;
     base_s[t] = pre;
