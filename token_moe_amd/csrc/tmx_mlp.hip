@@ -44,7 +44,7 @@ namespace {
 // (W = 768). 4 waves (one per SIMD, 512 registers each, every wave on all BM
 // rows) double the reuse of each weight fragment where BM is only 64
 // (W = 512) and serve W = 128.
-constexpr int mlp_waves(int W) { return (W == 256 || W > 512) ? 8 : 4; }
+constexpr int mlp_waves(int W) { return W == 256 ? 8 : 4; }
 
 template <int W, int NW>
 struct MlpShape {
@@ -59,7 +59,7 @@ struct MlpShape {
   static constexpr int S1 = W / 16;                 // GEMM1 k-steps per chunk
   static constexpr int S2 = HC / 16;                // GEMM2 k-steps per chunk
   static constexpr int S = S1 + S2;
-  static constexpr int DEPTH = (NW == 4) ? 4 : (W <= 256) ? 8 : (W <= 512) ? 4 : 2;  // weight prefetch distance (steps)
+  static constexpr int DEPTH = (NW == 4) ? (W <= 512 ? 4 : 2) : (W <= 256) ? 8 : (W <= 512) ? 4 : 2;  // weight prefetch distance (steps)
   static constexpr int NBR = NBO > 2 ? NBO : 2;     // fragments per step
   static constexpr int YS = (S1 - S2) / 2;          // ping-pong barrier step inside GEMM1
   static_assert(W % 128 == 0, "W must be a multiple of 128");
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
   constexpr int SBYTES = (BM / NPART) * SS * 4;
   constexpr int SMEM = (XBYTES + UBYTES > SBYTES) ? XBYTES + UBYTES : SBYTES;
   static_assert(SMEM + ROWTAB <= 160 * 1024, "LDS budget");
-  static_assert(NW == 8 || NPART == 1, "one wave per SIMD stages all rows at once");
+  static_assert(NW == 8 || NPART == 1 || RBW == NPART, "4 waves stage one row block per part");
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ int rowb[2][BM];
   __shared__ int rowgi[2][BM];       // ROUTED: flat (b, p, slot) index of the row
@@ -776,21 +776,24 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
 #pragma unroll
     for (int part = 0; part < NPART; ++part) {
       __syncthreads();
-      if (NPART == 1 || wr == part) {
+      if (NPART == 1 || NW == 4 || wr == part) {
         // C layout of an O^T block (32 columns x 32 rows): lane holds row l32
         // and columns 8*(v/4) + 4*h32 + v%4 -> 4 consecutive columns per v-group
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb)
+        for (int rb = 0; rb < RBW; ++rb) {
+          // parts of 4-wave tiles are row blocks: part p stages block p
+          if (NW == 4 && NPART > 1 && rb != part) continue;
 #pragma unroll
           for (int j = 0; j < NBO; ++j)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-              const int r = (NPART == 1 ? row0 : 0) + rb * 32 + l32;
+              const int r = (NPART == 1 ? row0 + rb * 32 : (NW == 4 ? 0 : rb * 32)) + l32;
               const int col = (wc * NBO + j) * 32 + 8 * g4 + 4 * h32;
               *reinterpret_cast<float4*>(&stage[r * SS + col]) =
                   make_float4(oacc[rb][j][4 * g4], oacc[rb][j][4 * g4 + 1], oacc[rb][j][4 * g4 + 2],
                               oacc[rb][j][4 * g4 + 3]);
             }
+        }
       }
       __syncthreads();
       if (part == NPART - 1) {
