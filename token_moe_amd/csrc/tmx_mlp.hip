@@ -675,59 +675,72 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
         }
       };
 
-      // preamble: stream positions q < S1 are GEMM1(0); beyond, GEMM1(1) of
-      // iteration 1, or with a single chunk the postamble's GEMM2(0)
-      gemm1([&](uint4* dst, int q2) __attribute__((always_inline)) {
-              if (q2 < S1) {
-                issue(dst, cw, 0, q2);
-              } else if (NC > 1) {
-                issue(dst, cw, 1, q2 - S1);
-              } else {
-                issue(dst, cw, 0, q2);
-              }
-            },
-            [] {});
-#pragma unroll
-      for (int gi = 0; gi < RBW * 4; ++gi) u_group(us, gi);
-      __syncthreads();
-
-      // iterations: positions [0, S1) GEMM1(i), [S1, NS) GEMM2(i-1); past
-      // NS the next iteration's GEMM1(i+1), or for the last iteration the
-      // postamble's GEMM2(NC-1)
-      auto iteration = [&](int i, auto last_tag) __attribute__((always_inline)) {
-        constexpr bool LAST = decltype(last_tag)::value;
-        uint16_t* ubw = us + (i & 1) * BM * US;
-        const uint16_t* ubr = us + ((i - 1) & 1) * BM * US;
-        auto refill_at = [&](uint4* dst, int q2) __attribute__((always_inline)) {
-          if (q2 < S1) {
-            issue(dst, cw, i, q2);
-          } else if (q2 < NS) {
-            issue(dst, cw, i - 1, q2);
-          } else if (!LAST) {
-            issue(dst, cw, i + 1, q2 - NS);
-          } else {
-            issue(dst, cw, NC - 1, q2 - NS + S1);
-          }
-        };
-        gemm1(refill_at, [&] { read_ua(ua[0], ubr, 0); });
-        gemm2(ubr, ubw, std::true_type{}, refill_at, std::integral_constant<int, S1>{});
-        __syncthreads();
-      };
-      for (int i = 1; i + 1 < NC; ++i) iteration(i, std::integral_constant<bool, false>{});
-      if (NC > 1) iteration(NC - 1, std::integral_constant<bool, true>{});
-
-      // postamble: GEMM2(NC-1); past its end the stream enters the next
-      // tile's preamble
-      {
-        const uint16_t* ubr = us + ((NC - 1) & 1) * BM * US;
-        read_ua(ua[0], ubr, 0);
-        gemm2(ubr, nullptr, std::false_type{},
-              [&](uint4* dst, int q2) __attribute__((always_inline)) {
-                if (q2 < S2) issue(dst, cw, NC - 1, S1 + q2);
-                else issue(dst, nw, 0, q2 - S2);
+      // The whole chunk loop comes in two copies, for one chunk and for more:
+      // the preamble's look-ahead reads GEMM1(1) fragments (2 loads per
+      // step) or, with a single chunk, GEMM2(0) fragments (NBO loads), and
+      // paths that rejoin with different loads in flight make the compiler
+      // drain them all (vmcnt(0)) at the join.
+      auto chunk_loop = [&](auto more_tag) __attribute__((always_inline)) {
+        constexpr bool MORE = decltype(more_tag)::value;
+        // preamble: stream positions q < S1 are GEMM1(0); beyond, GEMM1(1)
+        // of iteration 1, or with a single chunk the postamble's GEMM2(0)
+        gemm1([&](uint4* dst, int q2) __attribute__((always_inline)) {
+                if (q2 < S1)
+                  issue(dst, cw, 0, q2);
+                else if (MORE)
+                  issue(dst, cw, 1, q2 - S1);
+                else
+                  issue(dst, cw, 0, q2);
               },
-              std::integral_constant<int, 0>{});
-      }
+              [] {});
+#pragma unroll
+        for (int gi = 0; gi < RBW * 4; ++gi) u_group(us, gi);
+        __syncthreads();
+
+        // iterations: positions [0, S1) GEMM1(i), [S1, NS) GEMM2(i-1); past
+        // NS the next iteration's GEMM1(i+1), or for the last iteration the
+        // postamble's GEMM2(NC-1)
+        auto iteration = [&](int i, auto last_tag) __attribute__((always_inline)) {
+          constexpr bool LAST = decltype(last_tag)::value;
+          uint16_t* ubw = us + (i & 1) * BM * US;
+          const uint16_t* ubr = us + ((i - 1) & 1) * BM * US;
+          auto refill_at = [&](uint4* dst, int q2) __attribute__((always_inline)) {
+            if (q2 < S1) {
+              issue(dst, cw, i, q2);
+            } else if (q2 < NS) {
+              issue(dst, cw, i - 1, q2);
+            } else if (!LAST) {
+              issue(dst, cw, i + 1, q2 - NS);
+            } else {
+              issue(dst, cw, NC - 1, q2 - NS + S1);
+            }
+          };
+          gemm1(refill_at, [&] { read_ua(ua[0], ubr, 0); });
+          gemm2(ubr, ubw, std::true_type{}, refill_at, std::integral_constant<int, S1>{});
+          __syncthreads();
+        };
+        if constexpr (MORE) {
+          for (int i = 1; i + 1 < NC; ++i) iteration(i, std::integral_constant<bool, false>{});
+          iteration(NC - 1, std::integral_constant<bool, true>{});
+        }
+
+        // postamble: GEMM2(NC-1); past its end the stream enters the next
+        // tile's preamble
+        {
+          const uint16_t* ubr = us + ((NC - 1) & 1) * BM * US;
+          read_ua(ua[0], ubr, 0);
+          gemm2(ubr, nullptr, std::false_type{},
+                [&](uint4* dst, int q2) __attribute__((always_inline)) {
+                  if (q2 < S2) issue(dst, cw, NC - 1, S1 + q2);
+                  else issue(dst, nw, 0, q2 - S2);
+                },
+                std::integral_constant<int, 0>{});
+        }
+      };
+      if (NC > 1)
+        chunk_loop(std::true_type{});
+      else
+        chunk_loop(std::false_type{});
     }
 
     // ---- between tiles: stage O, start the next tile's loads, epilogue --------
