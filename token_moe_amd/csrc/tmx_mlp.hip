@@ -524,7 +524,14 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
           xa[0][rb] = *reinterpret_cast<const uint4*>(&xs[(row0 + rb * 32 + l32) * XS + h32 * 8]);
   #pragma unroll
         for (int s = 0; s < S1; ++s) {
-          if (s == YS) __syncthreads();                              // barrier Y
+          if (s == YS) {
+            __syncthreads();                                         // barrier Y
+            // this group computes U before its next barrier: its MFMAs issue
+            // ahead of the other group's, so that its SiLU runs while the
+            // other group's MFMAs keep the pipe busy (the arbiter otherwise
+            // favours the older waves, group A, in both halves)
+            __builtin_amdgcn_s_setprio(2);
+          }
           const int d = s % DEPTH;
           if (s + 1 < S1) {
   #pragma unroll
@@ -562,6 +569,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
           }
         }
         __syncthreads();                                             // barrier X
+        __builtin_amdgcn_s_setprio(0);
 
         // GEMM2: O^T += W_down[chunk]^T U^T, U fragments read one step ahead
         uint4 ua[2][RBW];
