@@ -25,6 +25,14 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+
 __device__ __forceinline__ float silu(float z) {
   // z * sigmoid(z); expf of a large positive argument gives +inf and 1/inf = 0,
   // which is the right limit.

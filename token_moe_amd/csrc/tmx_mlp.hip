@@ -82,14 +82,6 @@ __device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
-}
-
 // silu(z) = z * sigmoid(z) with the hardware exp and reciprocal (~1 ulp
 // each); the result is rounded to bf16 right after, so this is exact enough.
 __device__ __forceinline__ float silu_fast(float z) {

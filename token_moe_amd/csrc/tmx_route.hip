@@ -91,13 +91,6 @@ __global__ __launch_bounds__(64 * RT_WAVES) void norm_route_kernel(const RouteAr
   const bool valid = row < a.B;
   if (a.hist)
     for (int e = threadIdx.x; e < a.E; e += blockDim.x) hist_s[e] = 0;
-  // the position's router fragments, staged once for the four waves
-  {
-    const uint16_t* src = a.wr + (size_t)p * NFR * FRAG_ELEMS;
-    for (int i = threadIdx.x * 8; i < NFR * FRAG_ELEMS; i += 64 * RT_WAVES * 8)
-      *reinterpret_cast<uint4*>(&wr_s[i]) = ldg16(src + i);
-  }
-
   // row offset + column offsets of this lane's 8-column runs (k-blocks of
   // 32 columns, the lane's quarter q); the Mix map's division by D/H is
   // stepped through instead of repeated
@@ -119,6 +112,14 @@ __global__ __launch_bounds__(64 * RT_WAVES) void norm_route_kernel(const RouteAr
         ++seg;
       }
     }
+  }
+  // the position's router fragments, staged once for the four waves (L2
+  // hits after the first workgroup of a position; issued after the row
+  // loads so that those are already in flight)
+  {
+    const uint16_t* src = a.wr + (size_t)p * NFR * FRAG_ELEMS;
+    for (int i = threadIdx.x * 8; i < NFR * FRAG_ELEMS; i += 64 * RT_WAVES * 8)
+      *reinterpret_cast<uint4*>(&wr_s[i]) = ldg16(src + i);
   }
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
@@ -146,12 +147,18 @@ __global__ __launch_bounds__(64 * RT_WAVES) void norm_route_kernel(const RouteAr
 
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    uint16_t* h = reinterpret_cast<uint16_t*>(&xr[kb]);
+    const uint16_t* h = reinterpret_cast<const uint16_t*>(&xr[kb]);
     const float4 g0 = *reinterpret_cast<const float4*>(a.gain + kb * 32 + q * 8);
     const float4 g1 = *reinterpret_cast<const float4*>(a.gain + kb * 32 + q * 8 + 4);
     const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    float n[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = f2bf(bf2f(h[i]) * rinv * gv[i]);
+    for (int i = 0; i < 8; ++i) n[i] = bf2f(h[i]) * rinv * gv[i];
+    // round to nearest even (v_cvt_pk_bf16_f32)
+    xr[kb].x = pack_bf16x2(n[0], n[1]);
+    xr[kb].y = pack_bf16x2(n[2], n[3]);
+    xr[kb].z = pack_bf16x2(n[4], n[5]);
+    xr[kb].w = pack_bf16x2(n[6], n[7]);
     if (valid && a.xhat)
       *reinterpret_cast<uint4*>(a.xhat + ((size_t)p * a.B + row) * W + kb * 32 + q * 8) = xr[kb];
     const bf16x8 af = as_bf16x8(xr[kb]);
@@ -165,34 +172,51 @@ __global__ __launch_bounds__(64 * RT_WAVES) void norm_route_kernel(const RouteAr
   // the 16 lanes of one DPP row and every reduction is a 16-lane butterfly.
   // Selection key: larger logit first, the lower expert index on ties.
   const int rb0 = chunk * 16 * RT_WAVES + wave * 16 + 4 * q;
+  // the lane's four rows are independent: every step below runs on all four
+  // at once, so each DPP butterfly has four chains to interleave
+  float m[4], den[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    float m = lg[0][v];
+    m[v] = lg[0][v];
 #pragma unroll
-    for (int j = 1; j < NBE; ++j) m = fmaxf(m, lg[j][v]);
-    m = row16_max(m);
-    float den = 0.f;
+    for (int j = 1; j < NBE; ++j) m[v] = fmaxf(m[v], lg[j][v]);
+  }
 #pragma unroll
-    for (int j = 0; j < NBE; ++j) den += expf(lg[j][v] - m);
-    den = row16_sum(den);
-    const int r = rb0 + v;
-    const size_t o_rk = ((size_t)r * a.P + p) * a.top_k;
-    uint32_t taken = 0;
-    for (int s = 0; s < a.top_k; ++s) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
+  for (int v = 0; v < 4; ++v) m[v] = row16_max(m[v]);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    den[v] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NBE; ++j) den[v] += expf(lg[j][v] - m[v]);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) den[v] = row16_sum(den[v]);
+  uint32_t taken[4] = {0u, 0u, 0u, 0u};
+  for (int s = 0; s < a.top_k; ++s) {
+    float bv[4];
+    int be[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      bv[v] = -INFINITY;
+      be[v] = 0x7fffffff;
 #pragma unroll
       for (int j = 0; j < NBE; ++j)
-        if (!((taken >> j) & 1u) && lg[j][v] > bv) {   // j ascending: ties keep the lower index
-          bv = lg[j][v];
-          be = 16 * j + l16;
+        if (!((taken[v] >> j) & 1u) && lg[j][v] > bv[v]) {   // j ascending: ties keep the lower index
+          bv[v] = lg[j][v];
+          be[v] = 16 * j + l16;
         }
-      row16_argmax(bv, be);
-      if ((be & 15) == l16) taken |= 1u << (be >> 4);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) row16_argmax(bv[v], be[v]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      if ((be[v] & 15) == l16) taken[v] |= 1u << (be[v] >> 4);
+      const int r = rb0 + v;
       if (r < a.B && l16 == (s & 15)) {
-        a.idx[o_rk + s] = be;
-        a.gate[o_rk + s] = a.alpha * (expf(bv - m) / den);
-        if (a.hist) atomicAdd(&hist_s[be], 1);
+        const size_t o = ((size_t)r * a.P + p) * a.top_k + s;
+        a.idx[o] = be[v];
+        a.gate[o] = a.alpha * (expf(bv[v] - m[v]) / den[v]);
+        if (a.hist) atomicAdd(&hist_s[be[v]], 1);
       }
     }
   }
