@@ -317,6 +317,30 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
     }
   };
 
+  // 4-wave tiles treat the ring as NFR single fragments in stream order:
+  // fragment k of the stream sits in slot k % NFR. A GEMM1 step consumes
+  // 2 fragments and a GEMM2 step NBO, so GEMM1 looks NFR / 2 steps ahead
+  // instead of DEPTH (a weight stream that starts cold -- a new expert --
+  // needs the longer look-ahead). f1 = fragment f of chunk c in that order:
+  // GEMM1 step f / 2 (gate, up), then GEMM2 step (f - F1) / NBO.
+  constexpr int NFR = DEPTH * NBR;
+  constexpr int F1 = 2 * S1, F2 = NBO * S2, FS = F1 + F2;
+  static_assert(NW == 8 || (F1 % NFR == 0 && F2 % NFR == 0),
+                "every GEMM phase must start on a ring boundary");
+  auto fslot = [&](int k) __attribute__((always_inline)) -> uint4& {
+    return ring[(k % NFR) / NBR][(k % NFR) % NBR];
+  };
+  auto issue_frag = [&](uint4& dst, const Stream& w, int c, int f) __attribute__((always_inline)) {
+    c += w.rot;
+    if (c >= NC) c -= NC;
+    if (f < F1) {
+      dst = ldg16(w.gu + ((size_t)((c * 4 + wc) * (W / 16) + f / 2) * 2 + (f & 1)) * FRAG_ELEMS + lane * 8);
+    } else {
+      const int kb = c * (HC / 16) + (f - F1) / NBO;
+      dst = ldg16(w.d + ((size_t)kb * (W / 32) + wc * NBO + (f - F1) % NBO) * FRAG_ELEMS + lane * 8);
+    }
+  };
+
   // ---- row I/O ----------------------------------------------------------------
   // Unit u = (row, 8 columns) of the tile; lane-consecutive units cover one
   // row. Every global access of the rows is one 16-byte vector (8 columns
@@ -462,8 +486,13 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
   set_rows(cur, 0);
   cw = bind(cur);
   nw = has_nx ? bind(nx) : cw;
+  if constexpr (NW == 4) {
 #pragma unroll
-  for (int s = 0; s < DEPTH; ++s) issue(ring[s], cw, 0, s);
+    for (int f = 0; f < NFR; ++f) issue_frag(fslot(f), cw, 0, f);
+  } else {
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) issue(ring[s], cw, 0, s);
+  }
   __syncthreads();
   {
     uint4 v[NPRO];
@@ -625,9 +654,10 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
         w2.y = pack_bf16x2(uv[2], uv[3]);
         *reinterpret_cast<uint2*>(&ub[(rb * 32 + l32) * US + wc * 32 + 8 * g4 + 4 * h32]) = w2;
       };
-      // GEMM1 of chunk c over S1 k-steps; `after(q)` issues the refill for
-      // stream position q + DEPTH and `last` (the final step) may prefetch
-      // the first GEMM2 operands
+      // GEMM1 of chunk c over S1 k-steps; `refill_at(slot, k)` loads the
+      // fragment at position k of the segment's stream (k >= NFR: past the
+      // consumed one by a full ring) and `last` (the final step) may
+      // prefetch the first GEMM2 operands
       auto gemm1 = [&](auto refill_at, auto at_last) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < RBW; ++i) {
@@ -637,16 +667,16 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
         read_xa(xa[0], 0);
 #pragma unroll
         for (int q = 0; q < S1; ++q) {
-          const int d = q % DEPTH;
           if (q + 1 < S1) read_xa(xa[(q + 1) & 1], q + 1);
           else at_last();
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int rb = 0; rb < RBW; ++rb) {
-            sg[rb] = mfma32(ring[d][0], xa[q & 1][rb], sg[rb]);
-            su[rb] = mfma32(ring[d][1], xa[q & 1][rb], su[rb]);
+            sg[rb] = mfma32(fslot(2 * q), xa[q & 1][rb], sg[rb]);
+            su[rb] = mfma32(fslot(2 * q + 1), xa[q & 1][rb], su[rb]);
           }
-          refill_at(ring[d], q + DEPTH);
+          refill_at(fslot(2 * q), 2 * q + NFR);
+          refill_at(fslot(2 * q + 1), 2 * q + 1 + NFR);
           __builtin_amdgcn_sched_barrier(0);
         }
       };
@@ -656,21 +686,22 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
       auto gemm2 = [&](const uint16_t* ub, uint16_t* ubw, auto with_u_tag, auto refill_at, auto pos0_tag)
           __attribute__((always_inline)) {
         constexpr bool with_u = decltype(with_u_tag)::value;
-        constexpr int pos0 = decltype(pos0_tag)::value;
+        constexpr int pos0 = decltype(pos0_tag)::value;   // first fragment's segment position
 #pragma unroll
         for (int t = 0; t < S2; ++t) {
-          const int d = (pos0 + t) % DEPTH;
           if (t + 1 < S2) read_ua(ua[(t + 1) & 1], ub, t + 1);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-            for (int j = 0; j < NBO; ++j) oacc[rb][j] = mfma32(ring[d][j], ua[t & 1][rb], oacc[rb][j]);
+            for (int j = 0; j < NBO; ++j)
+              oacc[rb][j] = mfma32(fslot(pos0 + NBO * t + j), ua[t & 1][rb], oacc[rb][j]);   // O^T block
           if constexpr (with_u) {
 #pragma unroll
             for (int k = 0; k < SPS; ++k) u_group(ubw, t * SPS + k);
           }
-          refill_at(ring[d], pos0 + t + DEPTH);
+#pragma unroll
+          for (int j = 0; j < NBO; ++j) refill_at(fslot(pos0 + NBO * t + j), pos0 + NBO * t + j + NFR);
           __builtin_amdgcn_sched_barrier(0);
         }
       };
@@ -682,41 +713,41 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
       // drain them all (vmcnt(0)) at the join.
       auto chunk_loop = [&](auto more_tag) __attribute__((always_inline)) {
         constexpr bool MORE = decltype(more_tag)::value;
-        // preamble: stream positions q < S1 are GEMM1(0); beyond, GEMM1(1)
+        // preamble: segment positions k < F1 are GEMM1(0); beyond, GEMM1(1)
         // of iteration 1, or with a single chunk the postamble's GEMM2(0)
-        gemm1([&](uint4* dst, int q2) __attribute__((always_inline)) {
-                if (q2 < S1)
-                  issue(dst, cw, 0, q2);
+        gemm1([&](uint4& dst, int k2) __attribute__((always_inline)) {
+                if (k2 < F1)
+                  issue_frag(dst, cw, 0, k2);
                 else if (MORE)
-                  issue(dst, cw, 1, q2 - S1);
+                  issue_frag(dst, cw, 1, k2 - F1);
                 else
-                  issue(dst, cw, 0, q2);
+                  issue_frag(dst, cw, 0, k2);
               },
               [] {});
 #pragma unroll
         for (int gi = 0; gi < RBW * 4; ++gi) u_group(us, gi);
         __syncthreads();
 
-        // iterations: positions [0, S1) GEMM1(i), [S1, NS) GEMM2(i-1); past
-        // NS the next iteration's GEMM1(i+1), or for the last iteration the
+        // iterations: positions [0, F1) GEMM1(i), [F1, FS) GEMM2(i-1); past
+        // FS the next iteration's GEMM1(i+1), or for the last iteration the
         // postamble's GEMM2(NC-1)
         auto iteration = [&](int i, auto last_tag) __attribute__((always_inline)) {
           constexpr bool LAST = decltype(last_tag)::value;
           uint16_t* ubw = us + (i & 1) * BM * US;
           const uint16_t* ubr = us + ((i - 1) & 1) * BM * US;
-          auto refill_at = [&](uint4* dst, int q2) __attribute__((always_inline)) {
-            if (q2 < S1) {
-              issue(dst, cw, i, q2);
-            } else if (q2 < NS) {
-              issue(dst, cw, i - 1, q2);
+          auto refill_at = [&](uint4& dst, int k2) __attribute__((always_inline)) {
+            if (k2 < F1) {
+              issue_frag(dst, cw, i, k2);
+            } else if (k2 < FS) {
+              issue_frag(dst, cw, i - 1, k2);
             } else if (!LAST) {
-              issue(dst, cw, i + 1, q2 - NS);
+              issue_frag(dst, cw, i + 1, k2 - FS);
             } else {
-              issue(dst, cw, NC - 1, q2 - NS + S1);
+              issue_frag(dst, cw, NC - 1, k2 - FS + F1);
             }
           };
           gemm1(refill_at, [&] { read_ua(ua[0], ubr, 0); });
-          gemm2(ubr, ubw, std::true_type{}, refill_at, std::integral_constant<int, S1>{});
+          gemm2(ubr, ubw, std::true_type{}, refill_at, std::integral_constant<int, F1>{});
           __syncthreads();
         };
         if constexpr (MORE) {
@@ -730,9 +761,9 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
           const uint16_t* ubr = us + ((NC - 1) & 1) * BM * US;
           read_ua(ua[0], ubr, 0);
           gemm2(ubr, nullptr, std::false_type{},
-                [&](uint4* dst, int q2) __attribute__((always_inline)) {
-                  if (q2 < S2) issue(dst, cw, NC - 1, S1 + q2);
-                  else issue(dst, nw, 0, q2 - S2);
+                [&](uint4& dst, int k2) __attribute__((always_inline)) {
+                  if (k2 < F2) issue_frag(dst, cw, NC - 1, F1 + k2);
+                  else issue_frag(dst, nw, 0, k2 - F2);
                 },
                 std::integral_constant<int, 0>{});
         }
