@@ -345,21 +345,47 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
   // Unit u = (row, 8 columns) of the tile; lane-consecutive units cover one
   // row. Every global access of the rows is one 16-byte vector (8 columns
   // never straddle a Mix segment since D/H % 8 == 0).
+  // Row loads are issued without branches: every lane reads its row
+  // indices first, rows past the tile end load row 0, and their values are
+  // cleared afterwards, so all NPRO loads go out back to back. (With more
+  // than 16 units per lane, W = 768, the index copies would spill in the
+  // main loop: there each load stays behind its own row check.)
+  constexpr bool FLAT_IO = NPRO <= 16;
   auto load_x = [&](int tix, int buf, const Tile& T, uint4* v) {
+    if constexpr (!FLAT_IO) {
+#pragma unroll
+      for (int i = 0; i < NPRO; ++i) {
+        const int u = tix + i * NT;
+        const int r = u / U8, c8 = u - r * U8;
+        const int b = rowb[buf][r];
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (b >= 0) {
+          const int p = rowpos(T, r);
+          if (MODE == MLP_DENSE)
+            v[i] = ldg16(a.x + uoff(b, p, c8));
+          else
+            v[i] = ldg16(a.xhat + ((size_t)p * a.B + b) * W + c8 * 8);
+        }
+      }
+      return;
+    }
+    int bb[NPRO];
+#pragma unroll
+    for (int i = 0; i < NPRO; ++i) bb[i] = rowb[buf][(tix + i * NT) / U8];
 #pragma unroll
     for (int i = 0; i < NPRO; ++i) {
       const int u = tix + i * NT;
       const int r = u / U8, c8 = u - r * U8;
-      const int b = rowb[buf][r];
-      v[i] = make_uint4(0, 0, 0, 0);
-      if (b >= 0) {
-        const int p = rowpos(T, r);
-        if (MODE == MLP_DENSE)
-          v[i] = ldg16(a.x + uoff(b, p, c8));
-        else
-          v[i] = ldg16(a.xhat + ((size_t)p * a.B + b) * W + c8 * 8);
-      }
+      const int b = bb[i] < 0 ? 0 : bb[i];
+      const int p = rowpos(T, r);
+      if (MODE == MLP_DENSE)
+        v[i] = ldg16(a.x + uoff(b, p, c8));
+      else
+        v[i] = ldg16(a.xhat + ((size_t)p * a.B + b) * W + c8 * 8);
     }
+#pragma unroll
+    for (int i = 0; i < NPRO; ++i)
+      if (bb[i] < 0) v[i] = make_uint4(0, 0, 0, 0);
   };
   // x rows -> LDS x_hat; for DENSE the RMS statistics reduce across the lanes
   // of a row before x_hat is written (RMSNorm in fp32, rho to bf16:
@@ -454,13 +480,28 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
   };
   // residual rows of the tile, same unit order as load_x
   auto load_resid = [&](int tix, int buf, const Tile& T, uint4* rv) {
+    if constexpr (!FLAT_IO) {
+#pragma unroll
+      for (int i = 0; i < NPRO; ++i) {
+        const int u = tix + i * NT;
+        const int r = u / U8, c8 = u - r * U8;
+        const int b = rowb[buf][r];
+        rv[i] = b >= 0 ? ldg16(a.resid + uoff(b, rowpos(T, r), c8)) : make_uint4(0, 0, 0, 0);
+      }
+      return;
+    }
+    int bb[NPRO];
+#pragma unroll
+    for (int i = 0; i < NPRO; ++i) bb[i] = rowb[buf][(tix + i * NT) / U8];
 #pragma unroll
     for (int i = 0; i < NPRO; ++i) {
       const int u = tix + i * NT;
       const int r = u / U8, c8 = u - r * U8;
-      const int b = rowb[buf][r];
-      rv[i] = b >= 0 ? ldg16(a.resid + uoff(b, rowpos(T, r), c8)) : make_uint4(0, 0, 0, 0);
+      rv[i] = ldg16(a.resid + uoff(bb[i] < 0 ? 0 : bb[i], rowpos(T, r), c8));
     }
+#pragma unroll
+    for (int i = 0; i < NPRO; ++i)
+      if (bb[i] < 0) rv[i] = make_uint4(0, 0, 0, 0);
   };
 
   // ---- first tile ---------------------------------------------------------------
