@@ -345,47 +345,51 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
   // Unit u = (row, 8 columns) of the tile; lane-consecutive units cover one
   // row. Every global access of the rows is one 16-byte vector (8 columns
   // never straddle a Mix segment since D/H % 8 == 0).
-  // Row loads are issued without branches: every lane reads its row
-  // indices first, rows past the tile end load row 0, and their values are
-  // cleared afterwards, so all NPRO loads go out back to back. (With more
-  // than 16 units per lane, W = 768, the index copies would spill in the
-  // main loop: there each load stays behind its own row check.)
-  constexpr bool FLAT_IO = NPRO <= 16;
-  auto load_x = [&](int tix, int buf, const Tile& T, uint4* v) {
-    if constexpr (!FLAT_IO) {
-#pragma unroll
-      for (int i = 0; i < NPRO; ++i) {
-        const int u = tix + i * NT;
-        const int r = u / U8, c8 = u - r * U8;
-        const int b = rowb[buf][r];
-        v[i] = make_uint4(0, 0, 0, 0);
-        if (b >= 0) {
-          const int p = rowpos(T, r);
-          if (MODE == MLP_DENSE)
-            v[i] = ldg16(a.x + uoff(b, p, c8));
-          else
-            v[i] = ldg16(a.xhat + ((size_t)p * a.B + b) * W + c8 * 8);
-        }
-      }
-      return;
-    }
-    int bb[NPRO];
-#pragma unroll
-    for (int i = 0; i < NPRO; ++i) bb[i] = rowb[buf][(tix + i * NT) / U8];
-#pragma unroll
-    for (int i = 0; i < NPRO; ++i) {
+  // unit i of lane tix: row r and 8-column group c8. With LANE_COL a lane's
+  // column group is the same for every unit and its rows step by NT / U8,
+  // so both come from tix once instead of per unit.
+  auto unit_rc = [&](int tix, int i, int& r, int& c8) __attribute__((always_inline)) {
+    if constexpr (LANE_COL) {
+      r = tix / U8 + i * (NT / U8);
+      c8 = tix % U8;
+    } else {
       const int u = tix + i * NT;
-      const int r = u / U8, c8 = u - r * U8;
-      const int b = bb[i] < 0 ? 0 : bb[i];
-      const int p = rowpos(T, r);
-      if (MODE == MLP_DENSE)
-        v[i] = ldg16(a.x + uoff(b, p, c8));
-      else
-        v[i] = ldg16(a.xhat + ((size_t)p * a.B + b) * W + c8 * 8);
+      r = u / U8;
+      c8 = u - r * U8;
     }
+  };
+  // Row loads are issued without branches, IOB units at a time: the lane
+  // reads the batch's row indices first, rows past the tile end load row 0
+  // and are cleared afterwards, so the batch's loads go out back to back.
+  // (Batches of 8 at W = 768, 24 units per lane: all index copies at once
+  // would spill in the main loop.)
+  constexpr int IOB = NPRO <= 16 ? NPRO : 8;
+  static_assert(NPRO % IOB == 0, "row-load batches must divide the units per lane");
+  auto load_x = [&](int tix, int buf, const Tile& T, uint4* v) {
 #pragma unroll
-    for (int i = 0; i < NPRO; ++i)
-      if (bb[i] < 0) v[i] = make_uint4(0, 0, 0, 0);
+    for (int i0 = 0; i0 < NPRO; i0 += IOB) {
+      int bb[IOB];
+#pragma unroll
+      for (int k = 0; k < IOB; ++k) {
+        int r, c8;
+        unit_rc(tix, i0 + k, r, c8);
+        bb[k] = rowb[buf][r];
+      }
+#pragma unroll
+      for (int k = 0; k < IOB; ++k) {
+        int r, c8;
+        unit_rc(tix, i0 + k, r, c8);
+        const int b = bb[k] < 0 ? 0 : bb[k];
+        const int p = rowpos(T, r);
+        if (MODE == MLP_DENSE)
+          v[i0 + k] = ldg16(a.x + uoff(b, p, c8));
+        else
+          v[i0 + k] = ldg16(a.xhat + ((size_t)p * a.B + b) * W + c8 * 8);
+      }
+#pragma unroll
+      for (int k = 0; k < IOB; ++k)
+        if (bb[k] < 0) v[i0 + k] = make_uint4(0, 0, 0, 0);
+    }
   };
   // x rows -> LDS x_hat; for DENSE the RMS statistics reduce across the lanes
   // of a row before x_hat is written (RMSNorm in fp32, rho to bf16:
@@ -427,8 +431,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < NPRO; ++i) {
-        const int u = tix + i * NT;
-        const int c8 = u % U8;
+        int r, c8;
+        unit_rc(tix, i, r, c8);
         const float rinv = 1.0f / sqrtf(ss[i] / (float)W + a.eps);
         const uint16_t* h = reinterpret_cast<const uint16_t*>(&v[i]);
         float n[8];
@@ -442,8 +446,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < NPRO; ++i) {
-      const int u = tix + i * NT;
-      const int r = u / U8, c8 = u - r * U8;
+      int r, c8;
+      unit_rc(tix, i, r, c8);
       *reinterpret_cast<uint4*>(&xs[r * XS + c8 * 8]) = v[i];
     }
     __syncthreads();
@@ -480,28 +484,25 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
   };
   // residual rows of the tile, same unit order as load_x
   auto load_resid = [&](int tix, int buf, const Tile& T, uint4* rv) {
-    if constexpr (!FLAT_IO) {
 #pragma unroll
-      for (int i = 0; i < NPRO; ++i) {
-        const int u = tix + i * NT;
-        const int r = u / U8, c8 = u - r * U8;
-        const int b = rowb[buf][r];
-        rv[i] = b >= 0 ? ldg16(a.resid + uoff(b, rowpos(T, r), c8)) : make_uint4(0, 0, 0, 0);
+    for (int i0 = 0; i0 < NPRO; i0 += IOB) {
+      int bb[IOB];
+#pragma unroll
+      for (int k = 0; k < IOB; ++k) {
+        int r, c8;
+        unit_rc(tix, i0 + k, r, c8);
+        bb[k] = rowb[buf][r];
       }
-      return;
+#pragma unroll
+      for (int k = 0; k < IOB; ++k) {
+        int r, c8;
+        unit_rc(tix, i0 + k, r, c8);
+        rv[i0 + k] = ldg16(a.resid + uoff(bb[k] < 0 ? 0 : bb[k], rowpos(T, r), c8));
+      }
+#pragma unroll
+      for (int k = 0; k < IOB; ++k)
+        if (bb[k] < 0) rv[i0 + k] = make_uint4(0, 0, 0, 0);
     }
-    int bb[NPRO];
-#pragma unroll
-    for (int i = 0; i < NPRO; ++i) bb[i] = rowb[buf][(tix + i * NT) / U8];
-#pragma unroll
-    for (int i = 0; i < NPRO; ++i) {
-      const int u = tix + i * NT;
-      const int r = u / U8, c8 = u - r * U8;
-      rv[i] = ldg16(a.resid + uoff(bb[i] < 0 ? 0 : bb[i], rowpos(T, r), c8));
-    }
-#pragma unroll
-    for (int i = 0; i < NPRO; ++i)
-      if (bb[i] < 0) rv[i] = make_uint4(0, 0, 0, 0);
   };
 
   // ---- first tile ---------------------------------------------------------------
@@ -899,9 +900,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
         int bu[UB], pu[UB], c8u[UB], Ru[UB];
 #pragma unroll
         for (int k = 0; k < UB; ++k) {
-          const int u = etid + (i0 + k) * NT;
-          const int r = u / U8;
-          c8u[k] = u - r * U8;
+          int r;
+          unit_rc(etid, i0 + k, r, c8u[k]);
           Ru[k] = part * PR + r;
           bu[k] = rowb[buf][Ru[k]];
           pu[k] = rowpos(cur, Ru[k]);
