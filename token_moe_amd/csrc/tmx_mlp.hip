@@ -846,7 +846,12 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
     // tile loop, where it would stay live through the main loop
     int etid = tid;
     asm volatile("" : "+v"(etid));
-    constexpr bool PREF_R = (NPART == 1) && (MODE != MLP_ROUTED);
+    // EARLY: with at most 16 row units per lane the epilogue's row loads go
+    // out before the staging (their registers are free then); at W = 768
+    // (24 units, all accumulators in use until staged) they wait for the
+    // last part, and the residual is loaded beside each batch of units
+    constexpr bool EARLY = NPRO <= 16;
+    constexpr bool PREF_R = (MODE != MLP_ROUTED) && (EARLY || NPART == 1);
     constexpr int PR = BM / NPART;           // rows per staged part
     constexpr int NE = PR * U8 / NT;         // units per lane per part
     static_assert((PR * U8) % NT == 0, "part units must divide evenly");
@@ -862,6 +867,16 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
 #pragma unroll
     for (int part = 0; part < NPART; ++part) {
       __syncthreads();
+      if (part == (EARLY ? 0 : NPART - 1)) {
+        // the residual rows and the next tile's x rows do not depend on the
+        // staged accumulators: they go out first, after the barrier above
+        // (which also makes the next tile's row table visible)
+        if constexpr (PREF_R) load_resid(etid, buf, cur, pr);
+        if (has_next) {
+          load_gain(pg);
+          load_x(etid, buf ^ 1, nx, px);
+        }
+      }
       if (NPART == 1 || NW == 4 || wr == part) {
         // C layout of an O^T block (32 columns x 32 rows): lane holds row l32
         // and columns 8*(v/4) + 4*h32 + v%4 -> 4 consecutive columns per v-group
@@ -882,13 +897,6 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
         }
       }
       __syncthreads();
-      if (part == NPART - 1) {
-        if constexpr (PREF_R) load_resid(etid, buf, cur, pr);
-        if (has_next) {
-          load_gain(pg);
-          load_x(etid, buf ^ 1, nx, px);
-        }
-      }
       // O goes out of LDS in 16-byte units: residual / extra / output through
       // the row map, gated expert outputs as bf16 rows. Units go in batches
       // of UB whose global loads (partials, extra) are all issued before any
@@ -957,7 +965,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
           for (int k = 0; k < UB; ++k) {
             if (bu[k] < 0) continue;
             uint4 rvv;
-            if constexpr (PREF_R) rvv = pr[i0 + k];
+            if constexpr (PREF_R) rvv = pr[part * NE + i0 + k];
             else rvv = ldg16(a.resid + off[k]);
             const uint16_t* rh = reinterpret_cast<const uint16_t*>(&rvv);
             const uint16_t* eh = reinterpret_cast<const uint16_t*>(&ev[k]);
