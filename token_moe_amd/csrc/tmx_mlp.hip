@@ -528,19 +528,21 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
   set_rows(cur, 0);
   cw = bind(cur);
   nw = has_nx ? bind(nx) : cw;
-  if constexpr (NW == 4) {
-#pragma unroll
-    for (int f = 0; f < NFR; ++f) issue_frag(fslot(f), cw, 0, f);
-  } else {
-#pragma unroll
-    for (int s = 0; s < DEPTH; ++s) issue(ring[s], cw, 0, s);
-  }
-  __syncthreads();
+  __syncthreads();                         // row table visible
   {
+    // the first rows go out before the weight ring: a wave's loads retire
+    // in order, so the normalisation below waits for the rows only
     uint4 v[NPRO];
     float g[8];
     load_gain(g);
     load_x(tid, 0, cur, v);
+    if constexpr (NW == 4) {
+#pragma unroll
+      for (int f = 0; f < NFR; ++f) issue_frag(fslot(f), cw, 0, f);
+    } else {
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s) issue(ring[s], cw, 0, s);
+    }
     store_x(tid, v, g);
   }
 
