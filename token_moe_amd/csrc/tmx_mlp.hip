@@ -177,12 +177,18 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
   };
   auto decode = [&](int j, Tile& T) -> bool {
     int pu;
+    // SHARED walks each XCD's positions from the last: the routed launch
+    // before it wrote its expert outputs in ascending position order, so
+    // the most recently written -- the ones most likely still in the
+    // last-level cache -- are combined first
     if ((NPU & 7) == 0) {
       const int xcd = j & 7, q = j >> 3;
-      pu = xcd * (NPU >> 3) + q / per_pos;
+      const int k = q / per_pos;
+      pu = xcd * (NPU >> 3) + (MODE == MLP_SHARED ? (NPU >> 3) - 1 - k : k);
       T.t = q % per_pos;
     } else {
-      pu = j / per_pos;
+      const int k = j / per_pos;
+      pu = MODE == MLP_SHARED ? NPU - 1 - k : k;
       T.t = j % per_pos;
     }
     T.p = pair ? 2 * pu : pu;
