@@ -288,8 +288,17 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_SH_GATE).ptr);
   a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_SH_DOWN).ptr);
   set_row_tiles(a, sub, W, P, B, bm);
-  return check_launch(c, launch_mlp(MLP_SHARED, W, a, (a.pair ? P / 2 : P) * a.rtiles, c->workers, st),
-                      "shared MLP launch");
+  // The shared-expert tiles are all alike, so a persistent launch keeps its
+  // workgroups in step: every combine epilogue (k expert rows + residual per
+  // row, HBM-bound) would run at once while no MFMA runs. With 4 or more
+  // tiles per workgroup, every other workgroup of an XCD starts about one
+  // main loop (1.6 x the tile's MFMA clocks) late, so half of them combine
+  // while the other half compute.
+  const int sh_tiles = (a.pair ? P / 2 : P) * a.rtiles;
+  const int sh_grid = std::max(1, std::min(sh_tiles, c->workers & ~7));
+  const double mfma_clk = (double)bm * W * 3.0 * cfg.shared_hidden / (16384.0 * 4.0) * 32.0;
+  a.stagger = sh_tiles >= 4 * sh_grid ? (int)(1.6 * mfma_clk) : 0;
+  return check_launch(c, launch_mlp(MLP_SHARED, W, a, sh_tiles, c->workers, st), "shared MLP launch");
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -46,6 +46,8 @@ struct MlpArgs {
   int rtiles;              // DENSE / SHARED: row tiles per position unit
   int pair;                // DENSE / SHARED: 1 = a tile holds BM/2 rows of each of two
                            // adjacent positions (2q in rows [0, BM/2), 2q+1 above)
+  int stagger;             // clocks that every other workgroup of an XCD waits before
+                           // its first tile (0 = none)
 };
 
 struct RouteArgs {

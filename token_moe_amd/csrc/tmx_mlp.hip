@@ -511,6 +511,14 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
     }
   };
 
+  // ---- phase shift ----------------------------------------------------------------
+  // (set for the shared-expert launch: its alike tiles would otherwise keep
+  // every workgroup's HBM-bound epilogue in step; see the host launch)
+  if (a.stagger > 0 && ((blockIdx.x >> 3) & 1)) {
+    const long long t0 = clock64();
+    while (clock64() - t0 < a.stagger) __builtin_amdgcn_s_sleep(16);
+  }
+
   // ---- first tile ---------------------------------------------------------------
   Tile cur, nx;
   int ci = 0, ni = 0;
