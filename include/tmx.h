@@ -99,9 +99,11 @@ typedef struct tmx_ctx tmx_ctx;
 
 /* Validate `cfg`, select `device` (hipSetDevice) and allocate the context:
  * weight storage for all L blocks and a workspace sized for B_max.
- * bf16 contexts additionally need D/H % 8 == 0, every sub-layer width W a
- * multiple of 64 and every hidden size a multiple of 64; MoE contexts in
- * bf16 need E % 16 == 0 and top_k <= 8 (TMX_ERR_UNSUPPORTED otherwise).
+ * bf16 contexts additionally need D/H % 8 == 0, every sub-layer width W
+ * (T*D/H for MIX, D for REVERT) one of 128, 256, 512, 768 and every hidden
+ * size a multiple of 128; MoE contexts in bf16 need E % 16 == 0, E <= 64,
+ * top_k <= 8 and B_max*T*D < 2^31 (the normalised-row workspace is
+ * addressed with 32-bit byte offsets); TMX_ERR_UNSUPPORTED otherwise.
  * On error *out is set to NULL and nothing stays allocated. */
 tmx_status tmx_create(const tmx_config* cfg, int device, tmx_ctx** out);
 

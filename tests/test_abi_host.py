@@ -114,6 +114,9 @@ def _create(tmx, **kw):
     (dict(dtype=1, D=96, H=4, T=4, hidden_mix=64, hidden_rev=64), "UNSUPPORTED"),      # W = 96
     (dict(dtype=1, D=128, H=4, T=4, hidden_mix=100, hidden_rev=64), "UNSUPPORTED"),    # hidden % 64
     (dict(dtype=1, D=128, H=4, T=4, E=8, top_k=2, expert_hidden=64, shared_hidden=64), "UNSUPPORTED"),
+    # x_hat workspace (B_max*T*D bf16) must stay under 4 GiB
+    (dict(dtype=1, B_max=1 << 21, D=512, H=16, T=16, E=16, top_k=4, expert_hidden=256, shared_hidden=512),
+     "UNSUPPORTED"),
 ])
 def test_create_validation(tmx, kw, status):
     st, h, msg = _create(tmx, **kw)

@@ -180,6 +180,9 @@ tmx_status validate_config(const tmx_config* cfg) {
     if (c.E > 0 && (c.E % 16 != 0 || c.E > 64))
       return fail(nullptr, TMX_ERR_UNSUPPORTED, "bf16 MoE needs E %% 16 == 0 and E <= 64, got %d", c.E);
     if (c.E > 0 && c.top_k > 8) return fail(nullptr, TMX_ERR_UNSUPPORTED, "bf16 MoE needs top_k <= 8");
+    if (c.E > 0 && act >= (int64_t)1 << 31)
+      return fail(nullptr, TMX_ERR_UNSUPPORTED,
+                  "bf16 MoE needs B_max*T*D < 2^31 (the x_hat workspace is addressed with 32-bit byte offsets)");
   } else {
     if (c.E > 256 || c.top_k > 64) return fail(nullptr, TMX_ERR_UNSUPPORTED, "fp32 MoE needs E <= 256, top_k <= 64");
     const int hmax = std::max({c.hidden_mix, c.hidden_rev, c.expert_hidden, c.shared_hidden});

@@ -365,10 +365,14 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
     }
   };
   // Row loads are issued without branches, IOB units at a time: the lane
-  // reads the batch's row indices first, rows past the tile end load row 0
-  // and are cleared afterwards, so the batch's loads go out back to back.
-  // (Batches of 8 at W = 768, 24 units per lane: all index copies at once
-  // would spill in the main loop.)
+  // reads the batch's row indices first and rows past the tile end load row
+  // 0, so the batch's loads go out back to back. With one batch (up to 16
+  // units per lane) the padding rows are cleared after it. With several
+  // (W = 768: 24 units, batches of 8 -- all index copies at once would spill
+  // in the main loop) they are not: clearing a load's destination makes the
+  // wave wait for that load, which would serialise the batches, and an
+  // output row depends only on its own input row while no epilogue stores
+  // or reads a padding row.
   constexpr int IOB = NPRO <= 16 ? NPRO : 8;
   static_assert(NPRO % IOB == 0, "row-load batches must divide the units per lane");
   auto load_x = [&](int tix, int buf, const Tile& T, uint4* v) {
@@ -387,14 +391,21 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
         unit_rc(tix, i0 + k, r, c8);
         const int b = bb[k] < 0 ? 0 : bb[k];
         const int p = rowpos(T, r);
-        if (MODE == MLP_DENSE)
+        if (MODE == MLP_DENSE) {
           v[i0 + k] = ldg16(a.x + uoff(b, p, c8));
-        else
-          v[i0 + k] = ldg16(a.xhat + ((size_t)p * a.B + b) * W + c8 * 8);
+        } else {
+          // 32-bit byte offset from the x_hat base (the host keeps that
+          // buffer under 4 GiB): one address register per load, which keeps
+          // the W = 768 epilogue free of spills
+          const uint32_t off = (((uint32_t)p * (uint32_t)a.B + (uint32_t)b) * (uint32_t)W + (uint32_t)c8 * 8u) * 2u;
+          v[i0 + k] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.xhat) + off);
+        }
       }
+      if constexpr (IOB == NPRO) {
 #pragma unroll
-      for (int k = 0; k < IOB; ++k)
-        if (bb[k] < 0) v[i0 + k] = make_uint4(0, 0, 0, 0);
+        for (int k = 0; k < IOB; ++k)
+          if (bb[k] < 0) v[i0 + k] = make_uint4(0, 0, 0, 0);
+      }
     }
   };
   // x rows -> LDS x_hat; for DENSE the RMS statistics reduce across the lanes
@@ -505,9 +516,11 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
         unit_rc(tix, i0 + k, r, c8);
         rv[i0 + k] = ldg16(a.resid + uoff(bb[k] < 0 ? 0 : bb[k], rowpos(T, r), c8));
       }
+      if constexpr (IOB == NPRO) {
 #pragma unroll
-      for (int k = 0; k < IOB; ++k)
-        if (bb[k] < 0) rv[i0 + k] = make_uint4(0, 0, 0, 0);
+        for (int k = 0; k < IOB; ++k)
+          if (bb[k] < 0) rv[i0 + k] = make_uint4(0, 0, 0, 0);
+      }
     }
   };
 
