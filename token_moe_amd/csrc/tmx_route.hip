@@ -263,6 +263,8 @@ __global__ __launch_bounds__(BK_NT) void bucket_kernel(const BucketArgs a) {
     int tot = 0, pre = 0;
     if (g < G) {
       const int* h = a.hist + (size_t)p * C * E + e;
+      // unrolled so that the loads of one thread are in flight together
+#pragma unroll 8
       for (int cc = g; cc < C; cc += G) {
         const int n = h[(size_t)cc * E];
         tot += n;
@@ -293,17 +295,27 @@ __global__ __launch_bounds__(BK_NT) void bucket_kernel(const BucketArgs a) {
   }
   __syncthreads();
 
-  // tiles and counts of the position
-  if (c == 0 && t == 0) {
-    int nt = 0, off = 0;
-    int4* tl = a.tiles + (size_t)p * a.max_tiles;
-    for (int e = 0; e < E; ++e) {
-      const int n = tot_s[e];
-      a.counts[(size_t)p * E + e] = n;
-      for (int s0 = 0; s0 < n; s0 += a.bm) tl[nt++] = make_int4(e, off + s0, min(a.bm, n - s0), 0);
-      off += n;
+  // tiles and counts of the position: thread e writes expert e's tiles,
+  // which start after the tiles of experts 0 .. e-1
+  if (c == 0) {
+    __shared__ int tstart[BK_EMAX + 1];
+    if (t == 0) {
+      int nt = 0;
+      for (int e = 0; e < E; ++e) {
+        tstart[e] = nt;
+        nt += (tot_s[e] + a.bm - 1) / a.bm;
+      }
+      tstart[E] = nt;
+      a.ntiles[p] = nt;
     }
-    a.ntiles[p] = nt;
+    __syncthreads();
+    if (t < E) {
+      const int n = tot_s[t];
+      a.counts[(size_t)p * E + t] = n;
+      int4* tl = a.tiles + (size_t)p * a.max_tiles + tstart[t];
+      const int off = base_s[t];               // entries of experts before t (chunk 0: no prefix)
+      for (int s0 = 0, j = 0; s0 < n; s0 += a.bm, ++j) tl[j] = make_int4(t, off + s0, min(a.bm, n - s0), 0);
+    }
   }
 
   const int r0 = c * BK_ROWS;
