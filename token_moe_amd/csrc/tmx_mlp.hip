@@ -579,6 +579,30 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
     int nent = 0;
     if constexpr (MODE == MLP_ROUTED)
       if (has_nx && tid < nx.nrows) nent = a.rows[(size_t)nx.p * a.B * a.top_k + nx.start + tid];
+    // ROUTED: the next tile's row table from that entry, its gates, and the
+    // claim of the tile after next. The compiler cannot follow the entry's
+    // load across the main loop and waits for every load in flight at its
+    // first use, so 4-wave tiles run this before the postamble, while only
+    // the tile's own (warm) fragments are in flight -- not after it, when
+    // the next tile's first fragments (often a cold expert) are. Every
+    // thread issues the gate load (padding rows and threads past BM read
+    // entry 0 and never use it): a load on one path only makes the compiler
+    // drain every load in flight where the paths join. The gate and the
+    // claimed slot go to LDS after the epilogue (only the next epilogue
+    // reads them).
+    float ngate = 0.f;
+    int qs = 0;
+    auto routed_setup = [&]() __attribute__((always_inline)) {
+      const bool ok = has_nx && tid < BM && tid < nx.nrows;
+      const int b = ok ? nent / a.top_k : -1;
+      const int gi = ok ? (b * a.P + nx.p) * a.top_k + (nent - b * a.top_k) : 0;
+      ngate = a.gate[gi];
+      if (has_nx && tid < BM) {
+        rowb[buf ^ 1][tid] = b;
+        rowgi[buf ^ 1][tid] = gi;
+      }
+      if (has_nx && tid == 0) qs = atomicAdd(&a.qhead[qx], 1);
+    };
 
     // ---- main loop ---------------------------------------------------------------
     f32x16 oacc[RBW][NBO];
@@ -826,6 +850,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
           iteration(NC - 1, std::integral_constant<bool, true>{});
         }
 
+        if constexpr (MODE == MLP_ROUTED) routed_setup();
         // postamble: GEMM2(NC-1); past its end the stream enters the next
         // tile's preamble
         {
@@ -848,28 +873,11 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
     // ---- between tiles: stage O, start the next tile's loads, epilogue --------
     // The ring already holds the next tile's first fragments (see refill).
     const bool has_next = has_nx;
-    float ngate = 0.f;                     // ROUTED: gate of the next tile's row tid
-    if (has_next) {
-      if constexpr (MODE == MLP_ROUTED) {
-        // row table of the next tile from the entry loaded before the main
-        // loop; its gate is stored after this epilogue (only the next
-        // epilogue reads it), so that load is not waited for here
-        if (tid < BM) {
-          int b = -1, gi = 0;
-          if (tid < nx.nrows) {
-            b = nent / a.top_k;
-            gi = (b * a.P + nx.p) * a.top_k + (nent - b * a.top_k);
-            ngate = a.gate[gi];
-          }
-          rowb[buf ^ 1][tid] = b;
-          rowgi[buf ^ 1][tid] = gi;
-        }
-      } else {
-        set_rows(nx, buf ^ 1);
-      }
+    if constexpr (MODE == MLP_ROUTED) {
+      if constexpr (NW == 8) routed_setup();
+    } else if (has_next) {
+      set_rows(nx, buf ^ 1);
     }
-    // the tile after next (read back after the staging barriers below)
-    if (MODE == MLP_ROUTED && has_next && tid == 0) qslot = atomicAdd(&a.qhead[qx], 1);
     // an opaque copy of the thread index: keeps the compiler from hoisting
     // the epilogue's and the next prologue's address arithmetic out of the
     // tile loop, where it would stay live through the main loop
@@ -885,14 +893,21 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
     constexpr int NE = PR * U8 / NT;         // units per lane per part
     static_assert((PR * U8) % NT == 0, "part units must divide evenly");
     uint4 pr[PREF_R ? NPRO : 1];
-    // defined on every path: a conditionally written px becomes a value
-    // carried around the tile loop and stays live through the main loop
+    // Defined on every path: a conditionally written px becomes a value
+    // carried around the tile loop and stays live through the main loop.
+    // 4-wave ROUTED tiles with up to 16 units per lane leave it undefined
+    // off the has_next path (it is read only on that path): there the
+    // clearing writes made the compiler wait for every load in flight, the
+    // next tile's first weight fragments included, before the epilogue.
+    // (At W = 768 an undefined px is kept in scratch memory instead.)
     uint4 px[NPRO];
     float pg[8];
+    if constexpr (MODE != MLP_ROUTED || NW == 8 || !EARLY) {
 #pragma unroll
-    for (int i = 0; i < NPRO; ++i) px[i] = make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < NPRO; ++i) px[i] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pg[e] = 0.f;
+      for (int e = 0; e < 8; ++e) pg[e] = 0.f;
+    }
 #pragma unroll
     for (int part = 0; part < NPART; ++part) {
       __syncthreads();
@@ -1012,8 +1027,9 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
     }
     if (!has_next) break;
     if (MODE == MLP_ROUTED && tid < BM) rowg[buf ^ 1][tid] = ngate;
-    const int knext = qslot;
+    if (MODE == MLP_ROUTED && tid == 0) qslot = qs;
     __syncthreads();                       // staging reads done before x_hat is rewritten
+    const int knext = qslot;
     store_x(etid, px, pg);
     cur = nx;
     buf ^= 1;
