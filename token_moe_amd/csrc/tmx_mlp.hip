@@ -975,6 +975,14 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
             *reinterpret_cast<uint4*>(a.part + (size_t)rowgi[buf][Ru[k]] * W + c8u[k] * 8) = w;
           }
         } else {
+          // At W = 768 the expert-output and residual loads are
+          // unconditional (rows past the tile end read row 0, slots past
+          // top_k read slot 0; those values are not used): a load on one
+          // path only makes the compiler wait for every load in flight where
+          // the paths join -- the next tile's weight fragments included. (At
+          // W <= 512 that measured slower.) The inter-residual stays
+          // conditional: most launches have none, and reading a stand-in
+          // would add a whole operand's traffic.
           if constexpr (MODE == MLP_SHARED) {
             // the routed experts' gated outputs, four slots at a time
             for (int s0 = 0; s0 < a.top_k; s0 += 4) {
@@ -983,14 +991,21 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
               for (int k = 0; k < UB; ++k)
 #pragma unroll
                 for (int sl = 0; sl < 4; ++sl) {
-                  q[k][sl] = make_uint4(0, 0, 0, 0);
-                  if (bu[k] >= 0 && s0 + sl < a.top_k)
-                    q[k][sl] = ldg16(a.part + (((size_t)bu[k] * a.P + pu[k]) * a.top_k + s0 + sl) * W + c8u[k] * 8);
+                  if constexpr (EARLY) {
+                    q[k][sl] = make_uint4(0, 0, 0, 0);
+                    if (bu[k] >= 0 && s0 + sl < a.top_k)
+                      q[k][sl] = ldg16(a.part + (((size_t)bu[k] * a.P + pu[k]) * a.top_k + s0 + sl) * W + c8u[k] * 8);
+                  } else {
+                    const int bq = bu[k] < 0 ? 0 : bu[k];
+                    const int sq = s0 + sl < a.top_k ? s0 + sl : 0;
+                    q[k][sl] = ldg16(a.part + (((size_t)bq * a.P + pu[k]) * a.top_k + sq) * W + c8u[k] * 8);
+                  }
                 }
 #pragma unroll
               for (int k = 0; k < UB; ++k)
 #pragma unroll
                 for (int sl = 0; sl < 4; ++sl) {
+                  if (s0 + sl >= a.top_k) continue;
                   const uint16_t* qh = reinterpret_cast<const uint16_t*>(&q[k][sl]);
 #pragma unroll
                   for (int e = 0; e < 8; ++e) o[k][e] += bf2f(qh[e]);
@@ -998,19 +1013,20 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
             }
           }
           int64_t off[UB];
-          uint4 ev[UB];
+          uint4 ev[UB], rv[UB];
 #pragma unroll
           for (int k = 0; k < UB; ++k) {
             off[k] = uoff(bu[k] < 0 ? 0 : bu[k], pu[k], c8u[k]);
             ev[k] = make_uint4(0, 0, 0, 0);
             if (a.extra && bu[k] >= 0) ev[k] = ldg16(a.extra + off[k]);
+            if constexpr (!PREF_R) rv[k] = ldg16(a.resid + off[k]);
           }
 #pragma unroll
           for (int k = 0; k < UB; ++k) {
             if (bu[k] < 0) continue;
             uint4 rvv;
             if constexpr (PREF_R) rvv = pr[part * NE + i0 + k];
-            else rvv = ldg16(a.resid + off[k]);
+            else rvv = rv[k];
             const uint16_t* rh = reinterpret_cast<const uint16_t*>(&rvv);
             const uint16_t* eh = reinterpret_cast<const uint16_t*>(&ev[k]);
 #pragma unroll
