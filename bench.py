@@ -28,7 +28,7 @@ HBM_PEAK_GBS = 8000.0
 # rocprofv3 counter summary of the dominant kernel; its traffic figure is used
 # only while the kernel sources still hash to the value recorded there
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "mlp_dense_workload2_counters.md")
-KERNEL_SOURCES = ("token_moe_amd/csrc/tmx_mlp.hip", "token_moe_amd/csrc/tmx_device.h",
+KERNEL_SOURCES = ("token_moe_amd/csrc/tmx_mlp.hip", "token_moe_amd/csrc/tmx_device.h", "token_moe_amd/build.py",
                   "token_moe_amd/csrc/tmx_internal.h")
 
 

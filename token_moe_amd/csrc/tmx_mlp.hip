@@ -539,7 +539,13 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
   if constexpr (MODE == MLP_ROUTED) {
     __shared__ int qfirst[2];
     if (tid == 0) {
-      qfirst[0] = atomicAdd(&a.qhead[qx], 1);
+      // the second claim goes out only once the first has returned: the
+      // workgroups starting together then take queue entries w and about
+      // w + grid, not w and w + 1, so the tiles in flight at any time are
+      // consecutive entries (few experts' weights live at once)
+      const int q0 = atomicAdd(&a.qhead[qx], 1);
+      asm volatile("" ::"v"(q0));
+      qfirst[0] = q0;
       qfirst[1] = atomicAdd(&a.qhead[qx], 1);
     }
     __syncthreads();
