@@ -193,7 +193,7 @@ tmx_status validate_config(const tmx_config* cfg) {
   return TMX_OK;
 }
 
-int moe_bm(const tmx_config& c, int sub) { return mlp_bm_for_width(width(c, sub)); }
+int moe_bm(const tmx_config& c, int sub) { return mlp_bm(MLP_ROUTED, width(c, sub)); }
 int moe_max_tiles(const tmx_config& c, int sub, int B) {
   const int bm = moe_bm(c, sub);
   return (int)(((int64_t)B * c.top_k + bm - 1) / bm) + c.E;
@@ -219,10 +219,16 @@ tmx_status check_ready(tmx_ctx* c) {
 // Row tiling of the per-position MLP. On the Mix map two adjacent positions
 // share a tile (BM/2 rows each): their segments of a token are adjacent in
 // the block layout, so the tile reads and writes whole 2*D/H-element runs.
-void set_row_tiles(MlpArgs& a, int sub, int W, int P, int B, int bm) {
-  a.pair = (sub == TMX_MIX && P % 2 == 0 && mlp_pairs_positions(W)) ? 1 : 0;
+void set_row_tiles(MlpArgs& a, int mode, int sub, int W, int P, int B, int dh_bytes) {
+  const int bm = mlp_bm(mode, W);
+  a.pair = (sub == TMX_MIX && P % 2 == 0 && mlp_pairs_positions(mode, W)) ? 1 : 0;
   const int rows = a.pair ? bm / 2 : bm;
   a.rtiles = (B + rows - 1) / rows;
+  // Unpaired Mix tiles: positions 2q and 2q+1 alternate in the tile order,
+  // so the workgroups that read the two halves of a run start side by side
+  // (runs shorter than a 128-byte line only)
+  const int ppx = (P % 8 == 0) ? P / 8 : P;   // positions per tile range of an XCD
+  a.ileave = (sub == TMX_MIX && !a.pair && ppx % 2 == 0 && dh_bytes < 128) ? 1 : 0;
 }
 
 tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const void* resid, const void* extra,
@@ -253,17 +259,17 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   a.x = static_cast<const uint16_t*>(x_in); a.gain = gain;
   a.resid = static_cast<const uint16_t*>(resid); a.extra = static_cast<const uint16_t*>(extra);
   a.out = static_cast<uint16_t*>(x_out);
-  const int bm = mlp_bm_for_width(W);
   if (!is_moe(cfg)) {
     a.hidden = dense_hidden(cfg, sub);
     a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_GATE).ptr);
     a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_DOWN).ptr);
-    set_row_tiles(a, sub, W, P, B, bm);
+    set_row_tiles(a, MLP_DENSE, sub, W, P, B, map.dh * 2);
     return check_launch(c, launch_mlp(MLP_DENSE, W, a, (a.pair ? P / 2 : P) * a.rtiles, c->workers, st),
                         "dense MLP launch");
   }
 
   // MoE: norm + route -> bucket -> routed experts -> shared expert + combine
+  const int bm = mlp_bm(MLP_ROUTED, W);
   RouteArgs r{};
   r.B = B; r.P = P; r.E = cfg.E; r.top_k = cfg.top_k; r.alpha = c->alpha; r.eps = cfg.eps; r.map = map;
   r.x = static_cast<const uint16_t*>(x_in); r.gain = gain;
@@ -290,7 +296,7 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   a.hidden = cfg.shared_hidden;
   a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_SH_GATE).ptr);
   a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_SH_DOWN).ptr);
-  set_row_tiles(a, sub, W, P, B, bm);
+  set_row_tiles(a, MLP_SHARED, sub, W, P, B, map.dh * 2);
   // The shared-expert tiles are all alike, so a persistent launch keeps its
   // workgroups in step: every combine epilogue (k expert rows + residual per
   // row, HBM-bound) would run at once while no MFMA runs. With 4 or more

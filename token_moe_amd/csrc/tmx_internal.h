@@ -46,8 +46,11 @@ struct MlpArgs {
   int rtiles;              // DENSE / SHARED: row tiles per position unit
   int pair;                // DENSE / SHARED: 1 = a tile holds BM/2 rows of each of two
                            // adjacent positions (2q in rows [0, BM/2), 2q+1 above)
-  int stagger;             // clocks that every other workgroup of an XCD waits before
-                           // its first tile (0 = none)
+  int ileave;              // DENSE / SHARED, unpaired: positions 2q and 2q+1 alternate
+                           // in the tile order (row tile t of 2q, of 2q+1, t+1 of 2q, ...)
+  int stagger;             // clocks that the late half of the workgroups waits before
+                           // its first tile (0 = none): every other workgroup of an
+                           // XCD, or with two workgroups per CU the second of each CU
 };
 
 struct RouteArgs {
@@ -75,13 +78,17 @@ struct BucketArgs {
 };
 
 // bf16 launchers (return hipError_t of the launch)
-int mlp_bm_for_width(int W);
+// rows per tile of the MLP kernel for a mode (MlpMode) and width
+int mlp_bm(int mode, int W);
 bool mlp_width_supported(int W);
-// tiles = P * (rtiles or max_tiles); the grid is min(tiles, workers & ~7):
-// each workgroup walks tiles blockIdx.x, blockIdx.x + grid, ...
+// tiles = P * (rtiles or max_tiles); the grid is min(tiles, (workers & ~7) *
+// workgroups per CU): each workgroup walks tiles blockIdx.x, blockIdx.x +
+// grid, ...
 hipError_t launch_mlp(int mode, int W, const MlpArgs& a, int tiles, int workers, hipStream_t s);
-// whether DENSE / SHARED tiles of this width may hold two adjacent positions
-bool mlp_pairs_positions(int W);
+// whether DENSE / SHARED tiles of this mode and width may hold two adjacent positions
+bool mlp_pairs_positions(int mode, int W);
+// workgroups of the MLP kernel resident per CU for a mode and width
+int mlp_workgroups_per_cu(int mode, int W);
 hipError_t launch_norm_route(int W, const RouteArgs& a, hipStream_t s);
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
 // Repack G row-major [K, N] bf16 matrices into MFMA B-operand fragments of

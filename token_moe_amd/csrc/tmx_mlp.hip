@@ -46,10 +46,19 @@ namespace {
 // (W = 512) and serve W = 128.
 constexpr int mlp_waves(int W) { return W == 256 ? 8 : 4; }
 
-template <int W, int NW>
+// Workgroups per CU. The dense W = 256 sub-layer runs as two 4-wave
+// workgroups of 64 rows per CU (256 registers per wave, as in the 8-wave
+// tile) that start half a tile apart: while one streams its rows in and
+// out, the other's MFMAs keep the SIMDs busy. In a single 8-wave workgroup
+// both row groups cross every tile boundary together, so every CU moved its
+// rows at the same moment while no MFMA ran.
+constexpr int mlp_occupancy(int mode, int W) { return (mode == MLP_DENSE && W == 256) ? 2 : 1; }
+constexpr int mlp_waves(int mode, int W) { return mlp_occupancy(mode, W) == 2 ? 4 : mlp_waves(W); }
+
+template <int W, int NW, int OCC>
 struct MlpShape {
   static constexpr int NT = 64 * NW;
-  static constexpr int BM = (W <= 256) ? 128 : 64;  // rows per workgroup
+  static constexpr int BM = (W <= 256 && OCC == 1) ? 128 : 64;  // rows per workgroup
   static constexpr int HC = MLP_HC;                 // hidden chunk
   static constexpr int XS = W + 8;                  // x_hat row stride (+16 B: rows on distinct banks)
   static constexpr int US = HC + 8;                 // U row stride
@@ -88,9 +97,9 @@ __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
-template <int W, int MODE, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
-  using S = MlpShape<W, NW>;
+template <int W, int MODE, int NW, int OCC>
+__global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
+  using S = MlpShape<W, NW, OCC>;
   constexpr int NT = S::NT;
   constexpr int BM = S::BM, XS = S::XS, US = S::US, RBW = S::RBW, NBO = S::NBO;
   constexpr int S1 = S::S1, S2 = S::S2, NS = S::S, DEPTH = S::DEPTH, NBR = S::NBR, HC = S::HC, YS = S::YS;
@@ -181,16 +190,20 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
     // before it wrote its expert outputs in ascending position order, so
     // the most recently written -- the ones most likely still in the
     // last-level cache -- are combined first
-    if ((NPU & 7) == 0) {
-      const int xcd = j & 7, q = j >> 3;
-      const int k = q / per_pos;
-      pu = xcd * (NPU >> 3) + (MODE == MLP_SHARED ? (NPU >> 3) - 1 - k : k);
-      T.t = q % per_pos;
+    const bool split = (NPU & 7) == 0;
+    const int q = split ? j >> 3 : j;          // tile index within the XCD's range
+    const int npx = split ? NPU >> 3 : NPU;    // positions in that range
+    int k;
+    if (MODE != MLP_ROUTED && a.ileave) {
+      // positions 2m and 2m+1 alternate: row tile t of 2m, of 2m+1, t+1 of 2m, ...
+      const int m = q / (2 * per_pos), r = q - m * 2 * per_pos;
+      k = 2 * m + (r & 1);
+      T.t = r >> 1;
     } else {
-      const int k = j / per_pos;
-      pu = MODE == MLP_SHARED ? NPU - 1 - k : k;
-      T.t = j % per_pos;
+      k = q / per_pos;
+      T.t = q % per_pos;
     }
+    pu = (split ? (j & 7) * npx : 0) + (MODE == MLP_SHARED ? npx - 1 - k : k);
     T.p = pair ? 2 * pu : pu;
     if (MODE == MLP_ROUTED) {
       if (T.t >= a.ntiles[T.p]) return false;
@@ -527,7 +540,10 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
   // ---- phase shift ----------------------------------------------------------------
   // (set for the shared-expert launch: its alike tiles would otherwise keep
   // every workgroup's HBM-bound epilogue in step; see the host launch)
-  if (a.stagger > 0 && ((blockIdx.x >> 3) & 1)) {
+  // (with two workgroups per CU: the second dispatch round, which the
+  // dispatcher places beside the first round's workgroups)
+  const bool late = OCC == 2 ? blockIdx.x >= gridDim.x / 2 : ((blockIdx.x >> 3) & 1);
+  if (a.stagger > 0 && late) {
     const long long t0 = clock64();
     while (clock64() - t0 < a.stagger) __builtin_amdgcn_s_sleep(16);
   }
@@ -1067,13 +1083,18 @@ __global__ __launch_bounds__(64 * NW, 1) void mlp_kernel(const MlpArgs a) {
   }
 }
 
+template <int W, int MODE>
+void launch_wm(const MlpArgs& a, int grid, hipStream_t s) {
+  constexpr int NW = mlp_waves(MODE, W), OCC = mlp_occupancy(MODE, W);
+  hipLaunchKernelGGL((mlp_kernel<W, MODE, NW, OCC>), dim3(grid), dim3(64 * NW), 0, s, a);
+}
+
 template <int W>
 hipError_t launch_w(int mode, const MlpArgs& a, int grid, hipStream_t s) {
-  constexpr int NW = mlp_waves(W);
   switch (mode) {
-    case MLP_DENSE: hipLaunchKernelGGL((mlp_kernel<W, MLP_DENSE, NW>), dim3(grid), dim3(64 * NW), 0, s, a); break;
-    case MLP_ROUTED: hipLaunchKernelGGL((mlp_kernel<W, MLP_ROUTED, NW>), dim3(grid), dim3(64 * NW), 0, s, a); break;
-    default: hipLaunchKernelGGL((mlp_kernel<W, MLP_SHARED, NW>), dim3(grid), dim3(64 * NW), 0, s, a); break;
+    case MLP_DENSE: launch_wm<W, MLP_DENSE>(a, grid, s); break;
+    case MLP_ROUTED: launch_wm<W, MLP_ROUTED>(a, grid, s); break;
+    default: launch_wm<W, MLP_SHARED>(a, grid, s); break;
   }
   return hipGetLastError();
 }
@@ -1082,15 +1103,17 @@ hipError_t launch_w(int mode, const MlpArgs& a, int grid, hipStream_t s) {
 
 bool mlp_width_supported(int W) { return W == 128 || W == 256 || W == 512 || W == 768; }
 
-int mlp_bm_for_width(int W) { return W <= 256 ? 128 : 64; }
+int mlp_bm(int mode, int W) { return (W <= 256 && mlp_occupancy(mode, W) == 1) ? 128 : 64; }
 
-bool mlp_pairs_positions(int W) { return mlp_waves(W) == 8; }
+bool mlp_pairs_positions(int mode, int W) { return mode != MLP_ROUTED && mlp_waves(mode, W) == 8; }
+
+int mlp_workgroups_per_cu(int mode, int W) { return mlp_occupancy(mode, W); }
 
 hipError_t launch_mlp(int mode, int W, const MlpArgs& a, int tiles, int workers, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
-  // persistent grid: at most `workers` workgroups, a multiple of 8 so that a
-  // workgroup's tiles all sit on its own XCD
-  workers &= ~7;
+  // persistent grid: at most `workers` workgroups per CU round, a multiple
+  // of 8 so that a workgroup's tiles all sit on its own XCD
+  workers = (workers & ~7) * mlp_workgroups_per_cu(mode, W);
   const int grid = (workers <= 0 || tiles <= workers) ? tiles : workers;
   switch (W) {
     case 128: return launch_w<128>(mode, a, grid, s);
