@@ -74,6 +74,27 @@ def test_odd_positions_stack_all_rows():
     assert err <= TOL["bf16"]
 
 
+# W = 256 in both sub-layers with P = 16: two 64-row workgroups per CU, tile
+# ranges split per XCD, Mix positions 2m / 2m+1 alternating in the tile order;
+# ragged batch (1000 = 15 * 64 + 40), 3 hidden chunks in the Revert sub-layer,
+# inter-residual at block 2
+W256_RAGGED = dg.Workload("w256_ragged_dense_bf16", B=1000, T=16, H=16, D=256, L=3, hidden_mix=256,
+                          hidden_rev=384, gap=2, seed=33)
+
+
+def test_w256_interleaved_ragged_all_rows():
+    require_gpu()
+    wl = W256_RAGGED
+    say("W=256 ragged dense stack", wl)
+    ctx, banks, ws = context("w256_ragged", wl)
+    x = dg.make_x(wl)
+    y = to_np(_stack(wl, ctx, to_dev(wl, x), wl.B))
+    ref = orc.stack_forward(x.astype(np.float64), wl, ws)
+    err = row_err(y, ref)
+    say("W=256 ragged err", err)
+    assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("wid", [2, 3])
 @pytest.mark.parametrize("sub", [0, 1])
 def test_dense_sublayer_teacher_forced_full_batch(wid, sub):

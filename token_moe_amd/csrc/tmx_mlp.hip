@@ -97,8 +97,14 @@ __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
-template <int W, int MODE, int NW, int OCC>
+// RESX (dense Mix sub-layer): the residual is the tile's own input rows,
+// read through the same map, so the raw rows stay in registers from their
+// load to the epilogue instead of being read again (each Mix unit is a
+// separate 2*D/H-byte run of a token, so those reads touch a cache line per
+// run).
+template <int W, int MODE, int NW, int OCC, bool RESX>
 __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
+  static_assert(!RESX || MODE == MLP_DENSE, "input rows double as the residual only in dense sub-layers");
   using S = MlpShape<W, NW, OCC>;
   constexpr int NT = S::NT;
   constexpr int BM = S::BM, XS = S::XS, US = S::US, RBW = S::RBW, NBO = S::NBO;
@@ -550,6 +556,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
 
   // ---- first tile ---------------------------------------------------------------
   Tile cur, nx;
+  uint4 kx[RESX ? NPRO : 1];   // RESX: raw input rows of the current tile
   int ci = 0, ni = 0;
   bool has_nx;
   if constexpr (MODE == MLP_ROUTED) {
@@ -591,6 +598,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
     } else {
 #pragma unroll
       for (int s = 0; s < DEPTH; ++s) issue(ring[s], cw, 0, s);
+    }
+    if constexpr (RESX) {
+#pragma unroll
+      for (int i = 0; i < NPRO; ++i) kx[i] = v[i];
     }
     store_x(tid, v, g);
   }
@@ -914,7 +925,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
     constexpr int PR = BM / NPART;           // rows per staged part
     constexpr int NE = PR * U8 / NT;         // units per lane per part
     static_assert((PR * U8) % NT == 0, "part units must divide evenly");
-    uint4 pr[PREF_R ? NPRO : 1];
+    uint4 pr[PREF_R && !RESX ? NPRO : 1];
     // Defined on every path: a conditionally written px becomes a value
     // carried around the tile loop and stays live through the main loop.
     // 4-wave ROUTED tiles with up to 16 units per lane leave it undefined
@@ -937,7 +948,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
         // the residual rows and the next tile's x rows do not depend on the
         // staged accumulators: they go out first, after the barrier above
         // (which also makes the next tile's row table visible)
-        if constexpr (PREF_R) load_resid(etid, buf, cur, pr);
+        if constexpr (PREF_R && !RESX) load_resid(etid, buf, cur, pr);
         if (has_next) {
           load_gain(pg);
           load_x(etid, buf ^ 1, nx, px);
@@ -1040,14 +1051,16 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
           for (int k = 0; k < UB; ++k) {
             off[k] = uoff(bu[k] < 0 ? 0 : bu[k], pu[k], c8u[k]);
             ev[k] = make_uint4(0, 0, 0, 0);
-            if (a.extra && bu[k] >= 0) ev[k] = ldg16(a.extra + off[k]);
+            // (the inter-residual belongs to the Revert sub-layer: never with RESX)
+            if (!RESX && a.extra && bu[k] >= 0) ev[k] = ldg16(a.extra + off[k]);
             if constexpr (!PREF_R) rv[k] = ldg16(a.resid + off[k]);
           }
 #pragma unroll
           for (int k = 0; k < UB; ++k) {
             if (bu[k] < 0) continue;
             uint4 rvv;
-            if constexpr (PREF_R) rvv = pr[part * NE + i0 + k];
+            if constexpr (RESX) rvv = kx[part * NE + i0 + k];
+            else if constexpr (PREF_R) rvv = pr[part * NE + i0 + k];
             else rvv = rv[k];
             const uint16_t* rh = reinterpret_cast<const uint16_t*>(&rvv);
             const uint16_t* eh = reinterpret_cast<const uint16_t*>(&ev[k]);
@@ -1068,6 +1081,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
     if (MODE == MLP_ROUTED && tid == 0) qslot = qs;
     __syncthreads();                       // staging reads done before x_hat is rewritten
     const int knext = qslot;
+    if constexpr (RESX) {
+#pragma unroll
+      for (int i = 0; i < NPRO; ++i) kx[i] = px[i];
+    }
     store_x(etid, px, pg);
     cur = nx;
     buf ^= 1;
@@ -1086,7 +1103,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
 template <int W, int MODE>
 void launch_wm(const MlpArgs& a, int grid, hipStream_t s) {
   constexpr int NW = mlp_waves(MODE, W), OCC = mlp_occupancy(MODE, W);
-  hipLaunchKernelGGL((mlp_kernel<W, MODE, NW, OCC>), dim3(grid), dim3(64 * NW), 0, s, a);
+  // Mix: the residual is the input through the same map (the raw rows fit
+  // in registers up to W = 512)
+  constexpr bool RESX = MODE == MLP_DENSE && W <= 512;
+  if (RESX && a.map.mix)
+    hipLaunchKernelGGL((mlp_kernel<W, MODE, NW, OCC, RESX>), dim3(grid), dim3(64 * NW), 0, s, a);
+  else
+    hipLaunchKernelGGL((mlp_kernel<W, MODE, NW, OCC, false>), dim3(grid), dim3(64 * NW), 0, s, a);
 }
 
 template <int W>
