@@ -97,14 +97,24 @@ __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
-// RESX (dense Mix sub-layer): the residual is the tile's own input rows,
-// read through the same map, so the raw rows stay in registers from their
-// load to the epilogue instead of being read again (each Mix unit is a
-// separate 2*D/H-byte run of a token, so those reads touch a cache line per
-// run).
-template <int W, int MODE, int NW, int OCC, bool RESX>
+// Row variants of the epilogue (RV), one instantiation each, so that no
+// epilogue load sits on one path only (the compiler would then wait for
+// every load in flight, the next tile's rows and weights included):
+//   RV_PLAIN   residual rows loaded, no inter-residual
+//   RV_EXTRA   residual and inter-residual rows loaded (rows past the tile
+//              end read row 0 and are not used)
+//   RV_MIX     dense Mix sub-layer: the residual is the tile's own input
+//              rows, read through the same map, so the raw rows stay in
+//              registers from their load to the epilogue instead of being
+//              read again (each Mix unit is a separate 2*D/H-byte run of a
+//              token: those reads touch a cache line per run)
+enum { RV_PLAIN = 0, RV_EXTRA = 1, RV_MIX = 2 };
+
+template <int W, int MODE, int NW, int OCC, int RV>
 __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
+  constexpr bool RESX = RV == RV_MIX, EXTRA = RV == RV_EXTRA;
   static_assert(!RESX || MODE == MLP_DENSE, "input rows double as the residual only in dense sub-layers");
+  static_assert(!EXTRA || MODE != MLP_ROUTED, "routed tiles have no residual");
   using S = MlpShape<W, NW, OCC>;
   constexpr int NT = S::NT;
   constexpr int BM = S::BM, XS = S::XS, US = S::US, RBW = S::RBW, NBO = S::NBO;
@@ -1013,9 +1023,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
           // top_k read slot 0; those values are not used): a load on one
           // path only makes the compiler wait for every load in flight where
           // the paths join -- the next tile's weight fragments included. (At
-          // W <= 512 that measured slower.) The inter-residual stays
-          // conditional: most launches have none, and reading a stand-in
-          // would add a whole operand's traffic.
+          // W <= 512 that measured slower.) The inter-residual is loaded
+          // only by the RV_EXTRA instantiation, unconditionally.
           if constexpr (MODE == MLP_SHARED) {
             // the routed experts' gated outputs, four slots at a time
             for (int s0 = 0; s0 < a.top_k; s0 += 4) {
@@ -1051,8 +1060,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
           for (int k = 0; k < UB; ++k) {
             off[k] = uoff(bu[k] < 0 ? 0 : bu[k], pu[k], c8u[k]);
             ev[k] = make_uint4(0, 0, 0, 0);
-            // (the inter-residual belongs to the Revert sub-layer: never with RESX)
-            if (!RESX && a.extra && bu[k] >= 0) ev[k] = ldg16(a.extra + off[k]);
+            if constexpr (EXTRA) ev[k] = ldg16(a.extra + off[k]);
             if constexpr (!PREF_R) rv[k] = ldg16(a.resid + off[k]);
           }
 #pragma unroll
@@ -1105,11 +1113,15 @@ void launch_wm(const MlpArgs& a, int grid, hipStream_t s) {
   constexpr int NW = mlp_waves(MODE, W), OCC = mlp_occupancy(MODE, W);
   // Mix: the residual is the input through the same map (the raw rows fit
   // in registers up to W = 512)
-  constexpr bool RESX = MODE == MLP_DENSE && W <= 512;
-  if (RESX && a.map.mix)
-    hipLaunchKernelGGL((mlp_kernel<W, MODE, NW, OCC, RESX>), dim3(grid), dim3(64 * NW), 0, s, a);
+  constexpr bool MIX_OK = MODE == MLP_DENSE && W <= 512;
+  if (MIX_OK && a.map.mix && !a.extra)
+    hipLaunchKernelGGL((mlp_kernel<W, MODE, NW, OCC, MIX_OK ? RV_MIX : RV_PLAIN>), dim3(grid), dim3(64 * NW), 0, s,
+                       a);
+  else if (MODE != MLP_ROUTED && a.extra)
+    hipLaunchKernelGGL((mlp_kernel<W, MODE, NW, OCC, MODE != MLP_ROUTED ? RV_EXTRA : RV_PLAIN>), dim3(grid),
+                       dim3(64 * NW), 0, s, a);
   else
-    hipLaunchKernelGGL((mlp_kernel<W, MODE, NW, OCC, false>), dim3(grid), dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((mlp_kernel<W, MODE, NW, OCC, RV_PLAIN>), dim3(grid), dim3(64 * NW), 0, s, a);
 }
 
 template <int W>
