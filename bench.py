@@ -133,8 +133,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build runs the block stack on a single "
-              "MI355X (samples shard over GPUs with replicated weights; see DESIGN.md).",
+        print("bench.py measures one GPU only: the block stack runs on a single MI355X "
+              "(across GPUs, samples would shard with the weights replicated).",
               file=sys.stderr)
         return 2
 

@@ -15,7 +15,7 @@ Citations name the page and the equation / section / table they follow:
   mixing constraints, section 6.1 per-token weight layout).
 * [RMX-BOOK] the fun-rec mdbook chapter 7.4 on RankMixer (7.4.1, 7.4.2).
 
-Precision contract (the pages fix none, see the readings in the design doc): all
+Precision contract (the pages fix none; this is the plainest reading): all
 arithmetic is fp64. In bf16 mode the value is rounded to bf16 (round to
 nearest, ties to even) exactly at the storage points the GPU path has:
 the normalised rows x_hat, the SwiGLU hidden U, and each sub-layer output
