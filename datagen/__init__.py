@@ -76,7 +76,8 @@ class Workload:
     alpha: float = 0.0       # 0 means E / top_k
     eps: float = 1e-6
     gap: int = 2             # inter-residual gap (0 = none)
-    dtype: str = "bf16"      # "bf16" or "f32"
+    dtype: str = "bf16"      # "bf16", "f32", or "mxfp8" (bf16 activations and weights,
+                             # MXFP8 GEMM operands inside the library)
     seed: int = 0
     down_scale: float = 0.01
 
@@ -84,6 +85,11 @@ class Workload:
     @property
     def moe(self) -> bool:
         return self.E > 0
+
+    @property
+    def bf16_values(self) -> bool:
+        """Activations and weights are handed over as bf16 values."""
+        return self.dtype in ("bf16", "mxfp8")
 
     @property
     def dh(self) -> int:
@@ -185,7 +191,7 @@ def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
 
 
 def _finish(cfg: Workload, a: np.ndarray) -> np.ndarray:
-    return to_bf16_values(a) if cfg.dtype == "bf16" else a
+    return to_bf16_values(a) if cfg.bf16_values else a
 
 
 def make_x(cfg: Workload, seed: Optional[int] = None, B: Optional[int] = None) -> np.ndarray:
@@ -240,7 +246,7 @@ def weight_banks(cfg: Workload, seed: Optional[int] = None, workers: int = 0):
     the GIL); every slice has its own seed key, so the values do not depend
     on ``workers``."""
     from concurrent.futures import ThreadPoolExecutor
-    bf16 = cfg.dtype == "bf16"
+    bf16 = cfg.bf16_values
     banks = {}
     jobs = []
     for l in range(1, cfg.L + 1):

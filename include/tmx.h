@@ -50,7 +50,14 @@ typedef enum tmx_status {
   TMX_ERR_STATE = 5        /* e.g. forward before every weight was loaded */
 } tmx_status;
 
-typedef enum tmx_dtype { TMX_F32 = 0, TMX_BF16 = 1 } tmx_dtype;
+/* TMX_MXFP8: bf16 activations and weights at the boundary, with the GEMM
+ * operands of the dense per-token SwiGLU quantised to MXFP8 inside the
+ * library ("FP8 E4M3 post-training quantisation", TokenMixer-Large summary
+ * section 2.5.2; read as E4M3 elements with one power-of-two scale per 32
+ * values along each GEMM's contraction axis): weights when they are loaded,
+ * the normalised rows and the SwiGLU hidden in the kernel. Dense contexts
+ * only. */
+typedef enum tmx_dtype { TMX_F32 = 0, TMX_BF16 = 1, TMX_MXFP8 = 2 } tmx_dtype;
 
 typedef enum tmx_sublayer { TMX_MIX = 0, TMX_REVERT = 1 } tmx_sublayer;
 

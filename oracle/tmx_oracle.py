@@ -38,6 +38,8 @@ __all__ = [
     "round_bf16", "mix", "revert", "rmsnorm", "silu", "softmax", "swiglu",
     "route", "moe", "sublayer_positions", "block_forward", "stack_forward",
     "flops_per_sample", "param_count_closed_form",
+    "E4M3_MAX", "MX_BLOCK", "e4m3_value", "e4m3_round", "mx_exponent", "mx_quantize",
+    "mx_dequantize", "mx_round", "swiglu_mx",
 ]
 
 BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
@@ -150,6 +152,99 @@ def swiglu(v: np.ndarray, w_up: np.ndarray, w_gate: np.ndarray, w_down: np.ndarr
 
 
 # ---------------------------------------------------------------------------
+# FP8 serving   [TML] 2.5.2 (FP8 E4M3 post-training quantisation)
+#
+# The pages name the element format only. Reading: both operands of every
+# GEMM are quantised, with microscaling -- one power-of-two scale per 32
+# consecutive values along the contraction axis (the OCP MX layout: E4M3
+# elements, E8M0 shared scales) -- fp32 accumulation, and bf16 activations
+# between the GEMMs as in the bf16 path.
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0      # largest finite E4M3 value, 1.75 * 2**8
+MX_BLOCK = 32
+
+
+def e4m3_value(code) -> np.ndarray:
+    """Value of FP8 E4M3 codes: sign bit, 4 exponent bits (bias 7), 3
+    mantissa bits; exponent field 0 holds the subnormals m/8 * 2**-6; there
+    are no infinities and S.1111.111 is NaN."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+_E4M3_NONNEG = e4m3_value(np.arange(0x7F))     # codes 0x00..0x7E, ascending 0 .. 448
+
+
+def e4m3_round(x) -> np.ndarray:
+    """E4M3 code of finite x: the nearest representable value, ties to the
+    even code, with |x| > 448 taken as 448 (saturating conversion). The sign
+    bit follows x (a negative value that rounds to zero gives 0x80)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.minimum(np.searchsorted(_E4M3_NONNEG, a, side="left"), 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E4M3_NONNEG[lo]
+    d_hi = _E4M3_NONNEG[hi] - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def mx_exponent(amax) -> np.ndarray:
+    """Shared exponent k of a block with largest magnitude amax: the block is
+    stored as E4M3(x / 2**k) with k = floor(log2(amax)) - 8, 8 being the
+    exponent of E4M3's largest normal, so the largest value maps into
+    [2**8, 2**9) (values above 448 saturate). k is clamped to the E8M0 range
+    [-127, 127]; an all-zero block takes -127."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, e = np.frexp(amax)                       # amax = f * 2**e, 0.5 <= f < 1
+    k = np.where(amax > 0, e - 1 - 8, -127)
+    return np.clip(k, -127, 127).astype(np.int64)
+
+
+def mx_quantize(x):
+    """MXFP8 along the last axis (its length a multiple of 32): returns the
+    E4M3 codes and the block exponents k. x is taken as fp32, the precision
+    the quantised operands are produced in; x / 2**k is exact."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    n = x.shape[-1]
+    if n % MX_BLOCK:
+        raise ValueError(f"MX blocks need a multiple of {MX_BLOCK} values, got {n}")
+    xb = x.reshape(x.shape[:-1] + (n // MX_BLOCK, MX_BLOCK))
+    k = mx_exponent(np.max(np.abs(xb), axis=-1))
+    codes = e4m3_round(np.ldexp(xb, -k[..., None]))
+    return codes.reshape(x.shape), k
+
+
+def mx_dequantize(codes, k) -> np.ndarray:
+    codes = np.asarray(codes)
+    n = codes.shape[-1]
+    cb = codes.reshape(codes.shape[:-1] + (n // MX_BLOCK, MX_BLOCK))
+    return (e4m3_value(cb) * np.exp2(np.asarray(k, np.float64))[..., None]).reshape(codes.shape)
+
+
+def mx_round(x) -> np.ndarray:
+    """Quantise to MXFP8 along the last axis and back (fp64 values)."""
+    return mx_dequantize(*mx_quantize(x))
+
+
+def swiglu_mx(v: np.ndarray, w_up: np.ndarray, w_gate: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """pSwiGLU of one position ([TML] Eq. 17-18) with MXFP8 GEMM operands
+    ([TML] 2.5.2): the rows v and the columns of W_up, W_gate are quantised in
+    blocks of 32 along W, the hidden U = silu(g) * u (fp32) and the columns of
+    W_down in blocks of 32 along h; the products and sums are exact."""
+    vq = mx_round(v)
+    g = vq @ mx_round(np.asarray(w_gate).T).T
+    u = vq @ mx_round(np.asarray(w_up).T).T
+    U = mx_round(silu(g) * u)
+    return U @ mx_round(np.asarray(w_down).T).T
+
+
+# ---------------------------------------------------------------------------
 # Sparse-Pertoken MoE   [TML] section 2.4, Eq. 19-21
 # ---------------------------------------------------------------------------
 
@@ -210,16 +305,24 @@ _K_ROUTER, _K_EUP, _K_EGATE, _K_EDOWN, _K_SUP, _K_SGATE, _K_SDOWN = 4, 5, 6, 7, 
 
 def sublayer_positions(x: np.ndarray, resid: np.ndarray, cfg, layer: int, sub: int,
                        weights: WeightGetter, extra: Optional[np.ndarray] = None,
-                       rho: bool = False, record: Optional[dict] = None) -> np.ndarray:
+                       rho: bool = False, record: Optional[dict] = None, mx: bool = False) -> np.ndarray:
     """One Pre-Norm sub-layer over position-major rows:
     out[:, p] = resid[:, p] + F_p(RMSNorm(x[:, p])) [+ extra[:, p]], rounded
     once in bf16 mode. x, resid, extra are [n, P, W]; F_p is the position's
     own SwiGLU (dense) or Sparse-Pertoken MoE. ``record`` (optional dict)
-    receives per-position routing {(p): (idx, gate)} for MoE sub-layers."""
+    receives per-position routing {(p): (idx, gate)} for MoE sub-layers.
+    With ``mx`` (dense only) the SwiGLU runs on MXFP8 operands (swiglu_mx),
+    its input rows being the fp32 normalised rows."""
     n, P, W = x.shape
     gain = weights(layer, sub, _K_GAIN, 0)
     F = np.zeros((n, P, W))
     for p in range(P):
+        if mx:
+            if cfg.E != 0:
+                raise ValueError("the MXFP8 path covers dense sub-layers")
+            F[:, p] = swiglu_mx(rmsnorm(x[:, p, :], gain, cfg.eps), weights(layer, sub, _K_UP, p),
+                                weights(layer, sub, _K_GATE, p), weights(layer, sub, _K_DOWN, p))
+            continue
         xh = _rho(rmsnorm(x[:, p, :], gain, cfg.eps), rho)
         if cfg.E == 0:
             F[:, p] = swiglu(xh, weights(layer, sub, _K_UP, p), weights(layer, sub, _K_GATE, p),
@@ -241,7 +344,7 @@ def sublayer_positions(x: np.ndarray, resid: np.ndarray, cfg, layer: int, sub: i
 
 def block_forward(X: np.ndarray, cfg, layer: int, weights: WeightGetter,
                   extra: Optional[np.ndarray] = None, rho: bool = False,
-                  trace: Optional[dict] = None) -> np.ndarray:
+                  trace: Optional[dict] = None, mx: bool = False) -> np.ndarray:
     """One TokenMixer-Large block in Pre-Norm form ([TML-README] diagram;
     [TML] Eq. 12, 16 with Pre-Norm per section 2.3.3):
         Hm      = Mix(X)
@@ -251,28 +354,31 @@ def block_forward(X: np.ndarray, cfg, layer: int, weights: WeightGetter,
     ``extra`` is the inter-residual term added before the single rounding."""
     Hm = mix(X, cfg.H)
     Hn = sublayer_positions(Hm, Hm, cfg, layer, 0, weights, None, rho,
-                            None if trace is None else trace.setdefault((layer, 0), {}))
+                            None if trace is None else trace.setdefault((layer, 0), {}), mx)
     Xr = revert(Hn, cfg.T)
     if trace is not None:
         trace[("in", layer, 0)] = X
         trace[("in", layer, 1)] = Xr
     return sublayer_positions(Xr, X, cfg, layer, 1, weights, extra, rho,
-                              None if trace is None else trace.setdefault((layer, 1), {}))
+                              None if trace is None else trace.setdefault((layer, 1), {}), mx)
 
 
 def stack_forward(X: np.ndarray, cfg, weights: WeightGetter, rho: Optional[bool] = None,
-                  trace: Optional[dict] = None) -> np.ndarray:
+                  trace: Optional[dict] = None, mx: Optional[bool] = None) -> np.ndarray:
     """The L-block stack with inter-residuals ([TML] 2.3.4; [TML-README]):
     Y_0 = X; Z_l = Block_l(Y_{l-1}); Y_l = Z_l + Y_{l-g} when g > 0,
     l mod g == 0 and l < L (never after the last block); else Y_l = Z_l.
-    Returns Y_L. ``rho`` defaults to the workload dtype being bf16."""
+    Returns Y_L. ``rho`` defaults to the workload's activations being bf16
+    (dtype bf16 or mxfp8), ``mx`` to the dtype being mxfp8."""
+    if mx is None:
+        mx = cfg.dtype == "mxfp8"
     if rho is None:
-        rho = cfg.dtype == "bf16"
+        rho = cfg.dtype in ("bf16", "mxfp8")
     Y = [np.asarray(X, dtype=np.float64)]
     g = cfg.gap
     for l in range(1, cfg.L + 1):
         extra = Y[l - g] if (g > 0 and l % g == 0 and l < cfg.L) else None
-        Y.append(block_forward(Y[l - 1], cfg, l, weights, extra, rho, trace))
+        Y.append(block_forward(Y[l - 1], cfg, l, weights, extra, rho, trace, mx))
     return Y[cfg.L]
 
 

@@ -79,7 +79,7 @@ def test_status_and_enum_values_match_header(tmx):
                       ("TMX_W_EXP_GATE", dg.K_EXP_GATE), ("TMX_W_EXP_DOWN", dg.K_EXP_DOWN),
                       ("TMX_W_SH_UP", dg.K_SH_UP), ("TMX_W_SH_GATE", dg.K_SH_GATE),
                       ("TMX_W_SH_DOWN", dg.K_SH_DOWN), ("TMX_MIX", 0), ("TMX_REVERT", 1),
-                      ("TMX_F32", 0), ("TMX_BF16", 1)]:
+                      ("TMX_F32", 0), ("TMX_BF16", 1), ("TMX_MXFP8", 2)]:
         m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
         assert m and int(m.group(1)) == val, name
 

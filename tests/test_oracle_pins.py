@@ -463,3 +463,114 @@ def test_flops_equal_params_for_dense_pertoken():
     assert orc.flops_per_sample(dg.WORKLOADS[2]) == 201_326_592
     assert orc.flops_per_sample(dg.WORKLOADS[4]) == 1_212_153_856
     assert orc.flops_per_sample(dg.WORKLOADS[5]) == 5_460_983_808
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 operands of the FP8 serving path (TML 2.5.2): E4M3 elements checked
+# against torch's float8_e4m3fn (an independent implementation of the OCP
+# format) and the format's published extreme values; MX block scaling
+# against its defining properties
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decode_matches_torch_and_format_extremes():
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = orc.e4m3_value(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert np.isnan(got[[0x7F, 0xFF]]).all() and np.isnan(got).sum() == 2
+    assert got[0x7E] == 448.0 and got[0xFE] == -448.0          # largest normal
+    assert got[0x08] == 2.0 ** -6 and got[0x07] == 0.875 * 2.0 ** -6   # smallest normal, largest subnormal
+    assert got[0x01] == 2.0 ** -9 and got[0x38] == 1.0 and got[0x00] == 0.0
+
+
+def test_e4m3_round_matches_torch_and_saturates():
+    import torch
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(100000) * np.exp2(rng.integers(-14, 9, 100000))).astype(np.float32)
+    x = np.clip(x, -448, 448).astype(np.float32)
+    # exact midpoints between neighbouring codes (ties go to the even code)
+    v = orc.e4m3_value(np.arange(0x7F))
+    mid = ((v[:-1] + v[1:]) / 2).astype(np.float32)
+    x = np.concatenate([x, mid, -mid, v.astype(np.float32)])
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = orc.e4m3_round(x)
+    assert np.array_equal(got, want)
+    big = np.array([448.0, 449.0, 464.0, 480.0, 1e6, 3e38], np.float32)
+    assert (orc.e4m3_round(big) == 0x7E).all() and (orc.e4m3_round(-big) == 0xFE).all()
+
+
+def test_mx_exponent_cases():
+    # the block maximum lands in [2**8, 2**9) after scaling
+    amax = np.array([1.0, 448.0, 256.0, 255.99, 511.9, 2.0 ** -20, 3e-30, 1e38, 0.0])
+    assert orc.mx_exponent(amax).tolist() == [-8, 0, 0, -1, 0, -28, -107, 118, -127]
+    a = np.exp2(np.random.default_rng(3).uniform(-100, 100, 1000))
+    k = orc.mx_exponent(a)
+    assert ((a / np.exp2(k) >= 256) & (a / np.exp2(k) < 512)).all()
+
+
+def test_mx_quantize_blocks_error_bound_and_axis():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((7, 96)).astype(np.float32)
+    codes, k = orc.mx_quantize(x)
+    assert codes.shape == x.shape and k.shape == (7, 3)
+    # blocks along the last axis are independent: scaling one block by 2**s
+    # moves only its exponent
+    y = x.copy()
+    y[2, 32:64] *= np.float32(2.0 ** 13)
+    c2, k2 = orc.mx_quantize(y)
+    assert np.array_equal(c2, codes)
+    d = k2 - k
+    assert d[2, 1] == 13 and np.count_nonzero(d) == 1
+    # values already on the block's grid come back exactly
+    q = orc.mx_round(x)
+    assert np.array_equal(orc.mx_round(q), q)
+    # round to nearest: at most half a step of the E4M3 grid (relative 2**-4
+    # for normal values, 2**-10 * 2**k below the smallest normal), except
+    # values above 448 * 2**k, which saturate
+    s = np.repeat(np.exp2(k.astype(np.float64)), 32, axis=1)
+    r = np.abs(x.astype(np.float64)) / s
+    err = np.abs(q - x) / s
+    normal = (r >= 2.0 ** -6) & (r <= 448)
+    assert (err[normal] <= 2.0 ** (np.floor(np.log2(r[normal])) - 4) + 1e-12).all()
+    assert (err[r < 2.0 ** -6] <= 2.0 ** -10 + 1e-15).all()
+    assert (np.abs(q[r > 448]) / s[r > 448] == 448).all()
+    # rows of very different magnitude each keep their own scale only if the
+    # blocks run along the last axis: row-normwise error at most 1/8 (a
+    # block maximum in (448, 512) * 2**k saturates to 448 * 2**k); blocks
+    # across rows would flush the small rows to zero
+    m = (rng.standard_normal((4, 64)) * np.exp2(np.array([-30.0, -5.0, 10.0, 40.0]))[:, None]).astype(np.float32)
+    rel = np.max(np.abs(orc.mx_round(m) - m), axis=1) / np.max(np.abs(m), axis=1)
+    assert rel.max() <= 0.125 + 1e-9
+
+
+def test_swiglu_mx_close_to_exact_with_skewed_columns():
+    """The quantised SwiGLU stays within the fp8 error of the exact one even
+    when weight columns and input rows differ by many binades, which only
+    holds if every operand is blocked along its contraction axis."""
+    rng = np.random.default_rng(13)
+    W, h, n = 64, 96, 40
+    v = rng.standard_normal((n, W)) * np.exp2(rng.integers(-20, 20, (n, 1)))
+    wg = rng.standard_normal((W, h)) / 8 * np.exp2(rng.integers(-12, 12, (1, h)))
+    wu = rng.standard_normal((W, h)) / 8 * np.exp2(rng.integers(-12, 12, (1, h)))
+    wd = rng.standard_normal((h, W)) / 8 * np.exp2(rng.integers(-12, 12, (1, W)))
+    # keep the hidden activations O(1)-scaled per row so silu stays in range
+    v = v / np.max(np.abs(v), axis=1, keepdims=True)
+    exact = orc.swiglu(v, wu, wg, wd)
+    q = orc.swiglu_mx(v, wu, wg, wd)
+    # compare column-normwise: the down columns carry their own scales
+    err = np.max(np.abs(q - exact), axis=0) / np.max(np.abs(exact), axis=0)
+    assert err.max() < 0.15 and err.max() > 1e-4
+
+
+def test_mxfp8_stack_is_the_dense_stack_within_fp8_error():
+    cfg = dg.Workload("mx_small", B=24, T=4, H=2, D=64, L=2, hidden_mix=64, hidden_rev=96,
+                      gap=2, dtype="mxfp8", seed=17)
+    ws = dg.WeightSource(cfg)
+    X = dg.make_x(cfg).astype(np.float64)
+    a = orc.stack_forward(X, cfg, ws)                 # MXFP8 GEMMs, bf16 outputs
+    b = orc.stack_forward(X, cfg, ws, rho=True, mx=False)
+    err = np.max(np.abs(a - b), axis=-1) / np.max(np.abs(b), axis=-1)
+    assert 0 < err.max() < 5e-2

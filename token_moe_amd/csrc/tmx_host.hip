@@ -141,8 +141,11 @@ tmx_status check_launch(tmx_ctx* c, hipError_t e, const char* what) {
 tmx_status validate_config(const tmx_config* cfg) {
   if (!cfg) return fail(nullptr, TMX_ERR_INVALID_ARG, "cfg is NULL");
   const tmx_config& c = *cfg;
-  if (c.dtype != TMX_F32 && c.dtype != TMX_BF16)
-    return fail(nullptr, TMX_ERR_INVALID_ARG, "dtype must be TMX_F32 (0) or TMX_BF16 (1), got %d", c.dtype);
+  if (c.dtype != TMX_F32 && c.dtype != TMX_BF16 && c.dtype != TMX_MXFP8)
+    return fail(nullptr, TMX_ERR_INVALID_ARG, "dtype must be TMX_F32 (0), TMX_BF16 (1) or TMX_MXFP8 (2), got %d",
+                c.dtype);
+  if (c.dtype == TMX_MXFP8)
+    return fail(nullptr, TMX_ERR_UNSUPPORTED, "TMX_MXFP8 is not available in this build");
   if (c.B_max < 1 || c.T < 1 || c.H < 1 || c.D < 1 || c.L < 1)
     return fail(nullptr, TMX_ERR_INVALID_ARG, "B_max, T, H, D, L must be >= 1 (got %d, %d, %d, %d, %d)", c.B_max,
                 c.T, c.H, c.D, c.L);

@@ -18,12 +18,12 @@ def config_from_workload(wl, B_max: Optional[int] = None) -> tmx.tmx_config:
         hidden_mix=wl.hidden_mix, hidden_rev=wl.hidden_rev, E=wl.E, top_k=wl.top_k,
         expert_hidden=wl.expert_hidden, shared_hidden=wl.shared_hidden, alpha=wl.alpha,
         eps=wl.eps, inter_residual_gap=wl.gap,
-        dtype=tmx.TMX_BF16 if wl.dtype == "bf16" else tmx.TMX_F32)
+        dtype={"bf16": tmx.TMX_BF16, "mxfp8": tmx.TMX_MXFP8}.get(wl.dtype, tmx.TMX_F32))
 
 
 def torch_dtype(wl):
     import torch
-    return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    return torch.bfloat16 if wl.bf16_values else torch.float32
 
 
 def host_tensor(wl, a: np.ndarray):
@@ -32,7 +32,7 @@ def host_tensor(wl, a: np.ndarray):
     (already representable in the workload dtype)."""
     import torch
     if a.dtype == np.uint16:
-        if wl.dtype != "bf16":
+        if not wl.bf16_values:
             raise ValueError("bf16 bit patterns given for a non-bf16 workload")
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch_dtype(wl)).contiguous()

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libtmx.so")
 
 TMX_OK, TMX_ERR_INVALID_ARG, TMX_ERR_UNSUPPORTED, TMX_ERR_OOM, TMX_ERR_DEVICE, TMX_ERR_STATE = range(6)
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "OOM", 4: "DEVICE", 5: "STATE"}
-TMX_F32, TMX_BF16 = 0, 1
+TMX_F32, TMX_BF16, TMX_MXFP8 = 0, 1, 2
 TMX_MIX, TMX_REVERT = 0, 1
 
 EXPORTED = ("tmx_create", "tmx_destroy", "tmx_last_error", "tmx_load_weights",
