@@ -82,8 +82,9 @@ def sample_rows(B, n, seed=0):
 
 def oracle_sublayer(wl, ws, layer, sub, x_rows, resid_rows=None, extra_rows=None):
     """Oracle of one sub-layer in block layout [n, T, D] (layer is 1-based)."""
-    rho = wl.dtype == "bf16"
+    rho = wl.bf16_values
+    mx = wl.dtype == "mxfp8"
     if sub == 0:
         Hm = orc.mix(x_rows, wl.H)
-        return orc.revert(orc.sublayer_positions(Hm, Hm, wl, layer, 0, ws, None, rho), wl.T)
-    return orc.sublayer_positions(x_rows, resid_rows, wl, layer, 1, ws, extra_rows, rho)
+        return orc.revert(orc.sublayer_positions(Hm, Hm, wl, layer, 0, ws, None, rho, None, mx), wl.T)
+    return orc.sublayer_positions(x_rows, resid_rows, wl, layer, 1, ws, extra_rows, rho, None, mx)

@@ -114,6 +114,11 @@ def _create(tmx, **kw):
     (dict(dtype=1, D=96, H=4, T=4, hidden_mix=64, hidden_rev=64), "UNSUPPORTED"),      # W = 96
     (dict(dtype=1, D=128, H=4, T=4, hidden_mix=100, hidden_rev=64), "UNSUPPORTED"),    # hidden % 64
     (dict(dtype=1, D=128, H=4, T=4, E=8, top_k=2, expert_hidden=64, shared_hidden=64), "UNSUPPORTED"),
+    # MXFP8: dense, W = 256 in both sub-layers, hidden <= 1024
+    (dict(dtype=2, D=512, H=16, T=16, hidden_mix=256, hidden_rev=256), "UNSUPPORTED"),
+    (dict(dtype=2, D=256, H=16, T=16, hidden_mix=2048, hidden_rev=256), "UNSUPPORTED"),
+    (dict(dtype=2, D=256, H=16, T=16, E=16, top_k=4, expert_hidden=256, shared_hidden=512), "UNSUPPORTED"),
+    (dict(dtype=3), "INVALID_ARG"),
     # x_hat workspace (B_max*T*D bf16) must stay under 4 GiB
     (dict(dtype=1, B_max=1 << 21, D=512, H=16, T=16, E=16, top_k=4, expert_hidden=256, shared_hidden=512),
      "UNSUPPORTED"),

@@ -65,7 +65,7 @@ tmx_status fail(tmx_ctx* c, tmx_status s, const char* fmt, ...) {
   return s;
 }
 
-size_t esize(const tmx_config& c) { return c.dtype == TMX_BF16 ? 2 : 4; }
+size_t esize(const tmx_config& c) { return c.dtype == TMX_F32 ? 4 : 2; }   // MXFP8: bf16 activations
 int positions(const tmx_config& c, int sub) { return sub == TMX_MIX ? c.H : c.T; }
 int width(const tmx_config& c, int sub) { return sub == TMX_MIX ? c.T * (c.D / c.H) : c.D; }
 int dense_hidden(const tmx_config& c, int sub) { return sub == TMX_MIX ? c.hidden_mix : c.hidden_rev; }
@@ -106,7 +106,7 @@ Bank& bank(tmx_ctx* c, int layer, int sub, int kind) {
 
 // storage of a bank: gate and up share one interleaved fragment buffer in bf16
 Bank& storage(tmx_ctx* c, int layer, int sub, int kind) {
-  if (c->cfg.dtype == TMX_BF16) {
+  if (c->cfg.dtype != TMX_F32) {
     if (kind == TMX_W_UP) kind = TMX_W_GATE;
     if (kind == TMX_W_EXP_UP) kind = TMX_W_EXP_GATE;
     if (kind == TMX_W_SH_UP) kind = TMX_W_SH_GATE;
@@ -144,8 +144,19 @@ tmx_status validate_config(const tmx_config* cfg) {
   if (c.dtype != TMX_F32 && c.dtype != TMX_BF16 && c.dtype != TMX_MXFP8)
     return fail(nullptr, TMX_ERR_INVALID_ARG, "dtype must be TMX_F32 (0), TMX_BF16 (1) or TMX_MXFP8 (2), got %d",
                 c.dtype);
-  if (c.dtype == TMX_MXFP8)
-    return fail(nullptr, TMX_ERR_UNSUPPORTED, "TMX_MXFP8 is not available in this build");
+  if (c.dtype == TMX_MXFP8) {
+    if (c.E > 0) return fail(nullptr, TMX_ERR_UNSUPPORTED, "the MXFP8 path covers dense stacks (E = 0)");
+    if ((c.D / c.H) % 8 != 0)
+      return fail(nullptr, TMX_ERR_UNSUPPORTED, "MXFP8 path needs D/H %% 8 == 0, got %d", c.D / c.H);
+    for (int sub = 0; sub < 2; ++sub) {
+      if (width(c, sub) != 256)
+        return fail(nullptr, TMX_ERR_UNSUPPORTED, "MXFP8 path supports sub-layer width 256, got %d", width(c, sub));
+      const int h = dense_hidden(c, sub);
+      if (h % MLP_HC != 0 || h > (MX_REC_DWORDS / 3) * MLP_HC)
+        return fail(nullptr, TMX_ERR_UNSUPPORTED, "MXFP8 path needs hidden %% %d == 0 and hidden <= %d, got %d",
+                    MLP_HC, (MX_REC_DWORDS / 3) * MLP_HC, h);
+    }
+  }
   if (c.B_max < 1 || c.T < 1 || c.H < 1 || c.D < 1 || c.L < 1)
     return fail(nullptr, TMX_ERR_INVALID_ARG, "B_max, T, H, D, L must be >= 1 (got %d, %d, %d, %d, %d)", c.B_max,
                 c.T, c.H, c.D, c.L);
@@ -186,7 +197,7 @@ tmx_status validate_config(const tmx_config* cfg) {
     if (c.E > 0 && act >= (int64_t)1 << 31)
       return fail(nullptr, TMX_ERR_UNSUPPORTED,
                   "bf16 MoE needs B_max*T*D < 2^31 (the x_hat workspace is addressed with 32-bit byte offsets)");
-  } else {
+  } else if (c.dtype == TMX_F32) {
     if (c.E > 256 || c.top_k > 64) return fail(nullptr, TMX_ERR_UNSUPPORTED, "fp32 MoE needs E <= 256, top_k <= 64");
     const int hmax = std::max({c.hidden_mix, c.hidden_rev, c.expert_hidden, c.shared_hidden});
     const int Wmax = std::max(width(c, 0), width(c, 1));
@@ -267,6 +278,12 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
     a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_GATE).ptr);
     a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_DOWN).ptr);
     set_row_tiles(a, MLP_DENSE, sub, W, P, B, map.dh * 2);
+    if (cfg.dtype == TMX_MXFP8) {
+      a.wsc = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(a.wgu) +
+                                                (size_t)2 * kind_elems(cfg, sub, TMX_W_GATE));
+      return check_launch(c, launch_mlp_mx(a, (a.pair ? P / 2 : P) * a.rtiles, c->workers, st),
+                          "dense MXFP8 MLP launch");
+    }
     return check_launch(c, launch_mlp(MLP_DENSE, W, a, (a.pair ? P / 2 : P) * a.rtiles, c->workers, st),
                         "dense MLP launch");
   }
@@ -393,10 +410,15 @@ tmx_status tmx_create(const tmx_config* cfg, int device, tmx_ctx** out) {
           b.loaded = true;
           continue;
         }
-        if (C.dtype == TMX_BF16 && (k == TMX_W_UP || k == TMX_W_EXP_UP || k == TMX_W_SH_UP)) continue;
+        if (C.dtype != TMX_F32 && (k == TMX_W_UP || k == TMX_W_EXP_UP || k == TMX_W_SH_UP)) continue;
         size_t n = b.elems;
-        if (C.dtype == TMX_BF16 && (k == TMX_W_GATE || k == TMX_W_EXP_GATE || k == TMX_W_SH_GATE)) n *= 2;
-        s = dev_alloc(c, &b.ptr, n * es, "weights");
+        if (C.dtype != TMX_F32 && (k == TMX_W_GATE || k == TMX_W_EXP_GATE || k == TMX_W_SH_GATE)) n *= 2;
+        size_t bytes = n * es;
+        // MXFP8: one byte per weight; the gate bank also holds the scale
+        // records of the position's gate, up and down matrices
+        if (C.dtype == TMX_MXFP8)
+          bytes = n + (k == TMX_W_GATE ? (size_t)positions(C, sub) * 4 * 64 * MX_REC_DWORDS * 4 : 0);
+        s = dev_alloc(c, &b.ptr, bytes, "weights");
         if (s != TMX_OK) return bail(s);
       }
 
@@ -510,7 +532,14 @@ tmx_status tmx_load_weights(tmx_ctx* c, int layer, int sub, int kind, const void
   const bool gu = kind == TMX_W_UP || kind == TMX_W_GATE || kind == TMX_W_EXP_UP || kind == TMX_W_EXP_GATE ||
                   kind == TMX_W_SH_UP || kind == TMX_W_SH_GATE;
   const int which = (kind == TMX_W_UP || kind == TMX_W_EXP_UP || kind == TMX_W_SH_UP) ? 1 : 0;
-  if (e == hipSuccess)
+  if (e == hipSuccess && C.dtype == TMX_MXFP8) {
+    uint8_t* gu = static_cast<uint8_t*>(storage(c, layer, sub, TMX_W_GATE).ptr);
+    uint8_t* rec = gu + (size_t)2 * kind_elems(C, sub, TMX_W_GATE);
+    uint8_t* dst = gu;
+    if (kind == TMX_W_DOWN) dst = static_cast<uint8_t*>(bank(c, layer, sub, TMX_W_DOWN).ptr);
+    e = launch_pack_mx(static_cast<const uint16_t*>(stage), dst, rec, (int)G, K, N, kind == TMX_W_DOWN ? 1 : 0, which,
+                       st);
+  } else if (e == hipSuccess)
     e = launch_pack(static_cast<const uint16_t*>(stage), static_cast<uint16_t*>(storage(c, layer, sub, kind).ptr),
                     (int)G, K, N, gu ? 0 : 1, which, kind == TMX_W_ROUTER ? FRAG_16x16x32 : FRAG_32x32x16, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);

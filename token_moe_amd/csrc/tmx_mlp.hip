@@ -91,6 +91,55 @@ __device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 32x32x64 E4M3 x E4M3 -> fp32 with E8M0 block scales: lane l supplies the
+// scale of (row l % 32, K-block l / 32) of its operand in byte OA of sa (A)
+// and byte OB of sb (B). A lane's 32 operand bytes: 0-15 are K 16 (l / 32)
+// + j of K-block 0, 16-31 the same of K-block 1.
+__device__ __forceinline__ i32x8 join8(const uint4& a, const uint4& b) {
+  return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
+template <int OA, int OB>
+__device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, uint32_t sa, uint32_t sb, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OA, (int)sa, OB, (int)sb);
+}
+// the scale-byte selectors the kernel uses, from loop indices that are
+// constants after unrolling
+__device__ __forceinline__ f32x16 mfma8s(int oa, int ob, const i32x8& a, const i32x8& b, uint32_t sa, uint32_t sb,
+                                         const f32x16& c) {
+  switch (oa * 4 + ob) {
+    case 0: return mfma8<0, 0>(a, b, sa, sb, c);
+    case 5: return mfma8<1, 1>(a, b, sa, sb, c);
+    case 10: return mfma8<2, 2>(a, b, sa, sb, c);
+    case 15: return mfma8<3, 3>(a, b, sa, sb, c);
+    case 8: return mfma8<2, 0>(a, b, sa, sb, c);
+    case 13: return mfma8<3, 1>(a, b, sa, sb, c);
+    case 4: return mfma8<1, 0>(a, b, sa, sb, c);
+    default: return mfma8<0, 1>(a, b, sa, sb, c);
+  }
+}
+
+// E4M3 bytes of x[0..3] * 2^-k (exact scaling), clamped to +-448 first: the
+// hardware conversion rounds to nearest even but does not saturate
+__device__ __forceinline__ uint32_t e4m3x4(float x0, float x1, float x2, float x3, float sc) {
+  x0 = fminf(fmaxf(x0 * sc, -448.f), 448.f);
+  x1 = fminf(fmaxf(x1 * sc, -448.f), 448.f);
+  x2 = fminf(fmaxf(x2 * sc, -448.f), 448.f);
+  x3 = fminf(fmaxf(x3 * sc, -448.f), 448.f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+  return (uint32_t)w;
+}
+// MX shared exponent of a block with largest magnitude amax: floor(log2(amax))
+// - 8 (E4M3's largest normal is 1.75 * 2^8), clamped to the E8M0 range
+__device__ __forceinline__ int mx_exp(float amax) {
+  int e = 0;
+  (void)frexpf(amax, &e);
+  int k = amax > 0.f ? e - 9 : -127;
+  return k < -127 ? -127 : (k > 127 ? 127 : k);
+}
+
 // silu(z) = z * sigmoid(z) with the hardware exp and reciprocal (~1 ulp
 // each); the result is rounded to bf16 right after, so this is exact enough.
 __device__ __forceinline__ float silu_fast(float z) {
@@ -110,9 +159,13 @@ __device__ __forceinline__ float silu_fast(float z) {
 //              token: those reads touch a cache line per run)
 enum { RV_PLAIN = 0, RV_EXTRA = 1, RV_MIX = 2 };
 
-template <int W, int MODE, int NW, int OCC, int RV>
+// F8: the dense W = 256 kernel (two 4-wave workgroups per CU) with MXFP8 GEMM
+// operands: weights packed at load (launch_pack_mx), x_hat and U quantised
+// here per row and 32-element block along each GEMM's contraction axis.
+template <int W, int MODE, int NW, int OCC, int RV, bool F8>
 __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   constexpr bool RESX = RV == RV_MIX, EXTRA = RV == RV_EXTRA;
+  static_assert(!F8 || (W == 256 && MODE == MLP_DENSE && NW == 4 && OCC == 2), "MXFP8 kernel shape");
   static_assert(!RESX || MODE == MLP_DENSE, "input rows double as the residual only in dense sub-layers");
   static_assert(!EXTRA || MODE != MLP_ROUTED, "routed tiles have no residual");
   using S = MlpShape<W, NW, OCC>;
@@ -142,6 +195,17 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   uint16_t* const xs = reinterpret_cast<uint16_t*>(smem);
   uint16_t* const us = reinterpret_cast<uint16_t*>(smem + XBYTES);
   float* const stage = reinterpret_cast<float*>(smem);
+  // F8 layout of the same bytes during the main loop: x_hat codes [BM][XSB],
+  // two U code buffers [BM][USB], x_hat scale words [BM][2] (word h, byte s:
+  // 32-column block 2s + h), two U scale-word buffers [BM][2] (byte t: hidden
+  // block 2t + h of the chunk), the tile's weight scale records [4][24][64]
+  constexpr int XSB = W + 16, USB = HC + 16;
+  uint8_t* const xs8 = smem;
+  uint8_t* const us8 = smem + BM * XSB;
+  uint8_t* const xsc8 = us8 + 2 * BM * USB;
+  uint8_t* const usc8 = xsc8 + BM * 8;
+  uint32_t* const wsc8 = reinterpret_cast<uint32_t*>(usc8 + 2 * BM * 8);
+  static_assert(!F8 || BM * XSB + 2 * BM * USB + 3 * BM * 8 + 4 * MX_REC_DWORDS * 64 * 4 <= SMEM, "F8 LDS");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -306,6 +370,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   // (with `pair` the row group wr computes position p + wr and streams its weights)
   auto bind = [&](const Tile& T) -> Stream {
     const int g = T.group + (pair ? wr : 0);
+    if constexpr (F8)   // one byte per weight: 2 W h gate/up bytes, W h down bytes per position
+      return Stream{reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.wgu) +
+                                                      (size_t)g * 2 * W * a.hidden),
+                    reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.wd) +
+                                                      (size_t)g * W * a.hidden),
+                    T.t % NC};
     return Stream{a.wgu + (size_t)g * NBh * (W / 16) * 2 * FRAG_ELEMS,
                   a.wd + (size_t)g * KBd * (W / 32) * FRAG_ELEMS, T.t % NC};
   };
@@ -359,9 +429,14 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   // needs the longer look-ahead). f1 = fragment f of chunk c in that order:
   // GEMM1 step f / 2 (gate, up), then GEMM2 step (f - F1) / NBO.
   constexpr int NFR = DEPTH * NBR;
-  constexpr int F1 = 2 * S1, F2 = NBO * S2, FS = F1 + F2;
-  static_assert(NW == 8 || (F1 % NFR == 0 && F2 % NFR == 0),
+  // F8: the ring holds NFR8 whole 32-byte fragments (two 1 KiB halves each);
+  // a GEMM1 step (64 K) takes gate and up, a GEMM2 step NBO fragments
+  constexpr int KS8 = W / 64, TS8 = HC / 64, NFR8 = 4;
+  constexpr int F1 = F8 ? 2 * KS8 : 2 * S1, F2 = F8 ? NBO * TS8 : NBO * S2, FS = F1 + F2;
+  constexpr int NFRX = F8 ? NFR8 : NFR;
+  static_assert(NW == 8 || (F1 % NFRX == 0 && F2 % NFRX == 0),
                 "every GEMM phase must start on a ring boundary");
+  i32x8 ring8[F8 ? NFR8 : 1];
   auto fslot = [&](int k) __attribute__((always_inline)) -> uint4& {
     return ring[(k % NFR) / NBR][(k % NFR) % NBR];
   };
@@ -374,6 +449,22 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
       const int kb = c * (HC / 16) + (f - F1) / NBO;
       dst = ldg16(w.d + ((size_t)kb * (W / 32) + wc * NBO + (f - F1) % NBO) * FRAG_ELEMS + lane * 8);
     }
+  };
+
+  // F8 fragment f of chunk c: GEMM1 step f / 2, gate (f even) or up, of
+  // hidden block 4c + wc; then GEMM2 step t = (f - F1) / NBO, column block
+  // wc NBO + (f - F1) % NBO. Both 1 KiB halves in one call.
+  auto issue_frag8 = [&](i32x8& dst, const Stream& w, int c, int f) __attribute__((always_inline)) {
+    c += w.rot;
+    if (c >= NC) c -= NC;
+    const uint8_t* base;
+    if (f < F1) {
+      base = reinterpret_cast<const uint8_t*>(w.gu) + (((size_t)(c * 4 + wc) * KS8 + (f >> 1)) * 2 + (f & 1)) * 2048;
+    } else {
+      const int g = f - F1;
+      base = reinterpret_cast<const uint8_t*>(w.d) + ((size_t)(c * TS8 + g / NBO) * (W / 32) + wc * NBO + g % NBO) * 2048;
+    }
+    dst = join8(*reinterpret_cast<const uint4*>(base + lane * 16), *reinterpret_cast<const uint4*>(base + 1024 + lane * 16));
   };
 
   // ---- row I/O ----------------------------------------------------------------
@@ -441,6 +532,44 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   // of a row before x_hat is written (RMSNorm in fp32, rho to bf16:
   // TokenMixer-Large section 2.3.3)
   auto store_x = [&](int tix, uint4* v, const float* lgain) {
+    if constexpr (F8) {
+      // RMSNorm in fp32, then MXFP8 per 32-column block: the block's 4 units
+      // sit in 4 consecutive lanes of one row (32 units per row)
+      static_assert(!F8 || (LANE_COL && U8 == 32), "F8 row layout");
+#pragma unroll
+      for (int i = 0; i < NPRO; ++i) {
+        int r, c8;
+        unit_rc(tix, i, r, c8);
+        const uint16_t* h = reinterpret_cast<const uint16_t*>(&v[i]);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = bf2f(h[e]);
+          acc += f * f;
+        }
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+        const float rinv = 1.0f / sqrtf(acc / (float)W + a.eps);
+        float n[8], am = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          n[e] = bf2f(h[e]) * rinv * lgain[e];
+          am = fmaxf(am, fabsf(n[e]));
+        }
+        am = fmaxf(am, __shfl_xor(am, 1, 64));
+        am = fmaxf(am, __shfl_xor(am, 2, 64));
+        const int k = mx_exp(am);
+        const float sc = ldexpf(1.f, -k);
+        uint2 q;
+        q.x = e4m3x4(n[0], n[1], n[2], n[3], sc);
+        q.y = e4m3x4(n[4], n[5], n[6], n[7], sc);
+        *reinterpret_cast<uint2*>(&xs8[r * XSB + c8 * 8]) = q;
+        const int blk = c8 >> 2;
+        if ((c8 & 3) == 0) xsc8[r * 8 + (blk & 1) * 4 + (blk >> 1)] = (uint8_t)(k + 127);
+      }
+      __syncthreads();
+      return;
+    }
     constexpr bool kFusedNorm = (U8 <= 64 || U8 % 64 == 0);
     if constexpr (MODE == MLP_DENSE && kFusedNorm) {
       constexpr int LPR = U8 < 64 ? U8 : 64;  // lanes per row within a wave
@@ -528,6 +657,20 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
       __syncthreads();
     }
   };
+  // F8: the tile's weight scale records (24 dwords per lane and wave) go
+  // from global memory straight into LDS (no registers), 16 bytes per lane
+  // and load: dword d of lane l lands at wsc8 + ((wave 6 + d / 4) 64 + l) 4
+  // + d % 4. They share bytes with the epilogue's staged tile, so they are
+  // issued once the staging has been read; the main loop waits for them.
+  auto dma_wrec = [&](const Tile& T) __attribute__((always_inline)) {
+    if constexpr (F8) {
+      const uint4* p = reinterpret_cast<const uint4*>(a.wsc + (((size_t)T.group * 4 + wave) * 64 + lane) * MX_REC_DWORDS);
+#pragma unroll
+      for (int m = 0; m < MX_REC_DWORDS / 4; ++m)
+        __builtin_amdgcn_global_load_lds(p + m, wsc8 + (wave * (MX_REC_DWORDS / 4) + m) * 64 * 4, 16, 0, 0);
+    }
+  };
+
   // residual rows of the tile, same unit order as load_x
   auto load_resid = [&](int tix, int buf, const Tile& T, uint4* rv) {
 #pragma unroll
@@ -602,7 +745,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
     float g[8];
     load_gain(g);
     load_x(tid, 0, cur, v);
-    if constexpr (NW == 4) {
+    dma_wrec(cur);
+    if constexpr (F8) {
+#pragma unroll
+      for (int f = 0; f < NFR8; ++f) issue_frag8(ring8[f], cw, 0, f);
+    } else if constexpr (NW == 4) {
 #pragma unroll
       for (int f = 0; f < NFR; ++f) issue_frag(fslot(f), cw, 0, f);
     } else {
@@ -754,6 +901,172 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
         }
       }
       if (wr == 0) __syncthreads();
+    } else if constexpr (F8) {
+      // MXFP8: the chunk schedule of the 4-wave kernel below (GEMM1(i);
+      // GEMM2(i-1) with U(i) between its MFMAs; barrier) on 32x32x64 scaled
+      // MFMAs. GEMM1 step s reads 64 columns of x_hat codes and the rows'
+      // scale words (byte s), GEMM2 step t 64 hidden units of U codes (byte
+      // t); the weight scales come from the tile's records in LDS.
+      f32x16 sg[RBW], su[RBW];
+      uint32_t xsw[RBW];
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb)
+        xsw[rb] = *reinterpret_cast<const uint32_t*>(&xsc8[(rb * 32 + l32) * 8 + h32 * 4]);
+      const int rot = cw.rot;
+      // the scale records' LDS writes (global_load_lds, counted like loads)
+      __builtin_amdgcn_s_waitcnt(0);
+      auto wscale = [&](int cc, int d) __attribute__((always_inline)) -> uint32_t {
+        cc += rot;
+        if (cc >= NC) cc -= NC;
+        const int dw = cc * 3 + d;
+        return wsc8[((wave * (MX_REC_DWORDS / 4) + (dw >> 2)) * 64 + lane) * 4 + (dw & 3)];
+      };
+      auto read_xb = [&](i32x8* dst, int st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+          const uint8_t* q = xs8 + (rb * 32 + l32) * XSB + st * 64 + 16 * h32;
+          dst[rb] = join8(*reinterpret_cast<const uint4*>(q), *reinterpret_cast<const uint4*>(q + 32));
+        }
+      };
+      auto read_ub = [&](i32x8* dst, int ubuf, int t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+          const uint8_t* q = us8 + ubuf * BM * USB + (rb * 32 + l32) * USB + t * 64 + 16 * h32;
+          dst[rb] = join8(*reinterpret_cast<const uint4*>(q), *reinterpret_cast<const uint4*>(q + 32));
+        }
+      };
+      // U of row block rb: rho_fp8(silu(gate) * up) with one scale per row
+      // and this wave's 32 hidden units (16 in this lane, 16 in lane ^ 32)
+      // in two halves (8 values each, the second also quantises and stores),
+      // so that a GEMM2 step can place MFMAs between them; `am` carries the
+      // running block maximum from the first half to the second
+      auto u_half8 = [&](int ubuf, int rb, int part, float& am) __attribute__((always_inline)) {
+        f32x16& u = sg[rb];   // the gate accumulator is dead once U is formed
+        if (part == 0) am = 0.f;
+#pragma unroll
+        for (int v = 8 * part; v < 8 * part + 8; ++v) {
+          u[v] = silu_fast(u[v]) * su[rb][v];
+          am = fmaxf(am, fabsf(u[v]));
+        }
+        if (part == 0) return;
+        am = fmaxf(am, __shfl_xor(am, 32, 64));
+        const int k = mx_exp(am);
+        const float sc = ldexpf(1.f, -k);
+        uint8_t* row = us8 + ubuf * BM * USB + (rb * 32 + l32) * USB + wc * 32 + 4 * h32;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<uint32_t*>(row + 8 * g4) = e4m3x4(u[4 * g4], u[4 * g4 + 1], u[4 * g4 + 2], u[4 * g4 + 3], sc);
+        if (h32 == 0) usc8[ubuf * BM * 8 + (rb * 32 + l32) * 8 + (wc & 1) * 4 + (wc >> 1)] = (uint8_t)(k + 127);
+      };
+      auto u_group8 = [&](int ubuf, int rb) __attribute__((always_inline)) {
+        float am;
+        u_half8(ubuf, rb, 0, am);
+        __builtin_amdgcn_sched_barrier(0);
+        u_half8(ubuf, rb, 1, am);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto gemm1_8 = [&](auto refill_at, uint32_t gsc, uint32_t usc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < RBW; ++i) {
+          sg[i] = f32x16{};
+          su[i] = f32x16{};
+        }
+        i32x8 xb[2][RBW];
+#pragma unroll
+        for (int st = 0; st < KS8; ++st) {
+          read_xb(xb[st & 1], st);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb) {
+            sg[rb] = mfma8s(st, st, ring8[(2 * st) % NFR8], xb[st & 1][rb], gsc, xsw[rb], sg[rb]);
+            su[rb] = mfma8s(st, st, ring8[(2 * st + 1) % NFR8], xb[st & 1][rb], usc, xsw[rb], su[rb]);
+          }
+          refill_at(ring8[(2 * st) % NFR8], 2 * st + NFR8);
+          refill_at(ring8[(2 * st + 1) % NFR8], 2 * st + 1 + NFR8);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      // GEMM2 of a chunk from U buffer rbuf; with_u: U(next chunk) row block
+      // t goes to buffer wbuf after step t's MFMAs
+      auto gemm2_8 = [&](int rbuf, int wbuf, auto with_u_tag, auto refill_at, auto pos0_tag, uint32_t dsc)
+          __attribute__((always_inline)) {
+        constexpr bool with_u = decltype(with_u_tag)::value;
+        constexpr int pos0 = decltype(pos0_tag)::value;
+        static_assert(RBW == TS8, "one U row block per GEMM2 step");
+        uint32_t usw[RBW];
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb)
+          usw[rb] = *reinterpret_cast<const uint32_t*>(&usc8[rbuf * BM * 8 + (rb * 32 + l32) * 8 + h32 * 4]);
+        i32x8 ub[2][RBW];
+#pragma unroll
+        for (int t = 0; t < TS8; ++t) {
+          read_ub(ub[t & 1], rbuf, t);
+          __builtin_amdgcn_sched_barrier(0);
+          // row block 0's MFMAs, U half 0, row block 1's MFMAs, U half 1
+          float am;
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb) {
+#pragma unroll
+            for (int j = 0; j < NBO; ++j)
+              oacc[rb][j] = mfma8s(j * 2 + t, t, ring8[(pos0 + t * NBO + j) % NFR8], ub[t & 1][rb], dsc, usw[rb],
+                                   oacc[rb][j]);
+            if constexpr (with_u) {
+              u_half8(wbuf, t, rb, am);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < NBO; ++j) refill_at(ring8[(pos0 + t * NBO + j) % NFR8], pos0 + t * NBO + j + NFR8);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      auto chunk_loop8 = [&](auto more_tag) __attribute__((always_inline)) {
+        constexpr bool MORE = decltype(more_tag)::value;
+        gemm1_8([&](i32x8& dst, int k2) __attribute__((always_inline)) {
+                  if (k2 < F1)
+                    issue_frag8(dst, cw, 0, k2);
+                  else if (MORE)
+                    issue_frag8(dst, cw, 1, k2 - F1);
+                  else
+                    issue_frag8(dst, cw, 0, k2);
+                },
+                wscale(0, 0), wscale(0, 1));
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) u_group8(0, rb);
+        __syncthreads();
+        auto iteration = [&](int i, auto last_tag) __attribute__((always_inline)) {
+          constexpr bool LAST = decltype(last_tag)::value;
+          auto refill_at = [&](i32x8& dst, int k2) __attribute__((always_inline)) {
+            if (k2 < F1) {
+              issue_frag8(dst, cw, i, k2);
+            } else if (k2 < FS) {
+              issue_frag8(dst, cw, i - 1, k2);
+            } else if (!LAST) {
+              issue_frag8(dst, cw, i + 1, k2 - FS);
+            } else {
+              issue_frag8(dst, cw, NC - 1, k2 - FS + F1);
+            }
+          };
+          gemm1_8(refill_at, wscale(i, 0), wscale(i, 1));
+          gemm2_8((i - 1) & 1, i & 1, std::true_type{}, refill_at, std::integral_constant<int, F1>{},
+                  wscale(i - 1, 2));
+          __syncthreads();
+        };
+        if constexpr (MORE) {
+          for (int i = 1; i + 1 < NC; ++i) iteration(i, std::integral_constant<bool, false>{});
+          iteration(NC - 1, std::integral_constant<bool, true>{});
+        }
+        gemm2_8((NC - 1) & 1, 0, std::false_type{},
+                [&](i32x8& dst, int k2) __attribute__((always_inline)) {
+                  if (k2 < F2) issue_frag8(dst, cw, NC - 1, F1 + k2);
+                  else issue_frag8(dst, nw, 0, k2 - F2);
+                },
+                std::integral_constant<int, 0>{}, wscale(NC - 1, 2));
+      };
+      if (NC > 1)
+        chunk_loop8(std::true_type{});
+      else
+        chunk_loop8(std::false_type{});
     } else {
       // One wave per SIMD: every wave runs all BM rows, and the VALU work
       // (silu(gate) * up) is software-pipelined against the MFMAs instead of
@@ -1093,6 +1406,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
 #pragma unroll
       for (int i = 0; i < NPRO; ++i) kx[i] = px[i];
     }
+    dma_wrec(nx);
     store_x(etid, px, pg);
     cur = nx;
     buf ^= 1;
@@ -1115,13 +1429,13 @@ void launch_wm(const MlpArgs& a, int grid, hipStream_t s) {
   // in registers up to W = 512)
   constexpr bool MIX_OK = MODE == MLP_DENSE && W <= 512;
   if (MIX_OK && a.map.mix && !a.extra)
-    hipLaunchKernelGGL((mlp_kernel<W, MODE, NW, OCC, MIX_OK ? RV_MIX : RV_PLAIN>), dim3(grid), dim3(64 * NW), 0, s,
-                       a);
+    hipLaunchKernelGGL((mlp_kernel<W, MODE, NW, OCC, MIX_OK ? RV_MIX : RV_PLAIN, false>), dim3(grid), dim3(64 * NW),
+                       0, s, a);
   else if (MODE != MLP_ROUTED && a.extra)
-    hipLaunchKernelGGL((mlp_kernel<W, MODE, NW, OCC, MODE != MLP_ROUTED ? RV_EXTRA : RV_PLAIN>), dim3(grid),
+    hipLaunchKernelGGL((mlp_kernel<W, MODE, NW, OCC, MODE != MLP_ROUTED ? RV_EXTRA : RV_PLAIN, false>), dim3(grid),
                        dim3(64 * NW), 0, s, a);
   else
-    hipLaunchKernelGGL((mlp_kernel<W, MODE, NW, OCC, RV_PLAIN>), dim3(grid), dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((mlp_kernel<W, MODE, NW, OCC, RV_PLAIN, false>), dim3(grid), dim3(64 * NW), 0, s, a);
 }
 
 template <int W>
@@ -1143,6 +1457,21 @@ int mlp_bm(int mode, int W) { return (W <= 256 && mlp_occupancy(mode, W) == 1) ?
 bool mlp_pairs_positions(int mode, int W) { return mode != MLP_ROUTED && mlp_waves(mode, W) == 8; }
 
 int mlp_workgroups_per_cu(int mode, int W) { return mlp_occupancy(mode, W); }
+
+hipError_t launch_mlp_mx(const MlpArgs& a, int tiles, int workers, hipStream_t s) {
+  if (tiles <= 0) return hipSuccess;
+  constexpr int NW = mlp_waves(MLP_DENSE, 256), OCC = mlp_occupancy(MLP_DENSE, 256);
+  static_assert(NW == 4 && OCC == 2, "the MXFP8 kernel is the two-workgroup dense W = 256 kernel");
+  workers = (workers & ~7) * OCC;
+  const int grid = (workers <= 0 || tiles <= workers) ? tiles : workers;
+  // (the Mix sub-layer reads its residual again: with the raw rows kept in
+  // registers as in the bf16 kernel, the MXFP8 main loop would spill)
+  if (a.extra)
+    hipLaunchKernelGGL((mlp_kernel<256, MLP_DENSE, NW, OCC, RV_EXTRA, true>), dim3(grid), dim3(64 * NW), 0, s, a);
+  else
+    hipLaunchKernelGGL((mlp_kernel<256, MLP_DENSE, NW, OCC, RV_PLAIN, true>), dim3(grid), dim3(64 * NW), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_mlp(int mode, int W, const MlpArgs& a, int tiles, int workers, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;

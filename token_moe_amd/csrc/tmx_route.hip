@@ -378,6 +378,71 @@ __global__ void pack_kernel(const uint16_t* __restrict__ src, uint16_t* __restri
   }
 }
 
+// MXFP8 weight packing (load time, layout in tmx_internal.h): one thread per
+// (matrix, column, 32-element K-block). The block's shared exponent is
+// floor(log2(amax)) - 8 (E4M3's largest normal is 1.75 * 2^8), the codes are
+// the hardware's round-to-nearest-even conversion of x * 2^-k after clamping
+// to +-448 (the conversion itself does not saturate).
+__global__ void pack_mx_kernel(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst,
+                               uint8_t* __restrict__ rec, int G, int K, int N, int down, int which) {
+  const int KBLK = K / 32;
+  const int64_t total = (int64_t)G * N * KBLK;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int b = (int)(i % KBLK);
+    const int64_t gn = i / KBLK;
+    const int n = (int)(gn % N);
+    const int g = (int)(gn / N);
+    const uint16_t* col = src + (int64_t)g * K * N + n;
+    float v[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      v[r] = bf2f(col[(int64_t)(b * 32 + r) * N]);
+      amax = fmaxf(amax, fabsf(v[r]));
+    }
+    int e = 0;
+    (void)frexpf(amax, &e);
+    int k = amax > 0.f ? e - 1 - 8 : -127;
+    k = k < -127 ? -127 : (k > 127 ? 127 : k);
+    const int nb = n / 32, h0 = n % 32;
+    const int half = b & 1;   // K-block within the 64-K step
+    int64_t frag;
+    if (!down) {
+      const int KS = K / 64, NB = N / 32;
+      frag = (((int64_t)g * NB + nb) * KS + (b >> 1)) * 2 + which;
+    } else {
+      const int KB = K / 64, NB = N / 32;
+      frag = ((int64_t)g * KB + (b >> 1)) * NB + nb;
+    }
+#pragma unroll
+    for (int r = 0; r < 32; r += 2) {
+      float y0 = ldexpf(v[r], -k), y1 = ldexpf(v[r + 1], -k);
+      y0 = fminf(fmaxf(y0, -448.f), 448.f);
+      y1 = fminf(fmaxf(y1, -448.f), 448.f);
+      const int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+      const int lane = (r / 16) * 32 + h0;
+      uint8_t* d = dst + (frag * 2 + half) * 1024 + lane * 16 + (r % 16);
+      d[0] = (uint8_t)(w & 0xFF);
+      d[1] = (uint8_t)((w >> 8) & 0xFF);
+    }
+    // scale byte in the record of the lane that supplies it to the MFMA
+    // (row h0, K-block parity b & 1 -> lane h0 + 32 (b & 1))
+    const int lane_s = h0 + 32 * (b & 1);
+    int wave, dword, byte;
+    if (!down) {
+      wave = nb % 4;
+      dword = (nb / 4) * 3 + which;
+      byte = b >> 1;
+    } else {
+      wave = nb / 2;
+      dword = (b / 4) * 3 + 2;
+      byte = (nb % 2) * 2 + ((b % 4) >> 1);
+    }
+    rec[((((int64_t)g * 4 + wave) * 64 + lane_s) * MX_REC_DWORDS + dword) * 4 + byte] = (uint8_t)(k + 127);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // permute: Mix (inverse = 0) / Revert (inverse = 1) with the sub-layer
 // kernels' RowMap (TokenMixer-Large Eq. 9-11, 13-15).
@@ -444,6 +509,14 @@ hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int G, int K, int N, 
   const int64_t blocks = std::min<int64_t>((total + 255) / 256, 65536);
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, G, K, N, layout, which,
                      frag == FRAG_32x32x16 ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_mx(const uint16_t* src, uint8_t* dst, uint8_t* rec, int G, int K, int N, int down, int which,
+                          hipStream_t s) {
+  const int64_t total = (int64_t)G * N * (K / 32);
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(pack_mx_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, rec, G, K, N, down, which);
   return hipGetLastError();
 }
 
