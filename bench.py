@@ -22,6 +22,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "block-stack forward samples/s + TFLOP/s (% bf16 MFMA peak), 1×MI355X"
 BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+FP8_PEAK_TFLOPS = 5033.2      # dense fp8 MFMA: twice the bf16 rate
 HBM_PEAK_GBS = 8000.0
 
 
@@ -130,6 +131,8 @@ def main(argv=None):
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--dtype", choices=("bf16", "mxfp8"), default="bf16",
+                    help="mxfp8: the dense workload with MXFP8 GEMM operands (bf16 activations)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -148,6 +151,11 @@ def main(argv=None):
         return 1
     tmx.load_library()
     wl = dg.WORKLOADS[args.workload]
+    if args.dtype == "mxfp8":
+        if wl.moe or wl.dtype != "bf16":
+            print("--dtype mxfp8 applies to the bf16 dense workloads", file=sys.stderr)
+            return 2
+        wl = wl.with_(dtype="mxfp8")
     log("workload", wl)
     t0 = time.perf_counter()
     banks = dg.weight_banks(wl)
@@ -198,9 +206,11 @@ def main(argv=None):
         kms = sum(p[0] for p in per) / len(per)
         kfl = sum(p[1] for p in per) / len(per)
         achieved = kfl / (kms / 1e3) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                    "traffic": measured_traffic(wl.name), "kernel": f"mlp_kernel<{wl.width(1)}, DENSE>",
+        peak = FP8_PEAK_TFLOPS if wl.dtype == "mxfp8" else BF16_PEAK_TFLOPS
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                    "traffic": measured_traffic(wl.name) if wl.dtype == "bf16" else None,
+                    "kernel": f"mlp_kernel<{wl.width(1)}, DENSE{', MXFP8' if wl.dtype == 'mxfp8' else ''}>",
                     "flop_per_launch": kfl, "launch_ms": round(kms, 5)}
         log(f"fused MLP kernel: {kms:.4f} ms/launch, {achieved:.1f} TFLOP/s")
 
@@ -208,8 +218,9 @@ def main(argv=None):
         "metric": METRIC, "value": round(samples_s, 1), "unit": "samples/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "f32", "data": "synthetic",
-        "tflops": round(tflops, 2), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "dtype": {"bf16": "bf16", "mxfp8": "mxfp8"}.get(wl.dtype, "f32"), "data": "synthetic",
+        "tflops": round(tflops, 2),
+        "mfma_frac": round(tflops / (FP8_PEAK_TFLOPS if wl.dtype == "mxfp8" else BF16_PEAK_TFLOPS), 4),
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "D": wl.D, "L": wl.L,
                    "hidden": [wl.hidden_mix, wl.hidden_rev], "E": wl.E, "top_k": wl.top_k,
                    "expert_hidden": wl.expert_hidden, "shared_hidden": wl.shared_hidden,
