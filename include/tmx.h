@@ -125,7 +125,9 @@ const char* tmx_last_error(const tmx_ctx* ctx);
 
 /* Copy one weight bank (kind, layout as above, element type = ctx dtype)
  * of block `layer` (0..L-1), sub-layer `sublayer` (TMX_MIX / TMX_REVERT)
- * into the context and repack it into the kernels' fragment layout.
+ * into the context and repack it into the kernels' fragment layout
+ * (TMX_MXFP8: quantise it to E4M3 with per-32 E8M0 scales along the
+ * contraction axis first).
  * `src` is a host or device pointer (detected with hipPointerGetAttributes);
  * the call copies and the caller keeps ownership.  `nbytes` must equal the
  * bank's exact size.  Dense contexts accept NORM_GAIN, UP, GATE, DOWN; MoE
