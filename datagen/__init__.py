@@ -46,16 +46,27 @@ K_EXP_DOWN = 7
 K_SH_UP = 8
 K_SH_GATE = 9
 K_SH_DOWN = 10
+K_NORM_BIAS = 11     # RankMixer LayerNorm bias
+K_BIAS_UP = 12       # RankMixer per-token FFN first bias  [P, h]
+K_BIAS_DOWN = 13     # RankMixer per-token FFN second bias [P, W]
 
 KIND_NAMES = {
     K_NORM_GAIN: "norm_gain", K_UP: "up", K_GATE: "gate", K_DOWN: "down",
     K_ROUTER: "router", K_EXP_UP: "exp_up", K_EXP_GATE: "exp_gate",
     K_EXP_DOWN: "exp_down", K_SH_UP: "sh_up", K_SH_GATE: "sh_gate",
-    K_SH_DOWN: "sh_down",
+    K_SH_DOWN: "sh_down", K_NORM_BIAS: "norm_bias", K_BIAS_UP: "bias_up",
+    K_BIAS_DOWN: "bias_down",
 }
 
 DENSE_KINDS = (K_UP, K_GATE, K_DOWN)
 MOE_KINDS = (K_ROUTER, K_EXP_UP, K_EXP_GATE, K_EXP_DOWN, K_SH_UP, K_SH_GATE, K_SH_DOWN)
+# RankMixer: the token-mixing sub-layer has only its LayerNorm; the per-token
+# FFN sub-layer holds W1 (K_UP), W2 (K_DOWN) and their biases
+RMX_FFN_KINDS = (K_UP, K_DOWN, K_BIAS_UP, K_BIAS_DOWN)
+NORM_KINDS = (K_NORM_GAIN, K_NORM_BIAS)
+
+BLOCK_TML = "tml"
+BLOCK_RANKMIXER = "rankmixer"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -80,6 +91,8 @@ class Workload:
                              # MXFP8 GEMM operands inside the library)
     seed: int = 0
     down_scale: float = 0.01
+    block: str = BLOCK_TML   # "tml" (TokenMixer-Large) or "rankmixer"
+    random_norm: bool = False  # draw LayerNorm gains / biases instead of 1 / 0
 
     # -- derived -----------------------------------------------------------
     @property
@@ -108,14 +121,28 @@ class Workload:
     def hidden(self, sub: int) -> int:
         return self.hidden_mix if sub == SUB_MIX else self.hidden_rev
 
+    @property
+    def rankmixer(self) -> bool:
+        return self.block == BLOCK_RANKMIXER
+
     def kinds(self):
         return MOE_KINDS if self.moe else DENSE_KINDS
+
+    def sub_kinds(self, sub: int):
+        """Matrix and bias kinds of one sub-layer (norm parameters excluded)."""
+        if self.rankmixer:
+            return RMX_FFN_KINDS if sub == SUB_REVERT else ()
+        return self.kinds()
 
     def kind_shape(self, sub: int, kind: int) -> Tuple[int, ...]:
         """Logical row-major shape of one (sub-layer, kind) bank, all positions."""
         P, W = self.positions(sub), self.width(sub)
-        if kind == K_NORM_GAIN:
+        if kind in NORM_KINDS:
             return (W,)
+        if kind == K_BIAS_UP:
+            return (P, self.hidden(sub))
+        if kind == K_BIAS_DOWN:
+            return (P, W)
         if kind in (K_UP, K_GATE):
             return (P, W, self.hidden(sub))
         if kind == K_DOWN:
@@ -133,7 +160,7 @@ class Workload:
         raise ValueError(f"unknown kind {kind}")
 
     def fan_in(self, sub: int, kind: int) -> int:
-        if kind == K_DOWN:
+        if kind in (K_DOWN, K_BIAS_DOWN):
             return self.hidden(sub)
         if kind == K_EXP_DOWN:
             return self.expert_hidden
@@ -160,6 +187,21 @@ WORKLOADS: Dict[int, Workload] = {
     5: Workload("large_moe_15b", B=8192, T=32, H=32, D=768, L=8, E=32,
                 top_k=4, expert_hidden=384, shared_hidden=768, alpha=8.0,
                 gap=2, seed=4),
+}
+
+
+# RankMixer block stacks (the fun-rec chapter 7.4.0 block equations, H = T
+# as the reproduction guide's section 5 requires; per-token FFN hidden
+# kD = 4D as the guide's W1 [T, D, kD] with k = 4). Standard N(0, 1/fan_in)
+# init for both FFN matrices (post-LN blocks have no small-down init) and
+# LayerNorm eps 1e-5.
+RANKMIXER_WORKLOADS: Dict[str, Workload] = {
+    "rankmixer_d256": Workload("rankmixer_d256", B=4096, T=16, H=16, D=256, L=4,
+                               hidden_rev=1024, gap=0, eps=1e-5, seed=11,
+                               down_scale=1.0, block=BLOCK_RANKMIXER),
+    "rankmixer_d512": Workload("rankmixer_d512", B=4096, T=16, H=16, D=512, L=4,
+                               hidden_rev=2048, gap=0, eps=1e-5, seed=12,
+                               down_scale=1.0, block=BLOCK_RANKMIXER),
 }
 
 
@@ -214,18 +256,31 @@ def _draw(cfg: Workload, layer: int, sub: int, kind: int, p: int, seed: Optional
     return a
 
 
+def _norm_param(cfg: Workload, layer: int, sub: int, kind: int, seed: Optional[int]) -> np.ndarray:
+    """Norm gain (1) or bias (0); with ``random_norm`` gain 1 + 0.1 N(0, 1) and
+    bias 0.1 N(0, 1), drawn under the weight key of position 0."""
+    W = cfg.width(sub)
+    if not cfg.random_norm:
+        return (np.ones if kind == K_NORM_GAIN else np.zeros)(W, np.float32)
+    s = cfg.seed if seed is None else seed
+    a = _rng(s, (1, layer, sub, kind, 0)).standard_normal(W, dtype=np.float32) * np.float32(0.1)
+    if kind == K_NORM_GAIN:
+        a += np.float32(1.0)
+    return _finish(cfg, a)
+
+
 def weight_slice(cfg: Workload, layer: int, sub: int, kind: int, p: int,
                  seed: Optional[int] = None) -> np.ndarray:
     """One position's slice of a weight bank (fp32 array, dtype-representable)."""
-    if kind == K_NORM_GAIN:
-        return np.ones(cfg.kind_shape(sub, kind), np.float32)
+    if kind in NORM_KINDS:
+        return _norm_param(cfg, layer, sub, kind, seed)
     return _finish(cfg, _draw(cfg, layer, sub, kind, p, seed))
 
 
 def weight_bank(cfg: Workload, layer: int, sub: int, kind: int,
                 seed: Optional[int] = None) -> np.ndarray:
     """A whole (layer, sub-layer, kind) bank, all positions stacked (fp32 values)."""
-    if kind == K_NORM_GAIN:
+    if kind in NORM_KINDS:
         return weight_slice(cfg, layer, sub, kind, 0, seed)
     return np.stack([weight_slice(cfg, layer, sub, kind, p, seed) for p in range(cfg.positions(sub))])
 
@@ -251,7 +306,11 @@ def weight_banks(cfg: Workload, seed: Optional[int] = None, workers: int = 0):
     jobs = []
     for l in range(1, cfg.L + 1):
         for s in (SUB_MIX, SUB_REVERT):
-            for k in cfg.kinds():
+            if cfg.random_norm:
+                for k in NORM_KINDS if cfg.rankmixer else (K_NORM_GAIN,):
+                    v = _norm_param(cfg, l, s, k, seed)
+                    banks[(l, s, k)] = f32_to_bf16_bits(v) if bf16 else v
+            for k in cfg.sub_kinds(s):
                 shape = cfg.kind_shape(s, k)
                 arr = np.empty(shape, np.uint16 if bf16 else np.float32)
                 banks[(l, s, k)] = arr
@@ -273,10 +332,10 @@ def weight_banks(cfg: Workload, seed: Optional[int] = None, workers: int = 0):
 
 
 def param_count(cfg: Workload) -> int:
-    """Number of weight values of the stack (norm gains excluded)."""
+    """Number of weight and bias values of the stack (norm parameters excluded)."""
     total = 0
     for sub in (SUB_MIX, SUB_REVERT):
-        for kind in cfg.kinds():
+        for kind in cfg.sub_kinds(sub):
             total += int(np.prod(cfg.kind_shape(sub, kind)))
     return total * cfg.L
 
@@ -291,7 +350,10 @@ class WeightSource:
         self.seed = seed
 
     def __call__(self, layer: int, sub: int, kind: int, p: int) -> np.ndarray:
-        if kind == K_NORM_GAIN:
+        if kind in NORM_KINDS:
+            if self.banks is not None and (layer, sub, kind) in self.banks:
+                b = self.banks[(layer, sub, kind)]
+                return bf16_bits_to_f32(b) if b.dtype == np.uint16 else b
             return weight_slice(self.cfg, layer, sub, kind, p, self.seed)
         if self.banks is not None and (layer, sub, kind) in self.banks:
             b = self.banks[(layer, sub, kind)][p]

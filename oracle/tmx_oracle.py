@@ -40,6 +40,8 @@ __all__ = [
     "flops_per_sample", "param_count_closed_form",
     "E4M3_MAX", "MX_BLOCK", "e4m3_value", "e4m3_round", "mx_exponent", "mx_quantize",
     "mx_dequantize", "mx_round", "swiglu_mx",
+    "layernorm", "gelu", "pffn", "rankmixer_block", "rankmixer_ffn_sublayer", "rankmixer_stack",
+    "rankmixer_flops_per_sample",
 ]
 
 BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
@@ -416,3 +418,111 @@ def flops_per_sample(cfg) -> int:
             total += 2 * P * (3 * cfg.top_k * W * cfg.expert_hidden
                               + 3 * W * cfg.shared_hidden + W * cfg.E)
     return cfg.L * total
+
+
+# ---------------------------------------------------------------------------
+# RankMixer block   [RMX-BOOK] 7.4.0 block equations, 7.4.1, 7.4.2;
+# [RMX-GUIDE] sections 5, 6.1 and 7; the RankMixer README's per-token FFN
+#
+# Readings (the pages leave these open):
+# * LN is LayerNorm over the token width: subtract the row mean, divide by
+#   sqrt(biased variance + eps), then gain and bias ([RMX-GUIDE] 7 names the
+#   residual + LN of the block; the chapter's block equations use LN).
+# * GELU is the exact form z * Phi(z) with Phi the standard normal CDF (the
+#   pages write GELU without an approximation).
+# * Post-LN as the chapter's block equations write it ([RMX-GUIDE] 7 allows
+#   pre or post; the equations fix post).
+# * bf16 precision contract, as for TokenMixer-Large: inputs, weights,
+#   biases and norm parameters are bf16 values; S (the FFN input and its
+#   residual), the hidden GELU output and the block output are rounded to
+#   bf16 once each; LN statistics, the GEMM accumulations, the biases' and
+#   residual's additions stay unrounded.
+# ---------------------------------------------------------------------------
+
+_K_NBIAS, _K_BUP, _K_BDOWN = 11, 12, 13
+
+
+def layernorm(v: np.ndarray, gamma: Optional[np.ndarray], beta: Optional[np.ndarray],
+              eps: float) -> np.ndarray:
+    """LayerNorm over the last axis: (v - mean) / sqrt(var + eps) * gamma + beta,
+    var the biased (1/n) variance."""
+    v = np.asarray(v, dtype=np.float64)
+    mu = np.mean(v, axis=-1, keepdims=True)
+    d = v - mu
+    var = np.mean(d * d, axis=-1, keepdims=True)
+    out = d / np.sqrt(var + eps)
+    if gamma is not None:
+        out = out * np.asarray(gamma, dtype=np.float64)
+    if beta is not None:
+        out = out + np.asarray(beta, dtype=np.float64)
+    return out
+
+
+def gelu(z: np.ndarray) -> np.ndarray:
+    """Exact GELU: z * Phi(z), Phi(z) = (1 + erf(z / sqrt 2)) / 2."""
+    z = np.asarray(z, dtype=np.float64)
+    erf = np.vectorize(math.erf, otypes=[np.float64])
+    return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+
+
+def pffn(s: np.ndarray, w1: np.ndarray, b1: np.ndarray, w2: np.ndarray, b2: np.ndarray,
+         rho: bool = False) -> np.ndarray:
+    """One token's own FFN ([RMX-BOOK] 7.4.2; the RankMixer README's per-token
+    FFN): v = GELU(s W1 + b1) W2 + b2, row-vector convention with W1 [D, kD],
+    W2 [kD, D] ([RMX-GUIDE] 6.1). In bf16 mode the hidden is rounded to bf16
+    before the second matrix."""
+    s = np.asarray(s, dtype=np.float64)
+    hid = _rho(gelu(s @ np.asarray(w1, dtype=np.float64) + np.asarray(b1, dtype=np.float64)), rho)
+    return hid @ np.asarray(w2, dtype=np.float64) + np.asarray(b2, dtype=np.float64)
+
+
+def rankmixer_block(X: np.ndarray, cfg, layer: int, weights: WeightGetter,
+                    rho: bool = False, trace: Optional[dict] = None) -> np.ndarray:
+    """One RankMixer block ([RMX-BOOK] 7.4.0):
+        S      = LN_1(TokenMixing(X) + X)
+        X_next = LN_2(PFFN(S) + S)
+    TokenMixing is the parameter-free head split and cross-token concat
+    ([RMX-BOOK] 7.4.1) with H = T ([RMX-GUIDE] 5), so its output has the
+    shape of X and the residual adds token by token. PFFN applies token t's
+    own FFN to S[:, t]. LN_1 belongs to sub-layer 0, the FFN and LN_2 to
+    sub-layer 1. ``trace`` (optional dict) receives S under (layer, 'S')."""
+    B, T, D = X.shape
+    if cfg.H != T:
+        raise ValueError("RankMixer token mixing needs H == T")
+    X = np.asarray(X, dtype=np.float64)
+    S = _rho(layernorm(mix(X, cfg.H) + X, weights(layer, 0, _K_GAIN, 0),
+                       weights(layer, 0, _K_NBIAS, 0), cfg.eps), rho)
+    if trace is not None:
+        trace[(layer, "S")] = S
+    return rankmixer_ffn_sublayer(S, cfg, layer, weights, rho)
+
+
+def rankmixer_ffn_sublayer(S: np.ndarray, cfg, layer: int, weights: WeightGetter,
+                           rho: bool = False) -> np.ndarray:
+    """Second half of a RankMixer block: X_next[:, t] = LN_2(S[:, t] + PFFN_t(S[:, t]))."""
+    S = np.asarray(S, dtype=np.float64)
+    out = np.empty_like(S)
+    g2, b2n = weights(layer, 1, _K_GAIN, 0), weights(layer, 1, _K_NBIAS, 0)
+    for t in range(S.shape[1]):
+        v = pffn(S[:, t], weights(layer, 1, _K_UP, t), weights(layer, 1, _K_BUP, t),
+                 weights(layer, 1, _K_DOWN, t), weights(layer, 1, _K_BDOWN, t), rho)
+        out[:, t] = layernorm(S[:, t] + v, g2, b2n, cfg.eps)
+    return _rho(out, rho)
+
+
+def rankmixer_stack(X: np.ndarray, cfg, weights: WeightGetter, rho: Optional[bool] = None,
+                    trace: Optional[dict] = None) -> np.ndarray:
+    """L stacked RankMixer blocks ([RMX-BOOK] 7.4.0: X_n from X_{n-1}); no
+    inter-residual. ``rho`` defaults to the workload being bf16."""
+    if rho is None:
+        rho = cfg.dtype == "bf16"
+    Y = np.asarray(X, dtype=np.float64)
+    for l in range(1, cfg.L + 1):
+        Y = rankmixer_block(Y, cfg, l, weights, rho, trace)
+    return Y
+
+
+def rankmixer_flops_per_sample(cfg) -> int:
+    """GEMM FLOPs of one sample: per block and token 2 * (D kD + kD D)
+    ([RMX-BOOK] 7.4.2: 2TkD^2 multiply-adds per block)."""
+    return cfg.L * cfg.T * 2 * 2 * cfg.D * cfg.hidden_rev
