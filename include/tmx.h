@@ -30,6 +30,20 @@
  *    the failure.
  *  - A context is used by one host thread at a time.
  *  - Layers are numbered 0..L-1 (layer l here is the pages' block l+1).
+ *
+ * A context can instead hold a stack of RankMixer blocks (cfg.block =
+ * TMX_BLOCK_RANKMIXER; fun-rec chapter 7.4.0 block equations, 7.4.1 token
+ * mixing, 7.4.2 per-token FFN; the RankMixer reproduction README's per-token
+ * FFN with biases), post-LN, no inter-residual:
+ *
+ *   for l = 1..L:   S   = LN_1(TokenMixing(X) + X)          (H = T, so the
+ *                                                            mixed tensor has
+ *                                                            the shape of X)
+ *                   X   = LN_2(S + PFFN(S)),  PFFN_t(s) = GELU(s W1_t + b1_t) W2_t + b2_t
+ *
+ * LN is LayerNorm (biased variance, eps = cfg.eps, gain and bias), GELU the
+ * exact erf form.  Sub-layer 0 (TMX_MIX) is the token-mixing half, sub-layer
+ * 1 (TMX_REVERT) the FFN half; S is rounded to the ctx dtype once.
  */
 #ifndef TMX_H
 #define TMX_H
@@ -61,6 +75,9 @@ typedef enum tmx_dtype { TMX_F32 = 0, TMX_BF16 = 1, TMX_MXFP8 = 2 } tmx_dtype;
 
 typedef enum tmx_sublayer { TMX_MIX = 0, TMX_REVERT = 1 } tmx_sublayer;
 
+/* Block family of a context. */
+typedef enum tmx_block { TMX_BLOCK_TOKENMIXER_LARGE = 0, TMX_BLOCK_RANKMIXER = 1 } tmx_block;
+
 /* Weight kinds and their logical row-major layouts, with P and W of the
  * sub-layer (MIX: P = H, W = T*D/H; REVERT: P = T, W = D), h the dense
  * hidden of that sub-layer, E routed experts, h_e expert hidden, h_s
@@ -77,7 +94,14 @@ typedef enum tmx_weight_kind {
   TMX_W_EXP_DOWN = 7,  /* [P, E, h_e, W]                                   */
   TMX_W_SH_UP = 8,     /* [P, W, h_s]  per-token shared expert (Eq. 20)    */
   TMX_W_SH_GATE = 9,   /* [P, W, h_s]                                      */
-  TMX_W_SH_DOWN = 10   /* [P, h_s, W]                                      */
+  TMX_W_SH_DOWN = 10,  /* [P, h_s, W]                                      */
+  /* RankMixer contexts (P = T, W = D, h = hidden_rev): NORM_GAIN and
+   * NORM_BIAS are LN_1's (sub-layer 0) or LN_2's (sub-layer 1); UP is W1
+   * [T, D, h], DOWN is W2 [T, h, D] (sub-layer 1).  Gains default to 1,
+   * biases to 0. */
+  TMX_W_NORM_BIAS = 11, /* [W]          LayerNorm bias, optional            */
+  TMX_W_BIAS_UP = 12,   /* [P, h]       b1 of the per-token FFN, optional   */
+  TMX_W_BIAS_DOWN = 13  /* [P, W]       b2 of the per-token FFN, optional   */
 } tmx_weight_kind;
 
 /* Model configuration; the pages' problem statement (B, T, H, D, hidden, E,
@@ -97,9 +121,10 @@ typedef struct tmx_config {
   int32_t expert_hidden;  /* h_e                                               */
   int32_t shared_hidden;  /* h_s                                               */
   float alpha;            /* gate-value scaling (Eq. 21); 0 means E / top_k    */
-  float eps;              /* RMSNorm epsilon (> 0)                             */
+  float eps;              /* RMSNorm (LayerNorm for RankMixer) epsilon (> 0)   */
   int32_t inter_residual_gap; /* g (section 2.3.4); 0 disables               */
   int32_t dtype;          /* tmx_dtype of activations and weights              */
+  int32_t block;          /* tmx_block (0 = TokenMixer-Large)                  */
 } tmx_config;
 
 typedef struct tmx_ctx tmx_ctx;
@@ -111,6 +136,12 @@ typedef struct tmx_ctx tmx_ctx;
  * size a multiple of 128; MoE contexts in bf16 need E % 16 == 0, E <= 64,
  * top_k <= 8 and B_max*T*D < 2^31 (the normalised-row workspace is
  * addressed with 32-bit byte offsets); TMX_ERR_UNSUPPORTED otherwise.
+ * RankMixer contexts need H == T (the paper-strict token mixing; the
+ * reproduction guide's section 5 makes any other H an error), hidden_mix ==
+ * 0, inter_residual_gap == 0 and hidden_rev >= 1 (TMX_ERR_INVALID_ARG
+ * otherwise), and this build runs them dense (E = 0), in bf16, with D of
+ * 256 or 512, D/H % 8 == 0 and hidden_rev % 128 == 0
+ * (TMX_ERR_UNSUPPORTED otherwise).
  * On error *out is set to NULL and nothing stays allocated. */
 tmx_status tmx_create(const tmx_config* cfg, int device, tmx_ctx** out);
 
@@ -131,7 +162,9 @@ const char* tmx_last_error(const tmx_ctx* ctx);
  * `src` is a host or device pointer (detected with hipPointerGetAttributes);
  * the call copies and the caller keeps ownership.  `nbytes` must equal the
  * bank's exact size.  Dense contexts accept NORM_GAIN, UP, GATE, DOWN; MoE
- * contexts NORM_GAIN, ROUTER and the EXP_* / SH_* kinds.  The call is
+ * contexts NORM_GAIN, ROUTER and the EXP_* / SH_* kinds; RankMixer contexts
+ * NORM_GAIN and NORM_BIAS in both sub-layers and UP, DOWN, BIAS_UP,
+ * BIAS_DOWN in sub-layer 1 (UP and DOWN are required).  The call is
  * synchronous (it waits for `stream`); it is not meant for timed loops. */
 tmx_status tmx_load_weights(tmx_ctx* ctx, int layer, int sublayer, int kind,
                             const void* src, size_t nbytes, void* stream);
@@ -159,6 +192,9 @@ tmx_status tmx_moe_route(tmx_ctx* ctx, int layer, int sublayer, const void* x,
  *   TMX_REVERT: x_out = resid + F_rev(RMSNorm(x_in)) [+ extra];
  *               `resid` is the block input, `extra` (nullable) the
  *               inter-residual term.
+ * RankMixer contexts (`resid` and `extra` must be NULL):
+ *   TMX_MIX:    x_out = S = LN_1(TokenMixing(x_in) + x_in);
+ *   TMX_REVERT: x_out = LN_2(x_in + PFFN(x_in)), x_in being S.
  * The result is rounded once to the ctx dtype.  A chain of these calls
  * reproduces tmx_block_stack_forward bit for bit. */
 tmx_status tmx_sublayer_forward(tmx_ctx* ctx, int layer, int sublayer,

@@ -79,7 +79,10 @@ def test_status_and_enum_values_match_header(tmx):
                       ("TMX_W_EXP_GATE", dg.K_EXP_GATE), ("TMX_W_EXP_DOWN", dg.K_EXP_DOWN),
                       ("TMX_W_SH_UP", dg.K_SH_UP), ("TMX_W_SH_GATE", dg.K_SH_GATE),
                       ("TMX_W_SH_DOWN", dg.K_SH_DOWN), ("TMX_MIX", 0), ("TMX_REVERT", 1),
-                      ("TMX_F32", 0), ("TMX_BF16", 1), ("TMX_MXFP8", 2)]:
+                      ("TMX_F32", 0), ("TMX_BF16", 1), ("TMX_MXFP8", 2),
+                      ("TMX_W_NORM_BIAS", dg.K_NORM_BIAS), ("TMX_W_BIAS_UP", dg.K_BIAS_UP),
+                      ("TMX_W_BIAS_DOWN", dg.K_BIAS_DOWN), ("TMX_BLOCK_TOKENMIXER_LARGE", 0),
+                      ("TMX_BLOCK_RANKMIXER", tmx.TMX_BLOCK_RANKMIXER)]:
         m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
         assert m and int(m.group(1)) == val, name
 
@@ -119,6 +122,19 @@ def _create(tmx, **kw):
     (dict(dtype=2, D=256, H=16, T=16, hidden_mix=2048, hidden_rev=256), "UNSUPPORTED"),
     (dict(dtype=2, D=256, H=16, T=16, E=16, top_k=4, expert_hidden=256, shared_hidden=512), "UNSUPPORTED"),
     (dict(dtype=3), "INVALID_ARG"),
+    (dict(block=2), "INVALID_ARG"),
+    # RankMixer: H == T, no mix hidden, no inter-residual; bf16 dense, D 256 / 512
+    (dict(block=1, dtype=1, D=256, H=8, T=16, hidden_mix=0, hidden_rev=1024, inter_residual_gap=0), "INVALID_ARG"),
+    (dict(block=1, dtype=1, D=256, H=16, T=16, hidden_mix=1024, hidden_rev=1024, inter_residual_gap=0),
+     "INVALID_ARG"),
+    (dict(block=1, dtype=1, D=256, H=16, T=16, hidden_mix=0, hidden_rev=1024, inter_residual_gap=2), "INVALID_ARG"),
+    (dict(block=1, dtype=1, D=256, H=16, T=16, hidden_mix=0, hidden_rev=0, inter_residual_gap=0), "INVALID_ARG"),
+    (dict(block=1, dtype=0, D=256, H=16, T=16, hidden_mix=0, hidden_rev=1024, inter_residual_gap=0), "UNSUPPORTED"),
+    (dict(block=1, dtype=1, D=128, H=16, T=16, hidden_mix=0, hidden_rev=1024, inter_residual_gap=0), "UNSUPPORTED"),
+    (dict(block=1, dtype=1, D=256, H=64, T=64, hidden_mix=0, hidden_rev=1024, inter_residual_gap=0), "UNSUPPORTED"),
+    (dict(block=1, dtype=1, D=256, H=16, T=16, hidden_mix=0, hidden_rev=1000, inter_residual_gap=0), "UNSUPPORTED"),
+    (dict(block=1, dtype=1, D=256, H=16, T=16, hidden_mix=0, hidden_rev=1024, inter_residual_gap=0, E=16, top_k=4,
+          expert_hidden=256, shared_hidden=256), "UNSUPPORTED"),
     # x_hat workspace (B_max*T*D bf16) must stay under 4 GiB
     (dict(dtype=1, B_max=1 << 21, D=512, H=16, T=16, E=16, top_k=4, expert_hidden=256, shared_hidden=512),
      "UNSUPPORTED"),

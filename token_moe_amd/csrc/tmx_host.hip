@@ -16,7 +16,7 @@ using namespace tmx;
 
 namespace {
 
-constexpr int NKINDS = 11;
+constexpr int NKINDS = 14;
 thread_local std::string g_create_error;
 
 struct Bank {
@@ -70,6 +70,10 @@ int positions(const tmx_config& c, int sub) { return sub == TMX_MIX ? c.H : c.T;
 int width(const tmx_config& c, int sub) { return sub == TMX_MIX ? c.T * (c.D / c.H) : c.D; }
 int dense_hidden(const tmx_config& c, int sub) { return sub == TMX_MIX ? c.hidden_mix : c.hidden_rev; }
 bool is_moe(const tmx_config& c) { return c.E > 0; }
+bool is_rmx(const tmx_config& c) { return c.block == TMX_BLOCK_RANKMIXER; }
+bool is_norm(int kind) { return kind == TMX_W_NORM_GAIN || kind == TMX_W_NORM_BIAS; }
+// kinds a context may go without: gains default to 1, biases to 0
+bool optional_kind(int kind) { return is_norm(kind) || kind == TMX_W_BIAS_UP || kind == TMX_W_BIAS_DOWN; }
 
 // logical [G, K, N] view of a matrix bank; returns false for non-matrix kinds
 bool bank_dims(const tmx_config& c, int sub, int kind, int64_t* G, int* K, int* N) {
@@ -86,14 +90,21 @@ bool bank_dims(const tmx_config& c, int sub, int kind, int64_t* G, int* K, int* 
   }
 }
 
-bool kind_applies(const tmx_config& c, int kind) {
+bool kind_applies(const tmx_config& c, int sub, int kind) {
+  if (is_rmx(c)) {
+    if (is_norm(kind)) return true;
+    return sub == TMX_REVERT && (kind == TMX_W_UP || kind == TMX_W_DOWN || kind == TMX_W_BIAS_UP ||
+                                 kind == TMX_W_BIAS_DOWN);
+  }
   if (kind == TMX_W_NORM_GAIN) return true;
   if (is_moe(c)) return kind >= TMX_W_ROUTER && kind <= TMX_W_SH_DOWN;
   return kind >= TMX_W_UP && kind <= TMX_W_DOWN;
 }
 
 size_t kind_elems(const tmx_config& c, int sub, int kind) {
-  if (kind == TMX_W_NORM_GAIN) return (size_t)width(c, sub);
+  if (is_norm(kind)) return (size_t)width(c, sub);
+  if (kind == TMX_W_BIAS_UP) return (size_t)positions(c, sub) * dense_hidden(c, sub);
+  if (kind == TMX_W_BIAS_DOWN) return (size_t)positions(c, sub) * width(c, sub);
   int64_t G;
   int K, N;
   if (!bank_dims(c, sub, kind, &G, &K, &N)) return 0;
@@ -106,7 +117,7 @@ Bank& bank(tmx_ctx* c, int layer, int sub, int kind) {
 
 // storage of a bank: gate and up share one interleaved fragment buffer in bf16
 Bank& storage(tmx_ctx* c, int layer, int sub, int kind) {
-  if (c->cfg.dtype != TMX_F32) {
+  if (c->cfg.dtype != TMX_F32 && !is_rmx(c->cfg)) {
     if (kind == TMX_W_UP) kind = TMX_W_GATE;
     if (kind == TMX_W_EXP_UP) kind = TMX_W_EXP_GATE;
     if (kind == TMX_W_SH_UP) kind = TMX_W_SH_GATE;
@@ -164,6 +175,26 @@ tmx_status validate_config(const tmx_config* cfg) {
   if (!(c.eps > 0.f)) return fail(nullptr, TMX_ERR_INVALID_ARG, "eps must be > 0");
   if (c.inter_residual_gap < 0) return fail(nullptr, TMX_ERR_INVALID_ARG, "inter_residual_gap must be >= 0");
   if (c.E < 0) return fail(nullptr, TMX_ERR_INVALID_ARG, "E must be >= 0");
+  if (c.block != TMX_BLOCK_TOKENMIXER_LARGE && c.block != TMX_BLOCK_RANKMIXER)
+    return fail(nullptr, TMX_ERR_INVALID_ARG, "block must be 0 (TokenMixer-Large) or 1 (RankMixer), got %d", c.block);
+  if (is_rmx(c)) {
+    if (c.H != c.T)
+      return fail(nullptr, TMX_ERR_INVALID_ARG, "RankMixer token mixing needs H == T (got H %d, T %d)", c.H, c.T);
+    if (c.hidden_mix != 0 || c.inter_residual_gap != 0)
+      return fail(nullptr, TMX_ERR_INVALID_ARG, "RankMixer blocks take hidden_mix = 0 and inter_residual_gap = 0");
+    if (c.hidden_rev < 1) return fail(nullptr, TMX_ERR_INVALID_ARG, "RankMixer needs hidden_rev (kD) >= 1");
+    if (c.E != 0) return fail(nullptr, TMX_ERR_UNSUPPORTED, "RankMixer blocks run dense (E = 0) in this build");
+    if (c.dtype != TMX_BF16) return fail(nullptr, TMX_ERR_UNSUPPORTED, "RankMixer blocks run in bf16 in this build");
+    if (!rmx_width_supported(c.D))
+      return fail(nullptr, TMX_ERR_UNSUPPORTED, "RankMixer path supports D = 256 or 512, got %d", c.D);
+    if ((c.D / c.H) % 8 != 0)
+      return fail(nullptr, TMX_ERR_UNSUPPORTED, "RankMixer path needs D/H %% 8 == 0, got %d", c.D / c.H);
+    if (c.hidden_rev % 128 != 0)
+      return fail(nullptr, TMX_ERR_UNSUPPORTED, "RankMixer path needs hidden_rev %% 128 == 0, got %d", c.hidden_rev);
+    if ((int64_t)c.B_max * c.T * c.D > (int64_t)1 << 40)
+      return fail(nullptr, TMX_ERR_INVALID_ARG, "B_max*T*D too large");
+    return TMX_OK;
+  }
   if (c.E == 0) {
     if (c.hidden_mix < 1 || c.hidden_rev < 1)
       return fail(nullptr, TMX_ERR_INVALID_ARG, "dense config needs hidden_mix, hidden_rev >= 1");
@@ -216,8 +247,8 @@ int moe_max_tiles(const tmx_config& c, int sub, int B) {
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 bool sublayer_ready(tmx_ctx* c, int layer, int sub) {
-  for (int k = 1; k < NKINDS; ++k)
-    if (kind_applies(c->cfg, k) && !bank(c, layer, sub, k).loaded) return false;
+  for (int k = 0; k < NKINDS; ++k)
+    if (kind_applies(c->cfg, sub, k) && !bank(c, layer, sub, k).loaded) return false;
   return true;
 }
 
@@ -243,6 +274,22 @@ void set_row_tiles(MlpArgs& a, int mode, int sub, int W, int P, int B, int dh_by
   // (runs shorter than a 128-byte line only)
   const int ppx = (P % 8 == 0) ? P / 8 : P;   // positions per tile range of an XCD
   a.ileave = (sub == TMX_MIX && !a.pair && ppx % 2 == 0 && dh_bytes < 128) ? 1 : 0;
+}
+
+// RankMixer: part 0 = the token-mixing half (S), 1 = the FFN half from S,
+// 2 = the whole block in one kernel
+tmx_status run_rmx(tmx_ctx* c, int layer, int part, const void* x_in, void* x_out, int B, hipStream_t st) {
+  const tmx_config& cfg = c->cfg;
+  RmxArgs a{};
+  a.B = B; a.T = cfg.T; a.D = cfg.D; a.dh = cfg.D / cfg.H; a.hidden = cfg.hidden_rev; a.eps = cfg.eps;
+  a.x = static_cast<const uint16_t*>(x_in);
+  a.out = static_cast<uint16_t*>(x_out);
+  auto f = [&](int sub, int k) { return static_cast<const float*>(bank(c, layer, sub, k).ptr); };
+  auto h = [&](int k) { return static_cast<const uint16_t*>(bank(c, layer, TMX_REVERT, k).ptr); };
+  a.g1 = f(TMX_MIX, TMX_W_NORM_GAIN); a.be1 = f(TMX_MIX, TMX_W_NORM_BIAS);
+  a.g2 = f(TMX_REVERT, TMX_W_NORM_GAIN); a.be2 = f(TMX_REVERT, TMX_W_NORM_BIAS);
+  a.w1 = h(TMX_W_UP); a.w2 = h(TMX_W_DOWN); a.b1 = h(TMX_W_BIAS_UP); a.b2 = h(TMX_W_BIAS_DOWN);
+  return check_launch(c, launch_rmx(a, part, st), "RankMixer launch");
 }
 
 tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const void* resid, const void* extra,
@@ -398,16 +445,29 @@ tmx_status tmx_create(const tmx_config* cfg, int device, tmx_ctx** out) {
   for (int l = 0; l < C.L; ++l)
     for (int sub = 0; sub < 2; ++sub)
       for (int k = 0; k < NKINDS; ++k) {
-        if (!kind_applies(C, k)) continue;
+        if (!kind_applies(C, sub, k)) continue;
         Bank& b = bank(c, l, sub, k);
         b.elems = kind_elems(C, sub, k);
-        if (k == TMX_W_NORM_GAIN) {
-          s = dev_alloc(c, &b.ptr, b.elems * sizeof(float), "norm gain");
+        if (is_norm(k)) {
+          s = dev_alloc(c, &b.ptr, b.elems * sizeof(float), "norm parameters");
           if (s != TMX_OK) return bail(s);
-          std::vector<float> ones(b.elems, 1.0f);
-          if ((e = hipMemcpy(b.ptr, ones.data(), b.elems * sizeof(float), hipMemcpyHostToDevice)) != hipSuccess)
-            return bail(fail(c, TMX_ERR_DEVICE, "gain init: %s", hipGetErrorString(e)));
+          std::vector<float> init(b.elems, k == TMX_W_NORM_GAIN ? 1.0f : 0.0f);
+          if ((e = hipMemcpy(b.ptr, init.data(), b.elems * sizeof(float), hipMemcpyHostToDevice)) != hipSuccess)
+            return bail(fail(c, TMX_ERR_DEVICE, "norm init: %s", hipGetErrorString(e)));
           b.loaded = true;
+          continue;
+        }
+        if (k == TMX_W_BIAS_UP || k == TMX_W_BIAS_DOWN) {
+          s = dev_alloc(c, &b.ptr, b.elems * es, "biases");
+          if (s != TMX_OK) return bail(s);
+          std::vector<uint16_t> zero(b.elems, 0);   // bf16 +0
+          if ((e = hipMemcpy(b.ptr, zero.data(), b.elems * es, hipMemcpyHostToDevice)) != hipSuccess)
+            return bail(fail(c, TMX_ERR_DEVICE, "bias init: %s", hipGetErrorString(e)));
+          b.loaded = true;
+          continue;
+        }
+        if (is_rmx(C)) {   // W1 / W2, one fragment buffer each
+          if ((s = dev_alloc(c, &b.ptr, b.elems * es, "weights")) != TMX_OK) return bail(s);
           continue;
         }
         if (C.dtype != TMX_F32 && (k == TMX_W_UP || k == TMX_W_EXP_UP || k == TMX_W_SH_UP)) continue;
@@ -468,9 +528,9 @@ tmx_status tmx_load_weights(tmx_ctx* c, int layer, int sub, int kind, const void
   if (layer < 0 || layer >= C.L) return fail(c, TMX_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, C.L);
   if (sub != TMX_MIX && sub != TMX_REVERT) return fail(c, TMX_ERR_INVALID_ARG, "sublayer must be 0 or 1, got %d", sub);
   if (kind < 0 || kind >= NKINDS) return fail(c, TMX_ERR_INVALID_ARG, "unknown weight kind %d", kind);
-  if (!kind_applies(C, kind))
-    return fail(c, TMX_ERR_INVALID_ARG, "weight kind %d does not apply to a %s context", kind,
-                is_moe(C) ? "MoE" : "dense");
+  if (!kind_applies(C, sub, kind))
+    return fail(c, TMX_ERR_INVALID_ARG, "weight kind %d does not apply to sub-layer %d of a %s context", kind, sub,
+                is_rmx(C) ? "RankMixer" : is_moe(C) ? "MoE" : "dense");
   if (!src) return fail(c, TMX_ERR_INVALID_ARG, "src is NULL");
   const size_t es = esize(C);
   const size_t elems = kind_elems(C, sub, kind);
@@ -488,7 +548,7 @@ tmx_status tmx_load_weights(tmx_ctx* c, int layer, int sub, int kind, const void
   (void)hipGetLastError();
 
   Bank& b = bank(c, layer, sub, kind);
-  if (kind == TMX_W_NORM_GAIN) {
+  if (is_norm(kind)) {
     std::vector<float> g(elems);
     std::vector<unsigned char> raw(nbytes);
     e = hipMemcpy(raw.data(), src, nbytes, src_dev ? hipMemcpyDeviceToHost : hipMemcpyHostToHost);
@@ -509,7 +569,7 @@ tmx_status tmx_load_weights(tmx_ctx* c, int layer, int sub, int kind, const void
     return TMX_OK;
   }
 
-  if (C.dtype == TMX_F32) {
+  if (C.dtype == TMX_F32 || kind == TMX_W_BIAS_UP || kind == TMX_W_BIAS_DOWN) {
     e = hipMemcpyAsync(b.ptr, src, nbytes, src_dev ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return fail(c, TMX_ERR_DEVICE, "weight copy: %s", hipGetErrorString(e));
@@ -539,7 +599,10 @@ tmx_status tmx_load_weights(tmx_ctx* c, int layer, int sub, int kind, const void
     if (kind == TMX_W_DOWN) dst = static_cast<uint8_t*>(bank(c, layer, sub, TMX_W_DOWN).ptr);
     e = launch_pack_mx(static_cast<const uint16_t*>(stage), dst, rec, (int)G, K, N, kind == TMX_W_DOWN ? 1 : 0, which,
                        st);
-  } else if (e == hipSuccess)
+  } else if (e == hipSuccess && is_rmx(C))
+    e = launch_pack(static_cast<const uint16_t*>(stage), static_cast<uint16_t*>(b.ptr), (int)G, K, N, 2, 0,
+                    FRAG_32x32x16, st);
+  else if (e == hipSuccess)
     e = launch_pack(static_cast<const uint16_t*>(stage), static_cast<uint16_t*>(storage(c, layer, sub, kind).ptr),
                     (int)G, K, N, gu ? 0 : 1, which, kind == TMX_W_ROUTER ? FRAG_16x16x32 : FRAG_32x32x16, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
@@ -559,8 +622,8 @@ tmx_status tmx_sublayer_forward(tmx_ctx* c, int layer, int sub, const void* x_in
   if ((s = check_act(c, x_in, "x_in")) != TMX_OK) return s;
   if ((s = check_act(c, x_out, "x_out")) != TMX_OK) return s;
   const size_t bytes = (size_t)B * c->cfg.T * c->cfg.D * esize(c->cfg);
-  if (sub == TMX_MIX) {
-    if (resid || extra) return fail(c, TMX_ERR_INVALID_ARG, "MIX sub-layer takes no resid/extra (pass NULL)");
+  if (sub == TMX_MIX || is_rmx(c->cfg)) {
+    if (resid || extra) return fail(c, TMX_ERR_INVALID_ARG, "this sub-layer takes no resid/extra (pass NULL)");
   } else {
     if ((s = check_act(c, resid, "resid")) != TMX_OK) return s;
     if (extra && !aligned16(extra)) return fail(c, TMX_ERR_INVALID_ARG, "extra must be 16-byte aligned");
@@ -571,6 +634,7 @@ tmx_status tmx_sublayer_forward(tmx_ctx* c, int layer, int sub, const void* x_in
   if (!sublayer_ready(c, layer, sub))
     return fail(c, TMX_ERR_STATE, "weights of layer %d sub-layer %d are not all loaded", layer, sub);
   (void)hipSetDevice(c->device);
+  if (is_rmx(c->cfg)) return run_rmx(c, layer, sub, x_in, x_out, B, as_stream(stream));
   return run_sublayer(c, layer, sub, x_in, resid, extra, x_out, B, as_stream(stream));
 }
 
@@ -586,6 +650,15 @@ tmx_status tmx_block_stack_forward(tmx_ctx* c, const void* x_in, void* x_out, in
   (void)hipSetDevice(c->device);
   hipStream_t st = as_stream(stream);
   const int L = c->cfg.L, g = c->cfg.inter_residual_gap;
+  if (is_rmx(c->cfg)) {
+    const void* cur = x_in;
+    for (int l = 1; l <= L; ++l) {
+      void* dst = l == L ? x_out : c->act[l & 1];
+      if ((s = run_rmx(c, l - 1, 2, cur, dst, B, st)) != TMX_OK) return s;
+      cur = dst;
+    }
+    return TMX_OK;
+  }
   const void* cur = x_in;    // Y_{l-1}
   const void* save = x_in;   // Y_{l-g}: the output of the last multiple of g
   for (int l = 1; l <= L; ++l) {

@@ -95,7 +95,7 @@ hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
 // Repack G row-major [K, N] bf16 matrices into MFMA B-operand fragments of
 // shape `frag` (FragShape). layout 0: gate|up interleave (`which` = 0 gate,
 // 1 up), frag = ((g*NB + nb)*KB + kb)*2 + which; layout 1: k-major,
-// frag = (g*KB + kb)*NB + nb.
+// frag = (g*KB + kb)*NB + nb; layout 2: n-major, frag = (g*NB + nb)*KB + kb.
 hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int G, int K, int N, int layout,
                        int which, int frag, hipStream_t s);
 // MXFP8 weights of the dense W = 256 kernel (two 4-wave workgroups per CU):
@@ -117,6 +117,27 @@ hipError_t launch_mlp_mx(const MlpArgs& a, int tiles, int workers, hipStream_t s
 constexpr int MX_REC_DWORDS = 24;   // per lane: 3 scale dwords x up to 8 hidden chunks
 hipError_t launch_permute(const void* in, void* out, int B, int T, int D, int H, int elem_bytes,
                           int inverse, hipStream_t s);
+
+// RankMixer block (tmx_rankmixer.hip), bf16, H = T, D in {256, 512}:
+//   part 0: out = S = rho(LN_1(TokenMixing(x) + x))
+//   part 1: out = rho(LN_2(x + PFFN_t(x)))            (x = S)
+//   part 2: both in one kernel
+struct RmxArgs {
+  int B, T, D, dh, hidden;
+  float eps;
+  const uint16_t* x;       // [B, T, D]
+  uint16_t* out;           // [B, T, D]
+  const float* g1;         // LN_1 gain / bias [D]
+  const float* be1;
+  const float* g2;         // LN_2 gain / bias [D]
+  const float* be2;
+  const uint16_t* w1;      // W1 [T][D, hidden] packed with layout 2 (32x32x16 fragments)
+  const uint16_t* w2;      // W2 [T][hidden, D] packed with layout 2
+  const uint16_t* b1;      // [T][hidden] bf16
+  const uint16_t* b2;      // [T][D] bf16
+};
+bool rmx_width_supported(int D);
+hipError_t launch_rmx(const RmxArgs& a, int part, hipStream_t s);
 
 // fp32 path
 struct F32Args {

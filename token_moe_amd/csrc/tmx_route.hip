@@ -372,8 +372,10 @@ __global__ void pack_kernel(const uint16_t* __restrict__ src, uint16_t* __restri
     int64_t f;
     if (layout == 0)
       f = (((int64_t)g * NB + nb) * KB + kb) * 2 + which;
-    else
+    else if (layout == 1)
       f = ((int64_t)g * KB + kb) * NB + nb;
+    else
+      f = ((int64_t)g * NB + nb) * KB + kb;
     dst[f * FRAG_ELEMS + lane * 8 + e] = src[i];
   }
 }

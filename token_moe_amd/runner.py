@@ -18,7 +18,8 @@ def config_from_workload(wl, B_max: Optional[int] = None) -> tmx.tmx_config:
         hidden_mix=wl.hidden_mix, hidden_rev=wl.hidden_rev, E=wl.E, top_k=wl.top_k,
         expert_hidden=wl.expert_hidden, shared_hidden=wl.shared_hidden, alpha=wl.alpha,
         eps=wl.eps, inter_residual_gap=wl.gap,
-        dtype={"bf16": tmx.TMX_BF16, "mxfp8": tmx.TMX_MXFP8}.get(wl.dtype, tmx.TMX_F32))
+        dtype={"bf16": tmx.TMX_BF16, "mxfp8": tmx.TMX_MXFP8}.get(wl.dtype, tmx.TMX_F32),
+        block=tmx.TMX_BLOCK_RANKMIXER if getattr(wl, "rankmixer", False) else tmx.TMX_BLOCK_TOKENMIXER_LARGE)
 
 
 def torch_dtype(wl):

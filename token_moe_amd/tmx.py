@@ -17,6 +17,7 @@ TMX_OK, TMX_ERR_INVALID_ARG, TMX_ERR_UNSUPPORTED, TMX_ERR_OOM, TMX_ERR_DEVICE, T
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "OOM", 4: "DEVICE", 5: "STATE"}
 TMX_F32, TMX_BF16, TMX_MXFP8 = 0, 1, 2
 TMX_MIX, TMX_REVERT = 0, 1
+TMX_BLOCK_TOKENMIXER_LARGE, TMX_BLOCK_RANKMIXER = 0, 1
 
 EXPORTED = ("tmx_create", "tmx_destroy", "tmx_last_error", "tmx_load_weights",
             "tmx_block_stack_forward", "tmx_moe_route", "tmx_sublayer_forward", "tmx_debug_permute")
@@ -38,6 +39,7 @@ class tmx_config(ctypes.Structure):
         ("expert_hidden", ctypes.c_int32), ("shared_hidden", ctypes.c_int32),
         ("alpha", ctypes.c_float), ("eps", ctypes.c_float),
         ("inter_residual_gap", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("block", ctypes.c_int32),
     ]
 
 
@@ -70,9 +72,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 
 
 def make_config(B_max, T, H, D, L, hidden_mix=0, hidden_rev=0, E=0, top_k=0, expert_hidden=0,
-                shared_hidden=0, alpha=0.0, eps=1e-6, inter_residual_gap=2, dtype=TMX_BF16) -> tmx_config:
+                shared_hidden=0, alpha=0.0, eps=1e-6, inter_residual_gap=2, dtype=TMX_BF16,
+                block=TMX_BLOCK_TOKENMIXER_LARGE) -> tmx_config:
     return tmx_config(B_max, T, H, D, L, hidden_mix, hidden_rev, E, top_k, expert_hidden,
-                      shared_hidden, alpha, eps, inter_residual_gap, dtype)
+                      shared_hidden, alpha, eps, inter_residual_gap, dtype, block)
 
 
 def _ptr(x) -> Optional[int]:
