@@ -2,6 +2,7 @@
 """Throughput of the TokenMixer-Large block-stack forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload N] [--no-cpu-baseline]
+    python bench.py --workload rankmixer_d256      # the RankMixer block stack
 
 A step is one tmx_block_stack_forward over one batch of the workload (all
 blocks, both sub-layers, inter-residuals) with inputs and weights already
@@ -95,9 +96,11 @@ def cpu_baseline(wl, banks, x, budget_s):
     import oracle as orc
     ws = dg.WeightSource(wl, banks)
 
+    forward = orc.rankmixer_stack if wl.rankmixer else orc.stack_forward
+
     def run(n):
         t0 = time.perf_counter()
-        orc.stack_forward(x[:n].astype(np.float64), wl, ws)
+        forward(x[:n].astype(np.float64), wl, ws)
         return time.perf_counter() - t0
 
     run(2)                                     # first-touch costs out of the probes
@@ -127,7 +130,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2, help="workload id 1..5 (default 2)")
+    ap.add_argument("--workload", default="2",
+                    help="workload id 1..5 (default 2) or a RankMixer workload (rankmixer_d256, rankmixer_d512)")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -150,9 +154,15 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     tmx.load_library()
-    wl = dg.WORKLOADS[args.workload]
+    if args.workload in dg.RANKMIXER_WORKLOADS:
+        wl = dg.RANKMIXER_WORKLOADS[args.workload]
+    elif args.workload.isdigit() and int(args.workload) in dg.WORKLOADS:
+        wl = dg.WORKLOADS[int(args.workload)]
+    else:
+        print(f"unknown workload {args.workload!r}", file=sys.stderr)
+        return 2
     if args.dtype == "mxfp8":
-        if wl.moe or wl.dtype != "bf16":
+        if wl.moe or wl.dtype != "bf16" or wl.rankmixer:
             print("--dtype mxfp8 applies to the bf16 dense workloads", file=sys.stderr)
             return 2
         wl = wl.with_(dtype="mxfp8")
@@ -179,7 +189,7 @@ def main(argv=None):
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    flops = orc.flops_per_sample(wl) * wl.B
+    flops = (orc.rankmixer_flops_per_sample(wl) if wl.rankmixer else orc.flops_per_sample(wl)) * wl.B
     samples_s = wl.B / (ms / 1e3)
     tflops = flops / (ms / 1e3) / 1e12
     log(f"{ms:.3f} ms/step, {samples_s:.0f} samples/s, {tflops:.1f} TFLOP/s")
@@ -190,7 +200,19 @@ def main(argv=None):
     # one sub-layer call is exactly one launch of it.
     roofline = None
     kernel = {}
-    if not wl.moe:
+    if wl.rankmixer:
+        # the stack is L launches of the fused block kernel and nothing else,
+        # so one launch takes the stack's event-timed time / L
+        kms = time_launches(lambda: ctx.block_stack_forward(xd, yd, wl.B, sp), args.kernel_reps, stream) / wl.L
+        kfl = float(orc.rankmixer_flops_per_sample(wl) // wl.L * wl.B)
+        achieved = kfl / (kms / 1e3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": f"rmx_block_kernel<{wl.D}, fused>", "flop_per_launch": kfl,
+                    "launch_ms": round(kms, 5)}
+        kernel["rmx_block_ms"] = round(kms, 5)
+        log(f"fused RankMixer block kernel: {kms:.4f} ms/launch, {achieved:.1f} TFLOP/s")
+    elif not wl.moe:
         xr = torch.empty_like(xd)
         per = []
         for sub in (0, 1):
@@ -221,7 +243,7 @@ def main(argv=None):
         "dtype": {"bf16": "bf16", "mxfp8": "mxfp8"}.get(wl.dtype, "f32"), "data": "synthetic",
         "tflops": round(tflops, 2),
         "mfma_frac": round(tflops / (FP8_PEAK_TFLOPS if wl.dtype == "mxfp8" else BF16_PEAK_TFLOPS), 4),
-        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "D": wl.D, "L": wl.L,
+        "config": {"workload": wl.name, "block": wl.block, "B": wl.B, "T": wl.T, "H": wl.H, "D": wl.D, "L": wl.L,
                    "hidden": [wl.hidden_mix, wl.hidden_rev], "E": wl.E, "top_k": wl.top_k,
                    "expert_hidden": wl.expert_hidden, "shared_hidden": wl.shared_hidden,
                    "flop_per_step": flops},

@@ -58,8 +58,24 @@ __device__ __forceinline__ f32x16 mma(const uint4& a, const uint4& b, const f32x
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// exact GELU z * Phi(z) in fp32
-__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+// GELU z * Phi(z) in fp32, Phi(z) = (1 + erf(z / sqrt 2)) / 2, with erf from
+// Abramowitz & Stegun formula 7.1.26 (Hastings' rational approximation):
+// for x >= 0, erfc(x) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
+// t = 1 / (1 + p x), |error| <= 1.5e-7. Written for the lower tail,
+// q = erfc(|z| / sqrt 2) / 2 = Phi(-|z|), so Phi(z) = z < 0 ? q : 1 - q keeps
+// full relative accuracy for negative z. One reciprocal and one exp2 per
+// value against about three times the instructions of the library erff.
+__device__ __forceinline__ float gelu_erf(float z) {
+  const float x = fabsf(z) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  // coefficients a1..a5 halved (the 1/2 of q folded in)
+  float p = fmaf(t, 0.5307027145f, -0.7265760135f);
+  p = fmaf(t, p, 0.7107068705f);
+  p = fmaf(t, p, -0.1422483680f);
+  p = fmaf(t, p, 0.1274147960f);
+  const float q = p * t * __builtin_amdgcn_exp2f(-x * x * 1.4426950408889634f);
+  return z * (z < 0.f ? q : 1.0f - q);
+}
 
 template <int EPL>
 __device__ __forceinline__ void unpack_row(const typename VecOf<EPL>::type& q, float* v) {
@@ -228,6 +244,14 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
         acc1[1] = mma(wf[i], s1, acc1[1]);
       }
     }
+    // W2 fragments of the first GEMM2 group go out before the GELU work
+    constexpr int KG = 16 / NT2;   // K steps per group of 16 fragments
+    uint4 wf2[KG][NT2];
+#pragma unroll
+    for (int k = 0; k < KG; ++k)
+#pragma unroll
+      for (int j = 0; j < NT2; ++j)
+        wf2[k][j] = ld16(w2t + ((size_t)(w * NT2 + j) * KB2 + c * KT2 + k) * FRAG_ELEMS + lane * 8);
     // ---- bias + GELU, rounded hidden chunk into LDS --------------------------
     // lane holds hidden units 8q + 4 hi + r (q, r < 4) of rows l32 and 32 + l32
     {
@@ -248,15 +272,17 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
     }
     __syncthreads();
     // ---- GEMM2: output column tiles w*NT2 + j, K = this chunk ----------------
-    constexpr int KG = 16 / NT2;   // K steps per group of 16 fragments
 #pragma unroll
     for (int k0 = 0; k0 < KT2; k0 += KG) {
       uint4 wf[KG][NT2];
 #pragma unroll
       for (int k = 0; k < KG; ++k)
 #pragma unroll
-        for (int j = 0; j < NT2; ++j)
-          wf[k][j] = ld16(w2t + ((size_t)(w * NT2 + j) * KB2 + c * KT2 + k0 + k) * FRAG_ELEMS + lane * 8);
+        for (int j = 0; j < NT2; ++j) {
+          wf[k][j] = wf2[k][j];
+          if (k0 + KG < KT2)   // the next group's fragments (compile-time condition)
+            wf2[k][j] = ld16(w2t + ((size_t)(w * NT2 + j) * KB2 + c * KT2 + k0 + KG + k) * FRAG_ELEMS + lane * 8);
+        }
 #pragma unroll
       for (int k = 0; k < KG; ++k) {
         const int kc = (k0 + k) * 16 + 8 * hi;
