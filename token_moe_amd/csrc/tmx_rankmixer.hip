@@ -223,18 +223,45 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
       for (int v = 0; v < 16; ++v) acc2[m][j][v] = 0.f;
 
   const int nchunks = a.hidden / RMX_HC;
+  // W1 fragments of GEMM1 group (chunk c, K steps k0 .. k0 + 15) of this wave
+  auto w1frag = [&](int c, int k) {
+    return ld16(w1t + ((size_t)(c * RMX_NW + w) * KB1 + k) * FRAG_ELEMS + lane * 8);
+  };
+  uint4 wf1[16];   // the next GEMM1 group
+  if constexpr (D > 256) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wf1[i] = w1frag(0, i);
+  }
   for (int c = 0; c < nchunks; ++c) {
     uint16_t* const ub = us + (c & 1) * (RMX_BM * SU);
+    if constexpr (D <= 256) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) wf1[i] = w1frag(c, i);
+    }
+    // b1 of this wave's hidden units. At D = 256 issued before the W2
+    // prefetch below, so that the GELU waits for them only (loads complete
+    // in issue order); at D = 512 right where the GELU uses them, addressed
+    // from one base (both measured faster than the alternatives)
+    auto load_b1 = [&](int q) {
+      return *reinterpret_cast<const uint2*>(b1t + c * RMX_HC + w * 32 + 4 * hi + 8 * q);
+    };
+    uint2 bq[4];
+    if constexpr (D <= 256) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bq[q] = load_b1(q);
+    }
     // ---- GEMM1: hidden tile 4c + w (32 units) x 64 rows ----------------------
     f32x16 acc1[2];
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc1[0][v] = acc1[1][v] = 0.f;
-    const uint16_t* w1f = w1t + (size_t)(c * RMX_NW + w) * KB1 * FRAG_ELEMS + lane * 8;
 #pragma unroll
     for (int k0 = 0; k0 < KT1; k0 += 16) {
       uint4 wf[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) wf[i] = ld16(w1f + (size_t)(k0 + i) * FRAG_ELEMS);
+      for (int i = 0; i < 16; ++i) {
+        wf[i] = wf1[i];
+        if (k0 + 16 < KT1) wf1[i] = w1frag(c, k0 + 16 + i);   // compile-time condition
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kc = (k0 + i) * 16 + 8 * hi;
@@ -255,12 +282,16 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
     // ---- bias + GELU, rounded hidden chunk into LDS --------------------------
     // lane holds hidden units 8q + 4 hi + r (q, r < 4) of rows l32 and 32 + l32
     {
-      const int hb = c * RMX_HC + w * 32 + 4 * hi;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint2 bq = *reinterpret_cast<const uint2*>(b1t + hb + 8 * q);
         float bias[4];
-        unpack_row<4>(bq, bias);
+        if constexpr (D <= 256) {
+          unpack_row<4>(bq[q], bias);
+        } else {
+          const int hb = c * RMX_HC + w * 32 + 4 * hi;
+          const uint2 bv = *reinterpret_cast<const uint2*>(b1t + hb + 8 * q);
+          unpack_row<4>(bv, bias);
+        }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           uint2 o;
@@ -271,6 +302,16 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
       }
     }
     __syncthreads();
+    // the next chunk's first W1 group goes out ahead of GEMM2 at D = 512 (one
+    // workgroup per CU, registers to spare); at D = 256 (two per CU) at the
+    // top of the next chunk: 64 more live registers through GEMM2 cost more
+    // than the latency they hide. The last chunk reloads its own group: an
+    // unconditional load keeps the wait counts straight.
+    if constexpr (D > 256) {
+      const int cn = c + 1 < nchunks ? c + 1 : c;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) wf1[i] = w1frag(cn, i);
+    }
     // ---- GEMM2: output column tiles w*NT2 + j, K = this chunk ----------------
 #pragma unroll
     for (int k0 = 0; k0 < KT2; k0 += KG) {
