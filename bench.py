@@ -27,28 +27,31 @@ FP8_PEAK_TFLOPS = 5033.2      # dense fp8 MFMA: twice the bf16 rate
 HBM_PEAK_GBS = 8000.0
 
 
-# rocprofv3 counter summary of the dominant kernel; its traffic figure is used
-# only while the kernel sources still hash to the value recorded there
+# rocprofv3 counter summaries of the dominant kernels; a traffic figure is used
+# only while the kernel's sources still hash to the value recorded there
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "mlp_dense_workload2_counters.md")
 KERNEL_SOURCES = ("token_moe_amd/csrc/tmx_mlp.hip", "token_moe_amd/csrc/tmx_device.h", "token_moe_amd/build.py",
                   "token_moe_amd/csrc/tmx_internal.h")
+RMX_COUNTERS_FILE = os.path.join(ROOT, "profiles", "rmx_block_rankmixer_d256_counters.md")
+RMX_KERNEL_SOURCES = ("token_moe_amd/csrc/tmx_rankmixer.hip", "token_moe_amd/csrc/tmx_device.h",
+                      "token_moe_amd/build.py", "token_moe_amd/csrc/tmx_internal.h")
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, counters_file=COUNTERS_FILE, sources=KERNEL_SOURCES):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy's reading),
     or None when it was taken on other kernel sources or another workload."""
     try:
-        with open(COUNTERS_FILE) as f:
+        with open(counters_file) as f:
             text = f.read()
     except OSError:
         return None
@@ -59,7 +62,7 @@ def measured_traffic(workload):
                                                       "traffic_bytes_per_launch"):
             k, v = line.split(":", 1)
             vals[k] = v.strip()
-    if vals.get("kernel_source_sha256") != kernel_source_hash() or vals.get("workload") != workload:
+    if vals.get("kernel_source_sha256") != kernel_source_hash(sources) or vals.get("workload") != workload:
         return None
     try:
         return int(vals["traffic_bytes_per_launch"])
@@ -207,7 +210,8 @@ def main(argv=None):
         kfl = float(orc.rankmixer_flops_per_sample(wl) // wl.L * wl.B)
         achieved = kfl / (kms / 1e3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                    "traffic": measured_traffic(wl.name, RMX_COUNTERS_FILE, RMX_KERNEL_SOURCES),
                     "kernel": f"rmx_block_kernel<{wl.D}, fused>", "flop_per_launch": kfl,
                     "launch_ms": round(kms, 5)}
         kernel["rmx_block_ms"] = round(kms, 5)
