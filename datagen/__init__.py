@@ -49,13 +49,15 @@ K_SH_DOWN = 10
 K_NORM_BIAS = 11     # RankMixer LayerNorm bias
 K_BIAS_UP = 12       # RankMixer per-token FFN first bias  [P, h]
 K_BIAS_DOWN = 13     # RankMixer per-token FFN second bias [P, W]
+K_EXP_BIAS_UP = 14   # RankMixer ReLU-routed experts' first biases  [P, E, h_e]
+K_EXP_BIAS_DOWN = 15 # RankMixer ReLU-routed experts' second biases [P, E, W]
 
 KIND_NAMES = {
     K_NORM_GAIN: "norm_gain", K_UP: "up", K_GATE: "gate", K_DOWN: "down",
     K_ROUTER: "router", K_EXP_UP: "exp_up", K_EXP_GATE: "exp_gate",
     K_EXP_DOWN: "exp_down", K_SH_UP: "sh_up", K_SH_GATE: "sh_gate",
     K_SH_DOWN: "sh_down", K_NORM_BIAS: "norm_bias", K_BIAS_UP: "bias_up",
-    K_BIAS_DOWN: "bias_down",
+    K_BIAS_DOWN: "bias_down", K_EXP_BIAS_UP: "exp_bias_up", K_EXP_BIAS_DOWN: "exp_bias_down",
 }
 
 DENSE_KINDS = (K_UP, K_GATE, K_DOWN)
@@ -63,6 +65,9 @@ MOE_KINDS = (K_ROUTER, K_EXP_UP, K_EXP_GATE, K_EXP_DOWN, K_SH_UP, K_SH_GATE, K_S
 # RankMixer: the token-mixing sub-layer has only its LayerNorm; the per-token
 # FFN sub-layer holds W1 (K_UP), W2 (K_DOWN) and their biases
 RMX_FFN_KINDS = (K_UP, K_DOWN, K_BIAS_UP, K_BIAS_DOWN)
+# RankMixer sparse MoE (ReLU routing, inference router): router, the
+# experts' two matrices and their biases
+RMX_MOE_KINDS = (K_ROUTER, K_EXP_UP, K_EXP_DOWN, K_EXP_BIAS_UP, K_EXP_BIAS_DOWN)
 NORM_KINDS = (K_NORM_GAIN, K_NORM_BIAS)
 
 BLOCK_TML = "tml"
@@ -131,7 +136,9 @@ class Workload:
     def sub_kinds(self, sub: int):
         """Matrix and bias kinds of one sub-layer (norm parameters excluded)."""
         if self.rankmixer:
-            return RMX_FFN_KINDS if sub == SUB_REVERT else ()
+            if sub != SUB_REVERT:
+                return ()
+            return RMX_MOE_KINDS if self.moe else RMX_FFN_KINDS
         return self.kinds()
 
     def kind_shape(self, sub: int, kind: int) -> Tuple[int, ...]:
@@ -143,6 +150,10 @@ class Workload:
             return (P, self.hidden(sub))
         if kind == K_BIAS_DOWN:
             return (P, W)
+        if kind == K_EXP_BIAS_UP:
+            return (P, self.E, self.expert_hidden)
+        if kind == K_EXP_BIAS_DOWN:
+            return (P, self.E, W)
         if kind in (K_UP, K_GATE):
             return (P, W, self.hidden(sub))
         if kind == K_DOWN:
@@ -162,7 +173,7 @@ class Workload:
     def fan_in(self, sub: int, kind: int) -> int:
         if kind in (K_DOWN, K_BIAS_DOWN):
             return self.hidden(sub)
-        if kind == K_EXP_DOWN:
+        if kind in (K_EXP_DOWN, K_EXP_BIAS_DOWN):
             return self.expert_hidden
         if kind == K_SH_DOWN:
             return self.shared_hidden
@@ -202,6 +213,11 @@ RANKMIXER_WORKLOADS: Dict[str, Workload] = {
     "rankmixer_d512": Workload("rankmixer_d512", B=4096, T=16, H=16, D=512, L=4,
                                hidden_rev=2048, gap=0, eps=1e-5, seed=12,
                                down_scale=1.0, block=BLOCK_RANKMIXER),
+    # sparse version: every token's FFN replaced by 16 ReLU-routed experts of
+    # hidden 128 (fun-rec chapter 7.4.3 ReLU routing, inference router)
+    "rankmixer_moe_d256": Workload("rankmixer_moe_d256", B=4096, T=16, H=16, D=256, L=4,
+                                   E=16, expert_hidden=128, gap=0, eps=1e-5, seed=13,
+                                   down_scale=1.0, block=BLOCK_RANKMIXER),
 }
 
 

@@ -41,7 +41,7 @@ __all__ = [
     "E4M3_MAX", "MX_BLOCK", "e4m3_value", "e4m3_round", "mx_exponent", "mx_quantize",
     "mx_dequantize", "mx_round", "swiglu_mx",
     "layernorm", "gelu", "pffn", "rankmixer_block", "rankmixer_ffn_sublayer", "rankmixer_stack",
-    "rankmixer_flops_per_sample",
+    "rankmixer_flops_per_sample", "relu_route", "relu_moe",
 ]
 
 BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
@@ -437,9 +437,15 @@ def flops_per_sample(cfg) -> int:
 #   residual), the hidden GELU output and the block output are rounded to
 #   bf16 once each; LN statistics, the GEMM accumulations, the biases' and
 #   residual's additions stay unrounded.
+# * Sparse version ([RMX-BOOK] 7.4.3, inference router): each token's
+#   experts have the per-token FFN's form (GELU, biases); the router is a
+#   bias-free linear map; the gate multiplies the expert's whole output,
+#   its second bias included; in bf16 mode the gated hidden is the rounded
+#   quantity and the gates themselves are not rounded.
 # ---------------------------------------------------------------------------
 
 _K_NBIAS, _K_BUP, _K_BDOWN = 11, 12, 13
+_K_EBUP, _K_EBDOWN = 14, 15
 
 
 def layernorm(v: np.ndarray, gamma: Optional[np.ndarray], beta: Optional[np.ndarray],
@@ -497,15 +503,48 @@ def rankmixer_block(X: np.ndarray, cfg, layer: int, weights: WeightGetter,
     return rankmixer_ffn_sublayer(S, cfg, layer, weights, rho)
 
 
+def relu_route(s: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """ReLU routing ([RMX-BOOK] 7.4.3; the RankMixer README's ReLU routing):
+    G = ReLU(h(s)) with h the token's linear inference router s @ Wr, Wr
+    [D, E], no bias. A gate of 0 leaves its expert inactive, so each row
+    activates its own number of experts."""
+    return np.maximum(np.asarray(s, dtype=np.float64) @ np.asarray(w_router, dtype=np.float64), 0.0)
+
+
+def relu_moe(s: np.ndarray, w_router, w1, b1, w2, b2, rho: bool = False):
+    """v = sum_j G_j e_j(s) ([RMX-BOOK] 7.4.3) over one token's E experts,
+    each e_j the per-token FFN's form GELU(s W1_j + b1_j) W2_j + b2_j with
+    W1 [E, D, h_e], b1 [E, h_e], W2 [E, h_e, D], b2 [E, D]. In bf16 mode the
+    gated hidden G_j * GELU(.) is rounded once before the second matrix.
+    Returns (v, G)."""
+    s = np.asarray(s, dtype=np.float64)
+    G = relu_route(s, w_router)
+    v = np.zeros((s.shape[0], np.asarray(w2).shape[-1]))
+    for j in range(G.shape[1]):
+        g = G[:, j:j + 1]
+        hid = _rho(g * gelu(s @ np.asarray(w1[j], dtype=np.float64) + np.asarray(b1[j], dtype=np.float64)), rho)
+        v += hid @ np.asarray(w2[j], dtype=np.float64) + g * np.asarray(b2[j], dtype=np.float64)
+    return v, G
+
+
 def rankmixer_ffn_sublayer(S: np.ndarray, cfg, layer: int, weights: WeightGetter,
-                           rho: bool = False) -> np.ndarray:
-    """Second half of a RankMixer block: X_next[:, t] = LN_2(S[:, t] + PFFN_t(S[:, t]))."""
+                           rho: bool = False, record: Optional[dict] = None) -> np.ndarray:
+    """Second half of a RankMixer block: X_next[:, t] = LN_2(S[:, t] + F_t(S[:, t])),
+    F_t the token's FFN (dense) or its ReLU-routed experts (E > 0; the
+    gates of token t go to ``record[t]``)."""
     S = np.asarray(S, dtype=np.float64)
     out = np.empty_like(S)
     g2, b2n = weights(layer, 1, _K_GAIN, 0), weights(layer, 1, _K_NBIAS, 0)
     for t in range(S.shape[1]):
-        v = pffn(S[:, t], weights(layer, 1, _K_UP, t), weights(layer, 1, _K_BUP, t),
-                 weights(layer, 1, _K_DOWN, t), weights(layer, 1, _K_BDOWN, t), rho)
+        if cfg.E == 0:
+            v = pffn(S[:, t], weights(layer, 1, _K_UP, t), weights(layer, 1, _K_BUP, t),
+                     weights(layer, 1, _K_DOWN, t), weights(layer, 1, _K_BDOWN, t), rho)
+        else:
+            v, G = relu_moe(S[:, t], weights(layer, 1, _K_ROUTER, t), weights(layer, 1, _K_EUP, t),
+                            weights(layer, 1, _K_EBUP, t), weights(layer, 1, _K_EDOWN, t),
+                            weights(layer, 1, _K_EBDOWN, t), rho)
+            if record is not None:
+                record[t] = G
         out[:, t] = layernorm(S[:, t] + v, g2, b2n, cfg.eps)
     return _rho(out, rho)
 
@@ -524,5 +563,10 @@ def rankmixer_stack(X: np.ndarray, cfg, weights: WeightGetter, rho: Optional[boo
 
 def rankmixer_flops_per_sample(cfg) -> int:
     """GEMM FLOPs of one sample: per block and token 2 * (D kD + kD D)
-    ([RMX-BOOK] 7.4.2: 2TkD^2 multiply-adds per block)."""
-    return cfg.L * cfg.T * 2 * 2 * cfg.D * cfg.hidden_rev
+    ([RMX-BOOK] 7.4.2: 2TkD^2 multiply-adds per block). For the ReLU-routed
+    experts, every expert of the token and the router (what a forward that
+    evaluates each expert on all rows computes; rows with a zero gate need
+    none of it)."""
+    if cfg.E == 0:
+        return cfg.L * cfg.T * 2 * 2 * cfg.D * cfg.hidden_rev
+    return cfg.L * cfg.T * 2 * (2 * cfg.D * cfg.E * cfg.expert_hidden + cfg.D * cfg.E)

@@ -1,5 +1,6 @@
 """Pins of the RankMixer part of the CPU oracle (layernorm, gelu, pffn,
-rankmixer_block / rankmixer_ffn_sublayer / rankmixer_stack, the FLOP count).
+relu_route / relu_moe, rankmixer_block / rankmixer_ffn_sublayer /
+rankmixer_stack, the FLOP count).
 
 Each is checked against something other than itself: a hand-worked block
 (tests/golden/rankmixer_block_hand.json), torch's own LayerNorm / GELU /
@@ -237,15 +238,105 @@ def test_ffn_sublayer_is_the_second_half_of_the_block():
     np.testing.assert_array_equal(orc.rankmixer_ffn_sublayer(tr[(1, "S")], wl, 1, ws, rho=True), y)
 
 
+def _dense_rmx():
+    return [wl for wl in dg.RANKMIXER_WORKLOADS.values() if not wl.moe]
+
+
 def test_rankmixer_flops_closed_form():
     """Chapter 7.4.2: a block costs 2 T k D^2 multiply-adds (kD = hidden)."""
-    for wl in dg.RANKMIXER_WORKLOADS.values():
+    for wl in _dense_rmx():
         k = wl.hidden_rev // wl.D
         assert orc.rankmixer_flops_per_sample(wl) == wl.L * 2 * (2 * wl.T * k * wl.D ** 2)
 
 
 def test_rankmixer_param_count():
     """Chapter 7.4.2: per block 2 T k D^2 matrix weights, plus T (kD + D) biases."""
-    for wl in dg.RANKMIXER_WORKLOADS.values():
+    for wl in _dense_rmx():
         k = wl.hidden_rev // wl.D
         assert dg.param_count(wl) == wl.L * (2 * wl.T * k * wl.D ** 2 + wl.T * (k * wl.D + wl.D))
+
+
+# ---------------------------------------------------------------------------
+# ReLU-routed experts (chapter 7.4.3, inference router)
+# ---------------------------------------------------------------------------
+
+def _moe_weights(rng, D, E, he):
+    return (rng.standard_normal((D, E)), rng.standard_normal((E, D, he)) / np.sqrt(D),
+            rng.standard_normal((E, he)), rng.standard_normal((E, he, D)) / np.sqrt(he),
+            rng.standard_normal((E, D)))
+
+
+def test_relu_moe_matches_sparse_torch_evaluation():
+    """Row by row, only the experts with a positive gate, each a torch
+    Linear-GELU-Linear scaled by its gate (catches softmax or top-k in
+    place of ReLU, an ungated second bias, a wrong expert index)."""
+    torch = _torch()
+    rng = np.random.default_rng(11)
+    D, E, he, n = 6, 5, 7, 9
+    wr, w1, b1, w2, b2 = _moe_weights(rng, D, E, he)
+    s = rng.standard_normal((n, D))
+    v, G = orc.relu_moe(s, wr, w1, b1, w2, b2)
+    want = np.zeros((n, D))
+    with torch.no_grad():
+        for i in range(n):
+            logits = torch.from_numpy(s[i] @ wr)
+            for j in range(E):
+                g = float(torch.relu(logits[j]))
+                if g == 0.0:
+                    continue
+                l1 = torch.nn.Linear(D, he).double()
+                l2 = torch.nn.Linear(he, D).double()
+                l1.weight.copy_(torch.from_numpy(w1[j].T)); l1.bias.copy_(torch.from_numpy(b1[j]))
+                l2.weight.copy_(torch.from_numpy(w2[j].T)); l2.bias.copy_(torch.from_numpy(b2[j]))
+                want[i] += g * l2(torch.nn.GELU()(l1(torch.from_numpy(s[i])))).numpy()
+    np.testing.assert_allclose(v, want, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(G, np.maximum(s @ wr, 0.0))
+
+
+def test_relu_moe_active_counts_vary_and_zero_router_is_silent():
+    """Rows activate different numbers of experts (no fixed k); a zero
+    router activates none, so the FFN contributes exactly nothing."""
+    rng = np.random.default_rng(12)
+    D, E, he = 8, 16, 4
+    wr, w1, b1, w2, b2 = _moe_weights(rng, D, E, he)
+    s = rng.standard_normal((200, D))
+    _, G = orc.relu_moe(s, wr, w1, b1, w2, b2)
+    counts = (G > 0).sum(axis=1)
+    assert counts.min() < counts.max() and 0 < counts.mean() < E
+    v0, G0 = orc.relu_moe(s, np.zeros_like(wr), w1, b1, w2, b2)
+    assert not G0.any() and not v0.any()
+
+
+def test_relu_moe_is_positively_homogeneous_in_the_router():
+    """v(c Wr) = c v(Wr) for c > 0: the gates scale, the active set does not
+    change (a normalised router -- softmax -- fails this)."""
+    rng = np.random.default_rng(13)
+    wr, w1, b1, w2, b2 = _moe_weights(rng, 6, 5, 3)
+    s = rng.standard_normal((10, 6))
+    v, _ = orc.relu_moe(s, wr, w1, b1, w2, b2)
+    v3, _ = orc.relu_moe(s, 3.0 * wr, w1, b1, w2, b2)
+    np.testing.assert_allclose(v3, 3.0 * v, rtol=1e-12, atol=1e-13)
+
+
+def test_moe_block_with_zero_router_is_two_layernorms():
+    """With every router zero the block is X' = LN_2(S), S = LN_1(TM(X) + X)."""
+    wl = dg.RANKMIXER_WORKLOADS["rankmixer_moe_d256"].with_(B=3, L=1, random_norm=True)
+    ws = dg.WeightSource(wl)
+
+    def weights(layer, sub, kind, p):
+        w = ws(layer, sub, kind, p)
+        return np.zeros_like(w) if kind == dg.K_ROUTER else w
+    X = dg.make_x(wl).astype(np.float64)
+    tr = {}
+    y = orc.rankmixer_block(X, wl, 1, weights, rho=False, trace=tr)
+    want = orc.layernorm(tr[(1, "S")], ws(1, 1, dg.K_NORM_GAIN, 0), ws(1, 1, dg.K_NORM_BIAS, 0), wl.eps)
+    np.testing.assert_allclose(y, want, rtol=1e-13, atol=1e-13)
+
+
+def test_moe_workload_closed_forms():
+    """Parameters per block and token: router D E, experts E (2 D h_e + h_e + D);
+    FLOPs: every expert and the router on every row."""
+    wl = dg.RANKMIXER_WORKLOADS["rankmixer_moe_d256"]
+    D, E, he = wl.D, wl.E, wl.expert_hidden
+    assert dg.param_count(wl) == wl.L * wl.T * (D * E + E * (2 * D * he + he + D))
+    assert orc.rankmixer_flops_per_sample(wl) == wl.L * wl.T * 2 * (2 * D * E * he + D * E)
