@@ -44,6 +44,11 @@
  * LN is LayerNorm (biased variance, eps = cfg.eps, gain and bias), GELU the
  * exact erf form.  Sub-layer 0 (TMX_MIX) is the token-mixing half, sub-layer
  * 1 (TMX_REVERT) the FFN half; S is rounded to the ctx dtype once.
+ * With E > 0 each token's FFN is replaced by E ReLU-routed experts (fun-rec
+ * chapter 7.4.3, the inference router of dense-train / sparse-infer):
+ * G = ReLU(s Wr_t), PFFN_t(s) = sum_j G_j (GELU(s W1_tj + b1_tj) W2_tj + b2_tj),
+ * a varying number of active experts per row; an expert that no row of a
+ * 64-row tile activates is skipped for that tile.
  */
 #ifndef TMX_H
 #define TMX_H
@@ -101,7 +106,12 @@ typedef enum tmx_weight_kind {
    * biases to 0. */
   TMX_W_NORM_BIAS = 11, /* [W]          LayerNorm bias, optional            */
   TMX_W_BIAS_UP = 12,   /* [P, h]       b1 of the per-token FFN, optional   */
-  TMX_W_BIAS_DOWN = 13  /* [P, W]       b2 of the per-token FFN, optional   */
+  TMX_W_BIAS_DOWN = 13, /* [P, W]       b2 of the per-token FFN, optional   */
+  /* RankMixer ReLU-routed experts (E > 0, sub-layer 1): ROUTER [T, D, E] is
+   * the inference router, EXP_UP [T, E, D, h_e] and EXP_DOWN [T, E, h_e, D]
+   * the experts' W1 and W2. */
+  TMX_W_EXP_BIAS_UP = 14,  /* [P, E, h_e] experts' b1, optional            */
+  TMX_W_EXP_BIAS_DOWN = 15 /* [P, E, W]   experts' b2, optional            */
 } tmx_weight_kind;
 
 /* Model configuration; the pages' problem statement (B, T, H, D, hidden, E,
@@ -138,10 +148,12 @@ typedef struct tmx_ctx tmx_ctx;
  * addressed with 32-bit byte offsets); TMX_ERR_UNSUPPORTED otherwise.
  * RankMixer contexts need H == T (the paper-strict token mixing; the
  * reproduction guide's section 5 makes any other H an error), hidden_mix ==
- * 0, inter_residual_gap == 0 and hidden_rev >= 1 (TMX_ERR_INVALID_ARG
- * otherwise), and this build runs them dense (E = 0), in bf16, with D of
- * 256 or 512, D/H % 8 == 0 and hidden_rev % 128 == 0
- * (TMX_ERR_UNSUPPORTED otherwise).
+ * 0, inter_residual_gap == 0, and either hidden_rev >= 1 (dense) or E > 0
+ * with hidden_rev == 0, top_k == 0 and expert_hidden >= 1
+ * (TMX_ERR_INVALID_ARG otherwise); this build runs them in bf16 with D of
+ * 256 or 512, D/H % 8 == 0 and hidden_rev % 128 == 0, the experts at D =
+ * 256 with E of 16 or 32 and expert_hidden % 128 == 0 (TMX_ERR_UNSUPPORTED
+ * otherwise).
  * On error *out is set to NULL and nothing stays allocated. */
 tmx_status tmx_create(const tmx_config* cfg, int device, tmx_ctx** out);
 
@@ -164,7 +176,8 @@ const char* tmx_last_error(const tmx_ctx* ctx);
  * bank's exact size.  Dense contexts accept NORM_GAIN, UP, GATE, DOWN; MoE
  * contexts NORM_GAIN, ROUTER and the EXP_* / SH_* kinds; RankMixer contexts
  * NORM_GAIN and NORM_BIAS in both sub-layers and UP, DOWN, BIAS_UP,
- * BIAS_DOWN in sub-layer 1 (UP and DOWN are required).  The call is
+ * BIAS_DOWN in sub-layer 1 (UP and DOWN are required); with E > 0 ROUTER,
+ * EXP_UP, EXP_DOWN (required), EXP_BIAS_UP and EXP_BIAS_DOWN instead.  The call is
  * synchronous (it waits for `stream`); it is not meant for timed loops. */
 tmx_status tmx_load_weights(tmx_ctx* ctx, int layer, int sublayer, int kind,
                             const void* src, size_t nbytes, void* stream);
@@ -181,7 +194,7 @@ tmx_status tmx_block_stack_forward(tmx_ctx* ctx, const void* x_in, void* x_out,
  * dtype, logits = x_hat @ Wr_p, pi = softmax over all E, and the top_k
  * experts under the key (-logit, expert index) are written in that order:
  * idx [B, P, top_k] int32 and gate [B, P, top_k] float32 = alpha * pi
- * (device pointers).  TMX_ERR_UNSUPPORTED on a dense context. */
+ * (device pointers).  TMX_ERR_UNSUPPORTED on a dense or RankMixer context. */
 tmx_status tmx_moe_route(tmx_ctx* ctx, int layer, int sublayer, const void* x,
                          int B, int32_t* idx, float* gate, void* stream);
 

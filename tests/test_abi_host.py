@@ -82,7 +82,8 @@ def test_status_and_enum_values_match_header(tmx):
                       ("TMX_F32", 0), ("TMX_BF16", 1), ("TMX_MXFP8", 2),
                       ("TMX_W_NORM_BIAS", dg.K_NORM_BIAS), ("TMX_W_BIAS_UP", dg.K_BIAS_UP),
                       ("TMX_W_BIAS_DOWN", dg.K_BIAS_DOWN), ("TMX_BLOCK_TOKENMIXER_LARGE", 0),
-                      ("TMX_BLOCK_RANKMIXER", tmx.TMX_BLOCK_RANKMIXER)]:
+                      ("TMX_BLOCK_RANKMIXER", tmx.TMX_BLOCK_RANKMIXER),
+                      ("TMX_W_EXP_BIAS_UP", dg.K_EXP_BIAS_UP), ("TMX_W_EXP_BIAS_DOWN", dg.K_EXP_BIAS_DOWN)]:
         m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
         assert m and int(m.group(1)) == val, name
 
@@ -133,8 +134,19 @@ def _create(tmx, **kw):
     (dict(block=1, dtype=1, D=128, H=16, T=16, hidden_mix=0, hidden_rev=1024, inter_residual_gap=0), "UNSUPPORTED"),
     (dict(block=1, dtype=1, D=256, H=64, T=64, hidden_mix=0, hidden_rev=1024, inter_residual_gap=0), "UNSUPPORTED"),
     (dict(block=1, dtype=1, D=256, H=16, T=16, hidden_mix=0, hidden_rev=1000, inter_residual_gap=0), "UNSUPPORTED"),
-    (dict(block=1, dtype=1, D=256, H=16, T=16, hidden_mix=0, hidden_rev=1024, inter_residual_gap=0, E=16, top_k=4,
-          expert_hidden=256, shared_hidden=256), "UNSUPPORTED"),
+    # RankMixer ReLU-routed experts: hidden_rev 0, top_k 0 (variable count); D 256, E 16 / 32, h_e % 128
+    (dict(block=1, dtype=1, D=256, H=16, T=16, hidden_mix=0, hidden_rev=1024, inter_residual_gap=0, E=16, top_k=0,
+          expert_hidden=128), "INVALID_ARG"),
+    (dict(block=1, dtype=1, D=256, H=16, T=16, hidden_mix=0, hidden_rev=0, inter_residual_gap=0, E=16, top_k=4,
+          expert_hidden=128), "INVALID_ARG"),
+    (dict(block=1, dtype=1, D=256, H=16, T=16, hidden_mix=0, hidden_rev=0, inter_residual_gap=0, E=16, top_k=0,
+          expert_hidden=0), "INVALID_ARG"),
+    (dict(block=1, dtype=1, D=512, H=16, T=16, hidden_mix=0, hidden_rev=0, inter_residual_gap=0, E=16, top_k=0,
+          expert_hidden=128), "UNSUPPORTED"),
+    (dict(block=1, dtype=1, D=256, H=16, T=16, hidden_mix=0, hidden_rev=0, inter_residual_gap=0, E=8, top_k=0,
+          expert_hidden=128), "UNSUPPORTED"),
+    (dict(block=1, dtype=1, D=256, H=16, T=16, hidden_mix=0, hidden_rev=0, inter_residual_gap=0, E=16, top_k=0,
+          expert_hidden=96), "UNSUPPORTED"),
     # x_hat workspace (B_max*T*D bf16) must stay under 4 GiB
     (dict(dtype=1, B_max=1 << 21, D=512, H=16, T=16, E=16, top_k=4, expert_hidden=256, shared_hidden=512),
      "UNSUPPORTED"),

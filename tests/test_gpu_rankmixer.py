@@ -1,7 +1,7 @@
 """RankMixer block stack on the GPU vs the fp64 oracle (bf16, H = T, post-LN,
-per-token GELU FFN with biases). Tolerance: the bf16 bound, row-normwise
-2e-2; post-LN outputs have unit scale in every row, so no residual hides the
-FFN's contribution."""
+per-token GELU FFN with biases, or per-token ReLU-routed experts).
+Tolerance: the bf16 bound, row-normwise 2e-2; post-LN outputs have unit
+scale in every row, so no residual hides the FFN's contribution."""
 import numpy as np
 import pytest
 
@@ -20,6 +20,16 @@ SMALL_D512 = dg.Workload("rmx_small_d512", B=130, T=16, H=16, D=512, L=2, hidden
                          seed=72, down_scale=1.0, block=dg.BLOCK_RANKMIXER, random_norm=True)
 
 
+# ReLU-routed experts: 16 experts of hidden 128 per token (ragged batch), and
+# 32 experts of hidden 128 with 16 tokens
+SMALL_MOE16 = dg.Workload("rmx_small_moe16", B=300, T=8, H=8, D=256, L=2, E=16, expert_hidden=128, gap=0,
+                          eps=1e-5, seed=73, down_scale=1.0, block=dg.BLOCK_RANKMIXER, random_norm=True)
+SMALL_MOE32 = dg.Workload("rmx_small_moe32", B=130, T=16, H=16, D=256, L=2, E=32, expert_hidden=128, gap=0,
+                          eps=1e-5, seed=74, down_scale=1.0, block=dg.BLOCK_RANKMIXER, random_norm=True)
+SMALL = [SMALL_D256, SMALL_D512, SMALL_MOE16, SMALL_MOE32]
+SMALL_IDS = ["d256", "d512", "moe16", "moe32"]
+
+
 def _stack(ctx, x_dev, B):
     import torch
     y = torch.empty_like(x_dev)
@@ -28,7 +38,7 @@ def _stack(ctx, x_dev, B):
     return y
 
 
-@pytest.mark.parametrize("wl", [SMALL_D256, SMALL_D512], ids=["d256", "d512"])
+@pytest.mark.parametrize("wl", SMALL, ids=SMALL_IDS)
 def test_small_stack_all_rows(wl):
     require_gpu()
     say("RankMixer small stack", wl)
@@ -42,7 +52,7 @@ def test_small_stack_all_rows(wl):
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("wl", [SMALL_D256, SMALL_D512], ids=["d256", "d512"])
+@pytest.mark.parametrize("wl", SMALL, ids=SMALL_IDS)
 def test_chain_of_halves_is_the_stack_and_batch_independent(wl):
     """Sub-layer 0 then sub-layer 1 per block reproduces the fused stack bit
     for bit; two runs agree; B = 1 and a ragged B give the same rows."""
@@ -65,7 +75,7 @@ def test_chain_of_halves_is_the_stack_and_batch_independent(wl):
         assert torch.equal(_stack(ctx, x[:B].contiguous(), B), y1[:B])
 
 
-@pytest.mark.parametrize("name", ["rankmixer_d256", "rankmixer_d512"])
+@pytest.mark.parametrize("name", ["rankmixer_d256", "rankmixer_d512", "rankmixer_moe_d256"])
 def test_full_batch_halves_teacher_forced(name):
     """Both halves at the full batch (the launch shape of the timed stack):
     S on every row (it is one rounding of a LayerNorm: at most one bf16 step
@@ -96,7 +106,30 @@ def test_full_batch_halves_teacher_forced(name):
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("name", ["rankmixer_d256", "rankmixer_d512"])
+def test_skipped_experts_and_silent_token():
+    """Experts 3 and 7 never activate (zero router columns, so every tile
+    skips them) and token 0's router is zero (every chunk skipped: its output
+    is LN_2(S)); all rows against the oracle on the same weights."""
+    require_gpu()
+    wl = SMALL_MOE16.with_(name="rmx_moe16_dead", seed=75)
+    banks = dg.weight_banks(wl)
+    for (l, sub, kind), arr in banks.items():
+        if kind == dg.K_ROUTER:
+            arr[:, :, 3] = 0
+            arr[:, :, 7] = 0
+            arr[0] = 0
+    say("RankMixer experts with skips", wl)
+    ctx, _, ws = context(wl.name, wl, banks=banks)
+    x = dg.make_x(wl)
+    y = to_np(_stack(ctx, to_dev(wl, x), wl.B))
+    ref = orc.rankmixer_stack(x.astype(np.float64), wl, ws)
+    err = row_err(y, ref)
+    say("RankMixer experts with skips err", err)
+    drop(wl.name)
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name", ["rankmixer_d256", "rankmixer_d512", "rankmixer_moe_d256"])
 def test_full_stack_sampled_rows(name):
     require_gpu()
     wl = dg.RANKMIXER_WORKLOADS[name]

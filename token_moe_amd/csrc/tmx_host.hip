@@ -16,7 +16,7 @@ using namespace tmx;
 
 namespace {
 
-constexpr int NKINDS = 14;
+constexpr int NKINDS = 16;
 thread_local std::string g_create_error;
 
 struct Bank {
@@ -73,7 +73,9 @@ bool is_moe(const tmx_config& c) { return c.E > 0; }
 bool is_rmx(const tmx_config& c) { return c.block == TMX_BLOCK_RANKMIXER; }
 bool is_norm(int kind) { return kind == TMX_W_NORM_GAIN || kind == TMX_W_NORM_BIAS; }
 // kinds a context may go without: gains default to 1, biases to 0
-bool optional_kind(int kind) { return is_norm(kind) || kind == TMX_W_BIAS_UP || kind == TMX_W_BIAS_DOWN; }
+bool is_bias(int kind) {
+  return kind == TMX_W_BIAS_UP || kind == TMX_W_BIAS_DOWN || kind == TMX_W_EXP_BIAS_UP || kind == TMX_W_EXP_BIAS_DOWN;
+}
 
 // logical [G, K, N] view of a matrix bank; returns false for non-matrix kinds
 bool bank_dims(const tmx_config& c, int sub, int kind, int64_t* G, int* K, int* N) {
@@ -93,8 +95,11 @@ bool bank_dims(const tmx_config& c, int sub, int kind, int64_t* G, int* K, int* 
 bool kind_applies(const tmx_config& c, int sub, int kind) {
   if (is_rmx(c)) {
     if (is_norm(kind)) return true;
-    return sub == TMX_REVERT && (kind == TMX_W_UP || kind == TMX_W_DOWN || kind == TMX_W_BIAS_UP ||
-                                 kind == TMX_W_BIAS_DOWN);
+    if (sub != TMX_REVERT) return false;
+    if (is_moe(c))
+      return kind == TMX_W_ROUTER || kind == TMX_W_EXP_UP || kind == TMX_W_EXP_DOWN || kind == TMX_W_EXP_BIAS_UP ||
+             kind == TMX_W_EXP_BIAS_DOWN;
+    return kind == TMX_W_UP || kind == TMX_W_DOWN || kind == TMX_W_BIAS_UP || kind == TMX_W_BIAS_DOWN;
   }
   if (kind == TMX_W_NORM_GAIN) return true;
   if (is_moe(c)) return kind >= TMX_W_ROUTER && kind <= TMX_W_SH_DOWN;
@@ -105,6 +110,8 @@ size_t kind_elems(const tmx_config& c, int sub, int kind) {
   if (is_norm(kind)) return (size_t)width(c, sub);
   if (kind == TMX_W_BIAS_UP) return (size_t)positions(c, sub) * dense_hidden(c, sub);
   if (kind == TMX_W_BIAS_DOWN) return (size_t)positions(c, sub) * width(c, sub);
+  if (kind == TMX_W_EXP_BIAS_UP) return (size_t)positions(c, sub) * c.E * c.expert_hidden;
+  if (kind == TMX_W_EXP_BIAS_DOWN) return (size_t)positions(c, sub) * c.E * width(c, sub);
   int64_t G;
   int K, N;
   if (!bank_dims(c, sub, kind, &G, &K, &N)) return 0;
@@ -182,15 +189,22 @@ tmx_status validate_config(const tmx_config* cfg) {
       return fail(nullptr, TMX_ERR_INVALID_ARG, "RankMixer token mixing needs H == T (got H %d, T %d)", c.H, c.T);
     if (c.hidden_mix != 0 || c.inter_residual_gap != 0)
       return fail(nullptr, TMX_ERR_INVALID_ARG, "RankMixer blocks take hidden_mix = 0 and inter_residual_gap = 0");
-    if (c.hidden_rev < 1) return fail(nullptr, TMX_ERR_INVALID_ARG, "RankMixer needs hidden_rev (kD) >= 1");
-    if (c.E != 0) return fail(nullptr, TMX_ERR_UNSUPPORTED, "RankMixer blocks run dense (E = 0) in this build");
+    if (c.E == 0 && c.hidden_rev < 1) return fail(nullptr, TMX_ERR_INVALID_ARG, "RankMixer needs hidden_rev (kD) >= 1");
+    if (c.E > 0 && (c.hidden_rev != 0 || c.top_k != 0 || c.expert_hidden < 1))
+      return fail(nullptr, TMX_ERR_INVALID_ARG,
+                  "RankMixer ReLU-routed experts take hidden_rev = 0, top_k = 0 (the count of active experts varies) "
+                  "and expert_hidden >= 1");
     if (c.dtype != TMX_BF16) return fail(nullptr, TMX_ERR_UNSUPPORTED, "RankMixer blocks run in bf16 in this build");
     if (!rmx_width_supported(c.D))
       return fail(nullptr, TMX_ERR_UNSUPPORTED, "RankMixer path supports D = 256 or 512, got %d", c.D);
     if ((c.D / c.H) % 8 != 0)
       return fail(nullptr, TMX_ERR_UNSUPPORTED, "RankMixer path needs D/H %% 8 == 0, got %d", c.D / c.H);
-    if (c.hidden_rev % 128 != 0)
+    if (c.E == 0 && c.hidden_rev % 128 != 0)
       return fail(nullptr, TMX_ERR_UNSUPPORTED, "RankMixer path needs hidden_rev %% 128 == 0, got %d", c.hidden_rev);
+    if (c.E > 0 && !rmx_experts_supported(c.D, c.E, c.expert_hidden))
+      return fail(nullptr, TMX_ERR_UNSUPPORTED,
+                  "RankMixer experts need D = 256, E of 16 or 32 and expert_hidden %% 128 == 0 (got D %d, E %d, "
+                  "h_e %d)", c.D, c.E, c.expert_hidden);
     if ((int64_t)c.B_max * c.T * c.D > (int64_t)1 << 40)
       return fail(nullptr, TMX_ERR_INVALID_ARG, "B_max*T*D too large");
     return TMX_OK;
@@ -281,14 +295,21 @@ void set_row_tiles(MlpArgs& a, int mode, int sub, int W, int P, int B, int dh_by
 tmx_status run_rmx(tmx_ctx* c, int layer, int part, const void* x_in, void* x_out, int B, hipStream_t st) {
   const tmx_config& cfg = c->cfg;
   RmxArgs a{};
-  a.B = B; a.T = cfg.T; a.D = cfg.D; a.dh = cfg.D / cfg.H; a.hidden = cfg.hidden_rev; a.eps = cfg.eps;
+  a.B = B; a.T = cfg.T; a.D = cfg.D; a.dh = cfg.D / cfg.H; a.eps = cfg.eps;
+  a.E = cfg.E; a.h_e = cfg.expert_hidden;
+  a.hidden = cfg.E > 0 ? cfg.E * cfg.expert_hidden : cfg.hidden_rev;
   a.x = static_cast<const uint16_t*>(x_in);
   a.out = static_cast<uint16_t*>(x_out);
   auto f = [&](int sub, int k) { return static_cast<const float*>(bank(c, layer, sub, k).ptr); };
   auto h = [&](int k) { return static_cast<const uint16_t*>(bank(c, layer, TMX_REVERT, k).ptr); };
   a.g1 = f(TMX_MIX, TMX_W_NORM_GAIN); a.be1 = f(TMX_MIX, TMX_W_NORM_BIAS);
   a.g2 = f(TMX_REVERT, TMX_W_NORM_GAIN); a.be2 = f(TMX_REVERT, TMX_W_NORM_BIAS);
-  a.w1 = h(TMX_W_UP); a.w2 = h(TMX_W_DOWN); a.b1 = h(TMX_W_BIAS_UP); a.b2 = h(TMX_W_BIAS_DOWN);
+  if (cfg.E > 0) {
+    a.w1 = h(TMX_W_EXP_UP); a.w2 = h(TMX_W_EXP_DOWN); a.b1 = h(TMX_W_EXP_BIAS_UP); a.b2 = h(TMX_W_EXP_BIAS_DOWN);
+    a.wr = h(TMX_W_ROUTER);
+  } else {
+    a.w1 = h(TMX_W_UP); a.w2 = h(TMX_W_DOWN); a.b1 = h(TMX_W_BIAS_UP); a.b2 = h(TMX_W_BIAS_DOWN);
+  }
   return check_launch(c, launch_rmx(a, part, st), "RankMixer launch");
 }
 
@@ -457,16 +478,18 @@ tmx_status tmx_create(const tmx_config* cfg, int device, tmx_ctx** out) {
           b.loaded = true;
           continue;
         }
-        if (k == TMX_W_BIAS_UP || k == TMX_W_BIAS_DOWN) {
-          s = dev_alloc(c, &b.ptr, b.elems * es, "biases");
+        if (is_bias(k)) {
+          // the experts' second biases are stored packed and stacked twice
+          const size_t n = k == TMX_W_EXP_BIAS_DOWN ? 2 * b.elems : b.elems;
+          s = dev_alloc(c, &b.ptr, n * es, "biases");
           if (s != TMX_OK) return bail(s);
-          std::vector<uint16_t> zero(b.elems, 0);   // bf16 +0
-          if ((e = hipMemcpy(b.ptr, zero.data(), b.elems * es, hipMemcpyHostToDevice)) != hipSuccess)
+          std::vector<uint16_t> zero(n, 0);   // bf16 +0 (also as packed fragments)
+          if ((e = hipMemcpy(b.ptr, zero.data(), n * es, hipMemcpyHostToDevice)) != hipSuccess)
             return bail(fail(c, TMX_ERR_DEVICE, "bias init: %s", hipGetErrorString(e)));
           b.loaded = true;
           continue;
         }
-        if (is_rmx(C)) {   // W1 / W2, one fragment buffer each
+        if (is_rmx(C)) {   // W1 / W2 (router, experts' W1 / W2), one fragment buffer each
           if ((s = dev_alloc(c, &b.ptr, b.elems * es, "weights")) != TMX_OK) return bail(s);
           continue;
         }
@@ -569,7 +592,7 @@ tmx_status tmx_load_weights(tmx_ctx* c, int layer, int sub, int kind, const void
     return TMX_OK;
   }
 
-  if (C.dtype == TMX_F32 || kind == TMX_W_BIAS_UP || kind == TMX_W_BIAS_DOWN) {
+  if (C.dtype == TMX_F32 || kind == TMX_W_BIAS_UP || kind == TMX_W_BIAS_DOWN || kind == TMX_W_EXP_BIAS_UP) {
     e = hipMemcpyAsync(b.ptr, src, nbytes, src_dev ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return fail(c, TMX_ERR_DEVICE, "weight copy: %s", hipGetErrorString(e));
@@ -577,18 +600,28 @@ tmx_status tmx_load_weights(tmx_ctx* c, int layer, int sub, int kind, const void
     return TMX_OK;
   }
 
-  // bf16: stage on the device, then repack into MFMA fragments
+  // bf16: stage on the device, then repack into MFMA fragments (the experts'
+  // second biases staged twice per token: [T][2E][D])
+  const bool twice = kind == TMX_W_EXP_BIAS_DOWN;
   void* stage = nullptr;
-  e = hipMalloc(&stage, nbytes);
+  e = hipMalloc(&stage, twice ? 2 * nbytes : nbytes);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return fail(c, e == hipErrorOutOfMemory ? TMX_ERR_OOM : TMX_ERR_DEVICE, "staging buffer: %s",
                 hipGetErrorString(e));
   }
-  e = hipMemcpyAsync(stage, src, nbytes, src_dev ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, st);
-  int64_t G;
-  int K, N;
-  bank_dims(C, sub, kind, &G, &K, &N);
+  int64_t G = 0;
+  int K = 0, N = 0;
+  if (twice) {
+    const size_t row = (size_t)C.E * C.D * es;   // one token's [E][D]
+    for (int half = 0; half < 2 && e == hipSuccess; ++half)
+      e = hipMemcpy2DAsync(static_cast<char*>(stage) + half * row, 2 * row, src, row, row, C.T,
+                           src_dev ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, st);
+    G = C.T; K = 2 * C.E; N = C.D;
+  } else {
+    e = hipMemcpyAsync(stage, src, nbytes, src_dev ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, st);
+    bank_dims(C, sub, kind, &G, &K, &N);
+  }
   const bool gu = kind == TMX_W_UP || kind == TMX_W_GATE || kind == TMX_W_EXP_UP || kind == TMX_W_EXP_GATE ||
                   kind == TMX_W_SH_UP || kind == TMX_W_SH_GATE;
   const int which = (kind == TMX_W_UP || kind == TMX_W_EXP_UP || kind == TMX_W_SH_UP) ? 1 : 0;
@@ -600,8 +633,8 @@ tmx_status tmx_load_weights(tmx_ctx* c, int layer, int sub, int kind, const void
     e = launch_pack_mx(static_cast<const uint16_t*>(stage), dst, rec, (int)G, K, N, kind == TMX_W_DOWN ? 1 : 0, which,
                        st);
   } else if (e == hipSuccess && is_rmx(C))
-    e = launch_pack(static_cast<const uint16_t*>(stage), static_cast<uint16_t*>(b.ptr), (int)G, K, N, 2, 0,
-                    FRAG_32x32x16, st);
+    e = launch_pack(static_cast<const uint16_t*>(stage), static_cast<uint16_t*>(b.ptr), (int)G, K, N,
+                    kind == TMX_W_ROUTER ? 1 : 2, 0, kind == TMX_W_ROUTER ? FRAG_16x16x32 : FRAG_32x32x16, st);
   else if (e == hipSuccess)
     e = launch_pack(static_cast<const uint16_t*>(stage), static_cast<uint16_t*>(storage(c, layer, sub, kind).ptr),
                     (int)G, K, N, gu ? 0 : 1, which, kind == TMX_W_ROUTER ? FRAG_16x16x32 : FRAG_32x32x16, st);
@@ -683,7 +716,8 @@ tmx_status tmx_moe_route(tmx_ctx* c, int layer, int sub, const void* x, int B, i
                          void* stream) {
   if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
   const tmx_config& C = c->cfg;
-  if (!is_moe(C)) return fail(c, TMX_ERR_UNSUPPORTED, "tmx_moe_route needs an MoE context (E > 0)");
+  if (!is_moe(C) || is_rmx(C))
+    return fail(c, TMX_ERR_UNSUPPORTED, "tmx_moe_route needs a TokenMixer-Large MoE context (top-k softmax router)");
   tmx_status s;
   if (layer < 0 || layer >= C.L) return fail(c, TMX_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, C.L);
   if (sub != TMX_MIX && sub != TMX_REVERT) return fail(c, TMX_ERR_INVALID_ARG, "sublayer must be 0 or 1");

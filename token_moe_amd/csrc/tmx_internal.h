@@ -120,10 +120,15 @@ hipError_t launch_permute(const void* in, void* out, int B, int T, int D, int H,
 
 // RankMixer block (tmx_rankmixer.hip), bf16, H = T, D in {256, 512}:
 //   part 0: out = S = rho(LN_1(TokenMixing(x) + x))
-//   part 1: out = rho(LN_2(x + PFFN_t(x)))            (x = S)
+//   part 1: out = rho(LN_2(x + F_t(x)))               (x = S)
 //   part 2: both in one kernel
+// F_t is the token's FFN (E = 0) or its E ReLU-routed experts (D = 256,
+// E in {16, 32}): W1 / W2 / b1 then hold the experts end to end (hidden =
+// E * h_e), `wr` is the router ([T][D, E], 16x16x32 fragments, layout 1) and
+// b2 the experts' second biases stacked twice ([T][2E, D], layout 2).
 struct RmxArgs {
   int B, T, D, dh, hidden;
+  int E, h_e;
   float eps;
   const uint16_t* x;       // [B, T, D]
   uint16_t* out;           // [B, T, D]
@@ -134,9 +139,11 @@ struct RmxArgs {
   const uint16_t* w1;      // W1 [T][D, hidden] packed with layout 2 (32x32x16 fragments)
   const uint16_t* w2;      // W2 [T][hidden, D] packed with layout 2
   const uint16_t* b1;      // [T][hidden] bf16
-  const uint16_t* b2;      // [T][D] bf16
+  const uint16_t* b2;      // [T][D] bf16 (experts: packed, see above)
+  const uint16_t* wr;      // experts only: packed router
 };
 bool rmx_width_supported(int D);
+bool rmx_experts_supported(int D, int E, int h_e);
 hipError_t launch_rmx(const RmxArgs& a, int part, hipStream_t s);
 
 // fp32 path

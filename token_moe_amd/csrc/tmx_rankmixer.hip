@@ -28,7 +28,7 @@ constexpr int RMX_BM = 64;    // samples per workgroup
 constexpr int RMX_HC = 128;   // hidden units per chunk
 constexpr int RMX_NW = 4;     // waves per workgroup
 
-template <int D>
+template <int D, int EM = 0>
 struct RmxShape {
   static constexpr int EPL = D / 64;           // row elements per lane in a row pass
   static constexpr int SA = D + 8;             // LDS row stride of S (bf16 elements)
@@ -39,7 +39,12 @@ struct RmxShape {
   static constexpr int BYTES_S = RMX_BM * SA * 2;
   static constexpr int BYTES_U = RMX_BM * SU * 2;
   static constexpr int BYTES_RED = 2 * RMX_NW * RMX_BM * 4;
-  static constexpr int LDS = BYTES_S + 2 * BYTES_U + BYTES_RED;
+  // ReLU-routed experts (EM experts per token): each row's gates as bf16
+  // hi | lo pairs (g = hi + lo to 16 significant bits), [64][2 EM + 8], and
+  // one "any row active" flag per expert
+  static constexpr int SG = 2 * EM + 8;
+  static constexpr int BYTES_G = EM ? RMX_BM * SG * 2 + EM * 4 : 0;
+  static constexpr int LDS = BYTES_S + 2 * BYTES_U + BYTES_RED + BYTES_G;
 };
 
 template <int N> struct VecOf;
@@ -152,17 +157,22 @@ __global__ __launch_bounds__(256) void rmx_ln1_kernel(RmxArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// the block (FUSED: from X) or its FFN sub-layer (from S)
+// the block (FUSED: from X) or its FFN sub-layer (from S); EM > 0: the FFN is
+// EM ReLU-routed experts of hidden a.h_e per token (D = 256 only)
 // ---------------------------------------------------------------------------
-template <int D, bool FUSED>
+template <int D, bool FUSED, int EM>
 __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArgs a) {
-  typedef RmxShape<D> S_;
+  static_assert(EM == 0 || D == 256, "the expert path is laid out for D = 256");
+  typedef RmxShape<D, EM> S_;
   constexpr int EPL = S_::EPL, SA = S_::SA, SU = S_::SU, KT1 = S_::KT1, NT2 = S_::NT2, KT2 = S_::KT2;
   typedef typename VecOf<EPL>::type Vec;
   __shared__ __attribute__((aligned(16))) uint8_t smem[S_::LDS];
   uint16_t* const ss = reinterpret_cast<uint16_t*>(smem);                          // [64][SA]
   uint16_t* const us = reinterpret_cast<uint16_t*>(smem + S_::BYTES_S);            // [2][64][SU]
   float* const red = reinterpret_cast<float*>(smem + S_::BYTES_S + 2 * S_::BYTES_U);  // [2][NW][64]
+  uint16_t* const ug = reinterpret_cast<uint16_t*>(smem + S_::BYTES_S + 2 * S_::BYTES_U + S_::BYTES_RED);
+  int* const active = reinterpret_cast<int*>(smem + S_::BYTES_S + 2 * S_::BYTES_U + S_::BYTES_RED +
+                                             RMX_BM * S_::SG * 2);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -208,10 +218,43 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
   }
   __syncthreads();
 
-  const int KB1 = D / 16;                 // K fragments of a W1 column tile
-  const int KB2 = a.hidden / 16;          // K fragments of a W2 column tile
+  if constexpr (EM > 0) {
+    // router logits of the wave's 16 rows: Lt (experts x rows) = Wr^T S^T on
+    // 16x16x32 MFMAs (router fragments as A, S rows as B); gates ReLU(L)
+    // stored as bf16 hi | lo pairs
+    const int r16 = lane & 15, q16 = lane >> 4;
+#pragma unroll
+    for (int nb = 0; nb < EM / 16; ++nb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb) {
+        const uint4 wa = ld16(a.wr + (((size_t)t * (D / 32) + kb) * (EM / 16) + nb) * FRAG_ELEMS + lane * 8);
+        const uint4 sb = *reinterpret_cast<const uint4*>(&ss[(w * 16 + r16) * SA + kb * 32 + 8 * q16]);
+        acc = mfma16x16x32(as_bf16x8(wa), as_bf16x8(sb), acc);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int e = nb * 16 + 4 * q16 + v;
+        const float g = fmaxf(acc[v], 0.f);
+        const uint16_t gh = f2bf(g);
+        ug[(w * 16 + r16) * S_::SG + e] = gh;
+        ug[(w * 16 + r16) * S_::SG + EM + e] = f2bf(g - bf2f(gh));
+      }
+    }
+    __syncthreads();
+    if (tid < EM) {
+      int any = 0;
+      for (int r = 0; r < RMX_BM; ++r) any |= ug[r * S_::SG + tid] | ug[r * S_::SG + EM + tid];
+      active[tid] = any != 0;
+    }
+    __syncthreads();
+  }
+
+  const int KB1 = D / 16;                                   // K fragments of a W1 column tile
+  const int NE = EM > 0 ? EM : 1;                           // experts of the token
+  const int HE = EM > 0 ? a.h_e : a.hidden;                 // hidden units per expert
+  const int KB2 = HE / 16;                                  // K fragments of one expert's W2 column tile
   const uint16_t* const w1t = a.w1 + (size_t)t * (a.hidden / 32) * KB1 * FRAG_ELEMS;
-  const uint16_t* const w2t = a.w2 + (size_t)t * (D / 32) * KB2 * FRAG_ELEMS;
   const uint16_t* const b1t = a.b1 + (size_t)t * a.hidden;
 
   f32x16 acc2[2][NT2];
@@ -232,8 +275,19 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
 #pragma unroll
     for (int i = 0; i < 16; ++i) wf1[i] = w1frag(0, i);
   }
+  int ex = 0;   // chunks run so far: the hidden buffer alternates with it
   for (int c = 0; c < nchunks; ++c) {
-    uint16_t* const ub = us + (c & 1) * (RMX_BM * SU);
+    // expert of this chunk (hidden units [128 c, 128 c + 128) of the token's
+    // experts laid end to end); a chunk whose expert no row of the tile
+    // activates is skipped by the whole workgroup
+    const int je = EM > 0 ? (c * RMX_HC) / HE : 0;
+    if constexpr (EM > 0) {
+      if (!active[je]) continue;
+    }
+    const int kl0 = (c * RMX_HC - je * HE) / 16;            // first K fragment of the chunk in its expert
+    const uint16_t* const w2t = a.w2 + ((size_t)t * NE + je) * (D / 32) * KB2 * FRAG_ELEMS;
+    uint16_t* const ub = us + (ex & 1) * (RMX_BM * SU);
+    ++ex;
     if constexpr (D <= 256) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) wf1[i] = w1frag(c, i);
@@ -278,7 +332,7 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
     for (int k = 0; k < KG; ++k)
 #pragma unroll
       for (int j = 0; j < NT2; ++j)
-        wf2[k][j] = ld16(w2t + ((size_t)(w * NT2 + j) * KB2 + c * KT2 + k) * FRAG_ELEMS + lane * 8);
+        wf2[k][j] = ld16(w2t + ((size_t)(w * NT2 + j) * KB2 + kl0 + k) * FRAG_ELEMS + lane * 8);
     // ---- bias + GELU, rounded hidden chunk into LDS --------------------------
     // lane holds hidden units 8q + 4 hi + r (q, r < 4) of rows l32 and 32 + l32
     {
@@ -294,9 +348,14 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
         }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
+          // the row's gate of this chunk's expert scales the hidden (1 for the
+          // plain FFN); the gated value is what gets rounded
+          float gm = 1.f;
+          if constexpr (EM > 0)
+            gm = bf2f(ug[(m * 32 + l32) * S_::SG + je]) + bf2f(ug[(m * 32 + l32) * S_::SG + EM + je]);
           uint2 o;
-          o.x = pack_bf16x2(gelu_erf(acc1[m][4 * q] + bias[0]), gelu_erf(acc1[m][4 * q + 1] + bias[1]));
-          o.y = pack_bf16x2(gelu_erf(acc1[m][4 * q + 2] + bias[2]), gelu_erf(acc1[m][4 * q + 3] + bias[3]));
+          o.x = pack_bf16x2(gm * gelu_erf(acc1[m][4 * q] + bias[0]), gm * gelu_erf(acc1[m][4 * q + 1] + bias[1]));
+          o.y = pack_bf16x2(gm * gelu_erf(acc1[m][4 * q + 2] + bias[2]), gm * gelu_erf(acc1[m][4 * q + 3] + bias[3]));
           *reinterpret_cast<uint2*>(&ub[(m * 32 + l32) * SU + w * 32 + 8 * q + 4 * hi]) = o;
         }
       }
@@ -322,7 +381,7 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
         for (int j = 0; j < NT2; ++j) {
           wf[k][j] = wf2[k][j];
           if (k0 + KG < KT2)   // the next group's fragments (compile-time condition)
-            wf2[k][j] = ld16(w2t + ((size_t)(w * NT2 + j) * KB2 + c * KT2 + k0 + KG + k) * FRAG_ELEMS + lane * 8);
+            wf2[k][j] = ld16(w2t + ((size_t)(w * NT2 + j) * KB2 + kl0 + k0 + KG + k) * FRAG_ELEMS + lane * 8);
         }
 #pragma unroll
       for (int k = 0; k < KG; ++k) {
@@ -340,6 +399,24 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
     // write orders this chunk's reads before the buffer is written again
   }
 
+  if constexpr (EM > 0) {
+    // the experts' second biases, each scaled by its gate: one more GEMM2
+    // step with the gates (hi | lo halves as 2 EM K rows) as the hidden and
+    // the biases, stacked twice, as W2
+#pragma unroll
+    for (int k = 0; k < 2 * EM / 16; ++k) {
+      const uint4 u0 = *reinterpret_cast<const uint4*>(&ug[l32 * S_::SG + k * 16 + 8 * hi]);
+      const uint4 u1 = *reinterpret_cast<const uint4*>(&ug[(32 + l32) * S_::SG + k * 16 + 8 * hi]);
+#pragma unroll
+      for (int j = 0; j < NT2; ++j) {
+        const uint4 bf =
+            ld16(a.b2 + (((size_t)t * (D / 32) + w * NT2 + j) * (2 * EM / 16) + k) * FRAG_ELEMS + lane * 8);
+        acc2[0][j] = mma(bf, u0, acc2[0][j]);
+        acc2[1][j] = mma(bf, u1, acc2[1][j]);
+      }
+    }
+  }
+
   // ---- epilogue: y = acc + b2 + S; LayerNorm; rho -----------------------------
   // lane holds columns col(j, q) + r, col = 32 (w NT2 + j) + 8q + 4 hi, rows
   // l32 (m = 0) and 32 + l32 (m = 1)
@@ -350,8 +427,8 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int col = 32 * (w * NT2 + j) + 8 * q + 4 * hi;
-      float bias[4];
-      unpack_row<4>(*reinterpret_cast<const uint2*>(b2t + col), bias);
+      float bias[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (EM == 0) unpack_row<4>(*reinterpret_cast<const uint2*>(b2t + col), bias);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         float sv[4];
@@ -427,17 +504,31 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
   }
 }
 
+template <int D, int EM>
+void launch_block(const RmxArgs& a, int part, hipStream_t s) {
+  const int tiles = a.T * ((a.B + RMX_BM - 1) / RMX_BM);
+  if (part == 1)
+    hipLaunchKernelGGL((rmx_block_kernel<D, false, EM>), dim3(tiles), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((rmx_block_kernel<D, true, EM>), dim3(tiles), dim3(256), 0, s, a);
+}
+
 template <int D>
 hipError_t launch_d(const RmxArgs& a, int part, hipStream_t s) {
   if (part == 0) {
     const int64_t rows = (int64_t)a.B * a.T;
     hipLaunchKernelGGL(rmx_ln1_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
-  } else {
-    const int tiles = a.T * ((a.B + RMX_BM - 1) / RMX_BM);
-    if (part == 1)
-      hipLaunchKernelGGL((rmx_block_kernel<D, false>), dim3(tiles), dim3(256), 0, s, a);
+  } else if (a.E == 0) {
+    launch_block<D, 0>(a, part, s);
+  } else if constexpr (D == 256) {
+    if (a.E == 16)
+      launch_block<D, 16>(a, part, s);
+    else if (a.E == 32)
+      launch_block<D, 32>(a, part, s);
     else
-      hipLaunchKernelGGL((rmx_block_kernel<D, true>), dim3(tiles), dim3(256), 0, s, a);
+      return hipErrorInvalidValue;
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -445,6 +536,7 @@ hipError_t launch_d(const RmxArgs& a, int part, hipStream_t s) {
 }  // namespace
 
 bool rmx_width_supported(int D) { return D == 256 || D == 512; }
+bool rmx_experts_supported(int D, int E, int h_e) { return D == 256 && (E == 16 || E == 32) && h_e % RMX_HC == 0; }
 
 hipError_t launch_rmx(const RmxArgs& a, int part, hipStream_t s) {
   switch (a.D) {
