@@ -208,11 +208,30 @@ def main(argv=None):
         # so one launch takes the stack's event-timed time / L
         kms = time_launches(lambda: ctx.block_stack_forward(xd, yd, wl.B, sp), args.kernel_reps, stream) / wl.L
         kfl = float(orc.rankmixer_flops_per_sample(wl) // wl.L * wl.B)
+        if wl.moe:
+            # ReLU-routed experts: only the experts a row activates are the
+            # method's work. The share of positive gates is measured on the
+            # first block's router (outside the timed region, torch matmuls
+            # in fp32 on the library's own S); the kernel itself evaluates
+            # every expert that some row of its 64-row tile activates.
+            s_dev = torch.empty_like(xd)
+            ctx.sublayer_forward(0, 0, xd, None, None, s_dev, wl.B, sp)
+            wr = runner.host_tensor(wl, banks[(1, 1, dg.K_ROUTER)]).cuda().float()       # [T, D, E]
+            logits = torch.bmm(s_dev.float().transpose(0, 1).contiguous(), wr)          # [T, B, E]
+            active = float((logits > 0).float().mean().item())
+            per_row_expert = 2.0 * 2 * wl.D * wl.expert_hidden
+            executed = kfl
+            kfl = wl.B * wl.T * (2.0 * wl.D * wl.E + active * wl.E * per_row_expert)
+            kernel["active_expert_frac"] = round(active, 4)
+            kernel["executed_flop_per_launch"] = executed
+            flops = kfl * wl.L
+            tflops = flops / (ms / 1e3) / 1e12
         achieved = kfl / (kms / 1e3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                     "traffic": measured_traffic(wl.name, RMX_COUNTERS_FILE, RMX_KERNEL_SOURCES),
-                    "kernel": f"rmx_block_kernel<{wl.D}, fused>", "flop_per_launch": kfl,
+                    "kernel": f"rmx_block_kernel<{wl.D}, fused{f', {wl.E} experts' if wl.moe else ''}>",
+                    "flop_per_launch": kfl,
                     "launch_ms": round(kms, 5)}
         kernel["rmx_block_ms"] = round(kms, 5)
         log(f"fused RankMixer block kernel: {kms:.4f} ms/launch, {achieved:.1f} TFLOP/s")
