@@ -300,7 +300,7 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
       return *reinterpret_cast<const uint2*>(b1t + c * RMX_HC + w * 32 + 4 * hi + 8 * q);
     };
     uint2 bq[4];
-    if constexpr (D <= 256) {
+    if constexpr (D <= 256 && EM == 0) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) bq[q] = load_b1(q);
     }
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float bias[4];
-        if constexpr (D <= 256) {
+        if constexpr (D <= 256 && EM == 0) {
           unpack_row<4>(bq[q], bias);
         } else {
           const int hb = c * RMX_HC + w * 32 + 4 * hi;
