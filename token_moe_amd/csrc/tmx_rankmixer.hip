@@ -271,9 +271,17 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
     return ld16(w1t + ((size_t)(c * RMX_NW + w) * KB1 + k) * FRAG_ELEMS + lane * 8);
   };
   uint4 wf1[16];   // the next GEMM1 group
+  // D = 256 without experts: the first half of a chunk's W1 group is loaded
+  // during the previous chunk's GEMM2 (32 registers; the whole group, 64,
+  // costs more than it hides), the second half at the chunk's top
+  constexpr bool HALF_PF = D <= 256 && EM == 0;
   if constexpr (D > 256) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) wf1[i] = w1frag(0, i);
+  }
+  if constexpr (HALF_PF) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wf1[i] = w1frag(0, i);
   }
   int ex = 0;   // chunks run so far: the hidden buffer alternates with it
   for (int c = 0; c < nchunks; ++c) {
@@ -288,7 +296,10 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
     const uint16_t* const w2t = a.w2 + ((size_t)t * NE + je) * (D / 32) * KB2 * FRAG_ELEMS;
     uint16_t* const ub = us + (ex & 1) * (RMX_BM * SU);
     ++ex;
-    if constexpr (D <= 256) {
+    if constexpr (HALF_PF) {
+#pragma unroll
+      for (int i = 8; i < 16; ++i) wf1[i] = w1frag(c, i);
+    } else if constexpr (D <= 256) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) wf1[i] = w1frag(c, i);
     }
@@ -370,6 +381,11 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
       const int cn = c + 1 < nchunks ? c + 1 : c;
 #pragma unroll
       for (int i = 0; i < 16; ++i) wf1[i] = w1frag(cn, i);
+    }
+    if constexpr (HALF_PF) {
+      const int cn = c + 1 < nchunks ? c + 1 : c;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wf1[i] = w1frag(cn, i);
     }
     // ---- GEMM2: output column tiles w*NT2 + j, K = this chunk ----------------
 #pragma unroll
