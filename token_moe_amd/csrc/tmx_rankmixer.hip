@@ -1,19 +1,25 @@
 // tmx_rankmixer.hip -- the RankMixer block on gfx950 (fun-rec chapter 7.4.0
 // block equations; 7.4.1 token mixing with H = T as the reproduction guide's
-// section 5 requires; 7.4.2 per-token FFN with biases):
+// section 5 requires; 7.4.2 per-token FFN with biases; 7.4.3 ReLU routing):
 //
 //   S      = rho(LN_1(TokenMixing(X) + X))
 //   X_next = rho(LN_2(S + rho(GELU(S W1_t + b1_t)) W2_t + b2_t))
 //
+// or, with E ReLU-routed experts per token (inference router),
+//   X_next = rho(LN_2(S + sum_j [rho(G_j GELU(S W1_tj + b1_tj)) W2_tj + G_j b2_tj])),
+//   G = ReLU(S Wr_t).
+//
 // One kernel per block. A workgroup owns 64 samples of one token t:
 //  * prologue: each wave forms 16 rows of TokenMixing(X) + X straight from X
 //    (the mixing map folded into the loads), LayerNorm in fp32, S rounded to
-//    bf16 into LDS -- S is both the FFN input and its residual;
+//    bf16 into LDS -- S is both the FFN input and its residual; with experts
+//    the router logits and gates follow;
 //  * per hidden chunk of 128: GEMM1 (W1 fragments as the MFMA A operand, S
 //    rows as B, so each lane's accumulators hold 4 consecutive hidden units
-//    of one row), bias + exact GELU, the rounded chunk into LDS; GEMM2 the
-//    same way round (W2 fragments as A, the hidden chunk as B) accumulating
-//    the token's whole output row set in registers;
+//    of one row), bias + GELU (erf by a published rational approximation,
+//    below) [x gate], the rounded chunk into LDS; GEMM2 the same way round
+//    (W2 fragments as A, the hidden chunk as B) accumulating the token's
+//    whole output row set in registers;
 //  * epilogue: bias + residual S, LayerNorm statistics reduced across lanes
 //    and waves in fixed order, rounding, the tile staged through LDS and
 //    written with 16-byte row-contiguous stores.
