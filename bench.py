@@ -32,7 +32,7 @@ HBM_PEAK_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "mlp_dense_workload2_counters.md")
 KERNEL_SOURCES = ("token_moe_amd/csrc/tmx_mlp.hip", "token_moe_amd/csrc/tmx_device.h", "token_moe_amd/build.py",
                   "token_moe_amd/csrc/tmx_internal.h")
-RMX_COUNTERS_FILE = os.path.join(ROOT, "profiles", "rmx_block_rankmixer_d256_counters.md")
+RMX_COUNTERS_FILE = os.path.join(ROOT, "profiles", "rmx_block_{workload}_counters.md")
 RMX_KERNEL_SOURCES = ("token_moe_amd/csrc/tmx_rankmixer.hip", "token_moe_amd/csrc/tmx_device.h",
                       "token_moe_amd/build.py", "token_moe_amd/csrc/tmx_internal.h")
 
@@ -229,7 +229,8 @@ def main(argv=None):
         achieved = kfl / (kms / 1e3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                    "traffic": measured_traffic(wl.name, RMX_COUNTERS_FILE, RMX_KERNEL_SOURCES),
+                    "traffic": measured_traffic(wl.name, RMX_COUNTERS_FILE.format(workload=wl.name),
+                                                RMX_KERNEL_SOURCES),
                     "kernel": f"rmx_block_kernel<{wl.D}, fused{f', {wl.E} experts' if wl.moe else ''}>",
                     "flop_per_launch": kfl,
                     "launch_ms": round(kms, 5)}
