@@ -151,9 +151,9 @@ typedef struct tmx_ctx tmx_ctx;
  * 0, inter_residual_gap == 0, and either hidden_rev >= 1 (dense) or E > 0
  * with hidden_rev == 0, top_k == 0 and expert_hidden >= 1
  * (TMX_ERR_INVALID_ARG otherwise); this build runs them in bf16 with D of
- * 256 or 512, D/H % 8 == 0 and hidden_rev % 128 == 0, the experts at D =
- * 256 with E of 16 or 32 and expert_hidden % 128 == 0 (TMX_ERR_UNSUPPORTED
- * otherwise).
+ * 256 or 512, D/H % 8 == 0 and hidden_rev a multiple of 128 (D = 256) or
+ * 256 (D = 512), the experts at D = 256 with E of 16 or 32 and
+ * expert_hidden % 128 == 0 (TMX_ERR_UNSUPPORTED otherwise).
  * On error *out is set to NULL and nothing stays allocated. */
 tmx_status tmx_create(const tmx_config* cfg, int device, tmx_ctx** out);
 

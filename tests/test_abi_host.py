@@ -134,6 +134,7 @@ def _create(tmx, **kw):
     (dict(block=1, dtype=1, D=128, H=16, T=16, hidden_mix=0, hidden_rev=1024, inter_residual_gap=0), "UNSUPPORTED"),
     (dict(block=1, dtype=1, D=256, H=64, T=64, hidden_mix=0, hidden_rev=1024, inter_residual_gap=0), "UNSUPPORTED"),
     (dict(block=1, dtype=1, D=256, H=16, T=16, hidden_mix=0, hidden_rev=1000, inter_residual_gap=0), "UNSUPPORTED"),
+    (dict(block=1, dtype=1, D=512, H=16, T=16, hidden_mix=0, hidden_rev=384, inter_residual_gap=0), "UNSUPPORTED"),
     # RankMixer ReLU-routed experts: hidden_rev 0, top_k 0 (variable count); D 256, E 16 / 32, h_e % 128
     (dict(block=1, dtype=1, D=256, H=16, T=16, hidden_mix=0, hidden_rev=1024, inter_residual_gap=0, E=16, top_k=0,
           expert_hidden=128), "INVALID_ARG"),

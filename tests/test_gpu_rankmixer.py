@@ -15,8 +15,8 @@ pytestmark = pytest.mark.gpu
 # chunks, drawn LayerNorm gains and biases
 SMALL_D256 = dg.Workload("rmx_small_d256", B=300, T=8, H=8, D=256, L=2, hidden_rev=256, gap=0, eps=1e-5,
                          seed=71, down_scale=1.0, block=dg.BLOCK_RANKMIXER, random_norm=True)
-# width 512, 3 hidden chunks, ragged batch (130 = 2 * 64 + 2)
-SMALL_D512 = dg.Workload("rmx_small_d512", B=130, T=16, H=16, D=512, L=2, hidden_rev=384, gap=0, eps=1e-5,
+# width 512, 3 hidden chunks of 256, ragged batch (130 = 2 * 64 + 2)
+SMALL_D512 = dg.Workload("rmx_small_d512", B=130, T=16, H=16, D=512, L=2, hidden_rev=768, gap=0, eps=1e-5,
                          seed=72, down_scale=1.0, block=dg.BLOCK_RANKMIXER, random_norm=True)
 
 

@@ -199,8 +199,9 @@ tmx_status validate_config(const tmx_config* cfg) {
       return fail(nullptr, TMX_ERR_UNSUPPORTED, "RankMixer path supports D = 256 or 512, got %d", c.D);
     if ((c.D / c.H) % 8 != 0)
       return fail(nullptr, TMX_ERR_UNSUPPORTED, "RankMixer path needs D/H %% 8 == 0, got %d", c.D / c.H);
-    if (c.E == 0 && c.hidden_rev % 128 != 0)
-      return fail(nullptr, TMX_ERR_UNSUPPORTED, "RankMixer path needs hidden_rev %% 128 == 0, got %d", c.hidden_rev);
+    if (c.E == 0 && c.hidden_rev % rmx_hidden_multiple(c.D) != 0)
+      return fail(nullptr, TMX_ERR_UNSUPPORTED, "RankMixer path at D = %d needs hidden_rev %% %d == 0, got %d", c.D,
+                  rmx_hidden_multiple(c.D), c.hidden_rev);
     if (c.E > 0 && !rmx_experts_supported(c.D, c.E, c.expert_hidden))
       return fail(nullptr, TMX_ERR_UNSUPPORTED,
                   "RankMixer experts need D = 256, E of 16 or 32 and expert_hidden %% 128 == 0 (got D %d, E %d, "

@@ -143,6 +143,7 @@ struct RmxArgs {
   const uint16_t* wr;      // experts only: packed router
 };
 bool rmx_width_supported(int D);
+int rmx_hidden_multiple(int D);   // the dense FFN's hidden must be a multiple (the kernel's chunk)
 bool rmx_experts_supported(int D, int E, int h_e);
 hipError_t launch_rmx(const RmxArgs& a, int part, hipStream_t s);
 

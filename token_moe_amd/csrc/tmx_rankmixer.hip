@@ -31,20 +31,27 @@ namespace tmx {
 namespace {
 
 constexpr int RMX_BM = 64;    // samples per workgroup
-constexpr int RMX_HC = 128;   // hidden units per chunk
-constexpr int RMX_NW = 4;     // waves per workgroup
+// waves per workgroup and hidden units per chunk: 4 and 128 at D = 256 (two
+// workgroups per CU), 8 and 256 at D = 512 (one workgroup per CU, still two
+// waves per SIMD, each wave on a 64-column eighth); every wave owns 32 hidden
+// units of a chunk and 64 output columns
+constexpr int rmx_waves(int D) { return D / 64; }
+constexpr int rmx_chunk(int D) { return 32 * rmx_waves(D); }
+constexpr int RMX_HC = 128;   // chunk of the expert path (D = 256)
 
 template <int D, int EM = 0>
 struct RmxShape {
   static constexpr int EPL = D / 64;           // row elements per lane in a row pass
   static constexpr int SA = D + 8;             // LDS row stride of S (bf16 elements)
-  static constexpr int SU = RMX_HC + 8;        // LDS row stride of a hidden chunk
+  static constexpr int NW = rmx_waves(D);      // waves per workgroup
+  static constexpr int HC = rmx_chunk(D);      // hidden units per chunk
+  static constexpr int SU = HC + 8;            // LDS row stride of a hidden chunk
   static constexpr int KT1 = D / 16;           // GEMM1 K steps (over D)
-  static constexpr int NT2 = D / 32 / RMX_NW;  // GEMM2 output column tiles per wave
-  static constexpr int KT2 = RMX_HC / 16;      // GEMM2 K steps per chunk
+  static constexpr int NT2 = D / 32 / NW;      // GEMM2 output column tiles per wave
+  static constexpr int KT2 = HC / 16;          // GEMM2 K steps per chunk
   static constexpr int BYTES_S = RMX_BM * SA * 2;
   static constexpr int BYTES_U = RMX_BM * SU * 2;
-  static constexpr int BYTES_RED = 2 * RMX_NW * RMX_BM * 4;
+  static constexpr int BYTES_RED = 2 * NW * RMX_BM * 4;
   // ReLU-routed experts (EM experts per token): each row's gates as bf16
   // hi | lo pairs (g = hi + lo to 16 significant bits), [64][2 EM + 8], and
   // one "any row active" flag per expert
@@ -167,10 +174,12 @@ __global__ __launch_bounds__(256) void rmx_ln1_kernel(RmxArgs a) {
 // EM ReLU-routed experts of hidden a.h_e per token (D = 256 only)
 // ---------------------------------------------------------------------------
 template <int D, bool FUSED, int EM>
-__global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArgs a) {
+__global__ __launch_bounds__(64 * rmx_waves(D), D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArgs a) {
   static_assert(EM == 0 || D == 256, "the expert path is laid out for D = 256");
   typedef RmxShape<D, EM> S_;
   constexpr int EPL = S_::EPL, SA = S_::SA, SU = S_::SU, KT1 = S_::KT1, NT2 = S_::NT2, KT2 = S_::KT2;
+  constexpr int NW = S_::NW, HC = S_::HC, RPW = RMX_BM / NW;   // RPW: prologue rows per wave
+  static_assert(EM == 0 || HC == RMX_HC, "the expert path runs 128-unit chunks");
   typedef typename VecOf<EPL>::type Vec;
   __shared__ __attribute__((aligned(16))) uint8_t smem[S_::LDS];
   uint16_t* const ss = reinterpret_cast<uint16_t*>(smem);                          // [64][SA]
@@ -204,18 +213,18 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
       }
     }
 #pragma unroll
-    for (int i0 = 0; i0 < 16; i0 += 4) {
+    for (int i0 = 0; i0 < RPW; i0 += 4) {
       Vec xq[4], mq[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t b = b0 + w * 16 + i0 + i;
+        const int64_t b = b0 + w * RPW + i0 + i;
         const int64_t bb = b < a.B ? b : a.B - 1;   // rows past B: any valid row (not stored)
         xq[i] = *reinterpret_cast<const Vec*>(a.x + (bb * a.T + t) * D + c0);
         if constexpr (FUSED) mq[i] = *reinterpret_cast<const Vec*>(a.x + mix_offset<D>(bb, t, a.T, a.dh, c0));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = w * 16 + i0 + i;
+        const int r = w * RPW + i0 + i;
         Vec o = xq[i];
         if constexpr (FUSED) o = ln1_row<D>(xq[i], mq[i], g, be, a.eps);
         *reinterpret_cast<Vec*>(&ss[r * SA + c0]) = o;
@@ -271,10 +280,10 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc2[m][j][v] = 0.f;
 
-  const int nchunks = a.hidden / RMX_HC;
+  const int nchunks = a.hidden / HC;
   // W1 fragments of GEMM1 group (chunk c, K steps k0 .. k0 + 15) of this wave
   auto w1frag = [&](int c, int k) {
-    return ld16(w1t + ((size_t)(c * RMX_NW + w) * KB1 + k) * FRAG_ELEMS + lane * 8);
+    return ld16(w1t + ((size_t)(c * NW + w) * KB1 + k) * FRAG_ELEMS + lane * 8);
   };
   uint4 wf1[16];   // the next GEMM1 group
   // D = 256 without experts: the first half of a chunk's W1 group is loaded
@@ -294,11 +303,11 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
     // expert of this chunk (hidden units [128 c, 128 c + 128) of the token's
     // experts laid end to end); a chunk whose expert no row of the tile
     // activates is skipped by the whole workgroup
-    const int je = EM > 0 ? (c * RMX_HC) / HE : 0;
+    const int je = EM > 0 ? (c * HC) / HE : 0;
     if constexpr (EM > 0) {
       if (!active[je]) continue;
     }
-    const int kl0 = (c * RMX_HC - je * HE) / 16;            // first K fragment of the chunk in its expert
+    const int kl0 = (c * HC - je * HE) / 16;                // first K fragment of the chunk in its expert
     const uint16_t* const w2t = a.w2 + ((size_t)t * NE + je) * (D / 32) * KB2 * FRAG_ELEMS;
     uint16_t* const ub = us + (ex & 1) * (RMX_BM * SU);
     ++ex;
@@ -314,7 +323,7 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
     // in issue order); at D = 512 right where the GELU uses them, addressed
     // from one base (both measured faster than the alternatives)
     auto load_b1 = [&](int q) {
-      return *reinterpret_cast<const uint2*>(b1t + c * RMX_HC + w * 32 + 4 * hi + 8 * q);
+      return *reinterpret_cast<const uint2*>(b1t + c * HC + w * 32 + 4 * hi + 8 * q);
     };
     uint2 bq[4];
     if constexpr (D <= 256 && EM == 0) {
@@ -359,7 +368,7 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
         if constexpr (D <= 256 && EM == 0) {
           unpack_row<4>(bq[q], bias);
         } else {
-          const int hb = c * RMX_HC + w * 32 + 4 * hi;
+          const int hb = c * HC + w * 32 + 4 * hi;
           const uint2 bv = *reinterpret_cast<const uint2*>(b1t + hb + 8 * q);
           unpack_row<4>(bv, bias);
         }
@@ -469,15 +478,15 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const float p = part[m] + __shfl_xor(part[m], 32, 64);
-      if (hi == 0) red[(pass * RMX_NW + w) * RMX_BM + m * 32 + l32] = p;
+      if (hi == 0) red[(pass * NW + w) * RMX_BM + m * 32 + l32] = p;
     }
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const float* rr = red + pass * RMX_NW * RMX_BM + m * 32 + l32;
+      const float* rr = red + pass * NW * RMX_BM + m * 32 + l32;
       float tot = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < RMX_NW; ++ww) tot += rr[ww * RMX_BM];
+      for (int ww = 0; ww < NW; ++ww) tot += rr[ww * RMX_BM];
       if (pass == 0) {
         mean[m] = tot * (1.0f / D);
       } else {
@@ -517,7 +526,7 @@ __global__ __launch_bounds__(256, D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArg
     }
   __syncthreads();
   constexpr int SEG = D / 8;
-  for (int i = tid; i < RMX_BM * SEG; i += 256) {
+  for (int i = tid; i < RMX_BM * SEG; i += 64 * NW) {
     const int r = i / SEG, sg = i - r * SEG;
     const int64_t b = b0 + r;
     if (b < a.B)
@@ -530,9 +539,9 @@ template <int D, int EM>
 void launch_block(const RmxArgs& a, int part, hipStream_t s) {
   const int tiles = a.T * ((a.B + RMX_BM - 1) / RMX_BM);
   if (part == 1)
-    hipLaunchKernelGGL((rmx_block_kernel<D, false, EM>), dim3(tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((rmx_block_kernel<D, false, EM>), dim3(tiles), dim3(64 * rmx_waves(D)), 0, s, a);
   else
-    hipLaunchKernelGGL((rmx_block_kernel<D, true, EM>), dim3(tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((rmx_block_kernel<D, true, EM>), dim3(tiles), dim3(64 * rmx_waves(D)), 0, s, a);
 }
 
 template <int D>
@@ -558,6 +567,7 @@ hipError_t launch_d(const RmxArgs& a, int part, hipStream_t s) {
 }  // namespace
 
 bool rmx_width_supported(int D) { return D == 256 || D == 512; }
+int rmx_hidden_multiple(int D) { return rmx_chunk(D); }
 bool rmx_experts_supported(int D, int E, int h_e) { return D == 256 && (E == 16 || E == 32) && h_e % RMX_HC == 0; }
 
 hipError_t launch_rmx(const RmxArgs& a, int part, hipStream_t s) {
