@@ -26,8 +26,14 @@ SMALL_MOE16 = dg.Workload("rmx_small_moe16", B=300, T=8, H=8, D=256, L=2, E=16, 
                           eps=1e-5, seed=73, down_scale=1.0, block=dg.BLOCK_RANKMIXER, random_norm=True)
 SMALL_MOE32 = dg.Workload("rmx_small_moe32", B=130, T=16, H=16, D=256, L=2, E=32, expert_hidden=128, gap=0,
                           eps=1e-5, seed=74, down_scale=1.0, block=dg.BLOCK_RANKMIXER, random_norm=True)
-SMALL = [SMALL_D256, SMALL_D512, SMALL_MOE16, SMALL_MOE32]
-SMALL_IDS = ["d256", "d512", "moe16", "moe32"]
+# one token (T = H = 1): token mixing is the identity and S = LN_1(2 X); a
+# grid of two tiles (not a multiple of 8: tiles in launch order)
+SMALL_T1 = dg.Workload("rmx_small_t1", B=100, T=1, H=1, D=256, L=2, hidden_rev=256, gap=0, eps=1e-5,
+                       seed=76, down_scale=1.0, block=dg.BLOCK_RANKMIXER, random_norm=True)
+SMALL_T1_MOE = dg.Workload("rmx_small_t1_moe", B=100, T=1, H=1, D=256, L=2, E=16, expert_hidden=128, gap=0,
+                           eps=1e-5, seed=77, down_scale=1.0, block=dg.BLOCK_RANKMIXER, random_norm=True)
+SMALL = [SMALL_D256, SMALL_D512, SMALL_MOE16, SMALL_MOE32, SMALL_T1, SMALL_T1_MOE]
+SMALL_IDS = ["d256", "d512", "moe16", "moe32", "t1", "t1_moe"]
 
 
 def _stack(ctx, x_dev, B):
@@ -161,6 +167,10 @@ def test_state_and_kind_errors():
     for sub, kind in ((0, dg.K_UP), (1, dg.K_GATE), (1, dg.K_ROUTER)):
         with pytest.raises(tmx.TmxError) as e:
             ctx.load_weights(0, sub, kind, t.data_ptr(), t.numel() * 2)
+        assert e.value.status == tmx.TMX_ERR_INVALID_ARG
+    for B in (0, wl.B + 1):
+        with pytest.raises(tmx.TmxError) as e:
+            ctx.block_stack_forward(x, y, B, stream())
         assert e.value.status == tmx.TMX_ERR_INVALID_ARG
     with pytest.raises(tmx.TmxError) as e:          # a residual is not an input here
         ctx.sublayer_forward(0, 1, x, x, None, y, wl.B, stream())
