@@ -215,6 +215,15 @@ tmx_status tmx_sublayer_forward(tmx_ctx* ctx, int layer, int sublayer,
                                 const void* extra, void* x_out, int B,
                                 void* stream);
 
+/* The ReLU gates of one RankMixer block's experts (fun-rec chapter 7.4.3,
+ * inference router): s is that block's FFN-half input S in block layout
+ * [B, T, D] (device), gates [B, T, E] float32 (device) receives
+ * ReLU(s_t Wr_t) per sample and token, as the block kernel applies them
+ * (computed in fp32 from the bf16 operands, carried to 16 significant
+ * bits).  TMX_ERR_UNSUPPORTED unless the context is a RankMixer one with
+ * E > 0; TMX_ERR_STATE if that layer's router was never loaded. */
+tmx_status tmx_relu_route(tmx_ctx* ctx, int layer, const void* s, int B, float* gates, void* stream);
+
 /* Apply Mix (inverse = 0: out [B, H, T*D/H]) or Revert (inverse = 1:
  * in [B, H, T*D/H] -> out [B, T, D]) with the same device index code the
  * sub-layer kernels use; bit-exact data movement (Eq. 9-11, 13-15). */

@@ -175,6 +175,7 @@ def test_null_context_calls(tmx):
     assert lib.tmx_moe_route(None, 0, 0, None, 1, None, None, None) == tmx.TMX_ERR_INVALID_ARG
     assert lib.tmx_sublayer_forward(None, 0, 0, None, None, None, None, 1, None) == tmx.TMX_ERR_INVALID_ARG
     assert lib.tmx_debug_permute(None, None, None, 1, 0, None) == tmx.TMX_ERR_INVALID_ARG
+    assert lib.tmx_relu_route(None, 0, None, 1, None, None) == tmx.TMX_ERR_INVALID_ARG
     assert lib.tmx_last_error(None)
 
 

@@ -112,6 +112,37 @@ def test_full_batch_halves_teacher_forced(name):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("key", ["rankmixer_moe_d256", "moe32"])
+def test_relu_gates_teacher_forced_all_rows(key):
+    """The gates the expert kernel applies (tmx_relu_route on the GPU's own S)
+    against ReLU(S Wr_t) in fp64 on every row: values within the fp32
+    accumulation and 16-bit carry (1e-4 absolute + 2^-14 relative), and the
+    active set exact wherever the oracle's logit is farther than 1e-4 from 0
+    (a logit inside that band may fall on either side)."""
+    require_gpu()
+    import torch
+    wl = dg.RANKMIXER_WORKLOADS[key] if key in dg.RANKMIXER_WORKLOADS else SMALL_MOE32
+    ctx, banks, ws = context(wl.name, wl)
+    xd = to_dev(wl, dg.make_x(wl))
+    s = torch.empty_like(xd)
+    ctx.sublayer_forward(0, 0, xd, None, None, s, wl.B, stream())
+    gates = torch.empty((wl.B, wl.T, wl.E), dtype=torch.float32, device="cuda")
+    ctx.relu_route(0, s, wl.B, gates, stream())
+    torch.cuda.synchronize()
+    s_np, g = to_np(s), gates.cpu().numpy().astype(np.float64)
+    worst, band = 0.0, 0
+    for t in range(wl.T):
+        wr = ws(1, 1, dg.K_ROUTER, t)
+        logits = s_np[:, t] @ wr
+        ref = orc.relu_route(s_np[:, t], wr)
+        worst = max(worst, float(np.max(np.abs(g[:, t] - ref) - 2.0 ** -14 * ref)))
+        sure = np.abs(logits) > 1e-4
+        band += int((~sure).sum())
+        assert np.array_equal((g[:, t] > 0)[sure], (ref > 0)[sure])
+    say("relu gates", key, "worst excess", worst, "band entries", band)
+    assert worst <= 1e-4
+
+
 def test_skipped_experts_and_silent_token():
     """Experts 3 and 7 never activate (zero router columns, so every tile
     skips them) and token 0's router is zero (every chunk skipped: its output
@@ -178,5 +209,8 @@ def test_state_and_kind_errors():
     with pytest.raises(tmx.TmxError) as e:
         ctx.moe_route(0, 0, x, wl.B, torch.empty(1, dtype=torch.int32, device="cuda"),
                       torch.empty(1, device="cuda"), stream())
+    assert e.value.status == tmx.TMX_ERR_UNSUPPORTED
+    with pytest.raises(tmx.TmxError) as e:          # dense RankMixer: no router
+        ctx.relu_route(0, x, wl.B, torch.empty(1, device="cuda"), stream())
     assert e.value.status == tmx.TMX_ERR_UNSUPPORTED
     ctx.close()

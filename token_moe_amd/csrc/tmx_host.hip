@@ -292,8 +292,9 @@ void set_row_tiles(MlpArgs& a, int mode, int sub, int W, int P, int B, int dh_by
 }
 
 // RankMixer: part 0 = the token-mixing half (S), 1 = the FFN half from S,
-// 2 = the whole block in one kernel
-tmx_status run_rmx(tmx_ctx* c, int layer, int part, const void* x_in, void* x_out, int B, hipStream_t st) {
+// 2 = the whole block in one kernel, 3 = the experts' gates from S
+tmx_status run_rmx(tmx_ctx* c, int layer, int part, const void* x_in, void* x_out, int B, hipStream_t st,
+                   float* gates = nullptr) {
   const tmx_config& cfg = c->cfg;
   RmxArgs a{};
   a.B = B; a.T = cfg.T; a.D = cfg.D; a.dh = cfg.D / cfg.H; a.eps = cfg.eps;
@@ -301,6 +302,7 @@ tmx_status run_rmx(tmx_ctx* c, int layer, int part, const void* x_in, void* x_ou
   a.hidden = cfg.E > 0 ? cfg.E * cfg.expert_hidden : cfg.hidden_rev;
   a.x = static_cast<const uint16_t*>(x_in);
   a.out = static_cast<uint16_t*>(x_out);
+  a.gates = gates;
   auto f = [&](int sub, int k) { return static_cast<const float*>(bank(c, layer, sub, k).ptr); };
   auto h = [&](int k) { return static_cast<const uint16_t*>(bank(c, layer, TMX_REVERT, k).ptr); };
   a.g1 = f(TMX_MIX, TMX_W_NORM_GAIN); a.be1 = f(TMX_MIX, TMX_W_NORM_BIAS);
@@ -747,6 +749,22 @@ tmx_status tmx_moe_route(tmx_ctx* c, int layer, int sub, const void* x, int B, i
   r.wr = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_ROUTER).ptr);
   r.xhat = nullptr; r.idx = idx; r.gate = gate;
   return check_launch(c, launch_norm_route(W, r, st), "router launch");
+}
+
+tmx_status tmx_relu_route(tmx_ctx* c, int layer, const void* s, int B, float* gates, void* stream) {
+  if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
+  const tmx_config& C = c->cfg;
+  if (!is_rmx(C) || !is_moe(C))
+    return fail(c, TMX_ERR_UNSUPPORTED, "tmx_relu_route needs a RankMixer context with ReLU-routed experts");
+  tmx_status st;
+  if (layer < 0 || layer >= C.L) return fail(c, TMX_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, C.L);
+  if ((st = check_B(c, B)) != TMX_OK) return st;
+  if ((st = check_act(c, s, "s")) != TMX_OK) return st;
+  if (!gates) return fail(c, TMX_ERR_INVALID_ARG, "gates is NULL");
+  if (!bank(c, layer, TMX_REVERT, TMX_W_ROUTER).loaded)
+    return fail(c, TMX_ERR_STATE, "router of layer %d is not loaded", layer);
+  (void)hipSetDevice(c->device);
+  return run_rmx(c, layer, 3, s, nullptr, B, as_stream(stream), gates);
 }
 
 tmx_status tmx_debug_permute(tmx_ctx* c, const void* in, void* out, int B, int inverse, void* stream) {

@@ -122,6 +122,8 @@ hipError_t launch_permute(const void* in, void* out, int B, int T, int D, int H,
 //   part 0: out = S = rho(LN_1(TokenMixing(x) + x))
 //   part 1: out = rho(LN_2(x + F_t(x)))               (x = S)
 //   part 2: both in one kernel
+//   part 3: experts only: the gates ReLU(x Wr_t) the FFN half uses, to
+//           `gates` [B][T][E] fp32 (x = S)
 // F_t is the token's FFN (E = 0) or its E ReLU-routed experts (D = 256,
 // E in {16, 32}): W1 / W2 / b1 then hold the experts end to end (hidden =
 // E * h_e), `wr` is the router ([T][D, E], 16x16x32 fragments, layout 1) and
@@ -141,6 +143,7 @@ struct RmxArgs {
   const uint16_t* b1;      // [T][hidden] bf16
   const uint16_t* b2;      // [T][D] bf16 (experts: packed, see above)
   const uint16_t* wr;      // experts only: packed router
+  float* gates;            // part 3 only
 };
 bool rmx_width_supported(int D);
 int rmx_hidden_multiple(int D);   // the dense FFN's hidden must be a multiple (the kernel's chunk)

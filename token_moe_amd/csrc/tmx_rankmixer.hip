@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256) void rmx_ln1_kernel(RmxArgs a) {
 // the block (FUSED: from X) or its FFN sub-layer (from S); EM > 0: the FFN is
 // EM ReLU-routed experts of hidden a.h_e per token (D = 256 only)
 // ---------------------------------------------------------------------------
-template <int D, bool FUSED, int EM>
+template <int D, bool FUSED, int EM, bool ROUTE = false>
 __global__ __launch_bounds__(64 * rmx_waves(D), D <= 256 ? 2 : 1) void rmx_block_kernel(RmxArgs a) {
   static_assert(EM == 0 || D == 256, "the expert path is laid out for D = 256");
   typedef RmxShape<D, EM> S_;
@@ -257,6 +257,16 @@ __global__ __launch_bounds__(64 * rmx_waves(D), D <= 256 ? 2 : 1) void rmx_block
       }
     }
     __syncthreads();
+    if constexpr (ROUTE) {
+      // the gates as the FFN half uses them (hi + lo), then nothing else
+      for (int i = tid; i < RMX_BM * EM; i += 64 * NW) {
+        const int r = i / EM, e = i - r * EM;
+        const int64_t b = b0 + r;
+        if (b < a.B)
+          a.gates[(b * a.T + t) * EM + e] = bf2f(ug[r * S_::SG + e]) + bf2f(ug[r * S_::SG + EM + e]);
+      }
+      return;
+    }
     if (tid < EM) {
       int any = 0;
       for (int r = 0; r < RMX_BM; ++r) any |= ug[r * S_::SG + tid] | ug[r * S_::SG + EM + tid];
@@ -538,7 +548,10 @@ __global__ __launch_bounds__(64 * rmx_waves(D), D <= 256 ? 2 : 1) void rmx_block
 template <int D, int EM>
 void launch_block(const RmxArgs& a, int part, hipStream_t s) {
   const int tiles = a.T * ((a.B + RMX_BM - 1) / RMX_BM);
-  if (part == 1)
+  if (part == 3) {   // router only (the host allows it for expert contexts)
+    if constexpr (EM > 0)
+      hipLaunchKernelGGL((rmx_block_kernel<D, false, EM, true>), dim3(tiles), dim3(64 * rmx_waves(D)), 0, s, a);
+  } else if (part == 1)
     hipLaunchKernelGGL((rmx_block_kernel<D, false, EM>), dim3(tiles), dim3(64 * rmx_waves(D)), 0, s, a);
   else
     hipLaunchKernelGGL((rmx_block_kernel<D, true, EM>), dim3(tiles), dim3(64 * rmx_waves(D)), 0, s, a);

@@ -20,7 +20,8 @@ TMX_MIX, TMX_REVERT = 0, 1
 TMX_BLOCK_TOKENMIXER_LARGE, TMX_BLOCK_RANKMIXER = 0, 1
 
 EXPORTED = ("tmx_create", "tmx_destroy", "tmx_last_error", "tmx_load_weights",
-            "tmx_block_stack_forward", "tmx_moe_route", "tmx_sublayer_forward", "tmx_debug_permute")
+            "tmx_block_stack_forward", "tmx_moe_route", "tmx_sublayer_forward", "tmx_debug_permute",
+            "tmx_relu_route")
 
 
 class TmxError(RuntimeError):
@@ -64,6 +65,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tmx_moe_route.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp]
     lib.tmx_sublayer_forward.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, vp]
     lib.tmx_debug_permute.argtypes = [vp, vp, vp, i32, i32, vp]
+    lib.tmx_relu_route.argtypes = [vp, i32, vp, i32, vp, vp]
     for name in EXPORTED:
         if name != "tmx_last_error":
             getattr(lib, name).restype = ctypes.c_int
@@ -128,6 +130,9 @@ class Context:
     def moe_route(self, layer: int, sublayer: int, x, B: int, idx, gate, stream=None):
         self._check(self.lib.tmx_moe_route(self.h, layer, sublayer, _ptr(x), B, _ptr(idx), _ptr(gate),
                                            _ptr(stream)))
+
+    def relu_route(self, layer: int, s, B: int, gates, stream=None):
+        self._check(self.lib.tmx_relu_route(self.h, layer, _ptr(s), B, _ptr(gates), _ptr(stream)))
 
     def sublayer_forward(self, layer: int, sublayer: int, x_in, resid, extra, x_out, B: int, stream=None):
         self._check(self.lib.tmx_sublayer_forward(self.h, layer, sublayer, _ptr(x_in), _ptr(resid),
