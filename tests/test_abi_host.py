@@ -203,3 +203,21 @@ def test_bank_generation_is_worker_independent():
         np.testing.assert_array_equal(a[k], b[k])
     ws = dg.WeightSource(cfg, a)
     np.testing.assert_array_equal(ws(1, 1, dg.K_EXP_UP, 3), dg.weight_slice(cfg, 1, 1, dg.K_EXP_UP, 3))
+
+
+def test_rankmixer_bank_generation_is_worker_independent():
+    """RankMixer banks (dense FFN and ReLU-routed experts, with drawn norm
+    parameters): the same values for any worker count, and each slice equal
+    to its direct draw."""
+    for wl in (dg.RANKMIXER_WORKLOADS["rankmixer_d256"], dg.RANKMIXER_WORKLOADS["rankmixer_moe_d256"]):
+        cfg = wl.with_(L=1, B=8, T=4, H=4, random_norm=True)
+        a = dg.weight_banks(cfg, workers=1)
+        b = dg.weight_banks(cfg, workers=8)
+        assert a.keys() == b.keys()
+        for k in a:
+            np.testing.assert_array_equal(a[k], b[k])
+        kinds = {k[2] for k in a}
+        assert dg.K_NORM_BIAS in kinds and (dg.K_EXP_BIAS_DOWN in kinds) == cfg.moe
+        ws = dg.WeightSource(cfg, a)
+        kind = dg.K_EXP_UP if cfg.moe else dg.K_UP
+        np.testing.assert_array_equal(ws(1, 1, kind, 2), dg.weight_slice(cfg, 1, 1, kind, 2))
