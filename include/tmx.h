@@ -42,7 +42,8 @@
  *                   X   = LN_2(S + PFFN(S)),  PFFN_t(s) = GELU(s W1_t + b1_t) W2_t + b2_t
  *
  * LN is LayerNorm (biased variance, eps = cfg.eps, gain and bias), GELU the
- * exact erf form.  Sub-layer 0 (TMX_MIX) is the token-mixing half, sub-layer
+ * erf form z * Phi(z) (erf evaluated to within 1.5e-7, Abramowitz & Stegun
+ * 7.1.26).  Sub-layer 0 (TMX_MIX) is the token-mixing half, sub-layer
  * 1 (TMX_REVERT) the FFN half; S is rounded to the ctx dtype once.
  * With E > 0 each token's FFN is replaced by E ReLU-routed experts (fun-rec
  * chapter 7.4.3, the inference router of dense-train / sparse-infer):
