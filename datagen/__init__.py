@@ -61,6 +61,7 @@ KIND_NAMES = {
 }
 
 DENSE_KINDS = (K_UP, K_GATE, K_DOWN)
+DOWN_KINDS = (K_DOWN, K_EXP_DOWN, K_SH_DOWN)   # the kinds that carry the small-down factor
 MOE_KINDS = (K_ROUTER, K_EXP_UP, K_EXP_GATE, K_EXP_DOWN, K_SH_UP, K_SH_GATE, K_SH_DOWN)
 # RankMixer: the token-mixing sub-layer has only its LayerNorm; the per-token
 # FFN sub-layer holds W1 (K_UP), W2 (K_DOWN) and their biases
@@ -309,13 +310,15 @@ def default_workers() -> int:
     return max(1, min(16, n))
 
 
-def weight_banks(cfg: Workload, seed: Optional[int] = None, workers: int = 0):
-    """{(layer 1..L, sub, kind): bank} for every matrix bank of the stack.
+def weight_banks(cfg: Workload, seed: Optional[int] = None, workers: int = 0, kinds=None):
+    """{(layer 1..L, sub, kind): bank} for every matrix bank of the stack
+    (only the kinds in ``kinds`` when it is given).
 
     bf16 workloads give uint16 arrays of bf16 bit patterns, fp32 workloads
     float32 arrays. Slices are drawn in a thread pool (the generator releases
     the GIL); every slice has its own seed key, so the values do not depend
-    on ``workers``."""
+    on ``workers`` -- nor on which other kinds are drawn: two workloads that
+    differ only in ``down_scale`` share every bank but the down matrices."""
     from concurrent.futures import ThreadPoolExecutor
     bf16 = cfg.bf16_values
     banks = {}
@@ -324,9 +327,13 @@ def weight_banks(cfg: Workload, seed: Optional[int] = None, workers: int = 0):
         for s in (SUB_MIX, SUB_REVERT):
             if cfg.random_norm:
                 for k in NORM_KINDS if cfg.rankmixer else (K_NORM_GAIN,):
+                    if kinds is not None and k not in kinds:
+                        continue
                     v = _norm_param(cfg, l, s, k, seed)
                     banks[(l, s, k)] = f32_to_bf16_bits(v) if bf16 else v
             for k in cfg.sub_kinds(s):
+                if kinds is not None and k not in kinds:
+                    continue
                 shape = cfg.kind_shape(s, k)
                 arr = np.empty(shape, np.uint16 if bf16 else np.float32)
                 banks[(l, s, k)] = arr

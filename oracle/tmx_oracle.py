@@ -272,14 +272,24 @@ def route(xhat: np.ndarray, w_router: np.ndarray, top_k: int, alpha: float):
 
 
 def moe(xhat: np.ndarray, w_router, exp_up, exp_gate, exp_down,
-        sh_up, sh_gate, sh_down, top_k: int, alpha: float, rho: bool = False):
+        sh_up, sh_gate, sh_down, top_k: int, alpha: float, rho: bool = False,
+        idx_override: Optional[np.ndarray] = None):
     """Sparse-Pertoken MoE of one position ([TML] Eq. 19-21): the routed
     experts' SwiGLU outputs weighted by alpha * pi, plus the always-on shared
     SwiGLU expert of this position, ungated ([TML] 2.4.2). Only the chosen
     experts are evaluated, each on its own rows.
 
+    ``idx_override`` [n, top_k] replaces the chosen set (gates stay alpha * pi
+    of the named experts): where two logits sit closer than the rounding of
+    the inputs can resolve, both top-k sets are correct results, and a
+    comparison evaluates the method on the set the other side chose after
+    checking that it is one of them.
+
     Returns (y [n, W], idx, gate)."""
-    idx, gate, _, _ = route(xhat, w_router, top_k, alpha)
+    idx, gate, _, pi = route(xhat, w_router, top_k, alpha)
+    if idx_override is not None:
+        idx = np.asarray(idx_override, dtype=np.int64).reshape(idx.shape)
+        gate = alpha * np.take_along_axis(pi, idx, axis=-1)
     n = xhat.shape[0]
     E = np.asarray(w_router).shape[1]
     routed = np.zeros((n, np.asarray(exp_down).shape[-1]))
@@ -307,14 +317,17 @@ _K_ROUTER, _K_EUP, _K_EGATE, _K_EDOWN, _K_SUP, _K_SGATE, _K_SDOWN = 4, 5, 6, 7, 
 
 def sublayer_positions(x: np.ndarray, resid: np.ndarray, cfg, layer: int, sub: int,
                        weights: WeightGetter, extra: Optional[np.ndarray] = None,
-                       rho: bool = False, record: Optional[dict] = None, mx: bool = False) -> np.ndarray:
+                       rho: bool = False, record: Optional[dict] = None, mx: bool = False,
+                       route_override: Optional[np.ndarray] = None) -> np.ndarray:
     """One Pre-Norm sub-layer over position-major rows:
     out[:, p] = resid[:, p] + F_p(RMSNorm(x[:, p])) [+ extra[:, p]], rounded
     once in bf16 mode. x, resid, extra are [n, P, W]; F_p is the position's
     own SwiGLU (dense) or Sparse-Pertoken MoE. ``record`` (optional dict)
     receives per-position routing {(p): (idx, gate)} for MoE sub-layers.
     With ``mx`` (dense only) the SwiGLU runs on MXFP8 operands (swiglu_mx),
-    its input rows being the fp32 normalised rows."""
+    its input rows being the fp32 normalised rows. ``route_override``
+    [n, P, top_k] (MoE only) names the chosen experts of every row and
+    position (see ``moe``)."""
     n, P, W = x.shape
     gain = weights(layer, sub, _K_GAIN, 0)
     F = np.zeros((n, P, W))
@@ -334,7 +347,8 @@ def sublayer_positions(x: np.ndarray, resid: np.ndarray, cfg, layer: int, sub: i
                                weights(layer, sub, _K_EUP, p), weights(layer, sub, _K_EGATE, p),
                                weights(layer, sub, _K_EDOWN, p), weights(layer, sub, _K_SUP, p),
                                weights(layer, sub, _K_SGATE, p), weights(layer, sub, _K_SDOWN, p),
-                               cfg.top_k, cfg.gate_scale, rho)
+                               cfg.top_k, cfg.gate_scale, rho,
+                               None if route_override is None else route_override[:, p])
             F[:, p] = y
             if record is not None:
                 record[p] = (idx, gate)

@@ -312,6 +312,47 @@ def test_moe_linear_in_alpha_without_shared():
     np.testing.assert_allclose(y3, 3.0 * y1, rtol=1e-13, atol=1e-15)
 
 
+def test_moe_route_override():
+    """The routing override: its own top-k reproduces the plain result bit for
+    bit; any other set of k experts gives alpha * sum over that set of pi_e
+    SwiGLU_e + shared, with pi still the softmax over all E (a mistake that
+    renormalised the gates or kept the oracle's own set would fail)."""
+    rng = np.random.default_rng(5)
+    w = _rand_moe(rng)
+    x = rng.standard_normal((12, 6))
+    y, idx, gate = orc.moe(x, **w, top_k=2, alpha=2.5)
+    y1, idx1, gate1 = orc.moe(x, **w, top_k=2, alpha=2.5, idx_override=idx)
+    assert np.array_equal(y1, y) and np.array_equal(idx1, idx) and np.array_equal(gate1, gate)
+    other = np.stack([(idx[:, 0] + 1) % 5, (idx[:, 0] + 3) % 5], axis=1)
+    y2, idx2, gate2 = orc.moe(x, **w, top_k=2, alpha=2.5, idx_override=other)
+    logits = x @ w["w_router"]
+    pi = np.exp(logits) / np.exp(logits).sum(1, keepdims=True)
+    want = orc.swiglu(x, w["sh_up"], w["sh_gate"], w["sh_down"])
+    for r in range(x.shape[0]):
+        for e in other[r]:
+            want[r] += 2.5 * pi[r, e] * orc.swiglu(x[r:r + 1], w["exp_up"][e], w["exp_gate"][e],
+                                                   w["exp_down"][e])[0]
+    np.testing.assert_allclose(y2, want, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(idx2, other)
+    np.testing.assert_allclose(gate2, 2.5 * np.take_along_axis(pi, other, 1), rtol=1e-13)
+
+
+def test_weight_banks_kind_filter_shares_draws():
+    """Two workloads that differ only in down_scale draw the same banks except
+    the down matrices, which differ exactly by the factor before rounding."""
+    a = dg.WORKLOADS[4].with_(L=1, B=8, T=2, H=2, D=32, E=16, expert_hidden=128, shared_hidden=128)
+    b = a.with_(down_scale=1.0)
+    ba = dg.weight_banks(a)
+    bd = dg.weight_banks(b, kinds=dg.DOWN_KINDS)
+    assert set(bd) == {k for k in ba if k[2] in dg.DOWN_KINDS}
+    full_b = dg.weight_banks(b)
+    for k in full_b:
+        if k[2] in dg.DOWN_KINDS:
+            np.testing.assert_array_equal(bd[k], full_b[k])
+        else:
+            np.testing.assert_array_equal(ba[k], full_b[k])
+
+
 # ---------------------------------------------------------------------------
 # stack wiring (Pre-Norm block, residual to block input, inter-residual)
 # ---------------------------------------------------------------------------
