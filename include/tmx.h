@@ -199,6 +199,20 @@ tmx_status tmx_block_stack_forward(tmx_ctx* ctx, const void* x_in, void* x_out,
 tmx_status tmx_moe_route(tmx_ctx* ctx, int layer, int sublayer, const void* x,
                          int B, int32_t* idx, float* gate, void* stream);
 
+/* The expert-first row lists of one MoE sub-layer (MoEPermute,
+ * TokenMixer-Large summary section 2.5.1), for checks: x is the sub-layer's
+ * input in block layout [B, T, D] (device); the sub-layer's router and bucket
+ * kernels run on it exactly as in the forward, and their lists are copied
+ * out: counts [P, E] int32 (rows routed to expert e at position p) and rows
+ * [P, B*top_k] int32, where position p's entries are expert 0's, then expert
+ * 1's, ... (expert e's list starts at the exclusive prefix sum of counts[p])
+ * and each entry is b*top_k + slot, in ascending order within a list.
+ * Device pointers; uses the context's workspace, so it must not overlap a
+ * forward on another stream.  TMX_ERR_UNSUPPORTED unless the context is a
+ * bf16 TokenMixer-Large MoE one. */
+tmx_status tmx_moe_buckets(tmx_ctx* ctx, int layer, int sublayer, const void* x,
+                           int B, int32_t* counts, int32_t* rows, void* stream);
+
 /* One sub-layer, for teacher-forced checks; runs the same kernels as the
  * forward.  All tensors are [B, T, D] in block layout (device).
  *   TMX_MIX:    x_out = Revert(Mix(x_in) + F_mix(RMSNorm(Mix(x_in))));
@@ -225,11 +239,51 @@ tmx_status tmx_sublayer_forward(tmx_ctx* ctx, int layer, int sublayer,
  * E > 0; TMX_ERR_STATE if that layer's router was never loaded. */
 tmx_status tmx_relu_route(tmx_ctx* ctx, int layer, const void* s, int B, float* gates, void* stream);
 
+/* Address forms of the Mix / Revert map that tmx_debug_permute can run. */
+typedef enum tmx_perm_form {
+  TMX_PERM_ELEMENT = 0, /* one offset computation per element (fp32 path; the
+                           fused MLP's row I/O where a lane's columns change
+                           from unit to unit, W = 768)                      */
+  TMX_PERM_LANECOL = 1, /* the fused MLP's row I/O: 8-column units of whole
+                           rows, a lane's column part computed once         */
+  TMX_PERM_CURSOR = 2   /* the router's row loads: a row's 8-column runs at a
+                           stride of 32 columns through the column cursor   */
+} tmx_perm_form;
+
 /* Apply Mix (inverse = 0: out [B, H, T*D/H]) or Revert (inverse = 1:
- * in [B, H, T*D/H] -> out [B, T, D]) with the same device index code the
- * sub-layer kernels use; bit-exact data movement (Eq. 9-11, 13-15). */
+ * in [B, H, T*D/H] -> out [B, T, D]) (TokenMixer-Large Eq. 9-11, 13-15):
+ * bit-exact data movement through the library's single Mix / Revert address
+ * map, in the address form `form` (tmx_perm_form) -- the device functions
+ * and the unit-to-lane assignment the sub-layer kernels run.  in and out
+ * are device buffers of the ctx dtype, not overlapping; forms 1 and 2 need
+ * 16-byte aligned buffers, D/H % 8 == 0 and T*D/H % 32 == 0
+ * (TMX_ERR_UNSUPPORTED otherwise). */
 tmx_status tmx_debug_permute(tmx_ctx* ctx, const void* in, void* out, int B,
-                             int inverse, void* stream);
+                             int inverse, int form, void* stream);
+
+/* Kernels of the library, as counted by tmx_kernel_times. */
+typedef enum tmx_kernel_kind {
+  TMX_KERNEL_MLP_DENSE = 0,  /* fused per-position SwiGLU sub-layer (Eq. 12-18)  */
+  TMX_KERNEL_MLP_ROUTED = 1, /* grouped routed experts (section 2.5.1 GroupedFFN) */
+  TMX_KERNEL_MLP_SHARED = 2, /* shared expert + gated combine (Eq. 20-21)        */
+  TMX_KERNEL_ROUTER = 3,     /* RMSNorm + router + top-k (Eq. 19, 21)            */
+  TMX_KERNEL_BUCKET = 4,     /* expert-first row lists (section 2.5.1 MoEPermute) */
+  TMX_KERNEL_RMX_BLOCK = 5,  /* RankMixer block                                  */
+  TMX_KERNEL_F32 = 6,        /* fp32 sub-layer                                   */
+  TMX_KERNEL_KINDS = 7
+} tmx_kernel_kind;
+
+/* Measurement: with enable = 1 every kernel the context enqueues from then
+ * on is bracketed by a pair of HIP events recorded on its launch stream
+ * (events are created on first use and reused); enable = 0 stops that. */
+tmx_status tmx_set_kernel_timing(tmx_ctx* ctx, int enable);
+
+/* Waits for every bracketed launch, then writes, for the first n kernel kinds
+ * (tmx_kernel_kind), the summed event-timed duration in milliseconds and the
+ * number of launches since the previous call (host arrays ms[n] and
+ * launches[n]), and resets both.  Synchronises with the recorded streams;
+ * not for use inside a captured or timed region. */
+tmx_status tmx_kernel_times(tmx_ctx* ctx, double* ms, long long* launches, int n);
 
 #ifdef __cplusplus
 }

@@ -116,13 +116,19 @@ def _create(tmx, **kw):
     # bf16 fast path shape limits
     (dict(dtype=1, D=32, H=8, T=16, hidden_mix=64, hidden_rev=64), "UNSUPPORTED"),     # dh = 4
     (dict(dtype=1, D=96, H=4, T=4, hidden_mix=64, hidden_rev=64), "UNSUPPORTED"),      # W = 96
-    (dict(dtype=1, D=128, H=4, T=4, hidden_mix=100, hidden_rev=64), "UNSUPPORTED"),    # hidden % 64
+    (dict(dtype=1, D=128, H=4, T=4, hidden_mix=100, hidden_rev=64), "UNSUPPORTED"),    # hidden % 128
     (dict(dtype=1, D=128, H=4, T=4, E=8, top_k=2, expert_hidden=64, shared_hidden=64), "UNSUPPORTED"),
     # MXFP8: dense, W = 256 in both sub-layers, hidden <= 1024
     (dict(dtype=2, D=512, H=16, T=16, hidden_mix=256, hidden_rev=256), "UNSUPPORTED"),
     (dict(dtype=2, D=256, H=16, T=16, hidden_mix=2048, hidden_rev=256), "UNSUPPORTED"),
     (dict(dtype=2, D=256, H=16, T=16, E=16, top_k=4, expert_hidden=256, shared_hidden=512), "UNSUPPORTED"),
     (dict(dtype=3), "INVALID_ARG"),
+    # MXFP8 capability checks come after every shape check: H = 0 or D % H != 0
+    # must be INVALID_ARG, never a division by zero in the MXFP8 width check
+    (dict(dtype=2, D=256, H=0, T=16, hidden_mix=256, hidden_rev=256), "INVALID_ARG"),
+    (dict(dtype=2, D=256, H=7, T=16, hidden_mix=256, hidden_rev=256), "INVALID_ARG"),
+    (dict(dtype=2, D=256, H=16, T=0, hidden_mix=256, hidden_rev=256), "INVALID_ARG"),
+    (dict(dtype=2, D=256, H=16, T=16, hidden_mix=0, hidden_rev=256), "INVALID_ARG"),
     (dict(block=2), "INVALID_ARG"),
     # RankMixer: H == T, no mix hidden, no inter-residual; bf16 dense, D 256 / 512
     (dict(block=1, dtype=1, D=256, H=8, T=16, hidden_mix=0, hidden_rev=1024, inter_residual_gap=0), "INVALID_ARG"),
@@ -174,8 +180,11 @@ def test_null_context_calls(tmx):
     assert lib.tmx_load_weights(None, 0, 0, 1, None, 0, None) == tmx.TMX_ERR_INVALID_ARG
     assert lib.tmx_moe_route(None, 0, 0, None, 1, None, None, None) == tmx.TMX_ERR_INVALID_ARG
     assert lib.tmx_sublayer_forward(None, 0, 0, None, None, None, None, 1, None) == tmx.TMX_ERR_INVALID_ARG
-    assert lib.tmx_debug_permute(None, None, None, 1, 0, None) == tmx.TMX_ERR_INVALID_ARG
+    assert lib.tmx_debug_permute(None, None, None, 1, 0, 0, None) == tmx.TMX_ERR_INVALID_ARG
     assert lib.tmx_relu_route(None, 0, None, 1, None, None) == tmx.TMX_ERR_INVALID_ARG
+    assert lib.tmx_moe_buckets(None, 0, 0, None, 1, None, None, None) == tmx.TMX_ERR_INVALID_ARG
+    assert lib.tmx_set_kernel_timing(None, 1) == tmx.TMX_ERR_INVALID_ARG
+    assert lib.tmx_kernel_times(None, None, None, 0) == tmx.TMX_ERR_INVALID_ARG
     assert lib.tmx_last_error(None)
 
 

@@ -40,25 +40,53 @@ __device__ __forceinline__ float silu(float z) {
 }
 
 // ---------------------------------------------------------------------------
-// Position-major view of a [B, T, D] block tensor.
+// Position-major view of a [B, T, D] block tensor: the one Mix / Revert
+// address map of the library. Every kernel that reads or writes block-layout
+// rows by position (the fused MLP's row I/O, the router, the RankMixer token
+// mixing, the fp32 path, the debug permutation) computes its offsets with
+// the functions below and nothing else.
 //
 // Mix sub-layer (TokenMixer-Large Eq. 9-11): position p = head h, width
-// W = T*dh, element w = t*dh + j lives at X[b, t, h*dh + j].  Revert (Eq.
+// W = T*dh, element w = t*dh + j lives at X[b, t, h*dh + j]. Revert (Eq.
 // 13-15) is the same bijection read the other way, so the mix sub-layer
 // reads its input and writes X_rev through this one map.
 // Revert sub-layer: position p = token t, width W = D, identity.
+//
+// offset(b, p, w) = row(b) + pos(p) + col(w): the three parts are separate
+// so that a kernel can keep a part that does not change across its units
+// (a lane whose column group is fixed computes col() once), and cursor()
+// steps col() along a row by a constant stride without a division per step.
 // ---------------------------------------------------------------------------
 struct RowMap {
   int T, D, dh;   // dh = D / H
   int mix;        // 1: mixed positions, 0: token positions
 
-  __device__ __forceinline__ int64_t offset(int64_t b, int p, int w) const {
+  __device__ __forceinline__ int64_t row(int64_t b) const { return b * (int64_t)T * D; }
+  __device__ __forceinline__ int64_t pos(int p) const { return (int64_t)p * (mix ? dh : D); }
+  __device__ __forceinline__ int col(int w) const {
     if (mix) {
       const int t = w / dh;
-      const int j = w - t * dh;
-      return b * (int64_t)T * D + (int64_t)t * D + (int64_t)p * dh + j;
+      return t * D + (w - t * dh);
     }
-    return b * (int64_t)T * D + (int64_t)p * D + w;
+    return w;
+  }
+  __device__ __forceinline__ int64_t offset(int64_t b, int p, int w) const { return row(b) + pos(p) + col(w); }
+
+  // col(w0), col(w0 + s), col(w0 + 2s), ... for a stride s > 0
+  struct Cursor {
+    int seg, j, dh, D;
+    __device__ __forceinline__ int col() const { return seg * D + j; }
+    __device__ __forceinline__ void advance(int s) {
+      j += s;
+      while (j >= dh) {
+        j -= dh;
+        ++seg;
+      }
+    }
+  };
+  __device__ __forceinline__ Cursor cursor(int w0) const {
+    if (mix) return Cursor{w0 / dh, w0 % dh, dh, D};
+    return Cursor{0, w0, 0x7fffffff, 0};
   }
 };
 

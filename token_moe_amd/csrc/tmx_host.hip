@@ -48,6 +48,17 @@ struct tmx_ctx {
   uint16_t* part = nullptr;                    // [B_max][P][k][W] bf16
   std::vector<void*> allocs;
   std::string err;
+  // per-kernel timing (tmx_set_kernel_timing): an event pair around every
+  // launch while enabled, harvested by tmx_kernel_times
+  struct Timed {
+    int kind;
+    hipEvent_t start, end;
+  };
+  bool timing = false;
+  std::vector<Timed> pending;
+  std::vector<hipEvent_t> event_pool;
+  double kernel_ms[TMX_KERNEL_KINDS] = {};
+  long long kernel_launches[TMX_KERNEL_KINDS] = {};
 };
 
 namespace {
@@ -156,25 +167,43 @@ tmx_status check_launch(tmx_ctx* c, hipError_t e, const char* what) {
   return TMX_OK;
 }
 
+hipEvent_t take_event(tmx_ctx* c) {
+  if (!c->event_pool.empty()) {
+    hipEvent_t e = c->event_pool.back();
+    c->event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return e;
+}
+
+// launch() enqueues one kernel; with timing on, HIP events on the same
+// stream bracket it (kernel kind `kind`, tmx_kernel_kind)
+template <class F>
+tmx_status launch_timed(tmx_ctx* c, int kind, hipStream_t st, const char* what, F&& launch) {
+  if (!c->timing) return check_launch(c, launch(), what);
+  hipEvent_t a = take_event(c), b = take_event(c);
+  if (a) (void)hipEventRecord(a, st);
+  tmx_status s = check_launch(c, launch(), what);
+  if (a && b && hipEventRecord(b, st) == hipSuccess)
+    c->pending.push_back({kind, a, b});
+  else {
+    if (a) c->event_pool.push_back(a);
+    if (b) c->event_pool.push_back(b);
+  }
+  return s;
+}
+
 tmx_status validate_config(const tmx_config* cfg) {
   if (!cfg) return fail(nullptr, TMX_ERR_INVALID_ARG, "cfg is NULL");
   const tmx_config& c = *cfg;
   if (c.dtype != TMX_F32 && c.dtype != TMX_BF16 && c.dtype != TMX_MXFP8)
     return fail(nullptr, TMX_ERR_INVALID_ARG, "dtype must be TMX_F32 (0), TMX_BF16 (1) or TMX_MXFP8 (2), got %d",
                 c.dtype);
-  if (c.dtype == TMX_MXFP8) {
-    if (c.E > 0) return fail(nullptr, TMX_ERR_UNSUPPORTED, "the MXFP8 path covers dense stacks (E = 0)");
-    if ((c.D / c.H) % 8 != 0)
-      return fail(nullptr, TMX_ERR_UNSUPPORTED, "MXFP8 path needs D/H %% 8 == 0, got %d", c.D / c.H);
-    for (int sub = 0; sub < 2; ++sub) {
-      if (width(c, sub) != 256)
-        return fail(nullptr, TMX_ERR_UNSUPPORTED, "MXFP8 path supports sub-layer width 256, got %d", width(c, sub));
-      const int h = dense_hidden(c, sub);
-      if (h % MLP_HC != 0 || h > (MX_REC_DWORDS / 3) * MLP_HC)
-        return fail(nullptr, TMX_ERR_UNSUPPORTED, "MXFP8 path needs hidden %% %d == 0 and hidden <= %d, got %d",
-                    MLP_HC, (MX_REC_DWORDS / 3) * MLP_HC, h);
-    }
-  }
   if (c.B_max < 1 || c.T < 1 || c.H < 1 || c.D < 1 || c.L < 1)
     return fail(nullptr, TMX_ERR_INVALID_ARG, "B_max, T, H, D, L must be >= 1 (got %d, %d, %d, %d, %d)", c.B_max,
                 c.T, c.H, c.D, c.L);
@@ -222,6 +251,19 @@ tmx_status validate_config(const tmx_config* cfg) {
   }
   const int64_t act = (int64_t)c.B_max * c.T * c.D;
   if (act > (int64_t)1 << 40) return fail(nullptr, TMX_ERR_INVALID_ARG, "B_max*T*D too large");
+  if (c.dtype == TMX_MXFP8) {
+    if (c.E > 0) return fail(nullptr, TMX_ERR_UNSUPPORTED, "the MXFP8 path covers dense stacks (E = 0)");
+    if ((c.D / c.H) % 8 != 0)
+      return fail(nullptr, TMX_ERR_UNSUPPORTED, "MXFP8 path needs D/H %% 8 == 0, got %d", c.D / c.H);
+    for (int sub = 0; sub < 2; ++sub) {
+      if (width(c, sub) != 256)
+        return fail(nullptr, TMX_ERR_UNSUPPORTED, "MXFP8 path supports sub-layer width 256, got %d", width(c, sub));
+      const int h = dense_hidden(c, sub);
+      if (h % MLP_HC != 0 || h > (MX_REC_DWORDS / 3) * MLP_HC)
+        return fail(nullptr, TMX_ERR_UNSUPPORTED, "MXFP8 path needs hidden %% %d == 0 and hidden <= %d, got %d",
+                    MLP_HC, (MX_REC_DWORDS / 3) * MLP_HC, h);
+    }
+  }
 
   const int dh = c.D / c.H;
   if (c.dtype == TMX_BF16) {
@@ -313,7 +355,7 @@ tmx_status run_rmx(tmx_ctx* c, int layer, int part, const void* x_in, void* x_ou
   } else {
     a.w1 = h(TMX_W_UP); a.w2 = h(TMX_W_DOWN); a.b1 = h(TMX_W_BIAS_UP); a.b2 = h(TMX_W_BIAS_DOWN);
   }
-  return check_launch(c, launch_rmx(a, part, st), "RankMixer launch");
+  return launch_timed(c, TMX_KERNEL_RMX_BLOCK, st, "RankMixer launch", [&] { return launch_rmx(a, part, st); });
 }
 
 tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const void* resid, const void* extra,
@@ -336,7 +378,7 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
     a.w_up = w(TMX_W_UP); a.w_gate = w(TMX_W_GATE); a.w_down = w(TMX_W_DOWN);
     a.w_router = w(TMX_W_ROUTER); a.e_up = w(TMX_W_EXP_UP); a.e_gate = w(TMX_W_EXP_GATE);
     a.e_down = w(TMX_W_EXP_DOWN); a.s_up = w(TMX_W_SH_UP); a.s_gate = w(TMX_W_SH_GATE); a.s_down = w(TMX_W_SH_DOWN);
-    return check_launch(c, launch_f32_sublayer(a, st), "f32 sub-layer launch");
+    return launch_timed(c, TMX_KERNEL_F32, st, "f32 sub-layer launch", [&] { return launch_f32_sublayer(a, st); });
   }
 
   MlpArgs a{};
@@ -352,11 +394,11 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
     if (cfg.dtype == TMX_MXFP8) {
       a.wsc = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(a.wgu) +
                                                 (size_t)2 * kind_elems(cfg, sub, TMX_W_GATE));
-      return check_launch(c, launch_mlp_mx(a, (a.pair ? P / 2 : P) * a.rtiles, c->workers, st),
-                          "dense MXFP8 MLP launch");
+      return launch_timed(c, TMX_KERNEL_MLP_DENSE, st, "dense MXFP8 MLP launch",
+                          [&] { return launch_mlp_mx(a, (a.pair ? P / 2 : P) * a.rtiles, c->workers, st); });
     }
-    return check_launch(c, launch_mlp(MLP_DENSE, W, a, (a.pair ? P / 2 : P) * a.rtiles, c->workers, st),
-                        "dense MLP launch");
+    return launch_timed(c, TMX_KERNEL_MLP_DENSE, st, "dense MLP launch",
+                        [&] { return launch_mlp(MLP_DENSE, W, a, (a.pair ? P / 2 : P) * a.rtiles, c->workers, st); });
   }
 
   // MoE: norm + route -> bucket -> routed experts -> shared expert + combine
@@ -366,13 +408,13 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   r.x = static_cast<const uint16_t*>(x_in); r.gain = gain;
   r.wr = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_ROUTER).ptr);
   r.xhat = c->xhat; r.idx = c->idx; r.gate = c->gate; r.hist = c->hist;
-  tmx_status s = check_launch(c, launch_norm_route(W, r, st), "router launch");
+  tmx_status s = launch_timed(c, TMX_KERNEL_ROUTER, st, "router launch", [&] { return launch_norm_route(W, r, st); });
   if (s != TMX_OK) return s;
 
   BucketArgs k{};
   k.B = B; k.P = P; k.E = cfg.E; k.top_k = cfg.top_k; k.bm = bm; k.max_tiles = moe_max_tiles(cfg, sub, B);
   k.idx = c->idx; k.rows = c->rows; k.tiles = c->tiles; k.ntiles = c->ntiles; k.counts = c->counts; k.qhead = c->qhead; k.hist = c->hist;
-  s = check_launch(c, launch_bucket(k, st), "bucket launch");
+  s = launch_timed(c, TMX_KERNEL_BUCKET, st, "bucket launch", [&] { return launch_bucket(k, st); });
   if (s != TMX_OK) return s;
 
   a.xhat = c->xhat; a.top_k = cfg.top_k; a.E = cfg.E; a.max_tiles = k.max_tiles;
@@ -381,7 +423,8 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   a.hidden = cfg.expert_hidden;
   a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_EXP_GATE).ptr);
   a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_EXP_DOWN).ptr);
-  s = check_launch(c, launch_mlp(MLP_ROUTED, W, a, P * a.max_tiles, c->workers, st), "routed MLP launch");
+  s = launch_timed(c, TMX_KERNEL_MLP_ROUTED, st, "routed MLP launch",
+                   [&] { return launch_mlp(MLP_ROUTED, W, a, P * a.max_tiles, c->workers, st); });
   if (s != TMX_OK) return s;
 
   a.hidden = cfg.shared_hidden;
@@ -398,7 +441,8 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   const int sh_grid = std::max(1, std::min(sh_tiles, c->workers & ~7));
   const double mfma_clk = (double)bm * W * 3.0 * cfg.shared_hidden / (16384.0 * 4.0) * 32.0;
   a.stagger = sh_tiles >= 4 * sh_grid ? (int)(1.6 * mfma_clk) : 0;
-  return check_launch(c, launch_mlp(MLP_SHARED, W, a, sh_tiles, c->workers, st), "shared MLP launch");
+  return launch_timed(c, TMX_KERNEL_MLP_SHARED, st, "shared MLP launch",
+                      [&] { return launch_mlp(MLP_SHARED, W, a, sh_tiles, c->workers, st); });
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -542,6 +586,11 @@ tmx_status tmx_create(const tmx_config* cfg, int device, tmx_ctx** out) {
 tmx_status tmx_destroy(tmx_ctx* ctx) {
   if (!ctx) return TMX_OK;
   (void)hipSetDevice(ctx->device);
+  for (auto& t : ctx->pending) {
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.end);
+  }
+  for (hipEvent_t e : ctx->event_pool) (void)hipEventDestroy(e);
   release(ctx);
   delete ctx;
   return TMX_OK;
@@ -751,6 +800,42 @@ tmx_status tmx_moe_route(tmx_ctx* c, int layer, int sub, const void* x, int B, i
   return check_launch(c, launch_norm_route(W, r, st), "router launch");
 }
 
+tmx_status tmx_moe_buckets(tmx_ctx* c, int layer, int sub, const void* x, int B, int32_t* counts, int32_t* rows,
+                           void* stream) {
+  if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
+  const tmx_config& C = c->cfg;
+  if (!is_moe(C) || is_rmx(C) || C.dtype != TMX_BF16)
+    return fail(c, TMX_ERR_UNSUPPORTED, "tmx_moe_buckets needs a bf16 TokenMixer-Large MoE context");
+  tmx_status s;
+  if (layer < 0 || layer >= C.L) return fail(c, TMX_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, C.L);
+  if (sub != TMX_MIX && sub != TMX_REVERT) return fail(c, TMX_ERR_INVALID_ARG, "sublayer must be 0 or 1");
+  if ((s = check_B(c, B)) != TMX_OK) return s;
+  if ((s = check_act(c, x, "x")) != TMX_OK) return s;
+  if (!counts || !rows) return fail(c, TMX_ERR_INVALID_ARG, "counts and rows must be non-NULL");
+  if (!bank(c, layer, sub, TMX_W_ROUTER).loaded)
+    return fail(c, TMX_ERR_STATE, "router of layer %d sub-layer %d is not loaded", layer, sub);
+  (void)hipSetDevice(c->device);
+  hipStream_t st = as_stream(stream);
+  const int P = positions(C, sub), W = width(C, sub);
+  RouteArgs r{};
+  r.B = B; r.P = P; r.E = C.E; r.top_k = C.top_k; r.alpha = c->alpha; r.eps = C.eps;
+  r.map = RowMap{C.T, C.D, C.D / C.H, sub == TMX_MIX ? 1 : 0};
+  r.x = static_cast<const uint16_t*>(x);
+  r.gain = static_cast<const float*>(bank(c, layer, sub, TMX_W_NORM_GAIN).ptr);
+  r.wr = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_ROUTER).ptr);
+  r.xhat = c->xhat; r.idx = c->idx; r.gate = c->gate; r.hist = c->hist;
+  if ((s = check_launch(c, launch_norm_route(W, r, st), "router launch")) != TMX_OK) return s;
+  BucketArgs k{};
+  k.B = B; k.P = P; k.E = C.E; k.top_k = C.top_k; k.bm = mlp_bm(MLP_ROUTED, W); k.max_tiles = moe_max_tiles(C, sub, B);
+  k.idx = c->idx; k.rows = c->rows; k.tiles = c->tiles; k.ntiles = c->ntiles; k.counts = c->counts;
+  k.qhead = c->qhead; k.hist = c->hist;
+  if ((s = check_launch(c, launch_bucket(k, st), "bucket launch")) != TMX_OK) return s;
+  hipError_t e = hipMemcpyAsync(counts, c->counts, (size_t)P * C.E * 4, hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(rows, c->rows, (size_t)P * B * C.top_k * 4, hipMemcpyDeviceToDevice, st);
+  return check_launch(c, e, "bucket copy");
+}
+
 tmx_status tmx_relu_route(tmx_ctx* c, int layer, const void* s, int B, float* gates, void* stream) {
   if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
   const tmx_config& C = c->cfg;
@@ -767,19 +852,59 @@ tmx_status tmx_relu_route(tmx_ctx* c, int layer, const void* s, int B, float* ga
   return run_rmx(c, layer, 3, s, nullptr, B, as_stream(stream), gates);
 }
 
-tmx_status tmx_debug_permute(tmx_ctx* c, const void* in, void* out, int B, int inverse, void* stream) {
+tmx_status tmx_debug_permute(tmx_ctx* c, const void* in, void* out, int B, int inverse, int form, void* stream) {
   if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
   tmx_status s;
   if ((s = check_B(c, B)) != TMX_OK) return s;
   if (!in || !out) return fail(c, TMX_ERR_INVALID_ARG, "in/out must be non-NULL");
   if (inverse != 0 && inverse != 1) return fail(c, TMX_ERR_INVALID_ARG, "inverse must be 0 or 1");
-  const size_t bytes = (size_t)B * c->cfg.T * c->cfg.D * esize(c->cfg);
+  if (form < TMX_PERM_ELEMENT || form > TMX_PERM_CURSOR)
+    return fail(c, TMX_ERR_INVALID_ARG, "form must be 0, 1 or 2, got %d", form);
+  const tmx_config& C = c->cfg;
+  if (form != TMX_PERM_ELEMENT) {
+    if (!aligned16(in) || !aligned16(out)) return fail(c, TMX_ERR_INVALID_ARG, "in/out must be 16-byte aligned");
+    if ((C.D / C.H) % 8 != 0 || (C.T * (C.D / C.H)) % 32 != 0)
+      return fail(c, TMX_ERR_UNSUPPORTED, "8-column unit forms need D/H %% 8 == 0 and T*D/H %% 32 == 0");
+  }
+  const size_t bytes = (size_t)B * C.T * C.D * esize(C);
   if (overlaps(in, out, bytes)) return fail(c, TMX_ERR_INVALID_ARG, "in and out overlap");
   (void)hipSetDevice(c->device);
-  return check_launch(c,
-                      launch_permute(in, out, B, c->cfg.T, c->cfg.D, c->cfg.H, (int)esize(c->cfg), inverse,
-                                     as_stream(stream)),
+  return check_launch(c, launch_permute(in, out, B, C.T, C.D, C.H, (int)esize(C), inverse, form, as_stream(stream)),
                       "permute launch");
+}
+
+tmx_status tmx_set_kernel_timing(tmx_ctx* c, int enable) {
+  if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
+  if (enable != 0 && enable != 1) return fail(c, TMX_ERR_INVALID_ARG, "enable must be 0 or 1");
+  c->timing = enable == 1;
+  return TMX_OK;
+}
+
+tmx_status tmx_kernel_times(tmx_ctx* c, double* ms, long long* launches, int n) {
+  if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
+  if (n < 0 || ((!ms || !launches) && n > 0)) return fail(c, TMX_ERR_INVALID_ARG, "ms / launches / n invalid");
+  (void)hipSetDevice(c->device);
+  tmx_status st = TMX_OK;
+  for (auto& t : c->pending) {
+    float e_ms = 0.f;
+    hipError_t e = hipEventSynchronize(t.end);
+    if (e == hipSuccess) e = hipEventElapsedTime(&e_ms, t.start, t.end);
+    if (e != hipSuccess && st == TMX_OK) st = fail(c, TMX_ERR_DEVICE, "kernel timing: %s", hipGetErrorString(e));
+    c->kernel_ms[t.kind] += e_ms;
+    c->kernel_launches[t.kind] += 1;
+    c->event_pool.push_back(t.start);
+    c->event_pool.push_back(t.end);
+  }
+  c->pending.clear();
+  for (int k = 0; k < TMX_KERNEL_KINDS; ++k) {
+    if (k < n) {
+      ms[k] = c->kernel_ms[k];
+      launches[k] = c->kernel_launches[k];
+    }
+    c->kernel_ms[k] = 0.0;
+    c->kernel_launches[k] = 0;
+  }
+  return st;
 }
 
 }  // extern "C"

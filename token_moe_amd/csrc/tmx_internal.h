@@ -115,8 +115,12 @@ hipError_t launch_pack_mx(const uint16_t* src, uint8_t* dst, uint8_t* rec, int G
 // dense MXFP8 sub-layer at W = 256 (grid as launch_mlp)
 hipError_t launch_mlp_mx(const MlpArgs& a, int tiles, int workers, hipStream_t s);
 constexpr int MX_REC_DWORDS = 24;   // per lane: 3 scale dwords x up to 8 hidden chunks
+// Mix / Revert through RowMap in one of its address forms (PermForm; see
+// permute_kernel); forms other than PERM_ELEM need D/H % 8 == 0 and
+// T*D/H % 32 == 0
+enum PermForm { PERM_ELEM = 0, PERM_LANECOL = 1, PERM_CURSOR = 2 };
 hipError_t launch_permute(const void* in, void* out, int B, int T, int D, int H, int elem_bytes,
-                          int inverse, hipStream_t s);
+                          int inverse, int form, hipStream_t s);
 
 // RankMixer block (tmx_rankmixer.hip), bf16, H = T, D in {256, 512}:
 //   part 0: out = S = rho(LN_1(TokenMixing(x) + x))

@@ -224,12 +224,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   // computed once here.
   constexpr bool LANE_COL = (NT % U8) == 0;
   const int lw0 = (tid % U8) * 8;
-  const int64_t rowstride = (int64_t)a.map.T * a.map.D;
-  const int pstride = a.map.mix ? a.map.dh : a.map.D;
-  const int lcol = a.map.mix ? (lw0 / a.map.dh) * a.map.D + lw0 % a.map.dh : lw0;
+  const int lcol = a.map.col(lw0);
   auto uoff = [&](int b, int p, int c8) -> int64_t {
     if constexpr (LANE_COL)
-      return b * rowstride + lcol + (int64_t)p * pstride;
+      return a.map.row(b) + a.map.pos(p) + lcol;
     else
       return a.map.offset(b, p, c8 * 8);
   };

@@ -139,10 +139,10 @@ __device__ __forceinline__ typename VecOf<D / 64>::type ln1_row(const typename V
   return o;
 }
 
+// the mixed row t of sample b is position t of the Mix map (H = T)
 template <int D>
 __device__ __forceinline__ int64_t mix_offset(int64_t b, int t, int T, int dh, int c0) {
-  const int tp = c0 / dh, j = c0 - tp * dh;
-  return (b * T + tp) * (int64_t)D + (int64_t)t * dh + j;
+  return RowMap{T, D, dh, 1}.offset(b, t, c0);
 }
 
 // ---------------------------------------------------------------------------

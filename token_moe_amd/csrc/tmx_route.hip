@@ -91,26 +91,19 @@ __global__ __launch_bounds__(64 * RT_WAVES) void norm_route_kernel(const RouteAr
   const bool valid = row < a.B;
   if (a.hist)
     for (int e = threadIdx.x; e < a.E; e += blockDim.x) hist_s[e] = 0;
-  // row offset + column offsets of this lane's 8-column runs (k-blocks of
-  // 32 columns, the lane's quarter q); the Mix map's division by D/H is
-  // stepped through instead of repeated
-  const int64_t rbase = (int64_t)(valid ? row : 0) * a.map.T * a.map.D;
+  // row and position parts of this lane's offsets, and its 8-column runs
+  // (k-blocks of 32 columns, the lane's quarter q) through the map's column
+  // cursor, so the Mix map's division by D/H is stepped through instead of
+  // repeated
+  const int64_t rbase = a.map.row(valid ? row : 0) + a.map.pos(p);
   uint4 xr[KB];
   float ss = 0.f;
   {
-    const int dh = a.map.mix ? a.map.dh : W;
-    int seg = (q * 8) / dh, j = q * 8 - seg * dh;
-    const int64_t pbase = a.map.mix ? (int64_t)p * a.map.dh : (int64_t)p * a.map.D;
-    const int64_t segstride = a.map.mix ? a.map.D : 0;
+    RowMap::Cursor cur = a.map.cursor(q * 8);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const int64_t off = rbase + pbase + seg * segstride + j;
-      xr[kb] = valid ? ldg16(a.x + off) : make_uint4(0, 0, 0, 0);
-      j += 32;
-      while (j >= dh) {
-        j -= dh;
-        ++seg;
-      }
+      xr[kb] = valid ? ldg16(a.x + rbase + cur.col()) : make_uint4(0, 0, 0, 0);
+      cur.advance(32);
     }
   }
   // the position's router fragments, staged once for the four waves (L2
@@ -200,11 +193,16 @@ __global__ __launch_bounds__(64 * RT_WAVES) void norm_route_kernel(const RouteAr
       bv[v] = -INFINITY;
       be[v] = 0x7fffffff;
 #pragma unroll
-      for (int j = 0; j < NBE; ++j)
-        if (!((taken[v] >> j) & 1u) && lg[j][v] > bv[v]) {   // j ascending: ties keep the lower index
-          bv[v] = lg[j][v];
+      for (int j = 0; j < NBE; ++j) {
+        // a NaN logit (a non-finite input row) ranks as -inf, and the lane's
+        // first untaken expert is always a candidate: every slot then names a
+        // distinct expert in [0, E) whatever the row holds
+        const float l = lg[j][v] == lg[j][v] ? lg[j][v] : -INFINITY;
+        if (!((taken[v] >> j) & 1u) && (be[v] == 0x7fffffff || l > bv[v])) {   // j ascending: ties keep the lower index
+          bv[v] = l;
           be[v] = 16 * j + l16;
         }
+      }
     }
 #pragma unroll
     for (int v = 0; v < 4; ++v) row16_argmax(bv[v], be[v]);
@@ -333,7 +331,7 @@ __global__ __launch_bounds__(BK_NT) void bucket_kernel(const BucketArgs a) {
       if (lane == 0) wcnt[wave][ee] = __popcll(m);
     }
     __syncthreads();
-    if (e >= 0) {
+    if (e >= 0 && e < E) {
       int pos = base_s[e] + run_s[e] + rank;
       for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
       rows[pos] = b * k + sl;
@@ -446,26 +444,78 @@ __global__ void pack_mx_kernel(const uint16_t* __restrict__ src, uint8_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// permute: Mix (inverse = 0) / Revert (inverse = 1) with the sub-layer
-// kernels' RowMap (TokenMixer-Large Eq. 9-11, 13-15).
+// permute: Mix (inverse = 0) / Revert (inverse = 1) of [B, T, D] <-> [B, H,
+// T*D/H] (TokenMixer-Large Eq. 9-11, 13-15), through RowMap in each of the
+// forms the sub-layer kernels address block-layout rows with:
+//   PERM_ELEM    offset(b, p, w) per element (the fp32 path; the fused MLP's
+//                per-unit form when a lane's column group changes per unit)
+//   PERM_LANECOL the fused MLP's row I/O: 256 threads move 64 rows of one
+//                position in 8-column units, unit u = tid + 256 i covering
+//                row u / U8 and columns 8 (u % U8); when 256 % U8 == 0 a
+//                lane's column part col() is computed once and its offsets
+//                are row(b) + pos(p) + that part, as in the MLP kernel
+//   PERM_CURSOR  the router's form: the 4 lanes l16 + 16 q of a row read its
+//                8-column runs at columns 8 q + 32 kb through the column cursor
 // ---------------------------------------------------------------------------
 template <typename TE>
-__global__ void permute_kernel(const TE* __restrict__ in, TE* __restrict__ out, int B, int T, int D, int H,
-                               int inverse) {
-  RowMap m{T, D, D / H, 1};
+struct alignas(8 * sizeof(TE)) Vec8 {
+  TE v[8];
+};
+
+template <typename TE, int FORM>
+__global__ __launch_bounds__(256) void permute_kernel(const TE* __restrict__ in, TE* __restrict__ out, int B, int T,
+                                                      int D, int H, int inverse) {
+  const RowMap m{T, D, D / H, 1};
   const int W = T * (D / H);
-  const int64_t total = (int64_t)B * H * W;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int w = (int)(i % W);
-    const int64_t bh = i / W;
-    const int h = (int)(bh % H);
-    const int64_t b = bh / H;
-    const int64_t o = m.offset(b, h, w);
-    if (inverse)
-      out[o] = in[i];
-    else
-      out[i] = in[o];
+  if constexpr (FORM == PERM_ELEM) {
+    const int64_t total = (int64_t)B * H * W;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+      const int w = (int)(i % W);
+      const int64_t bh = i / W;
+      const int h = (int)(bh % H);
+      const int64_t b = bh / H;
+      const int64_t o = m.offset(b, h, w);
+      if (inverse)
+        out[o] = in[i];
+      else
+        out[i] = in[o];
+    }
+  } else {
+    // block (position h, 64-row chunk); 8-element units
+    const int chunks = (B + 63) / 64;
+    const int h = blockIdx.x / chunks;
+    const int64_t b0 = (int64_t)(blockIdx.x % chunks) * 64;
+    const int tid = threadIdx.x;
+    auto move = [&](int64_t b, int w, int64_t o) {
+      if (b >= B) return;
+      const int64_t mi = (b * H + h) * W + w;   // mixed-layout element
+      if (inverse)
+        *reinterpret_cast<Vec8<TE>*>(out + o) = *reinterpret_cast<const Vec8<TE>*>(in + mi);
+      else
+        *reinterpret_cast<Vec8<TE>*>(out + mi) = *reinterpret_cast<const Vec8<TE>*>(in + o);
+    };
+    if constexpr (FORM == PERM_LANECOL) {
+      const int U8 = W / 8;
+      if (256 % U8 == 0) {
+        const int lcol = m.col((tid % U8) * 8);
+        for (int r = tid / U8; r < 64; r += 256 / U8) move(b0 + r, (tid % U8) * 8, m.row(b0 + r) + m.pos(h) + lcol);
+      } else {
+        for (int u = tid; u < 64 * U8; u += 256) {
+          const int r = u / U8, c8 = u - r * U8;
+          move(b0 + r, c8 * 8, m.offset(b0 + r, h, c8 * 8));
+        }
+      }
+    } else {
+      const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, q = lane >> 4;
+      const int64_t b = b0 + wave * 16 + l16;
+      const int64_t rbase = m.row(b < B ? b : 0) + m.pos(h);
+      RowMap::Cursor cur = m.cursor(q * 8);
+      for (int kb = 0; kb < W / 32; ++kb) {
+        move(b, kb * 32 + q * 8, rbase + cur.col());
+        cur.advance(32);
+      }
+    }
   }
 }
 
@@ -522,16 +572,28 @@ hipError_t launch_pack_mx(const uint16_t* src, uint8_t* dst, uint8_t* rec, int G
   return hipGetLastError();
 }
 
-hipError_t launch_permute(const void* in, void* out, int B, int T, int D, int H, int elem_bytes, int inverse,
-                          hipStream_t s) {
-  const int64_t total = (int64_t)B * T * D;
-  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 65536);
-  if (elem_bytes == 2)
-    hipLaunchKernelGGL((permute_kernel<uint16_t>), dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), B, T, D, H, inverse);
+template <typename TE, int FORM>
+void launch_permute_t(const void* in, void* out, int B, int T, int D, int H, int inverse, hipStream_t s) {
+  int64_t blocks;
+  if (FORM == PERM_ELEM)
+    blocks = std::min<int64_t>(((int64_t)B * T * D + 255) / 256, 65536);
   else
-    hipLaunchKernelGGL((permute_kernel<uint32_t>), dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<const uint32_t*>(in), static_cast<uint32_t*>(out), B, T, D, H, inverse);
+    blocks = (int64_t)H * ((B + 63) / 64);
+  hipLaunchKernelGGL((permute_kernel<TE, FORM>), dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const TE*>(in),
+                     static_cast<TE*>(out), B, T, D, H, inverse);
+}
+
+hipError_t launch_permute(const void* in, void* out, int B, int T, int D, int H, int elem_bytes, int inverse,
+                          int form, hipStream_t s) {
+  if (elem_bytes == 2) {
+    if (form == PERM_ELEM) launch_permute_t<uint16_t, PERM_ELEM>(in, out, B, T, D, H, inverse, s);
+    else if (form == PERM_LANECOL) launch_permute_t<uint16_t, PERM_LANECOL>(in, out, B, T, D, H, inverse, s);
+    else launch_permute_t<uint16_t, PERM_CURSOR>(in, out, B, T, D, H, inverse, s);
+  } else {
+    if (form == PERM_ELEM) launch_permute_t<uint32_t, PERM_ELEM>(in, out, B, T, D, H, inverse, s);
+    else if (form == PERM_LANECOL) launch_permute_t<uint32_t, PERM_LANECOL>(in, out, B, T, D, H, inverse, s);
+    else launch_permute_t<uint32_t, PERM_CURSOR>(in, out, B, T, D, H, inverse, s);
+  }
   return hipGetLastError();
 }
 

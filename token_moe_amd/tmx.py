@@ -18,10 +18,12 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "OOM", 4: "DEVIC
 TMX_F32, TMX_BF16, TMX_MXFP8 = 0, 1, 2
 TMX_MIX, TMX_REVERT = 0, 1
 TMX_BLOCK_TOKENMIXER_LARGE, TMX_BLOCK_RANKMIXER = 0, 1
+TMX_PERM_ELEMENT, TMX_PERM_LANECOL, TMX_PERM_CURSOR = 0, 1, 2
 
 EXPORTED = ("tmx_create", "tmx_destroy", "tmx_last_error", "tmx_load_weights",
             "tmx_block_stack_forward", "tmx_moe_route", "tmx_sublayer_forward", "tmx_debug_permute",
-            "tmx_relu_route")
+            "tmx_relu_route", "tmx_moe_buckets", "tmx_set_kernel_timing", "tmx_kernel_times")
+KERNEL_KINDS = ("mlp_dense", "mlp_routed", "mlp_shared", "router", "bucket", "rmx_block", "f32")
 
 
 class TmxError(RuntimeError):
@@ -64,8 +66,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tmx_block_stack_forward.argtypes = [vp, vp, vp, i32, vp]
     lib.tmx_moe_route.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp]
     lib.tmx_sublayer_forward.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, vp]
-    lib.tmx_debug_permute.argtypes = [vp, vp, vp, i32, i32, vp]
+    lib.tmx_debug_permute.argtypes = [vp, vp, vp, i32, i32, i32, vp]
     lib.tmx_relu_route.argtypes = [vp, i32, vp, i32, vp, vp]
+    lib.tmx_moe_buckets.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp]
+    lib.tmx_set_kernel_timing.argtypes = [vp, i32]
+    lib.tmx_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong), i32]
     for name in EXPORTED:
         if name != "tmx_last_error":
             getattr(lib, name).restype = ctypes.c_int
@@ -131,6 +136,21 @@ class Context:
         self._check(self.lib.tmx_moe_route(self.h, layer, sublayer, _ptr(x), B, _ptr(idx), _ptr(gate),
                                            _ptr(stream)))
 
+    def moe_buckets(self, layer: int, sublayer: int, x, B: int, counts, rows, stream=None):
+        self._check(self.lib.tmx_moe_buckets(self.h, layer, sublayer, _ptr(x), B, _ptr(counts), _ptr(rows),
+                                             _ptr(stream)))
+
+    def set_kernel_timing(self, enable: bool):
+        self._check(self.lib.tmx_set_kernel_timing(self.h, 1 if enable else 0))
+
+    def kernel_times(self):
+        """{kernel name: (summed ms, launches)} since the previous call."""
+        n = len(KERNEL_KINDS)
+        ms = (ctypes.c_double * n)()
+        cnt = (ctypes.c_longlong * n)()
+        self._check(self.lib.tmx_kernel_times(self.h, ms, cnt, n))
+        return {KERNEL_KINDS[i]: (ms[i], cnt[i]) for i in range(n) if cnt[i]}
+
     def relu_route(self, layer: int, s, B: int, gates, stream=None):
         self._check(self.lib.tmx_relu_route(self.h, layer, _ptr(s), B, _ptr(gates), _ptr(stream)))
 
@@ -138,5 +158,6 @@ class Context:
         self._check(self.lib.tmx_sublayer_forward(self.h, layer, sublayer, _ptr(x_in), _ptr(resid),
                                                   _ptr(extra), _ptr(x_out), B, _ptr(stream)))
 
-    def debug_permute(self, x_in, x_out, B: int, inverse: int, stream=None):
-        self._check(self.lib.tmx_debug_permute(self.h, _ptr(x_in), _ptr(x_out), B, inverse, _ptr(stream)))
+    def debug_permute(self, x_in, x_out, B: int, inverse: int, form: int = 0, stream=None):
+        self._check(self.lib.tmx_debug_permute(self.h, _ptr(x_in), _ptr(x_out), B, inverse, form,
+                                               _ptr(stream)))
