@@ -51,6 +51,15 @@ K_BIAS_UP = 12       # RankMixer per-token FFN first bias  [P, h]
 K_BIAS_DOWN = 13     # RankMixer per-token FFN second bias [P, W]
 K_EXP_BIAS_UP = 14   # RankMixer ReLU-routed experts' first biases  [P, E, h_e]
 K_EXP_BIAS_DOWN = 15 # RankMixer ReLU-routed experts' second biases [P, E, W]
+# model front and back (one bank each, not per layer): the tokenizer's first
+# layers [2F, h_tok] (the global token's [F, h_tok], then every group's
+# [d_t, h_tok] in group order), second layers [T, h_tok, D], the head's
+# [D, h_head] and [h_head]
+K_TOK_UP = 16
+K_TOK_DOWN = 17
+K_HEAD_UP = 18
+K_HEAD_DOWN = 19
+IO_KINDS = (K_TOK_UP, K_TOK_DOWN, K_HEAD_UP, K_HEAD_DOWN)
 
 KIND_NAMES = {
     K_NORM_GAIN: "norm_gain", K_UP: "up", K_GATE: "gate", K_DOWN: "down",
@@ -58,6 +67,7 @@ KIND_NAMES = {
     K_EXP_DOWN: "exp_down", K_SH_UP: "sh_up", K_SH_GATE: "sh_gate",
     K_SH_DOWN: "sh_down", K_NORM_BIAS: "norm_bias", K_BIAS_UP: "bias_up",
     K_BIAS_DOWN: "bias_down", K_EXP_BIAS_UP: "exp_bias_up", K_EXP_BIAS_DOWN: "exp_bias_down",
+    K_TOK_UP: "tok_up", K_TOK_DOWN: "tok_down", K_HEAD_UP: "head_up", K_HEAD_DOWN: "head_down",
 }
 
 DENSE_KINDS = (K_UP, K_GATE, K_DOWN)
@@ -99,6 +109,9 @@ class Workload:
     down_scale: float = 0.01
     block: str = BLOCK_TML   # "tml" (TokenMixer-Large) or "rankmixer"
     random_norm: bool = False  # draw LayerNorm gains / biases instead of 1 / 0
+    groups: Tuple[int, ...] = ()   # model front: widths of the T - 1 semantic groups
+    tok_hidden: int = 0        # hidden width of the tokenizer MLPs
+    head_hidden: int = 0       # hidden width of the projection head
 
     # -- derived -----------------------------------------------------------
     @property
@@ -183,6 +196,30 @@ class Workload:
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
 
+    @property
+    def has_io(self) -> bool:
+        """The workload includes the tokenizer front and the mean-pool head."""
+        return len(self.groups) > 0
+
+    @property
+    def emb_width(self) -> int:
+        return int(sum(self.groups))
+
+    def io_shape(self, kind: int) -> Tuple[int, ...]:
+        F, h, hh = self.emb_width, self.tok_hidden, self.head_hidden
+        return {K_TOK_UP: (2 * F, h), K_TOK_DOWN: (self.T, h, self.D), K_HEAD_UP: (self.D, hh),
+                K_HEAD_DOWN: (hh,)}[kind]
+
+    def io_rows(self, kind: int, t: int) -> Tuple[int, int]:
+        """Row range of position t's slice of a tokenizer bank."""
+        F = self.emb_width
+        if kind == K_TOK_UP:
+            if t == 0:
+                return 0, F
+            off = int(sum(self.groups[:t - 1]))
+            return F + off, F + off + self.groups[t - 1]
+        return t, t + 1
+
 
 # The five workloads of the block-stack forward (TokenMixer-Large summary,
 # sections 2.3-2.4; batch sizes as in the reproduction README's commands).
@@ -199,6 +236,20 @@ WORKLOADS: Dict[int, Workload] = {
     5: Workload("large_moe_15b", B=8192, T=32, H=32, D=768, L=8, E=32,
                 top_k=4, expert_hidden=384, shared_hidden=768, alpha=8.0,
                 gap=2, seed=4),
+}
+
+
+# Whole-model workloads: the tokenizer front (T - 1 semantic groups of mixed
+# widths, a global token) and the mean-pool head around a block stack
+def _mixed_groups(n, widths):
+    return tuple(widths[i % len(widths)] for i in range(n))
+
+
+MODEL_WORKLOADS: Dict[str, Workload] = {
+    "model_dense": WORKLOADS[2].with_(name="model_dense", groups=_mixed_groups(15, (128, 256, 384)),
+                                      tok_hidden=256, head_hidden=256, seed=21),
+    "model_moe_15b": WORKLOADS[5].with_(name="model_moe_15b", groups=_mixed_groups(31, (128, 256, 384)),
+                                        tok_hidden=768, head_hidden=256, seed=24),
 }
 
 
@@ -271,6 +322,46 @@ def _draw(cfg: Workload, layer: int, sub: int, kind: int, p: int, seed: Optional
         std = np.float32(std * cfg.down_scale)
     a *= std
     return a
+
+
+def make_emb(cfg: Workload, seed: Optional[int] = None, B: Optional[int] = None) -> np.ndarray:
+    """Concatenated feature embeddings [B, F] (the tokenizer's input), N(0, 1)."""
+    s = cfg.seed if seed is None else seed
+    n = cfg.B if B is None else B
+    a = _rng(s, (3,)).standard_normal((n, cfg.emb_width), dtype=np.float32)
+    return _finish(cfg, a)
+
+
+def io_slice(cfg: Workload, kind: int, t: int = 0, seed: Optional[int] = None) -> np.ndarray:
+    """Position t's slice of a tokenizer / head bank, N(0, 1/fan_in), drawn
+    under key (2, kind, t); fp32 array of dtype-representable values."""
+    s = cfg.seed if seed is None else seed
+    if kind == K_TOK_UP:
+        lo, hi = cfg.io_rows(kind, t)
+        shape, fan = (hi - lo, cfg.tok_hidden), hi - lo
+    elif kind == K_TOK_DOWN:
+        shape, fan = (cfg.tok_hidden, cfg.D), cfg.tok_hidden
+    elif kind == K_HEAD_UP:
+        shape, fan = (cfg.D, cfg.head_hidden), cfg.D
+    else:
+        shape, fan = (cfg.head_hidden,), cfg.head_hidden
+    a = _rng(s, (2, kind, t)).standard_normal(shape, dtype=np.float32) * np.float32(1.0 / np.sqrt(fan))
+    return _finish(cfg, a)
+
+
+def io_banks(cfg: Workload, seed: Optional[int] = None):
+    """{(0, 0, kind): bank} of the tokenizer and the head, in the library's
+    layouts (bf16 bit patterns for bf16 workloads)."""
+    out = {}
+    for kind in IO_KINDS:
+        if kind == K_TOK_UP:
+            a = np.concatenate([io_slice(cfg, kind, t, seed) for t in range(cfg.T)], axis=0)
+        elif kind == K_TOK_DOWN:
+            a = np.stack([io_slice(cfg, kind, t, seed) for t in range(cfg.T)])
+        else:
+            a = io_slice(cfg, kind, 0, seed)
+        out[(0, 0, kind)] = f32_to_bf16_bits(a) if cfg.bf16_values else a
+    return out
 
 
 def _norm_param(cfg: Workload, layer: int, sub: int, kind: int, seed: Optional[int]) -> np.ndarray:
@@ -373,6 +464,16 @@ class WeightSource:
         self.seed = seed
 
     def __call__(self, layer: int, sub: int, kind: int, p: int) -> np.ndarray:
+        if kind in IO_KINDS:
+            if self.banks is not None and (0, 0, kind) in self.banks:
+                b = self.banks[(0, 0, kind)]
+                if kind == K_TOK_UP:
+                    lo, hi = self.cfg.io_rows(kind, p)
+                    b = b[lo:hi]
+                elif kind == K_TOK_DOWN:
+                    b = b[p]
+                return bf16_bits_to_f32(b) if b.dtype == np.uint16 else b
+            return io_slice(self.cfg, kind, p, self.seed)
         if kind in NORM_KINDS:
             if self.banks is not None and (layer, sub, kind) in self.banks:
                 b = self.banks[(layer, sub, kind)]

@@ -42,6 +42,7 @@ __all__ = [
     "mx_dequantize", "mx_round", "swiglu_mx",
     "layernorm", "gelu", "pffn", "rankmixer_block", "rankmixer_ffn_sublayer", "rankmixer_stack",
     "rankmixer_flops_per_sample", "relu_route", "relu_moe",
+    "relu", "mlp2", "group_offsets", "tokenize", "head", "model_forward", "io_flops_per_sample",
 ]
 
 BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
@@ -584,3 +585,81 @@ def rankmixer_flops_per_sample(cfg) -> int:
     if cfg.E == 0:
         return cfg.L * cfg.T * 2 * 2 * cfg.D * cfg.hidden_rev
     return cfg.L * cfg.T * 2 * (2 * cfg.D * cfg.E * cfg.expert_hidden + cfg.D * cfg.E)
+
+
+# ---------------------------------------------------------------------------
+# Model front and back   [TML] 2.2 Eq. 1-4 (semantic group-wise tokenizer,
+# global token), [TML] 2.1 (mean pooling of the output tokens for the
+# prediction), [TML-README] block diagram (group MLPs + global MLP -> tokens;
+# mean-pool over tokens -> projection head -> logit)
+#
+# Readings (the pages name the MLPs but not their form):
+# * every MLP here (MLP_i of a group, MLP_g of the global token, the
+#   projection head) is two bias-free linear maps with ReLU between them,
+#   v -> ReLU(v W1) W2 (bias off as everywhere in the model, [TML-README]);
+# * the tokenizer's input is the embeddings e of Eq. 1 already concatenated
+#   group by group, [n, F], F = sum of the T - 1 group widths; group t
+#   (1 <= t < T) is columns [off_t, off_t + d_t); the global token reads all
+#   F columns (Eq. 3) and is position 0 (Eq. 4);
+# * the head averages the T output tokens, applies its MLP and returns one
+#   logit per sample (one task; no sigmoid -- the pages end at the logit);
+# * bf16 contract as in the stack: the hidden ReLU outputs, the tokens X
+#   and the pooled mean are rounded to bf16 once each; sums and the logit
+#   stay unrounded.
+# ---------------------------------------------------------------------------
+
+_K_TOK_UP, _K_TOK_DOWN, _K_HEAD_UP, _K_HEAD_DOWN = 16, 17, 18, 19
+
+
+def relu(z: np.ndarray) -> np.ndarray:
+    z = np.asarray(z, dtype=np.float64)
+    return np.where(z > 0, z, 0.0)
+
+
+def mlp2(v: np.ndarray, w1: np.ndarray, w2: np.ndarray, rho: bool = False) -> np.ndarray:
+    """ReLU(v W1) W2, no biases; in bf16 mode the hidden is rounded once."""
+    h = _rho(relu(np.asarray(v, dtype=np.float64) @ np.asarray(w1, dtype=np.float64)), rho)
+    return h @ np.asarray(w2, dtype=np.float64)
+
+
+def group_offsets(group_widths) -> np.ndarray:
+    """Column offset of each semantic group in the concatenated embeddings."""
+    return np.concatenate([[0], np.cumsum(np.asarray(group_widths, dtype=np.int64))])
+
+
+def tokenize(emb: np.ndarray, cfg, weights: WeightGetter, rho: bool = False) -> np.ndarray:
+    """[TML] Eq. 2-4: X_t = MLP_t(group t's embeddings) for t = 1..T-1, the
+    global token X_0 = MLP_g(all F columns). emb [n, F] -> X [n, T, D]."""
+    emb = np.asarray(emb, dtype=np.float64)
+    off = group_offsets(cfg.groups)
+    if len(cfg.groups) != cfg.T - 1 or emb.shape[1] != off[-1]:
+        raise ValueError("need T - 1 groups whose widths sum to the embedding width")
+    X = np.empty((emb.shape[0], cfg.T, cfg.D))
+    for t in range(cfg.T):
+        v = emb if t == 0 else emb[:, off[t - 1]:off[t]]
+        X[:, t] = mlp2(v, weights(0, 0, _K_TOK_UP, t), weights(0, 0, _K_TOK_DOWN, t), rho)
+    return _rho(X, rho)
+
+
+def head(Y: np.ndarray, cfg, weights: WeightGetter, rho: bool = False) -> np.ndarray:
+    """[TML] 2.1, [TML-README]: mean over the T output tokens, then the
+    projection MLP to one logit per sample. Y [n, T, D] -> logits [n]."""
+    pooled = _rho(np.mean(np.asarray(Y, dtype=np.float64), axis=1), rho)
+    w2 = np.asarray(weights(0, 0, _K_HEAD_DOWN, 0), dtype=np.float64).reshape(-1, 1)
+    return mlp2(pooled, weights(0, 0, _K_HEAD_UP, 0), w2, rho)[:, 0]
+
+
+def model_forward(emb: np.ndarray, cfg, weights: WeightGetter, rho: Optional[bool] = None) -> np.ndarray:
+    """Embeddings -> tokens -> the block stack -> mean-pool head -> logits."""
+    if rho is None:
+        rho = cfg.dtype in ("bf16", "mxfp8")
+    X = tokenize(emb, cfg, weights, rho)
+    Y = rankmixer_stack(X, cfg, weights, rho) if cfg.rankmixer else stack_forward(X, cfg, weights, rho)
+    return head(Y, cfg, weights, rho)
+
+
+def io_flops_per_sample(cfg) -> int:
+    """GEMM FLOPs of the tokenizer and the head for one sample."""
+    F = int(np.sum(cfg.groups))
+    tok = 2 * (2 * F * cfg.tok_hidden + cfg.T * cfg.tok_hidden * cfg.D)
+    return tok + 2 * (cfg.D * cfg.head_hidden + cfg.head_hidden)
