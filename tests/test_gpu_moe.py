@@ -5,8 +5,8 @@ import pytest
 
 import datagen as dg
 import oracle as orc
-from gpu_common import (TOL, context, drop, oracle_sublayer, require_gpu, row_err, sample_rows,
-                        say, stream, to_dev, to_np)
+from gpu_common import (TOL, check_routing, check_xhat_and_route, context, drop, oracle_sublayer, require_gpu,
+                        route_gpu, route_oracle, row_err, sample_rows, say, stream, to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -15,83 +15,6 @@ SMALL_MOE = dg.Workload("small_moe_bf16", B=300, T=4, H=4, D=128, L=3, E=16, top
                         expert_hidden=128, shared_hidden=256, alpha=4.0, gap=2, seed=31)
 SMALL_MOE_F32 = SMALL_MOE.with_(name="small_moe_f32", dtype="f32", B=64, D=32, E=6, top_k=2,
                                 expert_hidden=16, shared_hidden=24, alpha=3.0, seed=32)
-
-DELTA = {"bf16": 1e-3, "f32": 1e-5}
-
-
-def _route_gpu(ctx, wl, layer, sub, xd, B):
-    import torch
-    P = wl.positions(sub)
-    idx = torch.empty((B, P, wl.top_k), dtype=torch.int32, device="cuda")
-    gate = torch.empty((B, P, wl.top_k), dtype=torch.float32, device="cuda")
-    ctx.moe_route(layer, sub, xd, B, idx, gate, stream())
-    torch.cuda.synchronize()
-    return idx.cpu().numpy(), gate.cpu().numpy().astype(np.float64)
-
-
-def _route_oracle(wl, ws, layer1, sub, x_rows):
-    """Oracle routing of rows x_rows [n, T, D] (block layout).
-
-    Also returns, per (row, position), a bound on how far the logits can move
-    because the GPU rounds x_hat from fp32 and the oracle from fp64: an element
-    whose exact value lies within 1e-4 ulp of a bf16 rounding midpoint may round
-    either way (the fp32 value carries a relative error of a few 2^-24, i.e.
-    < 1e-4 of a bf16 ulp), changing logit e by at most ulp_i * |Wr[i, e]|."""
-    rho = wl.dtype == "bf16"
-    v = orc.mix(x_rows, wl.H) if sub == 0 else x_rows
-    n, P, W = v.shape
-    out, bound = [], []
-    for p in range(P):
-        z = orc.rmsnorm(v[:, p], ws(layer1, sub, dg.K_NORM_GAIN, 0), wl.eps)
-        wr = ws(layer1, sub, dg.K_ROUTER, p).astype(np.float64)
-        if rho:
-            _, ex = np.frexp(z)
-            ulp = np.ldexp(1.0, ex - 8)
-            frac = z / ulp - np.floor(z / ulp)
-            near = np.abs(frac - 0.5) < 1e-4
-            bound.append(np.max((near * ulp) @ np.abs(wr), axis=-1))
-            xh = orc.round_bf16(z)
-        else:
-            bound.append(np.zeros(n))
-            xh = z
-        out.append(orc.route(xh, wr, wl.top_k, wl.gate_scale))
-    idx = np.stack([o[0] for o in out], 1)
-    gate = np.stack([o[1] for o in out], 1)
-    logits = np.stack([o[2] for o in out], 1)
-    return idx, gate, logits, np.stack(bound, 1)
-
-
-def _check_routing(wl, idx_g, gate_g, idx_o, gate_o, logits, bound):
-    """Per (row, position) band d = max(delta, 2.05 * bound): indices must be
-    exact where the k-th/(k+1)-th logit margin exceeds d (each logit can move
-    by at most `bound`, plus fp32 accumulation slack inside delta); the other
-    rows must be d-valid. Gates within 1e-5 relative plus the effect of the
-    x_hat rounding bound (softmax: |d log pi| <= 2 max |d logit|).
-    Returns the number of banded rows."""
-    k, E = wl.top_k, logits.shape[-1]
-    dband = np.maximum(DELTA[wl.dtype], 2.05 * bound)
-    srt = -np.sort(-logits, axis=-1)
-    kth = srt[..., k - 1]
-    margin = kth - (srt[..., k] if k < E else -np.inf)
-    clear = margin > dband
-    assert np.array_equal(idx_g[clear], idx_o[clear])
-    rtol = 1e-5 + 2.1 * bound
-    rel = np.abs(gate_g - gate_o) / np.abs(gate_o)
-    assert np.all(rel[clear] <= rtol[clear][:, None]), float(np.max(rel[clear]))
-    band = np.argwhere(~clear)
-    for pos in band:
-        r = tuple(pos)
-        d = dband[r]
-        chosen = set(idx_g[r].tolist())
-        assert len(chosen) == k
-        l = logits[r]
-        for e in range(E):
-            if e in chosen:
-                assert l[e] >= kth[r] - d
-            else:
-                assert l[e] <= kth[r] + d
-    return len(band)
-
 
 @pytest.mark.parametrize("which", ["small_bf16", "small_f32"])
 def test_small_moe_stack_all_rows(which):
@@ -123,15 +46,21 @@ def test_route_matches_oracle(which, sub):
     say("route", which, sub)
     ctx, banks, ws = context(which, wl)
     x = dg.make_x(wl)
-    idx_g, gate_g = _route_gpu(ctx, wl, 0, sub, to_dev(wl, x), wl.B)
+    idx_g, gate_g = route_gpu(ctx, wl, 0, sub, to_dev(wl, x), wl.B)
     rows = sample_rows(wl.B, 512, seed=sub) if wl.B > 512 else np.arange(wl.B)
-    idx_o, gate_o, logits, bound = _route_oracle(wl, ws, 1, sub, x[rows].astype(np.float64))
-    nb = _check_routing(wl, idx_g[rows], gate_g[rows], idx_o, gate_o, logits, bound)
+    idx_o, gate_o, logits, bound = route_oracle(wl, ws, 1, sub, x[rows].astype(np.float64))
+    nb = check_routing(wl, idx_g[rows], gate_g[rows], idx_o, gate_o, logits, bound)
     say("route strict-gate rows", which, sub, int(np.sum(bound == 0)), "max bound", float(bound.max()))
     say("route banded rows", which, sub, nb, "of", idx_o.shape[0] * idx_o.shape[1])
     # every row's selection is k distinct experts
     s = np.sort(idx_g, axis=-1)
     assert np.all(s[..., 1:] != s[..., :-1]) and s.min() >= 0 and s.max() < wl.E
+    if wl.dtype == "bf16":
+        xhat = xhat_gpu(ctx, wl, 0, sub, to_dev(wl, x), wl.B)
+        flips, nb2 = check_xhat_and_route(wl, ws, 1, sub, x[rows].astype(np.float64), xhat[rows],
+                                          idx_g[rows], gate_g[rows])
+        say("route from the GPU's x_hat", which, sub, "x_hat elements on the other neighbour", flips,
+            "banded rows", nb2)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -153,8 +82,8 @@ def test_route_exact_ties_lowest_index(dtype):
     ws = dg.WeightSource(wl, banks)
     x = np.where(rng.random((wl.B, wl.T, wl.D)) < 0.5, -1.0, 1.0).astype(np.float32)
     for sub in (0, 1):
-        idx_g, gate_g = _route_gpu(ctx, wl, 0, sub, to_dev(wl, x), wl.B)
-        idx_o, gate_o, logits, _ = _route_oracle(wl, ws, 1, sub, x.astype(np.float64))
+        idx_g, gate_g = route_gpu(ctx, wl, 0, sub, to_dev(wl, x), wl.B)
+        idx_o, gate_o, logits, _ = route_oracle(wl, ws, 1, sub, x.astype(np.float64))
         if dtype == "bf16":
             # x_hat = +-1 exactly, logits are exact dyadic sums: routing must match bit for bit
             np.testing.assert_array_equal(idx_g, idx_o)
@@ -171,15 +100,73 @@ def test_route_exact_ties_lowest_index(dtype):
     ctx.close()
 
 
+def buckets_gpu(ctx, wl, layer, sub, xd, B):
+    import torch
+    P = wl.positions(sub)
+    counts = torch.empty((P, wl.E), dtype=torch.int32, device="cuda")
+    rows = torch.empty((P, B * wl.top_k), dtype=torch.int32, device="cuda")
+    ctx.moe_buckets(layer, sub, xd, B, None, counts, rows, stream())
+    torch.cuda.synchronize()
+    return counts.cpu().numpy(), rows.cpu().numpy()
+
+
+def xhat_gpu(ctx, wl, layer, sub, xd, B):
+    """The normalised rows the sub-layer's experts consume, [B, P, W]."""
+    import torch
+    P, W = wl.positions(sub), wl.width(sub)
+    xh = torch.empty((P, B, W), dtype=torch.bfloat16, device="cuda")
+    ctx.moe_buckets(layer, sub, xd, B, xh, None, None, stream())
+    torch.cuda.synchronize()
+    return to_np(xh).transpose(1, 0, 2)
+
+
+def check_buckets(idx, counts, rows, E):
+    """MoEPermute lists against the routing table: per position, expert e's
+    count is the number of (row, slot) entries routed to it, its list starts
+    at the exclusive prefix sum of the counts, and holds exactly those
+    entries b * top_k + slot in ascending order (stable). Bit-exact."""
+    B, P, k = idx.shape
+    for p in range(P):
+        flat = idx[:, p, :].reshape(-1)
+        want = np.bincount(flat, minlength=E)
+        np.testing.assert_array_equal(counts[p], want)
+        off = np.concatenate([[0], np.cumsum(want)])
+        for e in range(E):
+            np.testing.assert_array_equal(rows[p, off[e]:off[e + 1]], np.nonzero(flat == e)[0])
+        assert off[E] == B * k
+
+
+@pytest.mark.parametrize("which", ["small_bf16", "w4"])
+@pytest.mark.parametrize("sub", [0, 1])
+def test_buckets_match_routing(which, sub):
+    require_gpu()
+    wl = {"small_bf16": SMALL_MOE, "w4": dg.WORKLOADS[4]}[which]
+    say("buckets", which, sub)
+    ctx, banks, ws = context(which, wl)
+    xd = to_dev(wl, dg.make_x(wl))
+    idx_g, _ = route_gpu(ctx, wl, 0, sub, xd, wl.B)
+    counts, rows = buckets_gpu(ctx, wl, 0, sub, xd, wl.B)
+    check_buckets(idx_g, counts, rows, wl.E)
+    # a smaller batch through the same context: lists of the first rows only
+    B2 = wl.B // 3 + 1
+    idx2, _ = route_gpu(ctx, wl, 0, sub, xd[:B2].contiguous(), B2)
+    c2, r2 = buckets_gpu(ctx, wl, 0, sub, xd[:B2].contiguous(), B2)
+    np.testing.assert_array_equal(idx2, idx_g[:B2])
+    check_buckets(idx2, c2, r2, wl.E)
+
+
 @pytest.mark.parametrize("sub", [0, 1])
 def test_skewed_routing_and_empty_buckets(sub):
     """Positive inputs, positive router columns except expert 5 (all
     negative): expert 5's bucket is always empty, and expert 3 (column x10)
-    is chosen by every row, so its bucket holds all B rows (several tiles)."""
+    is chosen by every row, so its bucket holds all B rows (16 tiles). The
+    down matrices at full scale and, in the Revert sub-layer, a zero
+    residual make the sub-layer output F itself, so the all-rows bucket's
+    expert outputs are what the comparison sees."""
     require_gpu()
     import torch
     from token_moe_amd import runner
-    wl = SMALL_MOE.with_(name="skew", L=1)
+    wl = SMALL_MOE.with_(name="skew", L=1, B=1000, down_scale=1.0)
     banks = dg.weight_banks(wl)
     for s in (0, 1):
         wr = np.abs(dg.bf16_bits_to_f32(banks[(1, s, dg.K_ROUTER)]))
@@ -189,24 +176,68 @@ def test_skewed_routing_and_empty_buckets(sub):
     ctx = runner.make_context(wl, banks)
     ws = dg.WeightSource(wl, banks)
     x = np.abs(dg.make_x(wl))
-    resid = dg.make_x(wl, seed=77)
-    xd, rd = to_dev(wl, x), to_dev(wl, resid)
-    idx_g, _ = _route_gpu(ctx, wl, 0, sub, xd, wl.B)
+    xd = to_dev(wl, x)
+    idx_g, gate_g = route_gpu(ctx, wl, 0, sub, xd, wl.B)
     assert not np.any(idx_g == 5)
     assert np.all(idx_g[..., 0] == 3)
+    counts, rows = buckets_gpu(ctx, wl, 0, sub, xd, wl.B)
+    check_buckets(idx_g, counts, rows, wl.E)
+    assert np.all(counts[:, 5] == 0) and np.all(counts[:, 3] == wl.B)
     out = torch.empty_like(xd)
+    zero = np.zeros(x.shape)
     if sub == 0:
         ctx.sublayer_forward(0, 0, xd, None, None, out, wl.B, stream())
-        torch.cuda.synchronize()
-        ref = oracle_sublayer(wl, ws, 1, 0, x.astype(np.float64))
     else:
-        ctx.sublayer_forward(0, 1, xd, rd, None, out, wl.B, stream())
-        torch.cuda.synchronize()
-        ref = oracle_sublayer(wl, ws, 1, 1, x.astype(np.float64), resid.astype(np.float64))
+        ctx.sublayer_forward(0, 1, xd, torch.zeros_like(xd), None, out, wl.B, stream())
+    torch.cuda.synchronize()
+    flips, nb = check_xhat_and_route(wl, ws, 1, sub, x.astype(np.float64), xhat_gpu(ctx, wl, 0, sub, xd, wl.B),
+                                     idx_g, gate_g)
+    say("skew: x_hat elements on the other neighbour", flips, "banded", nb)
+    idx_o, gate_o, logits, bound = route_oracle(wl, ws, 1, sub, x.astype(np.float64))
+    check_routing(wl, idx_g, gate_g, idx_o, gate_o, logits, bound)
+    ref = oracle_sublayer(wl, ws, 1, sub, x.astype(np.float64), None if sub == 0 else zero, route=idx_g)
     err = row_err(to_np(out), ref)
     say("skewed err", sub, err)
     assert err <= TOL["bf16"]
     ctx.close()
+
+
+@pytest.mark.parametrize("sub", [0, 1])
+def test_non_finite_row_keeps_routing_in_range(sub):
+    """A row of +inf inputs makes its normalised row NaN. Its routing must
+    still name top_k distinct experts in [0, E) (every bucket entry stays in
+    range), and every other row's routing and buckets are those of the same
+    batch without it."""
+    require_gpu()
+    import torch
+    wl = SMALL_MOE
+    ctx, banks, ws = context("small_bf16", wl)
+    x = dg.make_x(wl)
+    bad = 17
+    xb = x.copy()
+    xb[bad] = np.inf
+    xd, xbd = to_dev(wl, x), to_dev(wl, xb)
+    idx_ok, gate_ok = route_gpu(ctx, wl, 0, sub, xd, wl.B)
+    idx_b, gate_b = route_gpu(ctx, wl, 0, sub, xbd, wl.B)
+    s = np.sort(idx_b[bad], axis=-1)
+    assert s.min() >= 0 and s.max() < wl.E and np.all(s[:, 1:] != s[:, :-1])
+    keep = np.arange(wl.B) != bad
+    np.testing.assert_array_equal(idx_b[keep], idx_ok[keep])
+    np.testing.assert_array_equal(gate_b[keep], gate_ok[keep])
+    counts, rows = buckets_gpu(ctx, wl, 0, sub, xbd, wl.B)
+    check_buckets(idx_b, counts, rows, wl.E)
+    out = torch.empty_like(xd)
+    if sub == 0:
+        ctx.sublayer_forward(0, 0, xbd, None, None, out, wl.B, stream())
+    else:
+        ctx.sublayer_forward(0, 1, xbd, xd, None, out, wl.B, stream())
+    torch.cuda.synchronize()
+    y = to_np(out)
+    ref = oracle_sublayer(wl, ws, 1, sub, x[keep].astype(np.float64),
+                          None if sub == 0 else x[keep].astype(np.float64), route=idx_b[keep])
+    err = row_err(y[keep], ref)
+    say("non-finite row: other rows err", sub, err)
+    assert err <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("sub", [0, 1])
@@ -267,11 +298,15 @@ def test_large_moe_sublayer_and_route_full_batch(sub):
     x = dg.make_x(wl)
     xd = to_dev(wl, x)
     # routing of sampled rows, teacher-forced on the same input
-    idx_g, gate_g = _route_gpu(ctx, wl, 0, sub, xd, wl.B)
+    idx_g, gate_g = route_gpu(ctx, wl, 0, sub, xd, wl.B)
     rows = sample_rows(wl.B, 192, seed=50 + sub)
-    idx_o, gate_o, logits, bound = _route_oracle(wl, ws, 1, sub, x[rows].astype(np.float64))
-    nb = _check_routing(wl, idx_g[rows], gate_g[rows], idx_o, gate_o, logits, bound)
+    idx_o, gate_o, logits, bound = route_oracle(wl, ws, 1, sub, x[rows].astype(np.float64))
+    nb = check_routing(wl, idx_g[rows], gate_g[rows], idx_o, gate_o, logits, bound)
     say("large route banded rows", sub, nb)
+    xhat = xhat_gpu(ctx, wl, 0, sub, xd, wl.B)
+    flips, nb2 = check_xhat_and_route(wl, ws, 1, sub, x[rows].astype(np.float64), xhat[rows], idx_g[rows],
+                                      gate_g[rows])
+    say("large route from the GPU's x_hat: other-neighbour elements", flips, "banded", nb2)
     # one sub-layer at the full batch, oracle on sampled rows
     out = torch.empty_like(xd)
     rows = sample_rows(wl.B, 10, seed=60 + sub)
