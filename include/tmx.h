@@ -112,7 +112,15 @@ typedef enum tmx_weight_kind {
    * the inference router, EXP_UP [T, E, D, h_e] and EXP_DOWN [T, E, h_e, D]
    * the experts' W1 and W2. */
   TMX_W_EXP_BIAS_UP = 14,  /* [P, E, h_e] experts' b1, optional            */
-  TMX_W_EXP_BIAS_DOWN = 15 /* [P, E, W]   experts' b2, optional            */
+  TMX_W_EXP_BIAS_DOWN = 15, /* [P, E, W]   experts' b2, optional           */
+  /* The model's front and back (tmx_load_io_weights; F = sum of the group
+   * widths, h the tokenizer hidden, h_head the head hidden):            */
+  TMX_W_TOK_UP = 16,    /* [2F, h]   first layers of the tokenizer MLPs: the
+                           global token's [F, h], then each group's [d_t, h]
+                           in group order (Eq. 2-3)                        */
+  TMX_W_TOK_DOWN = 17,  /* [T, h, D] second layers, token 0 (global) first  */
+  TMX_W_HEAD_UP = 18,   /* [D, h_head] projection head, first layer         */
+  TMX_W_HEAD_DOWN = 19  /* [h_head]  projection head, second layer (-> logit) */
 } tmx_weight_kind;
 
 /* Model configuration; the pages' problem statement (B, T, H, D, hidden, E,
@@ -199,19 +207,22 @@ tmx_status tmx_block_stack_forward(tmx_ctx* ctx, const void* x_in, void* x_out,
 tmx_status tmx_moe_route(tmx_ctx* ctx, int layer, int sublayer, const void* x,
                          int B, int32_t* idx, float* gate, void* stream);
 
-/* The expert-first row lists of one MoE sub-layer (MoEPermute,
- * TokenMixer-Large summary section 2.5.1), for checks: x is the sub-layer's
- * input in block layout [B, T, D] (device); the sub-layer's router and bucket
- * kernels run on it exactly as in the forward, and their lists are copied
- * out: counts [P, E] int32 (rows routed to expert e at position p) and rows
- * [P, B*top_k] int32, where position p's entries are expert 0's, then expert
- * 1's, ... (expert e's list starts at the exclusive prefix sum of counts[p])
- * and each entry is b*top_k + slot, in ascending order within a list.
- * Device pointers; uses the context's workspace, so it must not overlap a
- * forward on another stream.  TMX_ERR_UNSUPPORTED unless the context is a
- * bf16 TokenMixer-Large MoE one. */
+/* The normalised rows and the expert-first row lists of one MoE sub-layer
+ * (RMSNorm, TokenMixer-Large summary section 2.3.3; MoEPermute, section
+ * 2.5.1), for checks: x is the sub-layer's input in block layout [B, T, D]
+ * (device); the sub-layer's router and bucket kernels run on it exactly as
+ * in the forward, and what they wrote is copied out to each non-NULL
+ * output (device pointers): xhat [P, B, W] bf16 (16-byte aligned), the rows
+ * the experts consume; counts [P, E] int32 (rows routed to expert e at
+ * position p); rows [P, B*top_k] int32, where position p's entries are
+ * expert 0's, then expert 1's, ... (expert e's list starts at the exclusive
+ * prefix sum of counts[p]) and each entry is b*top_k + slot, in ascending
+ * order within a list.  Uses the context's workspace, so it must not
+ * overlap a forward on another stream.  TMX_ERR_UNSUPPORTED unless the
+ * context is a bf16 TokenMixer-Large MoE one. */
 tmx_status tmx_moe_buckets(tmx_ctx* ctx, int layer, int sublayer, const void* x,
-                           int B, int32_t* counts, int32_t* rows, void* stream);
+                           int B, void* xhat, int32_t* counts, int32_t* rows,
+                           void* stream);
 
 /* One sub-layer, for teacher-forced checks; runs the same kernels as the
  * forward.  All tensors are [B, T, D] in block layout (device).
@@ -261,6 +272,50 @@ typedef enum tmx_perm_form {
 tmx_status tmx_debug_permute(tmx_ctx* ctx, const void* in, void* out, int B,
                              int inverse, int form, void* stream);
 
+/* ---- The model around the stack: tokenizer front and mean-pool head ----
+ * TokenMixer-Large summary section 2.2 (Eq. 1-4) and section 2.1; the
+ * tokenmixerlarge README's block diagram (group MLPs + global MLP -> tokens;
+ * mean-pool over tokens -> projection head -> logit).  The tokenizer maps
+ * the concatenated feature embeddings emb [B, F] (F = sum of the T - 1
+ * semantic group widths d_t, group t in columns [sum_{u<t} d_u, +d_t)) to
+ * the tokens X [B, T, D]: X[:, t] = MLP_t(group t's columns) for t >= 1
+ * (Eq. 2) and the global token X[:, 0] = MLP_g(all F columns) (Eq. 3-4).
+ * The head averages the T tokens of Y [B, T, D] and maps the mean to one
+ * logit per sample.  Every MLP is v -> ReLU(v W1) W2 without biases.  bf16:
+ * the hidden ReLU outputs, the tokens and the pooled mean are rounded to
+ * bf16 once each; GEMMs accumulate in fp32; the logit is fp32. */
+
+/* Declare the tokenizer and head of a bf16 (or MXFP8) context once:
+ * n_groups must be T - 1, group widths multiples of 32, tok_hidden in
+ * {128, 256, 512, 768}, head_hidden in {128, 256, 512}, D in {128, 256, 512,
+ * 768} (TMX_ERR_UNSUPPORTED otherwise).  Allocates their weight storage
+ * and two [B_max, T, D] buffers for tmx_model_forward.  TMX_ERR_STATE if
+ * called twice. */
+tmx_status tmx_set_model_io(tmx_ctx* ctx, const int32_t* group_widths, int n_groups,
+                            int tok_hidden, int head_hidden);
+
+/* Copy one tokenizer or head bank (TMX_W_TOK_UP .. TMX_W_HEAD_DOWN, row-major
+ * bf16, host or device `src`, exact `nbytes`) into the context and repack it
+ * into MFMA fragments.  Synchronous.  TMX_ERR_STATE before tmx_set_model_io. */
+tmx_status tmx_load_io_weights(tmx_ctx* ctx, int kind, const void* src, size_t nbytes,
+                               void* stream);
+
+/* X = tokenizer(emb): emb [B, F] bf16, x_out [B, T, D] bf16, device, 16-byte
+ * aligned, not overlapping; 1 <= B <= B_max.  TMX_ERR_STATE unless both
+ * tokenizer banks are loaded. */
+tmx_status tmx_tokenize(tmx_ctx* ctx, const void* emb, void* x_out, int B, void* stream);
+
+/* logits[b] = head(mean over t of y[b, t, :]): y [B, T, D] bf16 (device,
+ * 16-byte aligned), logits [B] float32 (device).  TMX_ERR_STATE unless both
+ * head banks are loaded. */
+tmx_status tmx_head(tmx_ctx* ctx, const void* y, float* logits, int B, void* stream);
+
+/* The whole model: logits = head(block stack(tokenizer(emb))), through the
+ * context's own token buffers; same arguments as tmx_tokenize / tmx_head.
+ * TMX_ERR_STATE unless every bank of the stack, tokenizer and head is
+ * loaded. */
+tmx_status tmx_model_forward(tmx_ctx* ctx, const void* emb, float* logits, int B, void* stream);
+
 /* Kernels of the library, as counted by tmx_kernel_times. */
 typedef enum tmx_kernel_kind {
   TMX_KERNEL_MLP_DENSE = 0,  /* fused per-position SwiGLU sub-layer (Eq. 12-18)  */
@@ -270,7 +325,9 @@ typedef enum tmx_kernel_kind {
   TMX_KERNEL_BUCKET = 4,     /* expert-first row lists (section 2.5.1 MoEPermute) */
   TMX_KERNEL_RMX_BLOCK = 5,  /* RankMixer block                                  */
   TMX_KERNEL_F32 = 6,        /* fp32 sub-layer                                   */
-  TMX_KERNEL_KINDS = 7
+  TMX_KERNEL_TOKENIZE = 7,   /* semantic group-wise tokenizer (Eq. 2-4)          */
+  TMX_KERNEL_HEAD = 8,       /* mean pool + projection head (section 2.1)       */
+  TMX_KERNEL_KINDS = 9
 } tmx_kernel_kind;
 
 /* Measurement: with enable = 1 every kernel the context enqueues from then

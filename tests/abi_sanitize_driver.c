@@ -97,12 +97,17 @@ int main(void) {
   EXPECT(tmx_load_weights(NULL, 0, 0, 1, NULL, 0, NULL) == TMX_ERR_INVALID_ARG, "load NULL");
   EXPECT(tmx_block_stack_forward(NULL, NULL, NULL, 1, NULL) == TMX_ERR_INVALID_ARG, "forward NULL");
   EXPECT(tmx_moe_route(NULL, 0, 0, NULL, 1, NULL, NULL, NULL) == TMX_ERR_INVALID_ARG, "route NULL");
-  EXPECT(tmx_moe_buckets(NULL, 0, 0, NULL, 1, NULL, NULL, NULL) == TMX_ERR_INVALID_ARG, "buckets NULL");
+  EXPECT(tmx_moe_buckets(NULL, 0, 0, NULL, 1, NULL, NULL, NULL, NULL) == TMX_ERR_INVALID_ARG, "buckets NULL");
   EXPECT(tmx_sublayer_forward(NULL, 0, 0, NULL, NULL, NULL, NULL, 1, NULL) == TMX_ERR_INVALID_ARG, "sublayer NULL");
   EXPECT(tmx_relu_route(NULL, 0, NULL, 1, NULL, NULL) == TMX_ERR_INVALID_ARG, "relu route NULL");
   EXPECT(tmx_debug_permute(NULL, NULL, NULL, 1, 0, 0, NULL) == TMX_ERR_INVALID_ARG, "permute NULL");
   EXPECT(tmx_set_kernel_timing(NULL, 1) == TMX_ERR_INVALID_ARG, "timing NULL");
   EXPECT(tmx_kernel_times(NULL, NULL, NULL, 0) == TMX_ERR_INVALID_ARG, "times NULL");
+  EXPECT(tmx_set_model_io(NULL, NULL, 0, 128, 128) == TMX_ERR_INVALID_ARG, "set model io NULL");
+  EXPECT(tmx_load_io_weights(NULL, TMX_W_TOK_UP, NULL, 0, NULL) == TMX_ERR_INVALID_ARG, "io weights NULL");
+  EXPECT(tmx_tokenize(NULL, NULL, NULL, 1, NULL) == TMX_ERR_INVALID_ARG, "tokenize NULL");
+  EXPECT(tmx_head(NULL, NULL, NULL, 1, NULL) == TMX_ERR_INVALID_ARG, "head NULL");
+  EXPECT(tmx_model_forward(NULL, NULL, NULL, 1, NULL) == TMX_ERR_INVALID_ARG, "model forward NULL");
   EXPECT(tmx_last_error(NULL) != NULL, "last error");
   printf("abi-sanitize ok %d\n", checks);
   return 0;

@@ -83,7 +83,9 @@ def test_status_and_enum_values_match_header(tmx):
                       ("TMX_W_NORM_BIAS", dg.K_NORM_BIAS), ("TMX_W_BIAS_UP", dg.K_BIAS_UP),
                       ("TMX_W_BIAS_DOWN", dg.K_BIAS_DOWN), ("TMX_BLOCK_TOKENMIXER_LARGE", 0),
                       ("TMX_BLOCK_RANKMIXER", tmx.TMX_BLOCK_RANKMIXER),
-                      ("TMX_W_EXP_BIAS_UP", dg.K_EXP_BIAS_UP), ("TMX_W_EXP_BIAS_DOWN", dg.K_EXP_BIAS_DOWN)]:
+                      ("TMX_W_EXP_BIAS_UP", dg.K_EXP_BIAS_UP), ("TMX_W_EXP_BIAS_DOWN", dg.K_EXP_BIAS_DOWN),
+                      ("TMX_W_TOK_UP", dg.K_TOK_UP), ("TMX_W_TOK_DOWN", dg.K_TOK_DOWN),
+                      ("TMX_W_HEAD_UP", dg.K_HEAD_UP), ("TMX_W_HEAD_DOWN", dg.K_HEAD_DOWN)]:
         m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
         assert m and int(m.group(1)) == val, name
 
@@ -182,9 +184,14 @@ def test_null_context_calls(tmx):
     assert lib.tmx_sublayer_forward(None, 0, 0, None, None, None, None, 1, None) == tmx.TMX_ERR_INVALID_ARG
     assert lib.tmx_debug_permute(None, None, None, 1, 0, 0, None) == tmx.TMX_ERR_INVALID_ARG
     assert lib.tmx_relu_route(None, 0, None, 1, None, None) == tmx.TMX_ERR_INVALID_ARG
-    assert lib.tmx_moe_buckets(None, 0, 0, None, 1, None, None, None) == tmx.TMX_ERR_INVALID_ARG
+    assert lib.tmx_moe_buckets(None, 0, 0, None, 1, None, None, None, None) == tmx.TMX_ERR_INVALID_ARG
     assert lib.tmx_set_kernel_timing(None, 1) == tmx.TMX_ERR_INVALID_ARG
     assert lib.tmx_kernel_times(None, None, None, 0) == tmx.TMX_ERR_INVALID_ARG
+    assert lib.tmx_set_model_io(None, None, 0, 128, 128) == tmx.TMX_ERR_INVALID_ARG
+    assert lib.tmx_load_io_weights(None, 16, None, 0, None) == tmx.TMX_ERR_INVALID_ARG
+    assert lib.tmx_tokenize(None, None, None, 1, None) == tmx.TMX_ERR_INVALID_ARG
+    assert lib.tmx_head(None, None, None, 1, None) == tmx.TMX_ERR_INVALID_ARG
+    assert lib.tmx_model_forward(None, None, None, 1, None) == tmx.TMX_ERR_INVALID_ARG
     assert lib.tmx_last_error(None)
 
 

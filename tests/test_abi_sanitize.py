@@ -15,7 +15,6 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CLANG = "/opt/rocm/llvm/bin/clang"
 CLANGXX = "/opt/rocm/llvm/bin/clang++"
-OTHER_OBJECTS = ("tmx_mlp.o", "tmx_route.o", "tmx_f32.o", "tmx_rankmixer.o")
 
 
 def test_host_abi_under_asan_ubsan(tmp_path):
@@ -26,7 +25,7 @@ def test_host_abi_under_asan_ubsan(tmp_path):
     if torch.cuda.is_available():
         pytest.skip("runs the no-device paths; a GPU is present")
     from token_moe_amd import build as b
-    objs = [os.path.join(b.OBJ, o) for o in OTHER_OBJECTS]
+    objs = [os.path.join(b.OBJ, src.replace(".hip", ".o")) for src in b.SOURCES if src != "tmx_host.hip"]
     if not all(os.path.exists(o) for o in objs):
         b.build()
     host_o = str(tmp_path / "tmx_host_asan.o")

@@ -25,6 +25,22 @@ struct Bank {
   bool loaded = false;
 };
 
+// The device workspace of a bf16 MoE sub-layer: everything its kernels
+// write besides the output. One region, carved by carve_moe_ws(); the
+// context's own region is laid out for B_max.
+struct MoeWs {
+  uint16_t* xhat = nullptr;   // [P][B][W] normalised rows (largest sub-layer)
+  int32_t* idx = nullptr;     // [B][P][k]
+  float* gate = nullptr;      // [B][P][k]
+  int* rows = nullptr;        // [P][B*k] expert-first row lists
+  int4* tiles = nullptr;      // [P][max_tiles] (expert, start, count, 0)
+  int* ntiles = nullptr;      // [P]
+  int* counts = nullptr;      // [P][E]
+  int* qhead = nullptr;       // [8] routed-MLP tile queues (zeroed by the bucket kernel)
+  int* hist = nullptr;        // [P][ceil(B/64)][E] router choices per 64-row chunk
+  uint16_t* part = nullptr;   // [B][P][k][W] gated expert outputs, bf16
+};
+
 }  // namespace
 
 struct tmx_ctx {
@@ -36,16 +52,21 @@ struct tmx_ctx {
   // workspace
   void* act[3] = {nullptr, nullptr, nullptr};  // [B_max, T, D] each
   void* xrev = nullptr;                        // [B_max, T, D]
-  uint16_t* xhat = nullptr;                    // [P][B_max][W] (max over sub-layers)
-  int32_t* idx = nullptr;                      // [B_max][P][k]
-  float* gate = nullptr;                       // [B_max][P][k]
-  int* rows = nullptr;                         // [P][B_max*k]
-  int4* tiles = nullptr;                       // [P][max_tiles]
-  int* ntiles = nullptr;                       // [P]
-  int* counts = nullptr;                       // [P][E]
-  int* qhead = nullptr;                        // [8] routed-MLP tile queues
-  int* hist = nullptr;                         // [P][ceil(B/64)][E] router choices per chunk
-  uint16_t* part = nullptr;                    // [B_max][P][k][W] bf16
+  MoeWs ws;                                    // bf16 MoE workspace, laid out for B_max
+  // model front and back (tmx_set_model_io)
+  struct Io {
+    bool set = false;
+    int F = 0, h = 0, hh = 0;
+    std::vector<int> widths;                   // T - 1 group widths
+    int4* pos = nullptr;                       // device [T]: (column offset, K, first W1 fragment, 0)
+    uint16_t* w1 = nullptr;                    // packed W1 of every position
+    uint16_t* w2 = nullptr;                    // packed [T] W2
+    uint16_t* hw1 = nullptr;                   // packed head W1
+    uint16_t* hw2 = nullptr;                   // head w2 [hh] bf16
+    void* xbuf = nullptr;                      // tmx_model_forward: tokens [B_max, T, D]
+    void* ybuf = nullptr;                      // tmx_model_forward: stack output
+    bool loaded[4] = {};
+  } io;
   std::vector<void*> allocs;
   std::string err;
   // per-kernel timing (tmx_set_kernel_timing): an event pair around every
@@ -301,6 +322,38 @@ int moe_max_tiles(const tmx_config& c, int sub, int B) {
   return (int)(((int64_t)B * c.top_k + bm - 1) / bm) + c.E;
 }
 
+// Lay the MoE workspace for batch B out from `base` (nullptr: sizes only);
+// returns the bytes used. Every array starts on a 256-byte boundary.
+size_t carve_moe_ws(const tmx_config& C, int64_t B, void* base, MoeWs* ws) {
+  const int Pmax = std::max(C.H, C.T);
+  int64_t tiles = 0, xh = 0, part = 0;
+  for (int sub = 0; sub < 2; ++sub) {
+    tiles = std::max<int64_t>(tiles, (int64_t)positions(C, sub) * moe_max_tiles(C, sub, (int)B));
+    xh = std::max<int64_t>(xh, (int64_t)positions(C, sub) * B * width(C, sub));
+    part = std::max<int64_t>(part, (int64_t)positions(C, sub) * B * C.top_k * width(C, sub));
+  }
+  const int64_t rk = B * Pmax * C.top_k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* p = base ? static_cast<char*>(base) + off : nullptr;
+    off += (bytes + 255) & ~size_t(255);
+    return p;
+  };
+  MoeWs w;
+  w.xhat = static_cast<uint16_t*>(take(xh * 2));
+  w.idx = static_cast<int32_t*>(take(rk * 4));
+  w.gate = static_cast<float*>(take(rk * 4));
+  w.rows = static_cast<int*>(take(rk * 4));
+  w.tiles = static_cast<int4*>(take(tiles * sizeof(int4)));
+  w.ntiles = static_cast<int*>(take(Pmax * 4));
+  w.counts = static_cast<int*>(take((int64_t)Pmax * C.E * 4));
+  w.qhead = static_cast<int*>(take(8 * 4));
+  w.hist = static_cast<int*>(take((int64_t)Pmax * ((B + 63) / 64) * C.E * 4));
+  w.part = static_cast<uint16_t*>(take(part * 2));
+  if (ws) *ws = w;
+  return off;
+}
+
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 bool sublayer_ready(tmx_ctx* c, int layer, int sub) {
@@ -359,7 +412,7 @@ tmx_status run_rmx(tmx_ctx* c, int layer, int part, const void* x_in, void* x_ou
 }
 
 tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const void* resid, const void* extra,
-                        void* x_out, int B, hipStream_t st) {
+                        void* x_out, int B, hipStream_t st, const MoeWs& ws) {
   const tmx_config& cfg = c->cfg;
   const int P = positions(cfg, sub), W = width(cfg, sub);
   RowMap map{cfg.T, cfg.D, cfg.D / cfg.H, sub == TMX_MIX ? 1 : 0};
@@ -407,19 +460,20 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   r.B = B; r.P = P; r.E = cfg.E; r.top_k = cfg.top_k; r.alpha = c->alpha; r.eps = cfg.eps; r.map = map;
   r.x = static_cast<const uint16_t*>(x_in); r.gain = gain;
   r.wr = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_ROUTER).ptr);
-  r.xhat = c->xhat; r.idx = c->idx; r.gate = c->gate; r.hist = c->hist;
+  r.xhat = ws.xhat; r.idx = ws.idx; r.gate = ws.gate; r.hist = ws.hist;
   tmx_status s = launch_timed(c, TMX_KERNEL_ROUTER, st, "router launch", [&] { return launch_norm_route(W, r, st); });
   if (s != TMX_OK) return s;
 
   BucketArgs k{};
   k.B = B; k.P = P; k.E = cfg.E; k.top_k = cfg.top_k; k.bm = bm; k.max_tiles = moe_max_tiles(cfg, sub, B);
-  k.idx = c->idx; k.rows = c->rows; k.tiles = c->tiles; k.ntiles = c->ntiles; k.counts = c->counts; k.qhead = c->qhead; k.hist = c->hist;
+  k.idx = ws.idx; k.rows = ws.rows; k.tiles = ws.tiles; k.ntiles = ws.ntiles; k.counts = ws.counts;
+  k.qhead = ws.qhead; k.hist = ws.hist;
   s = launch_timed(c, TMX_KERNEL_BUCKET, st, "bucket launch", [&] { return launch_bucket(k, st); });
   if (s != TMX_OK) return s;
 
-  a.xhat = c->xhat; a.top_k = cfg.top_k; a.E = cfg.E; a.max_tiles = k.max_tiles;
-  a.rows = c->rows; a.tiles = c->tiles; a.ntiles = c->ntiles; a.gate = c->gate; a.part = c->part;
-  a.qhead = c->qhead;
+  a.xhat = ws.xhat; a.top_k = cfg.top_k; a.E = cfg.E; a.max_tiles = k.max_tiles;
+  a.rows = ws.rows; a.tiles = ws.tiles; a.ntiles = ws.ntiles; a.gate = ws.gate; a.part = ws.part;
+  a.qhead = ws.qhead;
   a.hidden = cfg.expert_hidden;
   a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_EXP_GATE).ptr);
   a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_EXP_DOWN).ptr);
@@ -558,26 +612,10 @@ tmx_status tmx_create(const tmx_config* cfg, int device, tmx_ctx** out) {
   if ((s = dev_alloc(c, &c->xrev, act * es, "activations")) != TMX_OK) return bail(s);
 
   if (C.E > 0 && C.dtype == TMX_BF16) {
-    const int Pmax = std::max(C.H, C.T), Wmax = std::max(width(C, 0), width(C, 1));
-    int64_t tiles = 0, xh = 0, part = 0;
-    for (int sub = 0; sub < 2; ++sub) {
-      tiles = std::max<int64_t>(tiles, (int64_t)positions(C, sub) * moe_max_tiles(C, sub, C.B_max));
-      xh = std::max<int64_t>(xh, (int64_t)positions(C, sub) * C.B_max * width(C, sub));
-      part = std::max<int64_t>(part, (int64_t)positions(C, sub) * C.B_max * C.top_k * width(C, sub));
-    }
-    (void)Wmax;
-    const int64_t rk = (int64_t)C.B_max * Pmax * C.top_k;
-    if ((s = dev_alloc(c, (void**)&c->xhat, xh * 2, "x_hat")) != TMX_OK) return bail(s);
-    if ((s = dev_alloc(c, (void**)&c->idx, rk * 4, "routing")) != TMX_OK) return bail(s);
-    if ((s = dev_alloc(c, (void**)&c->gate, rk * 4, "routing")) != TMX_OK) return bail(s);
-    if ((s = dev_alloc(c, (void**)&c->rows, rk * 4, "bucket rows")) != TMX_OK) return bail(s);
-    if ((s = dev_alloc(c, (void**)&c->tiles, tiles * sizeof(int4), "bucket tiles")) != TMX_OK) return bail(s);
-    if ((s = dev_alloc(c, (void**)&c->ntiles, Pmax * 4, "bucket tiles")) != TMX_OK) return bail(s);
-    if ((s = dev_alloc(c, (void**)&c->counts, (int64_t)Pmax * C.E * 4, "bucket counts")) != TMX_OK) return bail(s);
-    if ((s = dev_alloc(c, (void**)&c->qhead, 8 * 4, "tile queues")) != TMX_OK) return bail(s);
-    if ((s = dev_alloc(c, (void**)&c->hist, (int64_t)Pmax * ((C.B_max + 63) / 64) * C.E * 4, "router counts")) != TMX_OK)
+    void* base = nullptr;
+    if ((s = dev_alloc(c, &base, carve_moe_ws(C, C.B_max, nullptr, nullptr), "MoE workspace")) != TMX_OK)
       return bail(s);
-    if ((s = dev_alloc(c, (void**)&c->part, part * 2, "expert partials")) != TMX_OK) return bail(s);
+    carve_moe_ws(C, C.B_max, base, &c->ws);
   }
   *out = c;
   return TMX_OK;
@@ -697,8 +735,12 @@ tmx_status tmx_load_weights(tmx_ctx* c, int layer, int sub, int kind, const void
   return TMX_OK;
 }
 
-tmx_status tmx_sublayer_forward(tmx_ctx* c, int layer, int sub, const void* x_in, const void* resid,
-                                const void* extra, void* x_out, int B, void* stream) {
+}  // extern "C"
+
+namespace {
+
+tmx_status check_sublayer_args(tmx_ctx* c, int layer, int sub, const void* x_in, const void* resid,
+                               const void* extra, void* x_out, int B) {
   if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
   tmx_status s;
   if (layer < 0 || layer >= c->cfg.L) return fail(c, TMX_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, c->cfg.L);
@@ -718,9 +760,20 @@ tmx_status tmx_sublayer_forward(tmx_ctx* c, int layer, int sub, const void* x_in
   if (overlaps(x_in, x_out, bytes)) return fail(c, TMX_ERR_INVALID_ARG, "x_in and x_out overlap");
   if (!sublayer_ready(c, layer, sub))
     return fail(c, TMX_ERR_STATE, "weights of layer %d sub-layer %d are not all loaded", layer, sub);
+  return TMX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tmx_status tmx_sublayer_forward(tmx_ctx* c, int layer, int sub, const void* x_in, const void* resid,
+                                const void* extra, void* x_out, int B, void* stream) {
+  tmx_status s = check_sublayer_args(c, layer, sub, x_in, resid, extra, x_out, B);
+  if (s != TMX_OK) return s;
   (void)hipSetDevice(c->device);
   if (is_rmx(c->cfg)) return run_rmx(c, layer, sub, x_in, x_out, B, as_stream(stream));
-  return run_sublayer(c, layer, sub, x_in, resid, extra, x_out, B, as_stream(stream));
+  return run_sublayer(c, layer, sub, x_in, resid, extra, x_out, B, as_stream(stream), c->ws);
 }
 
 tmx_status tmx_block_stack_forward(tmx_ctx* c, const void* x_in, void* x_out, int B, void* stream) {
@@ -747,7 +800,7 @@ tmx_status tmx_block_stack_forward(tmx_ctx* c, const void* x_in, void* x_out, in
   const void* cur = x_in;    // Y_{l-1}
   const void* save = x_in;   // Y_{l-g}: the output of the last multiple of g
   for (int l = 1; l <= L; ++l) {
-    if ((s = run_sublayer(c, l - 1, TMX_MIX, cur, nullptr, nullptr, c->xrev, B, st)) != TMX_OK) return s;
+    if ((s = run_sublayer(c, l - 1, TMX_MIX, cur, nullptr, nullptr, c->xrev, B, st, c->ws)) != TMX_OK) return s;
     const bool inter = g > 0 && l % g == 0 && l < L;
     void* dst = x_out;
     if (l < L)
@@ -756,7 +809,7 @@ tmx_status tmx_block_stack_forward(tmx_ctx* c, const void* x_in, void* x_out, in
           dst = cand;
           break;
         }
-    if ((s = run_sublayer(c, l - 1, TMX_REVERT, c->xrev, cur, inter ? save : nullptr, dst, B, st)) != TMX_OK)
+    if ((s = run_sublayer(c, l - 1, TMX_REVERT, c->xrev, cur, inter ? save : nullptr, dst, B, st, c->ws)) != TMX_OK)
       return s;
     if (g > 0 && l % g == 0) save = dst;
     cur = dst;
@@ -800,8 +853,8 @@ tmx_status tmx_moe_route(tmx_ctx* c, int layer, int sub, const void* x, int B, i
   return check_launch(c, launch_norm_route(W, r, st), "router launch");
 }
 
-tmx_status tmx_moe_buckets(tmx_ctx* c, int layer, int sub, const void* x, int B, int32_t* counts, int32_t* rows,
-                           void* stream) {
+tmx_status tmx_moe_buckets(tmx_ctx* c, int layer, int sub, const void* x, int B, void* xhat, int32_t* counts,
+                           int32_t* rows, void* stream) {
   if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
   const tmx_config& C = c->cfg;
   if (!is_moe(C) || is_rmx(C) || C.dtype != TMX_BF16)
@@ -811,7 +864,7 @@ tmx_status tmx_moe_buckets(tmx_ctx* c, int layer, int sub, const void* x, int B,
   if (sub != TMX_MIX && sub != TMX_REVERT) return fail(c, TMX_ERR_INVALID_ARG, "sublayer must be 0 or 1");
   if ((s = check_B(c, B)) != TMX_OK) return s;
   if ((s = check_act(c, x, "x")) != TMX_OK) return s;
-  if (!counts || !rows) return fail(c, TMX_ERR_INVALID_ARG, "counts and rows must be non-NULL");
+  if (xhat && !aligned16(xhat)) return fail(c, TMX_ERR_INVALID_ARG, "xhat must be 16-byte aligned");
   if (!bank(c, layer, sub, TMX_W_ROUTER).loaded)
     return fail(c, TMX_ERR_STATE, "router of layer %d sub-layer %d is not loaded", layer, sub);
   (void)hipSetDevice(c->device);
@@ -823,17 +876,20 @@ tmx_status tmx_moe_buckets(tmx_ctx* c, int layer, int sub, const void* x, int B,
   r.x = static_cast<const uint16_t*>(x);
   r.gain = static_cast<const float*>(bank(c, layer, sub, TMX_W_NORM_GAIN).ptr);
   r.wr = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_ROUTER).ptr);
-  r.xhat = c->xhat; r.idx = c->idx; r.gate = c->gate; r.hist = c->hist;
+  r.xhat = c->ws.xhat; r.idx = c->ws.idx; r.gate = c->ws.gate; r.hist = c->ws.hist;
   if ((s = check_launch(c, launch_norm_route(W, r, st), "router launch")) != TMX_OK) return s;
   BucketArgs k{};
   k.B = B; k.P = P; k.E = C.E; k.top_k = C.top_k; k.bm = mlp_bm(MLP_ROUTED, W); k.max_tiles = moe_max_tiles(C, sub, B);
-  k.idx = c->idx; k.rows = c->rows; k.tiles = c->tiles; k.ntiles = c->ntiles; k.counts = c->counts;
-  k.qhead = c->qhead; k.hist = c->hist;
+  k.idx = c->ws.idx; k.rows = c->ws.rows; k.tiles = c->ws.tiles; k.ntiles = c->ws.ntiles; k.counts = c->ws.counts;
+  k.qhead = c->ws.qhead; k.hist = c->ws.hist;
   if ((s = check_launch(c, launch_bucket(k, st), "bucket launch")) != TMX_OK) return s;
-  hipError_t e = hipMemcpyAsync(counts, c->counts, (size_t)P * C.E * 4, hipMemcpyDeviceToDevice, st);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(rows, c->rows, (size_t)P * B * C.top_k * 4, hipMemcpyDeviceToDevice, st);
-  return check_launch(c, e, "bucket copy");
+  hipError_t e = hipSuccess;
+  if (xhat) e = hipMemcpyAsync(xhat, c->ws.xhat, (size_t)P * B * W * 2, hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess && counts)
+    e = hipMemcpyAsync(counts, c->ws.counts, (size_t)P * C.E * 4, hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess && rows)
+    e = hipMemcpyAsync(rows, c->ws.rows, (size_t)P * B * C.top_k * 4, hipMemcpyDeviceToDevice, st);
+  return check_launch(c, e, "workspace copy");
 }
 
 tmx_status tmx_relu_route(tmx_ctx* c, int layer, const void* s, int B, float* gates, void* stream) {
@@ -871,6 +927,197 @@ tmx_status tmx_debug_permute(tmx_ctx* c, const void* in, void* out, int B, int i
   (void)hipSetDevice(c->device);
   return check_launch(c, launch_permute(in, out, B, C.T, C.D, C.H, (int)esize(C), inverse, form, as_stream(stream)),
                       "permute launch");
+}
+
+tmx_status tmx_set_model_io(tmx_ctx* c, const int32_t* group_widths, int n_groups, int tok_hidden,
+                            int head_hidden) {
+  if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
+  const tmx_config& C = c->cfg;
+  if (c->io.set) return fail(c, TMX_ERR_STATE, "the model's tokenizer and head are already set");
+  if (!group_widths) return fail(c, TMX_ERR_INVALID_ARG, "group_widths is NULL");
+  if (n_groups != C.T - 1 || n_groups < 1)
+    return fail(c, TMX_ERR_INVALID_ARG, "need T - 1 = %d semantic groups (token 0 is the global token), got %d",
+                C.T - 1, n_groups);
+  int64_t F = 0;
+  for (int i = 0; i < n_groups; ++i) {
+    if (group_widths[i] < 1) return fail(c, TMX_ERR_INVALID_ARG, "group %d has width %d", i, group_widths[i]);
+    F += group_widths[i];
+  }
+  if (tok_hidden < 1 || head_hidden < 1) return fail(c, TMX_ERR_INVALID_ARG, "hidden widths must be >= 1");
+  if (F > (1 << 20)) return fail(c, TMX_ERR_INVALID_ARG, "embedding width %lld too large", (long long)F);
+  if (C.dtype != TMX_BF16 && C.dtype != TMX_MXFP8)
+    return fail(c, TMX_ERR_UNSUPPORTED, "the tokenizer and head run on bf16 activations");
+  for (int i = 0; i < n_groups; ++i)
+    if (group_widths[i] % 32 != 0)
+      return fail(c, TMX_ERR_UNSUPPORTED, "group widths must be multiples of 32 (group %d: %d)", i, group_widths[i]);
+  if (!io_width_supported(C.D) || !io_tok_hidden_supported(tok_hidden) || !io_head_hidden_supported(head_hidden))
+    return fail(c, TMX_ERR_UNSUPPORTED,
+                "tokenizer/head need D in {128, 256, 512, 768}, tok_hidden in {128, 256, 512, 768} and head_hidden "
+                "in {128, 256, 512} (got %d, %d, %d)", C.D, tok_hidden, head_hidden);
+  (void)hipSetDevice(c->device);
+  {
+    auto& io = c->io;
+    const int T = C.T;
+    std::vector<int4> pos(T);
+    int64_t frag = 0, off = 0;
+    for (int t = 0; t < T; ++t) {
+      const int K = t == 0 ? (int)F : group_widths[t - 1];
+      pos[t] = make_int4(t == 0 ? 0 : (int)off, K, (int)frag, 0);
+      if (t > 0) off += K;
+      frag += (int64_t)(K / 16) * (tok_hidden / 32);
+    }
+    tmx_status s;
+    const int64_t act = (int64_t)C.B_max * C.T * C.D * 2;
+    if ((s = dev_alloc(c, (void**)&io.pos, T * sizeof(int4), "tokenizer table")) != TMX_OK ||
+        (s = dev_alloc(c, (void**)&io.w1, frag * FRAG_ELEMS * 2, "tokenizer W1")) != TMX_OK ||
+        (s = dev_alloc(c, (void**)&io.w2, (size_t)T * tok_hidden * C.D * 2, "tokenizer W2")) != TMX_OK ||
+        (s = dev_alloc(c, (void**)&io.hw1, (size_t)C.D * head_hidden * 2, "head W1")) != TMX_OK ||
+        (s = dev_alloc(c, (void**)&io.hw2, (size_t)head_hidden * 2, "head w2")) != TMX_OK ||
+        (s = dev_alloc(c, &io.xbuf, act, "model tokens")) != TMX_OK ||
+        (s = dev_alloc(c, &io.ybuf, act, "model stack output")) != TMX_OK)
+      return s;
+    hipError_t e = hipMemcpy(io.pos, pos.data(), T * sizeof(int4), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail(c, TMX_ERR_DEVICE, "tokenizer table: %s", hipGetErrorString(e));
+    io.widths.assign(group_widths, group_widths + n_groups);
+    io.F = (int)F;
+    io.h = tok_hidden;
+    io.hh = head_hidden;
+    io.set = true;
+  }
+  return TMX_OK;
+}
+
+tmx_status tmx_load_io_weights(tmx_ctx* c, int kind, const void* src, size_t nbytes, void* stream) {
+  if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
+  auto& io = c->io;
+  const tmx_config& C = c->cfg;
+  if (!io.set) return fail(c, TMX_ERR_STATE, "tmx_set_model_io has not been called");
+  if (kind < TMX_W_TOK_UP || kind > TMX_W_HEAD_DOWN)
+    return fail(c, TMX_ERR_INVALID_ARG, "kind %d is not a tokenizer or head bank", kind);
+  if (!src) return fail(c, TMX_ERR_INVALID_ARG, "src is NULL");
+  const size_t elems = kind == TMX_W_TOK_UP     ? (size_t)2 * io.F * io.h
+                       : kind == TMX_W_TOK_DOWN ? (size_t)C.T * io.h * C.D
+                       : kind == TMX_W_HEAD_UP  ? (size_t)C.D * io.hh
+                                                : (size_t)io.hh;
+  if (nbytes != elems * 2) return fail(c, TMX_ERR_INVALID_ARG, "nbytes %zu != expected %zu", nbytes, elems * 2);
+  (void)hipSetDevice(c->device);
+  hipStream_t st = as_stream(stream);
+  bool src_dev = false;
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, src) == hipSuccess) src_dev = attr.type == hipMemoryTypeDevice;
+  (void)hipGetLastError();
+  const hipMemcpyKind mk = src_dev ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+  hipError_t e;
+  if (kind == TMX_W_HEAD_DOWN) {
+    e = hipMemcpyAsync(io.hw2, src, nbytes, mk, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+  } else {
+    void* stage = nullptr;
+    e = hipMalloc(&stage, nbytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(c, e == hipErrorOutOfMemory ? TMX_ERR_OOM : TMX_ERR_DEVICE, "staging buffer: %s",
+                  hipGetErrorString(e));
+    }
+    e = hipMemcpyAsync(stage, src, nbytes, mk, st);
+    const uint16_t* sp = static_cast<const uint16_t*>(stage);
+    if (kind == TMX_W_TOK_UP) {
+      // position 0 (global token): rows [0, F); group t: the next d_t rows
+      int64_t row = 0, frag = 0;
+      for (int t = 0; t < C.T && e == hipSuccess; ++t) {
+        const int K = t == 0 ? io.F : io.widths[t - 1];
+        e = launch_pack(sp + row * io.h, io.w1 + frag * FRAG_ELEMS, 1, K, io.h, 2, 0, FRAG_32x32x16, st);
+        row += K;
+        frag += (int64_t)(K / 16) * (io.h / 32);
+      }
+    } else if (kind == TMX_W_TOK_DOWN) {
+      if (e == hipSuccess) e = launch_pack(sp, io.w2, C.T, io.h, C.D, 2, 0, FRAG_32x32x16, st);
+    } else {
+      if (e == hipSuccess) e = launch_pack(sp, io.hw1, 1, C.D, io.hh, 2, 0, FRAG_32x32x16, st);
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    (void)hipFree(stage);
+  }
+  if (e != hipSuccess) return fail(c, TMX_ERR_DEVICE, "tokenizer/head upload: %s", hipGetErrorString(e));
+  io.loaded[kind - TMX_W_TOK_UP] = true;
+  return TMX_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+IoArgs io_args(tmx_ctx* c, int B) {
+  IoArgs a{};
+  a.B = B; a.T = c->cfg.T; a.D = c->cfg.D; a.F = c->io.F; a.tok_hidden = c->io.h; a.head_hidden = c->io.hh;
+  a.tok_pos = c->io.pos; a.tok_w1 = c->io.w1; a.tok_w2 = c->io.w2; a.head_w1 = c->io.hw1; a.head_w2 = c->io.hw2;
+  return a;
+}
+
+tmx_status check_io(tmx_ctx* c, bool tok, bool head) {
+  if (!c->io.set) return fail(c, TMX_ERR_STATE, "tmx_set_model_io has not been called");
+  if (tok && !(c->io.loaded[0] && c->io.loaded[1]))
+    return fail(c, TMX_ERR_STATE, "the tokenizer weights (TMX_W_TOK_UP, TMX_W_TOK_DOWN) are not loaded");
+  if (head && !(c->io.loaded[2] && c->io.loaded[3]))
+    return fail(c, TMX_ERR_STATE, "the head weights (TMX_W_HEAD_UP, TMX_W_HEAD_DOWN) are not loaded");
+  return TMX_OK;
+}
+
+tmx_status run_tokenize(tmx_ctx* c, const void* emb, void* x_out, int B, hipStream_t st) {
+  IoArgs a = io_args(c, B);
+  a.emb = static_cast<const uint16_t*>(emb);
+  a.x_out = static_cast<uint16_t*>(x_out);
+  return launch_timed(c, TMX_KERNEL_TOKENIZE, st, "tokenizer launch", [&] { return launch_tokenize(a, st); });
+}
+
+tmx_status run_head(tmx_ctx* c, const void* y, float* logits, int B, hipStream_t st) {
+  IoArgs a = io_args(c, B);
+  a.y = static_cast<const uint16_t*>(y);
+  a.logits = logits;
+  return launch_timed(c, TMX_KERNEL_HEAD, st, "head launch", [&] { return launch_head(a, st); });
+}
+
+}  // namespace
+
+extern "C" {
+
+tmx_status tmx_tokenize(tmx_ctx* c, const void* emb, void* x_out, int B, void* stream) {
+  if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
+  tmx_status s;
+  if ((s = check_B(c, B)) != TMX_OK) return s;
+  if ((s = check_act(c, emb, "emb")) != TMX_OK) return s;
+  if ((s = check_act(c, x_out, "x_out")) != TMX_OK) return s;
+  if ((s = check_io(c, true, false)) != TMX_OK) return s;
+  if (overlaps(emb, x_out, (size_t)B * std::max<int64_t>(c->io.F, (int64_t)c->cfg.T * c->cfg.D) * 2))
+    return fail(c, TMX_ERR_INVALID_ARG, "emb and x_out overlap");
+  (void)hipSetDevice(c->device);
+  return run_tokenize(c, emb, x_out, B, as_stream(stream));
+}
+
+tmx_status tmx_head(tmx_ctx* c, const void* y, float* logits, int B, void* stream) {
+  if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
+  tmx_status s;
+  if ((s = check_B(c, B)) != TMX_OK) return s;
+  if ((s = check_act(c, y, "y")) != TMX_OK) return s;
+  if (!logits) return fail(c, TMX_ERR_INVALID_ARG, "logits is NULL");
+  if ((s = check_io(c, false, true)) != TMX_OK) return s;
+  (void)hipSetDevice(c->device);
+  return run_head(c, y, logits, B, as_stream(stream));
+}
+
+tmx_status tmx_model_forward(tmx_ctx* c, const void* emb, float* logits, int B, void* stream) {
+  if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
+  tmx_status s;
+  if ((s = check_B(c, B)) != TMX_OK) return s;
+  if ((s = check_act(c, emb, "emb")) != TMX_OK) return s;
+  if (!logits) return fail(c, TMX_ERR_INVALID_ARG, "logits is NULL");
+  if ((s = check_io(c, true, true)) != TMX_OK) return s;
+  if ((s = check_ready(c)) != TMX_OK) return s;
+  (void)hipSetDevice(c->device);
+  hipStream_t st = as_stream(stream);
+  if ((s = run_tokenize(c, emb, c->io.xbuf, B, st)) != TMX_OK) return s;
+  if ((s = tmx_block_stack_forward(c, c->io.xbuf, c->io.ybuf, B, stream)) != TMX_OK) return s;
+  return run_head(c, c->io.ybuf, logits, B, st);
 }
 
 tmx_status tmx_set_kernel_timing(tmx_ctx* c, int enable) {

@@ -154,6 +154,27 @@ int rmx_hidden_multiple(int D);   // the dense FFN's hidden must be a multiple (
 bool rmx_experts_supported(int D, int E, int h_e);
 hipError_t launch_rmx(const RmxArgs& a, int part, hipStream_t s);
 
+// Model front and back (tmx_io.hip), bf16: the tokenizer writes the tokens
+// X [B, T, D] from the concatenated embeddings [B, F]; the head reads the
+// stack's output Y [B, T, D] and writes one fp32 logit per sample.
+struct IoArgs {
+  int B, T, D, F, tok_hidden, head_hidden;
+  const uint16_t* emb;       // [B, F]
+  const int4* tok_pos;       // [T]: (column offset, K, first W1 fragment, 0)
+  const uint16_t* tok_w1;    // position t's W1 [K_t, h] packed (32x32x16, layout 2) from tok_pos[t].z
+  const uint16_t* tok_w2;    // [T] W2 [h, D] packed (32x32x16, layout 2)
+  uint16_t* x_out;           // [B, T, D]
+  const uint16_t* y;         // [B, T, D]
+  const uint16_t* head_w1;   // W1 [D, h_head] packed (32x32x16, layout 2)
+  const uint16_t* head_w2;   // [h_head] bf16
+  float* logits;             // [B]
+};
+bool io_width_supported(int D);
+bool io_tok_hidden_supported(int h);
+bool io_head_hidden_supported(int h);
+hipError_t launch_tokenize(const IoArgs& a, hipStream_t s);
+hipError_t launch_head(const IoArgs& a, hipStream_t s);
+
 // fp32 path
 struct F32Args {
   int B, P, W, hidden, E, top_k, expert_hidden, shared_hidden;

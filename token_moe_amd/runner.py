@@ -49,7 +49,15 @@ def upload_weights(ctx: tmx.Context, wl, banks: Dict[Tuple[int, int, int], np.nd
         ctx.load_weights(layer - 1, sub, kind, t.data_ptr(), t.numel() * t.element_size())
 
 
-def make_context(wl, banks, B_max: Optional[int] = None, device: int = 0) -> tmx.Context:
+def make_context(wl, banks, B_max: Optional[int] = None, device: int = 0, io_banks=None) -> tmx.Context:
+    """A context holding the workload's stack; with ``io_banks`` (a model
+    workload's tokenizer and head banks, {(0, 0, kind): array}) also its
+    front and back."""
     ctx = tmx.Context(config_from_workload(wl, B_max), device)
     upload_weights(ctx, wl, banks)
+    if io_banks is not None:
+        ctx.set_model_io(list(wl.groups), wl.tok_hidden, wl.head_hidden)
+        for (_, _, kind), arr in io_banks.items():
+            t = host_tensor(wl, arr).contiguous()
+            ctx.load_io_weights(kind, t.data_ptr(), t.numel() * t.element_size())
     return ctx

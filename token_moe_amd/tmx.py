@@ -22,8 +22,11 @@ TMX_PERM_ELEMENT, TMX_PERM_LANECOL, TMX_PERM_CURSOR = 0, 1, 2
 
 EXPORTED = ("tmx_create", "tmx_destroy", "tmx_last_error", "tmx_load_weights",
             "tmx_block_stack_forward", "tmx_moe_route", "tmx_sublayer_forward", "tmx_debug_permute",
-            "tmx_relu_route", "tmx_moe_buckets", "tmx_set_kernel_timing", "tmx_kernel_times")
-KERNEL_KINDS = ("mlp_dense", "mlp_routed", "mlp_shared", "router", "bucket", "rmx_block", "f32")
+            "tmx_relu_route", "tmx_moe_buckets", "tmx_set_kernel_timing", "tmx_kernel_times",
+            "tmx_set_model_io", "tmx_load_io_weights", "tmx_tokenize",
+            "tmx_head", "tmx_model_forward")
+KERNEL_KINDS = ("mlp_dense", "mlp_routed", "mlp_shared", "router", "bucket", "rmx_block", "f32", "tokenize",
+                "head")
 
 
 class TmxError(RuntimeError):
@@ -68,8 +71,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tmx_sublayer_forward.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, vp]
     lib.tmx_debug_permute.argtypes = [vp, vp, vp, i32, i32, i32, vp]
     lib.tmx_relu_route.argtypes = [vp, i32, vp, i32, vp, vp]
-    lib.tmx_moe_buckets.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp]
+    lib.tmx_moe_buckets.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp, vp]
     lib.tmx_set_kernel_timing.argtypes = [vp, i32]
+    lib.tmx_set_model_io.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), i32, i32, i32]
+    lib.tmx_load_io_weights.argtypes = [vp, i32, vp, sz, vp]
+    lib.tmx_tokenize.argtypes = [vp, vp, vp, i32, vp]
+    lib.tmx_head.argtypes = [vp, vp, vp, i32, vp]
+    lib.tmx_model_forward.argtypes = [vp, vp, vp, i32, vp]
     lib.tmx_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong), i32]
     for name in EXPORTED:
         if name != "tmx_last_error":
@@ -136,9 +144,25 @@ class Context:
         self._check(self.lib.tmx_moe_route(self.h, layer, sublayer, _ptr(x), B, _ptr(idx), _ptr(gate),
                                            _ptr(stream)))
 
-    def moe_buckets(self, layer: int, sublayer: int, x, B: int, counts, rows, stream=None):
-        self._check(self.lib.tmx_moe_buckets(self.h, layer, sublayer, _ptr(x), B, _ptr(counts), _ptr(rows),
-                                             _ptr(stream)))
+    def moe_buckets(self, layer: int, sublayer: int, x, B: int, xhat, counts, rows, stream=None):
+        self._check(self.lib.tmx_moe_buckets(self.h, layer, sublayer, _ptr(x), B, _ptr(xhat), _ptr(counts),
+                                             _ptr(rows), _ptr(stream)))
+
+    def set_model_io(self, group_widths, tok_hidden: int, head_hidden: int):
+        arr = (ctypes.c_int32 * len(group_widths))(*group_widths)
+        self._check(self.lib.tmx_set_model_io(self.h, arr, len(group_widths), tok_hidden, head_hidden))
+
+    def load_io_weights(self, kind: int, src_ptr: int, nbytes: int, stream=None):
+        self._check(self.lib.tmx_load_io_weights(self.h, kind, src_ptr, nbytes, _ptr(stream)))
+
+    def tokenize(self, emb, x_out, B: int, stream=None):
+        self._check(self.lib.tmx_tokenize(self.h, _ptr(emb), _ptr(x_out), B, _ptr(stream)))
+
+    def head(self, y, logits, B: int, stream=None):
+        self._check(self.lib.tmx_head(self.h, _ptr(y), _ptr(logits), B, _ptr(stream)))
+
+    def model_forward(self, emb, logits, B: int, stream=None):
+        self._check(self.lib.tmx_model_forward(self.h, _ptr(emb), _ptr(logits), B, _ptr(stream)))
 
     def set_kernel_timing(self, enable: bool):
         self._check(self.lib.tmx_set_kernel_timing(self.h, 1 if enable else 0))
