@@ -2,11 +2,14 @@
 """Throughput of the TokenMixer-Large block-stack forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload N] [--no-cpu-baseline]
+    python bench.py --workload 2                   # the dense per-token SwiGLU stack
     python bench.py --workload rankmixer_d256      # the RankMixer block stack
 
-A step is one tmx_block_stack_forward over one batch of the workload (all
-blocks, both sub-layers, inter-residuals) with inputs and weights already
-resident in HBM. Prints ONE JSON line.
+The default workload is the large MoE stack (B 8192, T = H = 32, D 768, E 32,
+top-4, 8 blocks, ~15.4e9 weights), the largest configuration that fits one
+GPU. A step is one tmx_block_stack_forward over one batch of the workload
+(all blocks, both sub-layers, inter-residuals) with inputs and weights
+already resident in HBM. Prints ONE JSON line.
 """
 from __future__ import annotations
 
@@ -89,43 +92,89 @@ def time_launches(fn, reps, stream):
     return start.elapsed_time(end) / reps
 
 
+def cpu_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(wl, banks, x, budget_s):
     """The oracle as it stands, on a bounded sample of the same workload.
 
     The oracle's cost is affine in the sample count (a fixed per-call part
     for the weight slices plus a per-sample part), so two probe runs fix both
-    and the sample is sized to fill about `budget_s` seconds."""
+    and the sample is sized to fill about `budget_s` seconds. MoE stacks run
+    the first block only (its weight slices alone take seconds to decode per
+    block) and the rate is scaled to the L-block stack."""
     import datagen as dg
     import oracle as orc
     ws = dg.WeightSource(wl, banks)
 
-    forward = orc.rankmixer_stack if wl.rankmixer else orc.stack_forward
+    one_block = wl.moe and not wl.rankmixer
+    if wl.rankmixer:
+        forward = orc.rankmixer_stack
+    elif one_block:
+        def forward(xx, w, s):
+            return orc.block_forward(xx, w, 1, s, None, w.bf16_values)
+    else:
+        forward = orc.stack_forward
 
     def run(n):
         t0 = time.perf_counter()
         forward(x[:n].astype(np.float64), wl, ws)
         return time.perf_counter() - t0
 
-    run(2)                                     # first-touch costs out of the probes
-    # grow the probe until it takes a quarter of the budget, then extrapolate
-    # from the last two probes (per-sample cost rises with n: cache effects)
-    n_prev, t_prev = 8, run(8)
-    n_cur, t_cur = n_prev, t_prev
-    while t_cur < budget_s / 4 and n_cur < wl.B:
-        n_prev, t_prev = n_cur, t_cur
-        n_cur = min(wl.B, n_cur * 4)
-        t_cur = run(n_cur)
-    per = max((t_cur - t_prev) / max(n_cur - n_prev, 1), 1e-6)
-    n = int(min(wl.B, max(n_cur, n_cur + (budget_s - t_cur) / per)))
-    dt = run(n)
+    if one_block:
+        # one run: decoding the block's weight slices (seconds at the 15B
+        # shapes) dominates, so probes would cost as much as the sample
+        n = min(wl.B, 64)
+        dt = run(n)
+    else:
+        run(2)                                 # first-touch costs out of the probes
+        # grow the probe until it takes a quarter of the budget, then extrapolate
+        # from the last two probes (per-sample cost rises with n: cache effects)
+        n_prev, t_prev = 8, run(8)
+        n_cur, t_cur = n_prev, t_prev
+        while t_cur < budget_s / 4 and n_cur < wl.B:
+            n_prev, t_prev = n_cur, t_cur
+            n_cur = min(wl.B, n_cur * 4)
+            t_cur = run(n_cur)
+        per = max((t_cur - t_prev) / max(n_cur - n_prev, 1), 1e-6)
+        n = int(min(wl.B, max(n_cur, n_cur + (budget_s - t_cur) / per)))
+        dt = run(n)
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
-    return {"value": n / dt, "unit": "samples/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n} of {wl.B} samples of the same workload, full {wl.L}-block stack "
-                      f"in fp64 numpy ({dt:.1f} s)"}
+    if one_block:
+        what = (f"first {n} of {wl.B} samples of the same workload through block 1 of {wl.L} in fp64 numpy "
+                f"({dt:.1f} s), rate divided by {wl.L} for the stack")
+        value = n / (dt * wl.L)
+    else:
+        what = (f"first {n} of {wl.B} samples of the same workload, full {wl.L}-block stack "
+                f"in fp64 numpy ({dt:.1f} s)")
+        value = n / dt
+    return {"value": value, "unit": "samples/s", "cores": cpu_cores(), "blas_threads": int(threads),
+            "kind": "oracle", "sample": what}
+
+
+def moe_kernel_work(wl):
+    """Algorithmic work per launch of each MoE kernel, as (bound, amount):
+    FLOPs for the GEMM kernels (2 per multiply-add; the top_k chosen experts
+    of every row for the routed launch, the shared expert for the other), HBM
+    bytes for the router (rows read, normalised rows written, routing table
+    written, router weights read) and the bucket kernel (routing table read,
+    row lists written). P * W = T * D in both sub-layers; P averages H and T."""
+    TD = wl.T * wl.D
+    P = (wl.H + wl.T) / 2.0
+    return {
+        "mlp_routed": ("mfma", 2.0 * wl.B * wl.top_k * TD * 3 * wl.expert_hidden),
+        "mlp_shared": ("mfma", 2.0 * wl.B * TD * 3 * wl.shared_hidden),
+        "router": ("hbm", 2.0 * wl.B * TD * 2 + wl.B * P * wl.top_k * 8 + TD * wl.E * 2),
+        "bucket": ("hbm", wl.B * P * wl.top_k * 8.0),
+    }
 
 
 def main(argv=None):
@@ -133,8 +182,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="2",
-                    help="workload id 1..5 (default 2) or a RankMixer workload (rankmixer_d256, rankmixer_d512)")
+    ap.add_argument("--workload", default="5",
+                    help="workload id 1..5 (default 5, the large MoE stack) or a RankMixer workload "
+                         "(rankmixer_d256, rankmixer_d512, rankmixer_moe_d256)")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -236,6 +286,49 @@ def main(argv=None):
                     "launch_ms": round(kms, 5)}
         kernel["rmx_block_ms"] = round(kms, 5)
         log(f"fused RankMixer block kernel: {kms:.4f} ms/launch, {achieved:.1f} TFLOP/s")
+    elif wl.moe:
+        # An MoE sub-layer runs four kernels. Their own durations come from
+        # HIP events the library records around each launch on the launch
+        # stream (tmx_set_kernel_timing), over as many steps as the timed
+        # region, run right after it.
+        ctx.set_kernel_timing(True)
+        for _ in range(args.steps):
+            ctx.block_stack_forward(xd, yd, wl.B, sp)
+        torch.cuda.synchronize()
+        times = ctx.kernel_times()
+        ctx.set_kernel_timing(False)
+        kinfo = moe_kernel_work(wl)
+        kernels = {}
+        for name, (tot, n) in times.items():
+            kms = tot / n
+            rec = {"launches_per_step": n / args.steps, "ms": round(kms, 5)}
+            work = kinfo.get(name)
+            if work is not None:
+                bound, amount = work
+                if bound == "mfma":
+                    rec.update(bound="mfma", flop_per_launch=amount,
+                               achieved_tflops=round(amount / (kms / 1e3) / 1e12, 2),
+                               frac=round(amount / (kms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4))
+                else:
+                    rec.update(bound="hbm", bytes_per_launch=amount,
+                               achieved_gbs=round(amount / (kms / 1e3) / 1e9, 1),
+                               frac=round(amount / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, 4))
+            kernels[name] = rec
+        step_sum = sum(t for t, _ in times.values()) / args.steps
+        log(f"kernel times sum to {step_sum:.3f} ms/step (timed step {ms:.3f} ms)")
+        for name, rec in kernels.items():
+            log(f"  {name}: {rec}")
+        dom = max(times, key=lambda k: times[k][0])
+        d = kernels[dom]
+        roofline = {"bound": d["bound"], "achieved": d.get("achieved_tflops", d.get("achieved_gbs")),
+                    "peak": BF16_PEAK_TFLOPS if d["bound"] == "mfma" else HBM_PEAK_GBS,
+                    "unit": "TFLOP/s" if d["bound"] == "mfma" else "GB/s", "frac": d["frac"],
+                    "traffic": measured_traffic(wl.name, os.path.join(ROOT, "profiles", f"{dom}_{wl.name}_counters.md")),
+                    "kernel": {"mlp_routed": f"mlp_kernel<{wl.width(1)}, ROUTED>",
+                               "mlp_shared": f"mlp_kernel<{wl.width(1)}, SHARED>"}.get(dom, dom),
+                    "flop_per_launch": d.get("flop_per_launch"), "launch_ms": d["ms"]}
+        kernel["kernels"] = kernels
+        kernel["kernel_ms_sum_per_step"] = round(step_sum, 4)
     elif not wl.moe:
         xr = torch.empty_like(xd)
         per = []
