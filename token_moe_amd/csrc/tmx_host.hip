@@ -1088,8 +1088,12 @@ tmx_status tmx_tokenize(tmx_ctx* c, const void* emb, void* x_out, int B, void* s
   if ((s = check_act(c, emb, "emb")) != TMX_OK) return s;
   if ((s = check_act(c, x_out, "x_out")) != TMX_OK) return s;
   if ((s = check_io(c, true, false)) != TMX_OK) return s;
-  if (overlaps(emb, x_out, (size_t)B * std::max<int64_t>(c->io.F, (int64_t)c->cfg.T * c->cfg.D) * 2))
-    return fail(c, TMX_ERR_INVALID_ARG, "emb and x_out overlap");
+  {
+    const char* e0 = static_cast<const char*>(emb);
+    const char* x0 = static_cast<const char*>(x_out);
+    const size_t eb = (size_t)B * c->io.F * 2, xb = (size_t)B * c->cfg.T * c->cfg.D * 2;
+    if (e0 < x0 + xb && x0 < e0 + eb) return fail(c, TMX_ERR_INVALID_ARG, "emb and x_out overlap");
+  }
   (void)hipSetDevice(c->device);
   return run_tokenize(c, emb, x_out, B, as_stream(stream));
 }
