@@ -207,6 +207,24 @@ tmx_status tmx_block_stack_forward(tmx_ctx* ctx, const void* x_in, void* x_out,
 tmx_status tmx_moe_route(tmx_ctx* ctx, int layer, int sublayer, const void* x,
                          int B, int32_t* idx, float* gate, void* stream);
 
+/* tmx_sublayer_forward for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels, same arguments, same result, but a bf16 MoE
+ * sub-layer keeps its workspace (normalised rows, routing table, bucket
+ * lists, tile queues, expert outputs) in a static device array of 64 MiB
+ * instead of the context's workspace; no call allocates or frees anything.
+ * The array holds the workspace of B rows only up to its size:
+ * TMX_ERR_INVALID_ARG names the largest B when a call needs more.  Dense,
+ * fp32 and RankMixer sub-layers use no workspace and run as in
+ * tmx_sublayer_forward.  Every call on one device shares that device's
+ * array (it keeps the last call's contents; what must start at zero is
+ * cleared by the kernels), so calls that overlap on one device -- on
+ * different streams or from different contexts -- race. */
+tmx_status tmx_sublayer_forward_noalloc(tmx_ctx* ctx, int layer, int sublayer,
+                                        const void* x_in, const void* resid,
+                                        const void* extra, void* x_out, int B,
+                                        void* stream);
+
 /* The normalised rows and the expert-first row lists of one MoE sub-layer
  * (RMSNorm, TokenMixer-Large summary section 2.3.3; MoEPermute, section
  * 2.5.1), for checks: x is the sub-layer's input in block layout [B, T, D]

@@ -99,6 +99,8 @@ int main(void) {
   EXPECT(tmx_moe_route(NULL, 0, 0, NULL, 1, NULL, NULL, NULL) == TMX_ERR_INVALID_ARG, "route NULL");
   EXPECT(tmx_moe_buckets(NULL, 0, 0, NULL, 1, NULL, NULL, NULL, NULL) == TMX_ERR_INVALID_ARG, "buckets NULL");
   EXPECT(tmx_sublayer_forward(NULL, 0, 0, NULL, NULL, NULL, NULL, 1, NULL) == TMX_ERR_INVALID_ARG, "sublayer NULL");
+  EXPECT(tmx_sublayer_forward_noalloc(NULL, 0, 0, NULL, NULL, NULL, NULL, 1, NULL) == TMX_ERR_INVALID_ARG,
+         "sublayer noalloc NULL");
   EXPECT(tmx_relu_route(NULL, 0, NULL, 1, NULL, NULL) == TMX_ERR_INVALID_ARG, "relu route NULL");
   EXPECT(tmx_debug_permute(NULL, NULL, NULL, 1, 0, 0, NULL) == TMX_ERR_INVALID_ARG, "permute NULL");
   EXPECT(tmx_set_kernel_timing(NULL, 1) == TMX_ERR_INVALID_ARG, "timing NULL");

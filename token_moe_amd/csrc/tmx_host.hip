@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -19,6 +20,33 @@ namespace {
 constexpr int NKINDS = 16;
 thread_local std::string g_create_error;
 
+// Scratch of tmx_sublayer_forward_noalloc: the MoE workspace of one
+// sub-layer call, for callers that cannot allocate. Each device holds its
+// own copy of the array for the life of the process. Host code never uses
+// the array's name as an address: tmx_create looks up each device's copy
+// with hipGetSymbolAddress (that device current) and keeps the pointer.
+constexpr size_t TMX_SCRATCH_BYTES = size_t(64) << 20;
+constexpr int TMX_SCRATCH_DEVICES = 64;
+static __device__ __align__(256) uint8_t scratch[TMX_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[TMX_SCRATCH_DEVICES] = {};
+hipError_t g_scratch_err[TMX_SCRATCH_DEVICES] = {};
+
+// once per device, with that device current
+void setup_scratch(int device) {
+  if (device < 0 || device >= TMX_SCRATCH_DEVICES) return;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device]) return;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    (void)hipGetLastError();
+    g_scratch_err[device] = e != hipSuccess ? e : hipErrorInvalidSymbol;
+    return;
+  }
+  g_scratch_ptr[device] = p;
+}
+
 struct Bank {
   void* ptr = nullptr;    // device storage (packed for bf16 matrices, fp32 for gains)
   size_t elems = 0;       // logical element count
@@ -27,7 +55,8 @@ struct Bank {
 
 // The device workspace of a bf16 MoE sub-layer: everything its kernels
 // write besides the output. One region, carved by carve_moe_ws(); the
-// context's own region is laid out for B_max.
+// context's own region is laid out for B_max, the static scratch of
+// tmx_sublayer_forward_noalloc for the call's B.
 struct MoeWs {
   uint16_t* xhat = nullptr;   // [P][B][W] normalised rows (largest sub-layer)
   int32_t* idx = nullptr;     // [B][P][k]
@@ -552,6 +581,7 @@ tmx_status tmx_create(const tmx_config* cfg, int device, tmx_ctx** out) {
     delete c;
     return fail(nullptr, TMX_ERR_DEVICE, "compute-unit count: %s", hipGetErrorString(e));
   }
+  setup_scratch(device);
   c->alpha = cfg->E > 0 ? (cfg->alpha != 0.f ? cfg->alpha : (float)cfg->E / (float)cfg->top_k) : 0.f;
   c->banks.resize((size_t)cfg->L * 2 * NKINDS);
   const tmx_config& C = c->cfg;
@@ -774,6 +804,41 @@ tmx_status tmx_sublayer_forward(tmx_ctx* c, int layer, int sub, const void* x_in
   (void)hipSetDevice(c->device);
   if (is_rmx(c->cfg)) return run_rmx(c, layer, sub, x_in, x_out, B, as_stream(stream));
   return run_sublayer(c, layer, sub, x_in, resid, extra, x_out, B, as_stream(stream), c->ws);
+}
+
+tmx_status tmx_sublayer_forward_noalloc(tmx_ctx* c, int layer, int sub, const void* x_in, const void* resid,
+                                        const void* extra, void* x_out, int B, void* stream) {
+  tmx_status s = check_sublayer_args(c, layer, sub, x_in, resid, extra, x_out, B);
+  if (s != TMX_OK) return s;
+  const tmx_config& C = c->cfg;
+  MoeWs ws;
+  if (is_moe(C) && !is_rmx(C) && C.dtype == TMX_BF16) {
+    const size_t need = carve_moe_ws(C, B, nullptr, nullptr);
+    if (need > TMX_SCRATCH_BYTES) {
+      int bmax = 0;
+      for (int lo = 1, hi = C.B_max; lo <= hi;) {   // largest B whose workspace fits
+        const int mid = lo + (hi - lo) / 2;
+        if (carve_moe_ws(C, mid, nullptr, nullptr) <= TMX_SCRATCH_BYTES) {
+          bmax = mid;
+          lo = mid + 1;
+        } else {
+          hi = mid - 1;
+        }
+      }
+      return fail(c, TMX_ERR_INVALID_ARG,
+                  "B = %d needs %zu bytes of MoE workspace; the static scratch holds %zu (B <= %d for this context)",
+                  B, need, TMX_SCRATCH_BYTES, bmax);
+    }
+    void* base = (c->device >= 0 && c->device < TMX_SCRATCH_DEVICES) ? g_scratch_ptr[c->device] : nullptr;
+    if (!base)
+      return fail(c, TMX_ERR_DEVICE, "static scratch of device %d unavailable: %s", c->device,
+                  hipGetErrorString(c->device >= 0 && c->device < TMX_SCRATCH_DEVICES ? g_scratch_err[c->device]
+                                                                                     : hipErrorInvalidDevice));
+    carve_moe_ws(C, B, base, &ws);
+  }
+  (void)hipSetDevice(c->device);
+  if (is_rmx(C)) return run_rmx(c, layer, sub, x_in, x_out, B, as_stream(stream));
+  return run_sublayer(c, layer, sub, x_in, resid, extra, x_out, B, as_stream(stream), ws);
 }
 
 tmx_status tmx_block_stack_forward(tmx_ctx* c, const void* x_in, void* x_out, int B, void* stream) {

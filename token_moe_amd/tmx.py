@@ -23,7 +23,7 @@ TMX_PERM_ELEMENT, TMX_PERM_LANECOL, TMX_PERM_CURSOR = 0, 1, 2
 EXPORTED = ("tmx_create", "tmx_destroy", "tmx_last_error", "tmx_load_weights",
             "tmx_block_stack_forward", "tmx_moe_route", "tmx_sublayer_forward", "tmx_debug_permute",
             "tmx_relu_route", "tmx_moe_buckets", "tmx_set_kernel_timing", "tmx_kernel_times",
-            "tmx_set_model_io", "tmx_load_io_weights", "tmx_tokenize",
+            "tmx_sublayer_forward_noalloc", "tmx_set_model_io", "tmx_load_io_weights", "tmx_tokenize",
             "tmx_head", "tmx_model_forward")
 KERNEL_KINDS = ("mlp_dense", "mlp_routed", "mlp_shared", "router", "bucket", "rmx_block", "f32", "tokenize",
                 "head")
@@ -69,6 +69,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tmx_block_stack_forward.argtypes = [vp, vp, vp, i32, vp]
     lib.tmx_moe_route.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp]
     lib.tmx_sublayer_forward.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, vp]
+    lib.tmx_sublayer_forward_noalloc.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, vp]
     lib.tmx_debug_permute.argtypes = [vp, vp, vp, i32, i32, i32, vp]
     lib.tmx_relu_route.argtypes = [vp, i32, vp, i32, vp, vp]
     lib.tmx_moe_buckets.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp, vp]
@@ -181,6 +182,11 @@ class Context:
     def sublayer_forward(self, layer: int, sublayer: int, x_in, resid, extra, x_out, B: int, stream=None):
         self._check(self.lib.tmx_sublayer_forward(self.h, layer, sublayer, _ptr(x_in), _ptr(resid),
                                                   _ptr(extra), _ptr(x_out), B, _ptr(stream)))
+
+    def sublayer_forward_noalloc(self, layer: int, sublayer: int, x_in, resid, extra, x_out, B: int,
+                                 stream=None):
+        self._check(self.lib.tmx_sublayer_forward_noalloc(self.h, layer, sublayer, _ptr(x_in), _ptr(resid),
+                                                          _ptr(extra), _ptr(x_out), B, _ptr(stream)))
 
     def debug_permute(self, x_in, x_out, B: int, inverse: int, form: int = 0, stream=None):
         self._check(self.lib.tmx_debug_permute(self.h, _ptr(x_in), _ptr(x_out), B, inverse, form,
