@@ -345,7 +345,11 @@ tmx_status validate_config(const tmx_config* cfg) {
   return TMX_OK;
 }
 
-int moe_bm(const tmx_config& c, int sub) { return mlp_bm(MLP_ROUTED, width(c, sub)); }
+// rows per routed bucket tile: the wide routed kernel's where it applies
+int moe_bm(const tmx_config& c, int sub) {
+  const int wide = routed_wide_rows(width(c, sub), c.expert_hidden);
+  return wide > 0 ? wide : mlp_bm(MLP_ROUTED, width(c, sub));
+}
 int moe_max_tiles(const tmx_config& c, int sub, int B) {
   const int bm = moe_bm(c, sub);
   return (int)(((int64_t)B * c.top_k + bm - 1) / bm) + c.E;
@@ -484,7 +488,8 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   }
 
   // MoE: norm + route -> bucket -> routed experts -> shared expert + combine
-  const int bm = mlp_bm(MLP_ROUTED, W);
+  const int bm = moe_bm(cfg, sub);
+  const bool wide = routed_wide_rows(W, cfg.expert_hidden) > 0;
   RouteArgs r{};
   r.B = B; r.P = P; r.E = cfg.E; r.top_k = cfg.top_k; r.alpha = c->alpha; r.eps = cfg.eps; r.map = map;
   r.x = static_cast<const uint16_t*>(x_in); r.gain = gain;
@@ -506,8 +511,10 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   a.hidden = cfg.expert_hidden;
   a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_EXP_GATE).ptr);
   a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_EXP_DOWN).ptr);
-  s = launch_timed(c, TMX_KERNEL_MLP_ROUTED, st, "routed MLP launch",
-                   [&] { return launch_mlp(MLP_ROUTED, W, a, P * a.max_tiles, c->workers, st); });
+  s = launch_timed(c, TMX_KERNEL_MLP_ROUTED, st, "routed MLP launch", [&] {
+    return wide ? launch_routed_wide(a, P * a.max_tiles, c->workers, st)
+                : launch_mlp(MLP_ROUTED, W, a, P * a.max_tiles, c->workers, st);
+  });
   if (s != TMX_OK) return s;
 
   a.hidden = cfg.shared_hidden;
@@ -522,7 +529,7 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   // while the other half compute.
   const int sh_tiles = (a.pair ? P / 2 : P) * a.rtiles;
   const int sh_grid = std::max(1, std::min(sh_tiles, c->workers & ~7));
-  const double mfma_clk = (double)bm * W * 3.0 * cfg.shared_hidden / (16384.0 * 4.0) * 32.0;
+  const double mfma_clk = (double)mlp_bm(MLP_SHARED, W) * W * 3.0 * cfg.shared_hidden / (16384.0 * 4.0) * 32.0;
   a.stagger = sh_tiles >= 4 * sh_grid ? (int)(1.6 * mfma_clk) : 0;
   return launch_timed(c, TMX_KERNEL_MLP_SHARED, st, "shared MLP launch",
                       [&] { return launch_mlp(MLP_SHARED, W, a, sh_tiles, c->workers, st); });
@@ -944,7 +951,7 @@ tmx_status tmx_moe_buckets(tmx_ctx* c, int layer, int sub, const void* x, int B,
   r.xhat = c->ws.xhat; r.idx = c->ws.idx; r.gate = c->ws.gate; r.hist = c->ws.hist;
   if ((s = check_launch(c, launch_norm_route(W, r, st), "router launch")) != TMX_OK) return s;
   BucketArgs k{};
-  k.B = B; k.P = P; k.E = C.E; k.top_k = C.top_k; k.bm = mlp_bm(MLP_ROUTED, W); k.max_tiles = moe_max_tiles(C, sub, B);
+  k.B = B; k.P = P; k.E = C.E; k.top_k = C.top_k; k.bm = moe_bm(C, sub); k.max_tiles = moe_max_tiles(C, sub, B);
   k.idx = c->ws.idx; k.rows = c->ws.rows; k.tiles = c->ws.tiles; k.ntiles = c->ws.ntiles; k.counts = c->ws.counts;
   k.qhead = c->ws.qhead; k.hist = c->ws.hist;
   if ((s = check_launch(c, launch_bucket(k, st), "bucket launch")) != TMX_OK) return s;

@@ -86,6 +86,11 @@ bool mlp_width_supported(int W);
 // workgroups per CU): each workgroup walks tiles blockIdx.x, blockIdx.x +
 // grid, ...
 hipError_t launch_mlp(int mode, int W, const MlpArgs& a, int tiles, int workers, hipStream_t s);
+// routed experts at W = 768, h_e = 384 (tmx_routed.hip): rows per bucket tile
+// (0 where that kernel does not apply) and its launch (grid as launch_mlp,
+// ROUTED arguments)
+int routed_wide_rows(int W, int h_e);
+hipError_t launch_routed_wide(const MlpArgs& a, int tiles, int workers, hipStream_t s);
 // whether DENSE / SHARED tiles of this mode and width may hold two adjacent positions
 bool mlp_pairs_positions(int mode, int W);
 // workgroups of the MLP kernel resident per CU for a mode and width

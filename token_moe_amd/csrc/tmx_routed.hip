@@ -1,0 +1,513 @@
+// tmx_routed.hip -- the grouped routed-expert MLP of the Sparse-Pertoken MoE
+// (TokenMixer-Large summary Eq. 19, section 2.5.1 MoEGroupedSwiGLU) for wide
+// rows (W = 768, h_e = 384), on gfx950 bf16 MFMA.
+//
+// Why a kernel of its own: in the general fused MLP kernel a W = 768 tile has
+// 64 rows (its GEMM2 accumulators, 64 x 768 fp32, fill the AGPRs), so every
+// weight fragment fed from L2 serves two 32-row MFMA blocks, and that weight
+// stream, not the MFMA rate, bounds the routed launch. Here a tile has
+// BM = 128 rows of one (position, expert) bucket, and each weight fragment
+// serves four MFMA blocks, which halves the weight bytes per FLOP. The
+// accumulators of 128 rows do not fit at once either, so a tile runs in
+// phases that each stay within the 256 AGPRs:
+//
+//   GEMM1 A  S_gate, S_up for hidden blocks [8 blocks of 32] (2 per wave,
+//            256 accumulator registers), K-outer: the rows' x_hat columns
+//            stream through LDS in 64-column slabs;
+//   U(A)     rho(silu(S_gate) * S_up) -> LDS U [128, h_e];
+//   GEMM1 B  the other 4 hidden blocks (1 per wave), x_hat streamed again;
+//   U(B)     -> LDS U;
+//   GEMM2 0  O [128, 0:384) = U @ W_down[:, 0:384) (3 column blocks per wave);
+//   out 0    gate * O -> bf16, staged 32 rows at a time through two free slab
+//            buffers and written as whole 16-byte units of the rows' slots of
+//            the expert-output buffer;
+//   GEMM2 1  O [128, 384:768) ... out 1 (staged through the U region).
+//
+// The second x_hat pass costs 196 KB of L2/last-level-cache reads per tile
+// against the 1.7 MB of expert weights every tile streams.
+//
+// Pipelines. Weight fragments stream through a 12-slot register ring in one
+// order per tile (GEMM1 A, GEMM1 B, GEMM2 0, GEMM2 1) that runs on into the
+// next tile; a slot is refilled as soon as its four MFMAs have issued. x_hat
+// slabs (24 per tile: 12 per GEMM1 pass) run through three LDS buffers:
+// at slab step s, slab s+1 goes from registers to LDS and slab s+3's loads go
+// out (two register sets, so a load has two slab steps to land); the last
+// three slab steps of a tile load the next tile's first slabs, which wait in
+// LDS buffer 0 and registers through GEMM2.
+#include <type_traits>
+
+#include "tmx_internal.h"
+
+namespace tmx {
+
+namespace {
+
+constexpr int RT_NT = 256;   // 4 waves
+constexpr int RT_RB = 4;     // 32-row blocks per tile
+constexpr int RT_BM = 32 * RT_RB;
+constexpr int RT_SC = 64;    // columns per x_hat slab
+constexpr int RT_RING = 12;  // weight fragments in flight per wave
+
+// 16 bytes as a native vector: arrays of it stay in registers (arrays of the
+// struct type uint4 are copied with memcpy, which can leave them in scratch)
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4u rt_ld16(const void* p) { return *reinterpret_cast<const v4u*>(p); }
+
+__device__ __forceinline__ f32x16 rt_mfma(const v4u& a, const v4u& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// z * sigmoid(z) with the hardware exp and reciprocal; rounded to bf16 next
+__device__ __forceinline__ float rt_silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
+template <int W, int HE>
+struct RtShape {
+  static constexpr int BM = RT_BM;
+  static constexpr int HA = 2;                    // hidden blocks per wave, GEMM1 pass A
+  static constexpr int HBB = HE / 128 - HA;       // ... pass B
+  static constexpr int NOH = W / 256;             // output blocks per wave and GEMM2 half
+  static constexpr int NSP = W / RT_SC;           // slabs per GEMM1 pass
+  static constexpr int NSL = 2 * NSP;             // slab steps per tile
+  static constexpr int KB1 = W / 16;              // GEMM1 k-steps per pass
+  static constexpr int KB2 = HE / 16;             // GEMM2 k-steps per half
+  static constexpr int FA = 2 * HA, FB = 2 * HBB, FC = NOH;   // fragments per k-step
+  static constexpr int LA = KB1 * FA, LB = KB1 * FB, LC = KB2 * FC;   // fragments per phase
+  static constexpr int US = HE + 8;               // U row stride (bf16): rows 16 B apart in banks
+  static constexpr int HS = W / 2 + 8;            // staged half-row stride (bf16)
+  static constexpr int SLAB = BM * RT_SC;         // bf16 per slab buffer
+  static constexpr int SU = BM * RT_SC / 8 / RT_NT;   // slab units per lane
+  static_assert(HE % 128 == 0 && HBB >= 1 && HBB <= 2, "two GEMM1 passes of at most 2 hidden blocks per wave");
+  static_assert(W % 256 == 0 && W % RT_SC == 0 && NSP % 6 == 0, "slab steps run in groups of six");
+  static_assert((BM * RT_SC / 8) % RT_NT == 0, "slab units per lane");
+  static_assert((24 * FA) % RT_RING == 0 && (24 * FB) % RT_RING == 0 && (4 * FC) % RT_RING == 0 &&
+                RT_RING % FA == 0 && RT_RING % FB == 0 && RT_RING % FC == 0,
+                "ring slots must repeat per loop iteration of every phase");
+  static_assert(KB2 % 4 == 0, "GEMM2 k-steps run in groups of four");
+  static_assert(32 * HS * 2 <= 2 * SLAB * 2, "a staged 32-row half fits in two slab buffers");
+  static_assert(BM * HS <= BM * US, "a staged 128-row half fits in the U region");
+  static_assert(3 * SLAB * 2 + BM * US * 2 + 3 * 2 * BM * 4 + 16 <= 160 * 1024, "LDS budget");
+};
+
+template <int W, int HE>
+__global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
+  using S = RtShape<W, HE>;
+  constexpr int BM = S::BM, HA = S::HA, HBB = S::HBB, NOH = S::NOH, NSP = S::NSP, NSL = S::NSL;
+  constexpr int KB1 = S::KB1, KB2 = S::KB2, FA = S::FA, FB = S::FB, FC = S::FC;
+  constexpr int LA = S::LA, LB = S::LB, LC = S::LC, US = S::US, HS = S::HS, SLAB = S::SLAB, SU = S::SU;
+
+  __shared__ __attribute__((aligned(16))) uint16_t slabs[3 * SLAB];
+  __shared__ __attribute__((aligned(16))) uint16_t us[BM * US];
+  __shared__ int rowb[2][BM];      // sample row of each tile row (-1: padding)
+  __shared__ int rowgi[2][BM];     // expert-output row (b, p, slot)
+  __shared__ float rowg[2][BM];    // gate of each tile row
+  __shared__ int claim;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Lane-dependent address arithmetic reads `ot`, an opaque copy of the
+  // thread index that is made anew before each phase: the compiler cannot
+  // then hoist one phase's addresses out of the tile loop (they would stay
+  // live, in registers or spilled, through every other phase).
+  int ot = tid;
+  auto fresh = [&]() __attribute__((always_inline)) { asm volatile("" : "+v"(ot)); };
+
+  // ---- tile queues (one per XCD over its positions when P % 8 == 0): entry
+  // k is the k-th non-empty tile of the queue's positions in order; the
+  // bucket kernel zeroes the heads
+  const bool split_q = (a.P & 7) == 0;
+  const int qx = split_q ? (int)(blockIdx.x & 7) : 0;
+  const int NPX = split_q ? (a.P >> 3) : a.P;
+  struct Tile {
+    int p, group, start, nrows;
+  };
+  // the decoded values are the same in every lane; readfirstlane keeps the
+  // weight addresses in scalar registers
+  auto qdecode = [&](int k, Tile& T) -> bool {
+    int p = qx * NPX;
+    for (int q = 0; q < NPX; ++q, ++p) {
+      const int n = a.ntiles[p];
+      if (k < n) {
+        const int4 tl = a.tiles[(size_t)p * a.max_tiles + k];
+        T.p = __builtin_amdgcn_readfirstlane(p);
+        T.group = __builtin_amdgcn_readfirstlane(p * a.E + tl.x);
+        T.start = __builtin_amdgcn_readfirstlane(tl.y);
+        T.nrows = __builtin_amdgcn_readfirstlane(tl.z);
+        return true;
+      }
+      k -= n;
+    }
+    return false;
+  };
+  auto set_rows = [&](const Tile& T, int buf) {
+    for (int r = tid; r < BM; r += RT_NT) {
+      int b = -1, gi = 0;
+      float g = 0.f;
+      if (r < T.nrows) {
+        const int ent = a.rows[(size_t)T.p * a.B * a.top_k + T.start + r];   // b * top_k + slot
+        b = ent / a.top_k;
+        gi = (b * a.P + T.p) * a.top_k + (ent - b * a.top_k);
+        g = a.gate[gi];
+      }
+      rowb[buf][r] = b;
+      rowgi[buf][r] = gi;
+      rowg[buf][r] = g;
+    }
+  };
+
+  // ---- weight stream of a tile, phase by phase:
+  //   0  GEMM1 A: k-step kb, hidden block HA wave + h, gate / up
+  //   1  GEMM1 B: hidden block 4 HA + HBB wave + h
+  //   2  GEMM2 0: k-step kb, output block NOH wave + j
+  //   3  GEMM2 1: output block W / 64 + NOH wave + j
+  //   4  the next tile's phase 0
+  // A super-step is one turn of the ring (12 fragments: 3 k-steps of phase
+  // 0, 6 of phase 1, 4 of a GEMM2 half). Slot i holds fragment i of the
+  // current super-step and is refilled with fragment i of the next one,
+  // which may belong to the next phase: both addresses are formed and one is
+  // selected, so every refill is one unconditional load (a load on one path
+  // only makes the compiler wait for every load in flight where the paths
+  // join). i is a compile-time constant; only the super-step index is not.
+  const uint16_t* cgu;
+  const uint16_t* cwd;
+  const uint16_t* ngu;
+  const uint16_t* nwd;
+  auto bases = [&](const Tile& T, const uint16_t*& gu, const uint16_t*& wd) {
+    gu = a.wgu + (size_t)T.group * (HE / 32) * KB1 * 2 * FRAG_ELEMS;
+    wd = a.wd + (size_t)T.group * KB2 * (W / 32) * FRAG_ELEMS;
+  };
+  constexpr int SA = LA / RT_RING, SB = LB / RT_RING, SC = LC / RT_RING;   // super-steps per phase
+  auto ss_frag = [&](int ph, int s, int i) -> const uint16_t* {
+    if (ph == 0 || ph == 4) {
+      const int kb = s * (RT_RING / FA) + i / FA, nb = HA * wave + ((i % FA) >> 1);
+      return (ph == 0 ? cgu : ngu) + ((size_t)(nb * KB1 + kb) * 2 + (i & 1)) * FRAG_ELEMS;
+    }
+    if (ph == 1) {
+      const int kb = s * (RT_RING / FB) + i / FB, nb = 4 * HA + HBB * wave + ((i % FB) >> 1);
+      return cgu + ((size_t)(nb * KB1 + kb) * 2 + (i & 1)) * FRAG_ELEMS;
+    }
+    const int kb = s * (RT_RING / FC) + i / FC, ob = (ph == 3 ? W / 64 : 0) + NOH * wave + i % FC;
+    return cwd + ((size_t)kb * (W / 32) + ob) * FRAG_ELEMS;
+  };
+  // slot I of phase PH, refilled for super-step sn of that phase
+  auto refill = [&](v4u& dst, auto ph_tag, int i, int sn) __attribute__((always_inline)) {
+    constexpr int PH = decltype(ph_tag)::value;
+    constexpr int NSS = PH == 0 ? SA : PH == 1 ? SB : SC;
+    const bool in = sn < NSS;
+    const uint16_t* pc = ss_frag(PH, in ? sn : 0, i);
+    const uint16_t* pn = ss_frag(PH + 1, in ? 0 : sn - NSS, i);
+    dst = rt_ld16((in ? pc : pn) + (ot & 63) * 8);
+  };
+  v4u ring[RT_RING];
+
+  // ---- x_hat slabs: unit u = tid + 256 i of a slab is row u / 8, 16-byte
+  // chunk u % 8 of the slab's 64 columns, stored at chunk (u % 8) ^ (row % 8)
+  // of its LDS row (XOR swizzle: the fragment reads of 8 consecutive rows hit
+  // 8 different bank groups). x_hat stays below 4 GiB (the host checks its
+  // size), so a lane keeps one 32-bit byte offset per row of its units, for
+  // this tile and the next.
+  uint32_t roff[SU], roffn[SU];
+  auto slab_rows = [&](int p, int buf, uint32_t* ro) {
+#pragma unroll
+    for (int i = 0; i < SU; ++i) {
+      const int u = ot + i * RT_NT;
+      const int b = rowb[buf][u >> 3];
+      ro[i] = (((uint32_t)p * (uint32_t)a.B + (uint32_t)(b < 0 ? 0 : b)) * (uint32_t)W + (uint32_t)(u & 7) * 8u) * 2u;
+    }
+  };
+  // slab t of the slab stream (t >= NSL: the next tile's slab t - NSL)
+  auto slab_load = [&](int t, v4u* v) __attribute__((always_inline)) {
+    const bool nxt = t >= NSL;
+    const int col = (nxt ? t - NSL : (t >= NSP ? t - NSP : t)) * RT_SC * 2;
+    const char* base = reinterpret_cast<const char*>(a.xhat) + col;
+    // a select of values, not of the two arrays (which would leave them in
+    // scratch memory)
+    const uint32_t m = nxt ? ~0u : 0u;
+#pragma unroll
+    for (int i = 0; i < SU; ++i) v[i] = rt_ld16(base + (roff[i] ^ ((roff[i] ^ roffn[i]) & m)));
+  };
+  auto slab_store = [&](int sb, const v4u* v) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < SU; ++i) {
+      const int u = ot + i * RT_NT, r = u >> 3;
+      *reinterpret_cast<v4u*>(&slabs[sb * SLAB + r * RT_SC + (((u & 7) ^ (r & 7)) * 8)]) = v[i];
+    }
+  };
+  // B operand of row block rb, k-step q of a slab: row 32 rb + l32, columns
+  // 16 q + 8 h32 .. + 8
+  auto slab_frag = [&](int sb, int rb, int q) -> v4u {
+    const int r = rb * 32 + (ot & 31);
+    return *reinterpret_cast<const v4u*>(&slabs[sb * SLAB + r * RT_SC + (((2 * q + ((ot >> 5) & 1)) ^ (r & 7)) * 8)]);
+  };
+  // B operand of GEMM2 k-step kb: U row 32 rb + l32, hidden 16 kb + 8 h32 .. + 8
+  auto u_frag = [&](int rb, int kb) -> v4u {
+    return *reinterpret_cast<const v4u*>(&us[(rb * 32 + (ot & 31)) * US + kb * 16 + ((ot >> 5) & 1) * 8]);
+  };
+
+  // ---- first tile -----------------------------------------------------------------
+  Tile cur, nx;
+  if (tid == 0) claim = atomicAdd(&a.qhead[qx], 1);
+  __syncthreads();
+  if (!qdecode(claim, cur)) return;                  // uniform per workgroup
+  __syncthreads();
+  if (tid == 0) claim = atomicAdd(&a.qhead[qx], 1);
+  __syncthreads();
+  bool has_nx = qdecode(claim, nx);
+  if (!has_nx) nx = cur;
+  set_rows(cur, 0);
+  set_rows(nx, 1);
+  bases(cur, cgu, cwd);
+  bases(nx, ngu, nwd);
+  __syncthreads();
+  int buf = 0;
+  v4u sv[2][SU];   // slab t waits in register set t % 2
+  slab_rows(cur.p, 0, roff);
+  slab_rows(nx.p, 1, roffn);
+  {
+    v4u s0[SU];
+    slab_load(0, s0);
+    slab_load(1, sv[1]);
+    slab_load(2, sv[0]);
+#pragma unroll
+    for (int f = 0; f < RT_RING; ++f) ring[f] = rt_ld16(ss_frag(0, 0, f) + (tid & 63) * 8);
+    slab_store(0, s0);
+  }
+  __syncthreads();
+
+  while (true) {
+    fresh();
+    v4u xb[2][RT_RB];
+#pragma unroll
+    for (int rb = 0; rb < RT_RB; ++rb) xb[0][rb] = slab_frag(0, rb, 0);
+
+    // ---- one slab step of GEMM1 pass PH (0: A, 1: B): slab t = 6 m + K of
+    // the pass (m runtime, K compile-time; t + NSP in the tile's slab stream
+    // for pass B). K % 3 is the slab's buffer. Slab t+1 goes from registers
+    // to its buffer and slab t+3's loads go out, then the slab's 4 k-steps.
+    // The barrier before the last k-step makes slab t+1 visible (that step
+    // prefetches its first fragments) and means every wave is done with slab
+    // t-1, whose buffer the next step fills.
+    auto slab_step = [&](auto ph_tag, auto k_tag, int m, auto& sg, auto& su) __attribute__((always_inline)) {
+      constexpr int PH = decltype(ph_tag)::value, K = decltype(k_tag)::value;
+      constexpr int F = PH == 0 ? FA : FB, KPS = RT_RING / F;   // k-steps per super-step
+      constexpr int sb = K % 3, sbn = (K + 1) % 3;
+      const int t = (PH == 0 ? 0 : NSP) + 6 * m + K;             // slab of the tile's stream
+      slab_store(sbn, sv[(K + 1) & 1]);
+      slab_load(t + 3, sv[(K + 1) & 1]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int cb = q & 1;
+        if (q == 3) __syncthreads();
+        if (q < 3) {
+#pragma unroll
+          for (int rb = 0; rb < RT_RB; ++rb) xb[cb ^ 1][rb] = slab_frag(sb, rb, q + 1);
+        } else if (t + 1 < NSL) {
+#pragma unroll
+          for (int rb = 0; rb < RT_RB; ++rb) xb[cb ^ 1][rb] = slab_frag(sbn, rb, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // k-step 24 m + 4 K + q of the pass: super-step 24 m / KPS + (4 K + q) / KPS
+        constexpr int KQ = 4 * K;
+        const int sn = m * (24 / KPS) + (KQ + q) / KPS + 1;
+#pragma unroll
+        for (int i = 0; i < F; ++i) {
+          const int slot = ((KQ + q) % KPS) * F + i;
+          const int h = i >> 1;
+#pragma unroll
+          for (int rb = 0; rb < RT_RB; ++rb) {
+            if (i & 1) su[rb][h] = rt_mfma(ring[slot], xb[cb][rb], su[rb][h]);
+            else sg[rb][h] = rt_mfma(ring[slot], xb[cb][rb], sg[rb][h]);
+          }
+          refill(ring[slot], std::integral_constant<int, PH>{}, slot, sn);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // U of a pass's hidden blocks (block nb0 + h of the wave) -> LDS
+    auto store_u = [&](int nb0, auto& sg, auto& su, auto nh_tag) __attribute__((always_inline)) {
+      constexpr int NH = decltype(nh_tag)::value;
+#pragma unroll
+      for (int rb = 0; rb < RT_RB; ++rb)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            float uv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) uv[e] = rt_silu(sg[rb][h][4 * g4 + e]) * su[rb][h][4 * g4 + e];
+            uint2 w2;
+            w2.x = pack_bf16x2(uv[0], uv[1]);
+            w2.y = pack_bf16x2(uv[2], uv[3]);
+            *reinterpret_cast<uint2*>(&us[(rb * 32 + (ot & 31)) * US + (nb0 + h) * 32 + 8 * g4 + 4 * ((ot >> 5) & 1)]) = w2;
+            // one accumulator quarter at a time: the scheduler would otherwise
+            // move every accumulator to VGPRs at once
+            __builtin_amdgcn_sched_barrier(0);
+          }
+    };
+
+    // ================= GEMM1 pass A =================
+    {
+      f32x16 sg[RT_RB][HA], su[RT_RB][HA];
+#pragma unroll
+      for (int rb = 0; rb < RT_RB; ++rb)
+#pragma unroll
+        for (int h = 0; h < HA; ++h) sg[rb][h] = su[rb][h] = f32x16{};
+#pragma unroll
+      for (int m = 0; m < NSP / 6; ++m) {
+        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, m, sg, su);
+        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, m, sg, su);
+        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, m, sg, su);
+        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{}, m, sg, su);
+        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 4>{}, m, sg, su);
+        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 5>{}, m, sg, su);
+      }
+      store_u(HA * wave, sg, su, std::integral_constant<int, HA>{});
+    }
+    // ================= GEMM1 pass B =================
+    fresh();
+    {
+      f32x16 sg[RT_RB][HBB], su[RT_RB][HBB];
+#pragma unroll
+      for (int rb = 0; rb < RT_RB; ++rb)
+#pragma unroll
+        for (int h = 0; h < HBB; ++h) sg[rb][h] = su[rb][h] = f32x16{};
+#pragma unroll
+      for (int m = 0; m < NSP / 6; ++m) {
+        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, m, sg, su);
+        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, m, sg, su);
+        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{}, m, sg, su);
+        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 3>{}, m, sg, su);
+        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 4>{}, m, sg, su);
+        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 5>{}, m, sg, su);
+      }
+      store_u(4 * HA + HBB * wave, sg, su, std::integral_constant<int, HBB>{});
+    }
+    __syncthreads();   // U complete
+
+    // the claim of the tile after next goes out now (read after the epilogue)
+    int qnext = 0;
+    if (tid == 0) qnext = atomicAdd(&a.qhead[qx], 1);
+
+    // ================= GEMM2, two column halves, each with its epilogue =================
+    v4u ub[2][RT_RB];
+    auto gemm2_half = [&](auto ph_tag, f32x16 (&o)[RT_RB][NOH]) __attribute__((always_inline)) {
+      constexpr int PH = decltype(ph_tag)::value;
+#pragma unroll
+      for (int rb = 0; rb < RT_RB; ++rb)
+#pragma unroll
+        for (int j = 0; j < NOH; ++j) o[rb][j] = f32x16{};
+#pragma unroll
+      for (int rb = 0; rb < RT_RB; ++rb) ub[0][rb] = u_frag(rb, 0);
+#pragma unroll
+      for (int k0 = 0; k0 < KB2; k0 += 4) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int kb = k0 + t, cb = t & 1;
+          // past the last k-step the prefetch reads k-step 0 again (unused)
+          const int kn = kb + 1 < KB2 ? kb + 1 : 0;
+#pragma unroll
+          for (int rb = 0; rb < RT_RB; ++rb) ub[cb ^ 1][rb] = u_frag(rb, kn);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < FC; ++j) {
+            const int slot = t * FC + j;   // super-step k0 / 4
+#pragma unroll
+            for (int rb = 0; rb < RT_RB; ++rb) o[rb][j] = rt_mfma(ring[slot], ub[cb][rb], o[rb][j]);
+            refill(ring[slot], std::integral_constant<int, PH>{}, slot, k0 / 4 + 1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    // gate * O of row block rb, half c -> staging rows [32 r0 ...) (stride HS)
+    auto stage_rb = [&](uint16_t* stg, int rs, int rb, const f32x16 (&o)[RT_RB][NOH]) __attribute__((always_inline)) {
+      const float g = rowg[buf][rb * 32 + (ot & 31)];
+#pragma unroll
+      for (int j = 0; j < NOH; ++j)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          uint2 w2;
+          w2.x = pack_bf16x2(g * o[rb][j][4 * g4], g * o[rb][j][4 * g4 + 1]);
+          w2.y = pack_bf16x2(g * o[rb][j][4 * g4 + 2], g * o[rb][j][4 * g4 + 3]);
+          *reinterpret_cast<uint2*>(&stg[(rs + (ot & 31)) * HS + (NOH * wave + j) * 32 + 8 * g4 + 4 * ((ot >> 5) & 1)]) = w2;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // staged rows [row0, row0 + nr) of half c -> the expert-output rows
+    constexpr int U8H = W / 16;   // 16-byte units per half row
+    auto store_rows = [&](const uint16_t* stg, int row0, int nr, int c) __attribute__((always_inline)) {
+      for (int u = ot; u < nr * U8H; u += RT_NT) {
+        const int r = u / U8H, c8 = u - r * U8H;
+        const v4u v = *reinterpret_cast<const v4u*>(&stg[r * HS + c8 * 8]);
+        const int row = row0 + r;
+        if (rowb[buf][row] >= 0)
+          *reinterpret_cast<v4u*>(a.part + (size_t)rowgi[buf][row] * W + c * (W / 2) + c8 * 8) = v;
+      }
+    };
+    {
+      fresh();
+      f32x16 o[RT_RB][NOH];
+      gemm2_half(std::integral_constant<int, 2>{}, o);
+      fresh();
+      // half 0 goes out through slab buffers 1 and 2 (free until the next
+      // tile), 32 rows at a time, while U is still needed
+      uint16_t* stg = slabs + SLAB;
+#pragma unroll
+      for (int rb = 0; rb < RT_RB; ++rb) {
+        stage_rb(stg, 0, rb, o);
+        __syncthreads();
+        store_rows(stg, rb * 32, 32, 0);
+        __syncthreads();
+      }
+    }
+    {
+      fresh();
+      f32x16 o[RT_RB][NOH];
+      gemm2_half(std::integral_constant<int, 3>{}, o);
+      fresh();
+      __syncthreads();   // every wave's U reads done: U becomes the stage
+#pragma unroll
+      for (int rb = 0; rb < RT_RB; ++rb) stage_rb(us, rb * 32, rb, o);
+      if (tid == 0) claim = qnext;
+      __syncthreads();
+      store_rows(us, 0, BM, 1);
+      __syncthreads();
+    }
+    if (!has_nx) break;
+
+    // ---- the next tile; the one after it is decoded into the freed row table
+    cur = nx;
+    buf ^= 1;
+    cgu = ngu;
+    cwd = nwd;
+#pragma unroll
+    for (int i = 0; i < SU; ++i) roff[i] = roffn[i];
+    has_nx = qdecode(claim, nx);
+    if (!has_nx) nx = cur;
+    set_rows(nx, buf ^ 1);
+    bases(nx, ngu, nwd);
+    __syncthreads();
+    slab_rows(nx.p, buf ^ 1, roffn);
+  }
+}
+
+template <int W, int HE>
+hipError_t launch_rt(const MlpArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((routed_kernel<W, HE>), dim3(grid), dim3(RT_NT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int routed_wide_rows(int W, int h_e) { return (W == 768 && h_e == 384) ? RT_BM : 0; }
+
+hipError_t launch_routed_wide(const MlpArgs& a, int tiles, int workers, hipStream_t s) {
+  if (tiles <= 0) return hipSuccess;
+  workers &= ~7;
+  const int grid = (workers <= 0 || tiles <= workers) ? tiles : workers;
+  if (a.hidden == 384) return launch_rt<768, 384>(a, grid, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tmx
