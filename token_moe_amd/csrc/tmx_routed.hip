@@ -47,6 +47,7 @@ constexpr int RT_RB = 4;     // 32-row blocks per tile
 constexpr int RT_BM = 32 * RT_RB;
 constexpr int RT_SC = 64;    // columns per x_hat slab
 constexpr int RT_RING = 12;  // weight fragments in flight per wave
+constexpr int RT_RSRC_W3 = 0x00020000;   // buffer resource word 3: raw 32-bit data, no swizzle
 
 // 16 bytes as a native vector: arrays of it stay in registers (arrays of the
 // struct type uint4 are copied with memcpy, which can leave them in scratch)
@@ -81,9 +82,9 @@ struct RtShape {
   static_assert(HE % 128 == 0 && HBB >= 1 && HBB <= 2, "two GEMM1 passes of at most 2 hidden blocks per wave");
   static_assert(W % 256 == 0 && W % RT_SC == 0 && NSP % 6 == 0, "slab steps run in groups of six");
   static_assert((BM * RT_SC / 8) % RT_NT == 0, "slab units per lane");
-  static_assert((24 * FA) % RT_RING == 0 && (24 * FB) % RT_RING == 0 && (4 * FC) % RT_RING == 0 &&
-                RT_RING % FA == 0 && RT_RING % FB == 0 && RT_RING % FC == 0,
-                "ring slots must repeat per loop iteration of every phase");
+  static_assert(LA % RT_RING == 0 && LB % RT_RING == 0 && LC % RT_RING == 0 && RT_RING % FA == 0 &&
+                RT_RING % FB == 0 && RT_RING % FC == 0,
+                "every phase is whole turns of the ring, each of whole k-steps");
   static_assert(KB2 % 4 == 0, "GEMM2 k-steps run in groups of four");
   static_assert(32 * HS * 2 <= 2 * SLAB * 2, "a staged 32-row half fits in two slab buffers");
   static_assert(BM * HS <= BM * US, "a staged 128-row half fits in the U region");
@@ -169,35 +170,46 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
   // selected, so every refill is one unconditional load (a load on one path
   // only makes the compiler wait for every load in flight where the paths
   // join). i is a compile-time constant; only the super-step index is not.
-  const uint16_t* cgu;
-  const uint16_t* cwd;
-  const uint16_t* ngu;
-  const uint16_t* nwd;
-  auto bases = [&](const Tile& T, const uint16_t*& gu, const uint16_t*& wd) {
-    gu = a.wgu + (size_t)T.group * (HE / 32) * KB1 * 2 * FRAG_ELEMS;
-    wd = a.wd + (size_t)T.group * KB2 * (W / 32) * FRAG_ELEMS;
+  // The weights of a bucket, and x_hat, are read through buffer resources:
+  // the lane's part of an address is a 32-bit VGPR offset (lane and wave),
+  // the fragment's a constant byte offset, so no load needs 64-bit address
+  // arithmetic (which, once unrolled, the compiler would keep in scalar
+  // registers for hundreds of fragments).
+  constexpr uint32_t GU_BYTES = (HE / 32) * KB1 * 2 * FRAG_ELEMS * 2;   // gate|up fragments of a bucket
+  constexpr uint32_t WD_BYTES = KB2 * (W / 32) * FRAG_ELEMS * 2;        // down fragments of a bucket
+  auto rsrc = [](const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, RT_RSRC_W3);
   };
-  constexpr int SA = LA / RT_RING, SB = LB / RT_RING, SC = LC / RT_RING;   // super-steps per phase
-  auto ss_frag = [&](int ph, int s, int i) -> const uint16_t* {
+  __amdgpu_buffer_rsrc_t cgu, cwd, ngu, nwd;
+  auto bases = [&](const Tile& T, __amdgpu_buffer_rsrc_t& gu, __amdgpu_buffer_rsrc_t& wd) {
+    gu = rsrc(a.wgu + (size_t)T.group * (GU_BYTES / 2), GU_BYTES);
+    wd = rsrc(a.wd + (size_t)T.group * (WD_BYTES / 2), WD_BYTES);
+  };
+  // per-lane byte offsets of the phases (lane and wave parts)
+  auto voff_gu = [&](int nb0) -> uint32_t { return (uint32_t)(ot & 63) * 16u + (uint32_t)nb0 * KB1 * 2048u; };
+  auto voff_wd = [&]() -> uint32_t { return (uint32_t)(ot & 63) * 16u + (uint32_t)(NOH * wave) * 1024u; };
+  // fragment at position pos of phase ph (ph and pos compile-time once unrolled)
+  auto wload = [&](int ph, int pos) __attribute__((always_inline)) -> v4u {
     if (ph == 0 || ph == 4) {
-      const int kb = s * (RT_RING / FA) + i / FA, nb = HA * wave + ((i % FA) >> 1);
-      return (ph == 0 ? cgu : ngu) + ((size_t)(nb * KB1 + kb) * 2 + (i & 1)) * FRAG_ELEMS;
+      const int kb = pos / FA, ii = pos % FA;
+      const int c = (((ii >> 1) * KB1 + kb) * 2 + (ii & 1)) * 1024;
+      return __builtin_amdgcn_raw_buffer_load_b128(ph == 0 ? cgu : ngu, voff_gu(HA * wave), c, 0);
     }
     if (ph == 1) {
-      const int kb = s * (RT_RING / FB) + i / FB, nb = 4 * HA + HBB * wave + ((i % FB) >> 1);
-      return cgu + ((size_t)(nb * KB1 + kb) * 2 + (i & 1)) * FRAG_ELEMS;
+      const int kb = pos / FB, ii = pos % FB;
+      const int c = (((ii >> 1) * KB1 + kb) * 2 + (ii & 1)) * 1024;
+      return __builtin_amdgcn_raw_buffer_load_b128(cgu, voff_gu(4 * HA + HBB * wave), c, 0);
     }
-    const int kb = s * (RT_RING / FC) + i / FC, ob = (ph == 3 ? W / 64 : 0) + NOH * wave + i % FC;
-    return cwd + ((size_t)kb * (W / 32) + ob) * FRAG_ELEMS;
+    const int kb = pos / FC, j = pos % FC;
+    const int c = (kb * (W / 32) + (ph == 3 ? W / 64 : 0) + j) * 1024;
+    return __builtin_amdgcn_raw_buffer_load_b128(cwd, voff_wd(), c, 0);
   };
-  // slot I of phase PH, refilled for super-step sn of that phase
+  constexpr int SA = LA / RT_RING, SB = LB / RT_RING, SC = LC / RT_RING;   // super-steps per phase
+  // slot i of phase PH, refilled for super-step sn (past the phase: the next one)
   auto refill = [&](v4u& dst, auto ph_tag, int i, int sn) __attribute__((always_inline)) {
     constexpr int PH = decltype(ph_tag)::value;
     constexpr int NSS = PH == 0 ? SA : PH == 1 ? SB : SC;
-    const bool in = sn < NSS;
-    const uint16_t* pc = ss_frag(PH, in ? sn : 0, i);
-    const uint16_t* pn = ss_frag(PH + 1, in ? 0 : sn - NSS, i);
-    dst = rt_ld16((in ? pc : pn) + (ot & 63) * 8);
+    dst = sn < NSS ? wload(PH, sn * RT_RING + i) : wload(PH + 1, (sn - NSS) * RT_RING + i);
   };
   v4u ring[RT_RING];
 
@@ -217,15 +229,12 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
     }
   };
   // slab t of the slab stream (t >= NSL: the next tile's slab t - NSL)
+  const __amdgpu_buffer_rsrc_t xr = rsrc(a.xhat, (uint32_t)((uint64_t)a.P * a.B * W * 2));
   auto slab_load = [&](int t, v4u* v) __attribute__((always_inline)) {
     const bool nxt = t >= NSL;
     const int col = (nxt ? t - NSL : (t >= NSP ? t - NSP : t)) * RT_SC * 2;
-    const char* base = reinterpret_cast<const char*>(a.xhat) + col;
-    // a select of values, not of the two arrays (which would leave them in
-    // scratch memory)
-    const uint32_t m = nxt ? ~0u : 0u;
 #pragma unroll
-    for (int i = 0; i < SU; ++i) v[i] = rt_ld16(base + (roff[i] ^ ((roff[i] ^ roffn[i]) & m)));
+    for (int i = 0; i < SU; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, nxt ? roffn[i] : roff[i], col, 0);
   };
   auto slab_store = [&](int sb, const v4u* v) __attribute__((always_inline)) {
 #pragma unroll
@@ -270,7 +279,7 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
     slab_load(1, sv[1]);
     slab_load(2, sv[0]);
 #pragma unroll
-    for (int f = 0; f < RT_RING; ++f) ring[f] = rt_ld16(ss_frag(0, 0, f) + (tid & 63) * 8);
+    for (int f = 0; f < RT_RING; ++f) ring[f] = wload(0, f);
     slab_store(0, s0);
   }
   __syncthreads();
@@ -290,7 +299,7 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
     // t-1, whose buffer the next step fills.
     auto slab_step = [&](auto ph_tag, auto k_tag, int m, auto& sg, auto& su) __attribute__((always_inline)) {
       constexpr int PH = decltype(ph_tag)::value, K = decltype(k_tag)::value;
-      constexpr int F = PH == 0 ? FA : FB, KPS = RT_RING / F;   // k-steps per super-step
+      constexpr int F = PH == 0 ? FA : FB;
       constexpr int sb = K % 3, sbn = (K + 1) % 3;
       const int t = (PH == 0 ? 0 : NSP) + 6 * m + K;             // slab of the tile's stream
       slab_store(sbn, sv[(K + 1) & 1]);
@@ -307,12 +316,11 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
           for (int rb = 0; rb < RT_RB; ++rb) xb[cb ^ 1][rb] = slab_frag(sbn, rb, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // k-step 24 m + 4 K + q of the pass: super-step 24 m / KPS + (4 K + q) / KPS
-        constexpr int KQ = 4 * K;
-        const int sn = m * (24 / KPS) + (KQ + q) / KPS + 1;
+        // k-step 24 m + 4 K + q of the pass (all compile-time once unrolled)
+        const int kb = 24 * m + 4 * K + q;
 #pragma unroll
         for (int i = 0; i < F; ++i) {
-          const int slot = ((KQ + q) % KPS) * F + i;
+          const int pos = kb * F + i, slot = pos % RT_RING, sn = pos / RT_RING + 1;
           const int h = i >> 1;
 #pragma unroll
           for (int rb = 0; rb < RT_RB; ++rb) {
@@ -411,10 +419,10 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int j = 0; j < FC; ++j) {
-            const int slot = t * FC + j;   // super-step k0 / 4
+            const int pos = kb * FC + j, slot = pos % RT_RING, sn = pos / RT_RING + 1;
 #pragma unroll
             for (int rb = 0; rb < RT_RB; ++rb) o[rb][j] = rt_mfma(ring[slot], ub[cb][rb], o[rb][j]);
-            refill(ring[slot], std::integral_constant<int, PH>{}, slot, k0 / 4 + 1);
+            refill(ring[slot], std::integral_constant<int, PH>{}, slot, sn);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
