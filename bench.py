@@ -35,6 +35,8 @@ HBM_PEAK_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "mlp_dense_workload2_counters.md")
 KERNEL_SOURCES = ("token_moe_amd/csrc/tmx_mlp.hip", "token_moe_amd/csrc/tmx_device.h", "token_moe_amd/build.py",
                   "token_moe_amd/csrc/tmx_internal.h")
+ROUTED_WIDE_SOURCES = ("token_moe_amd/csrc/tmx_routed.hip", "token_moe_amd/csrc/tmx_device.h", "token_moe_amd/build.py",
+                       "token_moe_amd/csrc/tmx_internal.h")
 RMX_COUNTERS_FILE = os.path.join(ROOT, "profiles", "rmx_block_{workload}_counters.md")
 RMX_KERNEL_SOURCES = ("token_moe_amd/csrc/tmx_rankmixer.hip", "token_moe_amd/csrc/tmx_device.h",
                       "token_moe_amd/build.py", "token_moe_amd/csrc/tmx_internal.h")
@@ -158,6 +160,18 @@ def cpu_baseline(wl, banks, x, budget_s):
         value = n / dt
     return {"value": value, "unit": "samples/s", "cores": cpu_cores(), "blas_threads": int(threads),
             "kind": "oracle", "sample": what}
+
+
+def routed_is_wide(wl):
+    """Whether the library runs this workload's routed experts in the
+    128-row wide kernel (W 768, h_e 384) rather than the fused MLP kernel."""
+    return wl.width(1) == 768 and wl.expert_hidden == 384
+
+
+def routed_kernel_name(wl):
+    if routed_is_wide(wl):
+        return "routed_kernel<768, 384> (128-row tiles)"
+    return f"mlp_kernel<{wl.width(1)}, ROUTED>"
 
 
 def moe_kernel_work(wl):
@@ -323,8 +337,10 @@ def main(argv=None):
         roofline = {"bound": d["bound"], "achieved": d.get("achieved_tflops", d.get("achieved_gbs")),
                     "peak": BF16_PEAK_TFLOPS if d["bound"] == "mfma" else HBM_PEAK_GBS,
                     "unit": "TFLOP/s" if d["bound"] == "mfma" else "GB/s", "frac": d["frac"],
-                    "traffic": measured_traffic(wl.name, os.path.join(ROOT, "profiles", f"{dom}_{wl.name}_counters.md")),
-                    "kernel": {"mlp_routed": f"mlp_kernel<{wl.width(1)}, ROUTED>",
+                    "traffic": measured_traffic(wl.name, os.path.join(ROOT, "profiles", f"{dom}_{wl.name}_counters.md"),
+                                                ROUTED_WIDE_SOURCES if dom == "mlp_routed" and routed_is_wide(wl)
+                                                else KERNEL_SOURCES),
+                    "kernel": {"mlp_routed": routed_kernel_name(wl),
                                "mlp_shared": f"mlp_kernel<{wl.width(1)}, SHARED>"}.get(dom, dom),
                     "flop_per_launch": d.get("flop_per_launch"), "launch_ms": d["ms"]}
         kernel["kernels"] = kernels

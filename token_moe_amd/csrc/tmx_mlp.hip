@@ -81,6 +81,21 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// Streaming (non-temporal) 16-byte accesses for the MoE row streams that are
+// touched once per launch -- normalised rows, gated expert outputs, combined
+// outputs -- so that they do not push the weight fragments, which every tile
+// of a position or bucket re-reads, out of L2.
+typedef unsigned int nt_v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldg16_nt(const void* p) {
+  const nt_v4u v = __builtin_nontemporal_load(reinterpret_cast<const nt_v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void stg16_nt(void* p, const uint4 v) {
+  nt_v4u w;
+  w.x = v.x; w.y = v.y; w.z = v.z; w.w = v.w;
+  __builtin_nontemporal_store(w, reinterpret_cast<nt_v4u*>(p));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -516,7 +531,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
           // buffer under 4 GiB): one address register per load, which keeps
           // the W = 768 epilogue free of spills
           const uint32_t off = (((uint32_t)p * (uint32_t)a.B + (uint32_t)b) * (uint32_t)W + (uint32_t)c8 * 8u) * 2u;
-          v[i0 + k] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.xhat) + off);
+          v[i0 + k] = ldg16_nt(reinterpret_cast<const char*>(a.xhat) + off);
         }
       }
       if constexpr (IOB == NPRO) {
@@ -1326,7 +1341,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
             w.y = pack_bf16x2(g * o[k][2], g * o[k][3]);
             w.z = pack_bf16x2(g * o[k][4], g * o[k][5]);
             w.w = pack_bf16x2(g * o[k][6], g * o[k][7]);
-            *reinterpret_cast<uint4*>(a.part + (size_t)rowgi[buf][Ru[k]] * W + c8u[k] * 8) = w;
+            stg16_nt(a.part + (size_t)rowgi[buf][Ru[k]] * W + c8u[k] * 8, w);
           }
         } else {
           // At W = 768 the expert-output and residual loads are
@@ -1351,7 +1366,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
                   } else {
                     const int bq = bu[k] < 0 ? 0 : bu[k];
                     const int sq = s0 + sl < a.top_k ? s0 + sl : 0;
-                    q[k][sl] = ldg16(a.part + (((size_t)bq * a.P + pu[k]) * a.top_k + sq) * W + c8u[k] * 8);
+                    q[k][sl] = ldg16_nt(a.part + (((size_t)bq * a.P + pu[k]) * a.top_k + sq) * W + c8u[k] * 8);
                   }
                 }
 #pragma unroll
@@ -1390,7 +1405,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
             w.y = pack_bf16x2(o[k][2], o[k][3]);
             w.z = pack_bf16x2(o[k][4], o[k][5]);
             w.w = pack_bf16x2(o[k][6], o[k][7]);
-            *reinterpret_cast<uint4*>(a.out + off[k]) = w;
+            if constexpr (MODE == MLP_SHARED) stg16_nt(a.out + off[k], w);
+            else *reinterpret_cast<uint4*>(a.out + off[k]) = w;
           }
         }
       }

@@ -46,8 +46,12 @@ constexpr int RT_NT = 256;   // 4 waves
 constexpr int RT_RB = 4;     // 32-row blocks per tile
 constexpr int RT_BM = 32 * RT_RB;
 constexpr int RT_SC = 64;    // columns per x_hat slab
-constexpr int RT_RING = 12;  // weight fragments in flight per wave
+constexpr int RT_RING = 24;  // weight fragments in flight per wave
 constexpr int RT_RSRC_W3 = 0x00020000;   // buffer resource word 3: raw 32-bit data, no swizzle
+// cache policy of the second pass's x_hat loads (the rows' last use) and of
+// the gated-output stores: streaming (non-temporal), which keeps the expert
+// weights, re-read by every tile of a bucket, in L2
+constexpr int RT_NT_POLICY = 2;
 
 // 16 bytes as a native vector: arrays of it stay in registers (arrays of the
 // struct type uint4 are copied with memcpy, which can leave them in scratch)
@@ -234,7 +238,11 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
     const bool nxt = t >= NSL;
     const int col = (nxt ? t - NSL : (t >= NSP ? t - NSP : t)) * RT_SC * 2;
 #pragma unroll
-    for (int i = 0; i < SU; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, nxt ? roffn[i] : roff[i], col, 0);
+    for (int i = 0; i < SU; ++i) {
+      const uint32_t o = nxt ? roffn[i] : roff[i];
+      v[i] = (t >= NSP && !nxt) ? __builtin_amdgcn_raw_buffer_load_b128(xr, o, col, RT_NT_POLICY)
+                                : __builtin_amdgcn_raw_buffer_load_b128(xr, o, col, 0);
+    }
   };
   auto slab_store = [&](int sb, const v4u* v) __attribute__((always_inline)) {
 #pragma unroll
@@ -286,9 +294,9 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
 
   while (true) {
     fresh();
-    v4u xb[2][RT_RB];
+    v4u xb[RT_RB];
 #pragma unroll
-    for (int rb = 0; rb < RT_RB; ++rb) xb[0][rb] = slab_frag(0, rb, 0);
+    for (int rb = 0; rb < RT_RB; ++rb) xb[rb] = slab_frag(0, rb, 0);
 
     // ---- one slab step of GEMM1 pass PH (0: A, 1: B): slab t = 6 m + K of
     // the pass (m runtime, K compile-time; t + NSP in the tile's slab stream
@@ -306,28 +314,31 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
       slab_load(t + 3, sv[(K + 1) & 1]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int cb = q & 1;
         if (q == 3) __syncthreads();
-        if (q < 3) {
-#pragma unroll
-          for (int rb = 0; rb < RT_RB; ++rb) xb[cb ^ 1][rb] = slab_frag(sb, rb, q + 1);
-        } else if (t + 1 < NSL) {
-#pragma unroll
-          for (int rb = 0; rb < RT_RB; ++rb) xb[cb ^ 1][rb] = slab_frag(sbn, rb, 0);
-        }
         __builtin_amdgcn_sched_barrier(0);
-        // k-step 24 m + 4 K + q of the pass (all compile-time once unrolled)
+        // k-step 24 m + 4 K + q of the pass (all compile-time once unrolled).
+        // Row block by row block: once a block's F MFMAs have issued, its
+        // x_hat fragment is replaced by the next k-step's (the next slab's on
+        // the last step), so one register set serves both; the weight
+        // fragments' slots are refilled after the last block.
         const int kb = 24 * m + 4 * K + q;
 #pragma unroll
-        for (int i = 0; i < F; ++i) {
-          const int pos = kb * F + i, slot = pos % RT_RING, sn = pos / RT_RING + 1;
-          const int h = i >> 1;
+        for (int rb = 0; rb < RT_RB; ++rb) {
 #pragma unroll
-          for (int rb = 0; rb < RT_RB; ++rb) {
-            if (i & 1) su[rb][h] = rt_mfma(ring[slot], xb[cb][rb], su[rb][h]);
-            else sg[rb][h] = rt_mfma(ring[slot], xb[cb][rb], sg[rb][h]);
+          for (int i = 0; i < F; ++i) {
+            // the pass's first k-step takes a zero accumulator operand: no
+            // separate clearing, which the compiler would hoist into the
+            // previous phase (evicting its live accumulators to VGPRs)
+            f32x16& acc = (i & 1) ? su[rb][i >> 1] : sg[rb][i >> 1];
+            acc = rt_mfma(ring[(kb * F + i) % RT_RING], xb[rb], kb == 0 ? f32x16{} : acc);
           }
-          refill(ring[slot], std::integral_constant<int, PH>{}, slot, sn);
+          if (q < 3) xb[rb] = slab_frag(sb, rb, q + 1);
+          else if (t + 1 < NSL) xb[rb] = slab_frag(sbn, rb, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < F; ++i) {
+          const int pos = kb * F + i;
+          refill(ring[pos % RT_RING], std::integral_constant<int, PH>{}, pos % RT_RING, pos / RT_RING + 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -358,10 +369,6 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
     {
       f32x16 sg[RT_RB][HA], su[RT_RB][HA];
 #pragma unroll
-      for (int rb = 0; rb < RT_RB; ++rb)
-#pragma unroll
-        for (int h = 0; h < HA; ++h) sg[rb][h] = su[rb][h] = f32x16{};
-#pragma unroll
       for (int m = 0; m < NSP / 6; ++m) {
         slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, m, sg, su);
         slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, m, sg, su);
@@ -376,10 +383,6 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
     fresh();
     {
       f32x16 sg[RT_RB][HBB], su[RT_RB][HBB];
-#pragma unroll
-      for (int rb = 0; rb < RT_RB; ++rb)
-#pragma unroll
-        for (int h = 0; h < HBB; ++h) sg[rb][h] = su[rb][h] = f32x16{};
 #pragma unroll
       for (int m = 0; m < NSP / 6; ++m) {
         slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, m, sg, su);
@@ -398,38 +401,38 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
     if (tid == 0) qnext = atomicAdd(&a.qhead[qx], 1);
 
     // ================= GEMM2, two column halves, each with its epilogue =================
-    v4u ub[2][RT_RB];
+    v4u ub[RT_RB];
     auto gemm2_half = [&](auto ph_tag, f32x16 (&o)[RT_RB][NOH]) __attribute__((always_inline)) {
       constexpr int PH = decltype(ph_tag)::value;
 #pragma unroll
-      for (int rb = 0; rb < RT_RB; ++rb)
+      for (int rb = 0; rb < RT_RB; ++rb) ub[rb] = u_frag(rb, 0);
 #pragma unroll
-        for (int j = 0; j < NOH; ++j) o[rb][j] = f32x16{};
+      for (int kb = 0; kb < KB2; ++kb) {
+        __builtin_amdgcn_sched_barrier(0);
+        // past the last k-step the prefetch reads k-step 0 again (unused)
+        const int kn = kb + 1 < KB2 ? kb + 1 : 0;
 #pragma unroll
-      for (int rb = 0; rb < RT_RB; ++rb) ub[0][rb] = u_frag(rb, 0);
+        for (int rb = 0; rb < RT_RB; ++rb) {
 #pragma unroll
-      for (int k0 = 0; k0 < KB2; k0 += 4) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int kb = k0 + t, cb = t & 1;
-          // past the last k-step the prefetch reads k-step 0 again (unused)
-          const int kn = kb + 1 < KB2 ? kb + 1 : 0;
-#pragma unroll
-          for (int rb = 0; rb < RT_RB; ++rb) ub[cb ^ 1][rb] = u_frag(rb, kn);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int j = 0; j < FC; ++j) {
-            const int pos = kb * FC + j, slot = pos % RT_RING, sn = pos / RT_RING + 1;
-#pragma unroll
-            for (int rb = 0; rb < RT_RB; ++rb) o[rb][j] = rt_mfma(ring[slot], ub[cb][rb], o[rb][j]);
-            refill(ring[slot], std::integral_constant<int, PH>{}, slot, sn);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+          for (int j = 0; j < FC; ++j)
+            o[rb][j] = rt_mfma(ring[(kb * FC + j) % RT_RING], ub[rb], kb == 0 ? f32x16{} : o[rb][j]);
+          ub[rb] = u_frag(rb, kn);
         }
+#pragma unroll
+        for (int j = 0; j < FC; ++j) {
+          const int pos = kb * FC + j;
+          refill(ring[pos % RT_RING], std::integral_constant<int, PH>{}, pos % RT_RING, pos / RT_RING + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     // gate * O of row block rb, half c -> staging rows [32 r0 ...) (stride HS)
-    auto stage_rb = [&](uint16_t* stg, int rs, int rb, const f32x16 (&o)[RT_RB][NOH]) __attribute__((always_inline)) {
+    auto stage_rb = [&](uint16_t* stg, int rs, int rb, f32x16 (&o)[RT_RB][NOH]) __attribute__((always_inline)) {
+      // the block's accumulators stay in AGPRs up to here (the compiler
+      // otherwise copies every block's to VGPRs at once, the kernel's
+      // register peak)
+#pragma unroll
+      for (int j = 0; j < NOH; ++j) asm volatile("" : "+a"(o[rb][j]));
       const float g = rowg[buf][rb * 32 + (ot & 31)];
 #pragma unroll
       for (int j = 0; j < NOH; ++j)
@@ -450,7 +453,7 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
         const v4u v = *reinterpret_cast<const v4u*>(&stg[r * HS + c8 * 8]);
         const int row = row0 + r;
         if (rowb[buf][row] >= 0)
-          *reinterpret_cast<v4u*>(a.part + (size_t)rowgi[buf][row] * W + c * (W / 2) + c8 * 8) = v;
+          __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(a.part + (size_t)rowgi[buf][row] * W + c * (W / 2) + c8 * 8));
       }
     };
     {
