@@ -447,13 +447,29 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
     };
     // staged rows [row0, row0 + nr) of half c -> the expert-output rows
     constexpr int U8H = W / 16;   // 16-byte units per half row
-    auto store_rows = [&](const uint16_t* stg, int row0, int nr, int c) __attribute__((always_inline)) {
-      for (int u = ot; u < nr * U8H; u += RT_NT) {
-        const int r = u / U8H, c8 = u - r * U8H;
-        const v4u v = *reinterpret_cast<const v4u*>(&stg[r * HS + c8 * 8]);
-        const int row = row0 + r;
-        if (rowb[buf][row] >= 0)
-          __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(a.part + (size_t)rowgi[buf][row] * W + c * (W / 2) + c8 * 8));
+    // (unrolled, in batches: every batch's LDS reads go out before its
+    // stores, so a lane waits once per batch, not once per unit)
+    auto store_rows = [&](const uint16_t* stg, int row0, auto nr_tag, int c) __attribute__((always_inline)) {
+      constexpr int NR = decltype(nr_tag)::value, NU = NR * U8H / RT_NT;
+      constexpr int BATCH = NU % 8 == 0 ? 8 : NU;
+      static_assert((NR * U8H) % RT_NT == 0 && NU % BATCH == 0, "output units per lane");
+#pragma unroll
+      for (int i0 = 0; i0 < NU; i0 += BATCH) {
+        v4u v[BATCH];
+        int gi[BATCH], c8s[BATCH];
+        bool ok[BATCH];
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+          const int u = ot + (i0 + k) * RT_NT, r = u / U8H, c8 = u - r * U8H, row = row0 + r;
+          v[k] = *reinterpret_cast<const v4u*>(&stg[r * HS + c8 * 8]);
+          ok[k] = rowb[buf][row] >= 0;
+          gi[k] = rowgi[buf][row];
+          c8s[k] = c8;
+        }
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k)
+          if (ok[k])
+            __builtin_nontemporal_store(v[k], reinterpret_cast<v4u*>(a.part + (size_t)gi[k] * W + c * (W / 2) + c8s[k] * 8));
       }
     };
     {
@@ -468,7 +484,7 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
       for (int rb = 0; rb < RT_RB; ++rb) {
         stage_rb(stg, 0, rb, o);
         __syncthreads();
-        store_rows(stg, rb * 32, 32, 0);
+        store_rows(stg, rb * 32, std::integral_constant<int, 32>{}, 0);
         __syncthreads();
       }
     }
@@ -482,7 +498,7 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
       for (int rb = 0; rb < RT_RB; ++rb) stage_rb(us, rb * 32, rb, o);
       if (tid == 0) claim = qnext;
       __syncthreads();
-      store_rows(us, 0, BM, 1);
+      store_rows(us, 0, std::integral_constant<int, BM>{}, 1);
       __syncthreads();
     }
     if (!has_nx) break;
