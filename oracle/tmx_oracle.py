@@ -274,7 +274,7 @@ def route(xhat: np.ndarray, w_router: np.ndarray, top_k: int, alpha: float):
 
 def moe(xhat: np.ndarray, w_router, exp_up, exp_gate, exp_down,
         sh_up, sh_gate, sh_down, top_k: int, alpha: float, rho: bool = False,
-        idx_override: Optional[np.ndarray] = None):
+        idx_override: Optional[np.ndarray] = None, mx: bool = False):
     """Sparse-Pertoken MoE of one position ([TML] Eq. 19-21): the routed
     experts' SwiGLU outputs weighted by alpha * pi, plus the always-on shared
     SwiGLU expert of this position, ungated ([TML] 2.4.2). Only the chosen
@@ -285,6 +285,11 @@ def moe(xhat: np.ndarray, w_router, exp_up, exp_gate, exp_down,
     the inputs can resolve, both top-k sets are correct results, and a
     comparison evaluates the method on the set the other side chose after
     checking that it is one of them.
+
+    With ``mx`` the routed and shared experts' GEMMs take MXFP8 operands
+    ([TML] 2.5.2 FP8 serving; swiglu_mx on the rows xhat); the router works on
+    xhat itself, unquantised (the top-k choice depends on logit differences
+    far below the fp8 step).
 
     Returns (y [n, W], idx, gate)."""
     idx, gate, _, pi = route(xhat, w_router, top_k, alpha)
@@ -298,9 +303,12 @@ def moe(xhat: np.ndarray, w_router, exp_up, exp_gate, exp_down,
         rows, slots = np.nonzero(idx == e)
         if rows.size == 0:
             continue
-        ye = swiglu(xhat[rows], exp_up[e], exp_gate[e], exp_down[e], rho)
+        if mx:
+            ye = swiglu_mx(xhat[rows], exp_up[e], exp_gate[e], exp_down[e])
+        else:
+            ye = swiglu(xhat[rows], exp_up[e], exp_gate[e], exp_down[e], rho)
         routed[rows] += gate[rows, slots][:, None] * ye
-    shared = swiglu(xhat, sh_up, sh_gate, sh_down, rho)
+    shared = swiglu_mx(xhat, sh_up, sh_gate, sh_down) if mx else swiglu(xhat, sh_up, sh_gate, sh_down, rho)
     return routed + shared, idx, gate
 
 
@@ -325,17 +333,17 @@ def sublayer_positions(x: np.ndarray, resid: np.ndarray, cfg, layer: int, sub: i
     once in bf16 mode. x, resid, extra are [n, P, W]; F_p is the position's
     own SwiGLU (dense) or Sparse-Pertoken MoE. ``record`` (optional dict)
     receives per-position routing {(p): (idx, gate)} for MoE sub-layers.
-    With ``mx`` (dense only) the SwiGLU runs on MXFP8 operands (swiglu_mx),
-    its input rows being the fp32 normalised rows. ``route_override``
+    With ``mx`` the SwiGLU GEMMs run on MXFP8 operands (swiglu_mx): in a
+    dense sub-layer on the fp32 normalised rows, in a MoE sub-layer on xhat
+    as the bf16 path forms it (rounded to bf16 in bf16 mode: the router's
+    input and the rows the expert kernels read). ``route_override``
     [n, P, top_k] (MoE only) names the chosen experts of every row and
     position (see ``moe``)."""
     n, P, W = x.shape
     gain = weights(layer, sub, _K_GAIN, 0)
     F = np.zeros((n, P, W))
     for p in range(P):
-        if mx:
-            if cfg.E != 0:
-                raise ValueError("the MXFP8 path covers dense sub-layers")
+        if mx and cfg.E == 0:
             F[:, p] = swiglu_mx(rmsnorm(x[:, p, :], gain, cfg.eps), weights(layer, sub, _K_UP, p),
                                 weights(layer, sub, _K_GATE, p), weights(layer, sub, _K_DOWN, p))
             continue
@@ -349,7 +357,7 @@ def sublayer_positions(x: np.ndarray, resid: np.ndarray, cfg, layer: int, sub: i
                                weights(layer, sub, _K_EDOWN, p), weights(layer, sub, _K_SUP, p),
                                weights(layer, sub, _K_SGATE, p), weights(layer, sub, _K_SDOWN, p),
                                cfg.top_k, cfg.gate_scale, rho,
-                               None if route_override is None else route_override[:, p])
+                               None if route_override is None else route_override[:, p], mx)
             F[:, p] = y
             if record is not None:
                 record[p] = (idx, gate)
