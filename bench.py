@@ -164,14 +164,15 @@ def cpu_baseline(wl, banks, x, budget_s):
 
 def routed_is_wide(wl):
     """Whether the library runs this workload's routed experts in the
-    128-row wide kernel (W 768, h_e 384) rather than the fused MLP kernel."""
-    return wl.width(1) == 768 and wl.expert_hidden == 384
+    128-row wide kernel (bf16, W 768, h_e 384) rather than the fused MLP
+    kernel."""
+    return wl.dtype == "bf16" and wl.width(1) == 768 and wl.expert_hidden == 384
 
 
 def routed_kernel_name(wl):
     if routed_is_wide(wl):
         return "routed_kernel<768, 384> (128-row tiles)"
-    return f"mlp_kernel<{wl.width(1)}, ROUTED>"
+    return f"mlp_kernel<{wl.width(1)}, ROUTED{', MXFP8' if wl.dtype == 'mxfp8' else ''}>"
 
 
 def moe_kernel_work(wl):
@@ -203,7 +204,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--dtype", choices=("bf16", "mxfp8"), default="bf16",
-                    help="mxfp8: the dense workload with MXFP8 GEMM operands (bf16 activations)")
+                    help="mxfp8: the workload with MXFP8 GEMM operands (bf16 activations; dense sub-layers "
+                         "of width 256 or 512, MoE sub-layers of width 512 or 768: workloads 2, 3, 4, 5)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -229,8 +231,12 @@ def main(argv=None):
         print(f"unknown workload {args.workload!r}", file=sys.stderr)
         return 2
     if args.dtype == "mxfp8":
-        if wl.moe or wl.dtype != "bf16" or wl.rankmixer:
-            print("--dtype mxfp8 applies to the bf16 dense workloads", file=sys.stderr)
+        widths = {wl.width(0), wl.width(1)}
+        ok = (wl.dtype == "bf16" and not wl.rankmixer and
+              (widths <= {256, 512} if not wl.moe else widths <= {512, 768}))
+        if not ok:
+            print("--dtype mxfp8 applies to the bf16 workloads whose sub-layer widths are 256 or 512 "
+                  "(dense) or 512 or 768 (MoE): workloads 2, 3, 4, 5", file=sys.stderr)
             return 2
         wl = wl.with_(dtype="mxfp8")
     log("workload", wl)
@@ -312,6 +318,7 @@ def main(argv=None):
         times = ctx.kernel_times()
         ctx.set_kernel_timing(False)
         kinfo = moe_kernel_work(wl)
+        mfma_peak = FP8_PEAK_TFLOPS if wl.dtype == "mxfp8" else BF16_PEAK_TFLOPS
         kernels = {}
         for name, (tot, n) in times.items():
             kms = tot / n
@@ -322,7 +329,7 @@ def main(argv=None):
                 if bound == "mfma":
                     rec.update(bound="mfma", flop_per_launch=amount,
                                achieved_tflops=round(amount / (kms / 1e3) / 1e12, 2),
-                               frac=round(amount / (kms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4))
+                               frac=round(amount / (kms / 1e3) / 1e12 / mfma_peak, 4))
                 else:
                     rec.update(bound="hbm", bytes_per_launch=amount,
                                achieved_gbs=round(amount / (kms / 1e3) / 1e9, 1),
@@ -335,13 +342,14 @@ def main(argv=None):
         dom = max(times, key=lambda k: times[k][0])
         d = kernels[dom]
         roofline = {"bound": d["bound"], "achieved": d.get("achieved_tflops", d.get("achieved_gbs")),
-                    "peak": BF16_PEAK_TFLOPS if d["bound"] == "mfma" else HBM_PEAK_GBS,
+                    "peak": mfma_peak if d["bound"] == "mfma" else HBM_PEAK_GBS,
                     "unit": "TFLOP/s" if d["bound"] == "mfma" else "GB/s", "frac": d["frac"],
                     "traffic": measured_traffic(wl.name, os.path.join(ROOT, "profiles", f"{dom}_{wl.name}_counters.md"),
                                                 ROUTED_WIDE_SOURCES if dom == "mlp_routed" and routed_is_wide(wl)
-                                                else KERNEL_SOURCES),
+                                                else KERNEL_SOURCES) if wl.dtype == "bf16" else None,
                     "kernel": {"mlp_routed": routed_kernel_name(wl),
-                               "mlp_shared": f"mlp_kernel<{wl.width(1)}, SHARED>"}.get(dom, dom),
+                               "mlp_shared": f"mlp_kernel<{wl.width(1)}, SHARED"
+                                             f"{', MXFP8' if wl.dtype == 'mxfp8' else ''}>"}.get(dom, dom),
                     "flop_per_launch": d.get("flop_per_launch"), "launch_ms": d["ms"]}
         kernel["kernels"] = kernels
         kernel["kernel_ms_sum_per_step"] = round(step_sum, 4)

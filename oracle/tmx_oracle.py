@@ -30,7 +30,7 @@ hand-worked fixtures under ``tests/golden/``). No function is unpinned.
 from __future__ import annotations
 
 import math
-from typing import Callable, Dict, Optional, Tuple
+from typing import Callable, Dict, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -327,7 +327,8 @@ _K_ROUTER, _K_EUP, _K_EGATE, _K_EDOWN, _K_SUP, _K_SGATE, _K_SDOWN = 4, 5, 6, 7, 
 def sublayer_positions(x: np.ndarray, resid: np.ndarray, cfg, layer: int, sub: int,
                        weights: WeightGetter, extra: Optional[np.ndarray] = None,
                        rho: bool = False, record: Optional[dict] = None, mx: bool = False,
-                       route_override: Optional[np.ndarray] = None) -> np.ndarray:
+                       route_override: Optional[np.ndarray] = None,
+                       positions: Optional[Sequence[int]] = None) -> np.ndarray:
     """One Pre-Norm sub-layer over position-major rows:
     out[:, p] = resid[:, p] + F_p(RMSNorm(x[:, p])) [+ extra[:, p]], rounded
     once in bf16 mode. x, resid, extra are [n, P, W]; F_p is the position's
@@ -338,11 +339,14 @@ def sublayer_positions(x: np.ndarray, resid: np.ndarray, cfg, layer: int, sub: i
     as the bf16 path forms it (rounded to bf16 in bf16 mode: the router's
     input and the rows the expert kernels read). ``route_override``
     [n, P, top_k] (MoE only) names the chosen experts of every row and
-    position (see ``moe``)."""
+    position (see ``moe``). ``positions`` (optional) evaluates only those
+    positions; the others come back as NaN."""
     n, P, W = x.shape
     gain = weights(layer, sub, _K_GAIN, 0)
     F = np.zeros((n, P, W))
-    for p in range(P):
+    if positions is not None:
+        F[:, [p for p in range(P) if p not in set(positions)]] = np.nan
+    for p in (range(P) if positions is None else positions):
         if mx and cfg.E == 0:
             F[:, p] = swiglu_mx(rmsnorm(x[:, p, :], gain, cfg.eps), weights(layer, sub, _K_UP, p),
                                 weights(layer, sub, _K_GATE, p), weights(layer, sub, _K_DOWN, p))

@@ -80,16 +80,19 @@ def sample_rows(B, n, seed=0):
     return np.array(sorted(rows))
 
 
-def oracle_sublayer(wl, ws, layer, sub, x_rows, resid_rows=None, extra_rows=None, route=None):
+def oracle_sublayer(wl, ws, layer, sub, x_rows, resid_rows=None, extra_rows=None, route=None, positions=None):
     """Oracle of one sub-layer in block layout [n, T, D] (layer is 1-based);
     ``route`` [n, P, top_k] names the chosen experts of an MoE sub-layer
-    (the other side's choice, once checked to be a correct one)."""
+    (the other side's choice, once checked to be a correct one);
+    ``positions`` evaluates only those positions of the sub-layer (the
+    elements of the others are NaN)."""
     rho = wl.bf16_values
     mx = wl.dtype == "mxfp8"
     if sub == 0:
         Hm = orc.mix(x_rows, wl.H)
-        return orc.revert(orc.sublayer_positions(Hm, Hm, wl, layer, 0, ws, None, rho, None, mx, route), wl.T)
-    return orc.sublayer_positions(x_rows, resid_rows, wl, layer, 1, ws, extra_rows, rho, None, mx, route)
+        return orc.revert(orc.sublayer_positions(Hm, Hm, wl, layer, 0, ws, None, rho, None, mx, route, positions),
+                          wl.T)
+    return orc.sublayer_positions(x_rows, resid_rows, wl, layer, 1, ws, extra_rows, rho, None, mx, route, positions)
 
 
 def tile_rows(B, bm, seed=0):
@@ -100,7 +103,7 @@ def tile_rows(B, bm, seed=0):
     return np.minimum(starts + rng.integers(0, bm, starts.size), B - 1)
 
 
-DELTA = {"bf16": 1e-3, "f32": 1e-5}
+DELTA = {"bf16": 1e-3, "mxfp8": 1e-3, "f32": 1e-5}   # (MXFP8 routes on the bf16 x_hat, as bf16)
 
 
 def route_gpu(ctx, wl, layer, sub, xd, B):
@@ -145,7 +148,7 @@ def route_oracle(wl, ws, layer1, sub, x_rows):
     midpoint (norm_near_midpoint) may round either way, changing logit e by
     at most ulp_i * |Wr[i, e]|, and the GPU accumulates in fp32
     (logit_acc_bound)."""
-    rho = wl.dtype == "bf16"
+    rho = wl.bf16_values
     v = orc.mix(x_rows, wl.H) if sub == 0 else x_rows
     n, P, W = v.shape
     out, bound = [], []

@@ -120,10 +120,14 @@ def _create(tmx, **kw):
     (dict(dtype=1, D=96, H=4, T=4, hidden_mix=64, hidden_rev=64), "UNSUPPORTED"),      # W = 96
     (dict(dtype=1, D=128, H=4, T=4, hidden_mix=100, hidden_rev=64), "UNSUPPORTED"),    # hidden % 128
     (dict(dtype=1, D=128, H=4, T=4, E=8, top_k=2, expert_hidden=64, shared_hidden=64), "UNSUPPORTED"),
-    # MXFP8: dense, W = 256 in both sub-layers, hidden <= 1024
-    (dict(dtype=2, D=512, H=16, T=16, hidden_mix=256, hidden_rev=256), "UNSUPPORTED"),
+    # MXFP8: dense sub-layers at W = 256 or 512, MoE at W = 512, hidden <= 1024
+    (dict(dtype=2, D=768, H=16, T=16, hidden_mix=256, hidden_rev=256), "UNSUPPORTED"),
+    (dict(dtype=2, D=128, H=4, T=4, hidden_mix=256, hidden_rev=256), "UNSUPPORTED"),
     (dict(dtype=2, D=256, H=16, T=16, hidden_mix=2048, hidden_rev=256), "UNSUPPORTED"),
     (dict(dtype=2, D=256, H=16, T=16, E=16, top_k=4, expert_hidden=256, shared_hidden=512), "UNSUPPORTED"),
+    (dict(dtype=2, D=512, H=16, T=16, E=16, top_k=4, expert_hidden=256, shared_hidden=2048), "UNSUPPORTED"),
+    (dict(dtype=2, D=512, H=16, T=16, E=12, top_k=4, expert_hidden=256, shared_hidden=512), "UNSUPPORTED"),
+    (dict(dtype=2, D=512, H=16, T=16, E=16, top_k=10, expert_hidden=256, shared_hidden=512), "UNSUPPORTED"),
     (dict(dtype=3), "INVALID_ARG"),
     # MXFP8 capability checks come after every shape check: H = 0 or D % H != 0
     # must be INVALID_ARG, never a division by zero in the MXFP8 width check

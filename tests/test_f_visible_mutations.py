@@ -95,3 +95,50 @@ def test_sublayer_mutations_fail(wid, sub, monkeypatch):
     else:
         f_alone = _sublayer(wl, ws, 1, x, zero_resid=True)
         assert _row_err(_sublayer(wl, _ZeroDown(ws), 1, x, zero_resid=True), f_alone) >= MARGIN * LIMIT
+
+
+# MXFP8 (tests/test_gpu_mxfp8_f_visible.py): rows are held to 2^-4 and the
+# median row to 5e-3; the mutations must break both by 10x
+MX_LIMIT, MX_MEDIAN = 2.0 ** -4, 5e-3
+
+
+def _mx_sublayer(wl, ws, sub, x, zero_resid=False):
+    # MoE: the first and the last position only (the oracle quantises every
+    # expert it evaluates); the other positions' elements are NaN
+    pos = (0, wl.positions(sub) - 1) if wl.moe else None
+    if sub == 0:
+        Hm = orc_mod.mix(x, wl.H)
+        return orc_mod.revert(orc_mod.sublayer_positions(Hm, Hm, wl, 1, 0, ws, None, True, None, True,
+                                                         positions=pos), wl.T)
+    resid = np.zeros_like(x) if zero_resid else dg.make_x(wl, seed=wl.seed + 7, B=x.shape[0]).astype(np.float64)
+    return orc_mod.sublayer_positions(x, resid, wl, 1, 1, ws, None, True, None, True, positions=pos)
+
+
+def _row_errs(y, ref):
+    """Row-normwise errors over the elements both sides evaluated."""
+    ok = ~np.isnan(ref) & ~np.isnan(y)
+    keep = ok.any(-1)
+    d = np.where(ok, np.abs(y - ref), -np.inf).max(-1)[keep]
+    m = np.where(ok, np.abs(ref), -np.inf).max(-1)[keep]
+    return d / m
+
+
+@pytest.mark.parametrize("wid", [3, 4])
+@pytest.mark.parametrize("sub", [0, 1])
+def test_mxfp8_sublayer_mutations_fail(wid, sub, monkeypatch):
+    wl = _vis(wid, L=1, dtype="mxfp8")
+    ws = dg.WeightSource(wl, dg.weight_banks(wl))
+    x = dg.make_x(wl, B=4).astype(np.float64)
+
+    def broken(e):
+        return e.max() >= MARGIN * MX_LIMIT and np.median(e) >= MARGIN * MX_MEDIAN
+
+    ref = _mx_sublayer(wl, ws, sub, x)
+    assert broken(_row_errs(_mx_sublayer(wl, _ZeroDown(ws), sub, x), ref))
+    if sub == 0:
+        with monkeypatch.context() as m:
+            _with_reshape_map(m)
+            assert broken(_row_errs(_mx_sublayer(wl, ws, sub, x), ref))
+    else:
+        f_alone = _mx_sublayer(wl, ws, 1, x, zero_resid=True)
+        assert broken(_row_errs(_mx_sublayer(wl, _ZeroDown(ws), 1, x, zero_resid=True), f_alone))

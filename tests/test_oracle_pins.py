@@ -699,3 +699,16 @@ def test_mxfp8_moe_stack_is_the_bf16_stack_within_fp8_error():
     b = orc.stack_forward(X, cfg, ws, rho=True, mx=False)
     err = np.max(np.abs(a - b), axis=-1) / np.max(np.abs(b), axis=-1)
     assert 0 < err.max() < 5e-2
+
+
+def test_sublayer_positions_subset_equals_full_evaluation():
+    """Evaluating a subset of positions gives those positions' outputs of the
+    full evaluation bit for bit and marks the others NaN."""
+    cfg = dg.Workload("sub_pos", B=6, T=4, H=4, D=64, L=1, E=4, top_k=2, expert_hidden=64,
+                      shared_hidden=64, alpha=2.0, gap=0, dtype="mxfp8", seed=24)
+    ws = dg.WeightSource(cfg)
+    x = dg.make_x(cfg).astype(np.float64)
+    full = orc.sublayer_positions(x, x, cfg, 1, 1, ws, rho=True, mx=True)
+    part = orc.sublayer_positions(x, x, cfg, 1, 1, ws, rho=True, mx=True, positions=(1, 3))
+    assert np.array_equal(part[:, [1, 3]], full[:, [1, 3]])
+    assert np.isnan(part[:, [0, 2]]).all()

@@ -193,6 +193,31 @@ Bank& storage(tmx_ctx* c, int layer, int sub, int kind) {
   return bank(c, layer, sub, kind);
 }
 
+// MXFP8: the gate kind of a matrix family (dense, routed experts, shared
+// expert) -- its buffer holds the family's gate|up codes, then the scale
+// records of gate, up and down -- or -1 for kinds kept in bf16 (the router)
+int mx_gate_kind(int kind) {
+  switch (kind) {
+    case TMX_W_UP: case TMX_W_GATE: case TMX_W_DOWN: return TMX_W_GATE;
+    case TMX_W_EXP_UP: case TMX_W_EXP_GATE: case TMX_W_EXP_DOWN: return TMX_W_EXP_GATE;
+    case TMX_W_SH_UP: case TMX_W_SH_GATE: case TMX_W_SH_DOWN: return TMX_W_SH_GATE;
+    default: return -1;
+  }
+}
+// dwords per lane of a family's scale records, and the records' bytes
+int mx_rec(const tmx_config& c, int sub, int gate_kind) {
+  int64_t G;
+  int K, N;
+  bank_dims(c, sub, gate_kind, &G, &K, &N);
+  return mx_rec_dwords(K, N);
+}
+size_t mx_rec_bytes(const tmx_config& c, int sub, int gate_kind) {
+  int64_t G;
+  int K, N;
+  bank_dims(c, sub, gate_kind, &G, &K, &N);
+  return (size_t)G * 4 * 64 * mx_rec(c, sub, gate_kind) * 4;
+}
+
 void release(tmx_ctx* c) {
   for (void* p : c->allocs) (void)hipFree(p);
   c->allocs.clear();
@@ -302,21 +327,23 @@ tmx_status validate_config(const tmx_config* cfg) {
   const int64_t act = (int64_t)c.B_max * c.T * c.D;
   if (act > (int64_t)1 << 40) return fail(nullptr, TMX_ERR_INVALID_ARG, "B_max*T*D too large");
   if (c.dtype == TMX_MXFP8) {
-    if (c.E > 0) return fail(nullptr, TMX_ERR_UNSUPPORTED, "the MXFP8 path covers dense stacks (E = 0)");
-    if ((c.D / c.H) % 8 != 0)
-      return fail(nullptr, TMX_ERR_UNSUPPORTED, "MXFP8 path needs D/H %% 8 == 0, got %d", c.D / c.H);
+    // (bf16 activations: the bf16 checks below apply as well)
     for (int sub = 0; sub < 2; ++sub) {
-      if (width(c, sub) != 256)
-        return fail(nullptr, TMX_ERR_UNSUPPORTED, "MXFP8 path supports sub-layer width 256, got %d", width(c, sub));
-      const int h = dense_hidden(c, sub);
-      if (h % MLP_HC != 0 || h > (MX_REC_DWORDS / 3) * MLP_HC)
-        return fail(nullptr, TMX_ERR_UNSUPPORTED, "MXFP8 path needs hidden %% %d == 0 and hidden <= %d, got %d",
-                    MLP_HC, (MX_REC_DWORDS / 3) * MLP_HC, h);
+      const int W = width(c, sub);
+      if (!mlp_mx_supported(c.E > 0 ? MLP_ROUTED : MLP_DENSE, W))
+        return fail(nullptr, TMX_ERR_UNSUPPORTED,
+                    "MXFP8 path supports sub-layer widths 256 and 512 (dense) or 512 and 768 (MoE), got %d", W);
+      const int hs[2] = {c.E ? c.expert_hidden : dense_hidden(c, sub), c.E ? c.shared_hidden : MLP_HC};
+      for (int h : hs)
+        if (h % MLP_HC != 0 || h > mx_max_chunks(W) * MLP_HC)
+          return fail(nullptr, TMX_ERR_UNSUPPORTED,
+                      "MXFP8 path needs hidden %% %d == 0 and hidden <= %d at width %d, got %d", MLP_HC,
+                      mx_max_chunks(W) * MLP_HC, W, h);
     }
   }
 
   const int dh = c.D / c.H;
-  if (c.dtype == TMX_BF16) {
+  if (c.dtype == TMX_BF16 || c.dtype == TMX_MXFP8) {
     if (dh % 8 != 0)
       return fail(nullptr, TMX_ERR_UNSUPPORTED, "bf16 path needs D/H %% 8 == 0 (16-byte Mix segments), got %d", dh);
     for (int sub = 0; sub < 2; ++sub) {
@@ -347,7 +374,7 @@ tmx_status validate_config(const tmx_config* cfg) {
 
 // rows per routed bucket tile: the wide routed kernel's where it applies
 int moe_bm(const tmx_config& c, int sub) {
-  const int wide = routed_wide_rows(width(c, sub), c.expert_hidden);
+  const int wide = c.dtype == TMX_BF16 ? routed_wide_rows(width(c, sub), c.expert_hidden) : 0;
   return wide > 0 ? wide : mlp_bm(MLP_ROUTED, width(c, sub));
 }
 int moe_max_tiles(const tmx_config& c, int sub, int B) {
@@ -480,8 +507,10 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
     if (cfg.dtype == TMX_MXFP8) {
       a.wsc = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(a.wgu) +
                                                 (size_t)2 * kind_elems(cfg, sub, TMX_W_GATE));
-      return launch_timed(c, TMX_KERNEL_MLP_DENSE, st, "dense MXFP8 MLP launch",
-                          [&] { return launch_mlp_mx(a, (a.pair ? P / 2 : P) * a.rtiles, c->workers, st); });
+      a.wrec = mx_rec(cfg, sub, TMX_W_GATE);
+      return launch_timed(c, TMX_KERNEL_MLP_DENSE, st, "dense MXFP8 MLP launch", [&] {
+        return launch_mlp_mx(MLP_DENSE, W, a, (a.pair ? P / 2 : P) * a.rtiles, c->workers, st);
+      });
     }
     return launch_timed(c, TMX_KERNEL_MLP_DENSE, st, "dense MLP launch",
                         [&] { return launch_mlp(MLP_DENSE, W, a, (a.pair ? P / 2 : P) * a.rtiles, c->workers, st); });
@@ -489,7 +518,8 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
 
   // MoE: norm + route -> bucket -> routed experts -> shared expert + combine
   const int bm = moe_bm(cfg, sub);
-  const bool wide = routed_wide_rows(W, cfg.expert_hidden) > 0;
+  const bool mx = cfg.dtype == TMX_MXFP8;
+  const bool wide = !mx && routed_wide_rows(W, cfg.expert_hidden) > 0;
   RouteArgs r{};
   r.B = B; r.P = P; r.E = cfg.E; r.top_k = cfg.top_k; r.alpha = c->alpha; r.eps = cfg.eps; r.map = map;
   r.x = static_cast<const uint16_t*>(x_in); r.gain = gain;
@@ -511,15 +541,26 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   a.hidden = cfg.expert_hidden;
   a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_EXP_GATE).ptr);
   a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_EXP_DOWN).ptr);
+  if (mx) {
+    a.wsc = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(a.wgu) +
+                                              (size_t)2 * kind_elems(cfg, sub, TMX_W_EXP_GATE));
+    a.wrec = mx_rec(cfg, sub, TMX_W_EXP_GATE);
+  }
   s = launch_timed(c, TMX_KERNEL_MLP_ROUTED, st, "routed MLP launch", [&] {
-    return wide ? launch_routed_wide(a, P * a.max_tiles, c->workers, st)
-                : launch_mlp(MLP_ROUTED, W, a, P * a.max_tiles, c->workers, st);
+    return mx     ? launch_mlp_mx(MLP_ROUTED, W, a, P * a.max_tiles, c->workers, st)
+           : wide ? launch_routed_wide(a, P * a.max_tiles, c->workers, st)
+                  : launch_mlp(MLP_ROUTED, W, a, P * a.max_tiles, c->workers, st);
   });
   if (s != TMX_OK) return s;
 
   a.hidden = cfg.shared_hidden;
   a.wgu = static_cast<const uint16_t*>(storage(c, layer, sub, TMX_W_SH_GATE).ptr);
   a.wd = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_SH_DOWN).ptr);
+  if (mx) {
+    a.wsc = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(a.wgu) +
+                                              (size_t)2 * kind_elems(cfg, sub, TMX_W_SH_GATE));
+    a.wrec = mx_rec(cfg, sub, TMX_W_SH_GATE);
+  }
   set_row_tiles(a, MLP_SHARED, sub, W, P, B, map.dh * 2);
   // The shared-expert tiles are all alike, so a persistent launch keeps its
   // workgroups in step: every combine epilogue (k expert rows + residual per
@@ -529,10 +570,14 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   // while the other half compute.
   const int sh_tiles = (a.pair ? P / 2 : P) * a.rtiles;
   const int sh_grid = std::max(1, std::min(sh_tiles, c->workers & ~7));
-  const double mfma_clk = (double)mlp_bm(MLP_SHARED, W) * W * 3.0 * cfg.shared_hidden / (16384.0 * 4.0) * 32.0;
+  // (MXFP8 MFMAs take half the clocks per multiply-add)
+  const double mfma_clk = (double)mlp_bm(MLP_SHARED, W) * W * 3.0 * cfg.shared_hidden / (16384.0 * 4.0) * 32.0 /
+                          (mx ? 2.0 : 1.0);
   a.stagger = sh_tiles >= 4 * sh_grid ? (int)(1.6 * mfma_clk) : 0;
-  return launch_timed(c, TMX_KERNEL_MLP_SHARED, st, "shared MLP launch",
-                      [&] { return launch_mlp(MLP_SHARED, W, a, sh_tiles, c->workers, st); });
+  return launch_timed(c, TMX_KERNEL_MLP_SHARED, st, "shared MLP launch", [&] {
+    return mx ? launch_mlp_mx(MLP_SHARED, W, a, sh_tiles, c->workers, st)
+              : launch_mlp(MLP_SHARED, W, a, sh_tiles, c->workers, st);
+  });
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -636,9 +681,10 @@ tmx_status tmx_create(const tmx_config* cfg, int device, tmx_ctx** out) {
         if (C.dtype != TMX_F32 && (k == TMX_W_GATE || k == TMX_W_EXP_GATE || k == TMX_W_SH_GATE)) n *= 2;
         size_t bytes = n * es;
         // MXFP8: one byte per weight; the gate bank also holds the scale
-        // records of the position's gate, up and down matrices
-        if (C.dtype == TMX_MXFP8)
-          bytes = n + (k == TMX_W_GATE ? (size_t)positions(C, sub) * 4 * 64 * MX_REC_DWORDS * 4 : 0);
+        // records of its family's gate, up and down matrices (the router
+        // stays bf16)
+        if (C.dtype == TMX_MXFP8 && mx_gate_kind(k) >= 0)
+          bytes = n + (mx_gate_kind(k) == k ? mx_rec_bytes(C, sub, k) : 0);
         s = dev_alloc(c, &b.ptr, bytes, "weights");
         if (s != TMX_OK) return bail(s);
       }
@@ -648,7 +694,7 @@ tmx_status tmx_create(const tmx_config* cfg, int device, tmx_ctx** out) {
     if ((s = dev_alloc(c, &c->act[i], act * es, "activations")) != TMX_OK) return bail(s);
   if ((s = dev_alloc(c, &c->xrev, act * es, "activations")) != TMX_OK) return bail(s);
 
-  if (C.E > 0 && C.dtype == TMX_BF16) {
+  if (C.E > 0 && (C.dtype == TMX_BF16 || C.dtype == TMX_MXFP8)) {
     void* base = nullptr;
     if ((s = dev_alloc(c, &base, carve_moe_ws(C, C.B_max, nullptr, nullptr), "MoE workspace")) != TMX_OK)
       return bail(s);
@@ -752,13 +798,14 @@ tmx_status tmx_load_weights(tmx_ctx* c, int layer, int sub, int kind, const void
   const bool gu = kind == TMX_W_UP || kind == TMX_W_GATE || kind == TMX_W_EXP_UP || kind == TMX_W_EXP_GATE ||
                   kind == TMX_W_SH_UP || kind == TMX_W_SH_GATE;
   const int which = (kind == TMX_W_UP || kind == TMX_W_EXP_UP || kind == TMX_W_SH_UP) ? 1 : 0;
-  if (e == hipSuccess && C.dtype == TMX_MXFP8) {
-    uint8_t* gu = static_cast<uint8_t*>(storage(c, layer, sub, TMX_W_GATE).ptr);
-    uint8_t* rec = gu + (size_t)2 * kind_elems(C, sub, TMX_W_GATE);
-    uint8_t* dst = gu;
-    if (kind == TMX_W_DOWN) dst = static_cast<uint8_t*>(bank(c, layer, sub, TMX_W_DOWN).ptr);
-    e = launch_pack_mx(static_cast<const uint16_t*>(stage), dst, rec, (int)G, K, N, kind == TMX_W_DOWN ? 1 : 0, which,
-                       st);
+  if (e == hipSuccess && C.dtype == TMX_MXFP8 && mx_gate_kind(kind) >= 0) {
+    const int gk = mx_gate_kind(kind);
+    uint8_t* gub = static_cast<uint8_t*>(bank(c, layer, sub, gk).ptr);
+    uint8_t* rec = gub + (size_t)2 * kind_elems(C, sub, gk);
+    const bool down = !gu;
+    uint8_t* dst = down ? static_cast<uint8_t*>(bank(c, layer, sub, kind).ptr) : gub;
+    e = launch_pack_mx(static_cast<const uint16_t*>(stage), dst, rec, (int)G, K, N, down ? 1 : 0, which,
+                       mx_rec(C, sub, gk), st);
   } else if (e == hipSuccess && is_rmx(C))
     e = launch_pack(static_cast<const uint16_t*>(stage), static_cast<uint16_t*>(b.ptr), (int)G, K, N,
                     kind == TMX_W_ROUTER ? 1 : 2, 0, kind == TMX_W_ROUTER ? FRAG_16x16x32 : FRAG_32x32x16, st);
@@ -819,7 +866,7 @@ tmx_status tmx_sublayer_forward_noalloc(tmx_ctx* c, int layer, int sub, const vo
   if (s != TMX_OK) return s;
   const tmx_config& C = c->cfg;
   MoeWs ws;
-  if (is_moe(C) && !is_rmx(C) && C.dtype == TMX_BF16) {
+  if (is_moe(C) && !is_rmx(C) && (C.dtype == TMX_BF16 || C.dtype == TMX_MXFP8)) {
     const size_t need = carve_moe_ws(C, B, nullptr, nullptr);
     if (need > TMX_SCRATCH_BYTES) {
       int bmax = 0;
@@ -929,8 +976,8 @@ tmx_status tmx_moe_buckets(tmx_ctx* c, int layer, int sub, const void* x, int B,
                            int32_t* rows, void* stream) {
   if (!c) return fail(nullptr, TMX_ERR_INVALID_ARG, "ctx is NULL");
   const tmx_config& C = c->cfg;
-  if (!is_moe(C) || is_rmx(C) || C.dtype != TMX_BF16)
-    return fail(c, TMX_ERR_UNSUPPORTED, "tmx_moe_buckets needs a bf16 TokenMixer-Large MoE context");
+  if (!is_moe(C) || is_rmx(C) || (C.dtype != TMX_BF16 && C.dtype != TMX_MXFP8))
+    return fail(c, TMX_ERR_UNSUPPORTED, "tmx_moe_buckets needs a bf16 or MXFP8 TokenMixer-Large MoE context");
   tmx_status s;
   if (layer < 0 || layer >= C.L) return fail(c, TMX_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, C.L);
   if (sub != TMX_MIX && sub != TMX_REVERT) return fail(c, TMX_ERR_INVALID_ARG, "sublayer must be 0 or 1");

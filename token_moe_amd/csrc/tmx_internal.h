@@ -46,7 +46,8 @@ struct MlpArgs {
   int rtiles;              // DENSE / SHARED: row tiles per position unit
   int pair;                // DENSE / SHARED: 1 = a tile holds BM/2 rows of each of two
                            // adjacent positions (2q in rows [0, BM/2), 2q+1 above)
-  const uint32_t* wsc;     // MXFP8 dense: weight scale records (see launch_pack_mx)
+  const uint32_t* wsc;     // MXFP8: weight scale records (see launch_pack_mx)
+  int wrec;                // MXFP8: dwords per lane record (mx_rec_dwords)
   int ileave;              // DENSE / SHARED, unpaired: positions 2q and 2q+1 alternate
                            // in the tile order (row tile t of 2q, of 2q+1, t+1 of 2q, ...)
   int stagger;             // clocks that the late half of the workgroups waits before
@@ -103,23 +104,32 @@ hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
 // frag = (g*KB + kb)*NB + nb; layout 2: n-major, frag = (g*NB + nb)*KB + kb.
 hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int G, int K, int N, int layout,
                        int which, int frag, hipStream_t s);
-// MXFP8 weights of the dense W = 256 kernel (two 4-wave workgroups per CU):
+// MXFP8 weights of the MXFP8 MLP kernels (sub-layer width W in {256, 512, 768}):
 // G row-major [K, N] bf16 matrices -> E4M3 codes in 32 x 64 fragments of the
 // v_mfma_scale_f32_32x32x64_f8f6f4 A operand (two 1 KiB halves: lane l holds
 // row l % 32, bytes 0-15 of K-block 0 and 16-31 of K-block 1 of the 64-K step,
 // k = 16 * (l / 32) + j within the block) plus E8M0 scales (one per column and
-// 32-element K-block) in per-lane records `rec` [G][4 waves][64 lanes][24]
-// dwords: dword 3c + which (gate 0 / up 1) of chunk c holds the gate/up scales
-// (byte s: K-step s, K-block 2s + l / 32 of column 32 * (4c + wave) + l % 32),
-// dword 3c + 2 the down scales (byte 2j + t: column 32 * (2 wave + j) + l % 32,
-// hidden block 4c + 2t + l / 32). down = 0: gate/up bank, K = W, N = hidden,
-// fragment ((g NB + nb) KS + s) 2 + which; down = 1: K = hidden, N = W,
-// fragment (g KB + kb) NB + nb.
+// 32-element K-block) in per-lane records `rec` [G][4 waves][64 lanes][R]
+// dwords, R = mx_rec_dwords(W, hidden). With DW = W / 256, hidden chunk c
+// (128 units) owns dwords [3 DW c, 3 DW (c + 1)): gate (m = 0), up (m = 1)
+// and down (m = 2) take DW dwords each, byte q of matrix m at dword
+// 3 DW c + DW m + q / 4, byte q % 4. Gate/up: q = K-step s of the 64-K steps
+// along W, the scale of K-block 2s + l / 32 of column 32 (4c + wave) + l % 32.
+// Down: q = 2j + t, the scale of column 32 (NBO wave + j) + l % 32 (NBO = W /
+// 128 column blocks per wave) and hidden block 4c + 2t + l / 32. down = 0:
+// gate/up bank, K = W, N = hidden, fragment ((g NB + nb) KS + s) 2 + which;
+// down = 1: K = hidden, N = W, fragment (g KB + kb) NB + nb.
 hipError_t launch_pack_mx(const uint16_t* src, uint8_t* dst, uint8_t* rec, int G, int K, int N, int down, int which,
-                          hipStream_t s);
-// dense MXFP8 sub-layer at W = 256 (grid as launch_mlp)
-hipError_t launch_mlp_mx(const MlpArgs& a, int tiles, int workers, hipStream_t s);
-constexpr int MX_REC_DWORDS = 24;   // per lane: 3 scale dwords x up to 8 hidden chunks
+                          int rec_dwords, hipStream_t s);
+// MXFP8 sub-layer kernels (grid as launch_mlp): DENSE at W = 256 (two
+// workgroups per CU) or 512; ROUTED and SHARED at W = 512 and 768
+bool mlp_mx_supported(int mode, int W);
+hipError_t launch_mlp_mx(int mode, int W, const MlpArgs& a, int tiles, int workers, hipStream_t s);
+// hidden <= this many chunks of MLP_HC (the scale records of a tile sit in LDS)
+constexpr int mx_max_chunks(int W) { return W == 768 ? 6 : 8; }
+// dwords of one lane's scale record (a multiple of 4: the kernel moves it in
+// 16-byte pieces)
+constexpr int mx_rec_dwords(int W, int hidden) { return ((hidden / MLP_HC) * 3 * (W / 256) + 3) & ~3; }
 // Mix / Revert through RowMap in one of its address forms (PermForm; see
 // permute_kernel); forms other than PERM_ELEM need D/H % 8 == 0 and
 // T*D/H % 32 == 0

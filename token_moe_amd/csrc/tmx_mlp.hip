@@ -119,19 +119,26 @@ template <int OA, int OB>
 __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, uint32_t sa, uint32_t sb, const f32x16& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OA, (int)sa, OB, (int)sb);
 }
-// the scale-byte selectors the kernel uses, from loop indices that are
-// constants after unrolling
+// scale-byte selectors from loop indices that are constants after unrolling
 __device__ __forceinline__ f32x16 mfma8s(int oa, int ob, const i32x8& a, const i32x8& b, uint32_t sa, uint32_t sb,
                                          const f32x16& c) {
   switch (oa * 4 + ob) {
     case 0: return mfma8<0, 0>(a, b, sa, sb, c);
-    case 5: return mfma8<1, 1>(a, b, sa, sb, c);
-    case 10: return mfma8<2, 2>(a, b, sa, sb, c);
-    case 15: return mfma8<3, 3>(a, b, sa, sb, c);
-    case 8: return mfma8<2, 0>(a, b, sa, sb, c);
-    case 13: return mfma8<3, 1>(a, b, sa, sb, c);
+    case 1: return mfma8<0, 1>(a, b, sa, sb, c);
+    case 2: return mfma8<0, 2>(a, b, sa, sb, c);
+    case 3: return mfma8<0, 3>(a, b, sa, sb, c);
     case 4: return mfma8<1, 0>(a, b, sa, sb, c);
-    default: return mfma8<0, 1>(a, b, sa, sb, c);
+    case 5: return mfma8<1, 1>(a, b, sa, sb, c);
+    case 6: return mfma8<1, 2>(a, b, sa, sb, c);
+    case 7: return mfma8<1, 3>(a, b, sa, sb, c);
+    case 8: return mfma8<2, 0>(a, b, sa, sb, c);
+    case 9: return mfma8<2, 1>(a, b, sa, sb, c);
+    case 10: return mfma8<2, 2>(a, b, sa, sb, c);
+    case 11: return mfma8<2, 3>(a, b, sa, sb, c);
+    case 12: return mfma8<3, 0>(a, b, sa, sb, c);
+    case 13: return mfma8<3, 1>(a, b, sa, sb, c);
+    case 14: return mfma8<3, 2>(a, b, sa, sb, c);
+    default: return mfma8<3, 3>(a, b, sa, sb, c);
   }
 }
 
@@ -174,13 +181,17 @@ __device__ __forceinline__ float silu_fast(float z) {
 //              token: those reads touch a cache line per run)
 enum { RV_PLAIN = 0, RV_EXTRA = 1, RV_MIX = 2 };
 
-// F8: the dense W = 256 kernel (two 4-wave workgroups per CU) with MXFP8 GEMM
-// operands: weights packed at load (launch_pack_mx), x_hat and U quantised
-// here per row and 32-element block along each GEMM's contraction axis.
+// F8: the 4-wave kernels with MXFP8 GEMM operands -- dense W = 256 (two
+// workgroups per CU), every mode at W = 512, the MoE modes at W = 768 (one)
+// -- weights packed at load
+// (launch_pack_mx), x_hat and U quantised here per row and 32-element block
+// along each GEMM's contraction axis.
 template <int W, int MODE, int NW, int OCC, int RV, bool F8>
 __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   constexpr bool RESX = RV == RV_MIX, EXTRA = RV == RV_EXTRA;
-  static_assert(!F8 || (W == 256 && MODE == MLP_DENSE && NW == 4 && OCC == 2), "MXFP8 kernel shape");
+  static_assert(!F8 || (NW == 4 && ((W == 256 && MODE == MLP_DENSE && OCC == 2) || (W == 512 && OCC == 1) ||
+                                    (W == 768 && MODE != MLP_DENSE && OCC == 1))),
+                "MXFP8 kernel shape");
   static_assert(!RESX || MODE == MLP_DENSE, "input rows double as the residual only in dense sub-layers");
   static_assert(!EXTRA || MODE != MLP_ROUTED, "routed tiles have no residual");
   using S = MlpShape<W, NW, OCC>;
@@ -211,16 +222,20 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   uint16_t* const us = reinterpret_cast<uint16_t*>(smem + XBYTES);
   float* const stage = reinterpret_cast<float*>(smem);
   // F8 layout of the same bytes during the main loop: x_hat codes [BM][XSB],
-  // two U code buffers [BM][USB], x_hat scale words [BM][2] (word h, byte s:
-  // 32-column block 2s + h), two U scale-word buffers [BM][2] (byte t: hidden
-  // block 2t + h of the chunk), the tile's weight scale records [4][24][64]
+  // two U code buffers [BM][USB], x_hat scale words [BM][2 DWX] (word 2 (s /
+  // 4) + h, byte s % 4: 32-column block 2s + h, s = 64-column K-step), two U
+  // scale-word buffers [BM][2] (word h, byte t: hidden block 2t + h of the
+  // chunk), the tile's weight scale records [4 waves][RECX / 4][64][4 dwords]
   constexpr int XSB = W + 16, USB = HC + 16;
+  constexpr int DWX = W / 256;                   // scale dwords per matrix, chunk and lane
+  constexpr int XSCB = W / 32;                   // x_hat scale bytes per row
+  constexpr int RECX = (3 * DWX * mx_max_chunks(W) + 3) & ~3;  // record dwords the LDS holds per lane
   uint8_t* const xs8 = smem;
   uint8_t* const us8 = smem + BM * XSB;
   uint8_t* const xsc8 = us8 + 2 * BM * USB;
-  uint8_t* const usc8 = xsc8 + BM * 8;
+  uint8_t* const usc8 = xsc8 + BM * XSCB;
   uint32_t* const wsc8 = reinterpret_cast<uint32_t*>(usc8 + 2 * BM * 8);
-  static_assert(!F8 || BM * XSB + 2 * BM * USB + 3 * BM * 8 + 4 * MX_REC_DWORDS * 64 * 4 <= SMEM, "F8 LDS");
+  static_assert(!F8 || BM * XSB + 2 * BM * USB + BM * XSCB + 2 * BM * 8 + 4 * RECX * 64 * 4 <= SMEM, "F8 LDS");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -443,12 +458,15 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   // GEMM1 step f / 2 (gate, up), then GEMM2 step (f - F1) / NBO.
   constexpr int NFR = DEPTH * NBR;
   // F8: the ring holds NFR8 whole 32-byte fragments (two 1 KiB halves each);
-  // a GEMM1 step (64 K) takes gate and up, a GEMM2 step NBO fragments
-  constexpr int KS8 = W / 64, TS8 = HC / 64, NFR8 = 4;
+  // a GEMM1 step (64 K) takes gate and up, a GEMM2 step NBO fragments, all
+  // of which must be in the ring at once
+  constexpr int KS8 = W / 64, TS8 = HC / 64, NFR8 = NBO > 4 ? NBO : 4;
   constexpr int F1 = F8 ? 2 * KS8 : 2 * S1, F2 = F8 ? NBO * TS8 : NBO * S2, FS = F1 + F2;
   constexpr int NFRX = F8 ? NFR8 : NFR;
   static_assert(NW == 8 || (F1 % NFRX == 0 && F2 % NFRX == 0),
                 "every GEMM phase must start on a ring boundary");
+  static_assert(!F8 || (NFR8 <= F1 && NFR8 <= F2), "the look-ahead stays within the next GEMM phase");
+  static_assert(!F8 || (NFR8 >= NBO && NFR8 >= 2), "a GEMM step's fragments fit in the ring together");
   i32x8 ring8[F8 ? NFR8 : 1];
   auto fslot = [&](int k) __attribute__((always_inline)) -> uint4& {
     return ring[(k % NFR) / NBR][(k % NFR) % NBR];
@@ -546,29 +564,36 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   // TokenMixer-Large section 2.3.3)
   auto store_x = [&](int tix, uint4* v, const float* lgain) {
     if constexpr (F8) {
-      // RMSNorm in fp32, then MXFP8 per 32-column block: the block's 4 units
-      // sit in 4 consecutive lanes of one row (32 units per row)
-      static_assert(!F8 || (LANE_COL && U8 == 32), "F8 row layout");
+      // DENSE: RMSNorm in fp32 (the row's U8 units sit in U8 consecutive
+      // lanes); ROUTED / SHARED rows arrive normalised. Then MXFP8 per
+      // 32-column block: the block's 4 units sit in 4 consecutive lanes
+      // (units are numbered row by row, and NT and U8 are multiples of 4).
+      static_assert(!F8 || (MODE == MLP_DENSE ? (LANE_COL && (U8 == 32 || U8 == 64)) : (U8 % 4 == 0 && NT % 4 == 0)),
+                    "F8 row layout");
 #pragma unroll
       for (int i = 0; i < NPRO; ++i) {
         int r, c8;
         unit_rc(tix, i, r, c8);
         const uint16_t* h = reinterpret_cast<const uint16_t*>(&v[i]);
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float f = bf2f(h[e]);
-          acc += f * f;
-        }
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-        const float rinv = 1.0f / sqrtf(acc / (float)W + a.eps);
         float n[8], am = 0.f;
+        if constexpr (MODE == MLP_DENSE) {
+          float acc = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          n[e] = bf2f(h[e]) * rinv * lgain[e];
-          am = fmaxf(am, fabsf(n[e]));
+          for (int e = 0; e < 8; ++e) {
+            const float f = bf2f(h[e]);
+            acc += f * f;
+          }
+#pragma unroll
+          for (int o = U8 / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+          const float rinv = 1.0f / sqrtf(acc / (float)W + a.eps);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) n[e] = bf2f(h[e]) * rinv * lgain[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) n[e] = bf2f(h[e]);
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(n[e]));
         am = fmaxf(am, __shfl_xor(am, 1, 64));
         am = fmaxf(am, __shfl_xor(am, 2, 64));
         const int k = mx_exp(am);
@@ -577,8 +602,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
         q.x = e4m3x4(n[0], n[1], n[2], n[3], sc);
         q.y = e4m3x4(n[4], n[5], n[6], n[7], sc);
         *reinterpret_cast<uint2*>(&xs8[r * XSB + c8 * 8]) = q;
-        const int blk = c8 >> 2;
-        if ((c8 & 3) == 0) xsc8[r * 8 + (blk & 1) * 4 + (blk >> 1)] = (uint8_t)(k + 127);
+        const int blk = c8 >> 2, st = blk >> 1;
+        if ((c8 & 3) == 0) xsc8[r * XSCB + ((st >> 2) * 2 + (blk & 1)) * 4 + (st & 3)] = (uint8_t)(k + 127);
       }
       __syncthreads();
       return;
@@ -670,17 +695,17 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
       __syncthreads();
     }
   };
-  // F8: the tile's weight scale records (24 dwords per lane and wave) go
-  // from global memory straight into LDS (no registers), 16 bytes per lane
-  // and load: dword d of lane l lands at wsc8 + ((wave 6 + d / 4) 64 + l) 4
-  // + d % 4. They share bytes with the epilogue's staged tile, so they are
-  // issued once the staging has been read; the main loop waits for them.
+  // F8: the tile's weight scale records (a.wrec dwords per lane and wave)
+  // go from global memory straight into LDS (no registers), 16 bytes per
+  // lane and load: dword d of lane l lands at wsc8 + ((wave RECX / 4 + d / 4)
+  // 64 + l) 4 + d % 4. They share bytes with the epilogue's staged tile, so
+  // they are issued once the staging has been read; the main loop waits for
+  // them.
   auto dma_wrec = [&](const Tile& T) __attribute__((always_inline)) {
     if constexpr (F8) {
-      const uint4* p = reinterpret_cast<const uint4*>(a.wsc + (((size_t)T.group * 4 + wave) * 64 + lane) * MX_REC_DWORDS);
-#pragma unroll
-      for (int m = 0; m < MX_REC_DWORDS / 4; ++m)
-        __builtin_amdgcn_global_load_lds(p + m, wsc8 + (wave * (MX_REC_DWORDS / 4) + m) * 64 * 4, 16, 0, 0);
+      const uint4* p = reinterpret_cast<const uint4*>(a.wsc + (((size_t)T.group * 4 + wave) * 64 + lane) * a.wrec);
+      for (int m = 0; m < a.wrec / 4; ++m)
+        __builtin_amdgcn_global_load_lds(p + m, wsc8 + (wave * (RECX / 4) + m) * 64 * 4, 16, 0, 0);
     }
   };
 
@@ -921,18 +946,29 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
       // scale words (byte s), GEMM2 step t 64 hidden units of U codes (byte
       // t); the weight scales come from the tile's records in LDS.
       f32x16 sg[RBW], su[RBW];
-      uint32_t xsw[RBW];
+      uint32_t xsw[RBW][DWX];
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb)
-        xsw[rb] = *reinterpret_cast<const uint32_t*>(&xsc8[(rb * 32 + l32) * 8 + h32 * 4]);
+#pragma unroll
+        for (int q = 0; q < DWX; ++q)
+          xsw[rb][q] = *reinterpret_cast<const uint32_t*>(&xsc8[(rb * 32 + l32) * XSCB + (2 * q + h32) * 4]);
       const int rot = cw.rot;
       // the scale records' LDS writes (global_load_lds, counted like loads)
       __builtin_amdgcn_s_waitcnt(0);
-      auto wscale = [&](int cc, int d) __attribute__((always_inline)) -> uint32_t {
+      // scale dwords of matrix m (0 gate, 1 up, 2 down) of chunk cc
+      struct Sc {
+        uint32_t w[DWX];
+      };
+      auto wscale = [&](int cc, int m) __attribute__((always_inline)) -> Sc {
         cc += rot;
         if (cc >= NC) cc -= NC;
-        const int dw = cc * 3 + d;
-        return wsc8[((wave * (MX_REC_DWORDS / 4) + (dw >> 2)) * 64 + lane) * 4 + (dw & 3)];
+        Sc r;
+#pragma unroll
+        for (int q = 0; q < DWX; ++q) {
+          const int dw = (cc * 3 + m) * DWX + q;
+          r.w[q] = wsc8[((wave * (RECX / 4) + (dw >> 2)) * 64 + lane) * 4 + (dw & 3)];
+        }
+        return r;
       };
       auto read_xb = [&](i32x8* dst, int st) __attribute__((always_inline)) {
 #pragma unroll
@@ -978,7 +1014,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
         u_half8(ubuf, rb, 1, am);
         __builtin_amdgcn_sched_barrier(0);
       };
-      auto gemm1_8 = [&](auto refill_at, uint32_t gsc, uint32_t usc) __attribute__((always_inline)) {
+      auto gemm1_8 = [&](auto refill_at, const Sc& gsc, const Sc& usc) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < RBW; ++i) {
           sg[i] = f32x16{};
@@ -991,8 +1027,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int rb = 0; rb < RBW; ++rb) {
-            sg[rb] = mfma8s(st, st, ring8[(2 * st) % NFR8], xb[st & 1][rb], gsc, xsw[rb], sg[rb]);
-            su[rb] = mfma8s(st, st, ring8[(2 * st + 1) % NFR8], xb[st & 1][rb], usc, xsw[rb], su[rb]);
+            sg[rb] = mfma8s(st & 3, st & 3, ring8[(2 * st) % NFR8], xb[st & 1][rb], gsc.w[st >> 2],
+                            xsw[rb][st >> 2], sg[rb]);
+            su[rb] = mfma8s(st & 3, st & 3, ring8[(2 * st + 1) % NFR8], xb[st & 1][rb], usc.w[st >> 2],
+                            xsw[rb][st >> 2], su[rb]);
           }
           refill_at(ring8[(2 * st) % NFR8], 2 * st + NFR8);
           refill_at(ring8[(2 * st + 1) % NFR8], 2 * st + 1 + NFR8);
@@ -1001,7 +1039,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
       };
       // GEMM2 of a chunk from U buffer rbuf; with_u: U(next chunk) row block
       // t goes to buffer wbuf after step t's MFMAs
-      auto gemm2_8 = [&](int rbuf, int wbuf, auto with_u_tag, auto refill_at, auto pos0_tag, uint32_t dsc)
+      auto gemm2_8 = [&](int rbuf, int wbuf, auto with_u_tag, auto refill_at, auto pos0_tag, const Sc& dsc)
           __attribute__((always_inline)) {
         constexpr bool with_u = decltype(with_u_tag)::value;
         constexpr int pos0 = decltype(pos0_tag)::value;
@@ -1021,8 +1059,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
           for (int rb = 0; rb < RBW; ++rb) {
 #pragma unroll
             for (int j = 0; j < NBO; ++j)
-              oacc[rb][j] = mfma8s(j * 2 + t, t, ring8[(pos0 + t * NBO + j) % NFR8], ub[t & 1][rb], dsc, usw[rb],
-                                   oacc[rb][j]);
+              oacc[rb][j] = mfma8s((j * 2 + t) & 3, t, ring8[(pos0 + t * NBO + j) % NFR8], ub[t & 1][rb],
+                                   dsc.w[(j * 2 + t) >> 2], usw[rb], oacc[rb][j]);
             if constexpr (with_u) {
               u_half8(wbuf, t, rb, am);
               __builtin_amdgcn_sched_barrier(0);
@@ -1069,6 +1107,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
           for (int i = 1; i + 1 < NC; ++i) iteration(i, std::integral_constant<bool, false>{});
           iteration(NC - 1, std::integral_constant<bool, true>{});
         }
+        if constexpr (MODE == MLP_ROUTED) routed_setup();
         gemm2_8((NC - 1) & 1, 0, std::false_type{},
                 [&](i32x8& dst, int k2) __attribute__((always_inline)) {
                   if (k2 < F2) issue_frag8(dst, cw, NC - 1, F1 + k2);
@@ -1472,18 +1511,44 @@ bool mlp_pairs_positions(int mode, int W) { return mode != MLP_ROUTED && mlp_wav
 
 int mlp_workgroups_per_cu(int mode, int W) { return mlp_occupancy(mode, W); }
 
-hipError_t launch_mlp_mx(const MlpArgs& a, int tiles, int workers, hipStream_t s) {
-  if (tiles <= 0) return hipSuccess;
-  constexpr int NW = mlp_waves(MLP_DENSE, 256), OCC = mlp_occupancy(MLP_DENSE, 256);
-  static_assert(NW == 4 && OCC == 2, "the MXFP8 kernel is the two-workgroup dense W = 256 kernel");
-  workers = (workers & ~7) * OCC;
-  const int grid = (workers <= 0 || tiles <= workers) ? tiles : workers;
+bool mlp_mx_supported(int mode, int W) {
+  return W == 512 || (W == 256 && mode == MLP_DENSE) || (W == 768 && mode != MLP_DENSE);
+}
+
+namespace {
+template <int W, int MODE>
+void launch_mx_wm(const MlpArgs& a, int grid, hipStream_t s) {
+  constexpr int NW = mlp_waves(MODE, W), OCC = mlp_occupancy(MODE, W);
+  static_assert(NW == 4, "the MXFP8 kernels are the 4-wave kernels");
   // (the Mix sub-layer reads its residual again: with the raw rows kept in
-  // registers as in the bf16 kernel, the MXFP8 main loop would spill)
-  if (a.extra)
-    hipLaunchKernelGGL((mlp_kernel<256, MLP_DENSE, NW, OCC, RV_EXTRA, true>), dim3(grid), dim3(64 * NW), 0, s, a);
+  // registers as in the bf16 kernel, the W = 256 MXFP8 main loop would spill)
+  if (MODE != MLP_ROUTED && a.extra)
+    hipLaunchKernelGGL((mlp_kernel<W, MODE, NW, OCC, MODE != MLP_ROUTED ? RV_EXTRA : RV_PLAIN, true>), dim3(grid),
+                       dim3(64 * NW), 0, s, a);
   else
-    hipLaunchKernelGGL((mlp_kernel<256, MLP_DENSE, NW, OCC, RV_PLAIN, true>), dim3(grid), dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((mlp_kernel<W, MODE, NW, OCC, RV_PLAIN, true>), dim3(grid), dim3(64 * NW), 0, s, a);
+}
+}  // namespace
+
+hipError_t launch_mlp_mx(int mode, int W, const MlpArgs& a, int tiles, int workers, hipStream_t s) {
+  if (tiles <= 0) return hipSuccess;
+  if (!mlp_mx_supported(mode, W) || a.hidden % MLP_HC != 0 || a.hidden > mx_max_chunks(W) * MLP_HC ||
+      a.wrec < mx_rec_dwords(W, a.hidden) || a.wrec % 4 != 0)
+    return hipErrorInvalidValue;
+  workers = (workers & ~7) * mlp_workgroups_per_cu(mode, W);
+  const int grid = (workers <= 0 || tiles <= workers) ? tiles : workers;
+  if (W == 256) {
+    launch_mx_wm<256, MLP_DENSE>(a, grid, s);
+  } else if (W == 768) {
+    if (mode == MLP_ROUTED) launch_mx_wm<768, MLP_ROUTED>(a, grid, s);
+    else launch_mx_wm<768, MLP_SHARED>(a, grid, s);
+  } else {
+    switch (mode) {
+      case MLP_DENSE: launch_mx_wm<512, MLP_DENSE>(a, grid, s); break;
+      case MLP_ROUTED: launch_mx_wm<512, MLP_ROUTED>(a, grid, s); break;
+      default: launch_mx_wm<512, MLP_SHARED>(a, grid, s); break;
+    }
+  }
   return hipGetLastError();
 }
 

@@ -384,7 +384,7 @@ __global__ void pack_kernel(const uint16_t* __restrict__ src, uint16_t* __restri
 // the hardware's round-to-nearest-even conversion of x * 2^-k after clamping
 // to +-448 (the conversion itself does not saturate).
 __global__ void pack_mx_kernel(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst,
-                               uint8_t* __restrict__ rec, int G, int K, int N, int down, int which) {
+                               uint8_t* __restrict__ rec, int G, int K, int N, int down, int which, int R) {
   const int KBLK = K / 32;
   const int64_t total = (int64_t)G * N * KBLK;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
@@ -428,18 +428,26 @@ __global__ void pack_mx_kernel(const uint16_t* __restrict__ src, uint8_t* __rest
     }
     // scale byte in the record of the lane that supplies it to the MFMA
     // (row h0, K-block parity b & 1 -> lane h0 + 32 (b & 1))
+    // (chunk c of 128 hidden units, matrix m, byte q of the matrix's DW
+    // dwords in that chunk; DW = W / 256 with W = K for gate/up, N for down)
     const int lane_s = h0 + 32 * (b & 1);
-    int wave, dword, byte;
+    int wave, c, m, q, DW;
     if (!down) {
+      DW = K / 256;
       wave = nb % 4;
-      dword = (nb / 4) * 3 + which;
-      byte = b >> 1;
+      c = nb / 4;
+      m = which;
+      q = b >> 1;
     } else {
-      wave = nb / 2;
-      dword = (b / 4) * 3 + 2;
-      byte = (nb % 2) * 2 + ((b % 4) >> 1);
+      DW = N / 256;
+      const int nbo = N / 128;   // column blocks per wave
+      wave = nb / nbo;
+      c = b / 4;
+      m = 2;
+      q = (nb % nbo) * 2 + ((b % 4) >> 1);
     }
-    rec[((((int64_t)g * 4 + wave) * 64 + lane_s) * MX_REC_DWORDS + dword) * 4 + byte] = (uint8_t)(k + 127);
+    const int dword = (c * 3 + m) * DW + (q >> 2);
+    rec[((((int64_t)g * 4 + wave) * 64 + lane_s) * R + dword) * 4 + (q & 3)] = (uint8_t)(k + 127);
   }
 }
 
@@ -565,10 +573,15 @@ hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int G, int K, int N, 
 }
 
 hipError_t launch_pack_mx(const uint16_t* src, uint8_t* dst, uint8_t* rec, int G, int K, int N, int down, int which,
-                          hipStream_t s) {
+                          int rec_dwords, hipStream_t s) {
+  const int W = down ? N : K, hidden = down ? K : N;
+  if ((W != 256 && W != 512 && W != 768) || hidden % MLP_HC != 0 || hidden > mx_max_chunks(W) * MLP_HC ||
+      rec_dwords < mx_rec_dwords(W, hidden))
+    return hipErrorInvalidValue;
   const int64_t total = (int64_t)G * N * (K / 32);
   const int64_t blocks = std::min<int64_t>((total + 255) / 256, 65536);
-  hipLaunchKernelGGL(pack_mx_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, rec, G, K, N, down, which);
+  hipLaunchKernelGGL(pack_mx_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, rec, G, K, N, down, which,
+                     rec_dwords);
   return hipGetLastError();
 }
 
