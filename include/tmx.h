@@ -71,12 +71,15 @@ typedef enum tmx_status {
 } tmx_status;
 
 /* TMX_MXFP8: bf16 activations and weights at the boundary, with the GEMM
- * operands of the dense per-token SwiGLU quantised to MXFP8 inside the
- * library ("FP8 E4M3 post-training quantisation", TokenMixer-Large summary
- * section 2.5.2; read as E4M3 elements with one power-of-two scale per 32
- * values along each GEMM's contraction axis): weights when they are loaded,
- * the normalised rows and the SwiGLU hidden in the kernel. Dense contexts
- * only. */
+ * operands of the per-token SwiGLUs quantised to MXFP8 inside the library
+ * ("FP8 E4M3 post-training quantisation", TokenMixer-Large summary section
+ * 2.5.2; read as E4M3 elements with one power-of-two scale per 32 values
+ * along each GEMM's contraction axis): weights when they are loaded, the
+ * normalised rows and the SwiGLU hidden in the kernel. Dense sub-layers of
+ * width 256 or 512; MoE sub-layers of width 512 or 768, where the routed
+ * and the shared experts run on MXFP8 operands and the router stays bf16
+ * (section 2.4, Eq. 19-21). Hidden sizes a multiple of 128, at most 1024
+ * (768 at width 768); other shapes give TMX_ERR_UNSUPPORTED. */
 typedef enum tmx_dtype { TMX_F32 = 0, TMX_BF16 = 1, TMX_MXFP8 = 2 } tmx_dtype;
 
 typedef enum tmx_sublayer { TMX_MIX = 0, TMX_REVERT = 1 } tmx_sublayer;

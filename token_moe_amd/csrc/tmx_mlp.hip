@@ -206,12 +206,30 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   // same bytes hold the fp32 output tile (all rows at once when it fits in
   // 160 KB, else one row half at a time). Stage row stride W + 4 floats: 16
   // consecutive rows land on distinct 16-byte bank groups.
+  // F8 layout of the same bytes during the main loop: x_hat codes [BM][XSB],
+  // two U code buffers [BM][USB], x_hat scale words [BM][2 DWX] (word 2 (s /
+  // 4) + h, byte s % 4: 32-column block 2s + h, s = 64-column K-step), two U
+  // scale-word buffers [BM][2] (word h, byte t: hidden block 2t + h of the
+  // chunk), and at W = 256 the tile's weight scale records [4 waves][RECX /
+  // 4][64][4 dwords]. From W = 512 the weight scales go to registers
+  // instead, straight from global memory one chunk ahead of their use
+  // (REC_REG): copying records into LDS takes the LDS DMA, after which the
+  // compiler makes every LDS read wait for all loads in flight, the weight
+  // stream included. The F8 kernels never use the bf16 layout.
   constexpr int XBYTES = BM * XS * 2, UBYTES = 2 * BM * US * 2;
   constexpr int SS = W + 4;
   constexpr int ROWTAB = 6 * BM * 4;
+  constexpr bool REC_REG = F8 && W >= 512;
   constexpr int NPART = (BM * SS * 4 + ROWTAB <= 160 * 1024) ? 1 : 2;
   constexpr int SBYTES = (BM / NPART) * SS * 4;
-  constexpr int SMEM = (XBYTES + UBYTES > SBYTES) ? XBYTES + UBYTES : SBYTES;
+  constexpr int XSB = W + 16, USB = HC + 16;
+  constexpr int DWX = W / 256;                   // scale dwords per matrix, chunk and lane
+  constexpr int XSCB = W / 32;                   // x_hat scale bytes per row
+  constexpr int RECX = (3 * DWX * mx_max_chunks(W) + 3) & ~3;  // record dwords the LDS holds per lane
+  constexpr int F8CODES = BM * XSB + 2 * BM * USB + BM * XSCB + 2 * BM * 8;
+  constexpr int F8BYTES = F8CODES + (REC_REG ? 0 : 4 * RECX * 64 * 4);
+  constexpr int SMEM0 = (XBYTES + UBYTES > SBYTES) ? XBYTES + UBYTES : SBYTES;
+  constexpr int SMEM = F8 ? (F8BYTES > SBYTES ? F8BYTES : SBYTES) : SMEM0;
   static_assert(SMEM + ROWTAB <= 160 * 1024, "LDS budget");
   static_assert(NW == 8 || NPART == 1 || RBW == NPART, "4 waves stage one row block per part");
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
@@ -221,21 +239,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   uint16_t* const xs = reinterpret_cast<uint16_t*>(smem);
   uint16_t* const us = reinterpret_cast<uint16_t*>(smem + XBYTES);
   float* const stage = reinterpret_cast<float*>(smem);
-  // F8 layout of the same bytes during the main loop: x_hat codes [BM][XSB],
-  // two U code buffers [BM][USB], x_hat scale words [BM][2 DWX] (word 2 (s /
-  // 4) + h, byte s % 4: 32-column block 2s + h, s = 64-column K-step), two U
-  // scale-word buffers [BM][2] (word h, byte t: hidden block 2t + h of the
-  // chunk), the tile's weight scale records [4 waves][RECX / 4][64][4 dwords]
-  constexpr int XSB = W + 16, USB = HC + 16;
-  constexpr int DWX = W / 256;                   // scale dwords per matrix, chunk and lane
-  constexpr int XSCB = W / 32;                   // x_hat scale bytes per row
-  constexpr int RECX = (3 * DWX * mx_max_chunks(W) + 3) & ~3;  // record dwords the LDS holds per lane
   uint8_t* const xs8 = smem;
   uint8_t* const us8 = smem + BM * XSB;
   uint8_t* const xsc8 = us8 + 2 * BM * USB;
   uint8_t* const usc8 = xsc8 + BM * XSCB;
-  uint32_t* const wsc8 = reinterpret_cast<uint32_t*>(usc8 + 2 * BM * 8);
-  static_assert(!F8 || BM * XSB + 2 * BM * USB + BM * XSCB + 2 * BM * 8 + 4 * RECX * 64 * 4 <= SMEM, "F8 LDS");
+  uint32_t* const wsc8 = reinterpret_cast<uint32_t*>(smem + F8CODES);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -695,18 +703,36 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
       __syncthreads();
     }
   };
-  // F8: the tile's weight scale records (a.wrec dwords per lane and wave)
-  // go from global memory straight into LDS (no registers), 16 bytes per
-  // lane and load: dword d of lane l lands at wsc8 + ((wave RECX / 4 + d / 4)
-  // 64 + l) 4 + d % 4. They share bytes with the epilogue's staged tile, so
-  // they are issued once the staging has been read; the main loop waits for
-  // them.
+  // F8 at W = 256: the tile's weight scale records (a.wrec dwords per lane
+  // and wave) go from global memory straight into LDS (no registers), 16
+  // bytes per lane and load: dword d of lane l lands at wsc8 + ((wave RECX /
+  // 4 + d / 4) 64 + l) 4 + d % 4, a region only this wave reads. They share
+  // bytes with the epilogue's staged tile, so they are issued once the
+  // staging has been read; the main loop waits for them.
   auto dma_wrec = [&](const Tile& T) __attribute__((always_inline)) {
-    if constexpr (F8) {
+    if constexpr (F8 && !REC_REG) {
       const uint4* p = reinterpret_cast<const uint4*>(a.wsc + (((size_t)T.group * 4 + wave) * 64 + lane) * a.wrec);
       for (int m = 0; m < a.wrec / 4; ++m)
         __builtin_amdgcn_global_load_lds(p + m, wsc8 + (wave * (RECX / 4) + m) * 64 * 4, 16, 0, 0);
     }
+  };
+
+  // F8 from W = 512: this lane's scale record of a tile's expert / position,
+  // and the DWX scale dwords of matrix m (0 gate, 1 up, 2 down) of hidden
+  // chunk cc in the tile's chunk order (rotation rot)
+  struct Sc {
+    uint32_t w[F8 ? DWX : 1];
+  };
+  auto rec_of = [&](const Tile& T) __attribute__((always_inline)) -> const uint32_t* {
+    return a.wsc + (((size_t)T.group * 4 + wave) * 64 + lane) * a.wrec;
+  };
+  auto gscale = [&](const uint32_t* rec, int rot, int cc, int m) __attribute__((always_inline)) -> Sc {
+    cc += rot;
+    if (cc >= NC) cc -= NC;
+    Sc r;
+#pragma unroll
+    for (int q = 0; q < (F8 ? DWX : 1); ++q) r.w[q] = rec[(cc * 3 + m) * DWX + q];
+    return r;
   };
 
   // residual rows of the tile, same unit order as load_x
@@ -775,6 +801,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   set_rows(cur, 0);
   cw = bind(cur);
   nw = has_nx ? bind(nx) : cw;
+  // REC_REG: the gate / up scales of the tile's first chunk, loaded with
+  // (or, for later tiles, ahead of) its first weight fragments
+  Sc g0{}, u0{};
   __syncthreads();                         // row table visible
   {
     // the first rows go out before the weight ring: a wave's loads retire
@@ -784,6 +813,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
     load_gain(g);
     load_x(tid, 0, cur, v);
     dma_wrec(cur);
+    if constexpr (REC_REG) {
+      g0 = gscale(rec_of(cur), cw.rot, 0, 0);
+      u0 = gscale(rec_of(cur), cw.rot, 0, 1);
+    }
     if constexpr (F8) {
 #pragma unroll
       for (int f = 0; f < NFR8; ++f) issue_frag8(ring8[f], cw, 0, f);
@@ -953,12 +986,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
         for (int q = 0; q < DWX; ++q)
           xsw[rb][q] = *reinterpret_cast<const uint32_t*>(&xsc8[(rb * 32 + l32) * XSCB + (2 * q + h32) * 4]);
       const int rot = cw.rot;
-      // the scale records' LDS writes (global_load_lds, counted like loads)
-      __builtin_amdgcn_s_waitcnt(0);
-      // scale dwords of matrix m (0 gate, 1 up, 2 down) of chunk cc
-      struct Sc {
-        uint32_t w[DWX];
-      };
+      // W = 256: the scale records' LDS writes (global_load_lds, counted
+      // like loads)
+      if constexpr (!REC_REG) __builtin_amdgcn_s_waitcnt(0);
+      const uint32_t* const rec = rec_of(cur);
+      // scale dwords of matrix m (0 gate, 1 up, 2 down) of chunk cc: from
+      // the LDS records (W = 256)
       auto wscale = [&](int cc, int m) __attribute__((always_inline)) -> Sc {
         cc += rot;
         if (cc >= NC) cc -= NC;
@@ -1071,8 +1104,25 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       };
+      // REC_REG: the scales of the next GEMM phases, loaded one phase ahead:
+      // gate / up of chunk i + 1 and down of chunk i go out as chunk i
+      // starts (ng, nu, nd), ahead of that chunk's weight refills
+      Sc ng{}, nu{}, nd{};
       auto chunk_loop8 = [&](auto more_tag) __attribute__((always_inline)) {
         constexpr bool MORE = decltype(more_tag)::value;
+        Sc cg, cu;
+        if constexpr (REC_REG) {
+          cg = g0;
+          cu = u0;
+          if constexpr (MORE) {
+            ng = gscale(rec, rot, 1, 0);
+            nu = gscale(rec, rot, 1, 1);
+          }
+          nd = gscale(rec, rot, 0, 2);
+        } else {
+          cg = wscale(0, 0);
+          cu = wscale(0, 1);
+        }
         gemm1_8([&](i32x8& dst, int k2) __attribute__((always_inline)) {
                   if (k2 < F1)
                     issue_frag8(dst, cw, 0, k2);
@@ -1081,7 +1131,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
                   else
                     issue_frag8(dst, cw, 0, k2);
                 },
-                wscale(0, 0), wscale(0, 1));
+                cg, cu);
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) u_group8(0, rb);
         __syncthreads();
@@ -1098,9 +1148,23 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
               issue_frag8(dst, cw, NC - 1, k2 - FS + F1);
             }
           };
-          gemm1_8(refill_at, wscale(i, 0), wscale(i, 1));
-          gemm2_8((i - 1) & 1, i & 1, std::true_type{}, refill_at, std::integral_constant<int, F1>{},
-                  wscale(i - 1, 2));
+          Sc ig, iu, id;
+          if constexpr (REC_REG) {
+            ig = ng;
+            iu = nu;
+            id = nd;
+            if constexpr (!LAST) {
+              ng = gscale(rec, rot, i + 1, 0);
+              nu = gscale(rec, rot, i + 1, 1);
+            }
+            nd = gscale(rec, rot, i, 2);
+          } else {
+            ig = wscale(i, 0);
+            iu = wscale(i, 1);
+            id = wscale(i - 1, 2);
+          }
+          gemm1_8(refill_at, ig, iu);
+          gemm2_8((i - 1) & 1, i & 1, std::true_type{}, refill_at, std::integral_constant<int, F1>{}, id);
           __syncthreads();
         };
         if constexpr (MORE) {
@@ -1108,12 +1172,25 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
           iteration(NC - 1, std::integral_constant<bool, true>{});
         }
         if constexpr (MODE == MLP_ROUTED) routed_setup();
+        Sc dsc;
+        if constexpr (REC_REG) {
+          dsc = nd;
+          // the next tile's first gate / up scales, ahead of its first
+          // weight fragments (after the last tile: this tile's, unused --
+          // loads on one path only would drain every load in flight where
+          // the paths join)
+          const uint32_t* const nrec = rec_of(has_nx ? nx : cur);
+          g0 = gscale(nrec, nw.rot, 0, 0);
+          u0 = gscale(nrec, nw.rot, 0, 1);
+        } else {
+          dsc = wscale(NC - 1, 2);
+        }
         gemm2_8((NC - 1) & 1, 0, std::false_type{},
                 [&](i32x8& dst, int k2) __attribute__((always_inline)) {
                   if (k2 < F2) issue_frag8(dst, cw, NC - 1, F1 + k2);
                   else issue_frag8(dst, nw, 0, k2 - F2);
                 },
-                std::integral_constant<int, 0>{}, wscale(NC - 1, 2));
+                std::integral_constant<int, 0>{}, dsc);
       };
       if (NC > 1)
         chunk_loop8(std::true_type{});
