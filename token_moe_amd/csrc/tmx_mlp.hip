@@ -226,7 +226,18 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   constexpr int DWX = W / 256;                   // scale dwords per matrix, chunk and lane
   constexpr int XSCB = W / 32;                   // x_hat scale bytes per row
   constexpr int RECX = (3 * DWX * mx_max_chunks(W) + 3) & ~3;  // record dwords the LDS holds per lane
-  constexpr int F8CODES = BM * XSB + 2 * BM * USB + BM * XSCB + 2 * BM * 8;
+  // TP (W = 768): two phases per tile instead of the chunk pipeline --
+  // GEMM1 and U of every hidden chunk first, U of the whole hidden kept in
+  // LDS (codes [BM][USBA], scales [BM][USCB] laid out like x_hat's), then
+  // one GEMM2 over the whole hidden -- so the gate / up accumulators and
+  // the output accumulators (6 column blocks per wave) are never live
+  // together
+  constexpr bool TP = F8 && W == 768;
+  constexpr int HMAX = mx_max_chunks(W) * HC;
+  constexpr int USBA = HMAX + 16, USCB = HMAX / 32;
+  constexpr int OFF_XSC = BM * XSB + (TP ? BM * USBA : 2 * BM * USB);
+  constexpr int OFF_USC = OFF_XSC + BM * XSCB;
+  constexpr int F8CODES = OFF_USC + (TP ? BM * USCB : 2 * BM * 8);
   constexpr int F8BYTES = F8CODES + (REC_REG ? 0 : 4 * RECX * 64 * 4);
   constexpr int SMEM0 = (XBYTES + UBYTES > SBYTES) ? XBYTES + UBYTES : SBYTES;
   constexpr int SMEM = F8 ? (F8BYTES > SBYTES ? F8BYTES : SBYTES) : SMEM0;
@@ -241,8 +252,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   float* const stage = reinterpret_cast<float*>(smem);
   uint8_t* const xs8 = smem;
   uint8_t* const us8 = smem + BM * XSB;
-  uint8_t* const xsc8 = us8 + 2 * BM * USB;
-  uint8_t* const usc8 = xsc8 + BM * XSCB;
+  uint8_t* const xsc8 = smem + OFF_XSC;
+  uint8_t* const usc8 = smem + OFF_USC;
   uint32_t* const wsc8 = reinterpret_cast<uint32_t*>(smem + F8CODES);
 
   const int tid = threadIdx.x;
@@ -1192,7 +1203,108 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
                 },
                 std::integral_constant<int, 0>{}, dsc);
       };
-      if (NC > 1)
+      // TP: U of chunk c, row block rb, into the whole-hidden U tile: one
+      // scale per row and 32 hidden units (this wave's block 4c + wc; 16
+      // values in this lane, 16 in lane ^ 32)
+      auto u_tp = [&](int c, int rb) __attribute__((always_inline)) {
+        f32x16& u = sg[rb];
+        float am = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          u[v] = silu_fast(u[v]) * su[rb][v];
+          am = fmaxf(am, fabsf(u[v]));
+        }
+        am = fmaxf(am, __shfl_xor(am, 32, 64));
+        const int k = mx_exp(am);
+        const float sc = ldexpf(1.f, -k);
+        uint8_t* row = us8 + (rb * 32 + l32) * USBA + c * HC + wc * 32 + 4 * h32;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<uint32_t*>(row + 8 * g4) = e4m3x4(u[4 * g4], u[4 * g4 + 1], u[4 * g4 + 2], u[4 * g4 + 3], sc);
+        const int blk = c * 4 + wc, T = blk >> 1;
+        if (h32 == 0) usc8[(rb * 32 + l32) * USCB + ((T >> 2) * 2 + (blk & 1)) * 4 + (T & 3)] = (uint8_t)(k + 127);
+      };
+      // TP: GEMM2 of chunk c over the whole-hidden U tile; step T = 2c + t
+      // of the hidden reads its U scales from the row's scale words (byte T
+      // % 4 shifted down: T is not a compile-time constant)
+      auto gemm2_tp = [&](int c, auto refill_at, const Sc& dsc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < TS8; ++t) {
+          const int T = c * TS8 + t;
+          uint32_t usw[RBW];
+          i32x8 ub[RBW];
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb) {
+            const int row = rb * 32 + l32;
+            usw[rb] = *reinterpret_cast<const uint32_t*>(&usc8[row * USCB + ((T >> 2) * 2 + h32) * 4]) >> (8 * (T & 3));
+            const uint8_t* q = us8 + row * USBA + T * 64 + 16 * h32;
+            ub[rb] = join8(*reinterpret_cast<const uint4*>(q), *reinterpret_cast<const uint4*>(q + 32));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+            for (int j = 0; j < NBO; ++j)
+              oacc[rb][j] = mfma8s((j * 2 + t) & 3, 0, ring8[(t * NBO + j) % NFR8], ub[rb], dsc.w[(j * 2 + t) >> 2],
+                                   usw[rb], oacc[rb][j]);
+#pragma unroll
+          for (int j = 0; j < NBO; ++j) refill_at(ring8[(t * NBO + j) % NFR8], t * NBO + j + NFR8);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      // TP tile: the weight stream runs GEMM1 fragments of chunks 0 .. NC-1,
+      // then GEMM2 fragments of chunks 0 .. NC-1, then the next tile's.
+      // Scales one chunk ahead, as in the chunk pipeline.
+      auto tp_tile = [&]() __attribute__((always_inline)) {
+        Sc ng = g0, nu = u0, nd{};
+        auto p1 = [&](int c, auto last_tag) __attribute__((always_inline)) {
+          constexpr bool LASTC = decltype(last_tag)::value;
+          const Sc g = ng, u = nu;
+          if constexpr (!LASTC) {
+            ng = gscale(rec, rot, c + 1, 0);
+            nu = gscale(rec, rot, c + 1, 1);
+          } else {
+            nd = gscale(rec, rot, 0, 2);
+          }
+          gemm1_8([&](i32x8& dst, int k2) __attribute__((always_inline)) {
+                    if (k2 < F1) issue_frag8(dst, cw, c, k2);
+                    else if (!LASTC) issue_frag8(dst, cw, c + 1, k2 - F1);
+                    else issue_frag8(dst, cw, 0, k2);          // GEMM2 fragment k2 - F1 of chunk 0
+                  },
+                  g, u);
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb) u_tp(c, rb);
+        };
+        for (int c = 0; c + 1 < NC; ++c) p1(c, std::false_type{});
+        p1(NC - 1, std::true_type{});
+        __syncthreads();                                     // the whole U tile written
+        if constexpr (MODE == MLP_ROUTED) routed_setup();
+        auto p2 = [&](int c, auto last_tag) __attribute__((always_inline)) {
+          constexpr bool LASTC = decltype(last_tag)::value;
+          const Sc d = nd;
+          if constexpr (!LASTC) {
+            nd = gscale(rec, rot, c + 1, 2);
+          } else {
+            // the next tile's first gate / up scales (after the last tile:
+            // this tile's, unused)
+            const uint32_t* const nrec = rec_of(has_nx ? nx : cur);
+            g0 = gscale(nrec, nw.rot, 0, 0);
+            u0 = gscale(nrec, nw.rot, 0, 1);
+          }
+          gemm2_tp(c,
+                   [&](i32x8& dst, int k2) __attribute__((always_inline)) {
+                     if (k2 < F2) issue_frag8(dst, cw, c, F1 + k2);
+                     else if (!LASTC) issue_frag8(dst, cw, c + 1, F1 + k2 - F2);
+                     else issue_frag8(dst, nw, 0, k2 - F2);
+                   },
+                   d);
+        };
+        for (int c = 0; c + 1 < NC; ++c) p2(c, std::false_type{});
+        p2(NC - 1, std::true_type{});
+      };
+      if constexpr (TP)
+        tp_tile();
+      else if (NC > 1)
         chunk_loop8(std::true_type{});
       else
         chunk_loop8(std::false_type{});
