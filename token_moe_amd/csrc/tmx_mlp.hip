@@ -226,13 +226,15 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   constexpr int DWX = W / 256;                   // scale dwords per matrix, chunk and lane
   constexpr int XSCB = W / 32;                   // x_hat scale bytes per row
   constexpr int RECX = (3 * DWX * mx_max_chunks(W) + 3) & ~3;  // record dwords the LDS holds per lane
-  // TP (W = 768): two phases per tile instead of the chunk pipeline --
-  // GEMM1 and U of every hidden chunk first, U of the whole hidden kept in
-  // LDS (codes [BM][USBA], scales [BM][USCB] laid out like x_hat's), then
-  // one GEMM2 over the whole hidden -- so the gate / up accumulators and
-  // the output accumulators (6 column blocks per wave) are never live
-  // together
-  constexpr bool TP = F8 && W == 768;
+  // TP (MoE modes from W = 512): two phases per tile instead of the chunk
+  // pipeline -- GEMM1 and U of every hidden chunk first, U of the whole
+  // hidden kept in LDS (codes [BM][USBA], scales [BM][USCB] laid out like
+  // x_hat's), then one GEMM2 over the whole hidden -- so the gate / up
+  // accumulators and the output accumulators (4 or 6 column blocks per
+  // wave) are never live together. (At W = 768 the pipeline spilled ~280
+  // VGPRs; at W = 512 the routed kernel ran 16% slower with it. The dense
+  // W = 512 kernel keeps the pipeline, which overlaps U with GEMM2.)
+  constexpr bool TP = F8 && (W == 768 || (W == 512 && MODE != MLP_DENSE));
   constexpr int HMAX = mx_max_chunks(W) * HC;
   constexpr int USBA = HMAX + 16, USCB = HMAX / 32;
   constexpr int OFF_XSC = BM * XSB + (TP ? BM * USBA : 2 * BM * USB);
@@ -878,10 +880,14 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
 
     // ---- main loop ---------------------------------------------------------------
     f32x16 oacc[RBW][NBO];
+    // (TP clears them where its GEMM2 phase starts: cleared here they
+    // would stay live through the GEMM1 phase)
+    if constexpr (!TP) {
 #pragma unroll
-    for (int i = 0; i < RBW; ++i)
+      for (int i = 0; i < RBW; ++i)
 #pragma unroll
-      for (int j = 0; j < NBO; ++j) oacc[i][j] = f32x16{};
+        for (int j = 0; j < NBO; ++j) oacc[i][j] = f32x16{};
+    }
 
     if constexpr (NW == 8) {
       // Ping-pong of the two row groups (wr = 0: A, wr = 1: B). Each chunk is
@@ -1279,6 +1285,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
         p1(NC - 1, std::true_type{});
         __syncthreads();                                     // the whole U tile written
         if constexpr (MODE == MLP_ROUTED) routed_setup();
+#pragma unroll
+        for (int i = 0; i < RBW; ++i)
+#pragma unroll
+          for (int j = 0; j < NBO; ++j) oacc[i][j] = f32x16{};
         auto p2 = [&](int c, auto last_tag) __attribute__((always_inline)) {
           constexpr bool LASTC = decltype(last_tag)::value;
           const Sc d = nd;
