@@ -5,7 +5,8 @@ from the library's static device array instead of the context's. Its
 output must equal the regular entry point's bit for bit (same kernels, same
 inputs, same order), and match the oracle to the bf16 bound, on consecutive
 calls -- the second with a smaller batch, so the array still holds the first
-call's larger contents -- for both sub-layers of a bf16 MoE context; the
+call's larger contents -- for both sub-layers of a bf16 MoE context and of an
+MXFP8 one (to the MXFP8 row bound 2^-4 with F visible); the
 largest batch the array holds runs, one more is rejected with an error that
 names the limit; dense sub-layers (no workspace) run as before."""
 import numpy as np
@@ -18,6 +19,7 @@ pytestmark = pytest.mark.gpu
 
 MOE = dg.Workload("noalloc_moe", B=600, T=4, H=4, D=128, L=1, E=16, top_k=4, expert_hidden=128,
                   shared_hidden=256, alpha=4.0, gap=0, seed=91, down_scale=1.0)
+MOE_MX = MOE.with_(name="noalloc_moe_mx", D=512, expert_hidden=256, dtype="mxfp8", seed=93)
 WIDE = dg.Workload("noalloc_wide", B=8192, T=4, H=4, D=512, L=1, E=16, top_k=4, expert_hidden=128,
                    shared_hidden=128, alpha=4.0, gap=0, seed=92, down_scale=1.0)
 
@@ -36,11 +38,12 @@ def _both(ctx, wl, sub, xd, rd, B):
     return ref, out
 
 
-def test_noalloc_matches_sublayer_forward_moe():
+@pytest.mark.parametrize("dtype", ["bf16", "mxfp8"])
+def test_noalloc_matches_sublayer_forward_moe(dtype):
     require_gpu()
     import torch
     from token_moe_amd import runner
-    wl = MOE
+    wl = MOE if dtype == "bf16" else MOE_MX
     banks = dg.weight_banks(wl)
     ctx = runner.make_context(wl, banks)
     ws = dg.WeightSource(wl, banks)
@@ -56,8 +59,8 @@ def test_noalloc_matches_sublayer_forward_moe():
             want = oracle_sublayer(wl, ws, 1, sub, x[:B].astype(np.float64),
                                    None if sub == 0 else r[:B].astype(np.float64), route=idx_g)
             err = row_err(to_np(out), want)
-            say("no-alloc MoE err", sub, B, err)
-            assert err <= TOL["bf16"]
+            say("no-alloc MoE err", dtype, sub, B, err)
+            assert err <= (TOL["bf16"] if dtype == "bf16" else 2.0 ** -4)
     ctx.close()
 
 
