@@ -566,14 +566,14 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   // workgroups in step: every combine epilogue (k expert rows + residual per
   // row, HBM-bound) would run at once while no MFMA runs. With 4 or more
   // tiles per workgroup, every other workgroup of an XCD starts about one
-  // main loop (1.6 x the tile's MFMA clocks) late, so half of them combine
+  // main loop (1.3 x the tile's MFMA clocks) late, so half of them combine
   // while the other half compute.
   const int sh_tiles = (a.pair ? P / 2 : P) * a.rtiles;
   const int sh_grid = std::max(1, std::min(sh_tiles, c->workers & ~7));
   // (MXFP8 MFMAs take half the clocks per multiply-add)
   const double mfma_clk = (double)mlp_bm(MLP_SHARED, W) * W * 3.0 * cfg.shared_hidden / (16384.0 * 4.0) * 32.0 /
                           (mx ? 2.0 : 1.0);
-  a.stagger = sh_tiles >= 4 * sh_grid ? (int)(1.6 * mfma_clk) : 0;
+  a.stagger = sh_tiles >= 4 * sh_grid ? (int)(1.3 * mfma_clk) : 0;
   return launch_timed(c, TMX_KERNEL_MLP_SHARED, st, "shared MLP launch", [&] {
     return mx ? launch_mlp_mx(MLP_SHARED, W, a, sh_tiles, c->workers, st)
               : launch_mlp(MLP_SHARED, W, a, sh_tiles, c->workers, st);
