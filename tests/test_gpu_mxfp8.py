@@ -273,3 +273,47 @@ def test_mxfp8_w512_sublayer_teacher_forced_full_batch(which, sub):
     assert err <= TOL["bf16"]
     if sub == 1:
         drop("mx_" + which)
+
+
+@pytest.mark.parametrize("sub", [0, 1])
+def test_mxfp8_skewed_routing_and_empty_buckets(sub):
+    """MXFP8 MoE at W = 512 with an always-empty bucket (expert 5: negative
+    router column on positive inputs) and an all-rows bucket (expert 3,
+    column x10: B = 1000 rows, 16 row tiles of one expert), down matrices at
+    full scale and, in the Revert sub-layer, a zero residual: the expert
+    outputs of the all-rows bucket and the shared expert are what the
+    comparison sees (F bounds)."""
+    require_gpu()
+    import torch
+    from token_moe_amd import runner
+    wl = MX_MOE_SMALL.with_(name="mx_skew", L=1, B=1000, down_scale=1.0, seed=48)
+    banks = dg.weight_banks(wl)
+    for s in (0, 1):
+        wr = np.abs(dg.bf16_bits_to_f32(banks[(1, s, dg.K_ROUTER)]))
+        wr[..., 3] *= 10.0
+        wr[..., 5] = -wr[..., 5]
+        banks[(1, s, dg.K_ROUTER)] = dg.f32_to_bf16_bits(wr)
+    ctx = runner.make_context(wl, banks)
+    ws = dg.WeightSource(wl, banks)
+    x = np.abs(dg.make_x(wl))
+    xd = to_dev(wl, x)
+    idx_g, gate_g = route_gpu(ctx, wl, 0, sub, xd, wl.B)
+    assert not np.any(idx_g == 5) and np.all(idx_g[..., 0] == 3)
+    out = torch.empty_like(xd)
+    if sub == 0:
+        ctx.sublayer_forward(0, 0, xd, None, None, out, wl.B, stream())
+    else:
+        ctx.sublayer_forward(0, 1, xd, torch.zeros_like(xd), None, out, wl.B, stream())
+    torch.cuda.synchronize()
+    xf = x.astype(np.float64)
+    rows = sample_rows(wl.B, 96, seed=80 + sub)
+    ref = oracle_sublayer(wl, ws, 1, sub, xf[rows], None if sub == 0 else np.zeros(xf[rows].shape),
+                          route=idx_g[rows])
+    y = to_np(out)[rows]
+    if sub == 0:
+        y, ref = y - xf[rows], ref - xf[rows]
+    per_row = np.max(np.abs(y - ref), axis=-1) / np.max(np.abs(ref), axis=-1)
+    say("mxfp8 skewed", sub, "max", per_row.max(), "median", np.median(per_row))
+    slack = 0.0 if sub == 1 else 2.0 ** -8 * float(np.max(np.abs(xf)) / np.min(np.max(np.abs(ref), axis=-1)))
+    assert per_row.max() <= TOL_F + slack and np.median(per_row) <= TOL_F_MEDIAN + slack
+    ctx.close()
