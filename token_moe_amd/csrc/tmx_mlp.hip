@@ -990,11 +990,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
       }
       if (wr == 0) __syncthreads();
     } else if constexpr (F8) {
-      // MXFP8: the chunk schedule of the 4-wave kernel below (GEMM1(i);
-      // GEMM2(i-1) with U(i) between its MFMAs; barrier) on 32x32x64 scaled
-      // MFMAs. GEMM1 step s reads 64 columns of x_hat codes and the rows'
-      // scale words (byte s), GEMM2 step t 64 hidden units of U codes (byte
-      // t); the weight scales come from the tile's records in LDS.
+      // MXFP8 on 32x32x64 scaled MFMAs. Dense sub-layers: the chunk schedule
+      // of the 4-wave kernel below (GEMM1(i); GEMM2(i-1) with U(i) between
+      // its MFMAs; barrier). MoE modes (TP): the two-phase tile (tp_tile).
+      // GEMM1 step s reads 64 columns of x_hat codes and the rows' scale
+      // words (byte s % 4 of word s / 4), GEMM2 step t 64 hidden units of U
+      // codes and their scales; the weight scales come from the tile's
+      // records in LDS (W = 256) or straight from global memory (REC_REG).
       f32x16 sg[RBW], su[RBW];
       uint32_t xsw[RBW][DWX];
 #pragma unroll
