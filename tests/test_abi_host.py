@@ -128,6 +128,7 @@ def _create(tmx, **kw):
     (dict(dtype=2, D=512, H=16, T=16, E=16, top_k=4, expert_hidden=256, shared_hidden=2048), "UNSUPPORTED"),
     (dict(dtype=2, D=512, H=16, T=16, E=12, top_k=4, expert_hidden=256, shared_hidden=512), "UNSUPPORTED"),
     (dict(dtype=2, D=512, H=16, T=16, E=16, top_k=10, expert_hidden=256, shared_hidden=512), "UNSUPPORTED"),
+    (dict(dtype=2, D=768, H=32, T=32, E=32, top_k=4, expert_hidden=384, shared_hidden=1024), "UNSUPPORTED"),
     (dict(dtype=3), "INVALID_ARG"),
     # MXFP8 capability checks come after every shape check: H = 0 or D % H != 0
     # must be INVALID_ARG, never a division by zero in the MXFP8 width check
@@ -171,11 +172,21 @@ def test_create_validation(tmx, kw, status):
     assert msg
 
 
-def test_create_without_device_reports_device_error(tmx):
+@pytest.mark.parametrize("kw", [
+    dict(),
+    # MXFP8 shapes that pass validation: dense W 512 / 256 (uneven mixing),
+    # MoE at W 512 and at W 768 (hidden 768 = the most W 768 allows)
+    dict(dtype=2, T=16, H=8, D=256, hidden_mix=1024, hidden_rev=1024),
+    dict(dtype=2, T=16, H=16, D=512, E=16, top_k=4, expert_hidden=256, shared_hidden=1024),
+    dict(dtype=2, T=32, H=32, D=768, E=32, top_k=4, expert_hidden=384, shared_hidden=768),
+])
+def test_create_without_device_reports_device_error(tmx, kw):
+    """Valid configurations get past validation and fail only for want of a
+    device."""
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
-    st, h, msg = _create(tmx)
+    st, h, msg = _create(tmx, **kw)
     assert st == tmx.TMX_ERR_DEVICE and h.value is None and msg
 
 
