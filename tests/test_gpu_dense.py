@@ -207,3 +207,33 @@ def test_state_error_before_weights():
         ctx.load_weights(0, 0, dg.K_ROUTER, t.data_ptr(), 20)
     assert e.value.status == tmx.TMX_ERR_INVALID_ARG
     ctx.close()
+
+
+def test_create_beyond_device_memory_reports_oom_and_device_stays_usable():
+    """A context whose activation buffers exceed the GPU's memory (B_max x T x
+    D = 2^39 bf16 elements, 1 TiB per buffer; within the shape limits) fails
+    with TMX_ERR_OOM and a message naming the allocation, releasing what it
+    had allocated; a context created next runs a forward as before."""
+    require_gpu()
+    import torch
+    from token_moe_amd import runner, tmx
+    cfg = tmx.make_config(B_max=1 << 29, T=4, H=4, D=256, L=1, hidden_mix=256, hidden_rev=256,
+                          dtype=tmx.TMX_BF16)
+    free = []
+    for _ in range(3):
+        with pytest.raises(tmx.TmxError) as e:
+            tmx.Context(cfg)
+        assert e.value.status == tmx.TMX_ERR_OOM and "hipMalloc" in e.value.message
+        free.append(torch.cuda.mem_get_info()[0])
+    say("OOM message:", e.value.message, "free after each attempt", free)
+    # (the first attempt also loads the library's device code and its static
+    # arrays); later attempts leave nothing allocated
+    assert abs(free[2] - free[1]) <= (16 << 20)
+    wl = SMALL_BF16.with_(name="after_oom", L=1)
+    banks = dg.weight_banks(wl)
+    ctx = runner.make_context(wl, banks)
+    x = dg.make_x(wl)
+    y = to_np(_stack(wl, ctx, to_dev(wl, x), wl.B))
+    ref = orc.stack_forward(x.astype(np.float64), wl, dg.WeightSource(wl, banks))
+    assert row_err(y, ref) <= TOL["bf16"]
+    ctx.close()
