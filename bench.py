@@ -373,7 +373,9 @@ def main(argv=None):
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                     "traffic": measured_traffic(wl.name) if wl.dtype == "bf16" else None,
-                    "kernel": f"mlp_kernel<{wl.width(1)}, DENSE{', MXFP8' if wl.dtype == 'mxfp8' else ''}>",
+                    "kernel": " / ".join(dict.fromkeys(
+                        f"mlp_kernel<{wl.width(sub)}, DENSE{', MXFP8' if wl.dtype == 'mxfp8' else ''}>"
+                        for sub in (0, 1))) + " (mean of the Mix and Revert launches)",
                     "flop_per_launch": kfl, "launch_ms": round(kms, 5)}
         log(f"fused MLP kernel: {kms:.4f} ms/launch, {achieved:.1f} TFLOP/s")
 
