@@ -6,7 +6,9 @@ in F hides inside the output comparison. Here the Revert sub-layer runs with
 a zero residual, which leaves F alone (rounded to bf16 once), for every
 kernel shape: the dense 4-wave kernels at W = 128, 512, 768 (W = 256 is
 covered in test_gpu_mxfp8.py) and the routed + shared MoE kernels at W = 512
-and 768. Tolerance: the bf16 bound, row-normwise 2e-2."""
+and 768 (at W = 768 both routed kernels: the 128-row one for expert hidden
+384, the fused kernel's 64-row tile for other expert widths). Tolerance: the
+bf16 bound, row-normwise 2e-2."""
 import numpy as np
 import pytest
 
@@ -26,6 +28,8 @@ CASES = {
                             shared_hidden=512, gap=0, seed=64),
     "moe_w768": dg.Workload("fa_moe_w768", B=130, T=4, H=4, D=768, L=1, E=32, top_k=4, expert_hidden=384,
                             shared_hidden=768, gap=0, seed=65),
+    "moe_w768_he256": dg.Workload("fa_moe_w768_he256", B=300, T=4, H=4, D=768, L=1, E=16, top_k=4,
+                                  expert_hidden=256, shared_hidden=384, gap=0, seed=66),
 }
 
 
