@@ -275,18 +275,21 @@ def test_mxfp8_w512_sublayer_teacher_forced_full_batch(which, sub):
         drop("mx_" + which)
 
 
+@pytest.mark.parametrize("W", [512, 768])
 @pytest.mark.parametrize("sub", [0, 1])
-def test_mxfp8_skewed_routing_and_empty_buckets(sub):
-    """MXFP8 MoE at W = 512 with an always-empty bucket (expert 5: negative
-    router column on positive inputs) and an all-rows bucket (expert 3,
-    column x10: B = 1000 rows, 16 row tiles of one expert), down matrices at
-    full scale and, in the Revert sub-layer, a zero residual: the expert
+def test_mxfp8_skewed_routing_and_empty_buckets(sub, W):
+    """MXFP8 MoE with an always-empty bucket (expert 5: negative router
+    column on positive inputs) and an all-rows bucket (expert 3, column x10:
+    B = 1000 rows, 16 row tiles of one expert at W = 512, 8 tiles of 128 rows
+    of the wide routed kernel at W = 768, the last one ragged), down matrices
+    at full scale and, in the Revert sub-layer, a zero residual: the expert
     outputs of the all-rows bucket and the shared expert are what the
     comparison sees (F bounds)."""
     require_gpu()
     import torch
     from token_moe_amd import runner
-    wl = MX_MOE_SMALL.with_(name="mx_skew", L=1, B=1000, down_scale=1.0, seed=48)
+    base = MX_MOE_SMALL if W == 512 else MX_MOE_768
+    wl = base.with_(name=f"mx_skew{W}", L=1, B=1000, down_scale=1.0, seed=48)
     banks = dg.weight_banks(wl)
     for s in (0, 1):
         wr = np.abs(dg.bf16_bits_to_f32(banks[(1, s, dg.K_ROUTER)]))

@@ -374,7 +374,9 @@ tmx_status validate_config(const tmx_config* cfg) {
 
 // rows per routed bucket tile: the wide routed kernel's where it applies
 int moe_bm(const tmx_config& c, int sub) {
-  const int wide = c.dtype == TMX_BF16 ? routed_wide_rows(width(c, sub), c.expert_hidden) : 0;
+  const int wide = c.dtype == TMX_BF16     ? routed_wide_rows(width(c, sub), c.expert_hidden)
+                   : c.dtype == TMX_MXFP8 ? routed_wide_mx_rows(width(c, sub), c.expert_hidden)
+                                          : 0;
   return wide > 0 ? wide : mlp_bm(MLP_ROUTED, width(c, sub));
 }
 int moe_max_tiles(const tmx_config& c, int sub, int B) {
@@ -519,7 +521,7 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   // MoE: norm + route -> bucket -> routed experts -> shared expert + combine
   const int bm = moe_bm(cfg, sub);
   const bool mx = cfg.dtype == TMX_MXFP8;
-  const bool wide = !mx && routed_wide_rows(W, cfg.expert_hidden) > 0;
+  const bool wide = mx ? routed_wide_mx_rows(W, cfg.expert_hidden) > 0 : routed_wide_rows(W, cfg.expert_hidden) > 0;
   RouteArgs r{};
   r.B = B; r.P = P; r.E = cfg.E; r.top_k = cfg.top_k; r.alpha = c->alpha; r.eps = cfg.eps; r.map = map;
   r.x = static_cast<const uint16_t*>(x_in); r.gain = gain;
@@ -547,9 +549,11 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
     a.wrec = mx_rec(cfg, sub, TMX_W_EXP_GATE);
   }
   s = launch_timed(c, TMX_KERNEL_MLP_ROUTED, st, "routed MLP launch", [&] {
-    return mx     ? launch_mlp_mx(MLP_ROUTED, W, a, P * a.max_tiles, c->workers, st)
-           : wide ? launch_routed_wide(a, P * a.max_tiles, c->workers, st)
-                  : launch_mlp(MLP_ROUTED, W, a, P * a.max_tiles, c->workers, st);
+    if (mx)
+      return wide ? launch_routed_wide_mx(a, P * a.max_tiles, c->workers, st)
+                  : launch_mlp_mx(MLP_ROUTED, W, a, P * a.max_tiles, c->workers, st);
+    return wide ? launch_routed_wide(a, P * a.max_tiles, c->workers, st)
+                : launch_mlp(MLP_ROUTED, W, a, P * a.max_tiles, c->workers, st);
   });
   if (s != TMX_OK) return s;
 

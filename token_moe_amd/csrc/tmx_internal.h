@@ -92,6 +92,10 @@ hipError_t launch_mlp(int mode, int W, const MlpArgs& a, int tiles, int workers,
 // ROUTED arguments)
 int routed_wide_rows(int W, int h_e);
 hipError_t launch_routed_wide(const MlpArgs& a, int tiles, int workers, hipStream_t s);
+// its MXFP8 form (tmx_routed_mx.hip): same tiles and arguments, weights and
+// scale records from launch_pack_mx
+int routed_wide_mx_rows(int W, int h_e);
+hipError_t launch_routed_wide_mx(const MlpArgs& a, int tiles, int workers, hipStream_t s);
 // whether DENSE / SHARED tiles of this mode and width may hold two adjacent positions
 bool mlp_pairs_positions(int mode, int W);
 // workgroups of the MLP kernel resident per CU for a mode and width
