@@ -10,27 +10,31 @@
 // serving four 32-row MFMA blocks, in phases that each stay within the 256
 // accumulator registers:
 //
-//   GEMM1 A  S_gate, S_up for hidden blocks 2w, 2w+1 of wave w, K-outer: the
-//            rows' x_hat columns stream through LDS in 64-column slabs
-//            (one MFMA k-step each), quantised to E4M3 as they are stored;
+//   GEMM1 A  S_gate, S_up for hidden blocks 2w, 2w+1 of wave w, K-outer over
+//            the 12 64-column slabs of the rows' x_hat (one MFMA k-step each)
 //   U(A)     E4M3(silu(S_gate) * S_up) with one scale per row and 32 hidden
-//            units -> LDS U [128, h_e];
-//   GEMM1 B  hidden block 8 + w, x_hat streamed again; U(B) -> LDS U;
+//            units -> LDS U [128, h_e]
+//   GEMM1 B  hidden block 8 + w; U(B) -> LDS U
 //   GEMM2 c  O [128, 256c : 256c + 256) = U @ W_down (2 column blocks per
-//            wave), c = 0, 1, 2, each followed by gate * O -> bf16, staged 32
-//            rows at a time and written as whole 16-byte units.
+//            wave), c = 0, 1, 2, each followed by gate * O -> bf16, staged in
+//            LDS and written as whole 16-byte units.
+//
+// x_hat is quantised to E4M3 once per tile, into an LDS copy of the whole
+// tile (128 x 768 codes, 96 KiB) that both GEMM1 passes read: GEMM1 B runs
+// from LDS alone. The quantisation runs 4 slabs ahead of the MFMAs that use
+// it, spread over the MFMAs of GEMM1 A (slabs 4..11) and of the previous
+// tile's GEMM2 parts (slabs 0..3); the global loads run 2 slabs ahead of the
+// quantisation. During the GEMM2 parts, slabs 4..11 of the copy hold the
+// epilogue's staging rows.
 //
 // The weights come from the MXFP8 packing of load time (launch_pack_mx):
 // 2 KiB fragments, and per-lane scale records in the layout the fused MLP
 // kernel reads them in (record wave = the fused kernel's owner of a column
-// block); each wave here reads the records of the blocks it computes, from
-// global memory into registers, one phase ahead of their use.
-//
-// Pipelines as in the bf16 kernel: weight fragments stream through a
-// 12-slot register ring (2 KiB fragments, 24 KiB in flight per wave) in one
+// block); each wave reads the records of the blocks it computes, from global
+// memory into registers, one phase ahead of their use. Weight fragments
+// stream through a 12-slot register ring (24 KiB in flight per wave) in one
 // order per tile (GEMM1 A, GEMM1 B, GEMM2 0, 1, 2) running on into the next
-// tile; x_hat slabs run through three LDS buffers, slab t + 1 quantised
-// into its buffer and slab t + 3 loaded at slab step t.
+// tile.
 #include <type_traits>
 
 #include "tmx_internal.h"
@@ -44,8 +48,9 @@ constexpr int RX_RB = 4;     // 32-row blocks per tile
 constexpr int RX_BM = 32 * RX_RB;
 constexpr int RX_SC = 64;    // columns per x_hat slab: one fp8 MFMA k-step
 constexpr int RX_RING = 12;  // weight fragments in flight per wave
+constexpr int RX_QA = 4;     // slabs between a slab's quantisation and its MFMAs
+constexpr int RX_QMAX = 64;  // positions per tile queue whose tile counts sit in LDS
 constexpr int RX_RSRC_W3 = 0x00020000;   // buffer resource word 3: raw 32-bit data, no swizzle
-constexpr int RX_NT_POLICY = 2;          // streaming cache policy (the rows' last read)
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -89,6 +94,17 @@ __device__ __forceinline__ int rx_exp(float amax) {
   const int k = amax > 0.f ? e - 9 : -127;
   return k < -127 ? -127 : (k > 127 ? 127 : k);
 }
+// largest x of the 4 lanes of a quad (DPP quad permutations: lane ^ 1, then
+// lane ^ 2)
+__device__ __forceinline__ uint32_t rx_quad_maxu(uint32_t x) {
+  uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);
+  x = x > y ? x : y;
+  y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);
+  return x > y ? x : y;
+}
+// the magnitude bits of two bf16 values
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ us2 rx_mag2(uint32_t w) { return __builtin_bit_cast(us2, w & 0x7FFF7FFFu); }
 
 __device__ __forceinline__ float rx_silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
@@ -97,47 +113,56 @@ struct RxShape {
   static constexpr int BM = RX_BM;
   static constexpr int HA = 2;                    // hidden blocks per wave, GEMM1 pass A
   static constexpr int HBB = HE / 128 - HA;       // ... pass B
-  static constexpr int NP2 = W / 256;             // GEMM2 parts (2 output blocks per wave each)
   static constexpr int NSP = W / RX_SC;           // slabs (= k-steps) per GEMM1 pass
-  static constexpr int NSL = 2 * NSP;             // slab steps per tile
   static constexpr int KS = W / 64;               // k-steps of a gate / up fragment column
   static constexpr int KB2 = HE / 64;             // GEMM2 k-steps
   static constexpr int FA = 2 * HA, FB = 2 * HBB, FC = 2;     // fragments per k-step
   static constexpr int LA = NSP * FA, LB = NSP * FB, LC = KB2 * FC;   // fragments per phase
   static constexpr int USB = HE + 16;             // U row stride (bytes)
   static constexpr int USC = HE / 32;             // U scale bytes per row
-  static constexpr int SLAB = BM * RX_SC;         // code bytes per slab buffer
+  static constexpr int XSL = BM * RX_SC;          // code bytes per slab of the x_hat copy
   static constexpr int SU = BM * RX_SC / 8 / RX_NT;   // 16-byte bf16 units of a slab per lane
   static constexpr int HS = 256 + 8;              // staged part-row stride (bf16)
-  static constexpr int NR = HE / 32;              // hidden blocks (record scale bytes per row of U)
+  // LDS: x_hat codes [slab][row][64] (slabs RX_QA.. and a pad after them
+  // double as the staging rows [128][HS]), x_hat exponents [slab][row][2],
+  // U [row][USB], U exponents [row][hidden block]
+  static constexpr int STG_PAD = BM * HS * 2 > (NSP - RX_QA) * XSL ? BM * HS * 2 - (NSP - RX_QA) * XSL : 0;
+  static constexpr int OFF_XSC = NSP * XSL + STG_PAD;
+  static constexpr int OFF_US = OFF_XSC + NSP * BM * 2;
+  static constexpr int OFF_USC = OFF_US + BM * USB;
+  static constexpr int LDS_BYTES = OFF_USC + BM * USC;
   static_assert(W == 768 && HE == 384, "the MXFP8 wide routed kernel is built for W 768, h_e 384");
-  static_assert(HBB == 1 && NSP % 6 == 0, "pass shapes");
+  static_assert(HBB == 1 && NSP == 12 && SU == RX_RB && KB2 >= SU + 2,
+                "pass shapes: slab units are quantised one per row block or GEMM2 k-step");
   static_assert((W / 128) % 2 == 0, "GEMM2 scale byte: a down block's index among its record's blocks has j's parity");
   static_assert(LA % RX_RING == 0 && LB % RX_RING == 0 && LC % RX_RING == 0 && RX_RING % FA == 0 &&
                 RX_RING % FB == 0 && RX_RING % FC == 0,
                 "every phase is whole turns of the ring, each of whole k-steps");
-  static_assert(3 * (SLAB + 2 * BM) + BM * USB + BM * USC + 32 * HS * 2 + 3 * 2 * BM * 4 + 16 <= 160 * 1024,
-                "LDS budget");
+  static_assert(LDS_BYTES + 3 * 2 * BM * 4 + 4 * (RX_QMAX + 2) <= 160 * 1024, "LDS budget");
 };
 
 template <int W, int HE>
 __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
   using S = RxShape<W, HE>;
-  constexpr int BM = S::BM, HA = S::HA, HBB = S::HBB, NP2 = S::NP2, NSP = S::NSP, NSL = S::NSL;
+  constexpr int BM = S::BM, HA = S::HA, HBB = S::HBB, NSP = S::NSP;
   constexpr int KS = S::KS, KB2 = S::KB2, FA = S::FA, FB = S::FB, FC = S::FC;
-  constexpr int LA = S::LA, LB = S::LB, LC = S::LC, USB = S::USB, USC = S::USC, SLAB = S::SLAB, SU = S::SU;
+  constexpr int LA = S::LA, LB = S::LB, LC = S::LC, USB = S::USB, USC = S::USC, XSL = S::XSL, SU = S::SU;
   constexpr int HS = S::HS;
   constexpr int NBO = W / 128;   // the fused kernel's down column blocks per wave (record layout)
 
-  __shared__ __attribute__((aligned(16))) uint8_t slabs[3 * SLAB];
-  __shared__ __attribute__((aligned(16))) uint8_t slabsc[3 * 2 * BM];   // [buffer][row][2 K-blocks]
-  __shared__ __attribute__((aligned(16))) uint8_t us[BM * USB];
-  __shared__ __attribute__((aligned(16))) uint8_t usc[BM * USC];         // [row][hidden block]
-  __shared__ __attribute__((aligned(16))) uint16_t stg[32 * HS];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS_BYTES];
   __shared__ int rowb[2][BM];      // sample row of each tile row (-1: padding)
   __shared__ int rowgi[2][BM];     // expert-output row (b, p, slot)
   __shared__ float rowg[2][BM];    // gate of each tile row
+  __shared__ int qcum[RX_QMAX + 1];   // tiles of the queue's positions before position q
   __shared__ int claim;
+  uint8_t* const xq = lds;
+  uint8_t* const xsc = lds + S::OFF_XSC;
+  uint8_t* const us = lds + S::OFF_US;
+  uint8_t* const usc = lds + S::OFF_USC;
+  // staging rows of the GEMM2 epilogue, over slabs RX_QA.. of the x_hat copy
+  // (free from the end of GEMM1 B to the next tile's GEMM1 A)
+  uint16_t* const stg = reinterpret_cast<uint16_t*>(lds + RX_QA * XSL);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -148,28 +173,51 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
   int ot = tid;
   auto fresh = [&]() __attribute__((always_inline)) { asm volatile("" : "+v"(ot)); };
 
-  // ---- tile queues, as the bf16 routed kernel
+  // ---- tile queues, as the bf16 routed kernel; the queue's tile counts are
+  // read once into LDS as running sums, and a claim is decoded with one
+  // ballot over them
   const bool split_q = (a.P & 7) == 0;
   const int qx = split_q ? (int)(blockIdx.x & 7) : 0;
   const int NPX = split_q ? (a.P >> 3) : a.P;
+  const bool qlds = NPX <= RX_QMAX;
+  if (qlds && tid < 64) {
+    int n = tid < NPX ? a.ntiles[qx * NPX + tid] : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(n, d, 64);
+      if (lane >= d) n += v;
+    }
+    qcum[tid + 1] = n;
+    if (tid == 0) qcum[0] = 0;
+  }
   struct Tile {
     int p, group, start, nrows;
   };
   auto qdecode = [&](int k, Tile& T) -> bool {
-    int p = qx * NPX;
-    for (int q = 0; q < NPX; ++q, ++p) {
-      const int n = a.ntiles[p];
-      if (k < n) {
-        const int4 tl = a.tiles[(size_t)p * a.max_tiles + k];
-        T.p = __builtin_amdgcn_readfirstlane(p);
-        T.group = __builtin_amdgcn_readfirstlane(p * a.E + tl.x);
-        T.start = __builtin_amdgcn_readfirstlane(tl.y);
-        T.nrows = __builtin_amdgcn_readfirstlane(tl.z);
-        return true;
+    int p;
+    if (qlds) {
+      const bool hit = lane < NPX && qcum[lane] <= k && k < qcum[lane + 1];
+      const uint64_t m = __ballot(hit);
+      if (m == 0) return false;
+      const int q = __builtin_amdgcn_readfirstlane(__builtin_ctzll(m));
+      p = qx * NPX + q;
+      k -= qcum[q];
+    } else {
+      p = qx * NPX;
+      int q = 0;
+      for (; q < NPX; ++q, ++p) {
+        const int n = a.ntiles[p];
+        if (k < n) break;
+        k -= n;
       }
-      k -= n;
+      if (q == NPX) return false;
     }
-    return false;
+    const int4 tl = a.tiles[(size_t)p * a.max_tiles + k];
+    T.p = __builtin_amdgcn_readfirstlane(p);
+    T.group = __builtin_amdgcn_readfirstlane(p * a.E + tl.x);
+    T.start = __builtin_amdgcn_readfirstlane(tl.y);
+    T.nrows = __builtin_amdgcn_readfirstlane(tl.z);
+    return true;
   };
   auto set_rows = [&](const Tile& T, int buf) {
     for (int r = tid; r < BM; r += RX_NT) {
@@ -193,11 +241,10 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
   //   2, 3, 4  GEMM2 part c = ph - 2: k-step kb, output block 8 c + 2 wave + j
   //   5  the next tile's phase 0
   // A super-step is one turn of the ring; slot i is refilled with fragment i
-  // of the next super-step, which may belong to the next phase (both
-  // addresses are formed and one selected: one unconditional load pair).
-  // Fragment sizes are 2 KiB (two 1 KiB halves, 16 bytes per lane each),
-  // read through buffer resources with a 32-bit lane offset.
-  constexpr uint32_t GU_BYTES = 2u * W * HE;   // gate|up codes of a bucket
+  // of the next super-step, which may belong to the next phase. Fragments
+  // are 2 KiB (two 1 KiB halves, 16 bytes per lane each), read through
+  // buffer resources with a 32-bit lane offset.
+  constexpr uint32_t GU_BYTES = 2u * W * HE;        // gate|up codes of a bucket
   constexpr uint32_t WD_BYTES = (uint32_t)HE * W;   // down codes of a bucket
   auto rsrc = [](const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, RX_RSRC_W3);
@@ -209,9 +256,14 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
     gu = rsrc(wgu8 + (size_t)T.group * GU_BYTES, GU_BYTES);
     wd = rsrc(wd8 + (size_t)T.group * WD_BYTES, WD_BYTES);
   };
+  // the fragment's constant offset is added to `zs`, an opaque zero made
+  // anew for every k-step: the compiler would otherwise hoist the ~100
+  // constant offsets of a tile out of the tile loop into scalar registers,
+  // which then spill
+  int zs = 0;
   auto frag = [&](__amdgpu_buffer_rsrc_t r, uint32_t voff, int c) __attribute__((always_inline)) -> i32x8 {
-    return rx_join(__builtin_amdgcn_raw_buffer_load_b128(r, voff, c, 0),
-                   __builtin_amdgcn_raw_buffer_load_b128(r, voff, c + 1024, 0));
+    return rx_join(__builtin_amdgcn_raw_buffer_load_b128(r, voff + 0u, zs + c, 0),
+                   __builtin_amdgcn_raw_buffer_load_b128(r, voff + 1024u, zs + c, 0));
   };
   // gate / up fragment (block nb, k-step kb, which) at byte ((nb KS + kb) 2 +
   // which) 2048; down fragment (k-step kb, block ob) at (kb W/32 + ob) 2048
@@ -287,65 +339,60 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
   };
 
   // ---- x_hat slabs: unit u = tid + 256 i of a slab is row u / 8, 8-column
-  // chunk u % 8 of the slab's 64 columns (bf16 in memory). The slab is stored
+  // chunk u % 8 of the slab's 64 columns (bf16 in memory). A slab is stored
   // quantised: 64 code bytes per row, 16-byte chunk k of a row at chunk k ^
   // (row % 4) (the fragment reads of 4 consecutive rows hit different bank
   // groups), and the row's two 32-column block exponents.
+  // byte offsets of this lane's slab units in x_hat, for this tile (roff)
+  // and the next (roffn; rows of padding read sample row 0)
   uint32_t roff[SU], roffn[SU];
-  auto slab_rows = [&](int p, int buf, uint32_t* ro) {
+  auto slab_rows = [&](int p, int tb, uint32_t* ro) {
 #pragma unroll
     for (int i = 0; i < SU; ++i) {
       const int u = ot + i * RX_NT;
-      const int b = rowb[buf][u >> 3];
+      const int b = rowb[tb][u >> 3];
       ro[i] = (((uint32_t)p * (uint32_t)a.B + (uint32_t)(b < 0 ? 0 : b)) * (uint32_t)W + (uint32_t)(u & 7) * 8u) * 2u;
     }
   };
   const __amdgpu_buffer_rsrc_t xr = rsrc(a.xhat, (uint32_t)((uint64_t)a.P * a.B * W * 2));
-  auto slab_load = [&](int t, v4u* v) __attribute__((always_inline)) {
-    const bool nxt = t >= NSL;
-    const int col = (nxt ? t - NSL : (t >= NSP ? t - NSP : t)) * RX_SC * 2;
+  // slab s of this tile (nxt: of the next tile)
+  auto slab_load = [&](int s, bool nxt, v4u* v) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < SU; ++i) {
-      const uint32_t o = nxt ? roffn[i] : roff[i];
-      v[i] = (t >= NSP && !nxt) ? __builtin_amdgcn_raw_buffer_load_b128(xr, o, col, RX_NT_POLICY)
-                                : __builtin_amdgcn_raw_buffer_load_b128(xr, o, col, 0);
-    }
+    for (int i = 0; i < SU; ++i)
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, nxt ? roffn[i] : roff[i], s * RX_SC * 2, 0);
   };
-  // quantise and store: the 4 units of a 32-column block are 4 consecutive
-  // lanes (u % 8 = 4k .. 4k + 3 of one row)
-  auto slab_store = [&](int sb, const v4u* v) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < SU; ++i) {
-      const int u = ot + i * RX_NT, r = u >> 3, c8 = u & 7;
-      const uint16_t* h = reinterpret_cast<const uint16_t*>(&v[i]);
-      float n[8], am = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        n[e] = bf2f(h[e]);
-        am = fmaxf(am, fabsf(n[e]));
-      }
-      am = fmaxf(am, __shfl_xor(am, 1, 64));
-      am = fmaxf(am, __shfl_xor(am, 2, 64));
-      const int k = rx_exp(am);
-      const float sc = ldexpf(1.f, -k);
-      uint2 q;
-      q.x = rx_e4m3x4(n[0], n[1], n[2], n[3], sc);
-      q.y = rx_e4m3x4(n[4], n[5], n[6], n[7], sc);
-      *reinterpret_cast<uint2*>(&slabs[sb * SLAB + r * RX_SC + (((c8 >> 1) ^ (r & 3)) * 16) + (c8 & 1) * 8]) = q;
-      if ((c8 & 3) == 0) slabsc[(sb * BM + r) * 2 + (c8 >> 2)] = (uint8_t)(k + 127);
-    }
+  // quantise and store unit i of slab s: the 4 units of a 32-column block are
+  // the 4 lanes of a quad (u % 8 = 4k .. 4k + 3 of one row)
+  auto quant_unit = [&](int s, int i, const v4u& v) __attribute__((always_inline)) {
+    const int u = ot + i * RX_NT, r = u >> 3, c8 = u & 7;
+    // largest magnitude of the 8 bf16 values: magnitudes order as their
+    // 15-bit patterns
+    const us2 m2 = __builtin_elementwise_max(__builtin_elementwise_max(rx_mag2(v.x), rx_mag2(v.y)),
+                                             __builtin_elementwise_max(rx_mag2(v.z), rx_mag2(v.w)));
+    const uint32_t mb = rx_quad_maxu(m2.x > m2.y ? (uint32_t)m2.x : (uint32_t)m2.y);
+    const int k = rx_exp(__uint_as_float(mb << 16));
+    const float sc = ldexpf(1.f, -k);
+    uint2 q;
+    q.x = rx_e4m3x4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u), __uint_as_float(v.y << 16),
+                    __uint_as_float(v.y & 0xFFFF0000u), sc);
+    q.y = rx_e4m3x4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u), __uint_as_float(v.w << 16),
+                    __uint_as_float(v.w & 0xFFFF0000u), sc);
+    *reinterpret_cast<uint2*>(&xq[s * XSL + r * RX_SC + (((c8 >> 1) ^ (r & 3)) * 16) + (c8 & 1) * 8]) = q;
+    // every lane of the quad stores the (same) exponent: no branch, so the
+    // scheduler may spread the quantisation between MFMAs
+    xsc[(s * BM + r) * 2 + (c8 >> 2)] = (uint8_t)(k + 127);
   };
-  // B operand of row block rb from a slab: row 32 rb + l32, bytes 16 h32 ..
-  // of K-block 0 and 32 + 16 h32 .. of K-block 1; its scale in byte 0
-  auto slab_frag = [&](int sb, int rb) -> i32x8 {
+  // B operand of row block rb from slab s: row 32 rb + l32, bytes 16 h32 ..
+  // of K-block 0 and 32 + 16 h32 .. of K-block 1; its exponent in byte 0
+  auto x_frag = [&](int s, int rb) -> i32x8 {
     const int r = rb * 32 + (ot & 31), h = (ot >> 5) & 1;
-    const uint8_t* row = slabs + sb * SLAB + r * RX_SC;
+    const uint8_t* row = xq + s * XSL + r * RX_SC;
     return rx_join(*reinterpret_cast<const v4u*>(row + ((h ^ (r & 3)) * 16)),
                    *reinterpret_cast<const v4u*>(row + (((2 + h) ^ (r & 3)) * 16)));
   };
-  auto slab_scale = [&](int sb, int rb) -> uint32_t {
+  auto x_scale = [&](int s, int rb) -> uint32_t {
     const int r = rb * 32 + (ot & 31), h = (ot >> 5) & 1;
-    return (uint32_t)slabsc[(sb * BM + r) * 2 + h];
+    return (uint32_t)xsc[(s * BM + r) * 2 + h];
   };
   // B operand of GEMM2 k-step kb: U row 32 rb + l32, hidden 64 kb + 16 h32 ..
   // (K-block 0) and 64 kb + 32 + 16 h32 .. (K-block 1); scale of hidden block
@@ -358,10 +405,10 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
     return (uint32_t)usc[(rb * 32 + (ot & 31)) * USC + 2 * kb + ((ot >> 5) & 1)];
   };
 
-  // ---- first tile -----------------------------------------------------------------
+  // ---- first tile: slabs 0..3 quantised, 4 and 5 loading ----------------------
   Tile cur, nx;
   if (tid == 0) claim = atomicAdd(&a.qhead[qx], 1);
-  __syncthreads();
+  __syncthreads();   // also publishes qcum
   if (!qdecode(claim, cur)) return;                  // uniform per workgroup
   __syncthreads();
   if (tid == 0) claim = atomicAdd(&a.qhead[qx], 1);
@@ -374,19 +421,29 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
   bases(nx, ngu, nwd);
   __syncthreads();
   int buf = 0;
-  v4u sv[2][SU];   // slab t waits in register set t % 2
+  v4u sv[2][SU];   // slab s waits in register set s % 2
   slab_rows(cur.p, 0, roff);
   slab_rows(nx.p, 1, roffn);
   ScA sa;
   {
-    v4u s0[SU];
-    slab_load(0, s0);
-    slab_load(1, sv[1]);
-    slab_load(2, sv[0]);
+    v4u t0[SU], t1[SU];
+    slab_load(0, false, sv[0]);
+    slab_load(1, false, sv[1]);
+    slab_load(2, false, t0);
+    slab_load(3, false, t1);
     load_sa(cur, sa);
 #pragma unroll
     for (int f = 0; f < RX_RING; ++f) ring[f] = wload(0, f);
-    slab_store(0, s0);
+#pragma unroll
+    for (int i = 0; i < SU; ++i) quant_unit(0, i, sv[0][i]);
+    slab_load(4, false, sv[0]);
+#pragma unroll
+    for (int i = 0; i < SU; ++i) quant_unit(1, i, sv[1][i]);
+    slab_load(5, false, sv[1]);
+#pragma unroll
+    for (int i = 0; i < SU; ++i) quant_unit(2, i, t0[i]);
+#pragma unroll
+    for (int i = 0; i < SU; ++i) quant_unit(3, i, t1[i]);
   }
   __syncthreads();
 
@@ -396,42 +453,62 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
     uint32_t xs[RX_RB];
 #pragma unroll
     for (int rb = 0; rb < RX_RB; ++rb) {
-      xb[rb] = slab_frag(0, rb);
-      xs[rb] = slab_scale(0, rb);
+      xb[rb] = x_frag(0, rb);
+      xs[rb] = x_scale(0, rb);
     }
     ScB sbs;
-    load_sb(cur, sbs);
 
-    // ---- one slab step of GEMM1 pass PH (0: A, 1: B): slab t = 6 m + K of
-    // the pass (t + NSP in the tile's slab stream for pass B), K % 3 its
-    // buffer. Slab t+1 is quantised into its buffer and slab t+3's loads go
-    // out, then the slab's k-step; the barrier after it makes slab t+1
-    // visible for the next step's operands, which are read row block by row
-    // block, and means every wave is done with slab t-1, whose buffer the
-    // next step fills.
-    auto slab_step = [&](auto ph_tag, auto k_tag, int m, auto& sg, auto& su, const auto& sc)
-        __attribute__((always_inline)) {
-      constexpr int PH = decltype(ph_tag)::value, K = decltype(k_tag)::value;
+    // ---- GEMM1 k-step t of pass PH (slab t; t compile-time). Pass A also
+    // quantises slab t + 4 (one unit per row block, between the MFMAs), whose
+    // register set then loads slab t + 6 (past slab 11: the next tile's slab
+    // t - 6). A barrier after k-steps 2, 5 and 7 publishes the slabs
+    // quantised since the previous one, each read (as the operand of the
+    // k-step before its own) at least one k-step later. The row blocks'
+    // x_hat operands are replaced by the next slab's as soon as their MFMAs
+    // have issued.
+    auto kstep = [&](auto ph_tag, auto t_tag, auto& sg, auto& su, const auto& sc) __attribute__((always_inline)) {
+      constexpr int PH = decltype(ph_tag)::value, t = decltype(t_tag)::value;
       constexpr int F = PH == 0 ? FA : FB;
-      constexpr int sbn = (K + 1) % 3;
-      const int t = (PH == 0 ? 0 : NSP) + 6 * m + K;
-      slab_store(sbn, sv[(K + 1) & 1]);
-      slab_load(t + 3, sv[(K + 1) & 1]);
-      const int kb = 6 * m + K;   // k-step of the pass (compile-time once unrolled)
+      constexpr bool QUANT = PH == 0 && t + RX_QA < NSP;
+      constexpr int QS = t & 1;   // register set of slab t + 4 (and t + 6)
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int rb = 0; rb < RX_RB; ++rb)
+      for (int rb = 0; rb < RX_RB; ++rb) {
 #pragma unroll
         for (int i = 0; i < F; ++i) {
           // the pass's first k-step takes a zero accumulator operand
           f32x16& acc = (i & 1) ? su[rb][i >> 1] : sg[rb][i >> 1];
-          acc = rx_mfma_s(kb & 3, ring[(kb * F + i) % RX_RING], xb[rb], sc.w[i >> 1][i & 1][kb >> 2], xs[rb],
-                          kb == 0 ? f32x16{} : acc);
+          acc = rx_mfma_s(t & 3, ring[(t * F + i) % RX_RING], xb[rb], sc.w[i >> 1][i & 1][t >> 2], xs[rb],
+                          t == 0 ? f32x16{} : acc);
         }
+        if (QUANT) quant_unit(t + RX_QA, rb, sv[QS][rb]);
+        if (t + 1 < NSP) {
+          xb[rb] = x_frag(t + 1, rb);
+          xs[rb] = x_scale(t + 1, rb);
+        }
+      }
+      asm volatile("" : "+s"(zs));
+      if (QUANT) {
+        if (t + 6 < NSP)
+          slab_load(t + 6, false, sv[QS]);
+        else
+          slab_load(t + 6 - NSP, true, sv[QS]);
+      }
+      // GEMM1 B's scales, late enough to leave the quantising k-steps their
+      // registers
+      if (PH == 0 && t == NSP - RX_QA) load_sb(cur, sbs);
 #pragma unroll
       for (int i = 0; i < F; ++i) {
-        const int pos = kb * F + i;
+        const int pos = t * F + i;
         refill(ring[pos % RX_RING], std::integral_constant<int, PH>{}, pos % RX_RING, pos / RX_RING + 1);
+      }
+      // the quantisation's vector ALU work between the MFMAs
+      if (QUANT) {
+#pragma unroll
+        for (int m = 0; m < RX_RB * F; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+        }
       }
       // the k-step's products are taken here: the compiler would otherwise
       // sink the MFMAs (pure operations) down to the accumulators' use after
@@ -440,14 +517,7 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
       for (int rb = 0; rb < RX_RB; ++rb)
 #pragma unroll
         for (int h = 0; h < F / 2; ++h) asm volatile("" : "+a"(sg[rb][h]), "+a"(su[rb][h]));
-      __syncthreads();
-      if (t + 1 < NSL) {
-#pragma unroll
-        for (int rb = 0; rb < RX_RB; ++rb) {
-          xb[rb] = slab_frag(sbn, rb);
-          xs[rb] = slab_scale(sbn, rb);
-        }
-      }
+      if (PH == 0 && (t == 2 || t == 5 || t == NSP - RX_QA - 1)) __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     };
     // U of a pass's hidden blocks (block nb0 + h of the wave) -> LDS: one
@@ -473,53 +543,60 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
           for (int g4 = 0; g4 < 4; ++g4)
             *reinterpret_cast<uint32_t*>(dst + 8 * g4) = rx_e4m3x4(u[4 * g4], u[4 * g4 + 1], u[4 * g4 + 2],
                                                                     u[4 * g4 + 3], sc);
-          if (((ot >> 5) & 1) == 0) usc[row * USC + nb] = (uint8_t)(k + 127);
+          usc[row * USC + nb] = (uint8_t)(k + 127);   // lanes l and l ^ 32 store the same byte
           // one accumulator block at a time: the scheduler would otherwise
           // move every accumulator to VGPRs at once
           __builtin_amdgcn_sched_barrier(0);
         }
     };
+    auto pass = [&](auto ph_tag, auto& sg, auto& su, const auto& sc) __attribute__((always_inline)) {
+      kstep(ph_tag, std::integral_constant<int, 0>{}, sg, su, sc);
+      kstep(ph_tag, std::integral_constant<int, 1>{}, sg, su, sc);
+      kstep(ph_tag, std::integral_constant<int, 2>{}, sg, su, sc);
+      kstep(ph_tag, std::integral_constant<int, 3>{}, sg, su, sc);
+      kstep(ph_tag, std::integral_constant<int, 4>{}, sg, su, sc);
+      kstep(ph_tag, std::integral_constant<int, 5>{}, sg, su, sc);
+      kstep(ph_tag, std::integral_constant<int, 6>{}, sg, su, sc);
+      kstep(ph_tag, std::integral_constant<int, 7>{}, sg, su, sc);
+      kstep(ph_tag, std::integral_constant<int, 8>{}, sg, su, sc);
+      kstep(ph_tag, std::integral_constant<int, 9>{}, sg, su, sc);
+      kstep(ph_tag, std::integral_constant<int, 10>{}, sg, su, sc);
+      kstep(ph_tag, std::integral_constant<int, 11>{}, sg, su, sc);
+    };
 
     // ================= GEMM1 pass A =================
     {
       f32x16 sg[RX_RB][HA], su[RX_RB][HA];
+      pass(std::integral_constant<int, 0>{}, sg, su, sa);
+      // pass B starts on slab 0 again
 #pragma unroll
-      for (int m = 0; m < NSP / 6; ++m) {
-        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, m, sg, su, sa);
-        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, m, sg, su, sa);
-        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, m, sg, su, sa);
-        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{}, m, sg, su, sa);
-        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 4>{}, m, sg, su, sa);
-        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 5>{}, m, sg, su, sa);
+      for (int rb = 0; rb < RX_RB; ++rb) {
+        xb[rb] = x_frag(0, rb);
+        xs[rb] = x_scale(0, rb);
       }
       store_u(HA * wave, sg, su, std::integral_constant<int, HA>{});
     }
     ScC scc;
     load_sc(cur, 0, scc);
-    // ================= GEMM1 pass B =================
+    // ================= GEMM1 pass B (x_hat from LDS only) =================
     fresh();
     {
       f32x16 sg[RX_RB][HBB], su[RX_RB][HBB];
-#pragma unroll
-      for (int m = 0; m < NSP / 6; ++m) {
-        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, m, sg, su, sbs);
-        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, m, sg, su, sbs);
-        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{}, m, sg, su, sbs);
-        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 3>{}, m, sg, su, sbs);
-        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 4>{}, m, sg, su, sbs);
-        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 5>{}, m, sg, su, sbs);
-      }
+      pass(std::integral_constant<int, 1>{}, sg, su, sbs);
       store_u(4 * HA + HBB * wave, sg, su, std::integral_constant<int, HBB>{});
     }
-    __syncthreads();   // U complete
+    __syncthreads();   // U complete; every wave is done with the x_hat copy
 
     // the claim of the tile after next goes out now (read after the epilogue)
     int qnext = 0;
     if (tid == 0) qnext = atomicAdd(&a.qhead[qx], 1);
 
     // ================= GEMM2 parts, each with its epilogue =================
+    // The parts also quantise the next tile's slabs 0..3 into the x_hat copy
+    // (one unit per k-step; part 0 takes slabs 0 and 1), each register set
+    // then loading the next tile's slab two further on.
     auto gemm2_part = [&](auto ph_tag, f32x16 (&o)[RX_RB][FC], const ScC& s) __attribute__((always_inline)) {
-      constexpr int PH = decltype(ph_tag)::value;
+      constexpr int PH = decltype(ph_tag)::value, C = PH - 2;
       i32x8 ub[RX_RB];
       uint32_t uss[RX_RB];
 #pragma unroll
@@ -544,6 +621,22 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
           ub[rb] = u_frag(rb, kn);
           uss[rb] = u_scale(rb, kn);
         }
+        // slab qs = C + (C > 0) from register set qs % 2, units kb (parts 1,
+        // 2) or, in part 0, slab 0 over k-steps 0..3 and slab 1 over 4, 5
+        asm volatile("" : "+s"(zs));
+        if (C == 0) {
+          if (kb < SU) quant_unit(0, kb, sv[0][kb]);
+          if (kb == SU - 1) slab_load(2, true, sv[0]);
+          if (kb >= SU) {
+            quant_unit(1, 2 * (kb - SU), sv[1][2 * (kb - SU)]);
+            quant_unit(1, 2 * (kb - SU) + 1, sv[1][2 * (kb - SU) + 1]);
+          }
+          if (kb == KB2 - 1) slab_load(3, true, sv[1]);
+        } else {
+          constexpr int QS = C + 1;   // slabs 2 (part 1), 3 (part 2)
+          if (kb < SU) quant_unit(QS, kb, sv[QS & 1][kb]);
+          if (kb == SU - 1) slab_load(QS + 2, true, sv[QS & 1]);
+        }
 #pragma unroll
         for (int j = 0; j < FC; ++j) {
           const int pos = kb * FC + j;
@@ -557,11 +650,12 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    // gate * O of row block rb -> staging rows (stride HS)
+    // gate * O of row block rb -> staging rows
     auto stage_rb = [&](int rb, f32x16 (&o)[RX_RB][FC]) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < FC; ++j) asm volatile("" : "+a"(o[rb][j]));
-      const float g = rowg[buf][rb * 32 + (ot & 31)];
+      const int row = rb * 32 + (ot & 31);
+      const float g = rowg[buf][row];
 #pragma unroll
       for (int j = 0; j < FC; ++j)
 #pragma unroll
@@ -569,7 +663,7 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
           uint2 w2;
           w2.x = pack_bf16x2(g * o[rb][j][4 * g4], g * o[rb][j][4 * g4 + 1]);
           w2.y = pack_bf16x2(g * o[rb][j][4 * g4 + 2], g * o[rb][j][4 * g4 + 3]);
-          *reinterpret_cast<uint2*>(&stg[(ot & 31) * HS + (2 * wave + j) * 32 + 8 * g4 + 4 * ((ot >> 5) & 1)]) = w2;
+          *reinterpret_cast<uint2*>(&stg[row * HS + (2 * wave + j) * 32 + 8 * g4 + 4 * ((ot >> 5) & 1)]) = w2;
           __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -584,7 +678,7 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
 #pragma unroll
       for (int k = 0; k < NU; ++k) {
         const int u = ot + k * RX_NT, r = u / U8P, c8 = u - r * U8P, row = row0 + r;
-        v[k] = *reinterpret_cast<const v4u*>(&stg[r * HS + c8 * 8]);
+        v[k] = *reinterpret_cast<const v4u*>(&stg[row * HS + c8 * 8]);
         ok[k] = rowb[buf][row] >= 0;
         gi[k] = rowgi[buf][row];
         c8s[k] = c8;
@@ -601,12 +695,11 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
       gemm2_part(ph_tag, o, s);
       fresh();
 #pragma unroll
-      for (int rb = 0; rb < RX_RB; ++rb) {
-        stage_rb(rb, o);
-        __syncthreads();
-        store_rows(rb * 32, PH - 2);
-        __syncthreads();
-      }
+      for (int rb = 0; rb < RX_RB; ++rb) stage_rb(rb, o);
+      __syncthreads();
+#pragma unroll
+      for (int rb = 0; rb < RX_RB; ++rb) store_rows(rb * 32, PH - 2);
+      __syncthreads();
     };
     {
       ScC s1;
