@@ -181,15 +181,18 @@ def moe_kernel_work(wl):
     """Algorithmic work per launch of each MoE kernel, as (bound, amount):
     FLOPs for the GEMM kernels (2 per multiply-add; the top_k chosen experts
     of every row for the routed launch, the shared expert for the other), HBM
-    bytes for the router (rows read, normalised rows written, routing table
-    written, router weights read) and the bucket kernel (routing table read,
-    row lists written). P * W = T * D in both sub-layers; P averages H and T."""
+    bytes for the router (rows read, normalised rows written -- bf16, or for
+    MXFP8 one code byte per element and one exponent byte per 32 -- routing
+    table written, router weights read) and the bucket kernel (routing table
+    read, row lists written). P * W = T * D in both sub-layers; P averages H
+    and T."""
     TD = wl.T * wl.D
     P = (wl.H + wl.T) / 2.0
+    xhat_bytes = TD * (33.0 / 32.0) if wl.dtype == "mxfp8" else TD * 2.0
     return {
         "mlp_routed": ("mfma", 2.0 * wl.B * wl.top_k * TD * 3 * wl.expert_hidden),
         "mlp_shared": ("mfma", 2.0 * wl.B * TD * 3 * wl.shared_hidden),
-        "router": ("hbm", 2.0 * wl.B * TD * 2 + wl.B * P * wl.top_k * 8 + TD * wl.E * 2),
+        "router": ("hbm", wl.B * (TD * 2.0 + xhat_bytes) + wl.B * P * wl.top_k * 8 + TD * wl.E * 2),
         "bucket": ("hbm", wl.B * P * wl.top_k * 8.0),
     }
 

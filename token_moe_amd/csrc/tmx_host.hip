@@ -68,6 +68,9 @@ struct MoeWs {
   int* qhead = nullptr;       // [8] routed-MLP tile queues (zeroed by the bucket kernel)
   int* hist = nullptr;        // [P][ceil(B/64)][E] router choices per 64-row chunk
   uint16_t* part = nullptr;   // [B][P][k][W] gated expert outputs, bf16
+  uint8_t* xq8 = nullptr;     // MXFP8 MoE only: x_hat's E4M3 codes [P][B][W], then
+                              // its exponents [P][B][W/32] (the router's output
+                              // that the expert kernels read instead of xhat)
 };
 
 }  // namespace
@@ -388,11 +391,13 @@ int moe_max_tiles(const tmx_config& c, int sub, int B) {
 // returns the bytes used. Every array starts on a 256-byte boundary.
 size_t carve_moe_ws(const tmx_config& C, int64_t B, void* base, MoeWs* ws) {
   const int Pmax = std::max(C.H, C.T);
-  int64_t tiles = 0, xh = 0, part = 0;
+  int64_t tiles = 0, xh = 0, part = 0, xq = 0;
   for (int sub = 0; sub < 2; ++sub) {
     tiles = std::max<int64_t>(tiles, (int64_t)positions(C, sub) * moe_max_tiles(C, sub, (int)B));
     xh = std::max<int64_t>(xh, (int64_t)positions(C, sub) * B * width(C, sub));
     part = std::max<int64_t>(part, (int64_t)positions(C, sub) * B * C.top_k * width(C, sub));
+    if (C.E > 0 && C.dtype == TMX_MXFP8)
+      xq = std::max<int64_t>(xq, (int64_t)positions(C, sub) * B * width(C, sub) / 32 * 33);
   }
   const int64_t rk = B * Pmax * C.top_k;
   size_t off = 0;
@@ -412,6 +417,7 @@ size_t carve_moe_ws(const tmx_config& C, int64_t B, void* base, MoeWs* ws) {
   w.qhead = static_cast<int*>(take(8 * 4));
   w.hist = static_cast<int*>(take((int64_t)Pmax * ((B + 63) / 64) * C.E * 4));
   w.part = static_cast<uint16_t*>(take(part * 2));
+  w.xq8 = xq ? static_cast<uint8_t*>(take(xq)) : nullptr;
   if (ws) *ws = w;
   return off;
 }
@@ -527,6 +533,11 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   r.x = static_cast<const uint16_t*>(x_in); r.gain = gain;
   r.wr = static_cast<const uint16_t*>(bank(c, layer, sub, TMX_W_ROUTER).ptr);
   r.xhat = ws.xhat; r.idx = ws.idx; r.gate = ws.gate; r.hist = ws.hist;
+  if (mx) {   // the expert kernels read x_hat in MXFP8 only
+    r.xhat = nullptr;
+    r.xq8 = ws.xq8;
+    r.xe8 = ws.xq8 + (size_t)P * B * W;
+  }
   tmx_status s = launch_timed(c, TMX_KERNEL_ROUTER, st, "router launch", [&] { return launch_norm_route(W, r, st); });
   if (s != TMX_OK) return s;
 
@@ -537,7 +548,8 @@ tmx_status run_sublayer(tmx_ctx* c, int layer, int sub, const void* x_in, const 
   s = launch_timed(c, TMX_KERNEL_BUCKET, st, "bucket launch", [&] { return launch_bucket(k, st); });
   if (s != TMX_OK) return s;
 
-  a.xhat = ws.xhat; a.top_k = cfg.top_k; a.E = cfg.E; a.max_tiles = k.max_tiles;
+  a.xhat = mx ? nullptr : ws.xhat; a.top_k = cfg.top_k; a.E = cfg.E; a.max_tiles = k.max_tiles;
+  a.xq8 = r.xq8; a.xe8 = r.xe8;
   a.rows = ws.rows; a.tiles = ws.tiles; a.ntiles = ws.ntiles; a.gate = ws.gate; a.part = ws.part;
   a.qhead = ws.qhead;
   a.hidden = cfg.expert_hidden;

@@ -30,6 +30,8 @@ struct MlpArgs {
   const uint16_t* x;       // DENSE source, [B, T, D]
   const float* gain;       // DENSE: RMSNorm gain [W]
   const uint16_t* xhat;    // ROUTED / SHARED source, [P][B][W]
+  const uint8_t* xq8;      // the MXFP8 wide routed kernel's source: x_hat in MXFP8
+  const uint8_t* xe8;      // (RouteArgs::xq8, xe8)
   const uint16_t* wgu;     // packed gate|up fragments
   const uint16_t* wd;      // packed down fragments
   const uint16_t* resid;   // DENSE / SHARED
@@ -63,6 +65,8 @@ struct RouteArgs {
   const float* gain;       // [W]
   const uint16_t* wr;      // packed router fragments
   uint16_t* xhat;          // [P][B][W] (nullable)
+  uint8_t* xq8;            // nullable: x_hat in MXFP8, E4M3 codes [P][B][W] ...
+  uint8_t* xe8;            // ... and exponents [P][B][W/32] (bias 127), one per 32 columns
   int32_t* idx;            // [B][P][top_k]
   float* gate;             // [B][P][top_k]
   int* hist;               // nullable: [P][ceil(B/64)][E] choices per 64-row chunk

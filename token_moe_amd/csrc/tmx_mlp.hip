@@ -184,8 +184,9 @@ enum { RV_PLAIN = 0, RV_EXTRA = 1, RV_MIX = 2 };
 // F8: the 4-wave kernels with MXFP8 GEMM operands -- dense W = 256 (two
 // workgroups per CU), every mode at W = 512, the MoE modes at W = 768 (one)
 // -- weights packed at load
-// (launch_pack_mx), x_hat and U quantised here per row and 32-element block
-// along each GEMM's contraction axis.
+// (launch_pack_mx), U and the DENSE rows quantised here per row and
+// 32-element block along each GEMM's contraction axis; the MoE modes read
+// the router's MXFP8 copy of x_hat (MlpArgs::xq8, xe8).
 template <int W, int MODE, int NW, int OCC, int RV, bool F8>
 __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   constexpr bool RESX = RV == RV_MIX, EXTRA = RV == RV_EXTRA;
@@ -565,6 +566,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
         const int p = rowpos(T, r);
         if (MODE == MLP_DENSE) {
           v[i0 + k] = ldg16(a.x + uoff(b, p, c8));
+        } else if (F8) {
+          // the router's MXFP8 copy of the row: 8 E4M3 codes, and the
+          // exponent of their 32-column block (every lane of the block loads it)
+          const uint32_t row8 = (uint32_t)p * (uint32_t)a.B + (uint32_t)b;
+          const uint2 cq = *reinterpret_cast<const uint2*>(a.xq8 + row8 * (uint32_t)W + (uint32_t)c8 * 8u);
+          v[i0 + k] = make_uint4(cq.x, cq.y, (uint32_t)a.xe8[row8 * (uint32_t)(W / 32) + (uint32_t)(c8 >> 2)], 0u);
         } else {
           // 32-bit byte offset from the x_hat base (the host keeps that
           // buffer under 4 GiB): one address register per load, which keeps
@@ -586,15 +593,24 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
   auto store_x = [&](int tix, uint4* v, const float* lgain) {
     if constexpr (F8) {
       // DENSE: RMSNorm in fp32 (the row's U8 units sit in U8 consecutive
-      // lanes); ROUTED / SHARED rows arrive normalised. Then MXFP8 per
-      // 32-column block: the block's 4 units sit in 4 consecutive lanes
-      // (units are numbered row by row, and NT and U8 are multiples of 4).
+      // lanes), then MXFP8 per 32-column block: the block's 4 units sit in 4
+      // consecutive lanes (units are numbered row by row, and NT and U8 are
+      // multiples of 4). ROUTED / SHARED rows arrive normalised and
+      // quantised the same way by the router.
       static_assert(!F8 || (MODE == MLP_DENSE ? (LANE_COL && (U8 == 32 || U8 == 64)) : (U8 % 4 == 0 && NT % 4 == 0)),
                     "F8 row layout");
 #pragma unroll
       for (int i = 0; i < NPRO; ++i) {
         int r, c8;
         unit_rc(tix, i, r, c8);
+        const int blk = c8 >> 2, st = blk >> 1;
+        uint8_t* const scl = &xsc8[r * XSCB + ((st >> 2) * 2 + (blk & 1)) * 4 + (st & 3)];
+        if constexpr (MODE != MLP_DENSE) {
+          // quantised by the router: codes in .x, .y, the block exponent in .z
+          *reinterpret_cast<uint2*>(&xs8[r * XSB + c8 * 8]) = make_uint2(v[i].x, v[i].y);
+          if ((c8 & 3) == 0) *scl = (uint8_t)v[i].z;
+          continue;
+        }
         const uint16_t* h = reinterpret_cast<const uint16_t*>(&v[i]);
         float n[8], am = 0.f;
         if constexpr (MODE == MLP_DENSE) {
@@ -623,8 +639,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void mlp_kernel(const MlpArgs a) {
         q.x = e4m3x4(n[0], n[1], n[2], n[3], sc);
         q.y = e4m3x4(n[4], n[5], n[6], n[7], sc);
         *reinterpret_cast<uint2*>(&xs8[r * XSB + c8 * 8]) = q;
-        const int blk = c8 >> 2, st = blk >> 1;
-        if ((c8 & 3) == 0) xsc8[r * XSCB + ((st >> 2) * 2 + (blk & 1)) * 4 + (st & 3)] = (uint8_t)(k + 127);
+        if ((c8 & 3) == 0) *scl = (uint8_t)(k + 127);
       }
       __syncthreads();
       return;

@@ -74,6 +74,33 @@ __device__ __forceinline__ void row16_argmax(float& bv, int& be) {
   argmax_step<DPP_MIRROR>(bv, be);
 }
 
+// E4M3 codes of the 8 bf16 values in w times 2^-k (exact), clamped to +-448
+// first (the conversion rounds to nearest even but does not saturate)
+__device__ __forceinline__ uint32_t e4m3x4_bf16(uint32_t v0, uint32_t v1, float sc) {
+  const float x0 = fminf(fmaxf(__uint_as_float(v0 << 16) * sc, -448.f), 448.f);
+  const float x1 = fminf(fmaxf(__uint_as_float(v0 & 0xFFFF0000u) * sc, -448.f), 448.f);
+  const float x2 = fminf(fmaxf(__uint_as_float(v1 << 16) * sc, -448.f), 448.f);
+  const float x3 = fminf(fmaxf(__uint_as_float(v1 & 0xFFFF0000u) * sc, -448.f), 448.f);
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+}
+__device__ __forceinline__ uint2 e4m3x8_bf16(const uint4& w, float sc) {
+  return make_uint2(e4m3x4_bf16(w.x, w.y, sc), e4m3x4_bf16(w.z, w.w, sc));
+}
+// largest magnitude among the 8 bf16 values of w, as its bf16 bit pattern
+// (magnitudes order as their 15-bit patterns)
+__device__ __forceinline__ uint32_t bf16x8_absmax_bits(const uint4& w) {
+  const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = v[i] & 0x7FFFu, hi = (v[i] >> 16) & 0x7FFFu;
+    m = m > lo ? m : lo;
+    m = m > hi ? m : hi;
+  }
+  return m;
+}
+
 template <int W, int NBE>
 __global__ __launch_bounds__(64 * RT_WAVES) void norm_route_kernel(const RouteArgs a) {
   constexpr int KB = W / 32;
@@ -137,6 +164,9 @@ __global__ __launch_bounds__(64 * RT_WAVES) void norm_route_kernel(const RouteAr
 #pragma unroll
   for (int j = 0; j < NBE; ++j) lg[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint16_t* wr = wr_s + lane * 8;
+  // MXFP8 copy of the rows (xq8): exponent bytes of the row's 32-column
+  // blocks, packed 4 to a dword (every lane of the row holds all of them)
+  uint32_t eb[KB / 4] = {};
 
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
@@ -154,10 +184,35 @@ __global__ __launch_bounds__(64 * RT_WAVES) void norm_route_kernel(const RouteAr
     xr[kb].w = pack_bf16x2(n[6], n[7]);
     if (valid && a.xhat)
       *reinterpret_cast<uint4*>(a.xhat + ((size_t)p * a.B + row) * W + kb * 32 + q * 8) = xr[kb];
+    if (a.xq8) {
+      // the bf16 row quantised per 32-column block (this lane's 8 columns and
+      // those of lanes ^ 16, ^ 32, ^ 48): exponent floor(log2(amax)) - 8
+      uint32_t mb = bf16x8_absmax_bits(xr[kb]);
+      const uint32_t m16 = (uint32_t)__shfl_xor((int)mb, 16, 64);
+      mb = mb > m16 ? mb : m16;
+      const uint32_t m32 = (uint32_t)__shfl_xor((int)mb, 32, 64);
+      mb = mb > m32 ? mb : m32;
+      const float amax = __uint_as_float(mb << 16);
+      int e = 0;
+      (void)frexpf(amax, &e);
+      int k = amax > 0.f ? e - 9 : -127;
+      k = k < -127 ? -127 : (k > 127 ? 127 : k);
+      const uint2 c = e4m3x8_bf16(xr[kb], ldexpf(1.f, -k));
+      if (valid) *reinterpret_cast<uint2*>(a.xq8 + ((size_t)p * a.B + row) * W + kb * 32 + q * 8) = c;
+      eb[kb / 4] |= (uint32_t)(k + 127) << (8 * (kb % 4));
+    }
     const bf16x8 af = as_bf16x8(xr[kb]);
 #pragma unroll
     for (int j = 0; j < NBE; ++j)
       lg[j] = mfma16x16x32(af, as_bf16x8(*reinterpret_cast<const uint4*>(wr + (kb * NBE + j) * FRAG_ELEMS)), lg[j]);
+  }
+
+  if (a.xq8 && valid) {
+    static_assert(KB % 4 == 0, "exponent dwords");
+    uint32_t* er = reinterpret_cast<uint32_t*>(a.xe8 + ((size_t)p * a.B + row) * KB);
+#pragma unroll
+    for (int d = 0; d < KB / 4; ++d)
+      if ((d & 3) == q) er[d] = eb[d];
   }
 
   // Softmax and top-k per row. C layout: lane (l16, q) holds the logits of

@@ -19,13 +19,15 @@
 //            wave), c = 0, 1, 2, each followed by gate * O -> bf16, staged in
 //            LDS and written as whole 16-byte units.
 //
-// x_hat is quantised to E4M3 once per tile, into an LDS copy of the whole
-// tile (128 x 768 codes, 96 KiB) that both GEMM1 passes read: GEMM1 B runs
-// from LDS alone. The quantisation runs 4 slabs ahead of the MFMAs that use
-// it, spread over the MFMAs of GEMM1 A (slabs 4..11) and of the previous
-// tile's GEMM2 parts (slabs 0..3); the global loads run 2 slabs ahead of the
-// quantisation. During the GEMM2 parts, slabs 4..11 of the copy hold the
-// epilogue's staging rows.
+// x_hat arrives quantised: the router writes an MXFP8 copy of its rows (E4M3
+// codes and one exponent per 32 columns, the same quantisation as every
+// other MXFP8 GEMM operand here), which this kernel gathers into an LDS copy
+// of the whole tile (128 x 768 codes, 96 KiB) that both GEMM1 passes read:
+// GEMM1 B runs from LDS alone. Slabs are copied into LDS 4 slabs ahead of
+// the MFMAs that use them, during GEMM1 A (slabs 4..11) and the previous
+// tile's GEMM2 parts (slabs 0..3); their global loads run 4 slabs ahead of
+// the copy (four register sets of 32 bytes per lane). During the GEMM2
+// parts, slabs 4..11 of the copy hold the epilogue's staging rows.
 //
 // The weights come from the MXFP8 packing of load time (launch_pack_mx):
 // 2 KiB fragments, and per-lane scale records in the layout the fused MLP
@@ -48,7 +50,8 @@ constexpr int RX_RB = 4;     // 32-row blocks per tile
 constexpr int RX_BM = 32 * RX_RB;
 constexpr int RX_SC = 64;    // columns per x_hat slab: one fp8 MFMA k-step
 constexpr int RX_RING = 12;  // weight fragments in flight per wave
-constexpr int RX_QA = 4;     // slabs between a slab's quantisation and its MFMAs
+constexpr int RX_QA = 4;     // slabs between a slab's copy into LDS and its MFMAs
+constexpr int RX_SETS = 4;   // register sets of slab loads in flight (slab s in set s % 4)
 constexpr int RX_QMAX = 64;  // positions per tile queue whose tile counts sit in LDS
 constexpr int RX_RSRC_W3 = 0x00020000;   // buffer resource word 3: raw 32-bit data, no swizzle
 
@@ -94,17 +97,6 @@ __device__ __forceinline__ int rx_exp(float amax) {
   const int k = amax > 0.f ? e - 9 : -127;
   return k < -127 ? -127 : (k > 127 ? 127 : k);
 }
-// largest x of the 4 lanes of a quad (DPP quad permutations: lane ^ 1, then
-// lane ^ 2)
-__device__ __forceinline__ uint32_t rx_quad_maxu(uint32_t x) {
-  uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);
-  x = x > y ? x : y;
-  y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);
-  return x > y ? x : y;
-}
-// the magnitude bits of two bf16 values
-typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ us2 rx_mag2(uint32_t w) { return __builtin_bit_cast(us2, w & 0x7FFF7FFFu); }
 
 __device__ __forceinline__ float rx_silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
@@ -121,19 +113,21 @@ struct RxShape {
   static constexpr int USB = HE + 16;             // U row stride (bytes)
   static constexpr int USC = HE / 32;             // U scale bytes per row
   static constexpr int XSL = BM * RX_SC;          // code bytes per slab of the x_hat copy
-  static constexpr int SU = BM * RX_SC / 8 / RX_NT;   // 16-byte bf16 units of a slab per lane
+  static constexpr int SU = BM * RX_SC / 16 / RX_NT;  // 16-byte code units of a slab per lane
+  static constexpr int XE = W / 32;               // exponent bytes per x_hat row
   static constexpr int HS = 256 + 8;              // staged part-row stride (bf16)
   // LDS: x_hat codes [slab][row][64] (slabs RX_QA.. and a pad after them
-  // double as the staging rows [128][HS]), x_hat exponents [slab][row][2],
+  // double as the staging rows [128][HS]), x_hat exponents [row][XE],
   // U [row][USB], U exponents [row][hidden block]
   static constexpr int STG_PAD = BM * HS * 2 > (NSP - RX_QA) * XSL ? BM * HS * 2 - (NSP - RX_QA) * XSL : 0;
   static constexpr int OFF_XSC = NSP * XSL + STG_PAD;
-  static constexpr int OFF_US = OFF_XSC + NSP * BM * 2;
+  static constexpr int OFF_US = OFF_XSC + BM * XE;
   static constexpr int OFF_USC = OFF_US + BM * USB;
   static constexpr int LDS_BYTES = OFF_USC + BM * USC;
   static_assert(W == 768 && HE == 384, "the MXFP8 wide routed kernel is built for W 768, h_e 384");
-  static_assert(HBB == 1 && NSP == 12 && SU == RX_RB && KB2 >= SU + 2,
-                "pass shapes: slab units are quantised one per row block or GEMM2 k-step");
+  static_assert(HBB == 1 && NSP == 12 && SU == 2 && NSP - RX_QA == 2 * RX_SETS && XE % 4 == 0 &&
+                BM * XE / 4 == 3 * RX_NT,
+                "pass shapes: slab pipeline and exponent rows as laid out below");
   static_assert((W / 128) % 2 == 0, "GEMM2 scale byte: a down block's index among its record's blocks has j's parity");
   static_assert(LA % RX_RING == 0 && LB % RX_RING == 0 && LC % RX_RING == 0 && RX_RING % FA == 0 &&
                 RX_RING % FB == 0 && RX_RING % FC == 0,
@@ -338,49 +332,52 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
     }
   };
 
-  // ---- x_hat slabs: unit u = tid + 256 i of a slab is row u / 8, 8-column
-  // chunk u % 8 of the slab's 64 columns (bf16 in memory). A slab is stored
-  // quantised: 64 code bytes per row, 16-byte chunk k of a row at chunk k ^
-  // (row % 4) (the fragment reads of 4 consecutive rows hit different bank
-  // groups), and the row's two 32-column block exponents.
-  // byte offsets of this lane's slab units in x_hat, for this tile (roff)
-  // and the next (roffn; rows of padding read sample row 0)
+  // ---- x_hat slabs, from the router's MXFP8 copy of x_hat (E4M3 codes
+  // [P][B][W], exponents [P][B][W/32]): unit u = tid + 256 i of a slab is row
+  // u / 4, 16-column chunk u % 4 of the slab's 64 columns. In LDS a row's
+  // chunk k sits at chunk k ^ (row % 4) (the fragment reads of 4 consecutive
+  // rows hit different bank groups); the tile's exponents are copied whole,
+  // [row][W/32].
+  // byte offsets of this lane's slab units in the codes, for this tile
+  // (roff) and the next (roffn; rows of padding read sample row 0)
   uint32_t roff[SU], roffn[SU];
   auto slab_rows = [&](int p, int tb, uint32_t* ro) {
 #pragma unroll
     for (int i = 0; i < SU; ++i) {
       const int u = ot + i * RX_NT;
-      const int b = rowb[tb][u >> 3];
-      ro[i] = (((uint32_t)p * (uint32_t)a.B + (uint32_t)(b < 0 ? 0 : b)) * (uint32_t)W + (uint32_t)(u & 7) * 8u) * 2u;
+      const int b = rowb[tb][u >> 2];
+      ro[i] = ((uint32_t)p * (uint32_t)a.B + (uint32_t)(b < 0 ? 0 : b)) * (uint32_t)W + (uint32_t)(u & 3) * 16u;
     }
   };
-  const __amdgpu_buffer_rsrc_t xr = rsrc(a.xhat, (uint32_t)((uint64_t)a.P * a.B * W * 2));
+  const __amdgpu_buffer_rsrc_t xr = rsrc(a.xq8, (uint32_t)((uint64_t)a.P * a.B * W));
+  const __amdgpu_buffer_rsrc_t er = rsrc(a.xe8, (uint32_t)((uint64_t)a.P * a.B * S::XE));
   // slab s of this tile (nxt: of the next tile)
   auto slab_load = [&](int s, bool nxt, v4u* v) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < SU; ++i)
-      v[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, nxt ? roffn[i] : roff[i], s * RX_SC * 2, 0);
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, nxt ? roffn[i] : roff[i], s * RX_SC, 0);
   };
-  // quantise and store unit i of slab s: the 4 units of a 32-column block are
-  // the 4 lanes of a quad (u % 8 = 4k .. 4k + 3 of one row)
-  auto quant_unit = [&](int s, int i, const v4u& v) __attribute__((always_inline)) {
-    const int u = ot + i * RX_NT, r = u >> 3, c8 = u & 7;
-    // largest magnitude of the 8 bf16 values: magnitudes order as their
-    // 15-bit patterns
-    const us2 m2 = __builtin_elementwise_max(__builtin_elementwise_max(rx_mag2(v.x), rx_mag2(v.y)),
-                                             __builtin_elementwise_max(rx_mag2(v.z), rx_mag2(v.w)));
-    const uint32_t mb = rx_quad_maxu(m2.x > m2.y ? (uint32_t)m2.x : (uint32_t)m2.y);
-    const int k = rx_exp(__uint_as_float(mb << 16));
-    const float sc = ldexpf(1.f, -k);
-    uint2 q;
-    q.x = rx_e4m3x4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u), __uint_as_float(v.y << 16),
-                    __uint_as_float(v.y & 0xFFFF0000u), sc);
-    q.y = rx_e4m3x4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u), __uint_as_float(v.w << 16),
-                    __uint_as_float(v.w & 0xFFFF0000u), sc);
-    *reinterpret_cast<uint2*>(&xq[s * XSL + r * RX_SC + (((c8 >> 1) ^ (r & 3)) * 16) + (c8 & 1) * 8]) = q;
-    // every lane of the quad stores the (same) exponent: no branch, so the
-    // scheduler may spread the quantisation between MFMAs
-    xsc[(s * BM + r) * 2 + (c8 >> 2)] = (uint8_t)(k + 127);
+  auto slab_store = [&](int s, const v4u* v) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < SU; ++i) {
+      const int u = ot + i * RX_NT, r = u >> 2;
+      *reinterpret_cast<v4u*>(&xq[s * XSL + r * RX_SC + (((u & 3) ^ (r & 3)) * 16)]) = v[i];
+    }
+  };
+  // the exponents of the tile at position p with row table tb: dword d =
+  // tid + 256 j of the tile's [128][XE] bytes
+  auto exp_load = [&](int p, int tb, uint32_t* e) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int d = ot + j * RX_NT, r = d / (S::XE / 4);
+      const int b = rowb[tb][r];
+      e[j] = __builtin_amdgcn_raw_buffer_load_b32(
+          er, ((uint32_t)p * (uint32_t)a.B + (uint32_t)(b < 0 ? 0 : b)) * (uint32_t)S::XE, (d - r * (S::XE / 4)) * 4, 0);
+    }
+  };
+  auto exp_store = [&](const uint32_t* e) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) reinterpret_cast<uint32_t*>(xsc)[ot + j * RX_NT] = e[j];
   };
   // B operand of row block rb from slab s: row 32 rb + l32, bytes 16 h32 ..
   // of K-block 0 and 32 + 16 h32 .. of K-block 1; its exponent in byte 0
@@ -392,7 +389,7 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
   };
   auto x_scale = [&](int s, int rb) -> uint32_t {
     const int r = rb * 32 + (ot & 31), h = (ot >> 5) & 1;
-    return (uint32_t)xsc[(s * BM + r) * 2 + h];
+    return (uint32_t)xsc[r * S::XE + 2 * s + h];
   };
   // B operand of GEMM2 k-step kb: U row 32 rb + l32, hidden 64 kb + 16 h32 ..
   // (K-block 0) and 64 kb + 32 + 16 h32 .. (K-block 1); scale of hidden block
@@ -405,7 +402,7 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
     return (uint32_t)usc[(rb * 32 + (ot & 31)) * USC + 2 * kb + ((ot >> 5) & 1)];
   };
 
-  // ---- first tile: slabs 0..3 quantised, 4 and 5 loading ----------------------
+  // ---- first tile: slabs 0..3 and the exponents in LDS, 4..7 loading ---------
   Tile cur, nx;
   if (tid == 0) claim = atomicAdd(&a.qhead[qx], 1);
   __syncthreads();   // also publishes qcum
@@ -421,29 +418,24 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
   bases(nx, ngu, nwd);
   __syncthreads();
   int buf = 0;
-  v4u sv[2][SU];   // slab s waits in register set s % 2
+  v4u sv[RX_SETS][SU];   // slab s waits in register set s % 4
   slab_rows(cur.p, 0, roff);
   slab_rows(nx.p, 1, roffn);
   ScA sa;
   {
-    v4u t0[SU], t1[SU];
-    slab_load(0, false, sv[0]);
-    slab_load(1, false, sv[1]);
-    slab_load(2, false, t0);
-    slab_load(3, false, t1);
+    uint32_t e[3];
+#pragma unroll
+    for (int k = 0; k < RX_SETS; ++k) slab_load(k, false, sv[k]);
+    exp_load(cur.p, 0, e);
     load_sa(cur, sa);
 #pragma unroll
     for (int f = 0; f < RX_RING; ++f) ring[f] = wload(0, f);
 #pragma unroll
-    for (int i = 0; i < SU; ++i) quant_unit(0, i, sv[0][i]);
-    slab_load(4, false, sv[0]);
-#pragma unroll
-    for (int i = 0; i < SU; ++i) quant_unit(1, i, sv[1][i]);
-    slab_load(5, false, sv[1]);
-#pragma unroll
-    for (int i = 0; i < SU; ++i) quant_unit(2, i, t0[i]);
-#pragma unroll
-    for (int i = 0; i < SU; ++i) quant_unit(3, i, t1[i]);
+    for (int k = 0; k < RX_SETS; ++k) {
+      slab_store(k, sv[k]);
+      slab_load(k + RX_SETS, false, sv[k]);
+    }
+    exp_store(e);
   }
   __syncthreads();
 
@@ -459,18 +451,17 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
     ScB sbs;
 
     // ---- GEMM1 k-step t of pass PH (slab t; t compile-time). Pass A also
-    // quantises slab t + 4 (one unit per row block, between the MFMAs), whose
-    // register set then loads slab t + 6 (past slab 11: the next tile's slab
-    // t - 6). A barrier after k-steps 2, 5 and 7 publishes the slabs
-    // quantised since the previous one, each read (as the operand of the
-    // k-step before its own) at least one k-step later. The row blocks'
-    // x_hat operands are replaced by the next slab's as soon as their MFMAs
-    // have issued.
+    // copies slab t + 4 from register set t % 4 into LDS, and that set then
+    // loads slab t + 8 (past slab 11: the next tile's slab t - 4). A barrier
+    // after k-steps 2, 5 and 7 publishes the slabs copied since the previous
+    // one, each read (as the operand of the k-step before its own) at least
+    // one k-step later. The row blocks' x_hat operands are replaced by the
+    // next slab's as soon as their MFMAs have issued.
     auto kstep = [&](auto ph_tag, auto t_tag, auto& sg, auto& su, const auto& sc) __attribute__((always_inline)) {
       constexpr int PH = decltype(ph_tag)::value, t = decltype(t_tag)::value;
       constexpr int F = PH == 0 ? FA : FB;
-      constexpr bool QUANT = PH == 0 && t + RX_QA < NSP;
-      constexpr int QS = t & 1;   // register set of slab t + 4 (and t + 6)
+      constexpr bool COPY = PH == 0 && t + RX_QA < NSP;
+      constexpr int QS = t % RX_SETS;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int rb = 0; rb < RX_RB; ++rb) {
@@ -481,34 +472,25 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
           acc = rx_mfma_s(t & 3, ring[(t * F + i) % RX_RING], xb[rb], sc.w[i >> 1][i & 1][t >> 2], xs[rb],
                           t == 0 ? f32x16{} : acc);
         }
-        if (QUANT) quant_unit(t + RX_QA, rb, sv[QS][rb]);
         if (t + 1 < NSP) {
           xb[rb] = x_frag(t + 1, rb);
           xs[rb] = x_scale(t + 1, rb);
         }
       }
       asm volatile("" : "+s"(zs));
-      if (QUANT) {
-        if (t + 6 < NSP)
-          slab_load(t + 6, false, sv[QS]);
+      if (COPY) {
+        slab_store(t + RX_QA, sv[QS]);
+        if (t + 2 * RX_SETS < NSP)
+          slab_load(t + 2 * RX_SETS, false, sv[QS]);
         else
-          slab_load(t + 6 - NSP, true, sv[QS]);
+          slab_load(t + 2 * RX_SETS - NSP, true, sv[QS]);
       }
-      // GEMM1 B's scales, late enough to leave the quantising k-steps their
-      // registers
+      // GEMM1 B's scales
       if (PH == 0 && t == NSP - RX_QA) load_sb(cur, sbs);
 #pragma unroll
       for (int i = 0; i < F; ++i) {
         const int pos = t * F + i;
         refill(ring[pos % RX_RING], std::integral_constant<int, PH>{}, pos % RX_RING, pos / RX_RING + 1);
-      }
-      // the quantisation's vector ALU work between the MFMAs
-      if (QUANT) {
-#pragma unroll
-        for (int m = 0; m < RX_RB * F; ++m) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
-        }
       }
       // the k-step's products are taken here: the compiler would otherwise
       // sink the MFMAs (pure operations) down to the accumulators' use after
@@ -592,6 +574,7 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
     if (tid == 0) qnext = atomicAdd(&a.qhead[qx], 1);
 
     // ================= GEMM2 parts, each with its epilogue =================
+    uint32_t en[3];   // the next tile's exponents, from part 1 to part 2
     // The parts also quantise the next tile's slabs 0..3 into the x_hat copy
     // (one unit per k-step; part 0 takes slabs 0 and 1), each register set
     // then loading the next tile's slab two further on.
@@ -621,22 +604,17 @@ __global__ __launch_bounds__(RX_NT, 1) void routed_mx_kernel(const MlpArgs a) {
           ub[rb] = u_frag(rb, kn);
           uss[rb] = u_scale(rb, kn);
         }
-        // slab qs = C + (C > 0) from register set qs % 2, units kb (parts 1,
-        // 2) or, in part 0, slab 0 over k-steps 0..3 and slab 1 over 4, 5
+        // the next tile: parts 0 and 1 copy its slabs 2C, 2C + 1 into LDS
+        // (k-steps 1, 3), their register sets then loading slabs 2C + 4,
+        // 2C + 5; part 1 loads its exponents (k-step 0), part 2 stores them
         asm volatile("" : "+s"(zs));
-        if (C == 0) {
-          if (kb < SU) quant_unit(0, kb, sv[0][kb]);
-          if (kb == SU - 1) slab_load(2, true, sv[0]);
-          if (kb >= SU) {
-            quant_unit(1, 2 * (kb - SU), sv[1][2 * (kb - SU)]);
-            quant_unit(1, 2 * (kb - SU) + 1, sv[1][2 * (kb - SU) + 1]);
-          }
-          if (kb == KB2 - 1) slab_load(3, true, sv[1]);
-        } else {
-          constexpr int QS = C + 1;   // slabs 2 (part 1), 3 (part 2)
-          if (kb < SU) quant_unit(QS, kb, sv[QS & 1][kb]);
-          if (kb == SU - 1) slab_load(QS + 2, true, sv[QS & 1]);
+        if (C < 2 && (kb == 1 || kb == 3)) {
+          const int sl = 2 * C + (kb >> 1);
+          slab_store(sl, sv[sl]);
+          slab_load(sl + RX_SETS, true, sv[sl]);
         }
+        if (C == 1 && kb == 0) exp_load(nx.p, buf ^ 1, en);
+        if (C == 2 && kb == 0) exp_store(en);
 #pragma unroll
         for (int j = 0; j < FC; ++j) {
           const int pos = kb * FC + j;
@@ -738,7 +716,7 @@ int routed_wide_mx_rows(int W, int h_e) { return (W == 768 && h_e == 384) ? RX_B
 
 hipError_t launch_routed_wide_mx(const MlpArgs& a, int tiles, int workers, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
-  if (a.hidden != 384 || a.wrec < mx_rec_dwords(768, 384)) return hipErrorInvalidValue;
+  if (a.hidden != 384 || a.wrec < mx_rec_dwords(768, 384) || !a.xq8 || !a.xe8) return hipErrorInvalidValue;
   workers &= ~7;
   const int grid = (workers <= 0 || tiles <= workers) ? tiles : workers;
   hipLaunchKernelGGL((routed_mx_kernel<768, 384>), dim3(grid), dim3(RX_NT), 0, s, a);
