@@ -101,7 +101,9 @@ __device__ __forceinline__ uint32_t bf16x8_absmax_bits(const uint4& w) {
   return m;
 }
 
-template <int W, int NBE>
+// XQ8: also write the MXFP8 copy of x_hat (a.xq8, a.xe8); a compile-time
+// switch, so the bf16 router carries none of its code or registers
+template <int W, int NBE, bool XQ8>
 __global__ __launch_bounds__(64 * RT_WAVES) void norm_route_kernel(const RouteArgs a) {
   constexpr int KB = W / 32;
   constexpr int EMAX = 64;
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(64 * RT_WAVES) void norm_route_kernel(const RouteAr
     xr[kb].w = pack_bf16x2(n[6], n[7]);
     if (valid && a.xhat)
       *reinterpret_cast<uint4*>(a.xhat + ((size_t)p * a.B + row) * W + kb * 32 + q * 8) = xr[kb];
-    if (a.xq8) {
+    if constexpr (XQ8) {
       // the bf16 row quantised per 32-column block (this lane's 8 columns and
       // those of lanes ^ 16, ^ 32, ^ 48): exponent floor(log2(amax)) - 8
       uint32_t mb = bf16x8_absmax_bits(xr[kb]);
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(64 * RT_WAVES) void norm_route_kernel(const RouteAr
       lg[j] = mfma16x16x32(af, as_bf16x8(*reinterpret_cast<const uint4*>(wr + (kb * NBE + j) * FRAG_ELEMS)), lg[j]);
   }
 
-  if (a.xq8 && valid) {
+  if (XQ8 && valid) {
     static_assert(KB % 4 == 0, "exponent dwords");
     uint32_t* er = reinterpret_cast<uint32_t*>(a.xe8 + ((size_t)p * a.B + row) * KB);
 #pragma unroll
@@ -585,7 +587,15 @@ __global__ __launch_bounds__(256) void permute_kernel(const TE* __restrict__ in,
 template <int W, int NBE>
 hipError_t launch_route_wn(const RouteArgs& a, hipStream_t s) {
   const int tiles = (a.B + 16 * RT_WAVES - 1) / (16 * RT_WAVES);
-  hipLaunchKernelGGL((norm_route_kernel<W, NBE>), dim3(a.P * tiles), dim3(64 * RT_WAVES), 0, s, a);
+  if (a.xq8) {
+    // the MXFP8 copy exists for the MXFP8 MoE widths only
+    if constexpr (W == 512 || W == 768)
+      hipLaunchKernelGGL((norm_route_kernel<W, NBE, true>), dim3(a.P * tiles), dim3(64 * RT_WAVES), 0, s, a);
+    else
+      return hipErrorInvalidValue;
+  } else {
+    hipLaunchKernelGGL((norm_route_kernel<W, NBE, false>), dim3(a.P * tiles), dim3(64 * RT_WAVES), 0, s, a);
+  }
   return hipGetLastError();
 }
 
