@@ -66,7 +66,7 @@ struct MoeWs {
   int* ntiles = nullptr;      // [P]
   int* counts = nullptr;      // [P][E]
   int* qhead = nullptr;       // [8] routed-MLP tile queues (zeroed by the bucket kernel)
-  int* hist = nullptr;        // [P][ceil(B/64)][E] router choices per 64-row chunk
+  int* hist = nullptr;        // [P][chunks][E] router choices per row chunk (128 rows; sized for 64)
   uint16_t* part = nullptr;   // [B][P][k][W] gated expert outputs, bf16
   uint8_t* xq8 = nullptr;     // MXFP8 MoE only: x_hat's E4M3 codes [P][B][W], then
                               // its exponents [P][B][W/32] (the router's output

@@ -40,10 +40,10 @@ namespace {
 // groups, 256 registers each) hide one group's SiLU and row I/O behind the
 // other group's MFMAs, and let a Mix tile hold two adjacent positions; they
 // are used where a wave's 64 rows keep each weight fragment busy for two
-// MFMAs (W = 256) or the accumulators of a 4-wave tile would not fit
-// (W = 768). 4 waves (one per SIMD, 512 registers each, every wave on all BM
-// rows) double the reuse of each weight fragment where BM is only 64
-// (W = 512) and serve W = 128.
+// MFMAs (W = 256). 4 waves (one per SIMD, 512 registers each, every wave on
+// all BM rows) double the reuse of each weight fragment where BM is only 64
+// (W = 512 and 768: at W = 768 the 64 x 768 fp32 output tile fills the 256
+// accumulator registers of each wave) and serve W = 128.
 constexpr int mlp_waves(int W) { return W == 256 ? 8 : 4; }
 
 // Workgroups per CU. The dense W = 256 sub-layer runs as two 4-wave
