@@ -127,24 +127,21 @@ def cpu_baseline(wl, banks, x, budget_s):
         forward(x[:n].astype(np.float64), wl, ws)
         return time.perf_counter() - t0
 
-    if one_block:
-        # one run: decoding the block's weight slices (seconds at the 15B
-        # shapes) dominates, so probes would cost as much as the sample
-        n = min(wl.B, 64)
-        dt = run(n)
-    else:
+    if not one_block:
         run(2)                                 # first-touch costs out of the probes
-        # grow the probe until it takes a quarter of the budget, then extrapolate
-        # from the last two probes (per-sample cost rises with n: cache effects)
-        n_prev, t_prev = 8, run(8)
-        n_cur, t_cur = n_prev, t_prev
-        while t_cur < budget_s / 4 and n_cur < wl.B:
-            n_prev, t_prev = n_cur, t_cur
-            n_cur = min(wl.B, n_cur * 4)
-            t_cur = run(n_cur)
-        per = max((t_cur - t_prev) / max(n_cur - n_prev, 1), 1e-6)
-        n = int(min(wl.B, max(n_cur, n_cur + (budget_s - t_cur) / per)))
-        dt = run(n)
+    # grow the probe until it takes a quarter of the budget, then extrapolate
+    # from the last two probes (per-sample cost rises with n: cache effects;
+    # for MoE stacks every run also decodes the block's weight slices, a
+    # fixed part that the difference of two probes leaves out)
+    n_prev, t_prev = 8, run(8)
+    n_cur, t_cur = n_prev, t_prev
+    while t_cur < budget_s / 4 and n_cur < wl.B:
+        n_prev, t_prev = n_cur, t_cur
+        n_cur = min(wl.B, n_cur * 4)
+        t_cur = run(n_cur)
+    per = max((t_cur - t_prev) / max(n_cur - n_prev, 1), 1e-6)
+    n = int(min(wl.B, max(n_cur, n_cur + (budget_s - t_cur) / per)))
+    dt = run(n)
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
