@@ -139,7 +139,10 @@ def cpu_baseline(wl, banks, x, budget_s):
         n_prev, t_prev = n_cur, t_cur
         n_cur = min(wl.B, n_cur * 4)
         t_cur = run(n_cur)
-    per = max((t_cur - t_prev) / max(n_cur - n_prev, 1), 1e-6)
+    # with a single probe (the first already took a quarter of the budget)
+    # its whole time counts as per-sample cost, which can only shrink the sample
+    per = (t_cur - t_prev) / (n_cur - n_prev) if n_cur > n_prev else t_cur / n_cur
+    per = max(per, t_cur / (4.0 * n_cur), 1e-6)
     n = int(min(wl.B, max(n_cur, n_cur + (budget_s - t_cur) / per)))
     dt = run(n)
     try:
