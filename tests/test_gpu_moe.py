@@ -15,11 +15,17 @@ SMALL_MOE = dg.Workload("small_moe_bf16", B=300, T=4, H=4, D=128, L=3, E=16, top
                         expert_hidden=128, shared_hidden=256, alpha=4.0, gap=2, seed=31)
 SMALL_MOE_F32 = SMALL_MOE.with_(name="small_moe_f32", dtype="f32", B=64, D=32, E=6, top_k=2,
                                 expert_hidden=16, shared_hidden=24, alpha=3.0, seed=32)
+# wider expert sets: the router's logits span 3 and 4 MFMA column blocks, and
+# the bucket kernel's per-expert tables reach their 64-expert limit
+SMALL_MOE_E48 = SMALL_MOE.with_(name="small_moe_e48", E=48, top_k=6, alpha=8.0, seed=33)
+SMALL_MOE_E64 = SMALL_MOE.with_(name="small_moe_e64", E=64, top_k=8, alpha=8.0, seed=34)
+SMALL = {"small_bf16": SMALL_MOE, "small_f32": SMALL_MOE_F32, "small_e48": SMALL_MOE_E48,
+         "small_e64": SMALL_MOE_E64}
 
-@pytest.mark.parametrize("which", ["small_bf16", "small_f32"])
+@pytest.mark.parametrize("which", ["small_bf16", "small_f32", "small_e48", "small_e64"])
 def test_small_moe_stack_all_rows(which):
     require_gpu()
-    wl = SMALL_MOE if which == "small_bf16" else SMALL_MOE_F32
+    wl = SMALL[which]
     say("small moe stack", wl)
     ctx, banks, ws = context(which, wl)
     import torch
@@ -38,11 +44,11 @@ def test_small_moe_stack_all_rows(which):
     assert torch.equal(y, y2)
 
 
-@pytest.mark.parametrize("which", ["small_bf16", "small_f32", "w4"])
+@pytest.mark.parametrize("which", ["small_bf16", "small_f32", "small_e48", "small_e64", "w4"])
 @pytest.mark.parametrize("sub", [0, 1])
 def test_route_matches_oracle(which, sub):
     require_gpu()
-    wl = {"small_bf16": SMALL_MOE, "small_f32": SMALL_MOE_F32, "w4": dg.WORKLOADS[4]}[which]
+    wl = SMALL[which] if which in SMALL else dg.WORKLOADS[4]
     say("route", which, sub)
     ctx, banks, ws = context(which, wl)
     x = dg.make_x(wl)
