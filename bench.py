@@ -164,8 +164,10 @@ def cpu_baseline(wl, banks, x, budget_s):
 
 def routed_is_wide(wl):
     """Whether the library runs this workload's routed experts in a 128-row
-    wide kernel (W 768, h_e 384: bf16 or MXFP8) rather than the fused MLP
-    kernel."""
+    wide kernel (W 768, h_e 384: bf16 or MXFP8; W 512, h_e 256: bf16)
+    rather than the fused MLP kernel."""
+    if wl.dtype == "bf16" and wl.width(1) == 512 and wl.expert_hidden == 256:
+        return True
     return wl.dtype in ("bf16", "mxfp8") and wl.width(1) == 768 and wl.expert_hidden == 384
 
 
@@ -173,7 +175,7 @@ def routed_kernel_name(wl):
     if routed_is_wide(wl):
         if wl.dtype == "mxfp8":
             return "routed_mx_kernel<768, 384> (128-row tiles, MXFP8)"
-        return "routed_kernel<768, 384> (128-row tiles)"
+        return f"routed_kernel<{wl.width(1)}, {wl.expert_hidden}> (128-row tiles)"
     return f"mlp_kernel<{wl.width(1)}, ROUTED{', MXFP8' if wl.dtype == 'mxfp8' else ''}>"
 
 

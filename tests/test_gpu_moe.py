@@ -161,11 +161,14 @@ def test_buckets_match_routing(which, sub):
     check_buckets(idx2, c2, r2, wl.E)
 
 
+@pytest.mark.parametrize("width", [128, 512])
 @pytest.mark.parametrize("sub", [0, 1])
-def test_skewed_routing_and_empty_buckets(sub):
+def test_skewed_routing_and_empty_buckets(sub, width):
     """Positive inputs, positive router columns except expert 5 (all
     negative): expert 5's bucket is always empty, and expert 3 (column x10)
-    is chosen by every row, so its bucket holds all B rows (16 tiles). The
+    is chosen by every row, so its bucket holds all B rows (8 tiles of the
+    128-row kernels: the fused one at W = 128, the wide routed-expert kernel
+    at W = 512 with expert hidden 256). The
     down matrices at full scale and, in the Revert sub-layer, a zero
     residual make the sub-layer output F itself, so the all-rows bucket's
     expert outputs are what the comparison sees."""
@@ -173,6 +176,8 @@ def test_skewed_routing_and_empty_buckets(sub):
     import torch
     from token_moe_amd import runner
     wl = SMALL_MOE.with_(name="skew", L=1, B=1000, down_scale=1.0)
+    if width == 512:
+        wl = wl.with_(name="skew512", D=512, expert_hidden=256, shared_hidden=512)
     banks = dg.weight_banks(wl)
     for s in (0, 1):
         wr = np.abs(dg.bf16_bits_to_f32(banks[(1, s, dg.K_ROUTER)]))

@@ -1,15 +1,16 @@
 // tmx_routed.hip -- the grouped routed-expert MLP of the Sparse-Pertoken MoE
 // (TokenMixer-Large summary Eq. 19, section 2.5.1 MoEGroupedSwiGLU) for wide
-// rows (W = 768, h_e = 384), on gfx950 bf16 MFMA.
+// rows (W = 768, h_e = 384; W = 512, h_e = 256), on gfx950 bf16 MFMA.
 //
 // Why a kernel of its own: in the general fused MLP kernel a W = 768 tile has
 // 64 rows (its GEMM2 accumulators, 64 x 768 fp32, fill the AGPRs), so every
 // weight fragment fed from L2 serves two 32-row MFMA blocks, and that weight
-// stream, not the MFMA rate, bounds the routed launch. Here a tile has
-// BM = 128 rows of one (position, expert) bucket, and each weight fragment
-// serves four MFMA blocks, which halves the weight bytes per FLOP. The
-// accumulators of 128 rows do not fit at once either, so a tile runs in
-// phases that each stay within the 256 AGPRs:
+// stream, not the MFMA rate, bounds the routed launch (at W = 512 the 4-wave
+// fused tile also holds 64 rows). Here a tile has BM = 128 rows of one
+// (position, expert) bucket, and each weight fragment serves four MFMA
+// blocks, which halves the weight bytes per FLOP. The accumulators of 128
+// rows do not fit at once either, so a tile runs in phases that each stay
+// within the 256 AGPRs (shown for W = 768, h_e = 384):
 //
 //   GEMM1 A  S_gate, S_up for hidden blocks [8 blocks of 32] (2 per wave,
 //            256 accumulator registers), K-outer: the rows' x_hat columns
@@ -23,17 +24,22 @@
 //            the expert-output buffer;
 //   GEMM2 1  O [128, 384:768) ... out 1 (staged through the U region).
 //
+// At h_e = 256 pass A covers the whole hidden (no pass B: x_hat is read once)
+// and each GEMM2 half has 2 column blocks per wave.
+//
 // The second x_hat pass costs 196 KB of L2/last-level-cache reads per tile
 // against the 1.7 MB of expert weights every tile streams.
 //
-// Pipelines. Weight fragments stream through a 12-slot register ring in one
-// order per tile (GEMM1 A, GEMM1 B, GEMM2 0, GEMM2 1) that runs on into the
-// next tile; a slot is refilled as soon as its four MFMAs have issued. x_hat
-// slabs (24 per tile: 12 per GEMM1 pass) run through three LDS buffers:
-// at slab step s, slab s+1 goes from registers to LDS and slab s+3's loads go
-// out (two register sets, so a load has two slab steps to land); the last
-// three slab steps of a tile load the next tile's first slabs, which wait in
-// LDS buffer 0 and registers through GEMM2.
+// Pipelines. Weight fragments stream through a register ring (24 slots at
+// W = 768, 16 at W = 512) in one order per tile (GEMM1 A, GEMM1 B, GEMM2 0,
+// GEMM2 1) that runs on into the next tile; a slot is refilled as soon as its
+// four MFMAs have issued. x_hat slabs (24 per tile at W = 768: 12 per GEMM1
+// pass; 8 at W = 512) run through three LDS buffers (four at W = 512, so
+// that a tile's slab count is a whole number of buffer turns): at slab step
+// s, slab s+1 goes from registers to LDS and slab s+3's loads go out (two
+// register sets, so a load has two slab steps to land); the last three slab
+// steps of a tile load the next tile's first slabs, which wait in LDS buffer
+// 0 and registers through GEMM2.
 #include <type_traits>
 
 #include "tmx_internal.h"
@@ -46,7 +52,6 @@ constexpr int RT_NT = 256;   // 4 waves
 constexpr int RT_RB = 4;     // 32-row blocks per tile
 constexpr int RT_BM = 32 * RT_RB;
 constexpr int RT_SC = 64;    // columns per x_hat slab
-constexpr int RT_RING = 24;  // weight fragments in flight per wave
 constexpr int RT_RSRC_W3 = 0x00020000;   // buffer resource word 3: raw 32-bit data, no swizzle
 // cache policy of the second pass's x_hat loads (the rows' last use) and of
 // the gated-output stores: streaming (non-temporal), which keeps the expert
@@ -71,10 +76,16 @@ template <int W, int HE>
 struct RtShape {
   static constexpr int BM = RT_BM;
   static constexpr int HA = 2;                    // hidden blocks per wave, GEMM1 pass A
-  static constexpr int HBB = HE / 128 - HA;       // ... pass B
+  static constexpr int HBB = HE / 128 - HA;       // ... pass B (none at h_e = 256)
   static constexpr int NOH = W / 256;             // output blocks per wave and GEMM2 half
   static constexpr int NSP = W / RT_SC;           // slabs per GEMM1 pass
-  static constexpr int NSL = 2 * NSP;             // slab steps per tile
+  static constexpr int NSL = (HBB > 0 ? 2 : 1) * NSP;   // slab steps per tile
+  // x_hat slab buffers in LDS and the slab-step group: slab t sits in buffer
+  // t % NBUF and register set t % 2, and a tile's NSL slab steps must be
+  // whole groups so that the next tile's slab 0 lands in buffer 0, set 0
+  static constexpr int NBUF = NSL % 3 == 0 ? 3 : 4;
+  static constexpr int G = NBUF == 3 ? 6 : 4;
+  static constexpr int RING = W == 768 ? 24 : 16; // weight fragments in flight per wave
   static constexpr int KB1 = W / 16;              // GEMM1 k-steps per pass
   static constexpr int KB2 = HE / 16;             // GEMM2 k-steps per half
   static constexpr int FA = 2 * HA, FB = 2 * HBB, FC = NOH;   // fragments per k-step
@@ -83,26 +94,28 @@ struct RtShape {
   static constexpr int HS = W / 2 + 8;            // staged half-row stride (bf16)
   static constexpr int SLAB = BM * RT_SC;         // bf16 per slab buffer
   static constexpr int SU = BM * RT_SC / 8 / RT_NT;   // slab units per lane
-  static_assert(HE % 128 == 0 && HBB >= 1 && HBB <= 2, "two GEMM1 passes of at most 2 hidden blocks per wave");
-  static_assert(W % 256 == 0 && W % RT_SC == 0 && NSP % 6 == 0, "slab steps run in groups of six");
+  static_assert(HE % 128 == 0 && HBB >= 0 && HBB <= 2, "one or two GEMM1 passes of at most 2 hidden blocks per wave");
+  static_assert(W % 256 == 0 && W % RT_SC == 0 && NSP % G == 0 && NSL % NBUF == 0,
+                "slab steps run in whole groups, and pass B starts at a group");
   static_assert((BM * RT_SC / 8) % RT_NT == 0, "slab units per lane");
-  static_assert(LA % RT_RING == 0 && LB % RT_RING == 0 && LC % RT_RING == 0 && RT_RING % FA == 0 &&
-                RT_RING % FB == 0 && RT_RING % FC == 0,
+  static_assert(LA % RING == 0 && LB % RING == 0 && LC % RING == 0 && RING % FA == 0 &&
+                (FB == 0 || RING % FB == 0) && RING % FC == 0,
                 "every phase is whole turns of the ring, each of whole k-steps");
   static_assert(KB2 % 4 == 0, "GEMM2 k-steps run in groups of four");
   static_assert(32 * HS * 2 <= 2 * SLAB * 2, "a staged 32-row half fits in two slab buffers");
   static_assert(BM * HS <= BM * US, "a staged 128-row half fits in the U region");
-  static_assert(3 * SLAB * 2 + BM * US * 2 + 3 * 2 * BM * 4 + 16 <= 160 * 1024, "LDS budget");
+  static_assert(NBUF * SLAB * 2 + BM * US * 2 + 3 * 2 * BM * 4 + 16 <= 160 * 1024, "LDS budget");
 };
 
 template <int W, int HE>
 __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
   using S = RtShape<W, HE>;
   constexpr int BM = S::BM, HA = S::HA, HBB = S::HBB, NOH = S::NOH, NSP = S::NSP, NSL = S::NSL;
+  constexpr int NBUF = S::NBUF, G = S::G, RING = S::RING;
   constexpr int KB1 = S::KB1, KB2 = S::KB2, FA = S::FA, FB = S::FB, FC = S::FC;
   constexpr int LA = S::LA, LB = S::LB, LC = S::LC, US = S::US, HS = S::HS, SLAB = S::SLAB, SU = S::SU;
 
-  __shared__ __attribute__((aligned(16))) uint16_t slabs[3 * SLAB];
+  __shared__ __attribute__((aligned(16))) uint16_t slabs[NBUF * SLAB];
   __shared__ __attribute__((aligned(16))) uint16_t us[BM * US];
   __shared__ int rowb[2][BM];      // sample row of each tile row (-1: padding)
   __shared__ int rowgi[2][BM];     // expert-output row (b, p, slot)
@@ -199,8 +212,9 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
       const int c = (((ii >> 1) * KB1 + kb) * 2 + (ii & 1)) * 1024;
       return __builtin_amdgcn_raw_buffer_load_b128(ph == 0 ? cgu : ngu, voff_gu(HA * wave), c, 0);
     }
-    if (ph == 1) {
-      const int kb = pos / FB, ii = pos % FB;
+    if (HBB > 0 && ph == 1) {
+      constexpr int FBn = FB > 0 ? FB : 1;
+      const int kb = pos / FBn, ii = pos % FBn;
       const int c = (((ii >> 1) * KB1 + kb) * 2 + (ii & 1)) * 1024;
       return __builtin_amdgcn_raw_buffer_load_b128(cgu, voff_gu(4 * HA + HBB * wave), c, 0);
     }
@@ -208,14 +222,16 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
     const int c = (kb * (W / 32) + (ph == 3 ? W / 64 : 0) + j) * 1024;
     return __builtin_amdgcn_raw_buffer_load_b128(cwd, voff_wd(), c, 0);
   };
-  constexpr int SA = LA / RT_RING, SB = LB / RT_RING, SC = LC / RT_RING;   // super-steps per phase
-  // slot i of phase PH, refilled for super-step sn (past the phase: the next one)
+  constexpr int SA = LA / RING, SB = LB / RING, SC = LC / RING;   // super-steps per phase
+  // slot i of phase PH, refilled for super-step sn (past the phase: the next
+  // one, which after pass A is GEMM2 when there is no pass B)
   auto refill = [&](v4u& dst, auto ph_tag, int i, int sn) __attribute__((always_inline)) {
     constexpr int PH = decltype(ph_tag)::value;
     constexpr int NSS = PH == 0 ? SA : PH == 1 ? SB : SC;
-    dst = sn < NSS ? wload(PH, sn * RT_RING + i) : wload(PH + 1, (sn - NSS) * RT_RING + i);
+    constexpr int NPH = (PH == 0 && HBB == 0) ? 2 : PH + 1;
+    dst = sn < NSS ? wload(PH, sn * RING + i) : wload(NPH, (sn - NSS) * RING + i);
   };
-  v4u ring[RT_RING];
+  v4u ring[RING];
 
   // ---- x_hat slabs: unit u = tid + 256 i of a slab is row u / 8, 16-byte
   // chunk u % 8 of the slab's 64 columns, stored at chunk (u % 8) ^ (row % 8)
@@ -287,7 +303,7 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
     slab_load(1, sv[1]);
     slab_load(2, sv[0]);
 #pragma unroll
-    for (int f = 0; f < RT_RING; ++f) ring[f] = wload(0, f);
+    for (int f = 0; f < RING; ++f) ring[f] = wload(0, f);
     slab_store(0, s0);
   }
   __syncthreads();
@@ -300,7 +316,7 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
 
     // ---- one slab step of GEMM1 pass PH (0: A, 1: B): slab t = 6 m + K of
     // the pass (m runtime, K compile-time; t + NSP in the tile's slab stream
-    // for pass B). K % 3 is the slab's buffer. Slab t+1 goes from registers
+    // for pass B). K % NBUF is the slab's buffer. Slab t+1 goes from registers
     // to its buffer and slab t+3's loads go out, then the slab's 4 k-steps.
     // The barrier before the last k-step makes slab t+1 visible (that step
     // prefetches its first fragments) and means every wave is done with slab
@@ -308,8 +324,8 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
     auto slab_step = [&](auto ph_tag, auto k_tag, int m, auto& sg, auto& su) __attribute__((always_inline)) {
       constexpr int PH = decltype(ph_tag)::value, K = decltype(k_tag)::value;
       constexpr int F = PH == 0 ? FA : FB;
-      constexpr int sb = K % 3, sbn = (K + 1) % 3;
-      const int t = (PH == 0 ? 0 : NSP) + 6 * m + K;             // slab of the tile's stream
+      constexpr int sb = K % NBUF, sbn = (K + 1) % NBUF;
+      const int t = (PH == 0 ? 0 : NSP) + G * m + K;             // slab of the tile's stream
       slab_store(sbn, sv[(K + 1) & 1]);
       slab_load(t + 3, sv[(K + 1) & 1]);
 #pragma unroll
@@ -321,7 +337,7 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
         // x_hat fragment is replaced by the next k-step's (the next slab's on
         // the last step), so one register set serves both; the weight
         // fragments' slots are refilled after the last block.
-        const int kb = 24 * m + 4 * K + q;
+        const int kb = 4 * (G * m + K) + q;
 #pragma unroll
         for (int rb = 0; rb < RT_RB; ++rb) {
 #pragma unroll
@@ -330,7 +346,7 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
             // separate clearing, which the compiler would hoist into the
             // previous phase (evicting its live accumulators to VGPRs)
             f32x16& acc = (i & 1) ? su[rb][i >> 1] : sg[rb][i >> 1];
-            acc = rt_mfma(ring[(kb * F + i) % RT_RING], xb[rb], kb == 0 ? f32x16{} : acc);
+            acc = rt_mfma(ring[(kb * F + i) % RING], xb[rb], kb == 0 ? f32x16{} : acc);
           }
           if (q < 3) xb[rb] = slab_frag(sb, rb, q + 1);
           else if (t + 1 < NSL) xb[rb] = slab_frag(sbn, rb, 0);
@@ -338,7 +354,7 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
 #pragma unroll
         for (int i = 0; i < F; ++i) {
           const int pos = kb * F + i;
-          refill(ring[pos % RT_RING], std::integral_constant<int, PH>{}, pos % RT_RING, pos / RT_RING + 1);
+          refill(ring[pos % RING], std::integral_constant<int, PH>{}, pos % RING, pos / RING + 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -365,33 +381,30 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
           }
     };
 
+    // one group of G slab steps of pass PH (K = 0 .. G-1, compile-time)
+    auto slab_group = [&](auto ph_tag, int m, auto& sg, auto& su) __attribute__((always_inline)) {
+      slab_step(ph_tag, std::integral_constant<int, 0>{}, m, sg, su);
+      slab_step(ph_tag, std::integral_constant<int, 1>{}, m, sg, su);
+      slab_step(ph_tag, std::integral_constant<int, 2>{}, m, sg, su);
+      slab_step(ph_tag, std::integral_constant<int, 3>{}, m, sg, su);
+      if constexpr (G == 6) {
+        slab_step(ph_tag, std::integral_constant<int, 4>{}, m, sg, su);
+        slab_step(ph_tag, std::integral_constant<int, 5>{}, m, sg, su);
+      }
+    };
     // ================= GEMM1 pass A =================
     {
       f32x16 sg[RT_RB][HA], su[RT_RB][HA];
 #pragma unroll
-      for (int m = 0; m < NSP / 6; ++m) {
-        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, m, sg, su);
-        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, m, sg, su);
-        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, m, sg, su);
-        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{}, m, sg, su);
-        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 4>{}, m, sg, su);
-        slab_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 5>{}, m, sg, su);
-      }
+      for (int m = 0; m < NSP / G; ++m) slab_group(std::integral_constant<int, 0>{}, m, sg, su);
       store_u(HA * wave, sg, su, std::integral_constant<int, HA>{});
     }
-    // ================= GEMM1 pass B =================
+    // ================= GEMM1 pass B (h_e > 256) =================
     fresh();
-    {
+    if constexpr (HBB > 0) {
       f32x16 sg[RT_RB][HBB], su[RT_RB][HBB];
 #pragma unroll
-      for (int m = 0; m < NSP / 6; ++m) {
-        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, m, sg, su);
-        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, m, sg, su);
-        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{}, m, sg, su);
-        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 3>{}, m, sg, su);
-        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 4>{}, m, sg, su);
-        slab_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 5>{}, m, sg, su);
-      }
+      for (int m = 0; m < NSP / G; ++m) slab_group(std::integral_constant<int, 1>{}, m, sg, su);
       store_u(4 * HA + HBB * wave, sg, su, std::integral_constant<int, HBB>{});
     }
     __syncthreads();   // U complete
@@ -415,13 +428,13 @@ __global__ __launch_bounds__(RT_NT, 1) void routed_kernel(const MlpArgs a) {
         for (int rb = 0; rb < RT_RB; ++rb) {
 #pragma unroll
           for (int j = 0; j < FC; ++j)
-            o[rb][j] = rt_mfma(ring[(kb * FC + j) % RT_RING], ub[rb], kb == 0 ? f32x16{} : o[rb][j]);
+            o[rb][j] = rt_mfma(ring[(kb * FC + j) % RING], ub[rb], kb == 0 ? f32x16{} : o[rb][j]);
           ub[rb] = u_frag(rb, kn);
         }
 #pragma unroll
         for (int j = 0; j < FC; ++j) {
           const int pos = kb * FC + j;
-          refill(ring[pos % RT_RING], std::integral_constant<int, PH>{}, pos % RT_RING, pos / RT_RING + 1);
+          refill(ring[pos % RING], std::integral_constant<int, PH>{}, pos % RING, pos / RING + 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -527,13 +540,15 @@ hipError_t launch_rt(const MlpArgs& a, int grid, hipStream_t s) {
 
 }  // namespace
 
-int routed_wide_rows(int W, int h_e) { return (W == 768 && h_e == 384) ? RT_BM : 0; }
+int routed_wide_rows(int W, int h_e) { return ((W == 768 && h_e == 384) || (W == 512 && h_e == 256)) ? RT_BM : 0; }
 
 hipError_t launch_routed_wide(const MlpArgs& a, int tiles, int workers, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
   workers &= ~7;
   const int grid = (workers <= 0 || tiles <= workers) ? tiles : workers;
+  // (routed_wide_rows admits one width per expert hidden size)
   if (a.hidden == 384) return launch_rt<768, 384>(a, grid, s);
+  if (a.hidden == 256) return launch_rt<512, 256>(a, grid, s);
   return hipErrorInvalidValue;
 }
 
