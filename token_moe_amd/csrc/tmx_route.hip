@@ -108,8 +108,11 @@ __device__ __forceinline__ uint32_t bf16x8_absmax_bits(const uint4& w) {
 
 // XQ8: also write the MXFP8 copy of x_hat (a.xq8, a.xe8); a compile-time
 // switch, so the bf16 router carries none of its code or registers
+// (the MXFP8 instantiations are held to four waves per SIMD, 128 VGPRs: they
+// spill a few dozen registers at W = 768 but run 3-6% faster than at two
+// waves per SIMD; the bf16 ones reach four waves unconstrained)
 template <int W, int NBE, bool XQ8>
-__global__ __launch_bounds__(64 * RT_WAVES) void norm_route_kernel(const RouteArgs a) {
+__global__ __launch_bounds__(64 * RT_WAVES, XQ8 ? 4 : 2) void norm_route_kernel(const RouteArgs a) {
   constexpr int KB = W / 32;
   constexpr int EMAX = 64;
   constexpr int NFR = KB * NBE;              // router fragments of one position
